@@ -1,0 +1,111 @@
+/*
+ * vla.h -- C ABI of the MI355X (gfx950) Variational Linear Attention forward library.
+ *
+ * Method: "Variational Linear Attention: Stable Associative Memory for Long-Context
+ * Transformers" (Pandey & Singh), as summarised on gist.science ("VLA summary" below).
+ * For every independent (batch, head) stream and every token t the library computes
+ *
+ *   khat_t = k_t / ||k_t||                                    (VLA summary §2.1, §2.3)
+ *   z_t    = A_{t-1} u_t
+ *   A_t    = A_{t-1} - z_t z_t^T / (1 + u_t^T z_t)            (§2.3 step 1, Sherman-Morrison)
+ *   ahat_t = A_t khat_t / ||A_t khat_t||                      (§2.3 step 2)
+ *   S_t    = S_{t-1} + (v_t - S_{t-1} khat_t) ahat_t^T        (§2.3 step 3)
+ *   n_t    = n_{t-1} + phi(k_t),  phi(x) = x + 1 (x > 0), e^x (x <= 0)   (ELU+1, §2.3)
+ *   o_t    = S_t phi(q_t) / (n_t^T phi(q_t) + eps)            (ratio readout, §2.3)
+ *
+ * from the fixed initial state A_0 = I / lambda0, S_0 = 0, n_0 = 0.  Readings of what the
+ * pages leave open: z_t = A_{t-1} u_t with u_t a per-token input used as given; a zero
+ * key gives khat = 0 and a zero A_t khat gives ahat = 0 (no memory write; A still
+ * downdates).
+ *
+ * Arithmetic: inputs are widened exactly to fp32; state and accumulation are fp32; `out`
+ * is rounded once (round to nearest even) to the input dtype.  Results are deterministic:
+ * the same inputs, shape and path give bitwise-identical outputs (no atomics).
+ */
+#ifndef RLS_VLA_H
+#define RLS_VLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t is `struct ihipStream_t *`; NULL means the default (null) stream. */
+struct ihipStream_t;
+
+typedef enum {
+  VLA_SUCCESS = 0,
+  VLA_ERROR_INVALID_VALUE = 1, /* NULL required pointer, size < 1, lambda0 <= 0 or not
+                                  finite, eps < 0 or not finite, unknown dtype or path,
+                                  workspace smaller than vla_workspace_size()          */
+  VLA_ERROR_NOT_SUPPORTED = 2, /* d not in {32, 64, 96, 128}; a pointer not 16-byte
+                                  aligned; a forced path or chunk the shape cannot use */
+  VLA_ERROR_OUT_OF_MEMORY = 3, /* internal workspace allocation failed                */
+  VLA_ERROR_LAUNCH = 4,        /* a HIP launch or runtime call failed                 */
+  VLA_ERROR_NO_DEVICE = 5      /* no usable gfx950 device is current                  */
+} vla_status_t;
+
+typedef enum { VLA_DTYPE_F32 = 0, VLA_DTYPE_BF16 = 1 } vla_dtype_t;
+
+typedef enum {
+  VLA_PATH_AUTO = 0,  /* library chooses from (B*H, T, d)                              */
+  VLA_PATH_SEQ = 1,   /* one workgroup per stream, token by token, state on chip       */
+  VLA_PATH_CHUNK = 2, /* chunked (Woodbury / WY) form; parallel over time segments     */
+} vla_path_t;
+
+typedef struct {
+  int64_t B, H, T, d;       /* q, k, v, u, out are [B, H, T, d], row-major, d fastest   */
+  int32_t dtype;            /* vla_dtype_t of q, k, v, u and out                        */
+  int32_t path;             /* vla_path_t                                               */
+  float eps;                /* readout denominator offset, >= 0 (1e-6 in all workloads) */
+  int32_t chunk;            /* chunk length of the chunked path; 0 = library default    */
+  void *workspace;          /* device scratch owned by the caller, or NULL              */
+  size_t workspace_bytes;   /* its size in bytes; ignored when workspace is NULL        */
+} vla_desc_t;
+
+/*
+ * vla_forward -- the recurrence above over all B*H streams, enqueued on `stream`.
+ *
+ * q, k, v, u  device pointers, [B, H, T, d] in desc->dtype, read only, 16-byte aligned.
+ * lambda0     initial penalty scale (M_0 = lambda0 I, A_0 = I / lambda0); > 0, finite.
+ * out         device pointer, [B, H, T, d] in desc->dtype, fully overwritten; must not
+ *             alias any input.
+ * S_final     device pointer to [B, H, d, d] fp32 (S[i][j], i = value index, j = key
+ *             index) receiving S_T, or NULL if not wanted.
+ * A_final     device pointer to [B, H, d, d] fp32 receiving A_T (symmetric), or NULL.
+ * desc        shapes, dtype, eps, path and workspace; read during the call only.
+ * stream      HIP stream (NULL = null stream); the call is asynchronous.
+ *
+ * Ownership: the caller owns every buffer; the library keeps no pointer after the call
+ * returns.  Workspace: the chunked path needs vla_workspace_size() bytes of device
+ * scratch.  If desc->workspace is NULL the library uses a per-device cache it grows on
+ * demand (that call may allocate, so time steady-state calls or pass a workspace).
+ * Calls that share a workspace (or the cache) on one device must be ordered on one
+ * stream.  Errors: a status code is returned and nothing is enqueued on an argument
+ * error; the call never aborts or throws.  Kernel faults surface at the caller's next
+ * synchronisation.  NaN and Inf in the inputs propagate and are not checked.
+ */
+vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
+                         float lambda0, void *out, float *S_final, float *A_final,
+                         const vla_desc_t *desc, struct ihipStream_t *stream);
+
+/* Bytes of device workspace vla_forward needs for this descriptor (0 for the
+ * sequential path).  Same argument checks as vla_forward; no device work. */
+vla_status_t vla_workspace_size(const vla_desc_t *desc, size_t *bytes);
+
+/* The path vla_forward would run for this descriptor (resolves VLA_PATH_AUTO). */
+vla_status_t vla_resolve_path(const vla_desc_t *desc, int32_t *path);
+
+/* Static, human-readable name of a status code. */
+const char *vla_status_string(vla_status_t status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int32_t vla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLS_VLA_H */

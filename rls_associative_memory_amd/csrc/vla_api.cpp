@@ -1,0 +1,213 @@
+// C-ABI front end of the VLA forward library: argument checks, path choice, workspace,
+// launches on the caller's stream.  No kernel code lives here.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "vla.h"
+#include "vla_internal.h"
+
+namespace {
+
+constexpr int32_t kVersion = 100;  // 0.1.0
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool d_supported(int64_t d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+
+// Shape / scalar checks shared by every entry point (no device work).
+vla_status_t check_desc(const vla_desc_t *desc) {
+  if (desc == nullptr) return VLA_ERROR_INVALID_VALUE;
+  if (desc->B < 1 || desc->H < 1 || desc->T < 1 || desc->d < 1) return VLA_ERROR_INVALID_VALUE;
+  if (desc->dtype != VLA_DTYPE_F32 && desc->dtype != VLA_DTYPE_BF16) return VLA_ERROR_INVALID_VALUE;
+  if (desc->path < VLA_PATH_AUTO || desc->path > VLA_PATH_CHUNK) return VLA_ERROR_INVALID_VALUE;
+  if (!(desc->eps >= 0.0f) || !std::isfinite(desc->eps)) return VLA_ERROR_INVALID_VALUE;
+  if (desc->chunk < 0) return VLA_ERROR_INVALID_VALUE;
+  // B*H*T*d must be addressable; B*H must fit a grid dimension.
+  const int64_t lim = int64_t(1) << 40;
+  if (desc->B > lim / desc->H) return VLA_ERROR_INVALID_VALUE;
+  const int64_t bh = desc->B * desc->H;
+  if (bh > (int64_t(1) << 31) - 1 || desc->T > lim / bh || desc->d > lim / (bh * desc->T))
+    return VLA_ERROR_INVALID_VALUE;
+  if (!d_supported(desc->d)) return VLA_ERROR_NOT_SUPPORTED;
+  return VLA_SUCCESS;
+}
+
+vla::Problem make_problem(const vla_desc_t *desc, float lambda0) {
+  vla::Problem p;
+  p.streams = desc->B * desc->H;
+  p.T = desc->T;
+  p.d = static_cast<int>(desc->d);
+  p.dtype = desc->dtype == VLA_DTYPE_F32 ? vla::Dtype::F32 : vla::Dtype::BF16;
+  p.lambda0 = lambda0;
+  p.eps = desc->eps;
+  return p;
+}
+
+// Resolve the path and chunk length; returns NOT_SUPPORTED for a forced path / chunk the
+// shape cannot use.
+vla_status_t resolve(const vla_desc_t *desc, const vla::Problem &p, int32_t *path, int *chunk) {
+  int c = desc->chunk;
+  int32_t want = desc->path;
+  if (want == VLA_PATH_AUTO) {
+    // Enough streams to fill the machine one workgroup each, or sequences too short to
+    // amortise the segment passes: run token by token.  Otherwise split time.
+    const bool few_streams = p.streams < 128;
+    const bool long_seq = p.T >= 1024;
+    want = (few_streams && long_seq && vla::chunk_supported(p, c ? c : vla::chunk_default(p)))
+               ? VLA_PATH_CHUNK
+               : VLA_PATH_SEQ;
+  }
+  if (want == VLA_PATH_CHUNK) {
+    if (c == 0) c = vla::chunk_default(p);
+    if (!vla::chunk_supported(p, c)) return VLA_ERROR_NOT_SUPPORTED;
+  } else {
+    c = 0;
+  }
+  *path = want;
+  *chunk = c;
+  return VLA_SUCCESS;
+}
+
+// Per-device check that the current device is gfx950, cached.
+struct DeviceInfo {
+  std::once_flag once;
+  bool ok = false;
+};
+std::mutex g_dev_mu;
+std::vector<DeviceInfo *> g_devs;
+
+bool device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  DeviceInfo *info;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (static_cast<int>(g_devs.size()) <= dev) g_devs.resize(dev + 1, nullptr);
+    if (g_devs[dev] == nullptr) g_devs[dev] = new DeviceInfo();
+    info = g_devs[dev];
+  }
+  std::call_once(info->once, [&] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      info->ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  });
+  return info->ok;
+}
+
+// Library-owned workspace cache, one buffer per device, grown on demand.
+struct WsCache {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::vector<WsCache> g_ws;
+
+vla_status_t cached_workspace(size_t need, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return VLA_ERROR_NO_DEVICE;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if (static_cast<int>(g_ws.size()) <= dev) g_ws.resize(dev + 1);
+  WsCache &c = g_ws[dev];
+  if (c.bytes < need) {
+    if (c.ptr != nullptr) {
+      // The old buffer may still be in use by work on other streams of this device.
+      if (hipDeviceSynchronize() != hipSuccess) return VLA_ERROR_LAUNCH;
+      (void)hipFree(c.ptr);
+      c.ptr = nullptr;
+      c.bytes = 0;
+    }
+    if (hipMalloc(&c.ptr, need) != hipSuccess) {
+      c.ptr = nullptr;
+      return VLA_ERROR_OUT_OF_MEMORY;
+    }
+    c.bytes = need;
+  }
+  *out = c.ptr;
+  return VLA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *vla_status_string(vla_status_t s) {
+  switch (s) {
+    case VLA_SUCCESS: return "VLA_SUCCESS";
+    case VLA_ERROR_INVALID_VALUE: return "VLA_ERROR_INVALID_VALUE";
+    case VLA_ERROR_NOT_SUPPORTED: return "VLA_ERROR_NOT_SUPPORTED";
+    case VLA_ERROR_OUT_OF_MEMORY: return "VLA_ERROR_OUT_OF_MEMORY";
+    case VLA_ERROR_LAUNCH: return "VLA_ERROR_LAUNCH";
+    case VLA_ERROR_NO_DEVICE: return "VLA_ERROR_NO_DEVICE";
+  }
+  return "VLA_ERROR_UNKNOWN";
+}
+
+int32_t vla_version(void) { return kVersion; }
+
+vla_status_t vla_resolve_path(const vla_desc_t *desc, int32_t *path) {
+  if (path == nullptr) return VLA_ERROR_INVALID_VALUE;
+  vla_status_t st = check_desc(desc);
+  if (st != VLA_SUCCESS) return st;
+  int chunk = 0;
+  return resolve(desc, make_problem(desc, 1.0f), path, &chunk);
+}
+
+vla_status_t vla_workspace_size(const vla_desc_t *desc, size_t *bytes) {
+  if (bytes == nullptr) return VLA_ERROR_INVALID_VALUE;
+  vla_status_t st = check_desc(desc);
+  if (st != VLA_SUCCESS) return st;
+  const vla::Problem p = make_problem(desc, 1.0f);
+  int32_t path = 0;
+  int chunk = 0;
+  st = resolve(desc, p, &path, &chunk);
+  if (st != VLA_SUCCESS) return st;
+  *bytes = path == VLA_PATH_CHUNK ? vla::chunk_workspace_bytes(p, chunk) : 0;
+  return VLA_SUCCESS;
+}
+
+vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
+                         float lambda0, void *out, float *S_final, float *A_final,
+                         const vla_desc_t *desc, struct ihipStream_t *stream) {
+  vla_status_t st = check_desc(desc);
+  if (st != VLA_SUCCESS) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || u == nullptr || out == nullptr)
+    return VLA_ERROR_INVALID_VALUE;
+  if (!(lambda0 > 0.0f) || !std::isfinite(lambda0)) return VLA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(u) || !aligned16(out) ||
+      !aligned16(S_final) || !aligned16(A_final))
+    return VLA_ERROR_NOT_SUPPORTED;
+  const vla::Problem p = make_problem(desc, lambda0);
+  int32_t path = 0;
+  int chunk = 0;
+  st = resolve(desc, p, &path, &chunk);
+  if (st != VLA_SUCCESS) return st;
+  void *ws = nullptr;
+  if (path == VLA_PATH_CHUNK) {
+    const size_t need = vla::chunk_workspace_bytes(p, chunk);
+    if (desc->workspace != nullptr) {
+      if (desc->workspace_bytes < need) return VLA_ERROR_INVALID_VALUE;
+      if (!aligned16(desc->workspace)) return VLA_ERROR_NOT_SUPPORTED;
+      ws = desc->workspace;
+    }
+  }
+  if (!device_ok()) return VLA_ERROR_NO_DEVICE;
+  if (path == VLA_PATH_CHUNK && ws == nullptr) {
+    st = cached_workspace(vla::chunk_workspace_bytes(p, chunk), &ws);
+    if (st != VLA_SUCCESS) return st;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (path == VLA_PATH_SEQ)
+    err = vla::launch_seq(p, q, k, v, u, out, S_final, A_final, s);
+  else
+    err = vla::launch_chunk(p, chunk, q, k, v, u, out, S_final, A_final, ws, s);
+  return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
+}
+
+}  // extern "C"

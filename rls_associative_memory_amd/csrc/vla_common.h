@@ -1,0 +1,85 @@
+// Device helpers shared by the VLA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vla {
+
+constexpr int kWave = 64;
+
+// ---- input / output element conversion ------------------------------------------------
+// bf16 is stored as its raw 16-bit pattern; widening to fp32 is exact.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet bit forced).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t x = __float_as_uint(f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((x >> 16) | 0x0040u);
+  x += 0x7fffu + ((x >> 16) & 1u);
+  return static_cast<uint16_t>(x >> 16);
+}
+
+template <typename T> struct io;
+
+template <> struct io<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte load
+  using vec_t = float4;
+  __device__ __forceinline__ static void unpack(const vec_t &r, float *o) {
+    o[0] = r.x; o[1] = r.y; o[2] = r.z; o[3] = r.w;
+  }
+  __device__ __forceinline__ static float store_cvt(float x) { return x; }
+};
+
+template <> struct io<bf16_t> {
+  static constexpr int kVec = 8;
+  using vec_t = uint4;
+  __device__ __forceinline__ static void unpack(const vec_t &r, float *o) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// ELU(x) + 1 with alpha = 1.
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+// ---- cross-lane sums ------------------------------------------------------------------
+// Every step pairs lanes symmetrically (a + b on one side, b + a on the other), so all
+// participating lanes finish with bitwise-identical sums.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_half_mirror(float x) {  // lane i <-> 7 - i within 8
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_mirror(float x) {  // lane i <-> 15 - i within 16
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float pair_sum(float x) { return x + dpp_xor1(x); }
+
+// Sum over all 64 lanes of the wave.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = x + dpp_xor1(x);
+  x = x + dpp_xor2(x);
+  x = x + dpp_half_mirror(x);
+  x = x + dpp_mirror(x);
+  x = x + __shfl_xor(x, 16);
+  x = x + __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace vla

@@ -146,3 +146,23 @@ def make_inputs(w: Workload, streams=None):
     idx = range(w.streams) if streams is None else list(streams)
     parts = [make_stream(w, s) for s in idx]
     return tuple(np.stack([p[i] for p in parts]) for i in range(4))
+
+
+def torch_dtype(w: Workload):
+    import torch
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def upload_inputs(w: Workload, device="cuda", streams=None):
+    """Device tensors q, k, v, u of shape [B, H, T, d] (or [len(streams), 1, T, d] for a
+    subset) in the workload's dtype, filled stream by stream to bound host memory."""
+    import torch
+    idx = list(range(w.streams)) if streams is None else list(streams)
+    shape = (w.B, w.H, w.T, w.d) if streams is None else (len(idx), 1, w.T, w.d)
+    dt = torch_dtype(w)
+    bufs = [torch.empty(shape, dtype=dt, device=device) for _ in range(4)]
+    flat = [b.view(-1, w.T, w.d) for b in bufs]
+    for slot, s in enumerate(idx):
+        for buf, x in zip(flat, make_stream(w, s)):
+            buf[slot].copy_(torch.from_numpy(x).to(dt))
+    return tuple(bufs)

@@ -1,0 +1,181 @@
+"""Thin ctypes binding of ``librls_vla.so`` (argument marshalling only).
+
+Every step of the recurrence runs in the library's HIP kernels; torch is used here only to
+hold device memory and to name the current HIP stream.  If the library has not been built
+the first call raises: there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+from typing import Optional
+
+import torch
+
+__all__ = ["forward", "workspace_size", "resolve_path", "library_path", "load_library",
+           "VlaError", "exported_symbols", "STATUS", "PATHS", "DTYPES", "VlaDesc"]
+
+STATUS = {
+    0: "VLA_SUCCESS",
+    1: "VLA_ERROR_INVALID_VALUE",
+    2: "VLA_ERROR_NOT_SUPPORTED",
+    3: "VLA_ERROR_OUT_OF_MEMORY",
+    4: "VLA_ERROR_LAUNCH",
+    5: "VLA_ERROR_NO_DEVICE",
+}
+PATHS = {"auto": 0, "seq": 1, "chunk": 2}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "vla.h")
+
+
+class VlaError(RuntimeError):
+    def __init__(self, status: int, where: str = "vla_forward"):
+        self.status = status
+        super().__init__(f"{where} failed: {STATUS.get(status, status)}")
+
+
+class VlaDesc(ctypes.Structure):
+    """Mirror of ``vla_desc_t`` in include/vla.h."""
+    _fields_ = [
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("path", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("chunk", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def library_path() -> str:
+    return os.environ.get("RLS_VLA_LIB", os.path.join(_PKG, "lib", "librls_vla.so"))
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load_library():
+    """Open the library once; raises if it is missing (build it first)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise FileNotFoundError(
+                f"{path} is missing: build it with `python -m rls_associative_memory_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        lib.vla_forward.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                    ctypes.POINTER(VlaDesc), vp]
+        lib.vla_forward.restype = ctypes.c_int
+        lib.vla_workspace_size.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_size_t)]
+        lib.vla_workspace_size.restype = ctypes.c_int
+        lib.vla_resolve_path.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_int32)]
+        lib.vla_resolve_path.restype = ctypes.c_int
+        lib.vla_status_string.argtypes = [ctypes.c_int]
+        lib.vla_status_string.restype = ctypes.c_char_p
+        lib.vla_version.argtypes = []
+        lib.vla_version.restype = ctypes.c_int32
+        _lib = lib
+        return lib
+
+
+def exported_symbols():
+    """Names of the functions include/vla.h declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vla_[a-z_0-9]+)\s*\(", text)))
+
+
+def make_desc(shape, dtype, eps=1e-6, path="auto", chunk=0, workspace=None) -> VlaDesc:
+    if len(shape) == 4:
+        B, H, T, d = shape
+    elif len(shape) == 3:
+        (B, T, d), H = shape, 1
+    else:
+        raise ValueError("inputs must be [B, H, T, d] or [N, T, d]")
+    if dtype not in DTYPES:
+        raise TypeError("dtype must be torch.float32 or torch.bfloat16")
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
+    desc = VlaDesc(B=B, H=H, T=T, d=d, dtype=DTYPES[dtype], path=PATHS[path], eps=float(eps),
+                   chunk=int(chunk), workspace=None, workspace_bytes=0)
+    if workspace is not None:
+        if not (workspace.is_cuda and workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous device tensor")
+        desc.workspace = workspace.data_ptr()
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    return desc
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise VlaError(status, where)
+
+
+def workspace_size(shape, dtype, path="auto", chunk=0) -> int:
+    lib = load_library()
+    desc = make_desc(shape, dtype, path=path, chunk=chunk)
+    n = ctypes.c_size_t(0)
+    _check(lib.vla_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "vla_workspace_size")
+    return n.value
+
+
+def resolve_path(shape, dtype, path="auto", chunk=0) -> str:
+    lib = load_library()
+    desc = make_desc(shape, dtype, path=path, chunk=chunk)
+    p = ctypes.c_int32(0)
+    _check(lib.vla_resolve_path(ctypes.byref(desc), ctypes.byref(p)), "vla_resolve_path")
+    return {v: k for k, v in PATHS.items()}[p.value]
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
+            lambda0: float, eps: float = 1e-6, path: str = "auto", chunk: int = 0,
+            return_state: bool = False, out: Optional[torch.Tensor] = None,
+            S_final: Optional[torch.Tensor] = None, A_final: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, stream: Optional[torch.cuda.Stream] = None):
+    """VLA forward over [B, H, T, d] (or [N, T, d]) device tensors.
+
+    Returns ``out`` (same shape and dtype as q), or ``(out, S_final, A_final)`` with the
+    fp32 [.., d, d] final states when ``return_state`` is set or state buffers are given.
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, u must share shape, dtype and device")
+    desc = make_desc(tuple(q.shape), q.dtype, eps=eps, path=path, chunk=chunk, workspace=workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q in shape and dtype and be contiguous")
+    state_shape = tuple(q.shape[:-2]) + (q.shape[-1], q.shape[-1])
+    if return_state:
+        if S_final is None:
+            S_final = torch.empty(state_shape, dtype=torch.float32, device=q.device)
+        if A_final is None:
+            A_final = torch.empty(state_shape, dtype=torch.float32, device=q.device)
+    for t in (S_final, A_final):
+        if t is not None and (tuple(t.shape) != state_shape or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise ValueError("S_final / A_final must be contiguous fp32 [.., d, d]")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = lib.vla_forward(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), u.data_ptr(), float(lambda0),
+            out.data_ptr(),
+            S_final.data_ptr() if S_final is not None else None,
+            A_final.data_ptr() if A_final is not None else None,
+            ctypes.byref(desc), s.cuda_stream)
+    _check(status, "vla_forward")
+    if S_final is not None or A_final is not None:
+        return out, S_final, A_final
+    return out

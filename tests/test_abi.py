@@ -1,0 +1,97 @@
+"""C-ABI library: loads, exports what include/vla.h declares, rejects bad arguments.
+
+The CPU cases never launch work: every call here fails argument validation, which the
+library performs before it touches a device.
+"""
+
+import ctypes
+
+import pytest
+import torch
+
+from rls_associative_memory_amd import vla
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vla.load_library()
+
+
+def desc(**kw):
+    base = dict(B=2, H=3, T=17, d=64, dtype=1, path=0, eps=1e-6, chunk=0, workspace=None,
+                workspace_bytes=0)
+    base.update(kw)
+    return vla.VlaDesc(**base)
+
+
+def test_header_symbols_are_exported(lib):
+    names = vla.exported_symbols()
+    assert {"vla_forward", "vla_workspace_size", "vla_status_string", "vla_resolve_path",
+            "vla_version"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/vla.h but not exported"
+
+
+def test_status_strings_and_version(lib):
+    for code, name in vla.STATUS.items():
+        assert lib.vla_status_string(code).decode() == name
+    assert lib.vla_status_string(99).decode() == "VLA_ERROR_UNKNOWN"
+    assert lib.vla_version() >= 100
+
+
+@pytest.mark.parametrize("bad", [
+    dict(B=0), dict(H=-1), dict(T=0), dict(d=0), dict(dtype=7), dict(path=9), dict(eps=-1.0),
+    dict(eps=float("nan")), dict(eps=float("inf")), dict(chunk=-4), dict(B=1 << 40, H=1 << 40),
+])
+def test_invalid_descriptors(lib, bad):
+    n = ctypes.c_size_t(123)
+    assert lib.vla_workspace_size(ctypes.byref(desc(**bad)), ctypes.byref(n)) == 1
+    p = ctypes.c_int32(0)
+    assert lib.vla_resolve_path(ctypes.byref(desc(**bad)), ctypes.byref(p)) == 1
+
+
+@pytest.mark.parametrize("d", [1, 16, 48, 80, 256])
+def test_unsupported_head_dim(lib, d):
+    n = ctypes.c_size_t(0)
+    assert lib.vla_workspace_size(ctypes.byref(desc(d=d)), ctypes.byref(n)) == 2
+
+
+def test_null_out_params(lib):
+    assert lib.vla_workspace_size(ctypes.byref(desc()), None) == 1
+    assert lib.vla_resolve_path(ctypes.byref(desc()), None) == 1
+    assert lib.vla_workspace_size(None, ctypes.byref(ctypes.c_size_t(0))) == 1
+
+
+def test_forward_argument_errors_before_any_device_work(lib):
+    ok = desc()
+    nul = None
+    fake = 4096  # never dereferenced: every call below fails validation first
+    # NULL required pointers
+    for i in range(5):
+        ptrs = [fake] * 5
+        ptrs[i] = nul
+        q, k, v, u, out = ptrs
+        assert lib.vla_forward(q, k, v, u, 1.0, out, None, None, ctypes.byref(ok), None) == 1
+    # lambda0 <= 0 or not finite
+    for lam in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.vla_forward(fake, fake, fake, fake, lam, fake, None, None,
+                               ctypes.byref(ok), None) == 1
+    # NULL descriptor
+    assert lib.vla_forward(fake, fake, fake, fake, 1.0, fake, None, None, None, None) == 1
+    # misaligned pointers
+    assert lib.vla_forward(fake + 2, fake, fake, fake, 1.0, fake, None, None,
+                           ctypes.byref(ok), None) == 2
+    assert lib.vla_forward(fake, fake, fake, fake, 1.0, fake, None, fake + 8,
+                           ctypes.byref(ok), None) == 2
+
+
+def test_sequential_path_needs_no_workspace(lib):
+    n = ctypes.c_size_t(99)
+    assert lib.vla_workspace_size(ctypes.byref(desc(path=1)), ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_binding_rejects_host_tensors():
+    x = torch.zeros(1, 1, 4, 32)
+    with pytest.raises(ValueError):
+        vla.forward(x, x, x, x, 1.0)
