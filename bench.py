@@ -1,0 +1,233 @@
+"""Throughput of the VLA forward recurrence on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--path auto|seq|chunk]
+
+One step is one ``vla_forward`` call over the whole workload (every (batch, head) stream,
+all T tokens, final S and A written when the workload asks for them), with inputs already
+resident in HBM.  The timed region is K steps between device synchronisations; the line
+printed on stdout is a single JSON object:
+
+  value        tokens*heads per second = B*H*T / seconds per step
+  roofline     the dominant kernel's algorithmic FLOP rate (12 d^2 + 20 d flops per
+               token*head, the plain count of the recurrence) over the published MI355X
+               peak of the unit it runs on, timed with HIP events on the launch stream
+  cpu_baseline the fp64 oracle timed on the host's cores on a bounded sample of the same
+               workload (the first ``--cpu-tokens`` tokens of ``cores`` streams), whose
+               outputs also give a causal parity check of the GPU run's first tokens
+
+Workloads are seeded synthetic inputs (rls_associative_memory_amd.inputs).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "VLA forward tokens·heads/sec at 1 MI355X; % of FP32/MFMA/HBM roofline"
+PEAK_FP32_TFLOPS = 157.3     # MI355X FP32 vector (packed) and FP32 MFMA, dense
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def flops_per_token_head(d: int) -> int:
+    # z = A u (2d^2), A downdate (2d^2), A khat (2d^2), S khat (2d^2), S update (2d^2),
+    # S phi(q) (2d^2), plus the O(d) vector work: 12 d^2 + 20 d.
+    return 12 * d * d + 20 * d
+
+
+def bytes_per_token_head(d: int, elem: int) -> int:
+    return 5 * d * elem  # q, k, v, u read; out written
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="long_t131072_d96")
+    ap.add_argument("--path", default="auto", choices=["auto", "seq", "chunk"])
+    ap.add_argument("--chunk", type=int, default=-1, help="chunk length (-1: the workload's)")
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens per stream in the oracle sample (0 disables the CPU leg)")
+    ap.add_argument("--cpu-cores", type=int, default=16)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
+    return ap.parse_args()
+
+
+def _oracle_job(args):
+    os.environ["OMP_NUM_THREADS"] = "1"
+    name, stream, T = args
+    from oracle import vla_forward as oracle_forward
+    from rls_associative_memory_amd.inputs import get_workload, make_stream
+    w = get_workload(name)
+    q, k, v, u = (x[:T] for x in make_stream(w, stream))
+    t0 = time.perf_counter()
+    out, _, _ = oracle_forward(q, k, v, u, w.lambda0, eps=w.eps)
+    return stream, time.perf_counter() - t0, out
+
+
+def cpu_baseline(w, tokens: int, cores: int):
+    """The oracle on the first ``tokens`` tokens of ``cores`` streams, one process per
+    stream (single-threaded BLAS in each).  Returns the report and the outputs."""
+    import multiprocessing as mp
+    tokens = min(tokens, w.T)
+    streams = list(range(min(cores, w.streams)))
+    env_before = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in env_before:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        t0 = time.perf_counter()
+        with ctx.Pool(processes=len(streams)) as pool:
+            res = pool.map(_oracle_job, [(w.name, s, tokens) for s in streams])
+        wall = time.perf_counter() - t0
+    finally:
+        for k, v in env_before.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    work = sum(r[1] for r in res)
+    value = len(streams) * tokens / max(max(r[1] for r in res), 1e-9)
+    rep = {
+        "value": value,
+        "unit": "tokens*heads/s",
+        "cores": len(streams),
+        "kind": "oracle",
+        "sample": (f"{w.name}: first {tokens} tokens of streams 0..{len(streams) - 1}, one "
+                   f"single-threaded fp64 numpy process per stream; {work:.1f} s of CPU work, "
+                   f"{wall:.1f} s wall including process start-up"),
+    }
+    return rep, {r[0]: r[2] for r in res}, tokens
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the VLA streams are independent, so the "
+              "multi-GPU split needs no communication and is not run here (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rls_associative_memory_amd import vla
+    from rls_associative_memory_amd.inputs import get_workload, upload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = get_workload(args.workload)
+    chunk = w.chunk if args.chunk < 0 else args.chunk
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calib_copy_mb > 0:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    t_gen = time.perf_counter()
+    q, k, v, u = upload_inputs(w, dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    shape = tuple(q.shape)
+    path = vla.resolve_path(shape, q.dtype, path=args.path, chunk=chunk)
+    ws_bytes = vla.workspace_size(shape, q.dtype, path=args.path, chunk=chunk)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if ws_bytes else None
+    out = torch.empty_like(q)
+    S = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev) if w.want_state else None
+    A = torch.empty_like(S) if S is not None else None
+
+    def step():
+        vla.forward(q, k, v, u, w.lambda0, eps=w.eps, path=args.path, chunk=chunk, out=out,
+                    S_final=S, A_final=A, workspace=ws)
+
+    print(f"[bench] workload={w.name} path={path} inputs generated in {t_gen:.1f}s; "
+          f"warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ms = max(wall * 1e3 / args.steps, ev_ms)
+    tokens = w.B * w.H * w.T
+    value = tokens / (ms * 1e-3)
+    print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (events {ev_ms:.3f} ms)",
+          file=sys.stderr, flush=True)
+
+    flops = flops_per_token_head(w.d) * tokens
+    kernel_ms = ev_ms  # single-kernel path: the launch is the step
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "alu" if path == "seq" else "mfma",
+        "achieved": round(achieved, 3),
+        "peak": PEAK_FP32_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+        "traffic": None,
+        "kernel": "vla_seq_kernel" if path == "seq" else "vla_chunk",
+        "hbm_frac": round(bytes_per_token_head(w.d, w.elem_bytes) * tokens / (kernel_ms * 1e-3)
+                          / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu, ref, ntok = cpu_baseline(w, args.cpu_tokens, args.cpu_cores)
+        o = out.view(-1, w.T, w.d)
+        worst = 0.0
+        for s, r in ref.items():
+            g = o[s, :ntok].double().cpu().numpy()
+            worst = max(worst, float(np.linalg.norm(g - r) / np.linalg.norm(r)))
+        print(f"[bench] causal parity of the first {ntok} tokens on {len(ref)} streams: "
+              f"worst rel L2 {worst:.3e}", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d,
+            "input_dtype": w.dtype, "state_dtype": "f32", "lambda0": w.lambda0,
+            "path": path, "chunk": chunk if path == "chunk" else 0,
+            "final_state": bool(w.want_state),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

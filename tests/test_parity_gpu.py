@@ -134,3 +134,80 @@ def test_auto_path_runs_and_matches():
     torch.cuda.synchronize()
     if vla.resolve_path(tuple(q.shape), q.dtype) == "seq":
         assert torch.equal(o_auto, o_seq)
+
+
+# ---------------------------------------------------------------------------------------
+# Chunked, time-segment-parallel path
+# ---------------------------------------------------------------------------------------
+
+CHUNK_SMALL = [
+    (d, dt, T, C)
+    for d in (32, 64, 96, 128)
+    for dt in ("f32", "bf16")
+    for T in (1, 37, 300, 700)
+    for C in (16, 32, 64)
+    if not (d == 128 and C == 64)
+]
+
+
+@pytest.mark.parametrize("d,dt,T,C", CHUNK_SMALL)
+def test_chunk_small_shapes(d, dt, T, C):
+    w = get_workload("tiny_t256_d32").resized(name=f"chunk_d{d}_{dt}_T{T}_C{C}", B=1, H=3,
+                                              T=T, d=d, dtype=dt, lambda0=0.7)
+    _say(f"[case] chunk small d={d} dtype={dt} T={T} C={C}")
+    out, S, A = _run(w, "chunk", chunk=C)
+    q, k, v, u = make_inputs(w)
+    refs = [oracle_forward(q[s], k[s], v[s], u[s], w.lambda0, eps=w.eps) for s in range(3)]
+    _check(w, range(3), out, S, A, refs, f"chunk d={d} {dt} T={T} C={C}")
+
+
+@pytest.mark.parametrize("name", ["mqar_t512_d32", "iid_t4096_d64"])
+def test_chunk_workloads_all_streams(name):
+    w = get_workload(name)
+    _say(f"[case] chunk workload {name} (all streams)")
+    out, S, A = _run(w, "chunk")
+    q, k, v, u = make_inputs(w)
+    ro, rS, rA = oracle_forward(q, k, v, u, w.lambda0, eps=w.eps)
+    refs = [(ro[s], rS[s], rA[s]) for s in range(w.streams)]
+    _check(w, range(w.streams), out, S, A, refs, f"chunk {name}")
+
+
+@pytest.mark.parametrize("name", ["crossover_t43008_d128", "long_t131072_d96"])
+def test_chunk_long_workloads_sampled_streams(name):
+    w = get_workload(name)
+    sample = [0, w.streams - 1]
+    _say(f"[case] chunk workload {name} full size, sampled streams {sample}")
+    out, S, A = _run(w, "chunk", chunk=w.chunk)
+    refs = oracle_streams(w, sample)
+    _check(w, range(len(sample)), out.view(-1, w.T, w.d)[sample],
+           S.view(-1, w.d, w.d)[sample], A.view(-1, w.d, w.d)[sample], refs,
+           f"chunk {name} sampled")
+
+
+def test_chunk_deterministic_and_workspace():
+    w = get_workload("long_t131072_d96").resized(name="det_chunk", B=1, H=3, T=5000)
+    q, k, v, u = upload_inputs(w, "cuda")
+    n = vla.workspace_size(tuple(q.shape), q.dtype, path="chunk", chunk=64)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    o1, S1, A1 = vla.forward(q, k, v, u, w.lambda0, path="chunk", chunk=64, return_state=True,
+                             workspace=ws)
+    o2, S2, A2 = vla.forward(q, k, v, u, w.lambda0, path="chunk", chunk=64, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(A1, A2)
+    small = torch.empty(max(n // 2, 16), dtype=torch.uint8, device="cuda")
+    with pytest.raises(vla.VlaError):
+        vla.forward(q, k, v, u, w.lambda0, path="chunk", chunk=64, workspace=small)
+
+
+def test_chunk_zero_key_tokens():
+    w = get_workload("tiny_t256_d32").resized(name="zero_key_chunk", B=1, H=2, T=600, d=64,
+                                              dtype="f32")
+    q, k, v, u = make_inputs(w)
+    k[:, 7] = 0.0
+    k[:, 300] = 0.0
+    u[:, 11] = 0.0
+    dev = [torch.from_numpy(x).view(1, 2, w.T, w.d).cuda() for x in (q, k, v, u)]
+    out, S, A = vla.forward(*dev, w.lambda0, eps=w.eps, path="chunk", chunk=32, return_state=True)
+    torch.cuda.synchronize()
+    refs = [oracle_forward(q[s], k[s], v[s], u[s], w.lambda0, eps=w.eps) for s in range(2)]
+    _check(w, range(2), out, S, A, refs, "chunk zero key / zero u")
