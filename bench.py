@@ -43,6 +43,19 @@ def flops_per_token_head(d: int) -> int:
     return 12 * d * d + 20 * d
 
 
+# Algorithmic flops per token*head of the work each kernel exists to do, and the unit it
+# runs on.  The A side (Sherman-Morrison, gate) and the S side (residual update, readout)
+# are each half of the recurrence; the segment map of the chunked path recomputes the
+# affine map of the S recurrence over 2d state rows (dot + update per row per token).
+KERNEL_WORK = {
+    "vla_seq_kernel": (lambda d: 12 * d * d + 20 * d, "alu"),
+    "k_aside": (lambda d: 6 * d * d + 10 * d, "alu"),
+    "k_swy_final": (lambda d: 6 * d * d + 10 * d, "mfma"),
+    "k_swy_map": (lambda d: 8 * d * d, "mfma"),
+    "k_gram": (lambda d: 2 * d * d, "mfma"),
+}
+
+
 def bytes_per_token_head(d: int, elem: int) -> int:
     return 5 * d * elem  # q, k, v, u read; out written
 
@@ -163,6 +176,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    vla.profile_reset()
+    vla.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -171,6 +186,8 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    vla.profile_enable(False)
+    kernels = vla.profile_read()
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms = max(wall * 1e3 / args.steps, ev_ms)
     tokens = w.B * w.H * w.T
@@ -178,19 +195,28 @@ def main():
     print(f"[bench] {args.steps} steps: {ms:.3f} ms/step (events {ev_ms:.3f} ms)",
           file=sys.stderr, flush=True)
 
-    flops = flops_per_token_head(w.d) * tokens
-    kernel_ms = ev_ms  # single-kernel path: the launch is the step
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    for name, (tot, n) in sorted(kernels.items(), key=lambda kv: -kv[1][0]):
+        print(f"[bench] kernel {name:16s} {tot / max(n, 1):9.3f} ms/launch x {n}",
+              file=sys.stderr, flush=True)
+    dom = max(kernels.items(), key=lambda kv: kv[1][0])
+    dom_name, (dom_total, dom_n) = dom
+    kernel_ms = dom_total / max(dom_n, 1)
+    work_fn, unit = KERNEL_WORK.get(dom_name, (lambda d: 0, "alu"))
+    achieved = work_fn(w.d) * tokens / (kernel_ms * 1e-3) / 1e12
+    path_tflops = flops_per_token_head(w.d) * tokens / (ms * 1e-3) / 1e12
     roofline = {
-        "bound": "alu" if path == "seq" else "mfma",
+        "bound": unit,
         "achieved": round(achieved, 3),
         "peak": PEAK_FP32_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
         "traffic": None,
-        "kernel": "vla_seq_kernel" if path == "seq" else "vla_chunk",
-        "hbm_frac": round(bytes_per_token_head(w.d, w.elem_bytes) * tokens / (kernel_ms * 1e-3)
-                          / 1e9 / PEAK_HBM_GBS, 4),
+        "kernel": dom_name,
+        "kernel_ms": round(kernel_ms, 4),
+        "path_achieved": round(path_tflops, 3),
+        "path_frac": round(path_tflops / PEAK_FP32_TFLOPS, 4),
+        "path_hbm_frac": round(bytes_per_token_head(w.d, w.elem_bytes) * tokens / (ms * 1e-3)
+                               / 1e9 / PEAK_HBM_GBS, 4),
     }
 
     cpu = None

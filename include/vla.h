@@ -101,6 +101,21 @@ vla_status_t vla_resolve_path(const vla_desc_t *desc, int32_t *path);
 /* Static, human-readable name of a status code. */
 const char *vla_status_string(vla_status_t status);
 
+/*
+ * Optional per-kernel timing, for benchmarks.  While enabled, every kernel the library
+ * launches is bracketed by a HIP event pair recorded on the launch stream; the pairs are
+ * resolved (waiting for them) by vla_profile_count / vla_profile_get and accumulated per
+ * kernel name.  Enabling creates events (host allocations); timing adds a few microseconds
+ * of event records per launch.  Not thread-safe against concurrent vla_forward calls.
+ */
+vla_status_t vla_profile_enable(int32_t enable);   /* 1 = record, 0 = stop recording     */
+vla_status_t vla_profile_reset(void);               /* drop all recorded timings          */
+int32_t vla_profile_count(void);                    /* kernels with timings (waits on GPU) */
+/* Name (NUL-terminated, truncated to name_cap), summed milliseconds and launch count of
+ * the index-th timed kernel; VLA_ERROR_INVALID_VALUE for an index out of range. */
+vla_status_t vla_profile_get(int32_t index, char *name, size_t name_cap, double *total_ms,
+                             int64_t *launches);
+
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
 int32_t vla_version(void);
 

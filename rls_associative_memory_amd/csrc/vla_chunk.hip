@@ -755,26 +755,26 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
   const unsigned S = static_cast<unsigned>(pl.S), P = static_cast<unsigned>(pl.P);
 
   if (P > 1) {
-    hipLaunchKernelGGL((k_gram<D, TIn>), dim3(S, P - 1), dim3(256), 0, st, uu, kk, Mw, nkw,
+    VLA_LAUNCH("k_gram", (k_gram<D, TIn>), dim3(S, P - 1), dim3(256), 0, st, uu, kk, Mw, nkw,
                        pl.T, pl.L, pl.P);
   }
-  hipLaunchKernelGGL((k_prefix<D>), dim3(S, (D * D + 255) / 256), dim3(256), 0, st, Mw, nkw,
+  VLA_LAUNCH("k_prefix", (k_prefix<D>), dim3(S, (D * D + 255) / 256), dim3(256), 0, st, Mw, nkw,
                      pl.P, pr.lambda0);
-  hipLaunchKernelGGL((k_inv<D>), dim3(S, P), dim3(256), 0, st, Mw, pl.P);
+  VLA_LAUNCH("k_inv", (k_inv<D>), dim3(S, P), dim3(256), 0, st, Mw, pl.P);
   {
     using AC = AsideCfg<D>;
     const int64_t units = pl.S * pl.P;
     const unsigned blocks = static_cast<unsigned>((units + AC::UPB - 1) / AC::UPB);
-    hipLaunchKernelGGL((k_aside<D, TIn>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
+    VLA_LAUNCH("k_aside", (k_aside<D, TIn>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
                        nkw, alw, rdw, A_final, pl.S, pl.T, pl.L, pl.P, pr.eps);
   }
   if (P > 1) {
-    hipLaunchKernelGGL((k_swy<D, CH, false, TIn>), dim3(S, P - 1),
+    VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1),
                        dim3(SwyCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw,
                        oo, S_final, pl.T, pl.L, pl.P);
   }
-  hipLaunchKernelGGL((k_sprefix<D>), dim3(S, D / 16), dim3(64), 0, st, pbw, s0w, pl.P);
-  hipLaunchKernelGGL((k_swy<D, CH, true, TIn>), dim3(S, P), dim3(SwyCfg<D, CH, true>::NT), 0,
+  VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(64), 0, st, pbw, s0w, pl.P);
+  VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P), dim3(SwyCfg<D, CH, true>::NT), 0,
                      st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
   return hipGetLastError();
 }

@@ -31,4 +31,26 @@ hipError_t launch_chunk(const Problem &p, int chunk, const void *q, const void *
                         const void *v, const void *u, void *out, float *S_final,
                         float *A_final, void *ws, hipStream_t stream);
 
+// Event-pair timing of one kernel launch when vla_profile_enable(1) is in effect.
+class ProfScope {
+ public:
+  ProfScope(const char *name, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope &) = delete;
+  ProfScope &operator=(const ProfScope &) = delete;
+
+ private:
+  const char *name_;
+  hipStream_t stream_;
+  hipEvent_t ev0_ = nullptr, ev1_ = nullptr;
+  bool active_ = false;
+};
+
 }  // namespace vla
+
+// Launch a kernel, timed under `name` when profiling is enabled.
+#define VLA_LAUNCH(name, kernel, grid, block, shmem, stream, ...)               \
+  do {                                                                          \
+    ::vla::ProfScope vla_prof_scope_(name, stream);                             \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);        \
+  } while (0)

@@ -365,7 +365,7 @@ static hipError_t launch_seq_t(const Problem &p, const void *q, const void *k, c
                                const void *u, void *out, float *S_final, float *A_final,
                                hipStream_t stream) {
   using C = SeqCfg<D>;
-  hipLaunchKernelGGL((vla_seq_kernel<D, TIn>), dim3(static_cast<unsigned>(p.streams)),
+  VLA_LAUNCH("vla_seq_kernel", (vla_seq_kernel<D, TIn>), dim3(static_cast<unsigned>(p.streams)),
                      dim3(C::NT), 0, stream, static_cast<const TIn *>(q),
                      static_cast<const TIn *>(k), static_cast<const TIn *>(v),
                      static_cast<const TIn *>(u), static_cast<TIn *>(out), S_final, A_final,

@@ -16,6 +16,7 @@ from typing import Optional
 import torch
 
 __all__ = ["forward", "workspace_size", "resolve_path", "library_path", "load_library",
+           "profile_enable", "profile_reset", "profile_read",
            "VlaError", "exported_symbols", "STATUS", "PATHS", "DTYPES", "VlaDesc"]
 
 STATUS = {
@@ -80,6 +81,16 @@ def load_library():
         lib.vla_status_string.restype = ctypes.c_char_p
         lib.vla_version.argtypes = []
         lib.vla_version.restype = ctypes.c_int32
+        lib.vla_profile_enable.argtypes = [ctypes.c_int32]
+        lib.vla_profile_enable.restype = ctypes.c_int
+        lib.vla_profile_reset.argtypes = []
+        lib.vla_profile_reset.restype = ctypes.c_int
+        lib.vla_profile_count.argtypes = []
+        lib.vla_profile_count.restype = ctypes.c_int32
+        lib.vla_profile_get.argtypes = [ctypes.c_int32, ctypes.c_char_p, ctypes.c_size_t,
+                                        ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64)]
+        lib.vla_profile_get.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -179,3 +190,27 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
     if S_final is not None or A_final is not None:
         return out, S_final, A_final
     return out
+
+
+def profile_enable(on: bool = True) -> None:
+    """Record a HIP event pair around every kernel the library launches (see vla.h)."""
+    _check(load_library().vla_profile_enable(1 if on else 0), "vla_profile_enable")
+
+
+def profile_reset() -> None:
+    _check(load_library().vla_profile_reset(), "vla_profile_reset")
+
+
+def profile_read() -> dict:
+    """{kernel name: (total milliseconds, launches)}; waits for the recorded events."""
+    lib = load_library()
+    n = lib.vla_profile_count()
+    res = {}
+    buf = ctypes.create_string_buffer(128)
+    for i in range(n):
+        ms = ctypes.c_double(0)
+        cnt = ctypes.c_int64(0)
+        _check(lib.vla_profile_get(i, buf, 128, ctypes.byref(ms), ctypes.byref(cnt)),
+               "vla_profile_get")
+        res[buf.value.decode()] = (ms.value, cnt.value)
+    return res
