@@ -110,7 +110,26 @@ __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, int64_t i, float x
 
 // ------------------------------------------------------------------------------------
 // k_gram: Gram_p = sum_{t in segment p} u_t u_t^T, nk_p = sum phi(k_t)   (segments 0..P-2)
+// bf16 inputs: v_mfma_f32_16x16x32_bf16 on the raw inputs (every product exact in fp32);
+// fp32 inputs: v_mfma_f32_16x16x4_f32.  Tokens are staged 64 at a time, transposed and
+// packed so each lane's MFMA operand is one 16-byte LDS read; the next block's 16-byte
+// global loads are issued before the current block is multiplied.
 // ------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+template <typename TIn>
+struct GramLds;
+template <>
+struct GramLds<bf16_t> {  // [f][token] bf16, rows padded to 72 tokens
+  static constexpr int LT = 72;
+  using elem = uint16_t;
+};
+template <>
+struct GramLds<float> {   // [token/4][f][token%4] fp32
+  static constexpr int LT = 0;
+  using elem = float;
+};
+
 template <int D, typename TIn>
 __global__ void __launch_bounds__(256)
 k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__ M,
@@ -119,8 +138,15 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
   constexpr int NTILE = NT16 * (NT16 + 1) / 2;
   constexpr int TPW = (NTILE + 3) / 4;
   constexpr int TB = 64;
-  constexpr int LDU = D + 4;
-  __shared__ float sU[TB][LDU];
+  constexpr bool BF = sizeof(TIn) == 2;
+  using IO = io<TIn>;
+  using vec_t = typename IO::vec_t;
+  constexpr int VW = IO::kVec;
+  constexpr int UB = TB * D / VW;      // vectors per array per block
+  constexpr int PU = UB / 256;         // per thread (exact for every supported D)
+  static_assert(UB % 256 == 0, "block staging must tile the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t sUb[BF ? D : 1][BF ? GramLds<bf16_t>::LT : 1];
+  __shared__ __attribute__((aligned(16))) float sUf[BF ? 1 : TB / 4][BF ? 1 : D + 1][4];
 
   const int64_t s = blockIdx.x;
   const int64_t p = blockIdx.y;
@@ -140,29 +166,76 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
   f4_t acc[TPW];
 #pragma unroll
   for (int m = 0; m < TPW; ++m) acc[m] = f4_zero();
-  float nka = 0.f;
-
+  // Unit ui = tid + 256 i covers token ui % 64 and features (ui / 64) * VW .. + VW.
+  float nka[PU][VW];
+#pragma unroll
+  for (int i = 0; i < PU; ++i)
+#pragma unroll
+    for (int e = 0; e < VW; ++e) nka[i][e] = 0.f;
+  vec_t pu[PU], pk[PU];
+  auto prefetch = [&](int64_t t0) {
+    const int nt = static_cast<int>(std::min<int64_t>(TB, te - t0));
+#pragma unroll
+    for (int i = 0; i < PU; ++i) {
+      const int ui = tid + 256 * i;
+      const int c = ui % TB, f0 = (ui / TB) * VW;
+      const bool ok = c < nt;
+      pu[i] = ok ? *reinterpret_cast<const vec_t *>(us + (t0 + c) * D + f0) : vec_t{};
+      pk[i] = ok ? *reinterpret_cast<const vec_t *>(ks + (t0 + c) * D + f0) : vec_t{};
+    }
+  };
+  prefetch(tb);
   for (int64_t t0 = tb; t0 < te; t0 += TB) {
     const int nt = static_cast<int>(std::min<int64_t>(TB, te - t0));
     __syncthreads();
-    for (int e = tid; e < TB * D; e += 256) {
-      const int j = e / D, c = e % D;
-      sU[j][c] = j < nt ? load_elem(us, (t0 + j) * D + c) : 0.f;
+#pragma unroll
+    for (int i = 0; i < PU; ++i) {
+      const int ui = tid + 256 * i;
+      const int c = ui % TB, f0 = (ui / TB) * VW;
+      if constexpr (BF) {
+        const uint32_t w[4] = {pu[i].x, pu[i].y, pu[i].z, pu[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sUb[f0 + 2 * e][c] = static_cast<uint16_t>(w[e] & 0xffffu);
+          sUb[f0 + 2 * e + 1][c] = static_cast<uint16_t>(w[e] >> 16);
+        }
+      } else {
+        float x[VW];
+        IO::unpack(pu[i], x);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) sUf[c / 4][f0 + e][c % 4] = x[e];
+      }
+      float kx[VW];
+      IO::unpack(pk[i], kx);
+      if (c < nt)
+#pragma unroll
+        for (int e = 0; e < VW; ++e) nka[i][e] += phi(kx[e]);
     }
-    if (tid < D)
-      for (int j = 0; j < nt; ++j) nka += phi(load_elem(ks, (t0 + j) * D + tid));
     __syncthreads();
+    if (t0 + TB < te) prefetch(t0 + TB);
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
       if (wave + 4 * m < NTILE) {
-        const int ci = 16 * ti_i[m] + li, cj = 16 * ti_j[m] + li;
+        const int fi = 16 * ti_i[m] + li, fj = 16 * ti_j[m] + li;
+        if constexpr (BF) {
 #pragma unroll
-        for (int kt = 0; kt < TB / 16; ++kt)
-#pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            const int tok = 16 * kt + 4 * gq + st;
-            acc[m] = mfma_f32_16x16x4(sU[tok][ci], sU[tok][cj], acc[m]);
+          for (int kk = 0; kk < TB / 32; ++kk) {
+            const uint4 a = *reinterpret_cast<const uint4 *>(&sUb[fi][32 * kk + 8 * gq]);
+            const uint4 b = *reinterpret_cast<const uint4 *>(&sUb[fj][32 * kk + 8 * gq]);
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                             __builtin_bit_cast(bf16x8_t, b), acc[m], 0, 0, 0);
           }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < TB / 16; ++kt) {
+            const float4 a = *reinterpret_cast<const float4 *>(&sUf[4 * kt + gq][fi][0]);
+            const float4 b = *reinterpret_cast<const float4 *>(&sUf[4 * kt + gq][fj][0]);
+            acc[m] = mfma_f32_16x16x4(a.x, b.x, acc[m]);
+            acc[m] = mfma_f32_16x16x4(a.y, b.y, acc[m]);
+            acc[m] = mfma_f32_16x16x4(a.z, b.z, acc[m]);
+            acc[m] = mfma_f32_16x16x4(a.w, b.w, acc[m]);
+          }
+        }
       }
     }
   }
@@ -179,7 +252,16 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
       }
     }
   }
-  if (tid < D) nk[(s * P + p) * D + tid] = nka;
+  // phi(k) sums: lanes of a wave share the feature block and differ in the token.
+#pragma unroll
+  for (int i = 0; i < PU; ++i) {
+    const int f0 = ((tid + 256 * i) / TB) * VW;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) {
+      const float tot = wave_sum(nka[i][e]);
+      if (lane == 0) nk[(s * P + p) * D + f0 + e] = tot;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -212,39 +294,52 @@ k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0
 }
 
 // ------------------------------------------------------------------------------------
-// k_inv: M_p <- M_p^{-1} in place (Gauss-Jordan without pivoting; M_p is SPD), symmetrised
+// k_inv: M_p <- M_p^{-1} in place (Gauss-Jordan without pivoting; M_p is SPD), symmetrised.
+// Each thread keeps D*D/256 elements in registers; per elimination step only the pivot row
+// and column go through LDS (parity double-buffered, one barrier per step).
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) k_inv(float *__restrict__ M, int64_t P) {
-  __shared__ float a[D][D + 1];
-  __shared__ float rowk[D], colk[D];
+  constexpr int NE = D * D / 256;
+  static_assert(D * D % 256 == 0, "elements must tile the threads");
+  __shared__ float rowk[2][D], colk[2][D];
+  __shared__ float sym[D][D + 1];
   const int64_t s = blockIdx.x, p = blockIdx.y;
   const int tid = threadIdx.x;
   float *base = M + (s * P + p) * D * D;
-  for (int e = tid; e < D * D; e += 256) a[e / D][e % D] = base[e];
+  float a[NE];
+  int ei[NE], ej[NE];
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int e = tid + 256 * m;
+    ei[m] = e / D;
+    ej[m] = e % D;
+    a[m] = base[e];
+  }
   for (int kk = 0; kk < D; ++kk) {
-    __syncthreads();
-    if (tid < D) {
-      rowk[tid] = a[kk][tid];
-      colk[tid] = a[tid][kk];
+    const int b = kk & 1;
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+      if (ei[m] == kk) rowk[b][ej[m]] = a[m];
+      if (ej[m] == kk) colk[b][ei[m]] = a[m];
     }
     __syncthreads();
-    const float piv = 1.0f / rowk[kk];
-    for (int e = tid; e < D * D; e += 256) {
-      const int i = e / D, j = e % D;
-      if (i == kk)
-        a[i][j] = (j == kk) ? piv : rowk[j] * piv;
-      else if (j == kk)
-        a[i][j] = -colk[i] * piv;
+    const float piv = 1.0f / rowk[b][kk];
+#pragma unroll
+    for (int m = 0; m < NE; ++m) {
+      if (ei[m] == kk)
+        a[m] = (ej[m] == kk) ? piv : a[m] * piv;
+      else if (ej[m] == kk)
+        a[m] = -a[m] * piv;
       else
-        a[i][j] = fmaf(-colk[i] * piv, rowk[j], a[i][j]);
+        a[m] = fmaf(-colk[b][ei[m]] * piv, rowk[b][ej[m]], a[m]);
     }
   }
+#pragma unroll
+  for (int m = 0; m < NE; ++m) sym[ei[m]][ej[m]] = a[m];
   __syncthreads();
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    base[e] = 0.5f * (a[i][j] + a[j][i]);
-  }
+#pragma unroll
+  for (int m = 0; m < NE; ++m) base[tid + 256 * m] = 0.5f * (a[m] + sym[ej[m]][ei[m]]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -261,7 +356,7 @@ struct AsideCfg {
   static constexpr int HALF = LA / 2;
   static constexpr int CW = D / 2;
   static constexpr int RPL = D / HALF;
-  static constexpr int CT = 16;
+  static constexpr int RING = 4;                // tokens in flight in registers
   static constexpr int NF = (D + LA - 1) / LA;  // normaliser features per lane
 };
 
@@ -283,12 +378,17 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
         float *__restrict__ rkden, float *__restrict__ A_final, int64_t S, int64_t T,
         int64_t L, int64_t P, float eps) {
   using C = AsideCfg<D>;
-  __shared__ __attribute__((aligned(16))) float sU[C::UPB][C::CT][D];
-  __shared__ __attribute__((aligned(16))) float sK[C::UPB][C::CT][D];
-  __shared__ __attribute__((aligned(16))) float sQ[C::UPB][C::CT][D];  // phi(q)
+  using IO = io<TIn>;
+  using vec_t = typename IO::vec_t;
+  constexpr int VW = IO::kVec;
+  constexpr int VPA = D / VW;                    // vectors per array per token
+  constexpr int NV = 3 * VPA;                    // u, k, q vectors per token
+  constexpr int PV = (NV + C::LA - 1) / C::LA;   // vectors per lane per token
+  __shared__ __attribute__((aligned(16))) float sU[C::UPB][2][D];
+  __shared__ __attribute__((aligned(16))) float sK[C::UPB][2][D];
+  __shared__ __attribute__((aligned(16))) float sQ[C::UPB][2][D];  // phi(q)
   __shared__ __attribute__((aligned(16))) float sW[C::UPB][D];
-  __shared__ float sRed[2][C::NWA][2];
-  __shared__ float sDen[C::NWA][C::CT];
+  __shared__ float sRed[2][C::NWA][3];
 
   const int tid = threadIdx.x;
   const int unit_in_blk = tid / C::LA;
@@ -299,14 +399,9 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
   const int h = lu & 1, g = lu >> 1, c0 = h * C::CW;
   const int wside = lu / kWave;
   const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
-  const TIn *qs = q + s * T * D;
-  const TIn *ks = k + s * T * D;
-  const TIn *us = u + s * T * D;
+  const TIn *base_in[3] = {u + s * T * D, k + s * T * D, q + s * T * D};
   float *al = alpha + s * T * D;
   float *rd = rkden + s * T * 2;
-  float(*U)[D] = sU[unit_in_blk];
-  float(*K)[D] = sK[unit_in_blk];
-  float(*Q)[D] = sQ[unit_in_blk];
   float *W = sW[unit_in_blk];
 
   float Mr[C::RPL][C::CW];
@@ -327,144 +422,163 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
     nrun[f] = feat < D ? nk0[(s * P + p) * D + feat] : 0.f;
   }
 
-  for (int64_t t0 = tb; t0 < te; t0 += C::CT) {
-    const int nt = static_cast<int>(std::min<int64_t>(C::CT, te - t0));
-    unit_sync<C::NWA>();
-    for (int e = lu; e < C::CT * D; e += C::LA) {
-      const int j = e / D, c = e % D;
-      const bool ok = j < nt;
-      U[j][c] = ok ? load_elem(us, (t0 + j) * D + c) : 0.f;
-      K[j][c] = ok ? load_elem(ks, (t0 + j) * D + c) : 0.f;
-      Q[j][c] = ok ? phi(load_elem(qs, (t0 + j) * D + c)) : 0.f;
+  // Ring of RING tokens in flight: ring[i % RING] holds token tb + i's raw vectors.
+  vec_t ring[C::RING][PV];
+  auto fetch = [&](int64_t t, vec_t *dst) {
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+      const int vi = lu + i * C::LA;
+      const bool ok = vi < NV && t < te;
+      const int arr = vi / VPA, f0 = (vi % VPA) * VW;
+      dst[i] = ok ? *reinterpret_cast<const vec_t *>(base_in[arr < 3 ? arr : 0] + t * D + f0) : vec_t{};
     }
-    unit_sync<C::NWA>();
-    // Readout denominators of the tile: n_t = n_{t-1} + phi(k_t), den_t = n_t . phi(q_t) + eps.
+  };
+#pragma unroll
+  for (int i = 0; i < C::RING; ++i) fetch(tb + i, ring[i]);
+
+  for (int64_t t = tb; t < te; ++t) {
+    const int j = static_cast<int>(t - tb);
+    const int slot = j & 1;
+    float *U = sU[unit_in_blk][slot];
+    float *K = sK[unit_in_blk][slot];
+    float *Q = sQ[unit_in_blk][slot];
+    // (a) token t from the ring into LDS (fp32; phi applied to q).
     {
-      float part[C::CT];
+      vec_t cur[PV];
 #pragma unroll
-      for (int j = 0; j < C::CT; ++j) {
-        part[j] = 0.f;
-        if (j < nt) {
+      for (int r = 0; r < C::RING; ++r)
+        if ((j % C::RING) == r)
 #pragma unroll
-          for (int f = 0; f < C::NF; ++f) {
-            const int feat = lu + f * C::LA;
-            if (feat < D) {
-              nrun[f] += phi(K[j][feat]);
-              part[j] = fmaf(nrun[f], Q[j][feat], part[j]);
-            }
-          }
+          for (int i = 0; i < PV; ++i) cur[i] = ring[r][i];
+#pragma unroll
+      for (int i = 0; i < PV; ++i) {
+        const int vi = lu + i * C::LA;
+        if (vi < NV) {
+          const int arr = vi / VPA, f0 = (vi % VPA) * VW;
+          float x[VW];
+          IO::unpack(cur[i], x);
+          float *dst = arr == 0 ? U : (arr == 1 ? K : Q);
+          if (arr == 2)
+#pragma unroll
+            for (int e = 0; e < VW; ++e) x[e] = phi(x[e]);
+#pragma unroll
+          for (int e = 0; e < VW; e += 4)
+            *reinterpret_cast<float4 *>(&dst[f0 + e]) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
         }
       }
+      // (b) refill this ring slot with token t + RING.
+      vec_t nxt[PV];
+      fetch(t + C::RING, nxt);
 #pragma unroll
-      for (int j = 0; j < C::CT; ++j) part[j] = wave_sum(part[j]);
-      if constexpr (C::NWA > 1) {
-        if ((lu & (kWave - 1)) == 0)
+      for (int r = 0; r < C::RING; ++r)
+        if ((j % C::RING) == r)
 #pragma unroll
-          for (int j = 0; j < C::CT; ++j) sDen[wside][j] = part[j];
-        __syncthreads();
-        if (lu == 0)
-          for (int j = 0; j < nt; ++j) {
-            float dsum = 0.f;
+          for (int i = 0; i < PV; ++i) ring[r][i] = nxt[i];
+    }
+    unit_sync<C::NWA>();
+    // (c) readout normaliser n_t = n_{t-1} + phi(k_t); partial of n_t . phi(q_t).
+    float dp = 0.f;
 #pragma unroll
-            for (int w = 0; w < C::NWA; ++w) dsum += sDen[w][j];
-            rd[(t0 + j) * 2 + 1] = dsum + eps;
-          }
-      } else {
-        if (lu == 0)
-          for (int j = 0; j < nt; ++j) rd[(t0 + j) * 2 + 1] = part[j] + eps;
+    for (int f = 0; f < C::NF; ++f) {
+      const int feat = lu + f * C::LA;
+      if (feat < D) {
+        nrun[f] += phi(K[feat]);
+        dp = fmaf(nrun[f], Q[feat], dp);
       }
     }
-    // Sherman-Morrison token by token.
-    for (int j = 0; j < nt; ++j) {
-      float z[C::RPL], a[C::RPL];
+    // (d) Sherman-Morrison step.
+    float z[C::RPL], a[C::RPL];
 #pragma unroll
-      for (int r = 0; r < C::RPL; ++r) { z[r] = 0.f; a[r] = 0.f; }
-      float kk = 0.f;
+    for (int r = 0; r < C::RPL; ++r) { z[r] = 0.f; a[r] = 0.f; }
+    float kk = 0.f;
 #pragma unroll
-      for (int m = 0; m < C::CW / 4; ++m) {
-        const float4 u4 = *reinterpret_cast<const float4 *>(&U[j][c0 + 4 * m]);
-        const float4 k4 = *reinterpret_cast<const float4 *>(&K[j][c0 + 4 * m]);
-        kk = fmaf(k4.x, k4.x, kk); kk = fmaf(k4.y, k4.y, kk);
-        kk = fmaf(k4.z, k4.z, kk); kk = fmaf(k4.w, k4.w, kk);
-#pragma unroll
-        for (int r = 0; r < C::RPL; ++r) {
-          z[r] = fmaf(Mr[r][4 * m + 0], u4.x, z[r]);
-          a[r] = fmaf(Mr[r][4 * m + 0], k4.x, a[r]);
-          z[r] = fmaf(Mr[r][4 * m + 1], u4.y, z[r]);
-          a[r] = fmaf(Mr[r][4 * m + 1], k4.y, a[r]);
-          z[r] = fmaf(Mr[r][4 * m + 2], u4.z, z[r]);
-          a[r] = fmaf(Mr[r][4 * m + 2], k4.z, a[r]);
-          z[r] = fmaf(Mr[r][4 * m + 3], u4.w, z[r]);
-          a[r] = fmaf(Mr[r][4 * m + 3], k4.w, a[r]);
-        }
-      }
-      kk = pair_sum(kk);
-      const float rk = kk > 0.f ? rsqrtf(kk) : 0.f;
-      float sd = 0.f, sg = 0.f;
+    for (int m = 0; m < C::CW / 4; ++m) {
+      const float4 u4 = *reinterpret_cast<const float4 *>(&U[c0 + 4 * m]);
+      const float4 k4 = *reinterpret_cast<const float4 *>(&K[c0 + 4 * m]);
+      kk = fmaf(k4.x, k4.x, kk); kk = fmaf(k4.y, k4.y, kk);
+      kk = fmaf(k4.z, k4.z, kk); kk = fmaf(k4.w, k4.w, kk);
 #pragma unroll
       for (int r = 0; r < C::RPL; ++r) {
-        const int row = g + r * C::HALF;
-        z[r] = pair_sum(z[r]);
-        a[r] = pair_sum(a[r]) * rk;
-        sd = fmaf(U[j][row], z[r], sd);
-        sg = fmaf(K[j][row] * rk, z[r], sg);
+        z[r] = fmaf(Mr[r][4 * m + 0], u4.x, z[r]);
+        a[r] = fmaf(Mr[r][4 * m + 0], k4.x, a[r]);
+        z[r] = fmaf(Mr[r][4 * m + 1], u4.y, z[r]);
+        a[r] = fmaf(Mr[r][4 * m + 1], k4.y, a[r]);
+        z[r] = fmaf(Mr[r][4 * m + 2], u4.z, z[r]);
+        a[r] = fmaf(Mr[r][4 * m + 2], k4.z, a[r]);
+        z[r] = fmaf(Mr[r][4 * m + 3], u4.w, z[r]);
+        a[r] = fmaf(Mr[r][4 * m + 3], k4.w, a[r]);
       }
-      if (h) { sd = 0.f; sg = 0.f; }
-      sd = wave_sum(sd);
-      sg = wave_sum(sg);
-      if constexpr (C::NWA > 1) {
-        if ((lu & (kWave - 1)) == 0) { sRed[0][wside][0] = sd; sRed[0][wside][1] = sg; }
-        __syncthreads();
-        sd = 0.f; sg = 0.f;
-#pragma unroll
-        for (int w = 0; w < C::NWA; ++w) { sd += sRed[0][w][0]; sg += sRed[0][w][1]; }
-      }
-      const float delta = 1.0f + sd;
-      const float cz = sg / delta;
-      float y[C::RPL];
-      float sy = 0.f;
-#pragma unroll
-      for (int r = 0; r < C::RPL; ++r) {
-        y[r] = fmaf(-cz, z[r], a[r]);
-        sy = fmaf(y[r], y[r], sy);
-      }
-      if (h) sy = 0.f;
-      sy = wave_sum(sy);
-      if constexpr (C::NWA > 1) {
-        if ((lu & (kWave - 1)) == 0) sRed[1][wside][0] = sy;
-        __syncthreads();
-        sy = 0.f;
-#pragma unroll
-        for (int w = 0; w < C::NWA; ++w) sy += sRed[1][w][0];
-      }
-      const float inv = sy > 0.f ? rsqrtf(sy) : 0.f;
-      const float rdl = rsqrtf(delta);
-      const int64_t t = t0 + j;
-      float w[C::RPL];
-#pragma unroll
-      for (int r = 0; r < C::RPL; ++r) {
-        const int row = g + r * C::HALF;
-        w[r] = z[r] * rdl;
-        if (h == 0) {
-          W[row] = w[r];
-          al[t * D + row] = y[r] * inv;
-        }
-      }
-      if (lu == 0) rd[t * 2] = rk;
-      unit_sync<C::NWA>();
-#pragma unroll
-      for (int m = 0; m < C::CW / 4; ++m) {
-        const float4 w4 = *reinterpret_cast<const float4 *>(&W[c0 + 4 * m]);
-#pragma unroll
-        for (int r = 0; r < C::RPL; ++r) {
-          Mr[r][4 * m + 0] = fmaf(-w[r], w4.x, Mr[r][4 * m + 0]);
-          Mr[r][4 * m + 1] = fmaf(-w[r], w4.y, Mr[r][4 * m + 1]);
-          Mr[r][4 * m + 2] = fmaf(-w[r], w4.z, Mr[r][4 * m + 2]);
-          Mr[r][4 * m + 3] = fmaf(-w[r], w4.w, Mr[r][4 * m + 3]);
-        }
-      }
-      if constexpr (C::NWA > 1) __syncthreads();  // W is rewritten by the next token
     }
+    kk = pair_sum(kk);
+    const float rk = kk > 0.f ? rsqrtf(kk) : 0.f;
+    float sd = 0.f, sg = 0.f;
+#pragma unroll
+    for (int r = 0; r < C::RPL; ++r) {
+      const int row = g + r * C::HALF;
+      z[r] = pair_sum(z[r]);
+      a[r] = pair_sum(a[r]) * rk;
+      sd = fmaf(U[row], z[r], sd);
+      sg = fmaf(K[row] * rk, z[r], sg);
+    }
+    if (h) { sd = 0.f; sg = 0.f; }
+    sd = wave_sum(sd);
+    sg = wave_sum(sg);
+    dp = wave_sum(dp);
+    if constexpr (C::NWA > 1) {
+      if ((lu & (kWave - 1)) == 0) {
+        sRed[0][wside][0] = sd; sRed[0][wside][1] = sg; sRed[0][wside][2] = dp;
+      }
+      __syncthreads();
+      sd = 0.f; sg = 0.f; dp = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::NWA; ++w) {
+        sd += sRed[0][w][0]; sg += sRed[0][w][1]; dp += sRed[0][w][2];
+      }
+    }
+    const float delta = 1.0f + sd;
+    const float cz = sg / delta;
+    float y[C::RPL];
+    float sy = 0.f;
+#pragma unroll
+    for (int r = 0; r < C::RPL; ++r) {
+      y[r] = fmaf(-cz, z[r], a[r]);
+      sy = fmaf(y[r], y[r], sy);
+    }
+    if (h) sy = 0.f;
+    sy = wave_sum(sy);
+    if constexpr (C::NWA > 1) {
+      if ((lu & (kWave - 1)) == 0) sRed[1][wside][0] = sy;
+      __syncthreads();
+      sy = 0.f;
+#pragma unroll
+      for (int w = 0; w < C::NWA; ++w) sy += sRed[1][w][0];
+    }
+    const float inv = sy > 0.f ? rsqrtf(sy) : 0.f;
+    const float rdl = rsqrtf(delta);
+    float w[C::RPL];
+#pragma unroll
+    for (int r = 0; r < C::RPL; ++r) {
+      const int row = g + r * C::HALF;
+      w[r] = z[r] * rdl;
+      if (h == 0) {
+        W[row] = w[r];
+        al[t * D + row] = y[r] * inv;
+      }
+    }
+    if (lu == 0) *reinterpret_cast<float2 *>(&rd[t * 2]) = make_float2(rk, dp + eps);
+    unit_sync<C::NWA>();
+#pragma unroll
+    for (int m = 0; m < C::CW / 4; ++m) {
+      const float4 w4 = *reinterpret_cast<const float4 *>(&W[c0 + 4 * m]);
+#pragma unroll
+      for (int r = 0; r < C::RPL; ++r) {
+        Mr[r][4 * m + 0] = fmaf(-w[r], w4.x, Mr[r][4 * m + 0]);
+        Mr[r][4 * m + 1] = fmaf(-w[r], w4.y, Mr[r][4 * m + 1]);
+        Mr[r][4 * m + 2] = fmaf(-w[r], w4.z, Mr[r][4 * m + 2]);
+        Mr[r][4 * m + 3] = fmaf(-w[r], w4.w, Mr[r][4 * m + 3]);
+      }
+    }
+    if constexpr (C::NWA > 1) __syncthreads();  // W and the LDS slots are rewritten next
   }
   if (A_final != nullptr && p == P - 1) {
     float *dst = A_final + s * D * D;
@@ -482,20 +596,26 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
 // ------------------------------------------------------------------------------------
 // k_swy: the S recurrence of one segment in WY form, one 16-row slice of the state per wave.
 //   FINAL: state S (d rows) from the true segment start; writes outputs and S_T.
-//   MAP:   state [Pi; B] (2d rows) from [I; 0]; writes the segment map.
+//   MAP:   state Pi (blockIdx.z = 0, from I, no values) or B (blockIdx.z = 1, from 0 with
+//          the values v); writes the segment map.
 // The state is held transposed (X^T, d x 16 per wave) in MFMA accumulators.
+//
+// LDS operands are packed "k-minor": element (k, i) of an MFMA operand lives at
+// [k / 4][i][k % 4], so the four k-steps a lane feeds in one 16-slice are one float4.
 // ------------------------------------------------------------------------------------
 template <int D, int CH, bool FINAL>
 struct SwyCfg {
-  static constexpr int ROWS = FINAL ? D : 2 * D;
-  static constexpr int NWV = ROWS / 16;
+  static constexpr int NWV = D / 16;    // waves = 16-row state slices per workgroup
   static constexpr int NT = NWV * kWave;
   static constexpr int NCT = CH / 16;   // 16-token tiles per chunk
   static constexpr int NFT = D / 16;    // 16-feature tiles
   static constexpr int NKT = NCT * (NCT + 1) / 2;
-  static constexpr int LC = CH + 4;     // row stride of [feature][token] arrays
-  static constexpr int LD = D + 4;      // row stride of [token][feature] arrays
+  static constexpr int DP = D + 1;      // padded feature count of the token-packed ahat
 };
+
+__device__ __forceinline__ float4 lds4(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
 
 template <int D, int CH, bool FINAL, typename TIn>
 __global__ void __launch_bounds__((SwyCfg<D, CH, FINAL>::NT))
@@ -504,13 +624,16 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
       const float *__restrict__ s0, float *__restrict__ pib, TIn *__restrict__ out,
       float *__restrict__ S_final, int64_t T, int64_t L, int64_t P) {
   using C = SwyCfg<D, CH, FINAL>;
-  __shared__ float KhT[D][C::LC];                 // khat^T
-  __shared__ float AlT[D][C::LC];                 // ahat^T
-  __shared__ float FqT[FINAL ? D : 1][C::LC];     // phi(q)^T
-  __shared__ float Al[CH][C::LD];                 // ahat
-  __shared__ float KaT[CH][C::LC];                // (strict lower of Kh ahat^T)^T
-  __shared__ float QaT[FINAL ? CH : 1][C::LC];    // (lower of Fq ahat^T)^T
-  __shared__ float InvT[C::NCT][16][20];          // diagonal-block inverses, transposed
+  // [f/4][c][f%4]: khat, phi(q), ahat packed by feature; [c/4][f][c%4]: ahat packed by token.
+  __shared__ __attribute__((aligned(16))) float KhP[D / 4][CH][4];
+  __shared__ __attribute__((aligned(16))) float AlP[D / 4][CH][4];
+  __shared__ __attribute__((aligned(16))) float FqP[FINAL ? D / 4 : 1][CH][4];
+  __shared__ __attribute__((aligned(16))) float AcP[CH / 4][C::DP][4];
+  // [c''/4][c][c''%4]: strict-lower (Kh ahat^T) and lower (Fq ahat^T), packed by column.
+  __shared__ __attribute__((aligned(16))) float KaP[CH / 4][CH][4];
+  __shared__ __attribute__((aligned(16))) float QaP[FINAL ? CH / 4 : 1][CH][4];
+  // Inverses of the unit-lower diagonal 16-blocks of I + Ka: [b][k/4][i][k%4].
+  __shared__ __attribute__((aligned(16))) float InvP[C::NCT][4][16][4];
   __shared__ float sDen[CH];
 
   const int64_t s = blockIdx.x, p = blockIdx.y;
@@ -522,9 +645,8 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
   const float *als = alpha + s * T * D;
   const float *rds = rkden + s * T * 2;
 
-  // This wave's 16 state rows.  MAP: waves [0, D/16) hold Pi rows, the rest B rows.
-  const bool pi_rows = !FINAL && wave < D / 16;
-  const int rowbase = 16 * (FINAL ? wave : (pi_rows ? wave : wave - D / 16));
+  const bool pi_rows = !FINAL && blockIdx.z == 0;
+  const int rowbase = 16 * wave;
   const bool has_v = FINAL || !pi_rows;
 
   f4_t X[C::NFT];
@@ -543,23 +665,84 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
         X[ft][r] = (pi_rows && rowbase + li == 16 * ft + 4 * gq + r) ? 1.f : 0.f;
   }
 
+  // Register prefetch of a chunk: 16-byte vectors of k (and q) and float4 of ahat; lanes
+  // run over consecutive tokens so the packed LDS writes are contiguous.
+  using IO = io<TIn>;
+  using vec_t = typename IO::vec_t;
+  constexpr int VW = IO::kVec;
+  constexpr int UK = CH * D / VW;
+  constexpr int UA = CH * D / 4;
+  constexpr int PK = (UK + C::NT - 1) / C::NT;
+  constexpr int PA = (UA + C::NT - 1) / C::NT;
+  vec_t pk[PK], pq[FINAL ? PK : 1];
+  float prk[PK];
+  float4 pa[PA];
+  float pden = 1.f;
+  auto prefetch = [&](int64_t cs) {
+    const int mm = static_cast<int>(std::min<int64_t>(CH, te - cs));
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      const int ui = tid + i * C::NT;
+      const int c = ui % CH, f0 = (ui / CH) * VW;
+      const bool ok = ui < UK && c < mm;
+      const int64_t off = (cs + c) * D + f0;
+      pk[i] = ok ? *reinterpret_cast<const vec_t *>(ks + off) : vec_t{};
+      prk[i] = ok ? rds[(cs + c) * 2] : 0.f;
+      if constexpr (FINAL) pq[i] = ok ? *reinterpret_cast<const vec_t *>(qs + off) : vec_t{};
+    }
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int ui = tid + i * C::NT;
+      const int c = ui % CH, f0 = (ui / CH) * 4;
+      const bool ok = ui < UA && c < mm;
+      pa[i] = ok ? *reinterpret_cast<const float4 *>(als + (cs + c) * D + f0)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if constexpr (FINAL) pden = (tid < mm) ? rds[(cs + tid) * 2 + 1] : 1.f;
+  };
+  prefetch(tb);
+
   for (int64_t c0 = tb; c0 < te; c0 += CH) {
     const int m = static_cast<int>(std::min<int64_t>(CH, te - c0));
     __syncthreads();
-    // ---- stage the chunk ------------------------------------------------------------
-    for (int e = tid; e < CH * D; e += C::NT) {
-      const int c = e / D, f = e % D;
-      const bool ok = c < m;
-      const int64_t t = c0 + c;
-      const float kh = ok ? load_elem(ks, t * D + f) * rds[t * 2] : 0.f;
-      const float a = ok ? als[t * D + f] : 0.f;
-      KhT[f][c] = kh;
-      AlT[f][c] = a;
-      Al[c][f] = a;
-      if constexpr (FINAL) FqT[f][c] = ok ? phi(load_elem(qs, t * D + f)) : 0.f;
+    // ---- stage the chunk from registers -----------------------------------------------
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      const int ui = tid + i * C::NT;
+      if (ui < UK) {
+        const int c = ui % CH, f0 = (ui / CH) * VW;
+        float kf[VW];
+        IO::unpack(pk[i], kf);
+#pragma unroll
+        for (int e = 0; e < VW; e += 4)
+          *reinterpret_cast<float4 *>(&KhP[(f0 + e) / 4][c][0]) =
+              make_float4(kf[e] * prk[i], kf[e + 1] * prk[i], kf[e + 2] * prk[i], kf[e + 3] * prk[i]);
+        if constexpr (FINAL) {
+          float qf[VW];
+          IO::unpack(pq[i], qf);
+          const bool ok = c < m;
+#pragma unroll
+          for (int e = 0; e < VW; e += 4)
+            *reinterpret_cast<float4 *>(&FqP[(f0 + e) / 4][c][0]) =
+                ok ? make_float4(phi(qf[e]), phi(qf[e + 1]), phi(qf[e + 2]), phi(qf[e + 3]))
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int ui = tid + i * C::NT;
+      if (ui < UA) {
+        const int c = ui % CH, f0 = (ui / CH) * 4;
+        *reinterpret_cast<float4 *>(&AlP[f0 / 4][c][0]) = pa[i];
+        AcP[c / 4][f0 + 0][c % 4] = pa[i].x;
+        AcP[c / 4][f0 + 1][c % 4] = pa[i].y;
+        AcP[c / 4][f0 + 2][c % 4] = pa[i].z;
+        AcP[c / 4][f0 + 3][c % 4] = pa[i].w;
+      }
     }
     if constexpr (FINAL)
-      for (int c = tid; c < CH; c += C::NT) sDen[c] = c < m ? rds[(c0 + c) * 2 + 1] : 1.f;
+      if (tid < CH) sDen[tid] = pden;
     __syncthreads();
     // ---- shared chunk products: Ka = strict-lower(Kh ahat^T), Qa = lower(Fq ahat^T) --
     for (int job = wave; job < (FINAL ? 2 : 1) * C::NKT; job += C::NWV) {
@@ -569,22 +752,26 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
       const int ct2 = t;
       f4_t acc = f4_zero();
 #pragma unroll
-      for (int kt = 0; kt < C::NFT; ++kt)
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int f = 16 * kt + 4 * gq + st;
-          const float aop = isq ? FqT[FINAL ? f : 0][16 * ct + li] : KhT[f][16 * ct + li];
-          acc = mfma_f32_16x16x4(aop, AlT[f][16 * ct2 + li], acc);
-        }
+      for (int kt = 0; kt < C::NFT; ++kt) {
+        const float4 a4 = isq ? lds4(&FqP[FINAL ? 4 * kt + gq : 0][16 * ct + li][0])
+                              : lds4(&KhP[4 * kt + gq][16 * ct + li][0]);
+        const float4 b4 = lds4(&AlP[4 * kt + gq][16 * ct2 + li][0]);
+        acc = mfma_f32_16x16x4(a4.x, b4.x, acc);
+        acc = mfma_f32_16x16x4(a4.y, b4.y, acc);
+        acc = mfma_f32_16x16x4(a4.z, b4.z, acc);
+        acc = mfma_f32_16x16x4(a4.w, b4.w, acc);
+      }
+      // acc[r] = product[c = 16 ct + 4 gq + r][c'' = 16 ct2 + li]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * gq + r;
         float val = acc[r];
         if (ct == ct2 && (isq ? (li > i) : (li >= i))) val = 0.f;
+        const int cc = 16 * ct2 + li;
         if (isq) {
-          if constexpr (FINAL) QaT[16 * ct2 + li][16 * ct + i] = val;
+          if constexpr (FINAL) QaP[cc / 4][16 * ct + i][cc % 4] = val;
         } else {
-          KaT[16 * ct2 + li][16 * ct + i] = val;
+          KaP[cc / 4][16 * ct + i][cc % 4] = val;
         }
       }
     }
@@ -597,67 +784,81 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
       for (int i = 0; i < 16; ++i) {
         float acc = (i == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int i2 = 0; i2 < i; ++i2) acc = fmaf(-KaT[16 * b + i2][16 * b + i], x[i2], acc);
+        for (int i2 = 0; i2 < i; ++i2) {
+          const int cc = 16 * b + i2;
+          acc = fmaf(-KaP[cc / 4][16 * b + i][cc % 4], x[i2], acc);
+        }
         x[i] = acc;
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) InvT[b][j][i] = x[i];
+      for (int i = 0; i < 16; ++i) InvP[b][j / 4][i][j % 4] = x[i];  // Inv[i][j] = x_j[i]
     }
     __syncthreads();
     // ---- this wave's rows -------------------------------------------------------------
     f4_t E[C::NCT];
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct) {
-      f4_t acc = f4_zero();
-#pragma unroll
-      for (int kt = 0; kt < C::NFT; ++kt)
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-          acc = mfma_f32_16x16x4(-KhT[16 * kt + 4 * gq + st][16 * ct + li], X[kt][st], acc);
+      float vv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = 16 * ct + 4 * gq + r;
-        if (has_v && c < m) acc[r] += load_elem(vs, (c0 + c) * D + rowbase + li);
+        vv[r] = (has_v && c < m) ? load_elem(vs, (c0 + c) * D + rowbase + li) : 0.f;
       }
-      E[ct] = acc;  // R for now
-    }
-    f4_t N[FINAL ? C::NCT : 1];
-    if constexpr (FINAL) {
+      f4_t acc = f4_zero();
 #pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct) {
-        f4_t acc = f4_zero();
-#pragma unroll
-        for (int kt = 0; kt < C::NFT; ++kt)
-#pragma unroll
-          for (int st = 0; st < 4; ++st)
-            acc = mfma_f32_16x16x4(FqT[16 * kt + 4 * gq + st][16 * ct + li], X[kt][st], acc);
-        N[ct] = acc;
+      for (int kt = 0; kt < C::NFT; ++kt) {
+        const float4 a4 = lds4(&KhP[4 * kt + gq][16 * ct + li][0]);
+        acc = mfma_f32_16x16x4(-a4.x, X[kt][0], acc);
+        acc = mfma_f32_16x16x4(-a4.y, X[kt][1], acc);
+        acc = mfma_f32_16x16x4(-a4.z, X[kt][2], acc);
+        acc = mfma_f32_16x16x4(-a4.w, X[kt][3], acc);
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += vv[r];
+      E[ct] = acc;  // R = Vx - Kh X^T
     }
     // E = (I + Ka)^{-1} R by block forward substitution.
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct) {
       f4_t acc = E[ct];
 #pragma unroll
-      for (int ct2 = 0; ct2 < ct; ++ct2)
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-          acc = mfma_f32_16x16x4(-KaT[16 * ct2 + 4 * gq + st][16 * ct + li], E[ct2][st], acc);
+      for (int ct2 = 0; ct2 < ct; ++ct2) {
+        const float4 a4 = lds4(&KaP[4 * ct2 + gq][16 * ct + li][0]);
+        acc = mfma_f32_16x16x4(-a4.x, E[ct2][0], acc);
+        acc = mfma_f32_16x16x4(-a4.y, E[ct2][1], acc);
+        acc = mfma_f32_16x16x4(-a4.z, E[ct2][2], acc);
+        acc = mfma_f32_16x16x4(-a4.w, E[ct2][3], acc);
+      }
+      const float4 i4 = lds4(&InvP[ct][gq][li][0]);
       f4_t e = f4_zero();
-#pragma unroll
-      for (int st = 0; st < 4; ++st) e = mfma_f32_16x16x4(InvT[ct][4 * gq + st][li], acc[st], e);
+      e = mfma_f32_16x16x4(i4.x, acc[0], e);
+      e = mfma_f32_16x16x4(i4.y, acc[1], e);
+      e = mfma_f32_16x16x4(i4.z, acc[2], e);
+      e = mfma_f32_16x16x4(i4.w, acc[3], e);
       E[ct] = e;
     }
     if constexpr (FINAL) {
+      // Num = Fq X_start^T + lower(Fq ahat^T) E, then o = Num / den.
       TIn *os = out + s * T * D;
 #pragma unroll
       for (int ct = 0; ct < C::NCT; ++ct) {
-        f4_t acc = N[ct];
+        f4_t acc = f4_zero();
 #pragma unroll
-        for (int ct2 = 0; ct2 <= ct; ++ct2)
+        for (int kt = 0; kt < C::NFT; ++kt) {
+          const float4 a4 = lds4(&FqP[4 * kt + gq][16 * ct + li][0]);
+          acc = mfma_f32_16x16x4(a4.x, X[kt][0], acc);
+          acc = mfma_f32_16x16x4(a4.y, X[kt][1], acc);
+          acc = mfma_f32_16x16x4(a4.z, X[kt][2], acc);
+          acc = mfma_f32_16x16x4(a4.w, X[kt][3], acc);
+        }
 #pragma unroll
-          for (int st = 0; st < 4; ++st)
-            acc = mfma_f32_16x16x4(QaT[16 * ct2 + 4 * gq + st][16 * ct + li], E[ct2][st], acc);
+        for (int ct2 = 0; ct2 <= ct; ++ct2) {
+          const float4 a4 = lds4(&QaP[4 * ct2 + gq][16 * ct + li][0]);
+          acc = mfma_f32_16x16x4(a4.x, E[ct2][0], acc);
+          acc = mfma_f32_16x16x4(a4.y, E[ct2][1], acc);
+          acc = mfma_f32_16x16x4(a4.z, E[ct2][2], acc);
+          acc = mfma_f32_16x16x4(a4.w, E[ct2][3], acc);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * gq + r;
@@ -665,17 +866,19 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
         }
       }
     }
+    // The next chunk's loads fly during the state update and the next barrier.
+    if (c0 + CH < te) prefetch(c0 + CH);
     // X^T += ahat^T E.
 #pragma unroll
-    for (int ft = 0; ft < C::NFT; ++ft) {
-      f4_t acc = X[ft];
+    for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct)
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-          acc = mfma_f32_16x16x4(Al[16 * ct + 4 * gq + st][16 * ft + li], E[ct][st], acc);
-      X[ft] = acc;
-    }
+      for (int ft = 0; ft < C::NFT; ++ft) {
+        const float4 a4 = lds4(&AcP[4 * ct + gq][16 * ft + li][0]);
+        X[ft] = mfma_f32_16x16x4(a4.x, E[ct][0], X[ft]);
+        X[ft] = mfma_f32_16x16x4(a4.y, E[ct][1], X[ft]);
+        X[ft] = mfma_f32_16x16x4(a4.z, E[ct][2], X[ft]);
+        X[ft] = mfma_f32_16x16x4(a4.w, E[ct][3], X[ft]);
+      }
   }
 
   float *dst = nullptr;
@@ -693,15 +896,21 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
 }
 
 // ------------------------------------------------------------------------------------
-// k_sprefix: S_0 = 0, S_{p+1} = S_p Pi_p + B_p; one wave per (stream, 16-row slice).
+// k_sprefix: S_0 = 0, S_{p+1} = S_p Pi_p + B_p.  One workgroup per stream, one wave per
+// 16-row slice of S (held transposed in MFMA accumulators); Pi_p is staged in LDS packed
+// as [f'/4][f][f'%4] and the next segment's Pi and B are loaded while this one multiplies.
 // ------------------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(D / 16 * kWave)
 k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P) {
   constexpr int NFT = D / 16;
+  constexpr int NT = NFT * kWave;
+  constexpr int U4 = D * D / 4;               // float4 of Pi
+  constexpr int PP = (U4 + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) float PiP[D / 4][D + 1][4];
   const int64_t s = blockIdx.x;
-  const int rowbase = 16 * blockIdx.y;
-  const int lane = threadIdx.x, li = lane & 15, gq = lane >> 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, gq = lane >> 4;
+  const int rowbase = 16 * wave;
   f4_t X[NFT];
 #pragma unroll
   for (int ft = 0; ft < NFT; ++ft) X[ft] = f4_zero();
@@ -709,21 +918,50 @@ k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P) {
 #pragma unroll
   for (int ft = 0; ft < NFT; ++ft)
     *reinterpret_cast<float4 *>(&out0[(rowbase + li) * D + 16 * ft + 4 * gq]) = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t p = 0; p + 1 < P; ++p) {
-    const float *Pi = pib + (s * P + p) * 2 * D * D;
+  float4 pp[PP], pb[NFT];
+  auto prefetch = [&](int64_t pseg) {
+    const float *Pi = pib + (s * P + pseg) * 2 * D * D;
     const float *Bm = Pi + D * D;
+#pragma unroll
+    for (int i = 0; i < PP; ++i) {
+      const int ui = tid + i * NT;              // row f' = ui % D, columns 4 * (ui / D) ..
+      pp[i] = ui < U4 ? *reinterpret_cast<const float4 *>(&Pi[(ui % D) * D + 4 * (ui / D)])
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+      pb[ft] = *reinterpret_cast<const float4 *>(&Bm[(rowbase + li) * D + 16 * ft + 4 * gq]);
+  };
+  if (P > 1) prefetch(0);
+  for (int64_t p = 0; p + 1 < P; ++p) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PP; ++i) {
+      const int ui = tid + i * NT;
+      if (ui < U4) {
+        const int fr = ui % D, fc = 4 * (ui / D);
+        PiP[fr / 4][fc + 0][fr % 4] = pp[i].x;
+        PiP[fr / 4][fc + 1][fr % 4] = pp[i].y;
+        PiP[fr / 4][fc + 2][fr % 4] = pp[i].z;
+        PiP[fr / 4][fc + 3][fr % 4] = pp[i].w;
+      }
+    }
     f4_t Y[NFT];
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) {
-      const float4 b = *reinterpret_cast<const float4 *>(&Bm[(rowbase + li) * D + 16 * ft + 4 * gq]);
-      f4_t acc = f4_t{b.x, b.y, b.z, b.w};
+    for (int ft = 0; ft < NFT; ++ft) Y[ft] = f4_t{pb[ft].x, pb[ft].y, pb[ft].z, pb[ft].w};
+    __syncthreads();
+    if (p + 2 < P) prefetch(p + 1);
+    // Y^T[f][row] = B^T + sum_f' Pi[f'][f] X^T[f'][row]
 #pragma unroll
-      for (int kt = 0; kt < NFT; ++kt)
+    for (int kt = 0; kt < NFT; ++kt)
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          acc = mfma_f32_16x16x4(Pi[(16 * kt + 4 * gq + st) * D + 16 * ft + li], X[kt][st], acc);
-      Y[ft] = acc;
-    }
+      for (int ft = 0; ft < NFT; ++ft) {
+        const float4 a4 = *reinterpret_cast<const float4 *>(&PiP[4 * kt + gq][16 * ft + li][0]);
+        Y[ft] = mfma_f32_16x16x4(a4.x, X[kt][0], Y[ft]);
+        Y[ft] = mfma_f32_16x16x4(a4.y, X[kt][1], Y[ft]);
+        Y[ft] = mfma_f32_16x16x4(a4.z, X[kt][2], Y[ft]);
+        Y[ft] = mfma_f32_16x16x4(a4.w, X[kt][3], Y[ft]);
+      }
     float *o = s0 + (s * P + p + 1) * D * D;
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) {
@@ -769,11 +1007,11 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                        nkw, alw, rdw, A_final, pl.S, pl.T, pl.L, pl.P, pr.eps);
   }
   if (P > 1) {
-    VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1),
+    VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),
                        dim3(SwyCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw,
                        oo, S_final, pl.T, pl.L, pl.P);
   }
-  VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(64), 0, st, pbw, s0w, pl.P);
+  VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
   VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P), dim3(SwyCfg<D, CH, true>::NT), 0,
                      st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
   return hipGetLastError();
