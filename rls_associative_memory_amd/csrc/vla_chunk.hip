@@ -294,52 +294,158 @@ k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0
 }
 
 // ------------------------------------------------------------------------------------
-// k_inv: M_p <- M_p^{-1} in place (Gauss-Jordan without pivoting; M_p is SPD), symmetrised.
-// Each thread keeps D*D/256 elements in registers; per elimination step only the pivot row
-// and column go through LDS (parity double-buffered, one barrier per step).
+// k_inv: M_p <- M_p^{-1} (block Gauss-Jordan without pivoting on 16 x 16 blocks; M_p is
+// SPD), symmetrised.  The nb x nb blocks live in MFMA accumulators spread over 4 waves.
+// Elimination step kb: invert the diagonal block P (one wave, scalar Gauss-Jordan), then
+//   row panel    A[kb][j] <- P^{-1} A[kb][j]
+//   trailing     A[i][j]  <- A[i][j] - A[i][kb] (P^{-1} A[kb][j])
+//   column panel A[i][kb] <- -A[i][kb] P^{-1},   A[kb][kb] <- P^{-1}
+// with every block product on v_mfma_f32_16x16x4_f32 (operands packed k-minor in LDS).
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) k_inv(float *__restrict__ M, int64_t P) {
-  constexpr int NE = D * D / 256;
-  static_assert(D * D % 256 == 0, "elements must tile the threads");
-  __shared__ float rowk[2][D], colk[2][D];
+  constexpr int NB = D / 16;
+  constexpr int NOWN = (NB * NB + 3) / 4;  // blocks per wave
+  __shared__ __attribute__((aligned(16))) float Pd[16][17];         // diagonal block, scalar GJ
+  __shared__ __attribute__((aligned(16))) float PiA[4][16][4];      // P^-1 as A operand [k/4][i][k%4]
+  __shared__ __attribute__((aligned(16))) float PiB[4][16][4];      // P^-1 as B operand [k/4][j][k%4]
+  __shared__ __attribute__((aligned(16))) float CP[NB][4][16][4];   // column panel (A operands)
+  __shared__ __attribute__((aligned(16))) float RP[NB][4][16][4];   // row panel (B operands)
   __shared__ float sym[D][D + 1];
   const int64_t s = blockIdx.x, p = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, gq = lane >> 4;
   float *base = M + (s * P + p) * D * D;
-  float a[NE];
-  int ei[NE], ej[NE];
+
+  // Block n = wave + 4 m is (n / NB, n % NB); acc element r = A[16 bi + 4 gq + r][16 bj + li].
+  f4_t acc[NOWN];
 #pragma unroll
-  for (int m = 0; m < NE; ++m) {
-    const int e = tid + 256 * m;
-    ei[m] = e / D;
-    ej[m] = e % D;
-    a[m] = base[e];
+  for (int m = 0; m < NOWN; ++m) {
+    const int n = wave + 4 * m;
+    if (n < NB * NB) {
+      const int bi = n / NB, bj = n % NB;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[m][r] = base[(16 * bi + 4 * gq + r) * D + 16 * bj + li];
+    }
   }
-  for (int kk = 0; kk < D; ++kk) {
-    const int b = kk & 1;
+  for (int kb = 0; kb < NB; ++kb) {
+    __syncthreads();
+    // (1) publish the diagonal block and the column panel
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {
-      if (ei[m] == kk) rowk[b][ej[m]] = a[m];
-      if (ej[m] == kk) colk[b][ei[m]] = a[m];
+    for (int m = 0; m < NOWN; ++m) {
+      const int n = wave + 4 * m;
+      if (n < NB * NB && n % NB == kb) {
+        const int bi = n / NB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (bi == kb) Pd[4 * gq + r][li] = acc[m][r];
+          CP[bi][li / 4][4 * gq + r][li % 4] = acc[m][r];  // C[i'][k]: i' = 4gq + r, k = li
+        }
+      }
     }
     __syncthreads();
-    const float piv = 1.0f / rowk[b][kk];
+    // (2) P^{-1} by scalar Gauss-Jordan in one wave: lane owns row lane/4, columns 4(lane%4)..
+    if (wave == 0) {
+      const int i = lane >> 2, j0 = 4 * (lane & 3);
+      float e[4];
 #pragma unroll
-    for (int m = 0; m < NE; ++m) {
-      if (ei[m] == kk)
-        a[m] = (ej[m] == kk) ? piv : a[m] * piv;
-      else if (ej[m] == kk)
-        a[m] = -a[m] * piv;
-      else
-        a[m] = fmaf(-colk[b][ei[m]] * piv, rowk[b][ej[m]], a[m]);
+      for (int c = 0; c < 4; ++c) e[c] = Pd[i][j0 + c];
+      for (int kk = 0; kk < 16; ++kk) {
+        const float piv = 1.0f / Pd[kk][kk];
+        const float cik = Pd[i][kk];
+        float rkj[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) rkj[c] = Pd[kk][j0 + c];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = j0 + c;
+          if (i == kk)
+            e[c] = (j == kk) ? piv : e[c] * piv;
+          else if (j == kk)
+            e[c] = -cik * piv;
+          else
+            e[c] = fmaf(-cik * piv, rkj[c], e[c]);
+          Pd[i][j] = e[c];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = j0 + c;
+        PiA[j / 4][i][j % 4] = e[c];  // A operand: element (row i, k = j)
+        PiB[i / 4][j][i % 4] = e[c];  // B operand: element (k = i, col j)
+      }
+    }
+    __syncthreads();
+    // (3) row panel: A[kb][j] <- P^{-1} A[kb][j]; publish as B operands.
+#pragma unroll
+    for (int m = 0; m < NOWN; ++m) {
+      const int n = wave + 4 * m;
+      if (n < NB * NB && n / NB == kb && n % NB != kb) {
+        const int bj = n % NB;
+        const float4 a4 = *reinterpret_cast<const float4 *>(&PiA[gq][li][0]);
+        f4_t r4 = f4_zero();
+        r4 = mfma_f32_16x16x4(a4.x, acc[m][0], r4);
+        r4 = mfma_f32_16x16x4(a4.y, acc[m][1], r4);
+        r4 = mfma_f32_16x16x4(a4.z, acc[m][2], r4);
+        r4 = mfma_f32_16x16x4(a4.w, acc[m][3], r4);
+        acc[m] = r4;
+        *reinterpret_cast<float4 *>(&RP[bj][gq][li][0]) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+      }
+    }
+    __syncthreads();
+    // (4) trailing blocks and the column panel.
+#pragma unroll
+    for (int m = 0; m < NOWN; ++m) {
+      const int n = wave + 4 * m;
+      if (n < NB * NB) {
+        const int bi = n / NB, bj = n % NB;
+        if (bi == kb) {
+          if (bj == kb) {
+            const float4 pv = *reinterpret_cast<const float4 *>(&PiB[gq][li][0]);
+            acc[m] = f4_t{pv.x, pv.y, pv.z, pv.w};
+          }
+        } else {
+          const float4 c4 = *reinterpret_cast<const float4 *>(&CP[bi][gq][li][0]);
+          if (bj == kb) {
+            const float4 b4 = *reinterpret_cast<const float4 *>(&PiB[gq][li][0]);
+            f4_t r4 = f4_zero();
+            r4 = mfma_f32_16x16x4(-c4.x, b4.x, r4);
+            r4 = mfma_f32_16x16x4(-c4.y, b4.y, r4);
+            r4 = mfma_f32_16x16x4(-c4.z, b4.z, r4);
+            r4 = mfma_f32_16x16x4(-c4.w, b4.w, r4);
+            acc[m] = r4;
+          } else {
+            const float4 b4 = *reinterpret_cast<const float4 *>(&RP[bj][gq][li][0]);
+            acc[m] = mfma_f32_16x16x4(-c4.x, b4.x, acc[m]);
+            acc[m] = mfma_f32_16x16x4(-c4.y, b4.y, acc[m]);
+            acc[m] = mfma_f32_16x16x4(-c4.z, b4.z, acc[m]);
+            acc[m] = mfma_f32_16x16x4(-c4.w, b4.w, acc[m]);
+          }
+        }
+      }
     }
   }
-#pragma unroll
-  for (int m = 0; m < NE; ++m) sym[ei[m]][ej[m]] = a[m];
+  // Symmetrise: A <- (A + A^T) / 2.
   __syncthreads();
 #pragma unroll
-  for (int m = 0; m < NE; ++m) base[tid + 256 * m] = 0.5f * (a[m] + sym[ej[m]][ei[m]]);
+  for (int m = 0; m < NOWN; ++m) {
+    const int n = wave + 4 * m;
+    if (n < NB * NB) {
+      const int bi = n / NB, bj = n % NB;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sym[16 * bi + 4 * gq + r][16 * bj + li] = acc[m][r];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < D * D; e += 256) {
+    const int i = e / D, j = e % D;
+    base[e] = 0.5f * (sym[i][j] + sym[j][i]);
+  }
 }
 
 // ------------------------------------------------------------------------------------
