@@ -730,17 +730,21 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
       const float *__restrict__ s0, float *__restrict__ pib, TIn *__restrict__ out,
       float *__restrict__ S_final, int64_t T, int64_t L, int64_t P) {
   using C = SwyCfg<D, CH, FINAL>;
+  using IO = io<TIn>;
+  using vec_t = typename IO::vec_t;
+  constexpr int VW = IO::kVec;
   // [f/4][c][f%4]: khat, phi(q), ahat packed by feature; [c/4][f][c%4]: ahat packed by token.
   __shared__ __attribute__((aligned(16))) float KhP[D / 4][CH][4];
   __shared__ __attribute__((aligned(16))) float AlP[D / 4][CH][4];
   __shared__ __attribute__((aligned(16))) float FqP[FINAL ? D / 4 : 1][CH][4];
   __shared__ __attribute__((aligned(16))) float AcP[CH / 4][C::DP][4];
-  // [c''/4][c][c''%4]: strict-lower (Kh ahat^T) and lower (Fq ahat^T), packed by column.
+  // [c''/4][c][c''%4]: -(strict lower of Kh ahat^T) and lower(Fq ahat^T), packed by column.
   __shared__ __attribute__((aligned(16))) float KaP[CH / 4][CH][4];
   __shared__ __attribute__((aligned(16))) float QaP[FINAL ? CH / 4 : 1][CH][4];
   // Inverses of the unit-lower diagonal 16-blocks of I + Ka: [b][k/4][i][k%4].
   __shared__ __attribute__((aligned(16))) float InvP[C::NCT][4][16][4];
-  __shared__ float sDen[CH];
+  __shared__ __attribute__((aligned(16))) TIn sV[CH][D];   // the chunk's values (input dtype)
+  __shared__ float sRden[CH];                                // 1 / readout denominator
 
   const int64_t s = blockIdx.x, p = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, gq = lane >> 4;
@@ -771,16 +775,13 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
         X[ft][r] = (pi_rows && rowbase + li == 16 * ft + 4 * gq + r) ? 1.f : 0.f;
   }
 
-  // Register prefetch of a chunk: 16-byte vectors of k (and q) and float4 of ahat; lanes
-  // run over consecutive tokens so the packed LDS writes are contiguous.
-  using IO = io<TIn>;
-  using vec_t = typename IO::vec_t;
-  constexpr int VW = IO::kVec;
+  // Register prefetch of a chunk: 16-byte vectors of k, q, v and float4 of ahat; lanes run
+  // over consecutive tokens so the packed LDS writes are contiguous.
   constexpr int UK = CH * D / VW;
   constexpr int UA = CH * D / 4;
   constexpr int PK = (UK + C::NT - 1) / C::NT;
   constexpr int PA = (UA + C::NT - 1) / C::NT;
-  vec_t pk[PK], pq[FINAL ? PK : 1];
+  vec_t pk[PK], pq[FINAL ? PK : 1], pv[PK];
   float prk[PK];
   float4 pa[PA];
   float pden = 1.f;
@@ -795,6 +796,7 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
       pk[i] = ok ? *reinterpret_cast<const vec_t *>(ks + off) : vec_t{};
       prk[i] = ok ? rds[(cs + c) * 2] : 0.f;
       if constexpr (FINAL) pq[i] = ok ? *reinterpret_cast<const vec_t *>(qs + off) : vec_t{};
+      pv[i] = (ok && has_v) ? *reinterpret_cast<const vec_t *>(vs + off) : vec_t{};
     }
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
@@ -833,6 +835,7 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
                 ok ? make_float4(phi(qf[e]), phi(qf[e + 1]), phi(qf[e + 2]), phi(qf[e + 3]))
                    : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        *reinterpret_cast<vec_t *>(&sV[c][f0]) = pv[i];
       }
     }
 #pragma unroll
@@ -848,14 +851,22 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
       }
     }
     if constexpr (FINAL)
-      if (tid < CH) sDen[tid] = pden;
+      if (tid < CH) sRden[tid] = 1.0f / pden;
     __syncthreads();
-    // ---- shared chunk products: Ka = strict-lower(Kh ahat^T), Qa = lower(Fq ahat^T) --
+    // ---- shared chunk products (diagonal tiles first; each diagonal Ka tile's wave also
+    //      inverts its unit-lower block) ------------------------------------------------
     for (int job = wave; job < (FINAL ? 2 : 1) * C::NKT; job += C::NWV) {
       const bool isq = job >= C::NKT;
-      int t = isq ? job - C::NKT : job, ct = 0;
-      while (t > ct) { t -= ct + 1; ++ct; }
-      const int ct2 = t;
+      const int jj = isq ? job - C::NKT : job;
+      int ct, ct2;
+      if (jj < C::NCT) {
+        ct = ct2 = jj;                          // diagonal tiles
+      } else {
+        int t = jj - C::NCT;                    // strictly-lower tiles, row by row
+        ct = 1;
+        while (t >= ct) { t -= ct; ++ct; }
+        ct2 = t;
+      }
       f4_t acc = f4_zero();
 #pragma unroll
       for (int kt = 0; kt < C::NFT; ++kt) {
@@ -868,72 +879,75 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
         acc = mfma_f32_16x16x4(a4.w, b4.w, acc);
       }
       // acc[r] = product[c = 16 ct + 4 gq + r][c'' = 16 ct2 + li]
+      const int cc = 16 * ct2 + li;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * gq + r;
         float val = acc[r];
         if (ct == ct2 && (isq ? (li > i) : (li >= i))) val = 0.f;
-        const int cc = 16 * ct2 + li;
         if (isq) {
           if constexpr (FINAL) QaP[cc / 4][16 * ct + i][cc % 4] = val;
         } else {
-          KaP[cc / 4][16 * ct + i][cc % 4] = val;
+          KaP[cc / 4][16 * ct + i][cc % 4] = -val;
         }
       }
-    }
-    __syncthreads();
-    // ---- inverses of the unit-lower diagonal blocks of I + Ka -------------------------
-    if (wave == 0 && lane < 16 * C::NCT) {
-      const int b = lane >> 4, j = li;
-      float x[16];
+      if (!isq && ct == ct2) {
+        // (I + Ka_bb)^{-1} by forward substitution in lanes 0..15 (column j = lane).
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < 16) {
+          const int b = ct, j = lane;
+          float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = (i == j) ? 1.f : 0.f;
+          for (int i = 0; i < 16; ++i) {
+            float a = (i == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int i2 = 0; i2 < i; ++i2) {
-          const int cc = 16 * b + i2;
-          acc = fmaf(-KaP[cc / 4][16 * b + i][cc % 4], x[i2], acc);
+            for (int i2 = 0; i2 < i; ++i2) {
+              const int c2 = 16 * b + i2;
+              a = fmaf(KaP[c2 / 4][16 * b + i][c2 % 4], x[i2], a);  // KaP holds -Ka
+            }
+            x[i] = a;
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) InvP[b][j / 4][i][j % 4] = x[i];  // Inv[i][j] = x_j[i]
         }
-        x[i] = acc;
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) InvP[b][j / 4][i][j % 4] = x[i];  // Inv[i][j] = x_j[i]
     }
     __syncthreads();
     // ---- this wave's rows -------------------------------------------------------------
     f4_t E[C::NCT];
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct) {
-      float vv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 16 * ct + 4 * gq + r;
-        vv[r] = (has_v && c < m) ? load_elem(vs, (c0 + c) * D + rowbase + li) : 0.f;
-      }
       f4_t acc = f4_zero();
 #pragma unroll
       for (int kt = 0; kt < C::NFT; ++kt) {
         const float4 a4 = lds4(&KhP[4 * kt + gq][16 * ct + li][0]);
-        acc = mfma_f32_16x16x4(-a4.x, X[kt][0], acc);
-        acc = mfma_f32_16x16x4(-a4.y, X[kt][1], acc);
-        acc = mfma_f32_16x16x4(-a4.z, X[kt][2], acc);
-        acc = mfma_f32_16x16x4(-a4.w, X[kt][3], acc);
+        acc = mfma_f32_16x16x4(a4.x, X[kt][0], acc);
+        acc = mfma_f32_16x16x4(a4.y, X[kt][1], acc);
+        acc = mfma_f32_16x16x4(a4.z, X[kt][2], acc);
+        acc = mfma_f32_16x16x4(a4.w, X[kt][3], acc);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] += vv[r];
+      for (int r = 0; r < 4; ++r) {
+        const float vv = has_v ? load_elem(&sV[0][0], (16 * ct + 4 * gq + r) * D + rowbase + li) : 0.f;
+        acc[r] = vv - acc[r];
+      }
       E[ct] = acc;  // R = Vx - Kh X^T
     }
-    // E = (I + Ka)^{-1} R by block forward substitution.
+    // The next chunk's loads fly during the solve, the readout and the state update.
+    if (c0 + CH < te) prefetch(c0 + CH);
+    // E = (I + Ka)^{-1} R by block forward substitution (KaP holds -Ka).
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct) {
       f4_t acc = E[ct];
 #pragma unroll
       for (int ct2 = 0; ct2 < ct; ++ct2) {
         const float4 a4 = lds4(&KaP[4 * ct2 + gq][16 * ct + li][0]);
-        acc = mfma_f32_16x16x4(-a4.x, E[ct2][0], acc);
-        acc = mfma_f32_16x16x4(-a4.y, E[ct2][1], acc);
-        acc = mfma_f32_16x16x4(-a4.z, E[ct2][2], acc);
-        acc = mfma_f32_16x16x4(-a4.w, E[ct2][3], acc);
+        acc = mfma_f32_16x16x4(a4.x, E[ct2][0], acc);
+        acc = mfma_f32_16x16x4(a4.y, E[ct2][1], acc);
+        acc = mfma_f32_16x16x4(a4.z, E[ct2][2], acc);
+        acc = mfma_f32_16x16x4(a4.w, E[ct2][3], acc);
       }
       const float4 i4 = lds4(&InvP[ct][gq][li][0]);
       f4_t e = f4_zero();
@@ -968,12 +982,10 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * gq + r;
-          if (c < m) store_elem(os, (c0 + c) * D + rowbase + li, acc[r] / sDen[c]);
+          if (c < m) store_elem(os, (c0 + c) * D + rowbase + li, acc[r] * sRden[c]);
         }
       }
     }
-    // The next chunk's loads fly during the state update and the next barrier.
-    if (c0 + CH < te) prefetch(c0 + CH);
     // X^T += ahat^T E.
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct)
