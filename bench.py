@@ -50,6 +50,7 @@ def flops_per_token_head(d: int) -> int:
 KERNEL_WORK = {
     "vla_seq_kernel": (lambda d: 12 * d * d + 20 * d, "alu"),
     "k_aside": (lambda d: 6 * d * d + 10 * d, "alu"),
+    "k_aside_wy": (lambda d: 6 * d * d + 10 * d, "mfma"),
     "k_swy_final": (lambda d: 6 * d * d + 10 * d, "mfma"),
     "k_swy_map": (lambda d: 8 * d * d, "mfma"),
     "k_gram": (lambda d: 2 * d * d, "mfma"),

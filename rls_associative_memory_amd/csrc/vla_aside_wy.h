@@ -1,0 +1,506 @@
+// A side of the chunked path on the bf16 matrix cores (bf16 inputs).
+//
+// Per segment (one workgroup of d/16 waves) the inverse penalty A starts from the
+// segment-start inverse and advances 32 tokens at a time.  For a chunk with rows U, K
+// (raw bf16 u_t, k_t) the Sherman-Morrison recursion of the VLA summary (§2.2, §2.3
+// step 1) is equivalent to (Woodbury, with G = I + U A U^T = L D L^T, L unit lower):
+//   Z  = L^{-1} (U A)        row j is z_j = A_{j-1} u_j,  D_jj = delta_j
+//   Y  = K A - tril0(K Z^T) D^{-1} Z          row j is A_j k_j (gate before normalising)
+//   A <- A - Z^T D^{-1} Z
+// and ahat_j = Y_j / ||Y_j|| (§2.3 step 2; the key's norm cancels).
+//
+// Layout.  Wave w holds column tile w of A (16 columns, all rows) in MFMA accumulators.
+// Because A is symmetric, those registers are also row tile w of A, i.e. exactly the
+// A operand of A [U^T | K^T] for rows 16w..16w+15, so A never goes through LDS; each
+// fp32 fragment is split into three bf16 terms (hi + mid + lo, about 24 bits) right before
+// use.  Products with the raw bf16 inputs are therefore exact term by term; products of
+// two derived fp32 operands use the six term pairs with a + b <= 2 (dropped terms are
+// below 2^-23 relative), accumulated in fp32 by v_mfma_f32_16x16x32_bf16.
+#pragma once
+
+#include "vla_common.h"
+#include "vla_mfma.h"
+
+namespace vla {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f4_t mfma_bf16(const bf16x8_t &a, const bf16x8_t &b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Split3 {
+  bf16x8_t t[3];
+};
+
+__device__ __forceinline__ Split3 split3(const float (&x)[8]) {
+  Split3 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(x[e]);
+    const float r1 = x[e] - static_cast<float>(h);
+    const __bf16 m = static_cast<__bf16>(r1);
+    const float r2 = r1 - static_cast<float>(m);
+    s.t[0][e] = h;
+    s.t[1][e] = m;
+    s.t[2][e] = static_cast<__bf16>(r2);
+  }
+  return s;
+}
+
+// exact A operand x split B operand
+__device__ __forceinline__ f4_t mm_xs(const bf16x8_t &a, const bf16x8_t (&b)[3], f4_t c) {
+  c = mfma_bf16(a, b[2], c);
+  c = mfma_bf16(a, b[1], c);
+  return mfma_bf16(a, b[0], c);
+}
+// split A operand x exact B operand
+__device__ __forceinline__ f4_t mm_sx(const bf16x8_t (&a)[3], const bf16x8_t &b, f4_t c) {
+  c = mfma_bf16(a[2], b, c);
+  c = mfma_bf16(a[1], b, c);
+  return mfma_bf16(a[0], b, c);
+}
+// split x split (term pairs a + b <= 2)
+__device__ __forceinline__ f4_t mm_ss(const bf16x8_t (&a)[3], const bf16x8_t (&b)[3], f4_t c) {
+  c = mfma_bf16(a[1], b[1], c);
+  c = mfma_bf16(a[0], b[2], c);
+  c = mfma_bf16(a[2], b[0], c);
+  c = mfma_bf16(a[0], b[1], c);
+  c = mfma_bf16(a[1], b[0], c);
+  return mfma_bf16(a[0], b[0], c);
+}
+
+__device__ __forceinline__ bf16x8_t ld_bf8(const uint16_t *p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(p));
+}
+__device__ __forceinline__ bf16x8_t ld_bf4x2(const uint16_t *p0, const uint16_t *p1) {
+  const uint2 a = *reinterpret_cast<const uint2 *>(p0);
+  const uint2 b = *reinterpret_cast<const uint2 *>(p1);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+__device__ __forceinline__ void ld_split(bf16x8_t (&dst)[3], const uint16_t *base, int term_stride) {
+#pragma unroll
+  for (int t = 0; t < 3; ++t) dst[t] = ld_bf8(base + t * term_stride);
+}
+__device__ __forceinline__ uint16_t bf_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+__device__ __forceinline__ float bf_val(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// Split one fp32 value into its three bf16 terms (bit patterns).
+__device__ __forceinline__ void split1(float x, uint16_t &h, uint16_t &m, uint16_t &l) {
+  const __bf16 bh = static_cast<__bf16>(x);
+  const float r1 = x - static_cast<float>(bh);
+  const __bf16 bm = static_cast<__bf16>(r1);
+  const float r2 = r1 - static_cast<float>(bm);
+  h = bf_bits(bh);
+  m = bf_bits(bm);
+  l = bf_bits(static_cast<__bf16>(r2));
+}
+
+template <int D>
+struct AwyCfg {
+  static constexpr int NW = D / 16;
+  static constexpr int NT = NW * kWave;  // = 4 D
+  static constexpr int C = 32;           // tokens per chunk
+  static constexpr int NKS = D / 32;     // 32-wide feature slices (D = 32 -> 1)
+  static constexpr int LDU = D + 8;      // padded bf16 row stride of token rows
+  static constexpr int LDL = 40;         // padded bf16 row stride of the 32 x 32 matrices
+  static_assert(D % 32 == 0, "feature dimension must be a multiple of 32");
+};
+
+template <int D>
+struct AwyLds {
+  using C = AwyCfg<D>;
+  uint16_t sU[C::C][C::LDU];
+  uint16_t sK[C::C][C::LDU];
+  uint16_t sQ[C::C][C::LDU];
+  uint16_t Zr[3][C::C][C::LDU];          // row-major Z0 / Z terms; later W (token-packed)
+  uint16_t Zc[3][C::C / 8][D][8];        // token-packed Z0 / Z terms: [c/8][f][c%8]
+  float G[C::C][C::C + 4];               // I + U A U^T (lower part used); then L^{-1} transposed
+  uint16_t LX[3][C::C][C::LDL];          // L^{-1} terms (A operand), then X~ terms (B operand)
+  float piv[2][2][kWave] __attribute__((aligned(16)));  // pivot columns (double buffered)
+  float rsd[C::C], rd[C::C];
+  float norm[C::NW][C::C];
+};
+
+template <int D>
+__global__ void __launch_bounds__(AwyCfg<D>::NT)
+k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+           const bf16_t *__restrict__ u, const float *__restrict__ A0,
+           const float *__restrict__ nk0, float *__restrict__ alpha, float *__restrict__ rkden,
+           float *__restrict__ A_final, int64_t T, int64_t L, int64_t P, float eps) {
+  using C = AwyCfg<D>;
+  constexpr int NW = C::NW, NT = C::NT, CH = C::C;
+  constexpr int ZR_T = CH * C::LDU;       // term stride of Zr
+  constexpr int ZC_T = CH * D;            // term stride of Zc / W
+  constexpr int LX_T = CH * C::LDL;       // term stride of LX
+  __shared__ __attribute__((aligned(16))) AwyLds<D> sh;
+
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
+  const uint16_t *us = reinterpret_cast<const uint16_t *>(u) + s * T * D;
+  const uint16_t *ks = reinterpret_cast<const uint16_t *>(k) + s * T * D;
+  const uint16_t *qs = reinterpret_cast<const uint16_t *>(q) + s * T * D;
+  float *al = alpha + s * T * D;
+  float *rd = rkden + s * T * 2;
+
+  // Column tile w of A: At[it][r] = A[16 it + 4 gq + r][16 w + li].
+  f4_t At[NW];
+  {
+    const float *a0 = A0 + (s * P + p) * D * D;
+#pragma unroll
+    for (int it = 0; it < NW; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) At[it][r] = a0[(16 * it + 4 * gq + r) * D + 16 * w + li];
+  }
+  // Readout normaliser n (sum of phi(k) so far) for features lane and lane + 64; kept by
+  // every wave w >= 1, which compute the denominators while wave 0 factors G.
+  const bool hf0 = lane < D, hf1 = lane + 64 < D;
+  float nrun0 = hf0 ? nk0[(s * P + p) * D + lane] : 0.f;
+  float nrun1 = hf1 ? nk0[(s * P + p) * D + lane + 64] : 0.f;
+
+  // Staging: thread tid loads token tid / (D/8), features (tid % (D/8)) * 8 of u, k, q.
+  const int sc = tid / (D / 8), sf0 = (tid % (D / 8)) * 8;
+  uint4 pv[3];
+  auto prefetch = [&](int64_t cs) {
+    const bool ok = cs + sc < te;
+    const int64_t off = (cs + sc) * D + sf0;
+    pv[0] = ok ? *reinterpret_cast<const uint4 *>(us + off) : make_uint4(0, 0, 0, 0);
+    pv[1] = ok ? *reinterpret_cast<const uint4 *>(ks + off) : make_uint4(0, 0, 0, 0);
+    pv[2] = ok ? *reinterpret_cast<const uint4 *>(qs + off) : make_uint4(0, 0, 0, 0);
+  };
+  prefetch(tb);
+
+  for (int64_t c0 = tb; c0 < te; c0 += CH) {
+    const int m = static_cast<int>(std::min<int64_t>(CH, te - c0));
+    __syncthreads();
+    *reinterpret_cast<uint4 *>(&sh.sU[sc][sf0]) = pv[0];
+    *reinterpret_cast<uint4 *>(&sh.sK[sc][sf0]) = pv[1];
+    *reinterpret_cast<uint4 *>(&sh.sQ[sc][sf0]) = pv[2];
+    __syncthreads();
+
+    // ---- [Z0^T | P^T] = A [U^T | K^T] (rows 16w.., 32 tokens) ---------------------------
+    f4_t Z0t[2], Pt[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) { Z0t[ct] = f4_zero(); Pt[ct] = f4_zero(); }
+#pragma unroll
+    for (int ksl = 0; ksl < C::NKS; ++ksl) {
+      float x[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { x[r] = At[2 * ksl][r]; x[4 + r] = At[2 * ksl + 1][r]; }
+      const Split3 af = split3(x);
+      const int f0 = 32 * ksl + 4 * gq, f1 = 32 * ksl + 16 + 4 * gq;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const bf16x8_t bu = ld_bf4x2(&sh.sU[16 * ct + li][f0], &sh.sU[16 * ct + li][f1]);
+        const bf16x8_t bk = ld_bf4x2(&sh.sK[16 * ct + li][f0], &sh.sK[16 * ct + li][f1]);
+        Z0t[ct] = mm_sx(af.t, bu, Z0t[ct]);
+        Pt[ct] = mm_sx(af.t, bk, Pt[ct]);
+      }
+    }
+    // ---- publish Z0: row-major (for G) and token-packed (for L^{-1} Z0) -----------------
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      uint16_t hh[4], mmv[4], ll[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) split1(Z0t[ct][r], hh[r], mmv[r], ll[r]);
+      const int c = 16 * ct + li, f = 16 * w + 4 * gq;
+      *reinterpret_cast<uint2 *>(&sh.Zr[0][c][f]) = make_uint2(hh[0] | (uint32_t(hh[1]) << 16), hh[2] | (uint32_t(hh[3]) << 16));
+      *reinterpret_cast<uint2 *>(&sh.Zr[1][c][f]) = make_uint2(mmv[0] | (uint32_t(mmv[1]) << 16), mmv[2] | (uint32_t(mmv[3]) << 16));
+      *reinterpret_cast<uint2 *>(&sh.Zr[2][c][f]) = make_uint2(ll[0] | (uint32_t(ll[1]) << 16), ll[2] | (uint32_t(ll[3]) << 16));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sh.Zc[0][c / 8][f + r][c % 8] = hh[r];
+        sh.Zc[1][c / 8][f + r][c % 8] = mmv[r];
+        sh.Zc[2][c / 8][f + r][c % 8] = ll[r];
+      }
+    }
+    __syncthreads();
+    // ---- G = I + U Z0^T on the lower 16-tiles (0,0), (1,0), (1,1) ----------------------
+    for (int tile = w; tile < 4; tile += NW) {
+      if (tile == 3) {  // the upper tile (0,1) is never read as data; keep it finite
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sh.G[4 * gq + r][16 + li] = 0.f;
+        continue;
+      }
+      const int it = (tile == 0) ? 0 : 1, jt = (tile == 2) ? 1 : 0;
+      f4_t g = f4_zero();
+#pragma unroll
+      for (int ksl = 0; ksl < C::NKS; ++ksl) {
+        const bf16x8_t a = ld_bf8(&sh.sU[16 * it + li][32 * ksl + 8 * gq]);
+        bf16x8_t b[3];
+        ld_split(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
+        g = mm_xs(a, b, g);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * it + 4 * gq + r, j = 16 * jt + li;
+        sh.G[i][j] = g[r] + (i == j ? 1.f : 0.f);
+      }
+    }
+    __syncthreads();
+    // ---- wave 0: G = L D L^T and L^{-1};  waves >= 1: readout denominators ----------------
+    if (w == 0) {
+      // Lane i < 32 holds row i of G; lane 32 + m holds column m of L^{-1}, starting from the
+      // identity.  Pivots are taken two at a time (j, j + 1): with c0, c1 the columns j, j + 1
+      // of the partly eliminated G (published by the row lanes through LDS), g = c0[j + 1],
+      // d0 = c0[j], d1 = c1[j + 1] - g^2 / d0 and, from the lane's own x[j], x[j + 1],
+      //   x1 = x[j + 1] - (g / d0) x[j],   s2 = x1 / d1,   s1 = (x[j] - g s2) / d0,
+      // every lane applies x[r] -= s1 c0[r] + s2 c1[r] for r > j + 1 and sets x[j + 1] = x1.
+      // For a row of G this eliminates both pivots (s1, s2 are its multipliers up to the
+      // d factors); for a column of L^{-1} it is the forward substitution of rows j, j + 1.
+      // Only lower entries of G are read, so the upper tile may hold anything finite.
+      const int i = lane & 31;
+      const bool grow = lane < 32;
+      float x[CH];
+#pragma unroll
+      for (int c4 = 0; c4 < CH / 4; ++c4) {
+        const f4_t gv = *reinterpret_cast<const f4_t *>(&sh.G[i][4 * c4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * c4 + e] = grow ? gv[e] : (4 * c4 + e == i ? 1.f : 0.f);
+      }
+      sh.piv[0][0][lane] = x[0];
+      sh.piv[0][1][lane] = x[1];
+      float myd = 1.f;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int jb = 0; jb < CH / 2; ++jb) {
+        const int j = 2 * jb, buf = jb & 1;
+        float c0[CH], c1[CH];
+#pragma unroll
+        for (int r4 = j / 4; r4 < CH / 4; ++r4) {
+          const f4_t a0 = *reinterpret_cast<const f4_t *>(&sh.piv[buf][0][4 * r4]);
+          const f4_t a1 = *reinterpret_cast<const f4_t *>(&sh.piv[buf][1][4 * r4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { c0[4 * r4 + e] = a0[e]; c1[4 * r4 + e] = a1[e]; }
+        }
+        const float d0 = c0[j], g = c0[j + 1];
+        const float rd0 = __builtin_amdgcn_rcpf(d0);
+        const float gd = g * rd0;
+        const float d1 = fmaf(-g, gd, c1[j + 1]);
+        const float rd1 = __builtin_amdgcn_rcpf(d1);
+        const float x1 = fmaf(-gd, x[j], x[j + 1]);
+        const float s2 = x1 * rd1;
+        const float s1 = fmaf(-g, s2, x[j]) * rd0;
+        x[j + 1] = x1;
+        if (lane == j) myd = d0;
+        if (lane == j + 1) myd = d1;
+        if (j + 2 < CH) {
+#pragma unroll
+          for (int r = j + 2; r < j + 4; ++r) x[r] = fmaf(-s2, c1[r], fmaf(-s1, c0[r], x[r]));
+          sh.piv[buf ^ 1][0][lane] = x[j + 2];  // lanes >= 32 fill unread slots
+          sh.piv[buf ^ 1][1][lane] = x[j + 3];
+#pragma unroll
+          for (int r = j + 4; r < CH; ++r) x[r] = fmaf(-s2, c1[r], fmaf(-s1, c0[r], x[r]));
+          // keep each pivot step's reads and updates together (bounded register use)
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+      }
+      // Pivots, and L^{-1} transposed into the (now free) G buffer: T[m][r] = L^{-1}[r][m].
+      float(*Tb)[CH + 4] = sh.G;
+      if (grow) {
+        sh.rd[i] = 1.0f / myd;
+        sh.rsd[i] = rsqrtf(myd);
+      } else {
+#pragma unroll
+        for (int r = 0; r < CH; ++r) Tb[i][r] = x[r];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Row-major split terms of L^{-1}: lane (row i2, half h) writes 16 entries per term.
+      const int i2 = lane >> 1, h = lane & 1;
+      uint32_t pk[3][8];
+#pragma unroll
+      for (int c = 0; c < 16; c += 2) {
+        uint16_t h0, m0, l0, h1, m1, l1;
+        split1(Tb[16 * h + c][i2], h0, m0, l0);
+        split1(Tb[16 * h + c + 1][i2], h1, m1, l1);
+        pk[0][c / 2] = h0 | (uint32_t(h1) << 16);
+        pk[1][c / 2] = m0 | (uint32_t(m1) << 16);
+        pk[2][c / 2] = l0 | (uint32_t(l1) << 16);
+      }
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        uint4 *dst = reinterpret_cast<uint4 *>(&sh.LX[t][i2][16 * h]);
+        dst[0] = make_uint4(pk[t][0], pk[t][1], pk[t][2], pk[t][3]);
+        dst[1] = make_uint4(pk[t][4], pk[t][5], pk[t][6], pk[t][7]);
+      }
+    } else {
+      // Token c of the chunk is finished by wave 1 + c % (NW - 1): den_c = n_c . phi(q_c)
+      // with n_c = n_{c-1} + phi(k_c), and ||k_c||^2; every helper wave runs the prefix.
+      constexpr int NH = NW - 1;
+      const int hw = w - 1;
+      float n0 = nrun0, n1 = nrun1;
+      int own = hw;  // next token this wave finishes
+#pragma unroll 2
+      for (int c = 0; c < m; ++c) {
+        {
+          const float k0 = hf0 ? bf_val(sh.sK[c][lane]) : 0.f;
+          const float k1 = hf1 ? bf_val(sh.sK[c][lane + 64]) : 0.f;
+          n0 += hf0 ? phi(k0) : 0.f;
+          n1 += hf1 ? phi(k1) : 0.f;
+          if (c == own) {
+            own += NH;
+            const float q0 = hf0 ? phi(bf_val(sh.sQ[c][lane])) : 0.f;
+            const float q1 = hf1 ? phi(bf_val(sh.sQ[c][lane + 64])) : 0.f;
+            const float dsum = wave_sum(fmaf(n1, q1, n0 * q0));
+            const float kk = wave_sum(fmaf(k1, k1, k0 * k0));
+            if (lane == 0)
+              *reinterpret_cast<float2 *>(&rd[(c0 + c) * 2]) =
+                  make_float2(kk > 0.f ? rsqrtf(kk) : 0.f, dsum + eps);
+          }
+        }
+      }
+      nrun0 = n0;
+      nrun1 = n1;
+    }
+    __syncthreads();
+    // next chunk's rows: issued here so the loads overlap the rest of this chunk
+    if (c0 + CH < te) prefetch(c0 + CH);
+    // ---- Z^T = Z0^T L^{-T} ---------------------------------------------------------------
+    f4_t Zt[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      bf16x8_t a[3], b[3];
+      ld_split(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
+      ld_split(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
+      Zt[ct] = mm_ss(a, b, f4_zero());
+    }
+    __syncthreads();
+    // ---- publish Z: row-major (for K Z^T) and token-packed (for X~ Z) ---------------------
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      uint16_t hh[4], mmv[4], ll[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) split1(Zt[ct][r], hh[r], mmv[r], ll[r]);
+      const int c = 16 * ct + li, f = 16 * w + 4 * gq;
+      *reinterpret_cast<uint2 *>(&sh.Zr[0][c][f]) = make_uint2(hh[0] | (uint32_t(hh[1]) << 16), hh[2] | (uint32_t(hh[3]) << 16));
+      *reinterpret_cast<uint2 *>(&sh.Zr[1][c][f]) = make_uint2(mmv[0] | (uint32_t(mmv[1]) << 16), mmv[2] | (uint32_t(mmv[3]) << 16));
+      *reinterpret_cast<uint2 *>(&sh.Zr[2][c][f]) = make_uint2(ll[0] | (uint32_t(ll[1]) << 16), ll[2] | (uint32_t(ll[3]) << 16));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sh.Zc[0][c / 8][f + r][c % 8] = hh[r];
+        sh.Zc[1][c / 8][f + r][c % 8] = mmv[r];
+        sh.Zc[2][c / 8][f + r][c % 8] = ll[r];
+      }
+    }
+    __syncthreads();
+    // ---- X~ = tril0(K Z^T) D^{-1} on tiles (0,0), (1,0), (1,1); the (0,1) tile is zero --
+    for (int tile = w; tile < 4; tile += NW) {
+      if (tile == 3) {  // X~ is lower triangular: the (0,1) tile is zero
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * gq + r, j = 16 + li;
+          sh.LX[0][i][j] = 0;
+          sh.LX[1][i][j] = 0;
+          sh.LX[2][i][j] = 0;
+        }
+        continue;
+      }
+      const int it = (tile == 0) ? 0 : 1, jt = (tile == 2) ? 1 : 0;
+      f4_t hacc = f4_zero();
+#pragma unroll
+      for (int ksl = 0; ksl < C::NKS; ++ksl) {
+        const bf16x8_t a = ld_bf8(&sh.sK[16 * it + li][32 * ksl + 8 * gq]);
+        bf16x8_t b[3];
+        ld_split(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
+        hacc = mm_xs(a, b, hacc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * it + 4 * gq + r, j = 16 * jt + li;
+        const float xv = (j <= i) ? hacc[r] * sh.rd[j] : 0.f;
+        uint16_t hh, mmv, ll;
+        split1(xv, hh, mmv, ll);
+        sh.LX[0][i][j] = hh;
+        sh.LX[1][i][j] = mmv;
+        sh.LX[2][i][j] = ll;
+      }
+    }
+    __syncthreads();
+    // ---- W = D^{-1/2} Z, token-packed, into the (now free) row-major buffer --------------
+    uint16_t *Wc = &sh.Zr[0][0][0];  // [3][C/8][D][8]
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int c = 16 * ct + li;
+      const float sc2 = sh.rsd[c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint16_t hh, mmv, ll;
+        split1(Zt[ct][r] * sc2, hh, mmv, ll);
+        const int f = 16 * w + 4 * gq + r;
+        const int idx = ((c / 8) * D + f) * 8 + (c % 8);
+        Wc[idx] = hh;
+        Wc[ZC_T + idx] = mmv;
+        Wc[2 * ZC_T + idx] = ll;
+      }
+    }
+    // ---- Y^T = P^T - Z^T X~^T, then the gates ----------------------------------------------
+    f4_t Yt[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      bf16x8_t a[3], b[3];
+      ld_split(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
+      ld_split(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
+      const f4_t xz = mm_ss(a, b, f4_zero());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Yt[ct][r] = Pt[ct][r] - xz[r];
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part = fmaf(Yt[ct][r], Yt[ct][r], part);
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (gq == 0) sh.norm[w][16 * ct + li] = part;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int c = 16 * ct + li;
+      float tot = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) tot += sh.norm[w2][c];
+      const float inv = tot > 0.f ? rsqrtf(tot) : 0.f;
+      if (c < m)
+        *reinterpret_cast<float4 *>(&al[(c0 + c) * D + 16 * w + 4 * gq]) =
+            make_float4(Yt[ct][0] * inv, Yt[ct][1] * inv, Yt[ct][2] * inv, Yt[ct][3] * inv);
+    }
+    // ---- A <- A - W^T W on this wave's column tile ------------------------------------------
+    {
+      bf16x8_t b[3];
+      ld_split(b, &Wc[(gq * D + 16 * w + li) * 8], ZC_T);
+#pragma unroll
+      for (int it = 0; it < NW; ++it) {
+        bf16x8_t a[3];
+        ld_split(a, &Wc[(gq * D + 16 * it + li) * 8], ZC_T);
+        const f4_t t4 = mm_ss(a, b, f4_zero());
+#pragma unroll
+        for (int r = 0; r < 4; ++r) At[it][r] -= t4[r];
+      }
+    }
+  }
+
+  if (A_final != nullptr && p == P - 1) {
+    // Symmetrise through LDS: A_T <- (A + A^T) / 2.
+    __syncthreads();
+    float(*sym)[D + 1] = reinterpret_cast<float(*)[D + 1]>(&sh);
+#pragma unroll
+    for (int it = 0; it < NW; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sym[16 * it + 4 * gq + r][16 * w + li] = At[it][r];
+    __syncthreads();
+    float *dst = A_final + s * D * D;
+    for (int e = tid; e < D * D; e += NT) {
+      const int i = e / D, j = e % D;
+      dst[e] = 0.5f * (sym[i][j] + sym[j][i]);
+    }
+  }
+}
+
+}  // namespace vla

@@ -34,6 +34,7 @@
 #include "vla_common.h"
 #include "vla_internal.h"
 #include "vla_mfma.h"
+#include "vla_aside_wy.h"
 
 namespace vla {
 
@@ -115,8 +116,6 @@ __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, int64_t i, float x
 // packed so each lane's MFMA operand is one 16-byte LDS read; the next block's 16-byte
 // global loads are issued before the current block is multiplied.
 // ------------------------------------------------------------------------------------
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
 template <typename TIn>
 struct GramLds;
 template <>
@@ -1117,12 +1116,16 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
   VLA_LAUNCH("k_prefix", (k_prefix<D>), dim3(S, (D * D + 255) / 256), dim3(256), 0, st, Mw, nkw,
                      pl.P, pr.lambda0);
   VLA_LAUNCH("k_inv", (k_inv<D>), dim3(S, P), dim3(256), 0, st, Mw, pl.P);
-  {
+  if constexpr (sizeof(TIn) == 2) {
+    // bf16 inputs: chunked A side on the bf16 matrix cores.
+    VLA_LAUNCH("k_aside_wy", (k_aside_wy<D>), dim3(S, P), dim3(AwyCfg<D>::NT), 0, st, qq, kk,
+               uu, Mw, nkw, alw, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
+  } else {
     using AC = AsideCfg<D>;
     const int64_t units = pl.S * pl.P;
     const unsigned blocks = static_cast<unsigned>((units + AC::UPB - 1) / AC::UPB);
     VLA_LAUNCH("k_aside", (k_aside<D, TIn>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
-                       nkw, alw, rdw, A_final, pl.S, pl.T, pl.L, pl.P, pr.eps);
+               nkw, alw, rdw, A_final, pl.S, pl.T, pl.L, pl.P, pr.eps);
   }
   if (P > 1) {
     VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),
