@@ -23,79 +23,6 @@
 
 namespace vla {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f4_t mfma_bf16(const bf16x8_t &a, const bf16x8_t &b, f4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-struct Split3 {
-  bf16x8_t t[3];
-};
-
-__device__ __forceinline__ Split3 split3(const float (&x)[8]) {
-  Split3 s;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 h = static_cast<__bf16>(x[e]);
-    const float r1 = x[e] - static_cast<float>(h);
-    const __bf16 m = static_cast<__bf16>(r1);
-    const float r2 = r1 - static_cast<float>(m);
-    s.t[0][e] = h;
-    s.t[1][e] = m;
-    s.t[2][e] = static_cast<__bf16>(r2);
-  }
-  return s;
-}
-
-// exact A operand x split B operand
-__device__ __forceinline__ f4_t mm_xs(const bf16x8_t &a, const bf16x8_t (&b)[3], f4_t c) {
-  c = mfma_bf16(a, b[2], c);
-  c = mfma_bf16(a, b[1], c);
-  return mfma_bf16(a, b[0], c);
-}
-// split A operand x exact B operand
-__device__ __forceinline__ f4_t mm_sx(const bf16x8_t (&a)[3], const bf16x8_t &b, f4_t c) {
-  c = mfma_bf16(a[2], b, c);
-  c = mfma_bf16(a[1], b, c);
-  return mfma_bf16(a[0], b, c);
-}
-// split x split (term pairs a + b <= 2)
-__device__ __forceinline__ f4_t mm_ss(const bf16x8_t (&a)[3], const bf16x8_t (&b)[3], f4_t c) {
-  c = mfma_bf16(a[1], b[1], c);
-  c = mfma_bf16(a[0], b[2], c);
-  c = mfma_bf16(a[2], b[0], c);
-  c = mfma_bf16(a[0], b[1], c);
-  c = mfma_bf16(a[1], b[0], c);
-  return mfma_bf16(a[0], b[0], c);
-}
-
-__device__ __forceinline__ bf16x8_t ld_bf8(const uint16_t *p) {
-  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(p));
-}
-__device__ __forceinline__ bf16x8_t ld_bf4x2(const uint16_t *p0, const uint16_t *p1) {
-  const uint2 a = *reinterpret_cast<const uint2 *>(p0);
-  const uint2 b = *reinterpret_cast<const uint2 *>(p1);
-  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
-}
-__device__ __forceinline__ void ld_split(bf16x8_t (&dst)[3], const uint16_t *base, int term_stride) {
-#pragma unroll
-  for (int t = 0; t < 3; ++t) dst[t] = ld_bf8(base + t * term_stride);
-}
-__device__ __forceinline__ uint16_t bf_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
-__device__ __forceinline__ float bf_val(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
-
-// Split one fp32 value into its three bf16 terms (bit patterns).
-__device__ __forceinline__ void split1(float x, uint16_t &h, uint16_t &m, uint16_t &l) {
-  const __bf16 bh = static_cast<__bf16>(x);
-  const float r1 = x - static_cast<float>(bh);
-  const __bf16 bm = static_cast<__bf16>(r1);
-  const float r2 = r1 - static_cast<float>(bm);
-  h = bf_bits(bh);
-  m = bf_bits(bm);
-  l = bf_bits(static_cast<__bf16>(r2));
-}
-
 template <int D>
 struct AwyCfg {
   static constexpr int NW = D / 16;

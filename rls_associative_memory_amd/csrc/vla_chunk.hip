@@ -35,6 +35,7 @@
 #include "vla_internal.h"
 #include "vla_mfma.h"
 #include "vla_aside_wy.h"
+#include "vla_swy_bf16.h"
 
 namespace vla {
 
@@ -1127,14 +1128,27 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     VLA_LAUNCH("k_aside", (k_aside<D, TIn>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
                nkw, alw, rdw, A_final, pl.S, pl.T, pl.L, pl.P, pr.eps);
   }
-  if (P > 1) {
-    VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),
-                       dim3(SwyCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw,
-                       oo, S_final, pl.T, pl.L, pl.P);
+  if constexpr (sizeof(TIn) == 2) {
+    // bf16 inputs: S side on the bf16 matrix cores.
+    using SC = SwbCfg<D, CH>;
+    if (P > 1) {
+      VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, P - 1, 2), dim3(SC::NT), 0, st, qq,
+                 kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
+    }
+    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
+    VLA_LAUNCH("k_swy_final", (k_swyb<D, CH, true>), dim3(S, P), dim3(SC::NT), 0, st, qq, kk, vv,
+               alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
+  } else {
+    if (P > 1) {
+      VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),
+                 dim3(SwyCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
+                 S_final, pl.T, pl.L, pl.P);
+    }
+    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
+    VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P),
+               dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final,
+               pl.T, pl.L, pl.P);
   }
-  VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
-  VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P), dim3(SwyCfg<D, CH, true>::NT), 0,
-                     st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
   return hipGetLastError();
 }
 

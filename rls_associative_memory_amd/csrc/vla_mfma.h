@@ -12,6 +12,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace vla {
 
@@ -22,5 +23,131 @@ __device__ __forceinline__ f4_t mfma_f32_16x16x4(float a, float b, f4_t c) {
 }
 
 __device__ __forceinline__ f4_t f4_zero() { return f4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// ---- bf16 matrix cores with fp32 operands split into bf16 terms ------------------------
+// v_mfma_f32_16x16x32_bf16 (checked on the device): A lane l supplies A[li][8 gq + e], B lane l
+// supplies B[8 gq + e][li] (e < 8); D as above.  The products below use a permuted
+// contraction index: element e < 4 of a lane is k = 32 s + 4 gq + e and element e >= 4 is
+// k = 32 s + 16 + 4 gq + (e - 4), so that the four accumulator values of two D-layout tiles
+// form one operand.  A raw bf16 input is exact in one term; an fp32 value x is split as
+// x = h + m + l (three terms, about 24 significant bits) or x = h + l (two terms, about 16).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f4_t mfma_bf16(const bf16x8_t &a, const bf16x8_t &b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Split3 {
+  bf16x8_t t[3];
+};
+
+__device__ __forceinline__ Split3 split3(const float (&x)[8]) {
+  Split3 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(x[e]);
+    const float r1 = x[e] - static_cast<float>(h);
+    const __bf16 m = static_cast<__bf16>(r1);
+    const float r2 = r1 - static_cast<float>(m);
+    s.t[0][e] = h;
+    s.t[1][e] = m;
+    s.t[2][e] = static_cast<__bf16>(r2);
+  }
+  return s;
+}
+
+// exact A operand x split B operand
+__device__ __forceinline__ f4_t mm_xs(const bf16x8_t &a, const bf16x8_t (&b)[3], f4_t c) {
+  c = mfma_bf16(a, b[2], c);
+  c = mfma_bf16(a, b[1], c);
+  return mfma_bf16(a, b[0], c);
+}
+// split A operand x exact B operand
+__device__ __forceinline__ f4_t mm_sx(const bf16x8_t (&a)[3], const bf16x8_t &b, f4_t c) {
+  c = mfma_bf16(a[2], b, c);
+  c = mfma_bf16(a[1], b, c);
+  return mfma_bf16(a[0], b, c);
+}
+// split x split (term pairs a + b <= 2)
+__device__ __forceinline__ f4_t mm_ss(const bf16x8_t (&a)[3], const bf16x8_t (&b)[3], f4_t c) {
+  c = mfma_bf16(a[1], b[1], c);
+  c = mfma_bf16(a[0], b[2], c);
+  c = mfma_bf16(a[2], b[0], c);
+  c = mfma_bf16(a[0], b[1], c);
+  c = mfma_bf16(a[1], b[0], c);
+  return mfma_bf16(a[0], b[0], c);
+}
+
+__device__ __forceinline__ bf16x8_t ld_bf8(const uint16_t *p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(p));
+}
+__device__ __forceinline__ bf16x8_t ld_bf4x2(const uint16_t *p0, const uint16_t *p1) {
+  const uint2 a = *reinterpret_cast<const uint2 *>(p0);
+  const uint2 b = *reinterpret_cast<const uint2 *>(p1);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+__device__ __forceinline__ void ld_split(bf16x8_t (&dst)[3], const uint16_t *base, int term_stride) {
+#pragma unroll
+  for (int t = 0; t < 3; ++t) dst[t] = ld_bf8(base + t * term_stride);
+}
+__device__ __forceinline__ uint16_t bf_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+__device__ __forceinline__ float bf_val(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// Split one fp32 value into its three bf16 terms (bit patterns).
+__device__ __forceinline__ void split1(float x, uint16_t &h, uint16_t &m, uint16_t &l) {
+  const __bf16 bh = static_cast<__bf16>(x);
+  const float r1 = x - static_cast<float>(bh);
+  const __bf16 bm = static_cast<__bf16>(r1);
+  const float r2 = r1 - static_cast<float>(bm);
+  h = bf_bits(bh);
+  m = bf_bits(bm);
+  l = bf_bits(static_cast<__bf16>(r2));
+}
+
+// ---- two-term split ----------------------------------------------------------------------
+struct Split2 {
+  bf16x8_t h, l;
+};
+
+__device__ __forceinline__ void split2_1(float x, uint16_t &h, uint16_t &l) {
+  const __bf16 bh = static_cast<__bf16>(x);
+  h = bf_bits(bh);
+  l = bf_bits(static_cast<__bf16>(x - static_cast<float>(bh)));
+}
+
+__device__ __forceinline__ Split2 split2(const float (&x)[8]) {
+  Split2 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(x[e]);
+    s.h[e] = h;
+    s.l[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
+  }
+  return s;
+}
+
+// exact x two-term
+__device__ __forceinline__ f4_t mm2_xs(const bf16x8_t &a, const Split2 &b, f4_t c) {
+  c = mfma_bf16(a, b.l, c);
+  return mfma_bf16(a, b.h, c);
+}
+// two-term x two-term (the l * l term, about 2^-16 relative, is dropped)
+__device__ __forceinline__ f4_t mm2_ss(const Split2 &a, const Split2 &b, f4_t c) {
+  c = mfma_bf16(a.l, b.h, c);
+  c = mfma_bf16(a.h, b.l, c);
+  return mfma_bf16(a.h, b.h, c);
+}
+// four bf16 at p0 and four at p1, or zeros for the second half
+__device__ __forceinline__ bf16x8_t ld_bf4z(const uint16_t *p0) {
+  const uint2 a = *reinterpret_cast<const uint2 *>(p0);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, 0u, 0u));
+}
+__device__ __forceinline__ Split2 ld2_4x2(const uint16_t *p0, const uint16_t *p1, int term_stride) {
+  return Split2{ld_bf4x2(p0, p1), ld_bf4x2(p0 + term_stride, p1 + term_stride)};
+}
+__device__ __forceinline__ Split2 ld2_4z(const uint16_t *p0, int term_stride) {
+  return Split2{ld_bf4z(p0), ld_bf4z(p0 + term_stride)};
+}
+
 
 }  // namespace vla

@@ -1,0 +1,392 @@
+// S side of the chunked path on the bf16 matrix cores (bf16 inputs).
+//
+// Same chunk algebra as the fp32 kernel (UT/WY form of the residual update S <- S +
+// (v - S khat) ahat^T over CH tokens, VLA summary §2.3 steps 3-4, and the ratio readout of
+// §2.4): with Ka = strict lower part of Khat Ahat^T and Qa = lower part of Phi(q) Ahat^T,
+//   R   = V - Khat X^T                        (X^T: this workgroup's 16-row state slice)
+//   E   = (I + Ka)^{-1} R                     (block forward substitution, 16-token blocks)
+//   Num = Phi(q) X^T + Qa E,   o = Num / den  (final pass only)
+//   X^T += Ahat^T E
+// Every product runs on v_mfma_f32_16x16x32_bf16.  Raw k and v are exact bf16; khat =
+// rk * k is applied after the product.  ahat, phi(q), the state, Ka, Qa and E are fp32 values
+// split into two bf16 terms (hi + lo, about 16 significant bits) and multiplied term pair by
+// term pair with fp32 accumulation, which keeps each product's relative error near 2^-16.
+#pragma once
+
+#include "vla_common.h"
+#include "vla_mfma.h"
+
+namespace vla {
+
+// v where ok, else zeros (component-wise, so the value stays in registers)
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
+template <int D, int CH>
+struct SwbCfg {
+  static constexpr int NWV = D / 16;          // waves = 16-row state slices per workgroup
+  static constexpr int NT = NWV * kWave;
+  static constexpr int NCT = CH / 16;         // 16-token tiles per chunk
+  static constexpr int NPR = (NCT + 1) / 2;   // pairs of token tiles (one 32-token operand)
+  static constexpr int NFT = D / 16;          // 16-feature tiles
+  static constexpr int NKS = D / 32;          // 32-feature slices
+  static constexpr int NKT = NCT * (NCT + 1) / 2;
+  static constexpr int LDF = D + 8;           // bf16 row stride of token rows
+  static constexpr int LDC = CH + 8;          // bf16 row stride of token-indexed columns
+  static constexpr int LDI = 24;              // bf16 row stride of the 16 x 16 inverses
+  static_assert(D % 32 == 0, "feature dimension must be a multiple of 32");
+};
+
+template <int D, int CH, bool FINAL>
+struct SwbLds {
+  using C = SwbCfg<D, CH>;
+  static constexpr int QR = FINAL ? CH : 1;
+  uint16_t sK[CH][C::LDF];                    // raw k, by token
+  uint16_t sV[CH][C::LDF];                    // raw v, by token
+  uint16_t sAh[2][CH][C::LDF];                // ahat terms, by token
+  uint16_t sAt[2][D][C::LDC];                 // ahat terms, by feature
+  uint16_t sFq[2][QR][C::LDF];                // phi(q) terms, by token (final pass)
+  uint16_t KaS[2][CH][C::LDC];                // -Ka terms, row-major
+  uint16_t QaS[2][QR][C::LDC];                // Qa terms, row-major (final pass)
+  uint16_t InvS[2][C::NCT][16][C::LDI];       // (I + Ka_bb)^{-1} terms, row-major
+  float Kd[C::NCT][16][17];                   // -Ka_bb in fp32 for the block inverses
+  float rk[CH];                               // 1 / ||k||
+  float rden[CH];                             // 1 / readout denominator
+};
+
+template <int D, int CH, bool FINAL>
+__global__ void __launch_bounds__((SwbCfg<D, CH>::NT))
+k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
+       const float *__restrict__ alpha, const float *__restrict__ rkden,
+       const float *__restrict__ s0, float *__restrict__ pib, bf16_t *__restrict__ out,
+       float *__restrict__ S_final, int64_t T, int64_t L, int64_t P) {
+  using C = SwbCfg<D, CH>;
+  constexpr int NT = C::NT, NCT = C::NCT, NPR = C::NPR, NFT = C::NFT, NKS = C::NKS;
+  constexpr int TF = CH * C::LDF;             // term strides
+  constexpr int TQ = SwbLds<D, CH, FINAL>::QR * C::LDF;
+  constexpr int TA = D * C::LDC;
+  constexpr int TC = CH * C::LDC;
+  constexpr int TQC = SwbLds<D, CH, FINAL>::QR * C::LDC;
+  constexpr int TI = NCT * 16 * C::LDI;
+  __shared__ __attribute__((aligned(16))) SwbLds<D, CH, FINAL> sh;
+
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, gq = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
+  const uint16_t *ks = reinterpret_cast<const uint16_t *>(k) + s * T * D;
+  const uint16_t *vs = reinterpret_cast<const uint16_t *>(v) + s * T * D;
+  const uint16_t *qs = reinterpret_cast<const uint16_t *>(q) + s * T * D;
+  const float *als = alpha + s * T * D;
+  const float *rds = rkden + s * T * 2;
+
+  const bool pi_rows = !FINAL && blockIdx.z == 0;
+  const int rowbase = 16 * wave;
+  const bool has_v = FINAL || !pi_rows;
+
+  // X[ft][r] = S[rowbase + li][16 ft + 4 gq + r]: a 16-row slice of S, transposed.
+  f4_t X[NFT];
+  if constexpr (FINAL) {
+    const float *st = s0 + (s * P + p) * D * D;
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) {
+      const float4 x = *reinterpret_cast<const float4 *>(&st[(rowbase + li) * D + 16 * ft + 4 * gq]);
+      X[ft] = f4_t{x.x, x.y, x.z, x.w};
+    }
+  } else {
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        X[ft][r] = (pi_rows && rowbase + li == 16 * ft + 4 * gq + r) ? 1.f : 0.f;
+  }
+
+  // Register prefetch of a chunk: 16-byte row pieces of k, q, v (features fastest) and
+  // float4 of ahat (tokens fastest, so the by-feature LDS writes are contiguous).  Loads
+  // past the segment read row 0 instead and are zeroed when staged, so no load result is
+  // selected on (which would make the load wait at once).
+  constexpr int RV = D / 8;                   // uint4 per token row
+  constexpr int UK = CH * RV;
+  constexpr int UA = CH * D / 4;
+  constexpr int PK = (UK + NT - 1) / NT;
+  constexpr int PA = (UA + NT - 1) / NT;
+  uint4 pk[PK], pq[FINAL ? PK : 1], pv[PK];
+  float4 pa[PA];
+  float prk = 0.f, pden = 1.f;
+  // Per-lane offsets are 32-bit (one stream's rows span far less than 4 GiB) from a
+  // workgroup-uniform base, so each load needs one offset register.
+  auto prefetch = [&](int64_t cs, int tid) {
+    const int mm = static_cast<int>(std::min<int64_t>(CH, te - cs));
+    const uint16_t *kc = ks + cs * D, *qc = qs + cs * D, *vc = vs + cs * D;
+    const float *ac = als + cs * D, *rc = rds + cs * 2;
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      const int ui = tid + i * NT;
+      const int c = ui / RV, f0 = (ui % RV) * 8;
+      const uint32_t off = (ui < UK && c < mm) ? static_cast<uint32_t>(c * D + f0) : 0u;
+      pk[i] = *reinterpret_cast<const uint4 *>(kc + off);
+      if constexpr (FINAL) pq[i] = *reinterpret_cast<const uint4 *>(qc + off);
+      pv[i] = *reinterpret_cast<const uint4 *>(vc + (has_v ? off : 0u));  // the Pi pass has no v
+    }
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int ui = tid + i * NT;
+      const int c = ui % CH, f0 = (ui / CH) * 4;
+      const uint32_t off = (ui < UA && c < mm) ? static_cast<uint32_t>(c * D + f0) : 0u;
+      pa[i] = *reinterpret_cast<const float4 *>(ac + off);
+    }
+    const uint32_t toff = (tid < mm) ? static_cast<uint32_t>(tid * 2) : 0u;
+    prk = rc[toff];
+    if constexpr (FINAL) pden = rc[toff + 1];
+  };
+  prefetch(tb, tid);
+
+  for (int64_t c0 = tb; c0 < te; c0 += CH) {
+    const int m = static_cast<int>(std::min<int64_t>(CH, te - c0));
+    // Opaque per-chunk copies of the lane indices: the addresses derived from them are
+    // recomputed each chunk rather than hoisted out of the loop and kept (or spilled).
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, li = lane & 15, gq = lane >> 4;
+    __syncthreads();
+    // ---- stage the chunk ------------------------------------------------------------------
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      const int ui = tid + i * NT;
+      if (ui < UK) {
+        const int c = ui / RV, f0 = (ui % RV) * 8;
+        const bool okv = c < m && has_v;
+        *reinterpret_cast<uint4 *>(&sh.sK[c][f0]) = keep_if(c < m, pk[i]);
+        *reinterpret_cast<uint4 *>(&sh.sV[c][f0]) = keep_if(okv, pv[i]);
+        if constexpr (FINAL) {
+          float qf[8];
+          io<bf16_t>::unpack(pq[i], qf);
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            uint16_t h0, l0, h1, l1;
+            split2_1(c < m ? phi(qf[e]) : 0.f, h0, l0);
+            split2_1(c < m ? phi(qf[e + 1]) : 0.f, h1, l1);
+            hw[e / 2] = h0 | (uint32_t(h1) << 16);
+            lw[e / 2] = l0 | (uint32_t(l1) << 16);
+          }
+          *reinterpret_cast<uint4 *>(&sh.sFq[0][c][f0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          *reinterpret_cast<uint4 *>(&sh.sFq[1][c][f0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PA; ++i) {
+      const int ui = tid + i * NT;
+      if (ui < UA) {
+        const int c = ui % CH, f0 = (ui / CH) * 4;
+        const bool ok = c < m;
+        const float a4[4] = {ok ? pa[i].x : 0.f, ok ? pa[i].y : 0.f, ok ? pa[i].z : 0.f,
+                             ok ? pa[i].w : 0.f};
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split2_1(a4[e], h[e], l[e]);
+        *reinterpret_cast<uint2 *>(&sh.sAh[0][c][f0]) =
+            make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+        *reinterpret_cast<uint2 *>(&sh.sAh[1][c][f0]) =
+            make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sh.sAt[0][f0 + e][c] = h[e];
+          sh.sAt[1][f0 + e][c] = l[e];
+        }
+      }
+    }
+    if (tid < CH) {
+      sh.rk[tid] = tid < m ? prk : 0.f;
+      if constexpr (FINAL) sh.rden[tid] = tid < m ? 1.0f / pden : 0.f;
+    }
+    __syncthreads();
+    // ---- shared chunk products: -Ka = -(strict lower of Khat Ahat^T) and Qa = lower of
+    //      Phi(q) Ahat^T, diagonal tiles first; each diagonal Ka tile's wave also inverts
+    //      its unit-lower block ------------------------------------------------------------
+    for (int job = wave; job < (FINAL ? 2 : 1) * C::NKT; job += C::NWV) {
+      const bool isq = job >= C::NKT;
+      const int jj = isq ? job - C::NKT : job;
+      int ct, ct2;
+      if (jj < NCT) {
+        ct = ct2 = jj;
+      } else {
+        int t = jj - NCT;
+        ct = 1;
+        while (t >= ct) { t -= ct; ++ct; }
+        ct2 = t;
+      }
+      f4_t acc = f4_zero();
+#pragma unroll
+      for (int ksl = 0; ksl < NKS; ++ksl) {
+        const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
+        const Split2 b = ld2_4x2(&sh.sAh[0][16 * ct2 + li][fa], &sh.sAh[0][16 * ct2 + li][fb], TF);
+        if (isq) {
+          if constexpr (FINAL) {
+            const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fb], TQ);
+            acc = mm2_ss(a, b, acc);
+          }
+        } else {
+          const bf16x8_t a = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fb]);
+          acc = mm2_xs(a, b, acc);
+        }
+      }
+      // acc[r] = product[c = 16 ct + 4 gq + r][c'' = 16 ct2 + li]
+      const int cc = 16 * ct2 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * gq + r, row = 16 * ct + i;
+        float val = isq ? acc[r] : -acc[r] * sh.rk[row];
+        if (ct == ct2 && (isq ? (li > i) : (li >= i))) val = 0.f;
+        uint16_t h, l;
+        split2_1(val, h, l);
+        if (isq) {
+          if constexpr (FINAL) {
+            sh.QaS[0][row][cc] = h;
+            sh.QaS[1][row][cc] = l;
+          }
+        } else {
+          sh.KaS[0][row][cc] = h;
+          sh.KaS[1][row][cc] = l;
+          if (ct == ct2) sh.Kd[ct][i][li] = val;
+        }
+      }
+      if (!isq && ct == ct2) {
+        // (I + Ka_bb)^{-1} by forward substitution in lanes 0..15 (column j = lane).
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < 16) {
+          const int b = ct, j = lane;
+          float x[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float a = (i == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int i2 = 0; i2 < i; ++i2) a = fmaf(sh.Kd[b][i][i2], x[i2], a);  // Kd holds -Ka
+            x[i] = a;
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            uint16_t h, l;
+            split2_1(x[i], h, l);
+            sh.InvS[0][b][i][j] = h;
+            sh.InvS[1][b][i][j] = l;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // ---- this wave's rows ---------------------------------------------------------------
+    // The state slice as the B operand of products over features (two tiles per operand).
+    Split2 xs[NKS];
+#pragma unroll
+    for (int ksl = 0; ksl < NKS; ++ksl) {
+      float t8[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { t8[r] = X[2 * ksl][r]; t8[4 + r] = X[2 * ksl + 1][r]; }
+      xs[ksl] = split2(t8);
+    }
+    // R = V - rk (K X^T)
+    f4_t E[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f4_t acc = f4_zero();
+#pragma unroll
+      for (int ksl = 0; ksl < NKS; ++ksl) {
+        const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
+        const bf16x8_t a = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fb]);
+        acc = mm2_xs(a, xs[ksl], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * ct + 4 * gq + r;
+        const float vv = has_v ? bf_val(sh.sV[c][rowbase + li]) : 0.f;
+        E[ct][r] = fmaf(-sh.rk[c], acc[r], vv);
+      }
+    }
+    // The next chunk's loads fly during the solve, the readout and the state update.
+    if (c0 + CH < te) prefetch(c0 + CH, tid);
+    // E = (I + Ka)^{-1} R by block forward substitution (KaS holds -Ka).
+    auto e_pair = [&](int ta, int tbb) {  // two E tiles (tbb may be absent) as a B operand
+      float t8[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        t8[r] = E[ta][r];
+        t8[4 + r] = (tbb < NCT) ? E[tbb < NCT ? tbb : 0][r] : 0.f;
+      }
+      return split2(t8);
+    };
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f4_t acc = E[ct];
+#pragma unroll
+      for (int c2 = 0; c2 < ct; c2 += 2) {
+        const int rowi = 16 * ct + li, ca = 16 * c2 + 4 * gq;
+        const Split2 a = (c2 + 1 < ct) ? ld2_4x2(&sh.KaS[0][rowi][ca], &sh.KaS[0][rowi][ca + 16], TC)
+                                       : ld2_4z(&sh.KaS[0][rowi][ca], TC);
+        acc = mm2_ss(a, e_pair(c2, (c2 + 1 < ct) ? c2 + 1 : NCT), acc);
+      }
+      float t8[8] = {acc[0], acc[1], acc[2], acc[3], 0.f, 0.f, 0.f, 0.f};
+      const Split2 a = ld2_4z(&sh.InvS[0][ct][li][4 * gq], TI);
+      E[ct] = mm2_ss(a, split2(t8), f4_zero());
+    }
+    if constexpr (FINAL) {
+      // Num = Phi(q) X_start^T + Qa E, then o = Num / den.
+      uint16_t *os = reinterpret_cast<uint16_t *>(out) + (s * T + c0) * D;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f4_t acc = f4_zero();
+#pragma unroll
+        for (int ksl = 0; ksl < NKS; ++ksl) {
+          const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
+          const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fb], TQ);
+          acc = mm2_ss(a, xs[ksl], acc);
+        }
+#pragma unroll
+        for (int c2 = 0; c2 <= ct; c2 += 2) {
+          const int rowi = 16 * ct + li, ca = 16 * c2 + 4 * gq;
+          const Split2 a = (c2 + 1 <= ct) ? ld2_4x2(&sh.QaS[0][rowi][ca], &sh.QaS[0][rowi][ca + 16], TQC)
+                                          : ld2_4z(&sh.QaS[0][rowi][ca], TQC);
+          acc = mm2_ss(a, e_pair(c2, (c2 + 1 <= ct) ? c2 + 1 : NCT), acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * ct + 4 * gq + r;
+          if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = f32_to_bf16(acc[r] * sh.rden[c]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one token tile at a time (bounded registers)
+      }
+    }
+    // X^T += Ahat^T E.
+#pragma unroll
+    for (int pr = 0; pr < NPR; ++pr) {
+      const int ta = 2 * pr, tbb = 2 * pr + 1;
+      const Split2 b = e_pair(ta, tbb);
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        const int fr = 16 * ft + li, ca = 16 * ta + 4 * gq;
+        const Split2 a = (tbb < NCT) ? ld2_4x2(&sh.sAt[0][fr][ca], &sh.sAt[0][fr][ca + 16], TA)
+                                     : ld2_4z(&sh.sAt[0][fr][ca], TA);
+        X[ft] = mm2_ss(a, b, X[ft]);
+      }
+    }
+  }
+
+  float *dst = nullptr;
+  if constexpr (FINAL) {
+    if (S_final != nullptr && p == P - 1) dst = S_final + s * D * D;
+  } else {
+    dst = pib + ((s * P + p) * 2 + (pi_rows ? 0 : 1)) * D * D;
+  }
+  if (dst != nullptr) {
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+      *reinterpret_cast<float4 *>(&dst[(rowbase + li) * D + 16 * ft + 4 * gq]) =
+          make_float4(X[ft][0], X[ft][1], X[ft][2], X[ft][3]);
+  }
+}
+
+}  // namespace vla
