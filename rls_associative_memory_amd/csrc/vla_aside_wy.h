@@ -44,8 +44,9 @@ struct AwyLds {
   uint16_t Zc[3][C::C / 8][D][8];        // token-packed Z0 / Z terms: [c/8][f][c%8]
   float G[C::C][C::C + 4];               // I + U A U^T (lower part used); then L^{-1} transposed
   uint16_t LX[3][C::C][C::LDL];          // L^{-1} terms (A operand), then X~ terms (B operand)
-  float piv[2][2][kWave] __attribute__((aligned(16)));  // pivot columns (double buffered)
   float rsd[C::C], rd[C::C];
+  float nbuf[2][D] __attribute__((aligned(16)));  // sum of phi(k) before the chunk
+  float dtmp[2][16];
   float norm[C::NW][C::C];
 };
 
@@ -81,31 +82,39 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
       for (int r = 0; r < 4; ++r) At[it][r] = a0[(16 * it + 4 * gq + r) * D + 16 * w + li];
   }
-  // Readout normaliser n (sum of phi(k) so far) for features lane and lane + 64; kept by
-  // every wave w >= 1, which compute the denominators while wave 0 factors G.
-  const bool hf0 = lane < D, hf1 = lane + 64 < D;
-  float nrun0 = hf0 ? nk0[(s * P + p) * D + lane] : 0.f;
-  float nrun1 = hf1 ? nk0[(s * P + p) * D + lane + 64] : 0.f;
+  // Readout normaliser n (sum of phi(k) before the chunk), double buffered in LDS: chunk
+  // number c reads nbuf[c & 1] and its update is written to nbuf[(c & 1) ^ 1].
+  for (int f = tid; f < D; f += NT) sh.nbuf[0][f] = nk0[(s * P + p) * D + f];
 
   // Staging: thread tid loads token tid / (D/8), features (tid % (D/8)) * 8 of u, k, q.
-  const int sc = tid / (D / 8), sf0 = (tid % (D / 8)) * 8;
+  // Rows past the segment are read as row 0 and zeroed when staged (no select on a load
+  // result, which would make the load wait at once); offsets are 32-bit from uniform bases.
   uint4 pv[3];
-  auto prefetch = [&](int64_t cs) {
-    const bool ok = cs + sc < te;
-    const int64_t off = (cs + sc) * D + sf0;
-    pv[0] = ok ? *reinterpret_cast<const uint4 *>(us + off) : make_uint4(0, 0, 0, 0);
-    pv[1] = ok ? *reinterpret_cast<const uint4 *>(ks + off) : make_uint4(0, 0, 0, 0);
-    pv[2] = ok ? *reinterpret_cast<const uint4 *>(qs + off) : make_uint4(0, 0, 0, 0);
+  auto prefetch = [&](int64_t cs, int tid) {
+    const int sc = tid / (D / 8), sf0 = (tid % (D / 8)) * 8;
+    const uint32_t off = (cs + sc < te) ? static_cast<uint32_t>(sc * D + sf0) : 0u;
+    pv[0] = *reinterpret_cast<const uint4 *>(us + cs * D + off);
+    pv[1] = *reinterpret_cast<const uint4 *>(ks + cs * D + off);
+    pv[2] = *reinterpret_cast<const uint4 *>(qs + cs * D + off);
   };
-  prefetch(tb);
+  prefetch(tb, tid);
 
   for (int64_t c0 = tb; c0 < te; c0 += CH) {
     const int m = static_cast<int>(std::min<int64_t>(CH, te - c0));
-    __syncthreads();
-    *reinterpret_cast<uint4 *>(&sh.sU[sc][sf0]) = pv[0];
-    *reinterpret_cast<uint4 *>(&sh.sK[sc][sf0]) = pv[1];
-    *reinterpret_cast<uint4 *>(&sh.sQ[sc][sf0]) = pv[2];
-    __syncthreads();
+    // Opaque per-chunk copies of the lane indices: the addresses derived from them are
+    // recomputed each chunk rather than hoisted out of the loop and kept (or spilled).
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, li = lane & 15, gq = lane >> 4;
+    {
+      const int sc = tid / (D / 8), sf0 = (tid % (D / 8)) * 8;
+      const bool ok = sc < m;
+      __syncthreads();
+      *reinterpret_cast<uint4 *>(&sh.sU[sc][sf0]) = keep_if(ok, pv[0]);
+      *reinterpret_cast<uint4 *>(&sh.sK[sc][sf0]) = keep_if(ok, pv[1]);
+      *reinterpret_cast<uint4 *>(&sh.sQ[sc][sf0]) = keep_if(ok, pv[2]);
+      __syncthreads();
+    }
 
     // ---- [Z0^T | P^T] = A [U^T | K^T] (rows 16w.., 32 tokens) ---------------------------
     f4_t Z0t[2], Pt[2];
@@ -170,14 +179,16 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // ---- wave 0: G = L D L^T and L^{-1};  waves >= 1: readout denominators ----------------
     if (w == 0) {
       // Lane i < 32 holds row i of G; lane 32 + m holds column m of L^{-1}, starting from the
-      // identity.  Pivots are taken two at a time (j, j + 1): with c0, c1 the columns j, j + 1
-      // of the partly eliminated G (published by the row lanes through LDS), g = c0[j + 1],
-      // d0 = c0[j], d1 = c1[j + 1] - g^2 / d0 and, from the lane's own x[j], x[j + 1],
-      //   x1 = x[j + 1] - (g / d0) x[j],   s2 = x1 / d1,   s1 = (x[j] - g s2) / d0,
-      // every lane applies x[r] -= s1 c0[r] + s2 c1[r] for r > j + 1 and sets x[j + 1] = x1.
-      // For a row of G this eliminates both pivots (s1, s2 are its multipliers up to the
-      // d factors); for a column of L^{-1} it is the forward substitution of rows j, j + 1.
-      // Only lower entries of G are read, so the upper tile may hold anything finite.
+      // identity.  Pivots go two at a time, j and j + 1, with the pivot columns broadcast
+      // from the row lanes through scalar registers (v_readlane): with d0 = G[j][j],
+      // g = G[j + 1][j], every lane first applies pivot j to its entry j + 1,
+      //   x[j + 1] -= (g / d0) x[j],
+      // which makes lane r's x[j + 1] the column j + 1 after pivot j (so d1 is lane j + 1's),
+      // and then both pivots to the entries r > j + 1:
+      //   x[r] -= (x[j] / d0) c0[r] + (x[j + 1] / d1) c1[r].
+      // For a row of G this is the elimination; for a column of L^{-1} it is the forward
+      // substitution L^{-1}[r][m] -= l_rj L^{-1}[j][m] of both pivots.  Only lower entries of
+      // G are read, so the upper tile may hold anything finite.
       const int i = lane & 31;
       const bool grow = lane < 32;
       float x[CH];
@@ -187,47 +198,23 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[4 * c4 + e] = grow ? gv[e] : (4 * c4 + e == i ? 1.f : 0.f);
       }
-      sh.piv[0][0][lane] = x[0];
-      sh.piv[0][1][lane] = x[1];
+      auto bcast = [](float v, int src) {
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+      };
       float myd = 1.f;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int jb = 0; jb < CH / 2; ++jb) {
-        const int j = 2 * jb, buf = jb & 1;
-        float c0[CH], c1[CH];
-#pragma unroll
-        for (int r4 = j / 4; r4 < CH / 4; ++r4) {
-          const f4_t a0 = *reinterpret_cast<const f4_t *>(&sh.piv[buf][0][4 * r4]);
-          const f4_t a1 = *reinterpret_cast<const f4_t *>(&sh.piv[buf][1][4 * r4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { c0[4 * r4 + e] = a0[e]; c1[4 * r4 + e] = a1[e]; }
-        }
-        const float d0 = c0[j], g = c0[j + 1];
+        const int j = 2 * jb;
+        const float d0 = bcast(x[j], j), g = bcast(x[j], j + 1);
         const float rd0 = __builtin_amdgcn_rcpf(d0);
-        const float gd = g * rd0;
-        const float d1 = fmaf(-g, gd, c1[j + 1]);
-        const float rd1 = __builtin_amdgcn_rcpf(d1);
-        const float x1 = fmaf(-gd, x[j], x[j + 1]);
-        const float s2 = x1 * rd1;
-        const float s1 = fmaf(-g, s2, x[j]) * rd0;
-        x[j + 1] = x1;
+        x[j + 1] = fmaf(-g * rd0, x[j], x[j + 1]);
+        const float d1 = bcast(x[j + 1], j + 1);
+        const float t1 = x[j] * rd0, t2 = x[j + 1] * __builtin_amdgcn_rcpf(d1);
         if (lane == j) myd = d0;
         if (lane == j + 1) myd = d1;
-        if (j + 2 < CH) {
 #pragma unroll
-          for (int r = j + 2; r < j + 4; ++r) x[r] = fmaf(-s2, c1[r], fmaf(-s1, c0[r], x[r]));
-          sh.piv[buf ^ 1][0][lane] = x[j + 2];  // lanes >= 32 fill unread slots
-          sh.piv[buf ^ 1][1][lane] = x[j + 3];
-#pragma unroll
-          for (int r = j + 4; r < CH; ++r) x[r] = fmaf(-s2, c1[r], fmaf(-s1, c0[r], x[r]));
-          // keep each pivot step's reads and updates together (bounded register use)
-          __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        for (int r = j + 2; r < CH; ++r)
+          x[r] = fmaf(-t2, bcast(x[j + 1], r), fmaf(-t1, bcast(x[j], r), x[r]));
       }
       // Pivots, and L^{-1} transposed into the (now free) G buffer: T[m][r] = L^{-1}[r][m].
       float(*Tb)[CH + 4] = sh.G;
@@ -260,37 +247,86 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         dst[1] = make_uint4(pk[t][4], pk[t][5], pk[t][6], pk[t][7]);
       }
     } else {
-      // Token c of the chunk is finished by wave 1 + c % (NW - 1): den_c = n_c . phi(q_c)
-      // with n_c = n_{c-1} + phi(k_c), and ||k_c||^2; every helper wave runs the prefix.
-      constexpr int NH = NW - 1;
-      const int hw = w - 1;
-      float n0 = nrun0, n1 = nrun1;
-      int own = hw;  // next token this wave finishes
-#pragma unroll 2
-      for (int c = 0; c < m; ++c) {
-        {
-          const float k0 = hf0 ? bf_val(sh.sK[c][lane]) : 0.f;
-          const float k1 = hf1 ? bf_val(sh.sK[c][lane + 64]) : 0.f;
-          n0 += hf0 ? phi(k0) : 0.f;
-          n1 += hf1 ? phi(k1) : 0.f;
-          if (c == own) {
-            own += NH;
-            const float q0 = hf0 ? phi(bf_val(sh.sQ[c][lane])) : 0.f;
-            const float q1 = hf1 ? phi(bf_val(sh.sQ[c][lane + 64])) : 0.f;
-            const float dsum = wave_sum(fmaf(n1, q1, n0 * q0));
-            const float kk = wave_sum(fmaf(k1, k1, k0 * k0));
-            if (lane == 0)
-              *reinterpret_cast<float2 *>(&rd[(c0 + c) * 2]) =
-                  make_float2(kk > 0.f ? rsqrtf(kk) : 0.f, dsum + eps);
+      // Readout denominators and key norms of the chunk, on the matrix cores of the waves
+      // that are otherwise idle here.  With M = phi(Q) phi(K)^T and n0 the sum of phi(k)
+      // before the chunk,  den_c = phi(q_c) . n0 + sum_{i <= c} M[c][i].  Jobs: token tile 0,
+      // token tile 1 (denominators and ||k||), then the 64-feature blocks of n's update.
+      constexpr int NH = NW - 1, NJ = 2 + (D + 63) / 64;
+      const int pc = static_cast<int>((c0 - tb) / CH) & 1;
+      const float *n0 = sh.nbuf[pc];
+      for (int job = w - 1; job < NJ; job += NH) {
+        if (job < 2) {
+          const int it = job;
+          f4_t macc[2] = {f4_zero(), f4_zero()};
+          float asum = 0.f, ksq = 0.f;
+#pragma unroll
+          for (int ksl = 0; ksl < C::NKS; ++ksl) {
+            const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
+            const bf16x8_t qr = ld_bf4x2(&sh.sQ[16 * it + li][fa], &sh.sQ[16 * it + li][fb]);
+            const f4_t na = *reinterpret_cast<const f4_t *>(&n0[fa]);
+            const f4_t nb = *reinterpret_cast<const f4_t *>(&n0[fb]);
+            float qv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              qv[e] = phi(static_cast<float>(qr[e]));
+              asum = fmaf(qv[e], e < 4 ? na[e] : nb[e - 4], asum);
+            }
+            const Split2 aq = split2(qv);
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              if (jt > it) continue;
+              const bf16x8_t kr = ld_bf4x2(&sh.sK[16 * jt + li][fa], &sh.sK[16 * jt + li][fb]);
+              float kv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float kf = static_cast<float>(kr[e]);
+                if (jt == it) ksq = fmaf(kf, kf, ksq);
+                kv[e] = phi(kf);
+              }
+              macc[jt] = mm2_ss(aq, split2(kv), macc[jt]);
+            }
+          }
+          // macc[jt][r] = M[16 it + 4 gq + r][16 jt + li]: masked sums over li (a lane row).
+          float rs[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * gq + r;
+            const float dg = it ? macc[1][r] : macc[0][r];  // diagonal tile
+            float v = (li <= i) ? dg : 0.f;
+            if (it == 1) v += macc[0][r];
+            v += dpp_xor1(v);
+            v += dpp_xor2(v);
+            v += dpp_half_mirror(v);
+            rs[r] = v + dpp_mirror(v);
+          }
+          // phi(q_c) . n0 and ||k_c||^2 of token 16 it + li: sums over the lane's gq copies.
+          asum += __shfl_xor(asum, 16);
+          asum += __shfl_xor(asum, 32);
+          ksq += __shfl_xor(ksq, 16);
+          ksq += __shfl_xor(ksq, 32);
+          if (li == 0)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sh.dtmp[it][4 * gq + r] = rs[r];
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int c = 16 * it + li;
+          if (gq == 0 && c < m)
+            *reinterpret_cast<float2 *>(&rd[(c0 + c) * 2]) =
+                make_float2(ksq > 0.f ? rsqrtf(ksq) : 0.f, asum + sh.dtmp[it][li] + eps);
+        } else {
+          const int f = 64 * (job - 2) + lane;
+          if (f < D) {
+            float sum = 0.f;
+            for (int c = 0; c < m; ++c) sum += phi(bf_val(sh.sK[c][f]));
+            sh.nbuf[pc ^ 1][f] = n0[f] + sum;
           }
         }
       }
-      nrun0 = n0;
-      nrun1 = n1;
     }
     __syncthreads();
     // next chunk's rows: issued here so the loads overlap the rest of this chunk
-    if (c0 + CH < te) prefetch(c0 + CH);
+    if (c0 + CH < te) prefetch(c0 + CH, tid);
     // ---- Z^T = Z0^T L^{-T} ---------------------------------------------------------------
     f4_t Zt[2];
 #pragma unroll
@@ -395,7 +431,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       for (int w2 = 0; w2 < NW; ++w2) tot += sh.norm[w2][c];
       const float inv = tot > 0.f ? rsqrtf(tot) : 0.f;
       if (c < m)
-        *reinterpret_cast<float4 *>(&al[(c0 + c) * D + 16 * w + 4 * gq]) =
+        *reinterpret_cast<float4 *>(&al[c0 * D + static_cast<uint32_t>(c * D + 16 * w + 4 * gq)]) =
             make_float4(Yt[ct][0] * inv, Yt[ct][1] * inv, Yt[ct][2] * inv, Yt[ct][3] * inv);
     }
     // ---- A <- A - W^T W on this wave's column tile ------------------------------------------

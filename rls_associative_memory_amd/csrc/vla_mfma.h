@@ -104,6 +104,11 @@ __device__ __forceinline__ void split1(float x, uint16_t &h, uint16_t &m, uint16
   l = bf_bits(static_cast<__bf16>(r2));
 }
 
+// v where ok, else zeros (component-wise, so the value stays in registers)
+__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &v) {
+  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+
 // ---- two-term split ----------------------------------------------------------------------
 struct Split2 {
   bf16x8_t h, l;

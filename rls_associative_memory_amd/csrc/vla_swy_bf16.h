@@ -18,11 +18,6 @@
 
 namespace vla {
 
-// v where ok, else zeros (component-wise, so the value stays in registers)
-__device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &v) {
-  return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
-}
-
 template <int D, int CH>
 struct SwbCfg {
   static constexpr int NWV = D / 16;          // waves = 16-row state slices per workgroup
