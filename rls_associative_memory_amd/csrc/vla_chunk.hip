@@ -1130,14 +1130,14 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
   }
   if constexpr (sizeof(TIn) == 2) {
     // bf16 inputs: S side on the bf16 matrix cores.
-    using SC = SwbCfg<D, CH>;
     if (P > 1) {
-      VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, P - 1, 2), dim3(SC::NT), 0, st, qq,
-                 kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
+      VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, P - 1),
+                 dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
+                 S_final, pl.T, pl.L, pl.P);
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
-    VLA_LAUNCH("k_swy_final", (k_swyb<D, CH, true>), dim3(S, P), dim3(SC::NT), 0, st, qq, kk, vv,
-               alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
+    VLA_LAUNCH("k_swy_final", (k_swyb<D, CH, true>), dim3(S, P), dim3(SwbCfg<D, CH, true>::NT), 0,
+               st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
   } else {
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),

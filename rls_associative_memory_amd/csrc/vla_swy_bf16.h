@@ -18,10 +18,14 @@
 
 namespace vla {
 
-template <int D, int CH>
+template <int D, int CH, bool FINAL>
 struct SwbCfg {
-  static constexpr int NWV = D / 16;          // waves = 16-row state slices per workgroup
-  static constexpr int NT = NWV * kWave;
+  static constexpr int NWV = D / 16;          // 16-row state slices
+  // The final pass runs one wave per slice; the segment-map pass runs the Pi rows (waves
+  // 0..NWV-1) and the B rows (waves NWV..2 NWV-1) of one segment in the same workgroup,
+  // which share the staged chunk, the Ka tiles and the block inverses.
+  static constexpr int NWT = FINAL ? NWV : 2 * NWV;
+  static constexpr int NT = NWT * kWave;
   static constexpr int NCT = CH / 16;         // 16-token tiles per chunk
   static constexpr int NPR = (NCT + 1) / 2;   // pairs of token tiles (one 32-token operand)
   static constexpr int NFT = D / 16;          // 16-feature tiles
@@ -35,7 +39,7 @@ struct SwbCfg {
 
 template <int D, int CH, bool FINAL>
 struct SwbLds {
-  using C = SwbCfg<D, CH>;
+  using C = SwbCfg<D, CH, FINAL>;
   static constexpr int QR = FINAL ? CH : 1;
   uint16_t sK[CH][C::LDF];                    // raw k, by token
   uint16_t sV[CH][C::LDF];                    // raw v, by token
@@ -45,18 +49,18 @@ struct SwbLds {
   uint16_t KaS[2][CH][C::LDC];                // -Ka terms, row-major
   uint16_t QaS[2][QR][C::LDC];                // Qa terms, row-major (final pass)
   uint16_t InvS[2][C::NCT][16][C::LDI];       // (I + Ka_bb)^{-1} terms, row-major
-  float Kd[C::NCT][16][17];                   // -Ka_bb in fp32 for the block inverses
+  float Kd[C::NCT][16][20];                   // -Ka_bb in fp32 for the block inverses
   float rk[CH];                               // 1 / ||k||
   float rden[CH];                             // 1 / readout denominator
 };
 
 template <int D, int CH, bool FINAL>
-__global__ void __launch_bounds__((SwbCfg<D, CH>::NT))
+__global__ void __launch_bounds__((SwbCfg<D, CH, FINAL>::NT))
 k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
        const float *__restrict__ alpha, const float *__restrict__ rkden,
        const float *__restrict__ s0, float *__restrict__ pib, bf16_t *__restrict__ out,
        float *__restrict__ S_final, int64_t T, int64_t L, int64_t P) {
-  using C = SwbCfg<D, CH>;
+  using C = SwbCfg<D, CH, FINAL>;
   constexpr int NT = C::NT, NCT = C::NCT, NPR = C::NPR, NFT = C::NFT, NKS = C::NKS;
   constexpr int TF = CH * C::LDF;             // term strides
   constexpr int TQ = SwbLds<D, CH, FINAL>::QR * C::LDF;
@@ -76,8 +80,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   const float *als = alpha + s * T * D;
   const float *rds = rkden + s * T * 2;
 
-  const bool pi_rows = !FINAL && blockIdx.z == 0;
-  const int rowbase = 16 * wave;
+  const bool pi_rows = !FINAL && wave < C::NWV;
+  const int rowbase = 16 * (wave % C::NWV);
   const bool has_v = FINAL || !pi_rows;
 
   // X[ft][r] = S[rowbase + li][16 ft + 4 gq + r]: a 16-row slice of S, transposed.
@@ -122,7 +126,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       const uint32_t off = (ui < UK && c < mm) ? static_cast<uint32_t>(c * D + f0) : 0u;
       pk[i] = *reinterpret_cast<const uint4 *>(kc + off);
       if constexpr (FINAL) pq[i] = *reinterpret_cast<const uint4 *>(qc + off);
-      pv[i] = *reinterpret_cast<const uint4 *>(vc + (has_v ? off : 0u));  // the Pi pass has no v
+      pv[i] = *reinterpret_cast<const uint4 *>(vc + off);
     }
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
@@ -151,7 +155,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       const int ui = tid + i * NT;
       if (ui < UK) {
         const int c = ui / RV, f0 = (ui % RV) * 8;
-        const bool okv = c < m && has_v;
+        const bool okv = c < m;
         *reinterpret_cast<uint4 *>(&sh.sK[c][f0]) = keep_if(c < m, pk[i]);
         *reinterpret_cast<uint4 *>(&sh.sV[c][f0]) = keep_if(okv, pv[i]);
         if constexpr (FINAL) {
@@ -201,32 +205,60 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     // ---- shared chunk products: -Ka = -(strict lower of Khat Ahat^T) and Qa = lower of
     //      Phi(q) Ahat^T, diagonal tiles first; each diagonal Ka tile's wave also inverts
     //      its unit-lower block ------------------------------------------------------------
-    for (int job = wave; job < (FINAL ? 2 : 1) * C::NKT; job += C::NWV) {
+    // Job j < NCT is a diagonal Ka tile plus its block inverse (the long ones): it goes to
+    // wave j; the other tiles are dealt out from the last wave down.
+    constexpr int NJOB = (FINAL ? 2 : 1) * C::NKT;
+    for (int job = 0; job < NJOB; ++job) {
+      const int owner = job < NCT ? job % C::NWT : C::NWT - 1 - (job - NCT) % C::NWT;
+      if (owner != wave) continue;
       const bool isq = job >= C::NKT;
       const int jj = isq ? job - C::NKT : job;
-      int ct, ct2;
-      if (jj < NCT) {
-        ct = ct2 = jj;
-      } else {
+      // tile (ct, ct2): the diagonal ones first, then the strictly lower ones row by row
+      int ct = jj, ct2 = jj;
+      if (jj >= NCT) {
         int t = jj - NCT;
         ct = 1;
-        while (t >= ct) { t -= ct; ++ct; }
+#pragma unroll
+        for (int r = 1; r < NCT; ++r)
+          if (t >= ct) { t -= ct; ++ct; }
         ct2 = t;
       }
-      f4_t acc = f4_zero();
+      ct = __builtin_amdgcn_readfirstlane(ct);
+      ct2 = __builtin_amdgcn_readfirstlane(ct2);
+      // Operands first, then one independent MFMA chain per feature slice.
+      f4_t acc;
+      {
+        Split2 b[NKS];
 #pragma unroll
-      for (int ksl = 0; ksl < NKS; ++ksl) {
-        const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
-        const Split2 b = ld2_4x2(&sh.sAh[0][16 * ct2 + li][fa], &sh.sAh[0][16 * ct2 + li][fb], TF);
+        for (int ksl = 0; ksl < NKS; ++ksl) {
+          const int fa = 32 * ksl + 4 * gq;
+          b[ksl] = ld2_4x2(&sh.sAh[0][16 * ct2 + li][fa], &sh.sAh[0][16 * ct2 + li][fa + 16], TF);
+        }
+        f4_t part[NKS];
         if (isq) {
           if constexpr (FINAL) {
-            const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fb], TQ);
-            acc = mm2_ss(a, b, acc);
+            Split2 a[NKS];
+#pragma unroll
+            for (int ksl = 0; ksl < NKS; ++ksl) {
+              const int fa = 32 * ksl + 4 * gq;
+              a[ksl] = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
+            }
+#pragma unroll
+            for (int ksl = 0; ksl < NKS; ++ksl) part[ksl] = mm2_ss(a[ksl], b[ksl], f4_zero());
           }
         } else {
-          const bf16x8_t a = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fb]);
-          acc = mm2_xs(a, b, acc);
+          bf16x8_t a[NKS];
+#pragma unroll
+          for (int ksl = 0; ksl < NKS; ++ksl) {
+            const int fa = 32 * ksl + 4 * gq;
+            a[ksl] = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fa + 16]);
+          }
+#pragma unroll
+          for (int ksl = 0; ksl < NKS; ++ksl) part[ksl] = mm2_xs(a[ksl], b[ksl], f4_zero());
         }
+        acc = part[0];
+#pragma unroll
+        for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
       }
       // acc[r] = product[c = 16 ct + 4 gq + r][c'' = 16 ct2 + li]
       const int cc = 16 * ct2 + li;
@@ -260,7 +292,12 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           for (int i = 0; i < 16; ++i) {
             float a = (i == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int i2 = 0; i2 < i; ++i2) a = fmaf(sh.Kd[b][i][i2], x[i2], a);  // Kd holds -Ka
+            for (int q4 = 0; q4 < i; q4 += 4) {
+              const f4_t kr = *reinterpret_cast<const f4_t *>(&sh.Kd[b][i][q4]);  // -Ka row
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (q4 + e < i) a = fmaf(kr[e], x[q4 + e], a);
+            }
             x[i] = a;
           }
 #pragma unroll
@@ -352,7 +389,6 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           const int c = 16 * ct + 4 * gq + r;
           if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = f32_to_bf16(acc[r] * sh.rden[c]);
         }
-        __builtin_amdgcn_sched_barrier(0);  // one token tile at a time (bounded registers)
       }
     }
     // X^T += Ahat^T E.
