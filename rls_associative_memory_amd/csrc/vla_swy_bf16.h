@@ -102,16 +102,17 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   }
 
   // Register prefetch of a chunk: 16-byte row pieces of k, q, v (features fastest) and
-  // float4 of ahat (tokens fastest, so the by-feature LDS writes are contiguous).  Loads
+  // float4 of ahat for two consecutive tokens (token pairs fastest, so the by-feature LDS
+  // writes are contiguous 32-bit words).  Loads
   // past the segment read row 0 instead and are zeroed when staged, so no load result is
   // selected on (which would make the load wait at once).
   constexpr int RV = D / 8;                   // uint4 per token row
   constexpr int UK = CH * RV;
-  constexpr int UA = CH * D / 4;
+  constexpr int UA = CH / 2 * D / 4;          // (token pair, 4 features) units of ahat
   constexpr int PK = (UK + NT - 1) / NT;
   constexpr int PA = (UA + NT - 1) / NT;
   uint4 pk[PK], pq[FINAL ? PK : 1], pv[PK];
-  float4 pa[PA];
+  float4 pa[PA][2];
   float prk = 0.f, pden = 1.f;
   // Per-lane offsets are 32-bit (one stream's rows span far less than 4 GiB) from a
   // workgroup-uniform base, so each load needs one offset register.
@@ -131,9 +132,12 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
       const int ui = tid + i * NT;
-      const int c = ui % CH, f0 = (ui / CH) * 4;
-      const uint32_t off = (ui < UA && c < mm) ? static_cast<uint32_t>(c * D + f0) : 0u;
-      pa[i] = *reinterpret_cast<const float4 *>(ac + off);
+      const int c = 2 * (ui % (CH / 2)), f0 = (ui / (CH / 2)) * 4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t off = (ui < UA && c + h < mm) ? static_cast<uint32_t>((c + h) * D + f0) : 0u;
+        pa[i][h] = *reinterpret_cast<const float4 *>(ac + off);
+      }
     }
     const uint32_t toff = (tid < mm) ? static_cast<uint32_t>(tid * 2) : 0u;
     prk = rc[toff];
@@ -179,21 +183,24 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     for (int i = 0; i < PA; ++i) {
       const int ui = tid + i * NT;
       if (ui < UA) {
-        const int c = ui % CH, f0 = (ui / CH) * 4;
-        const bool ok = c < m;
-        const float a4[4] = {ok ? pa[i].x : 0.f, ok ? pa[i].y : 0.f, ok ? pa[i].z : 0.f,
-                             ok ? pa[i].w : 0.f};
-        uint16_t h[4], l[4];
+        const int c = 2 * (ui % (CH / 2)), f0 = (ui / (CH / 2)) * 4;
+        uint16_t h[2][4], l[2][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split2_1(a4[e], h[e], l[e]);
-        *reinterpret_cast<uint2 *>(&sh.sAh[0][c][f0]) =
-            make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
-        *reinterpret_cast<uint2 *>(&sh.sAh[1][c][f0]) =
-            make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+        for (int t = 0; t < 2; ++t) {
+          const bool ok = c + t < m;
+          const float a4[4] = {ok ? pa[i][t].x : 0.f, ok ? pa[i][t].y : 0.f,
+                               ok ? pa[i][t].z : 0.f, ok ? pa[i][t].w : 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) split2_1(a4[e], h[t][e], l[t][e]);
+          *reinterpret_cast<uint2 *>(&sh.sAh[0][c + t][f0]) =
+              make_uint2(h[t][0] | (uint32_t(h[t][1]) << 16), h[t][2] | (uint32_t(h[t][3]) << 16));
+          *reinterpret_cast<uint2 *>(&sh.sAh[1][c + t][f0]) =
+              make_uint2(l[t][0] | (uint32_t(l[t][1]) << 16), l[t][2] | (uint32_t(l[t][3]) << 16));
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sh.sAt[0][f0 + e][c] = h[e];
-          sh.sAt[1][f0 + e][c] = l[e];
+          *reinterpret_cast<uint32_t *>(&sh.sAt[0][f0 + e][c]) = h[0][e] | (uint32_t(h[1][e]) << 16);
+          *reinterpret_cast<uint32_t *>(&sh.sAt[1][f0 + e][c]) = l[0][e] | (uint32_t(l[1][e]) << 16);
         }
       }
     }
@@ -341,15 +348,16 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     }
     // The next chunk's loads fly during the solve, the readout and the state update.
     if (c0 + CH < te) prefetch(c0 + CH, tid);
-    // E = (I + Ka)^{-1} R by block forward substitution (KaS holds -Ka).
-    auto e_pair = [&](int ta, int tbb) {  // two E tiles (tbb may be absent) as a B operand
-      float t8[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        t8[r] = E[ta][r];
-        t8[4 + r] = (tbb < NCT) ? E[tbb < NCT ? tbb : 0][r] : 0.f;
-      }
-      return split2(t8);
+    // E = (I + Ka)^{-1} R by block forward substitution (KaS holds -Ka).  Each finished E
+    // tile is split once into packed bf16 terms; pairs of tiles form B operands.
+    uint2 eh[NCT], el[NCT];
+    auto e_pair = [&](int ta, int tbb) {  // tiles ta and tbb (tbb >= NCT: zeros)
+      const bool two = tbb < NCT;
+      const int tb2 = two ? tbb : ta;
+      Split2 r;
+      r.h = __builtin_bit_cast(bf16x8_t, make_uint4(eh[ta].x, eh[ta].y, two ? eh[tb2].x : 0u, two ? eh[tb2].y : 0u));
+      r.l = __builtin_bit_cast(bf16x8_t, make_uint4(el[ta].x, el[ta].y, two ? el[tb2].x : 0u, two ? el[tb2].y : 0u));
+      return r;
     };
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -364,26 +372,35 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       float t8[8] = {acc[0], acc[1], acc[2], acc[3], 0.f, 0.f, 0.f, 0.f};
       const Split2 a = ld2_4z(&sh.InvS[0][ct][li][4 * gq], TI);
       E[ct] = mm2_ss(a, split2(t8), f4_zero());
+      uint16_t h[4], l[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) split2_1(E[ct][r], h[r], l[r]);
+      eh[ct] = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+      el[ct] = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
     }
     if constexpr (FINAL) {
       // Num = Phi(q) X_start^T + Qa E, then o = Num / den.
       uint16_t *os = reinterpret_cast<uint16_t *>(out) + (s * T + c0) * D;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        f4_t acc = f4_zero();
+        f4_t part[NKS + 1];  // independent chains: one per feature slice, one for Qa E
 #pragma unroll
         for (int ksl = 0; ksl < NKS; ++ksl) {
           const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
           const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fb], TQ);
-          acc = mm2_ss(a, xs[ksl], acc);
+          part[ksl] = mm2_ss(a, xs[ksl], f4_zero());
         }
+        part[NKS] = f4_zero();
 #pragma unroll
         for (int c2 = 0; c2 <= ct; c2 += 2) {
           const int rowi = 16 * ct + li, ca = 16 * c2 + 4 * gq;
           const Split2 a = (c2 + 1 <= ct) ? ld2_4x2(&sh.QaS[0][rowi][ca], &sh.QaS[0][rowi][ca + 16], TQC)
                                           : ld2_4z(&sh.QaS[0][rowi][ca], TQC);
-          acc = mm2_ss(a, e_pair(c2, (c2 + 1 <= ct) ? c2 + 1 : NCT), acc);
+          part[NKS] = mm2_ss(a, e_pair(c2, (c2 + 1 <= ct) ? c2 + 1 : NCT), part[NKS]);
         }
+        f4_t acc = part[0];
+#pragma unroll
+        for (int i = 1; i <= NKS; ++i) acc += part[i];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * gq + r;
