@@ -61,6 +61,39 @@ def bytes_per_token_head(d: int, elem: int) -> int:
     return 5 * d * elem  # q, k, v, u read; out written
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = os.path.join(ROOT, "rls_associative_memory_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    """Digest of the HIP sources; a stored counter reading is used only while it matches."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary of this workload (profiles/traffic_<workload>.md, lines starting "traffic:"),
+    scaled by the copy-kernel calibration stored with it; None if absent or stale."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    src = kernel_source_hash()
+    with open(path) as f:
+        for line in f:
+            if not line.startswith("traffic:"):
+                continue
+            rec = json.loads(line[len("traffic:"):])
+            if rec.get("kernel") == kernel and rec.get("source_hash") == src:
+                return (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,7 +102,7 @@ def parse():
     ap.add_argument("--workload", default="long_t131072_d96")
     ap.add_argument("--path", default="auto", choices=["auto", "seq", "chunk"])
     ap.add_argument("--chunk", type=int, default=-1, help="chunk length (-1: the workload's)")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per stream in the oracle sample (0 disables the CPU leg)")
     ap.add_argument("--cpu-cores", type=int, default=16)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -211,7 +244,7 @@ def main():
         "peak": PEAK_FP32_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-        "traffic": None,
+        "traffic": stored_traffic(w.name, dom_name),
         "kernel": dom_name,
         "kernel_ms": round(kernel_ms, 4),
         "path_achieved": round(path_tflops, 3),
