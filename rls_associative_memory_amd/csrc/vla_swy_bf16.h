@@ -1,16 +1,20 @@
 // S side of the chunked path on the bf16 matrix cores (bf16 inputs).
 //
-// Same chunk algebra as the fp32 kernel (UT/WY form of the residual update S <- S +
-// (v - S khat) ahat^T over CH tokens, VLA summary §2.3 steps 3-4, and the ratio readout of
-// §2.4): with Ka = strict lower part of Khat Ahat^T and Qa = lower part of Phi(q) Ahat^T,
-//   R   = V - Khat X^T                        (X^T: this workgroup's 16-row state slice)
-//   E   = (I + Ka)^{-1} R                     (block forward substitution, 16-token blocks)
-//   Num = Phi(q) X^T + Qa E,   o = Num / den  (final pass only)
-//   X^T += Ahat^T E
-// Every product runs on v_mfma_f32_16x16x32_bf16.  Raw k and v are exact bf16; khat =
-// rk * k is applied after the product.  ahat, phi(q), the state, Ka, Qa and E are fp32 values
-// split into two bf16 terms (hi + lo, about 16 significant bits) and multiplied term pair by
-// term pair with fp32 accumulation, which keeps each product's relative error near 2^-16.
+// The residual update S <- S + (v - S khat) ahat^T (VLA summary §2.3 steps 3-4) and the
+// ratio readout (§2.4) over a chunk of CH tokens, in UT/WY form with a left-looking block
+// solve over 16-token tiles b = 0, 1, ..: with X^T the state slice before tile b, Ka_b the
+// strict lower part of Khat_b Ahat_b^T and Qa_b the lower part of Phi(q)_b Ahat_b^T,
+//   R   = V_b - Khat_b X^T
+//   E   = (I + Ka_b)^{-1} R
+//   Num = Phi(q)_b X^T + Qa_b E,   o = Num / den   (final pass only)
+//   X^T += Ahat_b^T E
+// which is the block forward substitution of the chunk's (I + Ka) E = R with the
+// off-diagonal blocks applied through the updated state.  Only the diagonal tiles of Ka and
+// Qa, and the inverses of I + Ka_b, are shared by the workgroup's waves.  Every product runs
+// on v_mfma_f32_16x16x32_bf16.  Raw k and v are exact bf16; khat = rk * k is applied after
+// the product.  ahat, phi(q), the state, Ka, Qa and E are fp32 values split into two bf16
+// terms (hi + lo, about 16 significant bits) multiplied term pair by term pair with fp32
+// accumulation, which keeps each product's relative error near 2^-16.
 #pragma once
 
 #include "vla_common.h"
@@ -27,7 +31,6 @@ struct SwbCfg {
   static constexpr int NWT = FINAL ? NWV : 2 * NWV;
   static constexpr int NT = NWT * kWave;
   static constexpr int NCT = CH / 16;         // 16-token tiles per chunk
-  static constexpr int NPR = (NCT + 1) / 2;   // pairs of token tiles (one 32-token operand)
   static constexpr int NFT = D / 16;          // 16-feature tiles
   static constexpr int NKS = D / 32;          // 32-feature slices
   static constexpr int NKT = NCT * (NCT + 1) / 2;
@@ -46,10 +49,9 @@ struct SwbLds {
   uint16_t sAh[2][CH][C::LDF];                // ahat terms, by token
   uint16_t sAt[2][D][C::LDC];                 // ahat terms, by feature
   uint16_t sFq[2][QR][C::LDF];                // phi(q) terms, by token (final pass)
-  uint16_t KaS[2][CH][C::LDC];                // -Ka terms, row-major
-  uint16_t QaS[2][QR][C::LDC];                // Qa terms, row-major (final pass)
-  uint16_t InvS[2][C::NCT][16][C::LDI];       // (I + Ka_bb)^{-1} terms, row-major
-  float Kd[C::NCT][16][20];                   // -Ka_bb in fp32 for the block inverses
+  uint16_t InvS[2][C::NCT][16][C::LDI];       // (I + Ka_b)^{-1} terms, row-major
+  uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_b terms, row-major (final pass)
+  float Kd[C::NCT][16][20];                   // -Ka_b in fp32 for the block inverses
   float rk[CH];                               // 1 / ||k||
   float rden[CH];                             // 1 / readout denominator
 };
@@ -61,12 +63,11 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
        const float *__restrict__ s0, float *__restrict__ pib, bf16_t *__restrict__ out,
        float *__restrict__ S_final, int64_t T, int64_t L, int64_t P) {
   using C = SwbCfg<D, CH, FINAL>;
-  constexpr int NT = C::NT, NCT = C::NCT, NPR = C::NPR, NFT = C::NFT, NKS = C::NKS;
+  constexpr int NT = C::NT, NCT = C::NCT, NFT = C::NFT, NKS = C::NKS;
   constexpr int TF = CH * C::LDF;             // term strides
   constexpr int TQ = SwbLds<D, CH, FINAL>::QR * C::LDF;
   constexpr int TA = D * C::LDC;
-  constexpr int TC = CH * C::LDC;
-  constexpr int TQC = SwbLds<D, CH, FINAL>::QR * C::LDC;
+  constexpr int TQD = (FINAL ? NCT : 1) * 16 * C::LDI;
   constexpr int TI = NCT * 16 * C::LDI;
   __shared__ __attribute__((aligned(16))) SwbLds<D, CH, FINAL> sh;
 
@@ -209,29 +210,12 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       if constexpr (FINAL) sh.rden[tid] = tid < m ? 1.0f / pden : 0.f;
     }
     __syncthreads();
-    // ---- shared chunk products: -Ka = -(strict lower of Khat Ahat^T) and Qa = lower of
-    //      Phi(q) Ahat^T, diagonal tiles first; each diagonal Ka tile's wave also inverts
-    //      its unit-lower block ------------------------------------------------------------
-    // Job j < NCT is a diagonal Ka tile plus its block inverse (the long ones): it goes to
-    // wave j; the other tiles are dealt out from the last wave down.
-    constexpr int NJOB = (FINAL ? 2 : 1) * C::NKT;
-    for (int job = 0; job < NJOB; ++job) {
-      const int owner = job < NCT ? job % C::NWT : C::NWT - 1 - (job - NCT) % C::NWT;
-      if (owner != wave) continue;
-      const bool isq = job >= C::NKT;
-      const int jj = isq ? job - C::NKT : job;
-      // tile (ct, ct2): the diagonal ones first, then the strictly lower ones row by row
-      int ct = jj, ct2 = jj;
-      if (jj >= NCT) {
-        int t = jj - NCT;
-        ct = 1;
-#pragma unroll
-        for (int r = 1; r < NCT; ++r)
-          if (t >= ct) { t -= ct; ++ct; }
-        ct2 = t;
-      }
-      ct = __builtin_amdgcn_readfirstlane(ct);
-      ct2 = __builtin_amdgcn_readfirstlane(ct2);
+    // ---- shared tile products: diagonal tiles of -Ka (each with the inverse of I + Ka_b)
+    //      and, in the final pass, of Qa ---------------------------------------------------
+    constexpr int NJOB = (FINAL ? 2 : 1) * NCT;
+    for (int job = wave; job < NJOB; job += C::NWT) {
+      const bool isq = job >= NCT;
+      const int ct = isq ? job - NCT : job;
       // Operands first, then one independent MFMA chain per feature slice.
       f4_t acc;
       {
@@ -239,7 +223,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
         for (int ksl = 0; ksl < NKS; ++ksl) {
           const int fa = 32 * ksl + 4 * gq;
-          b[ksl] = ld2_4x2(&sh.sAh[0][16 * ct2 + li][fa], &sh.sAh[0][16 * ct2 + li][fa + 16], TF);
+          b[ksl] = ld2_4x2(&sh.sAh[0][16 * ct + li][fa], &sh.sAh[0][16 * ct + li][fa + 16], TF);
         }
         f4_t part[NKS];
         if (isq) {
@@ -267,40 +251,35 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
         for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
       }
-      // acc[r] = product[c = 16 ct + 4 gq + r][c'' = 16 ct2 + li]
-      const int cc = 16 * ct2 + li;
+      // acc[r] = product[i = 4 gq + r][i'' = li] within tile ct
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 4 * gq + r, row = 16 * ct + i;
-        float val = isq ? acc[r] : -acc[r] * sh.rk[row];
-        if (ct == ct2 && (isq ? (li > i) : (li >= i))) val = 0.f;
-        uint16_t h, l;
-        split2_1(val, h, l);
+        const int i = 4 * gq + r;
         if (isq) {
           if constexpr (FINAL) {
-            sh.QaS[0][row][cc] = h;
-            sh.QaS[1][row][cc] = l;
+            uint16_t h, l;
+            split2_1(li > i ? 0.f : acc[r], h, l);
+            sh.QaD[0][ct][i][li] = h;
+            sh.QaD[1][ct][i][li] = l;
           }
         } else {
-          sh.KaS[0][row][cc] = h;
-          sh.KaS[1][row][cc] = l;
-          if (ct == ct2) sh.Kd[ct][i][li] = val;
+          sh.Kd[ct][i][li] = li >= i ? 0.f : -acc[r] * sh.rk[16 * ct + i];
         }
       }
-      if (!isq && ct == ct2) {
-        // (I + Ka_bb)^{-1} by forward substitution in lanes 0..15 (column j = lane).
+      if (!isq) {
+        // (I + Ka_b)^{-1} by forward substitution in lanes 0..15 (column j = lane).
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (lane < 16) {
-          const int b = ct, j = lane;
+          const int j = lane;
           float x[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             float a = (i == j) ? 1.f : 0.f;
 #pragma unroll
             for (int q4 = 0; q4 < i; q4 += 4) {
-              const f4_t kr = *reinterpret_cast<const f4_t *>(&sh.Kd[b][i][q4]);  // -Ka row
+              const f4_t kr = *reinterpret_cast<const f4_t *>(&sh.Kd[ct][i][q4]);  // -Ka row
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 if (q4 + e < i) a = fmaf(kr[e], x[q4 + e], a);
@@ -311,115 +290,75 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           for (int i = 0; i < 16; ++i) {
             uint16_t h, l;
             split2_1(x[i], h, l);
-            sh.InvS[0][b][i][j] = h;
-            sh.InvS[1][b][i][j] = l;
+            sh.InvS[0][ct][i][j] = h;
+            sh.InvS[1][ct][i][j] = l;
           }
         }
       }
     }
     __syncthreads();
-    // ---- this wave's rows ---------------------------------------------------------------
-    // The state slice as the B operand of products over features (two tiles per operand).
-    Split2 xs[NKS];
-#pragma unroll
-    for (int ksl = 0; ksl < NKS; ++ksl) {
-      float t8[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) { t8[r] = X[2 * ksl][r]; t8[4 + r] = X[2 * ksl + 1][r]; }
-      xs[ksl] = split2(t8);
-    }
-    // R = V - rk (K X^T)
-    f4_t E[NCT];
+    // ---- this wave's rows: tile by tile ------------------------------------------------
+    // The next chunk's loads fly during the tiles.
+    if (c0 + CH < te) prefetch(c0 + CH, tid);
+    uint16_t *os = reinterpret_cast<uint16_t *>(out) + (s * T + c0) * D;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      f4_t acc = f4_zero();
+      // The state slice before this tile as the B operand of products over features.
+      Split2 xs[NKS];
 #pragma unroll
       for (int ksl = 0; ksl < NKS; ++ksl) {
-        const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
-        const bf16x8_t a = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fb]);
-        acc = mm2_xs(a, xs[ksl], acc);
+        float t8[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { t8[r] = X[2 * ksl][r]; t8[4 + r] = X[2 * ksl + 1][r]; }
+        xs[ksl] = split2(t8);
       }
+      // R = V - rk (K X^T)
+      f4_t part[NKS];
+#pragma unroll
+      for (int ksl = 0; ksl < NKS; ++ksl) {
+        const int fa = 32 * ksl + 4 * gq;
+        const bf16x8_t a = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fa + 16]);
+        part[ksl] = mm2_xs(a, xs[ksl], f4_zero());
+      }
+      f4_t acc = part[0];
+#pragma unroll
+      for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
+      float t8[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = 16 * ct + 4 * gq + r;
         const float vv = has_v ? bf_val(sh.sV[c][rowbase + li]) : 0.f;
-        E[ct][r] = fmaf(-sh.rk[c], acc[r], vv);
+        t8[r] = fmaf(-sh.rk[c], acc[r], vv);
+        t8[4 + r] = 0.f;
       }
-    }
-    // The next chunk's loads fly during the solve, the readout and the state update.
-    if (c0 + CH < te) prefetch(c0 + CH, tid);
-    // E = (I + Ka)^{-1} R by block forward substitution (KaS holds -Ka).  Each finished E
-    // tile is split once into packed bf16 terms; pairs of tiles form B operands.
-    uint2 eh[NCT], el[NCT];
-    auto e_pair = [&](int ta, int tbb) {  // tiles ta and tbb (tbb >= NCT: zeros)
-      const bool two = tbb < NCT;
-      const int tb2 = two ? tbb : ta;
-      Split2 r;
-      r.h = __builtin_bit_cast(bf16x8_t, make_uint4(eh[ta].x, eh[ta].y, two ? eh[tb2].x : 0u, two ? eh[tb2].y : 0u));
-      r.l = __builtin_bit_cast(bf16x8_t, make_uint4(el[ta].x, el[ta].y, two ? el[tb2].x : 0u, two ? el[tb2].y : 0u));
-      return r;
-    };
+      // E = (I + Ka_b)^{-1} R
+      const f4_t E = mm2_ss(ld2_4z(&sh.InvS[0][ct][li][4 * gq], TI), split2(t8), f4_zero());
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f4_t acc = E[ct];
-#pragma unroll
-      for (int c2 = 0; c2 < ct; c2 += 2) {
-        const int rowi = 16 * ct + li, ca = 16 * c2 + 4 * gq;
-        const Split2 a = (c2 + 1 < ct) ? ld2_4x2(&sh.KaS[0][rowi][ca], &sh.KaS[0][rowi][ca + 16], TC)
-                                       : ld2_4z(&sh.KaS[0][rowi][ca], TC);
-        acc = mm2_ss(a, e_pair(c2, (c2 + 1 < ct) ? c2 + 1 : NCT), acc);
-      }
-      float t8[8] = {acc[0], acc[1], acc[2], acc[3], 0.f, 0.f, 0.f, 0.f};
-      const Split2 a = ld2_4z(&sh.InvS[0][ct][li][4 * gq], TI);
-      E[ct] = mm2_ss(a, split2(t8), f4_zero());
-      uint16_t h[4], l[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) split2_1(E[ct][r], h[r], l[r]);
-      eh[ct] = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
-      el[ct] = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
-    }
-    if constexpr (FINAL) {
-      // Num = Phi(q) X_start^T + Qa E, then o = Num / den.
-      uint16_t *os = reinterpret_cast<uint16_t *>(out) + (s * T + c0) * D;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f4_t part[NKS + 1];  // independent chains: one per feature slice, one for Qa E
+      for (int r = 0; r < 4; ++r) { t8[r] = E[r]; t8[4 + r] = 0.f; }
+      const Split2 es = split2(t8);
+      if constexpr (FINAL) {
+        // Num = Phi(q)_b X^T + Qa_b E, then o = Num / den.
+        f4_t pq2[NKS + 1];
 #pragma unroll
         for (int ksl = 0; ksl < NKS; ++ksl) {
-          const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
-          const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fb], TQ);
-          part[ksl] = mm2_ss(a, xs[ksl], f4_zero());
+          const int fa = 32 * ksl + 4 * gq;
+          const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
+          pq2[ksl] = mm2_ss(a, xs[ksl], f4_zero());
         }
-        part[NKS] = f4_zero();
+        pq2[NKS] = mm2_ss(ld2_4z(&sh.QaD[0][ct][li][4 * gq], TQD), es, f4_zero());
+        f4_t num = pq2[0];
 #pragma unroll
-        for (int c2 = 0; c2 <= ct; c2 += 2) {
-          const int rowi = 16 * ct + li, ca = 16 * c2 + 4 * gq;
-          const Split2 a = (c2 + 1 <= ct) ? ld2_4x2(&sh.QaS[0][rowi][ca], &sh.QaS[0][rowi][ca + 16], TQC)
-                                          : ld2_4z(&sh.QaS[0][rowi][ca], TQC);
-          part[NKS] = mm2_ss(a, e_pair(c2, (c2 + 1 <= ct) ? c2 + 1 : NCT), part[NKS]);
-        }
-        f4_t acc = part[0];
-#pragma unroll
-        for (int i = 1; i <= NKS; ++i) acc += part[i];
+        for (int i = 1; i <= NKS; ++i) num += pq2[i];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * gq + r;
-          if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = f32_to_bf16(acc[r] * sh.rden[c]);
+          if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = f32_to_bf16(num[r] * sh.rden[c]);
         }
       }
-    }
-    // X^T += Ahat^T E.
+      // X^T += Ahat_b^T E
 #pragma unroll
-    for (int pr = 0; pr < NPR; ++pr) {
-      const int ta = 2 * pr, tbb = 2 * pr + 1;
-      const Split2 b = e_pair(ta, tbb);
-#pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        const int fr = 16 * ft + li, ca = 16 * ta + 4 * gq;
-        const Split2 a = (tbb < NCT) ? ld2_4x2(&sh.sAt[0][fr][ca], &sh.sAt[0][fr][ca + 16], TA)
-                                     : ld2_4z(&sh.sAt[0][fr][ca], TA);
-        X[ft] = mm2_ss(a, b, X[ft]);
-      }
+      for (int ft = 0; ft < NFT; ++ft)
+        X[ft] = mm2_ss(ld2_4z(&sh.sAt[0][16 * ft + li][16 * ct + 4 * gq], TA), es, X[ft]);
     }
   }
 
