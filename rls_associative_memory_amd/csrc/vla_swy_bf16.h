@@ -1,19 +1,20 @@
 // S side of the chunked path on the bf16 matrix cores (bf16 inputs).
 //
 // The residual update S <- S + (v - S khat) ahat^T (VLA summary §2.3 steps 3-4) and the
-// ratio readout (§2.4) over a chunk of CH tokens, in UT/WY form with a left-looking block
-// solve over 16-token tiles b = 0, 1, ..: with X^T the state slice before tile b, Ka_b the
-// strict lower part of Khat_b Ahat_b^T and Qa_b the lower part of Phi(q)_b Ahat_b^T,
-//   R   = V_b - Khat_b X^T
-//   E   = (I + Ka_b)^{-1} R
-//   Num = Phi(q)_b X^T + Qa_b E,   o = Num / den   (final pass only)
-//   X^T += Ahat_b^T E
-// which is the block forward substitution of the chunk's (I + Ka) E = R with the
-// off-diagonal blocks applied through the updated state.  Only the diagonal tiles of Ka and
-// Qa, and the inverses of I + Ka_b, are shared by the workgroup's waves.  Every product runs
-// on v_mfma_f32_16x16x32_bf16.  Raw k and v are exact bf16; khat = rk * k is applied after
-// the product.  ahat, phi(q), the state, Ka, Qa and E are fp32 values split into two bf16
-// terms (hi + lo, about 16 significant bits) multiplied term pair by term pair with fp32
+// ratio readout (§2.4) over a chunk of CH tokens, in UT/WY form.  The chunk's triangular
+// system (I + Ka) E = R, Ka the strict lower part of Khat Ahat^T, is solved left-looking in
+// steps of two 16-token tiles (a, b): with X^T the state slice before the step,
+//   R_t = V_t - Khat_t X^T                       (t = a, b)
+//   E_a = (I + Ka_aa)^{-1} R_a
+//   E_b = (I + Ka_bb)^{-1} (R_b - Ka_ba E_a)
+//   Num_t = Phi(q)_t X^T + sum_{t' <= t} Qa_tt' E_t',  o = Num / den   (final pass only)
+//   X^T += Ahat_a^T E_a + Ahat_b^T E_b
+// (Qa the lower part of Phi(q) Ahat^T); blocks further below the diagonal act through the
+// updated state.  The workgroup's waves share only the tiles Ka_aa, Ka_ba, Ka_bb (with the
+// inverses of I + Ka_tt) and the matching Qa tiles.  Every product runs on
+// v_mfma_f32_16x16x32_bf16.  Raw k and v are exact bf16; khat = rk * k is applied after the
+// product.  ahat, phi(q), the state, Ka, Qa and E are fp32 values split into two bf16 terms
+// (hi + lo, about 16 significant bits) multiplied term pair by term pair with fp32
 // accumulation, which keeps each product's relative error near 2^-16.
 #pragma once
 
@@ -31,6 +32,8 @@ struct SwbCfg {
   static constexpr int NWT = FINAL ? NWV : 2 * NWV;
   static constexpr int NT = NWT * kWave;
   static constexpr int NCT = CH / 16;         // 16-token tiles per chunk
+  static constexpr int NPR = (NCT + 1) / 2;   // steps of two tiles
+  static constexpr int NOD = NCT / 2;         // steps with both tiles (one off-diagonal tile)
   static constexpr int NFT = D / 16;          // 16-feature tiles
   static constexpr int NKS = D / 32;          // 32-feature slices
   static constexpr int NKT = NCT * (NCT + 1) / 2;
@@ -50,7 +53,9 @@ struct SwbLds {
   uint16_t sAt[2][D][C::LDC];                 // ahat terms, by feature
   uint16_t sFq[2][QR][C::LDF];                // phi(q) terms, by token (final pass)
   uint16_t InvS[2][C::NCT][16][C::LDI];       // (I + Ka_b)^{-1} terms, row-major
-  uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_b terms, row-major (final pass)
+  uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_tt terms, row-major (final pass)
+  uint16_t KaO[2][C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // -Ka_ba terms of each step
+  uint16_t QaO[2][FINAL && C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // Qa_ba terms (final pass)
   float Kd[C::NCT][16][20];                   // -Ka_b in fp32 for the block inverses
   float rk[CH];                               // 1 / ||k||
   float rden[CH];                             // 1 / readout denominator
@@ -68,6 +73,9 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   constexpr int TQ = SwbLds<D, CH, FINAL>::QR * C::LDF;
   constexpr int TA = D * C::LDC;
   constexpr int TQD = (FINAL ? NCT : 1) * 16 * C::LDI;
+  constexpr int NOD = C::NOD, NPR = C::NPR;
+  constexpr int TKO = (NOD > 0 ? NOD : 1) * 16 * C::LDI;
+  constexpr int TQO = (FINAL && NOD > 0 ? NOD : 1) * 16 * C::LDI;
   constexpr int TI = NCT * 16 * C::LDI;
   __shared__ __attribute__((aligned(16))) SwbLds<D, CH, FINAL> sh;
 
@@ -210,12 +218,17 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       if constexpr (FINAL) sh.rden[tid] = tid < m ? 1.0f / pden : 0.f;
     }
     __syncthreads();
-    // ---- shared tile products: diagonal tiles of -Ka (each with the inverse of I + Ka_b)
-    //      and, in the final pass, of Qa ---------------------------------------------------
-    constexpr int NJOB = (FINAL ? 2 : 1) * NCT;
+    // ---- shared tile products: Ka_tt (each with the inverse of I + Ka_tt), Ka_ba and, in
+    //      the final pass, Qa_tt and Qa_ba --------------------------------------------------
+    //      jobs: [0, NCT) Ka_tt, [NCT, NCT + NOD) Ka_ba, then Qa_tt, Qa_ba
+    constexpr int NKJ = NCT + NOD;
+    constexpr int NJOB = (FINAL ? 2 : 1) * NKJ;
     for (int job = wave; job < NJOB; job += C::NWT) {
-      const bool isq = job >= NCT;
-      const int ct = isq ? job - NCT : job;
+      const bool isq = job >= NKJ;
+      const int jk = isq ? job - NKJ : job;
+      const bool diag = jk < NCT;
+      const int ct = diag ? jk : 2 * (jk - NCT) + 1;   // row tile
+      const int ct2 = diag ? jk : 2 * (jk - NCT);      // column tile
       // Operands first, then one independent MFMA chain per feature slice.
       f4_t acc;
       {
@@ -223,7 +236,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
         for (int ksl = 0; ksl < NKS; ++ksl) {
           const int fa = 32 * ksl + 4 * gq;
-          b[ksl] = ld2_4x2(&sh.sAh[0][16 * ct + li][fa], &sh.sAh[0][16 * ct + li][fa + 16], TF);
+          b[ksl] = ld2_4x2(&sh.sAh[0][16 * ct2 + li][fa], &sh.sAh[0][16 * ct2 + li][fa + 16], TF);
         }
         f4_t part[NKS];
         if (isq) {
@@ -251,22 +264,35 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
         for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
       }
-      // acc[r] = product[i = 4 gq + r][i'' = li] within tile ct
+      // acc[r] = product[i = 4 gq + r][i'' = li] of tile (ct, ct2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * gq + r;
         if (isq) {
           if constexpr (FINAL) {
             uint16_t h, l;
-            split2_1(li > i ? 0.f : acc[r], h, l);
-            sh.QaD[0][ct][i][li] = h;
-            sh.QaD[1][ct][i][li] = l;
+            split2_1(diag && li > i ? 0.f : acc[r], h, l);
+            if (diag) {
+              sh.QaD[0][ct][i][li] = h;
+              sh.QaD[1][ct][i][li] = l;
+            } else {
+              sh.QaO[0][jk - NCT][i][li] = h;
+              sh.QaO[1][jk - NCT][i][li] = l;
+            }
           }
         } else {
-          sh.Kd[ct][i][li] = li >= i ? 0.f : -acc[r] * sh.rk[16 * ct + i];
+          const float nk = -acc[r] * sh.rk[16 * ct + i];
+          if (diag) {
+            sh.Kd[ct][i][li] = li >= i ? 0.f : nk;
+          } else {
+            uint16_t h, l;
+            split2_1(nk, h, l);
+            sh.KaO[0][jk - NCT][i][li] = h;
+            sh.KaO[1][jk - NCT][i][li] = l;
+          }
         }
       }
-      if (!isq) {
+      if (!isq && diag) {
         // (I + Ka_b)^{-1} by forward substitution in lanes 0..15 (column j = lane).
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -297,13 +323,19 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       }
     }
     __syncthreads();
-    // ---- this wave's rows: tile by tile ------------------------------------------------
-    // The next chunk's loads fly during the tiles.
+    // ---- this wave's rows: two tiles per step ---------------------------------------------
+    // The next chunk's loads fly during the steps.
     if (c0 + CH < te) prefetch(c0 + CH, tid);
     uint16_t *os = reinterpret_cast<uint16_t *>(out) + (s * T + c0) * D;
+    auto split4 = [](const f4_t &v) {  // one D-layout tile as a B operand (upper half zero)
+      float t8[8] = {v[0], v[1], v[2], v[3], 0.f, 0.f, 0.f, 0.f};
+      return split2(t8);
+    };
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      // The state slice before this tile as the B operand of products over features.
+    for (int pr = 0; pr < NPR; ++pr) {
+      const int ta = 2 * pr, tbb = 2 * pr + 1;
+      const bool two = tbb < NCT;
+      // The state slice before this step as the B operand of products over features.
       Split2 xs[NKS];
 #pragma unroll
       for (int ksl = 0; ksl < NKS; ++ksl) {
@@ -312,53 +344,79 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         for (int r = 0; r < 4; ++r) { t8[r] = X[2 * ksl][r]; t8[4 + r] = X[2 * ksl + 1][r]; }
         xs[ksl] = split2(t8);
       }
-      // R = V - rk (K X^T)
-      f4_t part[NKS];
+      // R_t = V_t - rk (K_t X^T), t = a, b
+      f4_t R[2];
 #pragma unroll
-      for (int ksl = 0; ksl < NKS; ++ksl) {
-        const int fa = 32 * ksl + 4 * gq;
-        const bf16x8_t a = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fa + 16]);
-        part[ksl] = mm2_xs(a, xs[ksl], f4_zero());
-      }
-      f4_t acc = part[0];
-#pragma unroll
-      for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
-      float t8[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 16 * ct + 4 * gq + r;
-        const float vv = has_v ? bf_val(sh.sV[c][rowbase + li]) : 0.f;
-        t8[r] = fmaf(-sh.rk[c], acc[r], vv);
-        t8[4 + r] = 0.f;
-      }
-      // E = (I + Ka_b)^{-1} R
-      const f4_t E = mm2_ss(ld2_4z(&sh.InvS[0][ct][li][4 * gq], TI), split2(t8), f4_zero());
-#pragma unroll
-      for (int r = 0; r < 4; ++r) { t8[r] = E[r]; t8[4 + r] = 0.f; }
-      const Split2 es = split2(t8);
-      if constexpr (FINAL) {
-        // Num = Phi(q)_b X^T + Qa_b E, then o = Num / den.
-        f4_t pq2[NKS + 1];
+      for (int h = 0; h < 2; ++h) {
+        const int ct = 2 * pr + h;
+        if (ct >= NCT) continue;
+        f4_t part[NKS];
 #pragma unroll
         for (int ksl = 0; ksl < NKS; ++ksl) {
           const int fa = 32 * ksl + 4 * gq;
-          const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
-          pq2[ksl] = mm2_ss(a, xs[ksl], f4_zero());
+          const bf16x8_t a = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fa + 16]);
+          part[ksl] = mm2_xs(a, xs[ksl], f4_zero());
         }
-        pq2[NKS] = mm2_ss(ld2_4z(&sh.QaD[0][ct][li][4 * gq], TQD), es, f4_zero());
-        f4_t num = pq2[0];
+        f4_t acc = part[0];
 #pragma unroll
-        for (int i = 1; i <= NKS; ++i) num += pq2[i];
+        for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * gq + r;
-          if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = f32_to_bf16(num[r] * sh.rden[c]);
+          const float vv = has_v ? bf_val(sh.sV[c][rowbase + li]) : 0.f;
+          R[h][r] = fmaf(-sh.rk[c], acc[r], vv);
         }
       }
-      // X^T += Ahat_b^T E
+      // E_a = (I + Ka_aa)^{-1} R_a;  E_b = (I + Ka_bb)^{-1} (R_b - Ka_ba E_a)
+      f4_t E[2];
+      E[0] = mm2_ss(ld2_4z(&sh.InvS[0][ta][li][4 * gq], TI), split4(R[0]), f4_zero());
+      const Split2 esa = split4(E[0]);
+      Split2 esb = esa;
+      if (two) {
+        const f4_t rb = mm2_ss(ld2_4z(&sh.KaO[0][pr][li][4 * gq], TKO), esa, R[1]);
+        E[1] = mm2_ss(ld2_4z(&sh.InvS[0][tbb][li][4 * gq], TI), split4(rb), f4_zero());
+        esb = split4(E[1]);
+      }
+      if constexpr (FINAL) {
+        // Num_t = Phi(q)_t X^T + sum_{t' <= t} Qa_tt' E_t', then o = Num / den.
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
-        X[ft] = mm2_ss(ld2_4z(&sh.sAt[0][16 * ft + li][16 * ct + 4 * gq], TA), es, X[ft]);
+        for (int h = 0; h < 2; ++h) {
+          const int ct = 2 * pr + h;
+          if (ct >= NCT) continue;
+          f4_t pq2[NKS + 2];
+#pragma unroll
+          for (int ksl = 0; ksl < NKS; ++ksl) {
+            const int fa = 32 * ksl + 4 * gq;
+            const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
+            pq2[ksl] = mm2_ss(a, xs[ksl], f4_zero());
+          }
+          pq2[NKS] = mm2_ss(ld2_4z(&sh.QaD[0][ct][li][4 * gq], TQD), h ? esb : esa, f4_zero());
+          pq2[NKS + 1] = h ? mm2_ss(ld2_4z(&sh.QaO[0][pr][li][4 * gq], TQO), esa, f4_zero()) : f4_zero();
+          f4_t num = pq2[0];
+#pragma unroll
+          for (int i = 1; i < NKS + 2; ++i) num += pq2[i];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 16 * ct + 4 * gq + r;
+            if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = f32_to_bf16(num[r] * sh.rden[c]);
+          }
+        }
+      }
+      // X^T += Ahat_a^T E_a + Ahat_b^T E_b  (one 32-token product)
+      Split2 ep;
+      ep.h = __builtin_bit_cast(bf16x8_t, make_uint4(
+          __builtin_bit_cast(uint4, esa.h).x, __builtin_bit_cast(uint4, esa.h).y,
+          two ? __builtin_bit_cast(uint4, esb.h).x : 0u, two ? __builtin_bit_cast(uint4, esb.h).y : 0u));
+      ep.l = __builtin_bit_cast(bf16x8_t, make_uint4(
+          __builtin_bit_cast(uint4, esa.l).x, __builtin_bit_cast(uint4, esa.l).y,
+          two ? __builtin_bit_cast(uint4, esb.l).x : 0u, two ? __builtin_bit_cast(uint4, esb.l).y : 0u));
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) {
+        const int fr = 16 * ft + li, ca = 16 * ta + 4 * gq;
+        const Split2 a = two ? ld2_4x2(&sh.sAt[0][fr][ca], &sh.sAt[0][fr][ca + 16], TA)
+                             : ld2_4z(&sh.sAt[0][fr][ca], TA);
+        X[ft] = mm2_ss(a, ep, X[ft]);
+      }
     }
   }
 
