@@ -12,10 +12,10 @@
 // Layout.  Wave w holds column tile w of A (16 columns, all rows) in MFMA accumulators.
 // Because A is symmetric, those registers are also row tile w of A, i.e. exactly the
 // A operand of A [U^T | K^T] for rows 16w..16w+15, so A never goes through LDS; each
-// fp32 fragment is split into three bf16 terms (hi + mid + lo, about 24 bits) right before
-// use.  Products with the raw bf16 inputs are therefore exact term by term; products of
-// two derived fp32 operands use the six term pairs with a + b <= 2 (dropped terms are
-// below 2^-23 relative), accumulated in fp32 by v_mfma_f32_16x16x32_bf16.
+// fp32 operand is split into NTERM bf16 terms right before use (two terms: hi + lo, about 16
+// significant bits).  Products with the raw bf16 inputs take one MFMA per term; products of
+// two derived fp32 operands take the term pairs (i, j) with i + j < NTERM (the dropped
+// ones are near 2^-16 relative), all accumulated in fp32 by v_mfma_f32_16x16x32_bf16.
 #pragma once
 
 #include "vla_common.h"
@@ -31,6 +31,7 @@ struct AwyCfg {
   static constexpr int NKS = D / 32;     // 32-wide feature slices (D = 32 -> 1)
   static constexpr int LDU = D + 8;      // padded bf16 row stride of token rows
   static constexpr int LDL = 40;         // padded bf16 row stride of the 32 x 32 matrices
+  static constexpr int NTERM = 2;        // bf16 terms per fp32 operand
   static_assert(D % 32 == 0, "feature dimension must be a multiple of 32");
 };
 
@@ -40,10 +41,10 @@ struct AwyLds {
   uint16_t sU[C::C][C::LDU];
   uint16_t sK[C::C][C::LDU];
   uint16_t sQ[C::C][C::LDU];
-  uint16_t Zr[3][C::C][C::LDU];          // row-major Z0 / Z terms; later W (token-packed)
-  uint16_t Zc[3][C::C / 8][D][8];        // token-packed Z0 / Z terms: [c/8][f][c%8]
+  uint16_t Zr[C::NTERM][C::C][C::LDU];          // row-major Z0 / Z terms; later W (token-packed)
+  uint16_t Zc[C::NTERM][C::C / 8][D][8];        // token-packed Z0 / Z terms: [c/8][f][c%8]
   float G[C::C][C::C + 4];               // I + U A U^T (lower part used); then L^{-1} transposed
-  uint16_t LX[3][C::C][C::LDL];          // L^{-1} terms (A operand), then X~ terms (B operand)
+  uint16_t LX[C::NTERM][C::C][C::LDL];          // L^{-1} terms (A operand), then X~ terms (B operand)
   float rsd[C::C], rd[C::C];
   float nbuf[2][D] __attribute__((aligned(16)));  // sum of phi(k) before the chunk
   float dtmp[2][16];
@@ -57,7 +58,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
            const float *__restrict__ nk0, float *__restrict__ alpha, float *__restrict__ rkden,
            float *__restrict__ A_final, int64_t T, int64_t L, int64_t P, float eps) {
   using C = AwyCfg<D>;
-  constexpr int NW = C::NW, NT = C::NT, CH = C::C;
+  constexpr int NW = C::NW, NT = C::NT, CH = C::C, NTM = C::NTERM;
   constexpr int ZR_T = CH * C::LDU;       // term stride of Zr
   constexpr int ZC_T = CH * D;            // term stride of Zc / W
   constexpr int LX_T = CH * C::LDL;       // term stride of LX
@@ -98,6 +99,25 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     pv[2] = *reinterpret_cast<const uint4 *>(qs + cs * D + off);
   };
   prefetch(tb, tid);
+  // Z0 or Z (this wave's 16 features x 32 tokens, features-as-rows accumulators) into LDS,
+  // row-major by token (B operand over features) and token-packed (A operand over tokens).
+  auto publish = [&](const f4_t (&zt)[2]) {
+    const int lane = threadIdx.x & 63, li = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      uint16_t tm[4][NTM];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) split_n<NTM>(zt[ct][r], tm[r]);
+      const int c = 16 * ct + li, f = 16 * w + 4 * gq;
+#pragma unroll
+      for (int t = 0; t < NTM; ++t) {
+        *reinterpret_cast<uint2 *>(&sh.Zr[t][c][f]) =
+            make_uint2(tm[0][t] | (uint32_t(tm[1][t]) << 16), tm[2][t] | (uint32_t(tm[3][t]) << 16));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sh.Zc[t][c / 8][f + r][c % 8] = tm[r][t];
+      }
+    }
+  };
 
   for (int64_t c0 = tb; c0 < te; c0 += CH) {
     const int m = static_cast<int>(std::min<int64_t>(CH, te - c0));
@@ -125,33 +145,19 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       float x[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) { x[r] = At[2 * ksl][r]; x[4 + r] = At[2 * ksl + 1][r]; }
-      const Split3 af = split3(x);
+      bf16x8_t af[NTM];
+      split_n8<NTM>(x, af);
       const int f0 = 32 * ksl + 4 * gq, f1 = 32 * ksl + 16 + 4 * gq;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const bf16x8_t bu = ld_bf4x2(&sh.sU[16 * ct + li][f0], &sh.sU[16 * ct + li][f1]);
         const bf16x8_t bk = ld_bf4x2(&sh.sK[16 * ct + li][f0], &sh.sK[16 * ct + li][f1]);
-        Z0t[ct] = mm_sx(af.t, bu, Z0t[ct]);
-        Pt[ct] = mm_sx(af.t, bk, Pt[ct]);
+        Z0t[ct] = mmn_sx<NTM>(af, bu, Z0t[ct]);
+        Pt[ct] = mmn_sx<NTM>(af, bk, Pt[ct]);
       }
     }
     // ---- publish Z0: row-major (for G) and token-packed (for L^{-1} Z0) -----------------
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      uint16_t hh[4], mmv[4], ll[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) split1(Z0t[ct][r], hh[r], mmv[r], ll[r]);
-      const int c = 16 * ct + li, f = 16 * w + 4 * gq;
-      *reinterpret_cast<uint2 *>(&sh.Zr[0][c][f]) = make_uint2(hh[0] | (uint32_t(hh[1]) << 16), hh[2] | (uint32_t(hh[3]) << 16));
-      *reinterpret_cast<uint2 *>(&sh.Zr[1][c][f]) = make_uint2(mmv[0] | (uint32_t(mmv[1]) << 16), mmv[2] | (uint32_t(mmv[3]) << 16));
-      *reinterpret_cast<uint2 *>(&sh.Zr[2][c][f]) = make_uint2(ll[0] | (uint32_t(ll[1]) << 16), ll[2] | (uint32_t(ll[3]) << 16));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sh.Zc[0][c / 8][f + r][c % 8] = hh[r];
-        sh.Zc[1][c / 8][f + r][c % 8] = mmv[r];
-        sh.Zc[2][c / 8][f + r][c % 8] = ll[r];
-      }
-    }
+    publish(Z0t);
     __syncthreads();
     // ---- G = I + U Z0^T on the lower 16-tiles (0,0), (1,0), (1,1) ----------------------
     for (int tile = w; tile < 4; tile += NW) {
@@ -165,9 +171,9 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
       for (int ksl = 0; ksl < C::NKS; ++ksl) {
         const bf16x8_t a = ld_bf8(&sh.sU[16 * it + li][32 * ksl + 8 * gq]);
-        bf16x8_t b[3];
-        ld_split(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
-        g = mm_xs(a, b, g);
+        bf16x8_t b[NTM];
+        ld_split_n<NTM>(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
+        g = mmn_xs<NTM>(a, b, g);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -230,18 +236,17 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       // Row-major split terms of L^{-1}: lane (row i2, half h) writes 16 entries per term.
       const int i2 = lane >> 1, h = lane & 1;
-      uint32_t pk[3][8];
+      uint32_t pk[NTM][8];
 #pragma unroll
       for (int c = 0; c < 16; c += 2) {
-        uint16_t h0, m0, l0, h1, m1, l1;
-        split1(Tb[16 * h + c][i2], h0, m0, l0);
-        split1(Tb[16 * h + c + 1][i2], h1, m1, l1);
-        pk[0][c / 2] = h0 | (uint32_t(h1) << 16);
-        pk[1][c / 2] = m0 | (uint32_t(m1) << 16);
-        pk[2][c / 2] = l0 | (uint32_t(l1) << 16);
+        uint16_t t0[NTM], t1[NTM];
+        split_n<NTM>(Tb[16 * h + c][i2], t0);
+        split_n<NTM>(Tb[16 * h + c + 1][i2], t1);
+#pragma unroll
+        for (int t = 0; t < NTM; ++t) pk[t][c / 2] = t0[t] | (uint32_t(t1[t]) << 16);
       }
 #pragma unroll
-      for (int t = 0; t < 3; ++t) {
+      for (int t = 0; t < NTM; ++t) {
         uint4 *dst = reinterpret_cast<uint4 *>(&sh.LX[t][i2][16 * h]);
         dst[0] = make_uint4(pk[t][0], pk[t][1], pk[t][2], pk[t][3]);
         dst[1] = make_uint4(pk[t][4], pk[t][5], pk[t][6], pk[t][7]);
@@ -331,29 +336,14 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     f4_t Zt[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      bf16x8_t a[3], b[3];
-      ld_split(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
-      ld_split(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
-      Zt[ct] = mm_ss(a, b, f4_zero());
+      bf16x8_t a[NTM], b[NTM];
+      ld_split_n<NTM>(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
+      ld_split_n<NTM>(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
+      Zt[ct] = mmn_ss<NTM>(a, b, f4_zero());
     }
     __syncthreads();
     // ---- publish Z: row-major (for K Z^T) and token-packed (for X~ Z) ---------------------
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      uint16_t hh[4], mmv[4], ll[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) split1(Zt[ct][r], hh[r], mmv[r], ll[r]);
-      const int c = 16 * ct + li, f = 16 * w + 4 * gq;
-      *reinterpret_cast<uint2 *>(&sh.Zr[0][c][f]) = make_uint2(hh[0] | (uint32_t(hh[1]) << 16), hh[2] | (uint32_t(hh[3]) << 16));
-      *reinterpret_cast<uint2 *>(&sh.Zr[1][c][f]) = make_uint2(mmv[0] | (uint32_t(mmv[1]) << 16), mmv[2] | (uint32_t(mmv[3]) << 16));
-      *reinterpret_cast<uint2 *>(&sh.Zr[2][c][f]) = make_uint2(ll[0] | (uint32_t(ll[1]) << 16), ll[2] | (uint32_t(ll[3]) << 16));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sh.Zc[0][c / 8][f + r][c % 8] = hh[r];
-        sh.Zc[1][c / 8][f + r][c % 8] = mmv[r];
-        sh.Zc[2][c / 8][f + r][c % 8] = ll[r];
-      }
-    }
+    publish(Zt);
     __syncthreads();
     // ---- X~ = tril0(K Z^T) D^{-1} on tiles (0,0), (1,0), (1,1); the (0,1) tile is zero --
     for (int tile = w; tile < 4; tile += NW) {
@@ -361,9 +351,8 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * gq + r, j = 16 + li;
-          sh.LX[0][i][j] = 0;
-          sh.LX[1][i][j] = 0;
-          sh.LX[2][i][j] = 0;
+#pragma unroll
+          for (int t = 0; t < NTM; ++t) sh.LX[t][i][j] = 0;
         }
         continue;
       }
@@ -372,47 +361,45 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
       for (int ksl = 0; ksl < C::NKS; ++ksl) {
         const bf16x8_t a = ld_bf8(&sh.sK[16 * it + li][32 * ksl + 8 * gq]);
-        bf16x8_t b[3];
-        ld_split(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
-        hacc = mm_xs(a, b, hacc);
+        bf16x8_t b[NTM];
+        ld_split_n<NTM>(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
+        hacc = mmn_xs<NTM>(a, b, hacc);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * it + 4 * gq + r, j = 16 * jt + li;
         const float xv = (j <= i) ? hacc[r] * sh.rd[j] : 0.f;
-        uint16_t hh, mmv, ll;
-        split1(xv, hh, mmv, ll);
-        sh.LX[0][i][j] = hh;
-        sh.LX[1][i][j] = mmv;
-        sh.LX[2][i][j] = ll;
+        uint16_t tm[NTM];
+        split_n<NTM>(xv, tm);
+#pragma unroll
+        for (int t = 0; t < NTM; ++t) sh.LX[t][i][j] = tm[t];
       }
     }
     __syncthreads();
     // ---- W = D^{-1/2} Z, token-packed, into the (now free) row-major buffer --------------
-    uint16_t *Wc = &sh.Zr[0][0][0];  // [3][C/8][D][8]
+    uint16_t *Wc = &sh.Zr[0][0][0];  // [NTERM][C/8][D][8]
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int c = 16 * ct + li;
       const float sc2 = sh.rsd[c];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        uint16_t hh, mmv, ll;
-        split1(Zt[ct][r] * sc2, hh, mmv, ll);
+        uint16_t tm[NTM];
+        split_n<NTM>(Zt[ct][r] * sc2, tm);
         const int f = 16 * w + 4 * gq + r;
         const int idx = ((c / 8) * D + f) * 8 + (c % 8);
-        Wc[idx] = hh;
-        Wc[ZC_T + idx] = mmv;
-        Wc[2 * ZC_T + idx] = ll;
+#pragma unroll
+        for (int t = 0; t < NTM; ++t) Wc[t * ZC_T + idx] = tm[t];
       }
     }
     // ---- Y^T = P^T - Z^T X~^T, then the gates ----------------------------------------------
     f4_t Yt[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      bf16x8_t a[3], b[3];
-      ld_split(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
-      ld_split(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
-      const f4_t xz = mm_ss(a, b, f4_zero());
+      bf16x8_t a[NTM], b[NTM];
+      ld_split_n<NTM>(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
+      ld_split_n<NTM>(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
+      const f4_t xz = mmn_ss<NTM>(a, b, f4_zero());
 #pragma unroll
       for (int r = 0; r < 4; ++r) Yt[ct][r] = Pt[ct][r] - xz[r];
       float part = 0.f;
@@ -436,13 +423,13 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
     // ---- A <- A - W^T W on this wave's column tile ------------------------------------------
     {
-      bf16x8_t b[3];
-      ld_split(b, &Wc[(gq * D + 16 * w + li) * 8], ZC_T);
+      bf16x8_t b[NTM];
+      ld_split_n<NTM>(b, &Wc[(gq * D + 16 * w + li) * 8], ZC_T);
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
-        bf16x8_t a[3];
-        ld_split(a, &Wc[(gq * D + 16 * it + li) * 8], ZC_T);
-        const f4_t t4 = mm_ss(a, b, f4_zero());
+        bf16x8_t a[NTM];
+        ld_split_n<NTM>(a, &Wc[(gq * D + 16 * it + li) * 8], ZC_T);
+        const f4_t t4 = mmn_ss<NTM>(a, b, f4_zero());
 #pragma unroll
         for (int r = 0; r < 4; ++r) At[it][r] -= t4[r];
       }

@@ -109,6 +109,57 @@ __device__ __forceinline__ uint4 keep_if(bool ok, const uint4 &v) {
   return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
 }
 
+// ---- N-term split (N = 2 or 3), generic over the number of terms ----------------------
+template <int N>
+__device__ __forceinline__ void split_n(float x, uint16_t (&out)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const __bf16 b = static_cast<__bf16>(x);
+    out[i] = bf_bits(b);
+    x -= static_cast<float>(b);
+  }
+}
+template <int N>
+__device__ __forceinline__ void split_n8(const float (&x)[8], bf16x8_t (&t)[N]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float r = x[e];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const __bf16 b = static_cast<__bf16>(r);
+      t[i][e] = b;
+      r -= static_cast<float>(b);
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void ld_split_n(bf16x8_t (&dst)[N], const uint16_t *base, int term_stride) {
+#pragma unroll
+  for (int t = 0; t < N; ++t) dst[t] = ld_bf8(base + t * term_stride);
+}
+// exact x N-term (smallest terms first)
+template <int N>
+__device__ __forceinline__ f4_t mmn_xs(const bf16x8_t &a, const bf16x8_t (&b)[N], f4_t c) {
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i) c = mfma_bf16(a, b[i], c);
+  return c;
+}
+template <int N>
+__device__ __forceinline__ f4_t mmn_sx(const bf16x8_t (&a)[N], const bf16x8_t &b, f4_t c) {
+#pragma unroll
+  for (int i = N - 1; i >= 0; --i) c = mfma_bf16(a[i], b, c);
+  return c;
+}
+// N-term x N-term: the term pairs (i, j) with i + j < N, smallest first
+template <int N>
+__device__ __forceinline__ f4_t mmn_ss(const bf16x8_t (&a)[N], const bf16x8_t (&b)[N], f4_t c) {
+#pragma unroll
+  for (int s = N - 1; s >= 0; --s)
+#pragma unroll
+    for (int i = 0; i <= s; ++i) c = mfma_bf16(a[i], b[s - i], c);
+  return c;
+}
+
 // ---- two-term split ----------------------------------------------------------------------
 struct Split2 {
   bf16x8_t h, l;
