@@ -46,6 +46,7 @@ struct AwyLds {
   float G[C::C][C::C + 4];               // I + U A U^T (lower part used); then L^{-1} transposed
   uint16_t LX[C::NTERM][C::C][C::LDL];          // L^{-1} terms (A operand), then X~ terms (B operand)
   float rsd[C::C], rd[C::C];
+  float lw[4][16][20] __attribute__((aligned(16)));  // blocked LDL^T scratch
   float nbuf[2][D] __attribute__((aligned(16)));  // sum of phi(k) before the chunk
   float dtmp[2][16];
   float norm[C::NW][C::C];
@@ -184,56 +185,132 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     __syncthreads();
     // ---- wave 0: G = L D L^T and L^{-1};  waves >= 1: readout denominators ----------------
     if (w == 0) {
-      // Lane i < 32 holds row i of G; lane 32 + m holds column m of L^{-1}, starting from the
-      // identity.  Pivots go two at a time, j and j + 1, with the pivot columns broadcast
-      // from the row lanes through scalar registers (v_readlane): with d0 = G[j][j],
-      // g = G[j + 1][j], every lane first applies pivot j to its entry j + 1,
-      //   x[j + 1] -= (g / d0) x[j],
-      // which makes lane r's x[j + 1] the column j + 1 after pivot j (so d1 is lane j + 1's),
-      // and then both pivots to the entries r > j + 1:
+      // Blocked LDL^T of G in two 16-column panels.  In a panel, lanes hold rows (of G, or of
+      // the Schur complement) restricted to the panel's 16 columns, lanes 32..47 hold the
+      // columns of the panel block of L^{-1} (starting from the identity), and pivots go two
+      // at a time, j and j + 1, broadcast from the row lanes through scalar registers
+      // (v_readlane): with d0 = G[j][j], g = G[j + 1][j], every lane first applies pivot j to
+      // its entry j + 1,  x[j + 1] -= (g / d0) x[j],  which makes lane r's x[j + 1] the column
+      // j + 1 after pivot j (so d1 is lane j + 1's), then both pivots to the entries r > j + 1:
       //   x[r] -= (x[j] / d0) c0[r] + (x[j + 1] / d1) c1[r].
-      // For a row of G this is the elimination; for a column of L^{-1} it is the forward
-      // substitution L^{-1}[r][m] -= l_rj L^{-1}[j][m] of both pivots.  Only lower entries of
-      // G are read, so the upper tile may hold anything finite.
-      const int i = lane & 31;
-      const bool grow = lane < 32;
-      float x[CH];
-#pragma unroll
-      for (int c4 = 0; c4 < CH / 4; ++c4) {
-        const f4_t gv = *reinterpret_cast<const f4_t *>(&sh.G[i][4 * c4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * c4 + e] = grow ? gv[e] : (4 * c4 + e == i ? 1.f : 0.f);
-      }
+      // For a row this is the elimination (the rows below the panel end holding L21 D1); for
+      // a column of L^{-1} it is the forward substitution.  Between the panels, and to join
+      // them, three 16 x 16 products run on the fp32 matrix core (k = 4 gq + s):
+      //   S22 = G22 - (L21 D1) D1^{-1} (L21 D1)^T,
+      //   L^{-1}_21 = -L22^{-1} L21 L11^{-1}.
+      // Only lower entries of G are read, so its upper tile may hold anything finite.
       auto bcast = [](float v, int src) {
         return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
       };
-      float myd = 1.f;
+      auto ldl16 = [&](float (&x)[16], float &myd) {
 #pragma unroll
-      for (int jb = 0; jb < CH / 2; ++jb) {
-        const int j = 2 * jb;
-        const float d0 = bcast(x[j], j), g = bcast(x[j], j + 1);
-        const float rd0 = __builtin_amdgcn_rcpf(d0);
-        x[j + 1] = fmaf(-g * rd0, x[j], x[j + 1]);
-        const float d1 = bcast(x[j + 1], j + 1);
-        const float t1 = x[j] * rd0, t2 = x[j + 1] * __builtin_amdgcn_rcpf(d1);
-        if (lane == j) myd = d0;
-        if (lane == j + 1) myd = d1;
+        for (int jb = 0; jb < 8; ++jb) {
+          const int j = 2 * jb;
+          const float d0 = bcast(x[j], j), g = bcast(x[j], j + 1);
+          const float rd0 = __builtin_amdgcn_rcpf(d0);
+          x[j + 1] = fmaf(-g * rd0, x[j], x[j + 1]);
+          const float d1 = bcast(x[j + 1], j + 1);
+          const float t1 = x[j] * rd0, t2 = x[j + 1] * __builtin_amdgcn_rcpf(d1);
+          if (lane == j) myd = d0;
+          if (lane == j + 1) myd = d1;
 #pragma unroll
-        for (int r = j + 2; r < CH; ++r)
-          x[r] = fmaf(-t2, bcast(x[j + 1], r), fmaf(-t1, bcast(x[j], r), x[r]));
+          for (int r = j + 2; r < 16; ++r)
+            x[r] = fmaf(-t2, bcast(x[j + 1], r), fmaf(-t1, bcast(x[j], r), x[r]));
+        }
+      };
+      auto wsync = []() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      };
+      const bool lrl = lane >= 32 && lane < 48;  // L^{-1} column lanes
+      const int mcol = lane - 32;
+      float (*Wb)[20] = sh.lw[0];   // L21 D1, row-major
+      float (*Sb)[20] = sh.lw[1];   // S22, row-major
+      float (*L1)[20] = sh.lw[2];   // L11^{-1} transposed: L1[m][r] = L11^{-1}[r][m]
+      float (*L2)[20] = sh.lw[3];   // L22^{-1} transposed
+      // ---- panel 0: rows 0..31 of G, columns 0..15 ----
+      float x[16];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f4_t gv = *reinterpret_cast<const f4_t *>(&sh.G[lane & 31][4 * c4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[4 * c4 + e] = lane < 32 ? gv[e] : ((lrl && 4 * c4 + e == mcol) ? 1.f : 0.f);
       }
-      // Pivots, and L^{-1} transposed into the (now free) G buffer: T[m][r] = L^{-1}[r][m].
+      float myd0 = 1.f;
+      ldl16(x, myd0);
+      if (lane < 16) {
+        sh.rd[lane] = 1.0f / myd0;
+        sh.rsd[lane] = rsqrtf(myd0);
+      } else if (lane < 32) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+          *reinterpret_cast<f4_t *>(&Wb[lane - 16][4 * c4]) = f4_t{x[4 * c4], x[4 * c4 + 1], x[4 * c4 + 2], x[4 * c4 + 3]};
+      } else if (lrl) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+          *reinterpret_cast<f4_t *>(&L1[mcol][4 * c4]) = f4_t{x[4 * c4], x[4 * c4 + 1], x[4 * c4 + 2], x[4 * c4 + 3]};
+      }
+      wsync();
+      // ---- S22 = G22 - W D1^{-1} W^T, W = L21 D1 ----
+      {
+        f4_t acc = f4_zero();
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int pp = 4 * gq + s4;
+          const float wv = Wb[li][pp];
+          acc = mfma_f32_16x16x4(wv * sh.rd[pp], wv, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sb[4 * gq + r][li] = sh.G[16 + 4 * gq + r][16 + li] - acc[r];
+      }
+      wsync();
+      // ---- panel 1: rows of S22 in lanes 0..15 ----
+      float y[16];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const f4_t sv = *reinterpret_cast<const f4_t *>(&Sb[lane & 15][4 * c4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[4 * c4 + e] = lane < 16 ? sv[e] : ((lrl && 4 * c4 + e == mcol) ? 1.f : 0.f);
+      }
+      float myd1 = 1.f;
+      ldl16(y, myd1);
+      if (lane < 16) {
+        sh.rd[16 + lane] = 1.0f / myd1;
+        sh.rsd[16 + lane] = rsqrtf(myd1);
+      } else if (lrl) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+          *reinterpret_cast<f4_t *>(&L2[mcol][4 * c4]) = f4_t{y[4 * c4], y[4 * c4 + 1], y[4 * c4 + 2], y[4 * c4 + 3]};
+      }
+      wsync();
+      // ---- L^{-1}_21 = -L22^{-1} (W D1^{-1}) L11^{-1} ----
+      f4_t xacc = f4_zero();
+      {
+        f4_t nacc = f4_zero();
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int pp = 4 * gq + s4;
+          nacc = mfma_f32_16x16x4(Wb[li][pp] * sh.rd[pp], L1[li][pp], nacc);
+        }
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) xacc = mfma_f32_16x16x4(L2[4 * gq + s4][li], nacc[s4], xacc);
+      }
+      // ---- L^{-1} transposed into the (now free) G buffer: T[m][r] = L^{-1}[r][m] ----
       float(*Tb)[CH + 4] = sh.G;
-      if (grow) {
-        sh.rd[i] = 1.0f / myd;
-        sh.rsd[i] = rsqrtf(myd);
-      } else {
 #pragma unroll
-        for (int r = 0; r < CH; ++r) Tb[i][r] = x[r];
+      for (int r = 0; r < 4; ++r) Tb[li][16 + 4 * gq + r] = -xacc[r];
+      if (lrl) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          *reinterpret_cast<f4_t *>(&Tb[mcol][4 * c4]) = f4_t{x[4 * c4], x[4 * c4 + 1], x[4 * c4 + 2], x[4 * c4 + 3]};
+          *reinterpret_cast<f4_t *>(&Tb[16 + mcol][4 * c4]) = f4_zero();
+          *reinterpret_cast<f4_t *>(&Tb[16 + mcol][16 + 4 * c4]) = f4_t{y[4 * c4], y[4 * c4 + 1], y[4 * c4 + 2], y[4 * c4 + 3]};
+        }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wsync();
       // Row-major split terms of L^{-1}: lane (row i2, half h) writes 16 entries per term.
       const int i2 = lane >> 1, h = lane & 1;
       uint32_t pk[NTM][8];
