@@ -1014,79 +1014,64 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
 }
 
 // ------------------------------------------------------------------------------------
-// k_sprefix: S_0 = 0, S_{p+1} = S_p Pi_p + B_p.  One workgroup per stream, one wave per
-// 16-row slice of S (held transposed in MFMA accumulators); Pi_p is staged in LDS packed
-// as [f'/4][f][f'%4] and the next segment's Pi and B are loaded while this one multiplies.
+// k_sprefix: S_0 = 0, S_{p+1} = S_p Pi_p + B_p.  A row of S_{p+1} depends only on the same
+// row of S_p, so each workgroup scans one 16-row tile of one stream: grid (streams, D/16).
+// Wave w owns output columns 16w..16w+15 (S^T in MFMA accumulators: X[r] = S[row li]
+// [16w + 4gq + r]) and reads its 96 x 16 column slice of Pi_p straight from memory in the
+// A-operand layout, one segment ahead.  The row tile of S_p is exchanged between the waves
+// through a double-buffered LDS copy (one barrier per segment).
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(D / 16 * kWave)
 k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P) {
   constexpr int NFT = D / 16;
-  constexpr int NT = NFT * kWave;
-  constexpr int U4 = D * D / 4;               // float4 of Pi
-  constexpr int PP = (U4 + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) float PiP[D / 4][D + 1][4];
+  __shared__ __attribute__((aligned(16))) float Xs[2][D / 4][16][4];  // S^T[f'][row], f' % 4 minor
   const int64_t s = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, gq = lane >> 4;
-  const int rowbase = 16 * wave;
-  f4_t X[NFT];
-#pragma unroll
-  for (int ft = 0; ft < NFT; ++ft) X[ft] = f4_zero();
-  float *out0 = s0 + s * P * D * D;
-#pragma unroll
-  for (int ft = 0; ft < NFT; ++ft)
-    *reinterpret_cast<float4 *>(&out0[(rowbase + li) * D + 16 * ft + 4 * gq]) = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 pp[PP], pb[NFT];
-  auto prefetch = [&](int64_t pseg) {
+  const int rt = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = 16 * rt + li, col = 16 * w + 4 * gq;
+  // S_0 = 0
+  *reinterpret_cast<float4 *>(&s0[(s * P) * D * D + row * D + col]) = make_float4(0.f, 0.f, 0.f, 0.f);
+  *reinterpret_cast<float4 *>(&Xs[0][4 * w + gq][li][0]) = make_float4(0.f, 0.f, 0.f, 0.f);
+  // a[kt][e] = Pi[16 kt + 4 gq + e][16 w + li];  b = B[row][col .. col + 3]
+  float a[NFT][4];
+  float4 b;
+  auto load = [&](int64_t pseg) {
     const float *Pi = pib + (s * P + pseg) * 2 * D * D;
-    const float *Bm = Pi + D * D;
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int ui = tid + i * NT;              // row f' = ui % D, columns 4 * (ui / D) ..
-      pp[i] = ui < U4 ? *reinterpret_cast<const float4 *>(&Pi[(ui % D) * D + 4 * (ui / D)])
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
-      pb[ft] = *reinterpret_cast<const float4 *>(&Bm[(rowbase + li) * D + 16 * ft + 4 * gq]);
-  };
-  if (P > 1) prefetch(0);
-  for (int64_t p = 0; p + 1 < P; ++p) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PP; ++i) {
-      const int ui = tid + i * NT;
-      if (ui < U4) {
-        const int fr = ui % D, fc = 4 * (ui / D);
-        PiP[fr / 4][fc + 0][fr % 4] = pp[i].x;
-        PiP[fr / 4][fc + 1][fr % 4] = pp[i].y;
-        PiP[fr / 4][fc + 2][fr % 4] = pp[i].z;
-        PiP[fr / 4][fc + 3][fr % 4] = pp[i].w;
-      }
-    }
-    f4_t Y[NFT];
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) Y[ft] = f4_t{pb[ft].x, pb[ft].y, pb[ft].z, pb[ft].w};
-    __syncthreads();
-    if (p + 2 < P) prefetch(p + 1);
-    // Y^T[f][row] = B^T + sum_f' Pi[f'][f] X^T[f'][row]
 #pragma unroll
     for (int kt = 0; kt < NFT; ++kt)
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        const float4 a4 = *reinterpret_cast<const float4 *>(&PiP[4 * kt + gq][16 * ft + li][0]);
-        Y[ft] = mfma_f32_16x16x4(a4.x, X[kt][0], Y[ft]);
-        Y[ft] = mfma_f32_16x16x4(a4.y, X[kt][1], Y[ft]);
-        Y[ft] = mfma_f32_16x16x4(a4.z, X[kt][2], Y[ft]);
-        Y[ft] = mfma_f32_16x16x4(a4.w, X[kt][3], Y[ft]);
-      }
-    float *o = s0 + (s * P + p + 1) * D * D;
+      for (int e = 0; e < 4; ++e) a[kt][e] = Pi[(16 * kt + 4 * gq + e) * D + 16 * w + li];
+    b = *reinterpret_cast<const float4 *>(&Pi[D * D + row * D + col]);
+  };
+  if (P > 1) load(0);
+  for (int64_t p = 0; p + 1 < P; ++p) {
+    const int cur = static_cast<int>(p & 1);
+    float ac[NFT][4];
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) {
-      X[ft] = Y[ft];
-      *reinterpret_cast<float4 *>(&o[(rowbase + li) * D + 16 * ft + 4 * gq]) =
-          make_float4(X[ft][0], X[ft][1], X[ft][2], X[ft][3]);
+    for (int kt = 0; kt < NFT; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ac[kt][e] = a[kt][e];
+    f4_t y[4] = {f4_t{b.x, b.y, b.z, b.w}, f4_zero(), f4_zero(), f4_zero()};
+    __syncthreads();
+    if (p + 2 < P) load(p + 1);
+    // Y^T[f][row] = B^T[f][row] + sum_f' Pi[f'][f] S^T[f'][row], four independent chains
+#pragma unroll
+    for (int kt = 0; kt < NFT; ++kt) {
+      const float4 x = *reinterpret_cast<const float4 *>(&Xs[cur][4 * kt + gq][li][0]);
+      y[0] = mfma_f32_16x16x4(ac[kt][0], x.x, y[0]);
+      y[1] = mfma_f32_16x16x4(ac[kt][1], x.y, y[1]);
+      y[2] = mfma_f32_16x16x4(ac[kt][2], x.z, y[2]);
+      y[3] = mfma_f32_16x16x4(ac[kt][3], x.w, y[3]);
     }
+    float4 o;
+    o.x = (y[0][0] + y[1][0]) + (y[2][0] + y[3][0]);
+    o.y = (y[0][1] + y[1][1]) + (y[2][1] + y[3][1]);
+    o.z = (y[0][2] + y[1][2]) + (y[2][2] + y[3][2]);
+    o.w = (y[0][3] + y[1][3]) + (y[2][3] + y[3][3]);
+    *reinterpret_cast<float4 *>(&Xs[cur ^ 1][4 * w + gq][li][0]) = o;
+    *reinterpret_cast<float4 *>(&s0[(s * P + p + 1) * D * D + row * D + col]) = o;
   }
 }
 
@@ -1135,7 +1120,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                  dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
                  S_final, pl.T, pl.L, pl.P);
     }
-    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
+    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
     VLA_LAUNCH("k_swy_final", (k_swyb<D, CH, true>), dim3(S, P), dim3(SwbCfg<D, CH, true>::NT), 0,
                st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
   } else {
@@ -1144,7 +1129,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                  dim3(SwyCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
                  S_final, pl.T, pl.L, pl.P);
     }
-    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
+    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
     VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P),
                dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final,
                pl.T, pl.L, pl.P);
