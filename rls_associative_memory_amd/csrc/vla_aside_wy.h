@@ -43,8 +43,8 @@ struct AwyLds {
   uint16_t sQ[C::C][C::LDU];
   uint16_t Zr[C::NTERM][C::C][C::LDU];          // row-major Z0 / Z terms; later W (token-packed)
   uint16_t Zc[C::NTERM][C::C / 8][D][8];        // token-packed Z0 / Z terms: [c/8][f][c%8]
-  float G[C::C][C::C + 4];               // I + U A U^T (lower part used); then L^{-1} transposed
-  uint16_t LX[C::NTERM][C::C][C::LDL];          // L^{-1} terms (A operand), then X~ terms (B operand)
+  float G[C::C][C::C + 4];               // I + U A U^T (lower part used); then L^{-1}, row-major
+  uint16_t LX[C::NTERM][C::C][C::LDL];          // X~ terms (B operand)
   float rsd[C::C], rd[C::C];
   float lw[4][16][20] __attribute__((aligned(16)));  // blocked LDL^T scratch
   float nbuf[2][D] __attribute__((aligned(16)));  // sum of phi(k) before the chunk
@@ -162,7 +162,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     __syncthreads();
     // ---- G = I + U Z0^T on the lower 16-tiles (0,0), (1,0), (1,1) ----------------------
     for (int tile = w; tile < 4; tile += NW) {
-      if (tile == 3) {  // the upper tile (0,1) is never read as data; keep it finite
+      if (tile == 3) {  // upper tile (0,1): zeros, never read as G; later L^{-1}'s zero tile
 #pragma unroll
         for (int r = 0; r < 4; ++r) sh.G[4 * gq + r][16 + li] = 0.f;
         continue;
@@ -194,11 +194,13 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       // j + 1 after pivot j (so d1 is lane j + 1's), then both pivots to the entries r > j + 1:
       //   x[r] -= (x[j] / d0) c0[r] + (x[j + 1] / d1) c1[r].
       // For a row this is the elimination (the rows below the panel end holding L21 D1); for
-      // a column of L^{-1} it is the forward substitution.  Between the panels, and to join
-      // them, three 16 x 16 products run on the fp32 matrix core (k = 4 gq + s):
-      //   S22 = G22 - (L21 D1) D1^{-1} (L21 D1)^T,
-      //   L^{-1}_21 = -L22^{-1} L21 L11^{-1}.
-      // Only lower entries of G are read, so its upper tile may hold anything finite.
+      // any other vector b it is the forward substitution b <- L^{-1} b.  Between the panels
+      // two 16 x 16 products run on the fp32 matrix core (k = 4 gq + s):
+      //   S22 = G22 - (L21 D1) D1^{-1} (L21 D1)^T,   N = L21 L11^{-1},
+      // and panel 1 carries the columns of -N (lanes 32..47) and of I (lanes 48..63), which
+      // leave it as the columns of L^{-1}_21 = -L22^{-1} N and of L22^{-1}.  L^{-1} is written
+      // row-major over G as it is found (G11 after panel 0, G21 and G22 after panel 1); the
+      // upper tile of G holds zeros from its construction, which is L^{-1}'s upper tile.
       auto bcast = [](float v, int src) {
         return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
       };
@@ -228,7 +230,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       float (*Wb)[20] = sh.lw[0];   // L21 D1, row-major
       float (*Sb)[20] = sh.lw[1];   // S22, row-major
       float (*L1)[20] = sh.lw[2];   // L11^{-1} transposed: L1[m][r] = L11^{-1}[r][m]
-      float (*L2)[20] = sh.lw[3];   // L22^{-1} transposed
+      float (*Nt)[20] = sh.lw[3];   // -N transposed: Nt[m][r] = -N[r][m]
       // ---- panel 0: rows 0..31 of G, columns 0..15 ----
       float x[16];
 #pragma unroll
@@ -251,82 +253,46 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
           *reinterpret_cast<f4_t *>(&L1[mcol][4 * c4]) = f4_t{x[4 * c4], x[4 * c4 + 1], x[4 * c4 + 2], x[4 * c4 + 3]};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sh.G[r][mcol] = x[r];  // L^{-1}_11, row-major
       }
       wsync();
-      // ---- S22 = G22 - W D1^{-1} W^T, W = L21 D1 ----
+      // ---- S22 = G22 - W D1^{-1} W^T and N = (W D1^{-1}) L11^{-1}, W = L21 D1 ----
       {
-        f4_t acc = f4_zero();
+        f4_t acc = f4_zero(), nacc = f4_zero();
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const int pp = 4 * gq + s4;
           const float wv = Wb[li][pp];
-          acc = mfma_f32_16x16x4(wv * sh.rd[pp], wv, acc);
+          const float lv = wv * sh.rd[pp];
+          acc = mfma_f32_16x16x4(lv, wv, acc);
+          nacc = mfma_f32_16x16x4(lv, L1[li][pp], nacc);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) Sb[4 * gq + r][li] = sh.G[16 + 4 * gq + r][16 + li] - acc[r];
+        *reinterpret_cast<f4_t *>(&Nt[li][4 * gq]) = f4_t{-nacc[0], -nacc[1], -nacc[2], -nacc[3]};
       }
       wsync();
-      // ---- panel 1: rows of S22 in lanes 0..15 ----
+      // ---- panel 1: rows of S22 in lanes 0..15, -N e_m in lanes 32..47, e_m in 48..63 ----
       float y[16];
+      {
+        const float *src = lane < 16 ? &Sb[lane][0] : &Nt[mcol & 15][0];
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const f4_t sv = *reinterpret_cast<const f4_t *>(&Sb[lane & 15][4 * c4]);
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const f4_t sv = *reinterpret_cast<const f4_t *>(src + 4 * c4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          y[4 * c4 + e] = lane < 16 ? sv[e] : ((lrl && 4 * c4 + e == mcol) ? 1.f : 0.f);
+          for (int e = 0; e < 4; ++e)
+            y[4 * c4 + e] = (lane < 16 || lrl) ? sv[e] : ((lane >= 48 && 4 * c4 + e == lane - 48) ? 1.f : 0.f);
+        }
       }
       float myd1 = 1.f;
       ldl16(y, myd1);
       if (lane < 16) {
         sh.rd[16 + lane] = 1.0f / myd1;
         sh.rsd[16 + lane] = rsqrtf(myd1);
-      } else if (lrl) {
+      } else if (lane >= 32) {
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4)
-          *reinterpret_cast<f4_t *>(&L2[mcol][4 * c4]) = f4_t{y[4 * c4], y[4 * c4 + 1], y[4 * c4 + 2], y[4 * c4 + 3]};
-      }
-      wsync();
-      // ---- L^{-1}_21 = -L22^{-1} (W D1^{-1}) L11^{-1} ----
-      f4_t xacc = f4_zero();
-      {
-        f4_t nacc = f4_zero();
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int pp = 4 * gq + s4;
-          nacc = mfma_f32_16x16x4(Wb[li][pp] * sh.rd[pp], L1[li][pp], nacc);
-        }
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) xacc = mfma_f32_16x16x4(L2[4 * gq + s4][li], nacc[s4], xacc);
-      }
-      // ---- L^{-1} transposed into the (now free) G buffer: T[m][r] = L^{-1}[r][m] ----
-      float(*Tb)[CH + 4] = sh.G;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Tb[li][16 + 4 * gq + r] = -xacc[r];
-      if (lrl) {
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          *reinterpret_cast<f4_t *>(&Tb[mcol][4 * c4]) = f4_t{x[4 * c4], x[4 * c4 + 1], x[4 * c4 + 2], x[4 * c4 + 3]};
-          *reinterpret_cast<f4_t *>(&Tb[16 + mcol][4 * c4]) = f4_zero();
-          *reinterpret_cast<f4_t *>(&Tb[16 + mcol][16 + 4 * c4]) = f4_t{y[4 * c4], y[4 * c4 + 1], y[4 * c4 + 2], y[4 * c4 + 3]};
-        }
-      }
-      wsync();
-      // Row-major split terms of L^{-1}: lane (row i2, half h) writes 16 entries per term.
-      const int i2 = lane >> 1, h = lane & 1;
-      uint32_t pk[NTM][8];
-#pragma unroll
-      for (int c = 0; c < 16; c += 2) {
-        uint16_t t0[NTM], t1[NTM];
-        split_n<NTM>(Tb[16 * h + c][i2], t0);
-        split_n<NTM>(Tb[16 * h + c + 1][i2], t1);
-#pragma unroll
-        for (int t = 0; t < NTM; ++t) pk[t][c / 2] = t0[t] | (uint32_t(t1[t]) << 16);
-      }
-#pragma unroll
-      for (int t = 0; t < NTM; ++t) {
-        uint4 *dst = reinterpret_cast<uint4 *>(&sh.LX[t][i2][16 * h]);
-        dst[0] = make_uint4(pk[t][0], pk[t][1], pk[t][2], pk[t][3]);
-        dst[1] = make_uint4(pk[t][4], pk[t][5], pk[t][6], pk[t][7]);
+        for (int r = 0; r < 16; ++r) sh.G[16 + r][mcol] = y[r];  // L^{-1}_21 | L^{-1}_22
       }
     } else {
       // Readout denominators and key norms of the chunk, on the matrix cores of the waves
@@ -415,7 +381,10 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     for (int ct = 0; ct < 2; ++ct) {
       bf16x8_t a[NTM], b[NTM];
       ld_split_n<NTM>(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
-      ld_split_n<NTM>(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
+      const f4_t l0 = *reinterpret_cast<const f4_t *>(&sh.G[16 * ct + li][8 * gq]);
+      const f4_t l1 = *reinterpret_cast<const f4_t *>(&sh.G[16 * ct + li][8 * gq + 4]);
+      const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+      split_n8<NTM>(lv, b);
       Zt[ct] = mmn_ss<NTM>(a, b, f4_zero());
     }
     __syncthreads();
