@@ -106,16 +106,17 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const int lane = threadIdx.x & 63, li = lane & 15, gq = lane >> 4;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      uint16_t tm[4][NTM];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) split_n<NTM>(zt[ct][r], tm[r]);
+      uint32_t w01[NTM], w23[NTM];  // features (f, f + 1) and (f + 2, f + 3), by term
+      split_pk<NTM>(zt[ct][0], zt[ct][1], w01);
+      split_pk<NTM>(zt[ct][2], zt[ct][3], w23);
       const int c = 16 * ct + li, f = 16 * w + 4 * gq;
 #pragma unroll
       for (int t = 0; t < NTM; ++t) {
-        *reinterpret_cast<uint2 *>(&sh.Zr[t][c][f]) =
-            make_uint2(tm[0][t] | (uint32_t(tm[1][t]) << 16), tm[2][t] | (uint32_t(tm[3][t]) << 16));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sh.Zc[t][c / 8][f + r][c % 8] = tm[r][t];
+        *reinterpret_cast<uint2 *>(&sh.Zr[t][c][f]) = make_uint2(w01[t], w23[t]);
+        sh.Zc[t][c / 8][f + 0][c % 8] = static_cast<uint16_t>(w01[t]);
+        sh.Zc[t][c / 8][f + 1][c % 8] = static_cast<uint16_t>(w01[t] >> 16);
+        sh.Zc[t][c / 8][f + 2][c % 8] = static_cast<uint16_t>(w23[t]);
+        sh.Zc[t][c / 8][f + 3][c % 8] = static_cast<uint16_t>(w23[t] >> 16);
       }
     }
   };
@@ -411,14 +412,18 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         ld_split_n<NTM>(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
         hacc = mmn_xs<NTM>(a, b, hacc);
       }
+      const int j = 16 * jt + li;
+      const float rdj = sh.rd[j];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * it + 4 * gq + r, j = 16 * jt + li;
-        const float xv = (j <= i) ? hacc[r] * sh.rd[j] : 0.f;
-        uint16_t tm[NTM];
-        split_n<NTM>(xv, tm);
+      for (int r = 0; r < 4; r += 2) {
+        const int i = 16 * it + 4 * gq + r;
+        uint32_t tm[NTM];
+        split_pk<NTM>((j <= i) ? hacc[r] * rdj : 0.f, (j <= i + 1) ? hacc[r + 1] * rdj : 0.f, tm);
 #pragma unroll
-        for (int t = 0; t < NTM; ++t) sh.LX[t][i][j] = tm[t];
+        for (int t = 0; t < NTM; ++t) {
+          sh.LX[t][i][j] = static_cast<uint16_t>(tm[t]);
+          sh.LX[t][i + 1][j] = static_cast<uint16_t>(tm[t] >> 16);
+        }
       }
     }
     __syncthreads();
@@ -429,13 +434,16 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       const int c = 16 * ct + li;
       const float sc2 = sh.rsd[c];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint16_t tm[NTM];
-        split_n<NTM>(Zt[ct][r] * sc2, tm);
+      for (int r = 0; r < 4; r += 2) {
+        uint32_t tm[NTM];
+        split_pk<NTM>(Zt[ct][r] * sc2, Zt[ct][r + 1] * sc2, tm);
         const int f = 16 * w + 4 * gq + r;
         const int idx = ((c / 8) * D + f) * 8 + (c % 8);
 #pragma unroll
-        for (int t = 0; t < NTM; ++t) Wc[t * ZC_T + idx] = tm[t];
+        for (int t = 0; t < NTM; ++t) {
+          Wc[t * ZC_T + idx] = static_cast<uint16_t>(tm[t]);
+          Wc[t * ZC_T + idx + 8] = static_cast<uint16_t>(tm[t] >> 16);
+        }
       }
     }
     // ---- Y^T = P^T - Z^T X~^T, then the gates ----------------------------------------------

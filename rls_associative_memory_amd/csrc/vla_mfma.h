@@ -93,6 +93,30 @@ __device__ __forceinline__ void ld_split(bf16x8_t (&dst)[3], const uint16_t *bas
 __device__ __forceinline__ uint16_t bf_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 __device__ __forceinline__ float bf_val(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
+// ---- packed splits: two fp32 values at a time through v_cvt_pk_bf16_f32 -----------------
+// pk_bf16(a, b) rounds both to bf16 (nearest even), a in the low half.  A term's value is
+// recovered by placing its half in the high bits of an fp32 word, so a residual costs a
+// shift or a mask and a subtraction; one split of two values into N terms is N conversions.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf16x2_t));
+}
+__device__ __forceinline__ float pk_lo_val(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float pk_hi_val(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+// a = sum_i lo(t[i]), b = sum_i hi(t[i]), each to about 8 N significant bits
+template <int N>
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t (&t)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    t[i] = pk_bf16(a, b);
+    if (i + 1 < N) {
+      a -= pk_lo_val(t[i]);
+      b -= pk_hi_val(t[i]);
+    }
+  }
+}
+
 // Split one fp32 value into its three bf16 terms (bit patterns).
 __device__ __forceinline__ void split1(float x, uint16_t &h, uint16_t &m, uint16_t &l) {
   const __bf16 bh = static_cast<__bf16>(x);
@@ -121,16 +145,11 @@ __device__ __forceinline__ void split_n(float x, uint16_t (&out)[N]) {
 }
 template <int N>
 __device__ __forceinline__ void split_n8(const float (&x)[8], bf16x8_t (&t)[N]) {
+  uint32_t w[4][N];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float r = x[e];
+  for (int e = 0; e < 4; ++e) split_pk<N>(x[2 * e], x[2 * e + 1], w[e]);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const __bf16 b = static_cast<__bf16>(r);
-      t[i][e] = b;
-      r -= static_cast<float>(b);
-    }
-  }
+  for (int i = 0; i < N; ++i) t[i] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0][i], w[1][i], w[2][i], w[3][i]));
 }
 template <int N>
 __device__ __forceinline__ void ld_split_n(bf16x8_t (&dst)[N], const uint16_t *base, int term_stride) {
@@ -172,14 +191,20 @@ __device__ __forceinline__ void split2_1(float x, uint16_t &h, uint16_t &l) {
 }
 
 __device__ __forceinline__ Split2 split2(const float (&x)[8]) {
-  Split2 s;
+  uint32_t w[4][2];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 h = static_cast<__bf16>(x[e]);
-    s.h[e] = h;
-    s.l[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
-  }
-  return s;
+  for (int e = 0; e < 4; ++e) split_pk<2>(x[2 * e], x[2 * e + 1], w[e]);
+  return Split2{__builtin_bit_cast(bf16x8_t, make_uint4(w[0][0], w[1][0], w[2][0], w[3][0])),
+                __builtin_bit_cast(bf16x8_t, make_uint4(w[0][1], w[1][1], w[2][1], w[3][1]))};
+}
+// Four values (an accumulator tile) split into the first half of two-term operands; the
+// second half is zero.
+__device__ __forceinline__ Split2 split2_4z(const f4_t &v) {
+  uint32_t a[2], b[2];
+  split_pk<2>(v[0], v[1], a);
+  split_pk<2>(v[2], v[3], b);
+  return Split2{__builtin_bit_cast(bf16x8_t, make_uint4(a[0], b[0], 0u, 0u)),
+                __builtin_bit_cast(bf16x8_t, make_uint4(a[1], b[1], 0u, 0u))};
 }
 
 // exact x two-term

@@ -177,11 +177,10 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           uint32_t hw[4], lw[4];
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            uint16_t h0, l0, h1, l1;
-            split2_1(c < m ? phi(qf[e]) : 0.f, h0, l0);
-            split2_1(c < m ? phi(qf[e + 1]) : 0.f, h1, l1);
-            hw[e / 2] = h0 | (uint32_t(h1) << 16);
-            lw[e / 2] = l0 | (uint32_t(l1) << 16);
+            uint32_t t2[2];
+            split_pk<2>(c < m ? phi(qf[e]) : 0.f, c < m ? phi(qf[e + 1]) : 0.f, t2);
+            hw[e / 2] = t2[0];
+            lw[e / 2] = t2[1];
           }
           *reinterpret_cast<uint4 *>(&sh.sFq[0][c][f0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
           *reinterpret_cast<uint4 *>(&sh.sFq[1][c][f0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
@@ -193,24 +192,26 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       const int ui = tid + i * NT;
       if (ui < UA) {
         const int c = 2 * (ui % (CH / 2)), f0 = (ui / (CH / 2)) * 4;
-        uint16_t h[2][4], l[2][4];
+        // w[t][pr][term]: features (f0 + 2 pr, f0 + 2 pr + 1) of token c + t
+        uint32_t w[2][2][2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const bool ok = c + t < m;
-          const float a4[4] = {ok ? pa[i][t].x : 0.f, ok ? pa[i][t].y : 0.f,
-                               ok ? pa[i][t].z : 0.f, ok ? pa[i][t].w : 0.f};
+          split_pk<2>(ok ? pa[i][t].x : 0.f, ok ? pa[i][t].y : 0.f, w[t][0]);
+          split_pk<2>(ok ? pa[i][t].z : 0.f, ok ? pa[i][t].w : 0.f, w[t][1]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) split2_1(a4[e], h[t][e], l[t][e]);
-          *reinterpret_cast<uint2 *>(&sh.sAh[0][c + t][f0]) =
-              make_uint2(h[t][0] | (uint32_t(h[t][1]) << 16), h[t][2] | (uint32_t(h[t][3]) << 16));
-          *reinterpret_cast<uint2 *>(&sh.sAh[1][c + t][f0]) =
-              make_uint2(l[t][0] | (uint32_t(l[t][1]) << 16), l[t][2] | (uint32_t(l[t][3]) << 16));
+          for (int term = 0; term < 2; ++term)
+            *reinterpret_cast<uint2 *>(&sh.sAh[term][c + t][f0]) = make_uint2(w[t][0][term], w[t][1][term]);
         }
+        // by feature: the two tokens of the pair in one 32-bit word
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          *reinterpret_cast<uint32_t *>(&sh.sAt[0][f0 + e][c]) = h[0][e] | (uint32_t(h[1][e]) << 16);
-          *reinterpret_cast<uint32_t *>(&sh.sAt[1][f0 + e][c]) = l[0][e] | (uint32_t(l[1][e]) << 16);
-        }
+        for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+          for (int term = 0; term < 2; ++term) {
+            const uint32_t a = w[0][pr][term], b = w[1][pr][term];
+            *reinterpret_cast<uint32_t *>(&sh.sAt[term][f0 + 2 * pr][c]) = (a & 0xffffu) | (b << 16);
+            *reinterpret_cast<uint32_t *>(&sh.sAt[term][f0 + 2 * pr + 1][c]) = (a >> 16) | (b & 0xffff0000u);
+          }
       }
     }
     if (tid < CH) {
@@ -264,31 +265,38 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
         for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
       }
-      // acc[r] = product[i = 4 gq + r][i'' = li] of tile (ct, ct2)
+      // acc[r] = product[i = 4 gq + r][i'' = li] of tile (ct, ct2); rows split in pairs
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; r += 2) {
         const int i = 4 * gq + r;
         if (isq) {
           if constexpr (FINAL) {
-            uint16_t h, l;
-            split2_1(diag && li > i ? 0.f : acc[r], h, l);
-            if (diag) {
-              sh.QaD[0][ct][i][li] = h;
-              sh.QaD[1][ct][i][li] = l;
-            } else {
-              sh.QaO[0][jk - NCT][i][li] = h;
-              sh.QaO[1][jk - NCT][i][li] = l;
+            uint32_t t2[2];
+            split_pk<2>(diag && li > i ? 0.f : acc[r], diag && li > i + 1 ? 0.f : acc[r + 1], t2);
+#pragma unroll
+            for (int term = 0; term < 2; ++term) {
+              if (diag) {
+                sh.QaD[term][ct][i][li] = static_cast<uint16_t>(t2[term]);
+                sh.QaD[term][ct][i + 1][li] = static_cast<uint16_t>(t2[term] >> 16);
+              } else {
+                sh.QaO[term][jk - NCT][i][li] = static_cast<uint16_t>(t2[term]);
+                sh.QaO[term][jk - NCT][i + 1][li] = static_cast<uint16_t>(t2[term] >> 16);
+              }
             }
           }
         } else {
-          const float nk = -acc[r] * sh.rk[16 * ct + i];
+          const float nk0 = -acc[r] * sh.rk[16 * ct + i], nk1 = -acc[r + 1] * sh.rk[16 * ct + i + 1];
           if (diag) {
-            sh.Kd[ct][i][li] = li >= i ? 0.f : nk;
+            sh.Kd[ct][i][li] = li >= i ? 0.f : nk0;
+            sh.Kd[ct][i + 1][li] = li >= i + 1 ? 0.f : nk1;
           } else {
-            uint16_t h, l;
-            split2_1(nk, h, l);
-            sh.KaO[0][jk - NCT][i][li] = h;
-            sh.KaO[1][jk - NCT][i][li] = l;
+            uint32_t t2[2];
+            split_pk<2>(nk0, nk1, t2);
+#pragma unroll
+            for (int term = 0; term < 2; ++term) {
+              sh.KaO[term][jk - NCT][i][li] = static_cast<uint16_t>(t2[term]);
+              sh.KaO[term][jk - NCT][i + 1][li] = static_cast<uint16_t>(t2[term] >> 16);
+            }
           }
         }
       }
@@ -313,11 +321,14 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
             x[i] = a;
           }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            uint16_t h, l;
-            split2_1(x[i], h, l);
-            sh.InvS[0][ct][i][j] = h;
-            sh.InvS[1][ct][i][j] = l;
+          for (int i = 0; i < 16; i += 2) {
+            uint32_t t2[2];
+            split_pk<2>(x[i], x[i + 1], t2);
+#pragma unroll
+            for (int term = 0; term < 2; ++term) {
+              sh.InvS[term][ct][i][j] = static_cast<uint16_t>(t2[term]);
+              sh.InvS[term][ct][i + 1][j] = static_cast<uint16_t>(t2[term] >> 16);
+            }
           }
         }
       }
@@ -327,10 +338,6 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     // The next chunk's loads fly during the steps.
     if (c0 + CH < te) prefetch(c0 + CH, tid);
     uint16_t *os = reinterpret_cast<uint16_t *>(out) + (s * T + c0) * D;
-    auto split4 = [](const f4_t &v) {  // one D-layout tile as a B operand (upper half zero)
-      float t8[8] = {v[0], v[1], v[2], v[3], 0.f, 0.f, 0.f, 0.f};
-      return split2(t8);
-    };
 #pragma unroll
     for (int pr = 0; pr < NPR; ++pr) {
       const int ta = 2 * pr, tbb = 2 * pr + 1;
@@ -367,15 +374,34 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           R[h][r] = fmaf(-sh.rk[c], acc[r], vv);
         }
       }
+      // Phi(q)_t X^T (final pass): independent of the solve, issued with the R products.
+      f4_t numq[2] = {f4_zero(), f4_zero()};
+      if constexpr (FINAL) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ct = 2 * pr + h;
+          if (ct >= NCT) continue;
+          f4_t part[NKS];
+#pragma unroll
+          for (int ksl = 0; ksl < NKS; ++ksl) {
+            const int fa = 32 * ksl + 4 * gq;
+            const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
+            part[ksl] = mm2_ss(a, xs[ksl], f4_zero());
+          }
+          numq[h] = part[0];
+#pragma unroll
+          for (int ksl = 1; ksl < NKS; ++ksl) numq[h] += part[ksl];
+        }
+      }
       // E_a = (I + Ka_aa)^{-1} R_a;  E_b = (I + Ka_bb)^{-1} (R_b - Ka_ba E_a)
       f4_t E[2];
-      E[0] = mm2_ss(ld2_4z(&sh.InvS[0][ta][li][4 * gq], TI), split4(R[0]), f4_zero());
-      const Split2 esa = split4(E[0]);
+      E[0] = mm2_ss(ld2_4z(&sh.InvS[0][ta][li][4 * gq], TI), split2_4z(R[0]), f4_zero());
+      const Split2 esa = split2_4z(E[0]);
       Split2 esb = esa;
       if (two) {
         const f4_t rb = mm2_ss(ld2_4z(&sh.KaO[0][pr][li][4 * gq], TKO), esa, R[1]);
-        E[1] = mm2_ss(ld2_4z(&sh.InvS[0][tbb][li][4 * gq], TI), split4(rb), f4_zero());
-        esb = split4(E[1]);
+        E[1] = mm2_ss(ld2_4z(&sh.InvS[0][tbb][li][4 * gq], TI), split2_4z(rb), f4_zero());
+        esb = split2_4z(E[1]);
       }
       if constexpr (FINAL) {
         // Num_t = Phi(q)_t X^T + sum_{t' <= t} Qa_tt' E_t', then o = Num / den.
@@ -383,22 +409,14 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         for (int h = 0; h < 2; ++h) {
           const int ct = 2 * pr + h;
           if (ct >= NCT) continue;
-          f4_t pq2[NKS + 2];
+          f4_t num = mm2_ss(ld2_4z(&sh.QaD[0][ct][li][4 * gq], TQD), h ? esb : esa, numq[h]);
+          if (h) num = mm2_ss(ld2_4z(&sh.QaO[0][pr][li][4 * gq], TQO), esa, num);
 #pragma unroll
-          for (int ksl = 0; ksl < NKS; ++ksl) {
-            const int fa = 32 * ksl + 4 * gq;
-            const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
-            pq2[ksl] = mm2_ss(a, xs[ksl], f4_zero());
-          }
-          pq2[NKS] = mm2_ss(ld2_4z(&sh.QaD[0][ct][li][4 * gq], TQD), h ? esb : esa, f4_zero());
-          pq2[NKS + 1] = h ? mm2_ss(ld2_4z(&sh.QaO[0][pr][li][4 * gq], TQO), esa, f4_zero()) : f4_zero();
-          f4_t num = pq2[0];
-#pragma unroll
-          for (int i = 1; i < NKS + 2; ++i) num += pq2[i];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int r = 0; r < 4; r += 2) {
             const int c = 16 * ct + 4 * gq + r;
-            if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = f32_to_bf16(num[r] * sh.rden[c]);
+            const uint32_t o2 = pk_bf16(num[r] * sh.rden[c], num[r + 1] * sh.rden[c + 1]);
+            if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = static_cast<uint16_t>(o2);
+            if (c + 1 < m) os[static_cast<uint32_t>((c + 1) * D + rowbase + li)] = static_cast<uint16_t>(o2 >> 16);
           }
         }
       }
