@@ -342,6 +342,29 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     for (int pr = 0; pr < NPR; ++pr) {
       const int ta = 2 * pr, tbb = 2 * pr + 1;
       const bool two = tbb < NCT;
+      // Operands of the step's products over features, loaded up front so that one LDS
+      // latency covers them all: K_t (and Phi(q)_t in the final pass) for both tiles.
+      bf16x8_t aK[2][NKS];
+      Split2 aQ[FINAL ? 2 : 1][NKS];
+      float vv[2][4], rkv[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ct = 2 * pr + h;
+        if (ct >= NCT) continue;
+#pragma unroll
+        for (int ksl = 0; ksl < NKS; ++ksl) {
+          const int fa = 32 * ksl + 4 * gq;
+          aK[h][ksl] = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fa + 16]);
+          if constexpr (FINAL)
+            aQ[h][ksl] = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * ct + 4 * gq + r;
+          vv[h][r] = has_v ? bf_val(sh.sV[c][rowbase + li]) : 0.f;
+          rkv[h][r] = sh.rk[c];
+        }
+      }
       // The state slice before this step as the B operand of products over features.
       Split2 xs[NKS];
 #pragma unroll
@@ -351,47 +374,29 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         for (int r = 0; r < 4; ++r) { t8[r] = X[2 * ksl][r]; t8[4 + r] = X[2 * ksl + 1][r]; }
         xs[ksl] = split2(t8);
       }
-      // R_t = V_t - rk (K_t X^T), t = a, b
-      f4_t R[2];
+      // R_t = V_t - rk (K_t X^T) and, in the final pass, Phi(q)_t X^T (independent of the
+      // solve): four accumulation chains.
+      f4_t R[2], numq[2] = {f4_zero(), f4_zero()};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int ct = 2 * pr + h;
         if (ct >= NCT) continue;
-        f4_t part[NKS];
+        f4_t acc = f4_zero();
 #pragma unroll
         for (int ksl = 0; ksl < NKS; ++ksl) {
-          const int fa = 32 * ksl + 4 * gq;
-          const bf16x8_t a = ld_bf4x2(&sh.sK[16 * ct + li][fa], &sh.sK[16 * ct + li][fa + 16]);
-          part[ksl] = mm2_xs(a, xs[ksl], f4_zero());
+          acc = mm2_xs(aK[h][ksl], xs[ksl], acc);
+          if constexpr (FINAL) numq[h] = mm2_ss(aQ[h][ksl], xs[ksl], numq[h]);
         }
-        f4_t acc = part[0];
 #pragma unroll
-        for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = 16 * ct + 4 * gq + r;
-          const float vv = has_v ? bf_val(sh.sV[c][rowbase + li]) : 0.f;
-          R[h][r] = fmaf(-sh.rk[c], acc[r], vv);
-        }
+        for (int r = 0; r < 4; ++r) R[h][r] = fmaf(-rkv[h][r], acc[r], vv[h][r]);
       }
-      // Phi(q)_t X^T (final pass): independent of the solve, issued with the R products.
-      f4_t numq[2] = {f4_zero(), f4_zero()};
-      if constexpr (FINAL) {
+      // Ahat^T operands of the state update, loaded while the solve runs.
+      Split2 aT[NFT];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ct = 2 * pr + h;
-          if (ct >= NCT) continue;
-          f4_t part[NKS];
-#pragma unroll
-          for (int ksl = 0; ksl < NKS; ++ksl) {
-            const int fa = 32 * ksl + 4 * gq;
-            const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
-            part[ksl] = mm2_ss(a, xs[ksl], f4_zero());
-          }
-          numq[h] = part[0];
-#pragma unroll
-          for (int ksl = 1; ksl < NKS; ++ksl) numq[h] += part[ksl];
-        }
+      for (int ft = 0; ft < NFT; ++ft) {
+        const int fr = 16 * ft + li, ca = 16 * ta + 4 * gq;
+        aT[ft] = two ? ld2_4x2(&sh.sAt[0][fr][ca], &sh.sAt[0][fr][ca + 16], TA)
+                     : ld2_4z(&sh.sAt[0][fr][ca], TA);
       }
       // E_a = (I + Ka_aa)^{-1} R_a;  E_b = (I + Ka_bb)^{-1} (R_b - Ka_ba E_a)
       f4_t E[2];
@@ -429,12 +434,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           __builtin_bit_cast(uint4, esa.l).x, __builtin_bit_cast(uint4, esa.l).y,
           two ? __builtin_bit_cast(uint4, esb.l).x : 0u, two ? __builtin_bit_cast(uint4, esb.l).y : 0u));
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft) {
-        const int fr = 16 * ft + li, ca = 16 * ta + 4 * gq;
-        const Split2 a = two ? ld2_4x2(&sh.sAt[0][fr][ca], &sh.sAt[0][fr][ca + 16], TA)
-                             : ld2_4z(&sh.sAt[0][fr][ca], TA);
-        X[ft] = mm2_ss(a, ep, X[ft]);
-      }
+      for (int ft = 0; ft < NFT; ++ft) X[ft] = mm2_ss(aT[ft], ep, X[ft]);
     }
   }
 
