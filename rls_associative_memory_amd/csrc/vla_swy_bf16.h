@@ -56,7 +56,7 @@ struct SwbLds {
   uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_tt terms, row-major (final pass)
   uint16_t KaO[2][C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // -Ka_ba terms of each step
   uint16_t QaO[2][FINAL && C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // Qa_ba terms (final pass)
-  float Kd[C::NCT][16][20];                   // -Ka_b in fp32 for the block inverses
+  float Kd[C::NCT][16][20];                   // -Ka_b transposed, fp32, for the block inverses
   float rk[CH];                               // 1 / ||k||
   float rden[CH];                             // 1 / readout denominator
 };
@@ -286,9 +286,9 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           }
         } else {
           const float nk0 = -acc[r] * sh.rk[16 * ct + i], nk1 = -acc[r + 1] * sh.rk[16 * ct + i + 1];
-          if (diag) {
-            sh.Kd[ct][i][li] = li >= i ? 0.f : nk0;
-            sh.Kd[ct][i + 1][li] = li >= i + 1 ? 0.f : nk1;
+          if (diag) {  // Kd[q][i] = -Ka[i][q]
+            sh.Kd[ct][li][i] = li >= i ? 0.f : nk0;
+            sh.Kd[ct][li][i + 1] = li >= i + 1 ? 0.f : nk1;
           } else {
             uint32_t t2[2];
             split_pk<2>(nk0, nk1, t2);
@@ -301,7 +301,9 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         }
       }
       if (!isq && diag) {
-        // (I + Ka_b)^{-1} by forward substitution in lanes 0..15 (column j = lane).
+        // (I + Ka_b)^{-1} by forward substitution in lanes 0..15 (column j = lane),
+        // right-looking: once x_q is final it is applied to all later rows at once, so the
+        // dependent chain is one multiply-add per pivot.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -309,16 +311,16 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           const int j = lane;
           float x[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float a = (i == j) ? 1.f : 0.f;
+          for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int q4 = 0; q4 < i; q4 += 4) {
-              const f4_t kr = *reinterpret_cast<const f4_t *>(&sh.Kd[ct][i][q4]);  // -Ka row
+          for (int q = 0; q < 15; ++q) {
+#pragma unroll
+            for (int i4 = (q + 1) / 4; i4 < 4; ++i4) {
+              const f4_t kc = *reinterpret_cast<const f4_t *>(&sh.Kd[ct][q][4 * i4]);  // -Ka column q
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (q4 + e < i) a = fmaf(kr[e], x[q4 + e], a);
+                if (4 * i4 + e > q) x[4 * i4 + e] = fmaf(kc[e], x[q], x[4 * i4 + e]);
             }
-            x[i] = a;
           }
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
