@@ -99,7 +99,16 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     pv[1] = *reinterpret_cast<const uint4 *>(ks + cs * D + off);
     pv[2] = *reinterpret_cast<const uint4 *>(qs + cs * D + off);
   };
+  // Rows of the chunk at cs, staged into LDS; rows past the segment become zeros.
+  auto stage = [&](int64_t cs, int tid) {
+    const int sc = tid / (D / 8), sf0 = (tid % (D / 8)) * 8;
+    const bool ok = cs + sc < te;
+    *reinterpret_cast<uint4 *>(&sh.sU[sc][sf0]) = keep_if(ok, pv[0]);
+    *reinterpret_cast<uint4 *>(&sh.sK[sc][sf0]) = keep_if(ok, pv[1]);
+    *reinterpret_cast<uint4 *>(&sh.sQ[sc][sf0]) = keep_if(ok, pv[2]);
+  };
   prefetch(tb, tid);
+  stage(tb, tid);
   // Z0 or Z (this wave's 16 features x 32 tokens, features-as-rows accumulators) into LDS,
   // row-major by token (B operand over features) and token-packed (A operand over tokens).
   auto publish = [&](const f4_t (&zt)[2]) {
@@ -128,15 +137,11 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     int tid_o = threadIdx.x;
     asm volatile("" : "+v"(tid_o));
     const int tid = tid_o, lane = tid & 63, li = lane & 15, gq = lane >> 4;
-    {
-      const int sc = tid / (D / 8), sf0 = (tid % (D / 8)) * 8;
-      const bool ok = sc < m;
-      __syncthreads();
-      *reinterpret_cast<uint4 *>(&sh.sU[sc][sf0]) = keep_if(ok, pv[0]);
-      *reinterpret_cast<uint4 *>(&sh.sK[sc][sf0]) = keep_if(ok, pv[1]);
-      *reinterpret_cast<uint4 *>(&sh.sQ[sc][sf0]) = keep_if(ok, pv[2]);
-      __syncthreads();
-    }
+    // The previous chunk's last readers are done and this chunk's rows (staged during the
+    // previous chunk) are visible.  The next chunk's rows are loaded now and staged once
+    // this chunk has read its own (after X~).
+    __syncthreads();
+    if (c0 + CH < te) prefetch(c0 + CH, tid);
 
     // ---- [Z0^T | P^T] = A [U^T | K^T] (rows 16w.., 32 tokens) ---------------------------
     f4_t Z0t[2], Pt[2];
@@ -244,7 +249,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       float myd0 = 1.f;
       ldl16(x, myd0);
       if (lane < 16) {
-        sh.rd[lane] = 1.0f / myd0;
+        sh.rd[lane] = __builtin_amdgcn_rcpf(myd0);
         sh.rsd[lane] = rsqrtf(myd0);
       } else if (lane < 32) {
 #pragma unroll
@@ -289,7 +294,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       float myd1 = 1.f;
       ldl16(y, myd1);
       if (lane < 16) {
-        sh.rd[16 + lane] = 1.0f / myd1;
+        sh.rd[16 + lane] = __builtin_amdgcn_rcpf(myd1);
         sh.rsd[16 + lane] = rsqrtf(myd1);
       } else if (lane >= 32) {
 #pragma unroll
@@ -374,8 +379,6 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       }
     }
     __syncthreads();
-    // next chunk's rows: issued here so the loads overlap the rest of this chunk
-    if (c0 + CH < te) prefetch(c0 + CH, tid);
     // ---- Z^T = Z0^T L^{-T} ---------------------------------------------------------------
     f4_t Zt[2];
 #pragma unroll
@@ -427,6 +430,8 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       }
     }
     __syncthreads();
+    // the next chunk's rows (sU, sK, sQ are not read again in this chunk)
+    if (c0 + CH < te) stage(c0 + CH, tid);
     // ---- W = D^{-1/2} Z, token-packed, into the (now free) row-major buffer --------------
     uint16_t *Wc = &sh.Zr[0][0][0];  // [NTERM][C/8][D][8]
 #pragma unroll
