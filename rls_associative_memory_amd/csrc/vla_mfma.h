@@ -93,6 +93,26 @@ __device__ __forceinline__ void ld_split(bf16x8_t (&dst)[3], const uint16_t *bas
 __device__ __forceinline__ uint16_t bf_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 __device__ __forceinline__ float bf_val(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
+// ---- transposing LDS load (ds_read_b64_tr_b16) --------------------------------------------
+// In each group of 16 lanes, lane j supplies the address of four 16-bit elements and lane i
+// receives element i % 4 of lane 4 e + i / 4 (e = 0..3), as checked on the device.  So when
+// lane j of the group addresses &M[r0 + j / 4][c0 + 4 (j % 4)] of a row-major 16-bit matrix
+// M, lane i receives M[r0 + e][c0 + i], e = 0..3: four consecutive rows of its column.
+typedef short s4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ld_tr4(const uint16_t *p) {
+  typedef s4_t __attribute__((address_space(3))) *lds_s4_ptr;  // p points into LDS
+  const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+// Two transposed 4 x 16 blocks as one bf16 operand: lane i gets M[r0 + e][c0 + i] (e < 4) and
+// M[r1 + e][c0 + i]; `li` is the lane's index in its group of 16.
+__device__ __forceinline__ bf16x8_t ld_tr4x2(const uint16_t *m, int ld, int r0, int r1, int c0, int li) {
+  const int dr = li >> 2, dc = 4 * (li & 3);
+  const uint2 a = ld_tr4(m + (r0 + dr) * ld + c0 + dc);
+  const uint2 b = ld_tr4(m + (r1 + dr) * ld + c0 + dc);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+
 // ---- packed splits: two fp32 values at a time through v_cvt_pk_bf16_f32 -----------------
 // pk_bf16(a, b) rounds both to bf16 (nearest even), a in the low half.  A term's value is
 // recovered by placing its half in the high bits of an fp32 word, so a residual costs a

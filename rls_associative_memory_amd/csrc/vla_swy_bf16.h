@@ -49,8 +49,7 @@ struct SwbLds {
   static constexpr int QR = FINAL ? CH : 1;
   uint16_t sK[CH][C::LDF];                    // raw k, by token
   uint16_t sV[CH][C::LDF];                    // raw v, by token
-  uint16_t sAh[2][CH][C::LDF];                // ahat terms, by token
-  uint16_t sAt[2][D][C::LDC];                 // ahat terms, by feature
+  uint16_t sAt[2][D][C::LDC];                 // ahat terms, by feature (read transposed for Ka, Qa)
   uint16_t sFq[2][QR][C::LDF];                // phi(q) terms, by token (final pass)
   uint16_t InvS[2][C::NCT][16][C::LDI];       // (I + Ka_b)^{-1} terms, row-major
   uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_tt terms, row-major (final pass)
@@ -69,7 +68,6 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
        float *__restrict__ S_final, int64_t T, int64_t L, int64_t P) {
   using C = SwbCfg<D, CH, FINAL>;
   constexpr int NT = C::NT, NCT = C::NCT, NFT = C::NFT, NKS = C::NKS;
-  constexpr int TF = CH * C::LDF;             // term strides
   constexpr int TQ = SwbLds<D, CH, FINAL>::QR * C::LDF;
   constexpr int TA = D * C::LDC;
   constexpr int TQD = (FINAL ? NCT : 1) * 16 * C::LDI;
@@ -199,9 +197,6 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           const bool ok = c + t < m;
           split_pk<2>(ok ? pa[i][t].x : 0.f, ok ? pa[i][t].y : 0.f, w[t][0]);
           split_pk<2>(ok ? pa[i][t].z : 0.f, ok ? pa[i][t].w : 0.f, w[t][1]);
-#pragma unroll
-          for (int term = 0; term < 2; ++term)
-            *reinterpret_cast<uint2 *>(&sh.sAh[term][c + t][f0]) = make_uint2(w[t][0][term], w[t][1][term]);
         }
         // by feature: the two tokens of the pair in one 32-bit word
 #pragma unroll
@@ -237,7 +232,9 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
         for (int ksl = 0; ksl < NKS; ++ksl) {
           const int fa = 32 * ksl + 4 * gq;
-          b[ksl] = ld2_4x2(&sh.sAh[0][16 * ct2 + li][fa], &sh.sAh[0][16 * ct2 + li][fa + 16], TF);
+          // Ahat[16 ct2 + li][fa + e], [fa + 16 + e] from the by-feature copy, transposed
+          b[ksl].h = ld_tr4x2(&sh.sAt[0][0][0], C::LDC, fa, fa + 16, 16 * ct2, li);
+          b[ksl].l = ld_tr4x2(&sh.sAt[1][0][0], C::LDC, fa, fa + 16, 16 * ct2, li);
         }
         f4_t part[NKS];
         if (isq) {
