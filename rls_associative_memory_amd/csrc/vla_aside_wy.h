@@ -41,8 +41,8 @@ struct AwyLds {
   uint16_t sU[C::C][C::LDU];
   uint16_t sK[C::C][C::LDU];
   uint16_t sQ[C::C][C::LDU];
-  uint16_t Zr[C::NTERM][C::C][C::LDU];          // row-major Z0 / Z terms; later W (token-packed)
-  uint16_t Zc[C::NTERM][C::C / 8][D][8];        // token-packed Z0 / Z terms: [c/8][f][c%8]
+  uint16_t Zr[C::NTERM][C::C][C::LDU];          // row-major Z0 terms, later W terms
+  uint16_t Zb[C::NTERM][C::C][C::LDU];          // row-major Z terms
   float G[C::C][C::C + 4];               // I + U A U^T (lower part used); then L^{-1}, row-major
   uint16_t LX[C::NTERM][C::C][C::LDL];          // X~ terms (B operand)
   float rsd[C::C], rd[C::C];
@@ -61,7 +61,6 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   using C = AwyCfg<D>;
   constexpr int NW = C::NW, NT = C::NT, CH = C::C, NTM = C::NTERM;
   constexpr int ZR_T = CH * C::LDU;       // term stride of Zr
-  constexpr int ZC_T = CH * D;            // term stride of Zc / W
   constexpr int LX_T = CH * C::LDL;       // term stride of LX
   __shared__ __attribute__((aligned(16))) AwyLds<D> sh;
 
@@ -109,9 +108,10 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   };
   prefetch(tb, tid);
   stage(tb, tid);
-  // Z0 or Z (this wave's 16 features x 32 tokens, features-as-rows accumulators) into LDS,
-  // row-major by token (B operand over features) and token-packed (A operand over tokens).
-  auto publish = [&](const f4_t (&zt)[2]) {
+  // Z0, Z or W (this wave's 16 features x 32 tokens, features-as-rows accumulators) into LDS,
+  // row-major by token: a B operand over features as it is, an A or B operand over tokens
+  // through the transposing load.
+  auto publish = [&](const f4_t (&zt)[2], uint16_t (*buf)[CH][C::LDU]) {
     const int lane = threadIdx.x & 63, li = lane & 15, gq = lane >> 4;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -121,11 +121,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       const int c = 16 * ct + li, f = 16 * w + 4 * gq;
 #pragma unroll
       for (int t = 0; t < NTM; ++t) {
-        *reinterpret_cast<uint2 *>(&sh.Zr[t][c][f]) = make_uint2(w01[t], w23[t]);
-        sh.Zc[t][c / 8][f + 0][c % 8] = static_cast<uint16_t>(w01[t]);
-        sh.Zc[t][c / 8][f + 1][c % 8] = static_cast<uint16_t>(w01[t] >> 16);
-        sh.Zc[t][c / 8][f + 2][c % 8] = static_cast<uint16_t>(w23[t]);
-        sh.Zc[t][c / 8][f + 3][c % 8] = static_cast<uint16_t>(w23[t] >> 16);
+        *reinterpret_cast<uint2 *>(&buf[t][c][f]) = make_uint2(w01[t], w23[t]);
       }
     }
   };
@@ -163,8 +159,8 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         Pt[ct] = mmn_sx<NTM>(af, bk, Pt[ct]);
       }
     }
-    // ---- publish Z0: row-major (for G) and token-packed (for L^{-1} Z0) -----------------
-    publish(Z0t);
+    // ---- publish Z0 (for G and L^{-1} Z0) -------------------------------------------------
+    publish(Z0t, sh.Zr);
     __syncthreads();
     // ---- G = I + U Z0^T on the lower 16-tiles (0,0), (1,0), (1,1) ----------------------
     for (int tile = w; tile < 4; tile += NW) {
@@ -384,16 +380,15 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       bf16x8_t a[NTM], b[NTM];
-      ld_split_n<NTM>(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
+      ld_tr_n<NTM>(a, &sh.Zr[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * w, li);  // Z0^T
       const f4_t l0 = *reinterpret_cast<const f4_t *>(&sh.G[16 * ct + li][8 * gq]);
       const f4_t l1 = *reinterpret_cast<const f4_t *>(&sh.G[16 * ct + li][8 * gq + 4]);
       const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
       split_n8<NTM>(lv, b);
       Zt[ct] = mmn_ss<NTM>(a, b, f4_zero());
     }
-    __syncthreads();
-    // ---- publish Z: row-major (for K Z^T) and token-packed (for X~ Z) ---------------------
-    publish(Zt);
+    // ---- publish Z into the second buffer (for K Z^T and X~ Z) ----------------------------
+    publish(Zt, sh.Zb);
     __syncthreads();
     // ---- X~ = tril0(K Z^T) D^{-1} on tiles (0,0), (1,0), (1,1); the (0,1) tile is zero --
     for (int tile = w; tile < 4; tile += NW) {
@@ -412,7 +407,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       for (int ksl = 0; ksl < C::NKS; ++ksl) {
         const bf16x8_t a = ld_bf8(&sh.sK[16 * it + li][32 * ksl + 8 * gq]);
         bf16x8_t b[NTM];
-        ld_split_n<NTM>(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
+        ld_split_n<NTM>(b, &sh.Zb[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
         hacc = mmn_xs<NTM>(a, b, hacc);
       }
       const int j = 16 * jt + li;
@@ -432,31 +427,23 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     __syncthreads();
     // the next chunk's rows (sU, sK, sQ are not read again in this chunk)
     if (c0 + CH < te) stage(c0 + CH, tid);
-    // ---- W = D^{-1/2} Z, token-packed, into the (now free) row-major buffer --------------
-    uint16_t *Wc = &sh.Zr[0][0][0];  // [NTERM][C/8][D][8]
+    // ---- W = D^{-1/2} Z into the first buffer (Z0 is no longer read) ----------------------
+    {
+      f4_t Ws[2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int c = 16 * ct + li;
-      const float sc2 = sh.rsd[c];
+      for (int ct = 0; ct < 2; ++ct) {
+        const float sc2 = sh.rsd[16 * ct + li];
 #pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        uint32_t tm[NTM];
-        split_pk<NTM>(Zt[ct][r] * sc2, Zt[ct][r + 1] * sc2, tm);
-        const int f = 16 * w + 4 * gq + r;
-        const int idx = ((c / 8) * D + f) * 8 + (c % 8);
-#pragma unroll
-        for (int t = 0; t < NTM; ++t) {
-          Wc[t * ZC_T + idx] = static_cast<uint16_t>(tm[t]);
-          Wc[t * ZC_T + idx + 8] = static_cast<uint16_t>(tm[t] >> 16);
-        }
+        for (int r = 0; r < 4; ++r) Ws[ct][r] = Zt[ct][r] * sc2;
       }
+      publish(Ws, sh.Zr);
     }
     // ---- Y^T = P^T - Z^T X~^T, then the gates ----------------------------------------------
     f4_t Yt[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       bf16x8_t a[NTM], b[NTM];
-      ld_split_n<NTM>(a, &sh.Zc[0][gq][16 * w + li][0], ZC_T);
+      ld_tr_n<NTM>(a, &sh.Zb[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * w, li);  // Z^T
       ld_split_n<NTM>(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
       const f4_t xz = mmn_ss<NTM>(a, b, f4_zero());
 #pragma unroll
@@ -483,11 +470,11 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // ---- A <- A - W^T W on this wave's column tile ------------------------------------------
     {
       bf16x8_t b[NTM];
-      ld_split_n<NTM>(b, &Wc[(gq * D + 16 * w + li) * 8], ZC_T);
+      ld_tr_n<NTM>(b, &sh.Zr[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * w, li);
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
         bf16x8_t a[NTM];
-        ld_split_n<NTM>(a, &Wc[(gq * D + 16 * it + li) * 8], ZC_T);
+        ld_tr_n<NTM>(a, &sh.Zr[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * it, li);
         const f4_t t4 = mmn_ss<NTM>(a, b, f4_zero());
 #pragma unroll
         for (int r = 0; r < 4; ++r) At[it][r] -= t4[r];

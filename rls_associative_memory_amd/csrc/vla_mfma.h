@@ -113,6 +113,14 @@ __device__ __forceinline__ bf16x8_t ld_tr4x2(const uint16_t *m, int ld, int r0, 
   return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
 }
 
+// N terms of a row-major matrix (term stride in elements), each read as ld_tr4x2
+template <int N>
+__device__ __forceinline__ void ld_tr_n(bf16x8_t (&dst)[N], const uint16_t *m, int term_stride, int ld,
+                                        int r0, int r1, int c0, int li) {
+#pragma unroll
+  for (int t = 0; t < N; ++t) dst[t] = ld_tr4x2(m + t * term_stride, ld, r0, r1, c0, li);
+}
+
 // ---- packed splits: two fp32 values at a time through v_cvt_pk_bf16_f32 -----------------
 // pk_bf16(a, b) rounds both to bf16 (nearest even), a in the low half.  A term's value is
 // recovered by placing its half in the high bits of an fp32 word, so a residual costs a
