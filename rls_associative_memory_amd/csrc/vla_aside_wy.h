@@ -143,20 +143,31 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     f4_t Z0t[2], Pt[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) { Z0t[ct] = f4_zero(); Pt[ct] = f4_zero(); }
+    // Token rows of U and K for feature slice ksl; the next slice's are loaded before this
+    // slice's products so that one LDS latency hides behind the matrix cores.
+    auto ld_uk = [&](int ksl, bf16x8_t (&o)[2][2]) {
+      const int f0 = 32 * ksl + 4 * gq, f1 = 32 * ksl + 16 + 4 * gq;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        o[ct][0] = ld_bf4x2(&sh.sU[16 * ct + li][f0], &sh.sU[16 * ct + li][f1]);
+        o[ct][1] = ld_bf4x2(&sh.sK[16 * ct + li][f0], &sh.sK[16 * ct + li][f1]);
+      }
+    };
+    bf16x8_t uk[2][2][2];
+    ld_uk(0, uk[0]);
 #pragma unroll
     for (int ksl = 0; ksl < C::NKS; ++ksl) {
+      if (ksl + 1 < C::NKS) ld_uk(ksl + 1, uk[(ksl + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this slice's products
       float x[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) { x[r] = At[2 * ksl][r]; x[4 + r] = At[2 * ksl + 1][r]; }
       bf16x8_t af[NTM];
       split_n8<NTM>(x, af);
-      const int f0 = 32 * ksl + 4 * gq, f1 = 32 * ksl + 16 + 4 * gq;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const bf16x8_t bu = ld_bf4x2(&sh.sU[16 * ct + li][f0], &sh.sU[16 * ct + li][f1]);
-        const bf16x8_t bk = ld_bf4x2(&sh.sK[16 * ct + li][f0], &sh.sK[16 * ct + li][f1]);
-        Z0t[ct] = mmn_sx<NTM>(af, bu, Z0t[ct]);
-        Pt[ct] = mmn_sx<NTM>(af, bk, Pt[ct]);
+        Z0t[ct] = mmn_sx<NTM>(af, uk[ksl & 1][ct][0], Z0t[ct]);
+        Pt[ct] = mmn_sx<NTM>(af, uk[ksl & 1][ct][1], Pt[ct]);
       }
     }
     // ---- publish Z0 (for G and L^{-1} Z0) -------------------------------------------------
@@ -469,13 +480,15 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
     // ---- A <- A - W^T W on this wave's column tile ------------------------------------------
     {
-      bf16x8_t b[NTM];
+      bf16x8_t b[NTM], a[2][NTM];
       ld_tr_n<NTM>(b, &sh.Zr[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * w, li);
+      ld_tr_n<NTM>(a[0], &sh.Zr[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 0, li);
 #pragma unroll
       for (int it = 0; it < NW; ++it) {
-        bf16x8_t a[NTM];
-        ld_tr_n<NTM>(a, &sh.Zr[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * it, li);
-        const f4_t t4 = mmn_ss<NTM>(a, b, f4_zero());
+        if (it + 1 < NW)  // next row tile's operand first
+          ld_tr_n<NTM>(a[(it + 1) & 1], &sh.Zr[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * (it + 1), li);
+        __builtin_amdgcn_sched_barrier(0);
+        const f4_t t4 = mmn_ss<NTM>(a[it & 1], b, f4_zero());
 #pragma unroll
         for (int r = 0; r < 4; ++r) At[it][r] -= t4[r];
       }
