@@ -181,14 +181,16 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         continue;
       }
       const int it = (tile == 0) ? 0 : 1, jt = (tile == 2) ? 1 : 0;
-      f4_t g = f4_zero();
+      bf16x8_t a[C::NKS], b[C::NKS][NTM];  // all operands first: one LDS latency
 #pragma unroll
       for (int ksl = 0; ksl < C::NKS; ++ksl) {
-        const bf16x8_t a = ld_bf8(&sh.sU[16 * it + li][32 * ksl + 8 * gq]);
-        bf16x8_t b[NTM];
-        ld_split_n<NTM>(b, &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
-        g = mmn_xs<NTM>(a, b, g);
+        a[ksl] = ld_bf8(&sh.sU[16 * it + li][32 * ksl + 8 * gq]);
+        ld_split_n<NTM>(b[ksl], &sh.Zr[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      f4_t g = f4_zero();
+#pragma unroll
+      for (int ksl = 0; ksl < C::NKS; ++ksl) g = mmn_xs<NTM>(a[ksl], b[ksl], g);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * it + 4 * gq + r, j = 16 * jt + li;
@@ -388,15 +390,24 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     __syncthreads();
     // ---- Z^T = Z0^T L^{-T} ---------------------------------------------------------------
     f4_t Zt[2];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      bf16x8_t a[NTM], b[NTM];
+    {
+      bf16x8_t a[NTM];
+      f4_t l[2][2];
       ld_tr_n<NTM>(a, &sh.Zr[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * w, li);  // Z0^T
-      const f4_t l0 = *reinterpret_cast<const f4_t *>(&sh.G[16 * ct + li][8 * gq]);
-      const f4_t l1 = *reinterpret_cast<const f4_t *>(&sh.G[16 * ct + li][8 * gq + 4]);
-      const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-      split_n8<NTM>(lv, b);
-      Zt[ct] = mmn_ss<NTM>(a, b, f4_zero());
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        l[ct][0] = *reinterpret_cast<const f4_t *>(&sh.G[16 * ct + li][8 * gq]);
+        l[ct][1] = *reinterpret_cast<const f4_t *>(&sh.G[16 * ct + li][8 * gq + 4]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        bf16x8_t b[NTM];
+        const float lv[8] = {l[ct][0][0], l[ct][0][1], l[ct][0][2], l[ct][0][3],
+                             l[ct][1][0], l[ct][1][1], l[ct][1][2], l[ct][1][3]};
+        split_n8<NTM>(lv, b);
+        Zt[ct] = mmn_ss<NTM>(a, b, f4_zero());
+      }
     }
     // ---- publish Z into the second buffer (for K Z^T and X~ Z) ----------------------------
     publish(Zt, sh.Zb);
@@ -413,14 +424,16 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         continue;
       }
       const int it = (tile == 0) ? 0 : 1, jt = (tile == 2) ? 1 : 0;
-      f4_t hacc = f4_zero();
+      bf16x8_t a[C::NKS], b[C::NKS][NTM];  // all operands first: one LDS latency
 #pragma unroll
       for (int ksl = 0; ksl < C::NKS; ++ksl) {
-        const bf16x8_t a = ld_bf8(&sh.sK[16 * it + li][32 * ksl + 8 * gq]);
-        bf16x8_t b[NTM];
-        ld_split_n<NTM>(b, &sh.Zb[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
-        hacc = mmn_xs<NTM>(a, b, hacc);
+        a[ksl] = ld_bf8(&sh.sK[16 * it + li][32 * ksl + 8 * gq]);
+        ld_split_n<NTM>(b[ksl], &sh.Zb[0][16 * jt + li][32 * ksl + 8 * gq], ZR_T);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      f4_t hacc = f4_zero();
+#pragma unroll
+      for (int ksl = 0; ksl < C::NKS; ++ksl) hacc = mmn_xs<NTM>(a[ksl], b[ksl], hacc);
       const int j = 16 * jt + li;
       const float rdj = sh.rd[j];
 #pragma unroll
@@ -451,12 +464,14 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
     // ---- Y^T = P^T - Z^T X~^T, then the gates ----------------------------------------------
     f4_t Yt[2];
+    bf16x8_t za[NTM], xb[2][NTM];
+    ld_tr_n<NTM>(za, &sh.Zb[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * w, li);  // Z^T
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) ld_split_n<NTM>(xb[ct], &sh.LX[0][16 * ct + li][8 * gq], LX_T);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      bf16x8_t a[NTM], b[NTM];
-      ld_tr_n<NTM>(a, &sh.Zb[0][0][0], ZR_T, C::LDU, 8 * gq, 8 * gq + 4, 16 * w, li);  // Z^T
-      ld_split_n<NTM>(b, &sh.LX[0][16 * ct + li][8 * gq], LX_T);
-      const f4_t xz = mmn_ss<NTM>(a, b, f4_zero());
+      const f4_t xz = mmn_ss<NTM>(za, xb[ct], f4_zero());
 #pragma unroll
       for (int r = 0; r < 4; ++r) Yt[ct][r] = Pt[ct][r] - xz[r];
       float part = 0.f;
