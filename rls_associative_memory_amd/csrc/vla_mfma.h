@@ -246,6 +246,34 @@ __device__ __forceinline__ f4_t mm2_ss(const Split2 &a, const Split2 &b, f4_t c)
   c = mfma_bf16(a.h, b.l, c);
   return mfma_bf16(a.h, b.h, c);
 }
+// ---- K = 16 products (v_mfma_f32_16x16x16_bf16, checked on the device): lane l supplies
+// A[li][4 gq + e] and B[4 gq + e][li] (e < 4, two VGPRs each), D as above.  A D-layout tile is
+// then directly the B operand of the next product over its 16 rows.
+__device__ __forceinline__ f4_t mfma_bf16_k16(const uint2 &a, const uint2 &b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a), __builtin_bit_cast(s4_t, b),
+                                                   c, 0, 0, 0);
+}
+struct Split2h {
+  uint2 h, l;
+};
+// an accumulator tile (4 values) as a two-term K = 16 operand
+__device__ __forceinline__ Split2h split2_4h(const f4_t &v) {
+  uint32_t a[2], b[2];
+  split_pk<2>(v[0], v[1], a);
+  split_pk<2>(v[2], v[3], b);
+  return Split2h{make_uint2(a[0], b[0]), make_uint2(a[1], b[1])};
+}
+// four bf16 per term at p (term stride in elements)
+__device__ __forceinline__ Split2h ld2_4h(const uint16_t *p, int term_stride) {
+  return Split2h{*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + term_stride)};
+}
+// two-term x two-term over K = 16 (the l * l term dropped)
+__device__ __forceinline__ f4_t mm2h_ss(const Split2h &a, const Split2h &b, f4_t c) {
+  c = mfma_bf16_k16(a.l, b.h, c);
+  c = mfma_bf16_k16(a.h, b.l, c);
+  return mfma_bf16_k16(a.h, b.h, c);
+}
+
 // four bf16 at p0 and four at p1, or zeros for the second half
 __device__ __forceinline__ bf16x8_t ld_bf4z(const uint16_t *p0) {
   const uint2 a = *reinterpret_cast<const uint2 *>(p0);

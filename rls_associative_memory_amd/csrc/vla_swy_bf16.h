@@ -399,13 +399,13 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       }
       // E_a = (I + Ka_aa)^{-1} R_a;  E_b = (I + Ka_bb)^{-1} (R_b - Ka_ba E_a)
       f4_t E[2];
-      E[0] = mm2_ss(ld2_4z(&sh.InvS[0][ta][li][4 * gq], TI), split2_4z(R[0]), f4_zero());
-      const Split2 esa = split2_4z(E[0]);
-      Split2 esb = esa;
+      E[0] = mm2h_ss(ld2_4h(&sh.InvS[0][ta][li][4 * gq], TI), split2_4h(R[0]), f4_zero());
+      const Split2h esa = split2_4h(E[0]);
+      Split2h esb = esa;
       if (two) {
-        const f4_t rb = mm2_ss(ld2_4z(&sh.KaO[0][pr][li][4 * gq], TKO), esa, R[1]);
-        E[1] = mm2_ss(ld2_4z(&sh.InvS[0][tbb][li][4 * gq], TI), split2_4z(rb), f4_zero());
-        esb = split2_4z(E[1]);
+        const f4_t rb = mm2h_ss(ld2_4h(&sh.KaO[0][pr][li][4 * gq], TKO), esa, R[1]);
+        E[1] = mm2h_ss(ld2_4h(&sh.InvS[0][tbb][li][4 * gq], TI), split2_4h(rb), f4_zero());
+        esb = split2_4h(E[1]);
       }
       if constexpr (FINAL) {
         // Num_t = Phi(q)_t X^T + sum_{t' <= t} Qa_tt' E_t', then o = Num / den.
@@ -413,8 +413,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         for (int h = 0; h < 2; ++h) {
           const int ct = 2 * pr + h;
           if (ct >= NCT) continue;
-          f4_t num = mm2_ss(ld2_4z(&sh.QaD[0][ct][li][4 * gq], TQD), h ? esb : esa, numq[h]);
-          if (h) num = mm2_ss(ld2_4z(&sh.QaO[0][pr][li][4 * gq], TQO), esa, num);
+          f4_t num = mm2h_ss(ld2_4h(&sh.QaD[0][ct][li][4 * gq], TQD), h ? esb : esa, numq[h]);
+          if (h) num = mm2h_ss(ld2_4h(&sh.QaO[0][pr][li][4 * gq], TQO), esa, num);
 #pragma unroll
           for (int r = 0; r < 4; r += 2) {
             const int c = 16 * ct + 4 * gq + r;
@@ -426,12 +426,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       }
       // X^T += Ahat_a^T E_a + Ahat_b^T E_b  (one 32-token product)
       Split2 ep;
-      ep.h = __builtin_bit_cast(bf16x8_t, make_uint4(
-          __builtin_bit_cast(uint4, esa.h).x, __builtin_bit_cast(uint4, esa.h).y,
-          two ? __builtin_bit_cast(uint4, esb.h).x : 0u, two ? __builtin_bit_cast(uint4, esb.h).y : 0u));
-      ep.l = __builtin_bit_cast(bf16x8_t, make_uint4(
-          __builtin_bit_cast(uint4, esa.l).x, __builtin_bit_cast(uint4, esa.l).y,
-          two ? __builtin_bit_cast(uint4, esb.l).x : 0u, two ? __builtin_bit_cast(uint4, esb.l).y : 0u));
+      ep.h = __builtin_bit_cast(bf16x8_t, make_uint4(esa.h.x, esa.h.y, two ? esb.h.x : 0u, two ? esb.h.y : 0u));
+      ep.l = __builtin_bit_cast(bf16x8_t, make_uint4(esa.l.x, esa.l.y, two ? esb.l.x : 0u, two ? esb.l.y : 0u));
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) X[ft] = mm2_ss(aT[ft], ep, X[ft]);
     }
