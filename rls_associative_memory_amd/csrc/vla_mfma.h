@@ -267,6 +267,12 @@ __device__ __forceinline__ Split2h split2_4h(const f4_t &v) {
 __device__ __forceinline__ Split2h ld2_4h(const uint16_t *p, int term_stride) {
   return Split2h{*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + term_stride)};
 }
+// A 16 x 16 tile stored transposed (Tt[col][row], row stride ld) as the two-term K = 16 A
+// operand of lane (gq, li): M[li][4 gq + e] = Tt[4 gq + e][li], read with the transposing load.
+__device__ __forceinline__ Split2h ld2_tr4h(const uint16_t *tt, int ld, int term_stride, int gq, int li) {
+  const uint16_t *p = tt + (4 * gq + (li >> 2)) * ld + 4 * (li & 3);
+  return Split2h{ld_tr4(p), ld_tr4(p + term_stride)};
+}
 // two-term x two-term over K = 16 (the l * l term dropped)
 __device__ __forceinline__ f4_t mm2h_ss(const Split2h &a, const Split2h &b, f4_t c) {
   c = mfma_bf16_k16(a.l, b.h, c);

@@ -51,10 +51,12 @@ struct SwbLds {
   uint16_t sV[CH][C::LDF];                    // raw v, by token
   uint16_t sAt[2][D][C::LDC];                 // ahat terms, by feature (read transposed for Ka, Qa)
   uint16_t sFq[2][QR][C::LDF];                // phi(q) terms, by token (final pass)
-  uint16_t InvS[2][C::NCT][16][C::LDI];       // (I + Ka_b)^{-1} terms, row-major
-  uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_tt terms, row-major (final pass)
-  uint16_t KaO[2][C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // -Ka_ba terms of each step
-  uint16_t QaO[2][FINAL && C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // Qa_ba terms (final pass)
+  // 16 x 16 tiles as two bf16 terms, stored transposed ([col][row]): a lane writes its column
+  // with wide stores, and the A operands are read back with the transposing load.
+  uint16_t InvS[2][C::NCT][16][C::LDI];       // (I + Ka_b)^{-1}
+  uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_tt (final pass)
+  uint16_t KaO[2][C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // -Ka_ba of each step
+  uint16_t QaO[2][FINAL && C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // Qa_ba (final pass)
   float Kd[C::NCT][16][20];                   // -Ka_b transposed, fp32, for the block inverses
   float rk[CH];                               // 1 / ||k||
   float rden[CH];                             // 1 / readout denominator
@@ -262,38 +264,34 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
         for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
       }
-      // acc[r] = product[i = 4 gq + r][i'' = li] of tile (ct, ct2); rows split in pairs
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const int i = 4 * gq + r;
+      // acc[r] = product[i = 4 gq + r][i'' = li] of tile (ct, ct2): this lane's column li,
+      // rows 4 gq .. 4 gq + 3, stored transposed as one 8-byte piece per term.
+      {
+        const int i = 4 * gq;
         if (isq) {
           if constexpr (FINAL) {
-            uint32_t t2[2];
-            split_pk<2>(diag && li > i ? 0.f : acc[r], diag && li > i + 1 ? 0.f : acc[r + 1], t2);
+            f4_t v;
 #pragma unroll
-            for (int term = 0; term < 2; ++term) {
-              if (diag) {
-                sh.QaD[term][ct][i][li] = static_cast<uint16_t>(t2[term]);
-                sh.QaD[term][ct][i + 1][li] = static_cast<uint16_t>(t2[term] >> 16);
-              } else {
-                sh.QaO[term][jk - NCT][i][li] = static_cast<uint16_t>(t2[term]);
-                sh.QaO[term][jk - NCT][i + 1][li] = static_cast<uint16_t>(t2[term] >> 16);
-              }
-            }
+            for (int r = 0; r < 4; ++r) v[r] = diag && li > i + r ? 0.f : acc[r];
+            const Split2h t = split2_4h(v);
+            uint16_t *dst = diag ? &sh.QaD[0][ct][li][i] : &sh.QaO[0][jk - NCT][li][i];
+            const int ts = diag ? TQD : TQO;
+            *reinterpret_cast<uint2 *>(dst) = t.h;
+            *reinterpret_cast<uint2 *>(dst + ts) = t.l;
           }
         } else {
-          const float nk0 = -acc[r] * sh.rk[16 * ct + i], nk1 = -acc[r + 1] * sh.rk[16 * ct + i + 1];
-          if (diag) {  // Kd[q][i] = -Ka[i][q]
-            sh.Kd[ct][li][i] = li >= i ? 0.f : nk0;
-            sh.Kd[ct][li][i + 1] = li >= i + 1 ? 0.f : nk1;
-          } else {
-            uint32_t t2[2];
-            split_pk<2>(nk0, nk1, t2);
+          f4_t nk;
 #pragma unroll
-            for (int term = 0; term < 2; ++term) {
-              sh.KaO[term][jk - NCT][i][li] = static_cast<uint16_t>(t2[term]);
-              sh.KaO[term][jk - NCT][i + 1][li] = static_cast<uint16_t>(t2[term] >> 16);
-            }
+          for (int r = 0; r < 4; ++r) nk[r] = -acc[r] * sh.rk[16 * ct + i + r];
+          if (diag) {  // Kd[q][i] = -Ka[i][q]
+            f4_t kd;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) kd[r] = li >= i + r ? 0.f : nk[r];
+            *reinterpret_cast<f4_t *>(&sh.Kd[ct][li][i]) = kd;
+          } else {
+            const Split2h t = split2_4h(nk);
+            *reinterpret_cast<uint2 *>(&sh.KaO[0][jk - NCT][li][i]) = t.h;
+            *reinterpret_cast<uint2 *>(&sh.KaO[1][jk - NCT][li][i]) = t.l;
           }
         }
       }
@@ -319,15 +317,15 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
                 if (4 * i4 + e > q) x[4 * i4 + e] = fmaf(kc[e], x[q], x[4 * i4 + e]);
             }
           }
+          // column j of the inverse, transposed: row j of InvS, 16 values per term
+          uint32_t w[8][2];
 #pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            uint32_t t2[2];
-            split_pk<2>(x[i], x[i + 1], t2);
+          for (int i = 0; i < 16; i += 2) split_pk<2>(x[i], x[i + 1], w[i / 2]);
 #pragma unroll
-            for (int term = 0; term < 2; ++term) {
-              sh.InvS[term][ct][i][j] = static_cast<uint16_t>(t2[term]);
-              sh.InvS[term][ct][i + 1][j] = static_cast<uint16_t>(t2[term] >> 16);
-            }
+          for (int term = 0; term < 2; ++term) {
+            uint4 *dst = reinterpret_cast<uint4 *>(&sh.InvS[term][ct][j][0]);
+            dst[0] = make_uint4(w[0][term], w[1][term], w[2][term], w[3][term]);
+            dst[1] = make_uint4(w[4][term], w[5][term], w[6][term], w[7][term]);
           }
         }
       }
@@ -399,12 +397,12 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       }
       // E_a = (I + Ka_aa)^{-1} R_a;  E_b = (I + Ka_bb)^{-1} (R_b - Ka_ba E_a)
       f4_t E[2];
-      E[0] = mm2h_ss(ld2_4h(&sh.InvS[0][ta][li][4 * gq], TI), split2_4h(R[0]), f4_zero());
+      E[0] = mm2h_ss(ld2_tr4h(&sh.InvS[0][ta][0][0], C::LDI, TI, gq, li), split2_4h(R[0]), f4_zero());
       const Split2h esa = split2_4h(E[0]);
       Split2h esb = esa;
       if (two) {
-        const f4_t rb = mm2h_ss(ld2_4h(&sh.KaO[0][pr][li][4 * gq], TKO), esa, R[1]);
-        E[1] = mm2h_ss(ld2_4h(&sh.InvS[0][tbb][li][4 * gq], TI), split2_4h(rb), f4_zero());
+        const f4_t rb = mm2h_ss(ld2_tr4h(&sh.KaO[0][pr][0][0], C::LDI, TKO, gq, li), esa, R[1]);
+        E[1] = mm2h_ss(ld2_tr4h(&sh.InvS[0][tbb][0][0], C::LDI, TI, gq, li), split2_4h(rb), f4_zero());
         esb = split2_4h(E[1]);
       }
       if constexpr (FINAL) {
@@ -413,8 +411,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         for (int h = 0; h < 2; ++h) {
           const int ct = 2 * pr + h;
           if (ct >= NCT) continue;
-          f4_t num = mm2h_ss(ld2_4h(&sh.QaD[0][ct][li][4 * gq], TQD), h ? esb : esa, numq[h]);
-          if (h) num = mm2h_ss(ld2_4h(&sh.QaO[0][pr][li][4 * gq], TQO), esa, num);
+          f4_t num = mm2h_ss(ld2_tr4h(&sh.QaD[0][ct][0][0], C::LDI, TQD, gq, li), h ? esb : esa, numq[h]);
+          if (h) num = mm2h_ss(ld2_tr4h(&sh.QaO[0][pr][0][0], C::LDI, TQO, gq, li), esa, num);
 #pragma unroll
           for (int r = 0; r < 4; r += 2) {
             const int c = 16 * ct + 4 * gq + r;
