@@ -13,7 +13,8 @@
  *   n_t    = n_{t-1} + phi(k_t),  phi(x) = x + 1 (x > 0), e^x (x <= 0)   (ELU+1, §2.3)
  *   o_t    = S_t phi(q_t) / (n_t^T phi(q_t) + eps)            (ratio readout, §2.3)
  *
- * from the fixed initial state A_0 = I / lambda0, S_0 = 0, n_0 = 0.  Readings of what the
+ * from the initial state A_0 = I / lambda0, S_0 = 0, n_0 = 0 (vla_forward) or a carried
+ * state (vla_forward_state).  Readings of what the
  * pages leave open: z_t = A_{t-1} u_t with u_t a per-token input used as given; a zero
  * key gives khat = 0 and a zero A_t khat gives ahat = 0 (no memory write; A still
  * downdates).
@@ -90,6 +91,33 @@ typedef struct {
 vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
                          float lambda0, void *out, float *S_final, float *A_final,
                          const vla_desc_t *desc, struct ihipStream_t *stream);
+
+/*
+ * vla_forward_state -- vla_forward continuing from a carried state: the streaming use of
+ * the recurrence (VLA summary §5, practical scope: a fixed-size state for streaming
+ * inference without a KV cache), where a long stream is fed in
+ * pieces (or one token at a time, T = 1: decoding) and each call starts from the state the
+ * previous one ended in.
+ *
+ * S0          device pointer to [B, H, d, d] fp32: S before the first token, or NULL for 0.
+ * A0          device pointer to [B, H, d, d] fp32: A before the first token (the inverse
+ *             penalty; symmetric positive definite, e.g. a previous call's A_final), or NULL
+ *             for I / lambda0.  It is used as (A0 + A0^T) / 2.
+ * n0          device pointer to [B, H, d] fp32: the readout normaliser n before the first
+ *             token (a previous call's n_final), or NULL for 0.
+ * lambda0     as in vla_forward; only read when A0 is NULL.
+ * S_final, A_final   as in vla_forward.
+ * n_final     device pointer to [B, H, d] fp32 receiving n_T, or NULL.
+ * The other arguments, ownership, workspace and error behaviour are those of vla_forward
+ * (state pointers must be 16-byte aligned, else VLA_ERROR_NOT_SUPPORTED).  Splitting a
+ * sequence into two calls, the second starting from the first's (S_final, A_final,
+ * n_final), gives the single call's result up to rounding.  vla_forward is this call with
+ * S0 = A0 = n0 = NULL and n_final = NULL.
+ */
+vla_status_t vla_forward_state(const void *q, const void *k, const void *v, const void *u,
+                               float lambda0, const float *S0, const float *A0, const float *n0,
+                               void *out, float *S_final, float *A_final, float *n_final,
+                               const vla_desc_t *desc, struct ihipStream_t *stream);
 
 /* Bytes of device workspace vla_forward needs for this descriptor (0 for the
  * sequential path).  Same argument checks as vla_forward; no device work. */

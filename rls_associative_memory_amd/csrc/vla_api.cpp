@@ -171,18 +171,20 @@ vla_status_t vla_workspace_size(const vla_desc_t *desc, size_t *bytes) {
   return VLA_SUCCESS;
 }
 
-vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
-                         float lambda0, void *out, float *S_final, float *A_final,
-                         const vla_desc_t *desc, struct ihipStream_t *stream) {
+vla_status_t vla_forward_state(const void *q, const void *k, const void *v, const void *u,
+                               float lambda0, const float *S0, const float *A0, const float *n0,
+                               void *out, float *S_final, float *A_final, float *n_final,
+                               const vla_desc_t *desc, struct ihipStream_t *stream) {
   vla_status_t st = check_desc(desc);
   if (st != VLA_SUCCESS) return st;
   if (q == nullptr || k == nullptr || v == nullptr || u == nullptr || out == nullptr)
     return VLA_ERROR_INVALID_VALUE;
-  if (!(lambda0 > 0.0f) || !std::isfinite(lambda0)) return VLA_ERROR_INVALID_VALUE;
+  if (A0 == nullptr && (!(lambda0 > 0.0f) || !std::isfinite(lambda0))) return VLA_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(u) || !aligned16(out) ||
-      !aligned16(S_final) || !aligned16(A_final))
+      !aligned16(S_final) || !aligned16(A_final) || !aligned16(n_final) || !aligned16(S0) ||
+      !aligned16(A0) || !aligned16(n0))
     return VLA_ERROR_NOT_SUPPORTED;
-  const vla::Problem p = make_problem(desc, lambda0);
+  const vla::Problem p = make_problem(desc, A0 != nullptr ? 1.0f : lambda0);
   int32_t path = 0;
   int chunk = 0;
   st = resolve(desc, p, &path, &chunk);
@@ -201,13 +203,31 @@ vla_status_t vla_forward(const void *q, const void *k, const void *v, const void
     st = cached_workspace(vla::chunk_workspace_bytes(p, chunk), &ws);
     if (st != VLA_SUCCESS) return st;
   }
+  vla::StateIO sio;
+  sio.S0 = S0;
+  sio.A0 = A0;
+  sio.n0 = n0;
+  sio.S_final = S_final;
+  sio.A_final = A_final;
+  sio.n_final = n_final;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t err;
   if (path == VLA_PATH_SEQ)
-    err = vla::launch_seq(p, q, k, v, u, out, S_final, A_final, s);
+    err = vla::launch_seq(p, q, k, v, u, out, sio, s);
   else
-    err = vla::launch_chunk(p, chunk, q, k, v, u, out, S_final, A_final, ws, s);
+    err = vla::launch_chunk(p, chunk, q, k, v, u, out, sio, ws, s);
   return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
+}
+
+vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
+                         float lambda0, void *out, float *S_final, float *A_final,
+                         const vla_desc_t *desc, struct ihipStream_t *stream) {
+  if (!(lambda0 > 0.0f) || !std::isfinite(lambda0)) {
+    const vla_status_t st = check_desc(desc);
+    return st != VLA_SUCCESS ? st : VLA_ERROR_INVALID_VALUE;
+  }
+  return vla_forward_state(q, k, v, u, lambda0, nullptr, nullptr, nullptr, out, S_final, A_final,
+                           nullptr, desc, stream);
 }
 
 }  // extern "C"

@@ -57,7 +57,8 @@ __global__ void __launch_bounds__(AwyCfg<D>::NT)
 k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
            const bf16_t *__restrict__ u, const float *__restrict__ A0,
            const float *__restrict__ nk0, float *__restrict__ alpha, float *__restrict__ rkden,
-           float *__restrict__ A_final, int64_t T, int64_t L, int64_t P, float eps) {
+           float *__restrict__ A_final, float *__restrict__ n_final, int64_t T, int64_t L,
+           int64_t P, float eps) {
   using C = AwyCfg<D>;
   constexpr int NW = C::NW, NT = C::NT, CH = C::C, NTM = C::NTERM;
   constexpr int ZR_T = CH * C::LDU;       // term stride of Zr
@@ -510,6 +511,13 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
   }
 
+  if (n_final != nullptr && p == P - 1) {
+    // n after the segment's last chunk (chunk c writes nbuf[(c & 1) ^ 1]), before any reuse
+    // of the LDS below.
+    __syncthreads();
+    const int nch = static_cast<int>((te - tb + CH - 1) / CH);
+    for (int f = tid; f < D; f += NT) n_final[s * D + f] = sh.nbuf[nch & 1][f];
+  }
   if (A_final != nullptr && p == P - 1) {
     // Symmetrise through LDS: A_T <- (A + A^T) / 2.
     __syncthreads();

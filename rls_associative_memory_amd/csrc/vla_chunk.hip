@@ -45,7 +45,7 @@ namespace vla {
 struct ChunkPlan {
   int D = 0, C = 0;
   int64_t S = 0, T = 0, L = 0, P = 0;
-  size_t off_m = 0, off_nk = 0, off_alpha = 0, off_rkden = 0, off_pib = 0, off_s0 = 0;
+  size_t off_m = 0, off_nk = 0, off_alpha = 0, off_rkden = 0, off_pib = 0, off_s0 = 0, off_minv = 0;
   size_t total = 0;
 };
 
@@ -75,6 +75,7 @@ static ChunkPlan make_plan(const Problem &p, int C) {
   pl.off_rkden = off; off = align256(off + S * static_cast<size_t>(pl.T) * 2 * 4);
   pl.off_pib = off;   off = align256(off + S * P * 2 * D * D * 4);
   pl.off_s0 = off;    off = align256(off + S * P * D * D * 4);
+  pl.off_minv = off;  off = align256(off + S * D * D * 4);  // A0^{-1} of a carried state
   pl.total = off;
   return pl;
 }
@@ -265,31 +266,51 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
 }
 
 // ------------------------------------------------------------------------------------
-// k_prefix: M_p <- lambda0 I + sum_{p' < p} Gram_p' (fp64 sums), nk_p <- sum_{p'<p} nk_p'
+// k_prefix: M_p <- M_0 + sum_{p' < p} Gram_p' (fp64 sums), nk_p <- n_0 + sum_{p'<p} nk_p',
+// with M_0 = lambda0 I and n_0 = 0, or a carried state's A_0^{-1} (Minit) and n_0.
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256)
-k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0) {
+k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0,
+         const float *__restrict__ Minit, const float *__restrict__ n0) {
   const int64_t s = blockIdx.x;
   const int e = blockIdx.y * 256 + threadIdx.x;
   if (e < D * D) {
-    const double diag = (e / D) == (e % D) ? static_cast<double>(lambda0) : 0.0;
+    const double init = Minit != nullptr ? static_cast<double>(Minit[s * D * D + e])
+                        : (e / D) == (e % D) ? static_cast<double>(lambda0) : 0.0;
     float *base = M + s * P * D * D + e;
     double acc = 0.0;
     for (int64_t p = 0; p < P; ++p) {
       const float g = (p + 1 < P) ? base[p * D * D] : 0.f;
-      base[p * D * D] = static_cast<float>(acc + diag);
+      base[p * D * D] = static_cast<float>(acc + init);
       acc += g;
     }
   }
   if (blockIdx.y == 0 && threadIdx.x < D) {
+    const double init = n0 != nullptr ? static_cast<double>(n0[s * D + threadIdx.x]) : 0.0;
     float *base = nk + s * P * D + threadIdx.x;
     double acc = 0.0;
     for (int64_t p = 0; p < P; ++p) {
       const float g = (p + 1 < P) ? base[p * D] : 0.f;
-      base[p * D] = static_cast<float>(acc);
+      base[p * D] = static_cast<float>(acc + init);
       acc += g;
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// k_sym_copy: dst_s = (A_s + A_s^T) / 2 for every stream s (src [streams][D][D], dst matrices
+// dst_stride floats apart): a carried A_0, symmetrised, where the path starts from it.
+// ------------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+k_sym_copy(const float *__restrict__ src, float *__restrict__ dst, int64_t dst_stride) {
+  const int64_t s = blockIdx.x;
+  const int e = blockIdx.y * 256 + threadIdx.x;
+  if (e < D * D) {
+    const int i = e / D, j = e % D;
+    const float *a = src + s * D * D;
+    dst[s * dst_stride + e] = 0.5f * (a[i * D + j] + a[j * D + i]);
   }
 }
 
@@ -481,8 +502,8 @@ template <int D, typename TIn>
 __global__ void __launch_bounds__(AsideCfg<D>::NT)
 k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ u,
         const float *__restrict__ A0, const float *__restrict__ nk0, float *__restrict__ alpha,
-        float *__restrict__ rkden, float *__restrict__ A_final, int64_t S, int64_t T,
-        int64_t L, int64_t P, float eps) {
+        float *__restrict__ rkden, float *__restrict__ A_final, float *__restrict__ n_final,
+        int64_t S, int64_t T, int64_t L, int64_t P, float eps) {
   using C = AsideCfg<D>;
   using IO = io<TIn>;
   using vec_t = typename IO::vec_t;
@@ -695,6 +716,13 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
       for (int m = 0; m < C::CW / 4; ++m)
         *reinterpret_cast<float4 *>(&dst[row * D + c0 + 4 * m]) =
             make_float4(Mr[r][4 * m], Mr[r][4 * m + 1], Mr[r][4 * m + 2], Mr[r][4 * m + 3]);
+    }
+  }
+  if (n_final != nullptr && p == P - 1) {
+#pragma unroll
+    for (int f = 0; f < C::NF; ++f) {
+      const int feat = lu + f * C::LA;
+      if (feat < D) n_final[s * D + feat] = nrun[f];
     }
   }
 }
@@ -1023,7 +1051,8 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
 // ------------------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(D / 16 * kWave)
-k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P) {
+k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P,
+          const float *__restrict__ S0) {
   constexpr int NFT = D / 16;
   __shared__ __attribute__((aligned(16))) float Xs[2][D / 4][16][4];  // S^T[f'][row], f' % 4 minor
   const int64_t s = blockIdx.x;
@@ -1031,9 +1060,11 @@ k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P) {
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = 16 * rt + li, col = 16 * w + 4 * gq;
-  // S_0 = 0
-  *reinterpret_cast<float4 *>(&s0[(s * P) * D * D + row * D + col]) = make_float4(0.f, 0.f, 0.f, 0.f);
-  *reinterpret_cast<float4 *>(&Xs[0][4 * w + gq][li][0]) = make_float4(0.f, 0.f, 0.f, 0.f);
+  // S at the first segment start: 0, or a carried S_0
+  const float4 st0 = S0 != nullptr ? *reinterpret_cast<const float4 *>(&S0[s * D * D + row * D + col])
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  *reinterpret_cast<float4 *>(&s0[(s * P) * D * D + row * D + col]) = st0;
+  *reinterpret_cast<float4 *>(&Xs[0][4 * w + gq][li][0]) = st0;
   // a[kt][e] = Pi[16 kt + 4 gq + e][16 w + li];  b = B[row][col .. col + 3]
   float a[NFT][4];
   float4 b;
@@ -1081,7 +1112,7 @@ k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P) {
 template <int D, int CH, typename TIn>
 static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const void *q,
                                  const void *k, const void *v, const void *u, void *out,
-                                 float *S_final, float *A_final, char *ws, hipStream_t st) {
+                                 const StateIO &sio, char *ws, hipStream_t st) {
   const TIn *qq = static_cast<const TIn *>(q);
   const TIn *kk = static_cast<const TIn *>(k);
   const TIn *vv = static_cast<const TIn *>(v);
@@ -1093,25 +1124,37 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
   float *rdw = reinterpret_cast<float *>(ws + pl.off_rkden);
   float *pbw = reinterpret_cast<float *>(ws + pl.off_pib);
   float *s0w = reinterpret_cast<float *>(ws + pl.off_s0);
+  float *miw = reinterpret_cast<float *>(ws + pl.off_minv);
+  float *S_final = sio.S_final, *A_final = sio.A_final, *n_final = sio.n_final;
   const unsigned S = static_cast<unsigned>(pl.S), P = static_cast<unsigned>(pl.P);
+  const dim3 gmat(S, (D * D + 255) / 256);
 
   if (P > 1) {
     VLA_LAUNCH("k_gram", (k_gram<D, TIn>), dim3(S, P - 1), dim3(256), 0, st, uu, kk, Mw, nkw,
                        pl.T, pl.L, pl.P);
   }
-  VLA_LAUNCH("k_prefix", (k_prefix<D>), dim3(S, (D * D + 255) / 256), dim3(256), 0, st, Mw, nkw,
-                     pl.P, pr.lambda0);
+  if (sio.A0 != nullptr) {  // M_0 = A_0^{-1} for the segment prefix
+    VLA_LAUNCH("k_sym_copy", (k_sym_copy<D>), gmat, dim3(256), 0, st, sio.A0, miw,
+               static_cast<int64_t>(D) * D);
+    VLA_LAUNCH("k_inv", (k_inv<D>), dim3(S, 1), dim3(256), 0, st, miw, int64_t(1));
+  }
+  VLA_LAUNCH("k_prefix", (k_prefix<D>), gmat, dim3(256), 0, st, Mw, nkw, pl.P, pr.lambda0,
+             sio.A0 != nullptr ? static_cast<const float *>(miw) : nullptr, sio.n0);
   VLA_LAUNCH("k_inv", (k_inv<D>), dim3(S, P), dim3(256), 0, st, Mw, pl.P);
+  if (sio.A0 != nullptr) {  // the first segment starts from A_0 itself
+    VLA_LAUNCH("k_sym_copy", (k_sym_copy<D>), gmat, dim3(256), 0, st, sio.A0, Mw,
+               static_cast<int64_t>(pl.P) * D * D);
+  }
   if constexpr (sizeof(TIn) == 2) {
     // bf16 inputs: chunked A side on the bf16 matrix cores.
     VLA_LAUNCH("k_aside_wy", (k_aside_wy<D>), dim3(S, P), dim3(AwyCfg<D>::NT), 0, st, qq, kk,
-               uu, Mw, nkw, alw, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
+               uu, Mw, nkw, alw, rdw, A_final, n_final, pl.T, pl.L, pl.P, pr.eps);
   } else {
     using AC = AsideCfg<D>;
     const int64_t units = pl.S * pl.P;
     const unsigned blocks = static_cast<unsigned>((units + AC::UPB - 1) / AC::UPB);
     VLA_LAUNCH("k_aside", (k_aside<D, TIn>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
-               nkw, alw, rdw, A_final, pl.S, pl.T, pl.L, pl.P, pr.eps);
+               nkw, alw, rdw, A_final, n_final, pl.S, pl.T, pl.L, pl.P, pr.eps);
   }
   if constexpr (sizeof(TIn) == 2) {
     // bf16 inputs: S side on the bf16 matrix cores.
@@ -1120,7 +1163,8 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                  dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
                  S_final, pl.T, pl.L, pl.P);
     }
-    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
+    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
+               s0w, pl.P, sio.S0);
     VLA_LAUNCH("k_swy_final", (k_swyb<D, CH, true>), dim3(S, P), dim3(SwbCfg<D, CH, true>::NT), 0,
                st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
   } else {
@@ -1129,7 +1173,8 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                  dim3(SwyCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
                  S_final, pl.T, pl.L, pl.P);
     }
-    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw, s0w, pl.P);
+    VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
+               s0w, pl.P, sio.S0);
     VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P),
                dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final,
                pl.T, pl.L, pl.P);
@@ -1140,10 +1185,9 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
 template <typename TIn>
 static hipError_t launch_chunk_dt(const Problem &pr, const ChunkPlan &pl, const void *q,
                                   const void *k, const void *v, const void *u, void *out,
-                                  float *S_final, float *A_final, char *ws, hipStream_t st) {
+                                  const StateIO &sio, char *ws, hipStream_t st) {
 #define VLA_CASE(DD, CC)                                                                      \
-  if (pr.d == DD && pl.C == CC)                                                              \
-    return launch_chunk_t<DD, CC, TIn>(pr, pl, q, k, v, u, out, S_final, A_final, ws, st);
+  if (pr.d == DD && pl.C == CC) return launch_chunk_t<DD, CC, TIn>(pr, pl, q, k, v, u, out, sio, ws, st);
   VLA_CASE(32, 16) VLA_CASE(32, 32) VLA_CASE(32, 64)
   VLA_CASE(64, 16) VLA_CASE(64, 32) VLA_CASE(64, 64)
   VLA_CASE(96, 16) VLA_CASE(96, 32) VLA_CASE(96, 64)
@@ -1153,14 +1197,13 @@ static hipError_t launch_chunk_dt(const Problem &pr, const ChunkPlan &pl, const 
 }
 
 hipError_t launch_chunk(const Problem &p, int chunk, const void *q, const void *k,
-                        const void *v, const void *u, void *out, float *S_final,
-                        float *A_final, void *ws, hipStream_t stream) {
+                        const void *v, const void *u, void *out, const StateIO &st, void *ws,
+                        hipStream_t stream) {
   if (!chunk_supported(p, chunk)) return hipErrorInvalidValue;
   const ChunkPlan pl = make_plan(p, chunk);
   char *w = static_cast<char *>(ws);
-  if (p.dtype == Dtype::F32)
-    return launch_chunk_dt<float>(p, pl, q, k, v, u, out, S_final, A_final, w, stream);
-  return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, out, S_final, A_final, w, stream);
+  if (p.dtype == Dtype::F32) return launch_chunk_dt<float>(p, pl, q, k, v, u, out, st, w, stream);
+  return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, out, st, w, stream);
 }
 
 }  // namespace vla

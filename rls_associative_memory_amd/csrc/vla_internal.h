@@ -18,18 +18,25 @@ struct Problem {
   float eps;
 };
 
+// Carried state of every stream, fp32 device tensors: the state the recurrence starts from
+// (S0 [streams][d][d], A0 [streams][d][d] symmetric, n0 [streams][d]; NULL = the fixed
+// start S = 0, A = I / lambda0, n = 0) and the state it ends in (NULL = not wanted).
+struct StateIO {
+  const float *S0 = nullptr, *A0 = nullptr, *n0 = nullptr;
+  float *S_final = nullptr, *A_final = nullptr, *n_final = nullptr;
+};
+
 // Sequential path: one workgroup per stream.  Returns hipSuccess or the launch error.
 hipError_t launch_seq(const Problem &p, const void *q, const void *k, const void *v,
-                      const void *u, void *out, float *S_final, float *A_final,
-                      hipStream_t stream);
+                      const void *u, void *out, const StateIO &st, hipStream_t stream);
 
 // Chunked path (time-segment parallel).  `ws` must hold chunk_workspace_bytes(p, C).
 size_t chunk_workspace_bytes(const Problem &p, int chunk);
 bool chunk_supported(const Problem &p, int chunk);
 int chunk_default(const Problem &p);
 hipError_t launch_chunk(const Problem &p, int chunk, const void *q, const void *k,
-                        const void *v, const void *u, void *out, float *S_final,
-                        float *A_final, void *ws, hipStream_t stream);
+                        const void *v, const void *u, void *out, const StateIO &st, void *ws,
+                        hipStream_t stream);
 
 // Event-pair timing of one kernel launch when vla_profile_enable(1) is in effect.
 class ProfScope {

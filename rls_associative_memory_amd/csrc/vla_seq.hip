@@ -47,7 +47,9 @@ template <int D, typename TIn>
 __global__ void __launch_bounds__(SeqCfg<D>::NT)
 vla_seq_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
                const TIn *__restrict__ u, TIn *__restrict__ out, float *__restrict__ S_final,
-               float *__restrict__ A_final, int64_t T, float lambda0, float eps) {
+               float *__restrict__ A_final, const float *__restrict__ S0,
+               const float *__restrict__ A0, const float *__restrict__ n0,
+               float *__restrict__ n_final, int64_t T, float lambda0, float eps) {
   using C = SeqCfg<D>;
   using IO = io<TIn>;
   constexpr int VW = IO::kVec;
@@ -81,16 +83,30 @@ vla_seq_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *
   const TIn *us = u + base;
   TIn *os = out + base;
 
-  // Matrix state: A on the A side, S on the S side, same registers.
+  // Matrix state: A on the A side, S on the S side, same registers.  A carried A0 is
+  // symmetrised as it is read ((A0 + A0^T) / 2), which keeps A exactly symmetric.
   float M[C::RPL][C::CW];
   const float inv_l0 = 1.0f / lambda0;
+  const float *m0 = is_a ? A0 : S0;
+  if (m0 != nullptr) {
+    m0 += sid * D * D;
 #pragma unroll
-  for (int j = 0; j < C::RPL; ++j) {
-    const int r = g + j * C::HALF;
+    for (int j = 0; j < C::RPL; ++j) {
+      const int r = g + j * C::HALF;
 #pragma unroll
-    for (int c = 0; c < C::CW; ++c) M[j][c] = (is_a && r == c0 + c) ? inv_l0 : 0.0f;
+      for (int c = 0; c < C::CW; ++c)
+        M[j][c] = is_a ? 0.5f * (m0[r * D + c0 + c] + m0[(c0 + c) * D + r]) : m0[r * D + c0 + c];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < C::RPL; ++j) {
+      const int r = g + j * C::HALF;
+#pragma unroll
+      for (int c = 0; c < C::CW; ++c) M[j][c] = (is_a && r == c0 + c) ? inv_l0 : 0.0f;
+    }
   }
-  float n_run = 0.0f;  // normaliser component tid (tid < D)
+  // normaliser component tid (tid < D)
+  float n_run = (n0 != nullptr && tid < D) ? n0[sid * D + tid] : 0.0f;
 
   typename IO::vec_t pf[4][PF];
   auto prefetch = [&](int64_t t0) {
@@ -346,6 +362,7 @@ vla_seq_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *
   }
 
   // Final state.
+  if (n_final != nullptr && tid < D) n_final[sid * D + tid] = n_run;
   float *dst = is_a ? A_final : S_final;
   if (dst != nullptr) {
     dst += sid * D * D;
@@ -362,36 +379,32 @@ vla_seq_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *
 
 template <int D, typename TIn>
 static hipError_t launch_seq_t(const Problem &p, const void *q, const void *k, const void *v,
-                               const void *u, void *out, float *S_final, float *A_final,
-                               hipStream_t stream) {
+                               const void *u, void *out, const StateIO &st, hipStream_t stream) {
   using C = SeqCfg<D>;
   VLA_LAUNCH("vla_seq_kernel", (vla_seq_kernel<D, TIn>), dim3(static_cast<unsigned>(p.streams)),
                      dim3(C::NT), 0, stream, static_cast<const TIn *>(q),
                      static_cast<const TIn *>(k), static_cast<const TIn *>(v),
-                     static_cast<const TIn *>(u), static_cast<TIn *>(out), S_final, A_final,
-                     p.T, p.lambda0, p.eps);
+                     static_cast<const TIn *>(u), static_cast<TIn *>(out), st.S_final, st.A_final,
+                     st.S0, st.A0, st.n0, st.n_final, p.T, p.lambda0, p.eps);
   return hipGetLastError();
 }
 
 template <typename TIn>
 static hipError_t launch_seq_dt(const Problem &p, const void *q, const void *k, const void *v,
-                                const void *u, void *out, float *S_final, float *A_final,
-                                hipStream_t stream) {
+                                const void *u, void *out, const StateIO &st, hipStream_t stream) {
   switch (p.d) {
-    case 32: return launch_seq_t<32, TIn>(p, q, k, v, u, out, S_final, A_final, stream);
-    case 64: return launch_seq_t<64, TIn>(p, q, k, v, u, out, S_final, A_final, stream);
-    case 96: return launch_seq_t<96, TIn>(p, q, k, v, u, out, S_final, A_final, stream);
-    case 128: return launch_seq_t<128, TIn>(p, q, k, v, u, out, S_final, A_final, stream);
+    case 32: return launch_seq_t<32, TIn>(p, q, k, v, u, out, st, stream);
+    case 64: return launch_seq_t<64, TIn>(p, q, k, v, u, out, st, stream);
+    case 96: return launch_seq_t<96, TIn>(p, q, k, v, u, out, st, stream);
+    case 128: return launch_seq_t<128, TIn>(p, q, k, v, u, out, st, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_seq(const Problem &p, const void *q, const void *k, const void *v,
-                      const void *u, void *out, float *S_final, float *A_final,
-                      hipStream_t stream) {
-  if (p.dtype == Dtype::F32)
-    return launch_seq_dt<float>(p, q, k, v, u, out, S_final, A_final, stream);
-  return launch_seq_dt<bf16_t>(p, q, k, v, u, out, S_final, A_final, stream);
+                      const void *u, void *out, const StateIO &st, hipStream_t stream) {
+  if (p.dtype == Dtype::F32) return launch_seq_dt<float>(p, q, k, v, u, out, st, stream);
+  return launch_seq_dt<bf16_t>(p, q, k, v, u, out, st, stream);
 }
 
 }  // namespace vla

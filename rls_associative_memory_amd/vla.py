@@ -15,7 +15,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["forward", "workspace_size", "resolve_path", "library_path", "load_library",
+__all__ = ["forward", "forward_state", "workspace_size", "resolve_path", "library_path", "load_library",
            "profile_enable", "profile_reset", "profile_read",
            "VlaError", "exported_symbols", "STATUS", "PATHS", "DTYPES", "VlaDesc"]
 
@@ -73,6 +73,9 @@ def load_library():
         lib.vla_forward.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                     ctypes.POINTER(VlaDesc), vp]
         lib.vla_forward.restype = ctypes.c_int
+        lib.vla_forward_state.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
+                                          ctypes.POINTER(VlaDesc), vp]
+        lib.vla_forward_state.restype = ctypes.c_int
         lib.vla_workspace_size.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.vla_workspace_size.restype = ctypes.c_int
         lib.vla_resolve_path.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_int32)]
@@ -190,6 +193,52 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
     if S_final is not None or A_final is not None:
         return out, S_final, A_final
     return out
+
+
+def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
+                  lambda0: float = 1.0, S0: Optional[torch.Tensor] = None,
+                  A0: Optional[torch.Tensor] = None, n0: Optional[torch.Tensor] = None,
+                  eps: float = 1e-6, path: str = "auto", chunk: int = 0,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None):
+    """VLA forward continuing from a carried state (vla_forward_state in vla.h).
+
+    S0 and A0 are fp32 [.., d, d] and n0 fp32 [.., d] device tensors, or None for the fixed
+    start (S = 0, A = I / lambda0, n = 0); lambda0 is only used when A0 is None.  Returns
+    (out, S_T, A_T, n_T), which a next call takes as its (S0, A0, n0).
+    """
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, u must share shape, dtype and device")
+    desc = make_desc(tuple(q.shape), q.dtype, eps=eps, path=path, chunk=chunk, workspace=workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q in shape and dtype and be contiguous")
+    d = q.shape[-1]
+    mat_shape = tuple(q.shape[:-2]) + (d, d)
+    vec_shape = tuple(q.shape[:-2]) + (d,)
+    for name, t, shp in (("S0", S0, mat_shape), ("A0", A0, mat_shape), ("n0", n0, vec_shape)):
+        if t is not None and (tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous()
+                              or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous fp32 {shp} tensor on q's device")
+    S_T = torch.empty(mat_shape, dtype=torch.float32, device=q.device)
+    A_T = torch.empty(mat_shape, dtype=torch.float32, device=q.device)
+    n_T = torch.empty(vec_shape, dtype=torch.float32, device=q.device)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = lib.vla_forward_state(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), u.data_ptr(), float(lambda0),
+            ptr(S0), ptr(A0), ptr(n0), out.data_ptr(), S_T.data_ptr(), A_T.data_ptr(),
+            n_T.data_ptr(), ctypes.byref(desc), s.cuda_stream)
+    _check(status, "vla_forward_state")
+    return out, S_T, A_T, n_T
 
 
 def profile_enable(on: bool = True) -> None:

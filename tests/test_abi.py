@@ -85,6 +85,28 @@ def test_forward_argument_errors_before_any_device_work(lib):
                            ctypes.byref(ok), None) == 2
 
 
+def test_forward_state_argument_errors_before_any_device_work(lib):
+    ok = desc()
+    fake = 4096  # never dereferenced
+    call = lambda lam, S0=None, A0=None, n0=None, nf=None, q=fake: lib.vla_forward_state(
+        q, fake, fake, fake, lam, S0, A0, n0, fake, None, None, nf, ctypes.byref(ok), None)
+    assert call(1.0, q=None) == 1                       # NULL input
+    for lam in (0.0, float("nan")):
+        assert call(lam) == 1                           # lambda0 checked when A0 is NULL
+    for kw in ({"S0": fake + 4}, {"A0": fake + 8}, {"n0": fake + 2}, {"nf": fake + 12}):
+        assert call(1.0, **kw) == 2                     # misaligned state pointers
+
+
+def test_forward_state_binding_checks_state_tensors():
+    x = torch.zeros(1, 1, 4, 32)
+    with pytest.raises(ValueError):
+        vla.forward_state(x, x, x, x, 1.0)
+    if torch.cuda.is_available():  # shapes are checked before the library is called
+        y = x.cuda()
+        with pytest.raises(ValueError):
+            vla.forward_state(y, y, y, y, 1.0, n0=torch.zeros(1, 1, 31, device="cuda"))
+
+
 def test_sequential_path_needs_no_workspace(lib):
     n = ctypes.c_size_t(99)
     assert lib.vla_workspace_size(ctypes.byref(desc(path=1)), ctypes.byref(n)) == 0

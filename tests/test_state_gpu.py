@@ -1,0 +1,137 @@
+"""Carried state (vla_forward_state): parity against the fp64 oracle continuing a stream,
+and continuation identities on the device (GPU only).
+
+A stream is run by the oracle over a prefix of tokens; the state it ends in (S, A, n,
+rounded to fp32) is handed to the library, which continues over the next tokens.  The
+oracle continues from the same fp32 values.  Bars as for vla_forward: relative L2 < 1e-4
+(fp32 inputs), < 1e-2 (bf16 inputs) per tensor, here also for n_T.  On the device,
+splitting a sequence into two calls (or into T = 1 decode steps) must give the single
+call's result to the same bars.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from rls_associative_memory_amd import vla
+from rls_associative_memory_amd.inputs import get_workload, make_inputs, torch_dtype
+
+from .parity import TOL, rel_l2
+from oracle import vla_forward as oracle_forward
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _dev(x, w, shape):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).view(shape).to(
+        torch_dtype(w)).cuda()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _case(d, dt, T0, T1, H=3):
+    """Inputs rounded as the library sees them, the oracle state after T0 tokens (in fp32)
+    and the oracle's continuation over the next T1 tokens from that state."""
+    w = get_workload("tiny_t256_d32").resized(name=f"state_d{d}_{dt}", B=1, H=H, T=T0 + T1, d=d,
+                                              dtype=dt, lambda0=0.8)
+    q, k, v, u = make_inputs(w)
+    if dt == "bf16":  # the oracle sees the bf16-rounded values
+        q, k, v, u = (torch.from_numpy(x).to(torch.bfloat16).float().numpy() for x in (q, k, v, u))
+    pre = oracle_forward(q[:, :T0], k[:, :T0], v[:, :T0], u[:, :T0], w.lambda0, eps=w.eps,
+                         return_n=True)
+    state = tuple(x.astype(np.float32) for x in pre[1:])  # S, A, n
+    ref = oracle_forward(q[:, T0:], k[:, T0:], v[:, T0:], u[:, T0:], w.lambda0, eps=w.eps,
+                         state=state, return_n=True)
+    return w, (q, k, v, u), state, ref
+
+
+def _compare(label, tol, got, ref):
+    names = ("out", "S", "A", "n")
+    worst = {n: rel_l2(g, r) for n, g, r in zip(names, got, ref)}
+    _say(f"[parity] {label}: " + " ".join(f"{n}={e:.3e}" for n, e in worst.items()) + f" (tol {tol:g})")
+    for n, e in worst.items():
+        assert e < tol, f"{label}: {n} rel L2 {e:.3e} >= {tol:g}"
+
+
+STATE_CASES = [(d, dt, path) for d in (32, 64, 96, 128) for dt in ("f32", "bf16")
+               for path in ("seq", "chunk")]
+
+
+@pytest.mark.parametrize("d,dt,path", STATE_CASES)
+def test_state_continuation_matches_oracle(d, dt, path):
+    T0, T1 = 150, 1100 if path == "chunk" else 300
+    _say(f"[case] carried state d={d} {dt} path={path} T0={T0} T1={T1}")
+    w, (q, k, v, u), (S0, A0, n0), ref = _case(d, dt, T0, T1)
+    H = w.H
+    shp = (1, H, T1, d)
+    dq, dk, dv, du = (_dev(x[:, T0:], w, shp) for x in (q, k, v, u))
+    S0d = torch.from_numpy(S0).view(1, H, d, d).cuda()
+    A0d = torch.from_numpy(A0).view(1, H, d, d).cuda()
+    n0d = torch.from_numpy(n0).view(1, H, d).cuda()
+    chunk = 32 if d > 96 else 64
+    out, S, A, n = vla.forward_state(dq, dk, dv, du, 0.0, S0=S0d, A0=A0d, n0=n0d, eps=w.eps,
+                                     path=path, chunk=chunk if path == "chunk" else 0)
+    torch.cuda.synchronize()
+    got = (_np(out).reshape(H, T1, d), _np(S).reshape(H, d, d), _np(A).reshape(H, d, d),
+           _np(n).reshape(H, d))
+    _compare(f"state d={d} {dt} {path}", TOL[dt], got, ref)
+
+
+@pytest.mark.parametrize("path", ["seq", "chunk"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_two_calls_equal_one_call(path, dt):
+    d, T = 64, 1400
+    split = 611
+    w = get_workload("tiny_t256_d32").resized(name="split", B=1, H=2, T=T, d=d, dtype=dt,
+                                              lambda0=0.6)
+    _say(f"[case] two calls vs one: {dt} path={path} T={T} split={split}")
+    q, k, v, u = make_inputs(w)
+    full = [_dev(x, w, (1, 2, T, d)) for x in (q, k, v, u)]
+    o1, S1, A1, n1 = vla.forward_state(*full, w.lambda0, eps=w.eps, path=path)
+    a = [x[:, :, :split].contiguous() for x in full]
+    b = [x[:, :, split:].contiguous() for x in full]
+    oa, Sa, Aa, na = vla.forward_state(*a, w.lambda0, eps=w.eps, path=path)
+    ob, Sb, Ab, nb = vla.forward_state(*b, w.lambda0, S0=Sa, A0=Aa, n0=na, eps=w.eps, path=path)
+    torch.cuda.synchronize()
+    got = (_np(torch.cat([oa, ob], dim=2)), _np(Sb), _np(Ab), _np(nb))
+    ref = (_np(o1), _np(S1), _np(A1), _np(n1))
+    _compare(f"two calls {dt} {path}", TOL[dt], got, ref)
+
+
+def test_decode_steps_equal_one_call():
+    d, T = 96, 24
+    w = get_workload("tiny_t256_d32").resized(name="decode", B=1, H=4, T=T, d=d, dtype="bf16",
+                                              lambda0=0.5)
+    _say(f"[case] {T} decode steps (T = 1 calls) vs one call, d={d}")
+    q, k, v, u = make_inputs(w)
+    full = [_dev(x, w, (1, 4, T, d)) for x in (q, k, v, u)]
+    o1, S1, A1, n1 = vla.forward_state(*full, w.lambda0, eps=w.eps, path="seq")
+    S = A = n = None
+    outs = []
+    for t in range(T):
+        step = [x[:, :, t:t + 1].contiguous() for x in full]
+        o, S, A, n = vla.forward_state(*step, w.lambda0, S0=S, A0=A, n0=n, eps=w.eps, path="seq")
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = (_np(torch.cat(outs, dim=2)), _np(S), _np(A), _np(n))
+    ref = (_np(o1), _np(S1), _np(A1), _np(n1))
+    _compare("decode steps", TOL["bf16"], got, ref)
+
+
+def test_default_state_equals_vla_forward():
+    w = get_workload("tiny_t256_d32").resized(name="defaults", B=1, H=2, T=700, d=96, dtype="bf16")
+    q, k, v, u = make_inputs(w)
+    dev = [_dev(x, w, (1, 2, w.T, w.d)) for x in (q, k, v, u)]
+    for path in ("seq", "chunk"):
+        o1, S1, A1 = vla.forward(*dev, w.lambda0, eps=w.eps, path=path, return_state=True)
+        o2, S2, A2, _ = vla.forward_state(*dev, w.lambda0, eps=w.eps, path=path)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(A1, A2), path
