@@ -16,6 +16,11 @@ printed on stdout is a single JSON object:
                outputs also give a causal parity check of the GPU run's first tokens
 
 Workloads are seeded synthetic inputs (rls_associative_memory_amd.inputs).
+
+``--mode decode`` measures the streaming use instead: every stream of the workload advances
+one token per call (T = 1, state carried from call to call through vla_forward_state), and
+the line reports token*heads per second of such calls with the HBM rate of the state they
+read and write (S and A in, S and A out, per stream per call).
 """
 
 from __future__ import annotations
@@ -105,6 +110,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per stream in the oracle sample (0 disables the CPU leg)")
     ap.add_argument("--cpu-cores", type=int, default=16)
+    ap.add_argument("--mode", default="forward", choices=["forward", "decode"],
+                    help="forward: whole sequences (default); decode: T = 1 calls, state carried")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -173,6 +180,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     w = get_workload(args.workload)
+    if args.mode == "decode":
+        return decode_bench(args, w)
     chunk = w.chunk if args.chunk < 0 else args.chunk
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -285,6 +294,84 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def decode_bench(args, w):
+    """T = 1 calls over every stream of the workload, state carried (ping-pong buffers)."""
+    import torch
+    from rls_associative_memory_amd import vla
+    from rls_associative_memory_amd.inputs import upload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nsteps = args.warmup + args.steps
+    tok = upload_inputs(w.resized(name=w.name + "_decode", T=nsteps), dev)  # [B, H, steps, d]
+    steps_in = [[x[:, :, t:t + 1].contiguous() for x in tok] for t in range(nsteps)]
+    mat = (w.B, w.H, w.d, w.d)
+    st = [(torch.zeros(mat, dtype=torch.float32, device=dev),
+           torch.empty(mat, dtype=torch.float32, device=dev),
+           torch.zeros((w.B, w.H, w.d), dtype=torch.float32, device=dev)) for _ in range(2)]
+    eye = torch.eye(w.d, dtype=torch.float32, device=dev) / w.lambda0
+    st[0][1].copy_(eye.expand(mat))
+    out = torch.empty_like(steps_in[0][0])
+
+    def step(t):
+        S0, A0, n0 = st[t & 1]
+        S1, A1, n1 = st[(t & 1) ^ 1]
+        vla.forward_state(*steps_in[t], w.lambda0, S0=S0, A0=A0, n0=n0, eps=w.eps, path="seq",
+                          out=out, S_final=S1, A_final=A1, n_final=n1)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    vla.profile_reset()
+    vla.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for t in range(args.warmup, nsteps):
+        step(t)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    vla.profile_enable(False)
+    kernels = vla.profile_read()
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ms = max(wall * 1e3 / args.steps, ev_ms)
+    streams = w.B * w.H
+    k_total, k_n = kernels.get("vla_seq_kernel", (0.0, 1))
+    kernel_ms = k_total / max(k_n, 1)
+    # per stream and call: S, A read and written (fp32 d x d each), n read and written,
+    # q, k, v, u read and o written in the input dtype
+    state_bytes = streams * (4 * w.d * w.d * 4 + 2 * w.d * 4 + 5 * w.d * w.elem_bytes)
+    gbs = state_bytes / (kernel_ms * 1e-3) / 1e9 if kernel_ms > 0 else 0.0
+    print(f"[bench] decode: {args.steps} calls of T = 1 over {streams} streams: {ms * 1e3:.1f} us/call "
+          f"(events {ev_ms * 1e3:.1f} us, kernel {kernel_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
+    line = {
+        "metric": "VLA decode (T = 1 calls, state carried) tokens·heads/sec at 1 MI355X",
+        "value": streams / (ms * 1e-3),
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name + "_decode", "B": w.B, "H": w.H, "T": 1, "d": w.d,
+                   "input_dtype": w.dtype, "state_dtype": "f32", "lambda0": w.lambda0,
+                   "path": "seq"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "vla_seq_kernel", "kernel_ms": round(kernel_ms, 5)},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

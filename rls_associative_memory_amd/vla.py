@@ -200,12 +200,15 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
                   A0: Optional[torch.Tensor] = None, n0: Optional[torch.Tensor] = None,
                   eps: float = 1e-6, path: str = "auto", chunk: int = 0,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  stream: Optional[torch.cuda.Stream] = None):
+                  stream: Optional[torch.cuda.Stream] = None,
+                  S_final: Optional[torch.Tensor] = None, A_final: Optional[torch.Tensor] = None,
+                  n_final: Optional[torch.Tensor] = None):
     """VLA forward continuing from a carried state (vla_forward_state in vla.h).
 
     S0 and A0 are fp32 [.., d, d] and n0 fp32 [.., d] device tensors, or None for the fixed
     start (S = 0, A = I / lambda0, n = 0); lambda0 is only used when A0 is None.  Returns
-    (out, S_T, A_T, n_T), which a next call takes as its (S0, A0, n0).
+    (out, S_T, A_T, n_T), which a next call takes as its (S0, A0, n0); S_final, A_final and
+    n_final optionally give the buffers to write them to (they must not be S0, A0, n0).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
@@ -227,9 +230,15 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
         if t is not None and (tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous()
                               or t.device != q.device):
             raise ValueError(f"{name} must be a contiguous fp32 {shp} tensor on q's device")
-    S_T = torch.empty(mat_shape, dtype=torch.float32, device=q.device)
-    A_T = torch.empty(mat_shape, dtype=torch.float32, device=q.device)
-    n_T = torch.empty(vec_shape, dtype=torch.float32, device=q.device)
+    def _final(t, shp, name):
+        if t is None:
+            return torch.empty(shp, dtype=torch.float32, device=q.device)
+        if tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 {shp} tensor")
+        return t
+    S_T = _final(S_final, mat_shape, "S_final")
+    A_T = _final(A_final, mat_shape, "A_final")
+    n_T = _final(n_final, vec_shape, "n_final")
     ptr = lambda t: t.data_ptr() if t is not None else None
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
