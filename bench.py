@@ -112,6 +112,8 @@ def parse():
     ap.add_argument("--cpu-cores", type=int, default=16)
     ap.add_argument("--mode", default="forward", choices=["forward", "decode"],
                     help="forward: whole sequences (default); decode: T = 1 calls, state carried")
+    ap.add_argument("--decode-path", default="decode", choices=["decode", "seq"],
+                    help="path of the T = 1 calls in --mode decode")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -320,7 +322,7 @@ def decode_bench(args, w):
     def step(t):
         S0, A0, n0 = st[t & 1]
         S1, A1, n1 = st[(t & 1) ^ 1]
-        vla.forward_state(*steps_in[t], w.lambda0, S0=S0, A0=A0, n0=n0, eps=w.eps, path="seq",
+        vla.forward_state(*steps_in[t], w.lambda0, S0=S0, A0=A0, n0=n0, eps=w.eps, path=args.decode_path,
                           out=out, S_final=S1, A_final=A1, n_final=n1)
 
     for t in range(args.warmup):
@@ -344,7 +346,8 @@ def decode_bench(args, w):
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms = max(wall * 1e3 / args.steps, ev_ms)
     streams = w.B * w.H
-    k_total, k_n = kernels.get("vla_seq_kernel", (0.0, 1))
+    kname = "vla_decode_kernel" if args.decode_path == "decode" else "vla_seq_kernel"
+    k_total, k_n = kernels.get(kname, (0.0, 1))
     kernel_ms = k_total / max(k_n, 1)
     # per stream and call: S, A read and written (fp32 d x d each), n read and written,
     # q, k, v, u read and o written in the input dtype
@@ -367,10 +370,10 @@ def decode_bench(args, w):
         "data": "synthetic",
         "config": {"workload": w.name + "_decode", "B": w.B, "H": w.H, "T": 1, "d": w.d,
                    "input_dtype": w.dtype, "state_dtype": "f32", "lambda0": w.lambda0,
-                   "path": "seq"},
+                   "path": args.decode_path},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "vla_seq_kernel", "kernel_ms": round(kernel_ms, 5)},
+                     "kernel": kname, "kernel_ms": round(kernel_ms, 5)},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

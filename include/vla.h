@@ -54,6 +54,8 @@ typedef enum {
   VLA_PATH_AUTO = 0,  /* library chooses from (B*H, T, d)                              */
   VLA_PATH_SEQ = 1,   /* one workgroup per stream, token by token, state on chip       */
   VLA_PATH_CHUNK = 2, /* chunked (Woodbury / WY) form; parallel over time segments     */
+  VLA_PATH_DECODE = 3 /* T = 1 only: one token per stream, a stream's rows spread over
+                         d / 16 workgroups (chosen by AUTO whenever T = 1)              */
 } vla_path_t;
 
 typedef struct {
@@ -108,6 +110,9 @@ vla_status_t vla_forward(const void *q, const void *k, const void *v, const void
  * lambda0     as in vla_forward; only read when A0 is NULL.
  * S_final, A_final   as in vla_forward.
  * n_final     device pointer to [B, H, d] fp32 receiving n_T, or NULL.
+ *             S_final, A_final and n_final must not overlap S0, A0 or n0 (no in-place
+ *             update: feed a decode loop from two sets of state buffers in turn); an
+ *             overlap returns VLA_ERROR_INVALID_VALUE.
  * The other arguments, ownership, workspace and error behaviour are those of vla_forward
  * (state pointers must be 16-byte aligned, else VLA_ERROR_NOT_SUPPORTED).  Splitting a
  * sequence into two calls, the second starting from the first's (S_final, A_final,

@@ -17,6 +17,12 @@ namespace {
 constexpr int32_t kVersion = 100;  // 0.1.0
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// Whether [a, a + na) and [b, b + nb) share a byte (false when either pointer is NULL).
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (a == nullptr || b == nullptr) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
 
 bool d_supported(int64_t d) { return d == 32 || d == 64 || d == 96 || d == 128; }
 
@@ -25,7 +31,7 @@ vla_status_t check_desc(const vla_desc_t *desc) {
   if (desc == nullptr) return VLA_ERROR_INVALID_VALUE;
   if (desc->B < 1 || desc->H < 1 || desc->T < 1 || desc->d < 1) return VLA_ERROR_INVALID_VALUE;
   if (desc->dtype != VLA_DTYPE_F32 && desc->dtype != VLA_DTYPE_BF16) return VLA_ERROR_INVALID_VALUE;
-  if (desc->path < VLA_PATH_AUTO || desc->path > VLA_PATH_CHUNK) return VLA_ERROR_INVALID_VALUE;
+  if (desc->path < VLA_PATH_AUTO || desc->path > VLA_PATH_DECODE) return VLA_ERROR_INVALID_VALUE;
   if (!(desc->eps >= 0.0f) || !std::isfinite(desc->eps)) return VLA_ERROR_INVALID_VALUE;
   if (desc->chunk < 0) return VLA_ERROR_INVALID_VALUE;
   // B*H*T*d must be addressable; B*H must fit a grid dimension.
@@ -54,6 +60,8 @@ vla::Problem make_problem(const vla_desc_t *desc, float lambda0) {
 vla_status_t resolve(const vla_desc_t *desc, const vla::Problem &p, int32_t *path, int *chunk) {
   int c = desc->chunk;
   int32_t want = desc->path;
+  if (want == VLA_PATH_DECODE && p.T != 1) return VLA_ERROR_NOT_SUPPORTED;
+  if (want == VLA_PATH_AUTO && p.T == 1) want = VLA_PATH_DECODE;
   if (want == VLA_PATH_AUTO) {
     // Enough streams to fill the machine one workgroup each, or sequences too short to
     // amortise the segment passes: run token by token.  Otherwise split time.
@@ -184,6 +192,15 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
       !aligned16(S_final) || !aligned16(A_final) || !aligned16(n_final) || !aligned16(S0) ||
       !aligned16(A0) || !aligned16(n0))
     return VLA_ERROR_NOT_SUPPORTED;
+  {  // no output state may overlap an input state: the kernels do not update in place
+    const size_t mat = static_cast<size_t>(desc->B * desc->H) * desc->d * desc->d * sizeof(float);
+    const size_t vec = static_cast<size_t>(desc->B * desc->H) * desc->d * sizeof(float);
+    const void *outs[3] = {S_final, A_final, n_final}, *ins[3] = {S0, A0, n0};
+    const size_t osz[3] = {mat, mat, vec}, isz[3] = {mat, mat, vec};
+    for (int a = 0; a < 3; ++a)
+      for (int b = 0; b < 3; ++b)
+        if (overlaps(outs[a], osz[a], ins[b], isz[b])) return VLA_ERROR_INVALID_VALUE;
+  }
   const vla::Problem p = make_problem(desc, A0 != nullptr ? 1.0f : lambda0);
   int32_t path = 0;
   int chunk = 0;
@@ -214,6 +231,8 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
   hipError_t err;
   if (path == VLA_PATH_SEQ)
     err = vla::launch_seq(p, q, k, v, u, out, sio, s);
+  else if (path == VLA_PATH_DECODE)
+    err = vla::launch_decode(p, q, k, v, u, out, sio, s);
   else
     err = vla::launch_chunk(p, chunk, q, k, v, u, out, sio, ws, s);
   return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;

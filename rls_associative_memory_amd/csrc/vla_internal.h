@@ -30,6 +30,10 @@ struct StateIO {
 hipError_t launch_seq(const Problem &p, const void *q, const void *k, const void *v,
                       const void *u, void *out, const StateIO &st, hipStream_t stream);
 
+// Decode path (T = 1): a stream's rows spread over d / 16 workgroups.
+hipError_t launch_decode(const Problem &p, const void *q, const void *k, const void *v,
+                         const void *u, void *out, const StateIO &st, hipStream_t stream);
+
 // Chunked path (time-segment parallel).  `ws` must hold chunk_workspace_bytes(p, C).
 size_t chunk_workspace_bytes(const Problem &p, int chunk);
 bool chunk_supported(const Problem &p, int chunk);

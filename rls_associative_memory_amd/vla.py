@@ -27,7 +27,7 @@ STATUS = {
     4: "VLA_ERROR_LAUNCH",
     5: "VLA_ERROR_NO_DEVICE",
 }
-PATHS = {"auto": 0, "seq": 1, "chunk": 2}
+PATHS = {"auto": 0, "seq": 1, "chunk": 2, "decode": 3}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -195,6 +195,14 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
     return out
 
 
+def _overlap(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """Whether two contiguous tensors share any byte of memory."""
+    if a.device != b.device:
+        return False
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    return a0 < b0 + b.numel() * b.element_size() and b0 < a0 + a.numel() * a.element_size()
+
+
 def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
                   lambda0: float = 1.0, S0: Optional[torch.Tensor] = None,
                   A0: Optional[torch.Tensor] = None, n0: Optional[torch.Tensor] = None,
@@ -239,6 +247,10 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
     S_T = _final(S_final, mat_shape, "S_final")
     A_T = _final(A_final, mat_shape, "A_final")
     n_T = _final(n_final, vec_shape, "n_final")
+    for a_name, a in (("S_final", S_T), ("A_final", A_T), ("n_final", n_T)):
+        for b_name, b in (("S0", S0), ("A0", A0), ("n0", n0)):
+            if b is not None and _overlap(a, b):
+                raise ValueError(f"{a_name} overlaps {b_name}: the state is not updated in place")
     ptr = lambda t: t.data_ptr() if t is not None else None
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):

@@ -107,6 +107,39 @@ def test_forward_state_binding_checks_state_tensors():
             vla.forward_state(y, y, y, y, 1.0, n0=torch.zeros(1, 1, 31, device="cuda"))
 
 
+def test_forward_state_rejects_in_place_state(lib):
+    """Output state overlapping input state is an argument error (checked on the host).
+
+    The pointers are fake: without the check the call would return VLA_ERROR_NO_DEVICE on a
+    machine without a GPU, and on one with a GPU it would launch, so it runs without one only.
+    """
+    if torch.cuda.is_available():
+        pytest.skip("fake device pointers are only passed where no GPU can be reached")
+    d = desc(B=1, H=2, T=8, d=32)
+    mat = 2 * 32 * 32 * 4
+    base = 1 << 20
+    fake = lambda off: ctypes.c_void_p(base + off)
+    args = [fake(0)] * 4
+    # A_final == A0
+    assert lib.vla_forward_state(*args, ctypes.c_float(1.0), fake(mat), fake(2 * mat), None,
+                                 fake(8 * mat), None, fake(2 * mat), None, ctypes.byref(d), None) == 1
+    # n_final inside S0
+    assert lib.vla_forward_state(*args, ctypes.c_float(1.0), fake(mat), None, None,
+                                 fake(8 * mat), None, None, fake(mat + 256), ctypes.byref(d), None) == 1
+
+
+def test_decode_path_resolution(lib):
+    p = ctypes.c_int32(-1)
+    assert lib.vla_resolve_path(ctypes.byref(desc(T=1)), ctypes.byref(p)) == 0
+    assert p.value == vla.PATHS["decode"]                 # AUTO picks decode for T = 1
+    assert lib.vla_resolve_path(ctypes.byref(desc(T=1, path=1)), ctypes.byref(p)) == 0
+    assert p.value == vla.PATHS["seq"]                    # a forced path is kept
+    assert lib.vla_resolve_path(ctypes.byref(desc(T=2, path=3)), ctypes.byref(p)) == 2
+    assert lib.vla_resolve_path(ctypes.byref(desc(path=4)), ctypes.byref(p)) == 1
+    n = ctypes.c_size_t(99)
+    assert lib.vla_workspace_size(ctypes.byref(desc(T=1)), ctypes.byref(n)) == 0 and n.value == 0
+
+
 def test_sequential_path_needs_no_workspace(lib):
     n = ctypes.c_size_t(99)
     assert lib.vla_workspace_size(ctypes.byref(desc(path=1)), ctypes.byref(n)) == 0

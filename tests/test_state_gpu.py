@@ -126,6 +126,64 @@ def test_decode_steps_equal_one_call():
     _compare("decode steps", TOL["bf16"], got, ref)
 
 
+DECODE_CASES = [(d, dt) for d in (32, 64, 96, 128) for dt in ("f32", "bf16")]
+
+
+@pytest.mark.parametrize("d,dt", DECODE_CASES)
+def test_decode_kernel_matches_oracle(d, dt):
+    """One token per stream on the decode path from an oracle state after 150 tokens."""
+    T0, T1 = 150, 1
+    _say(f"[case] decode kernel d={d} {dt}")
+    w, (q, k, v, u), (S0, A0, n0), ref = _case(d, dt, T0, T1, H=5)
+    H = w.H
+    dq, dk, dv, du = (_dev(x[:, T0:], w, (1, H, 1, d)) for x in (q, k, v, u))
+    out, S, A, n = vla.forward_state(dq, dk, dv, du, 0.0, S0=torch.from_numpy(S0).view(1, H, d, d).cuda(),
+                                     A0=torch.from_numpy(A0).view(1, H, d, d).cuda(),
+                                     n0=torch.from_numpy(n0).view(1, H, d).cuda(), eps=w.eps,
+                                     path="decode")
+    torch.cuda.synchronize()
+    got = (_np(out).reshape(H, 1, d), _np(S).reshape(H, d, d), _np(A).reshape(H, d, d),
+           _np(n).reshape(H, d))
+    _compare(f"decode d={d} {dt}", TOL[dt], got, ref)
+    Af = A.view(H, d, d)
+    assert torch.equal(Af, Af.transpose(1, 2)), "decode kept A exactly symmetric"
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_decode_path_steps_equal_one_call(dt):
+    d, T = 64, 40
+    w = get_workload("tiny_t256_d32").resized(name="decode_steps", B=2, H=3, T=T, d=d, dtype=dt,
+                                              lambda0=0.9)
+    _say(f"[case] {T} decode-path steps vs one sequential call, {dt}")
+    q, k, v, u = make_inputs(w)
+    full = [_dev(x, w, (2, 3, T, d)) for x in (q, k, v, u)]
+    o1, S1, A1, n1 = vla.forward_state(*full, w.lambda0, eps=w.eps, path="seq")
+    S = A = n = None
+    outs = []
+    for t in range(T):
+        step = [x[:, :, t:t + 1].contiguous() for x in full]
+        o, S, A, n = vla.forward_state(*step, w.lambda0, S0=S, A0=A, n0=n, eps=w.eps)  # auto: decode
+        outs.append(o)
+    torch.cuda.synchronize()
+    got = (_np(torch.cat(outs, dim=2)), _np(S), _np(A), _np(n))
+    ref = (_np(o1), _np(S1), _np(A1), _np(n1))
+    _compare(f"decode path steps {dt}", TOL[dt], got, ref)
+
+
+def test_decode_zero_key_and_zero_gain():
+    d = 32
+    w = get_workload("tiny_t256_d32").resized(name="decode_zero", B=1, H=2, T=1, d=d, dtype="f32")
+    q, k, v, u = make_inputs(w)
+    k[0] = 0.0  # stream 0: zero key (no memory write, A still downdates)
+    ref = oracle_forward(q, k, v, u, w.lambda0, eps=w.eps, return_n=True)
+    dev = [_dev(x, w, (1, 2, 1, d)) for x in (q, k, v, u)]
+    out, S, A, n = vla.forward_state(*dev, w.lambda0, eps=w.eps, path="decode")
+    torch.cuda.synchronize()
+    got = (_np(out).reshape(2, 1, d), _np(S).reshape(2, d, d), _np(A).reshape(2, d, d),
+           _np(n).reshape(2, d))
+    _compare("decode zero key", TOL["f32"], got, ref)
+
+
 def test_default_state_equals_vla_forward():
     w = get_workload("tiny_t256_d32").resized(name="defaults", B=1, H=2, T=700, d=96, dtype="bf16")
     q, k, v, u = make_inputs(w)
