@@ -114,6 +114,8 @@ def parse():
                     help="forward: whole sequences (default); decode: T = 1 calls, state carried")
     ap.add_argument("--decode-path", default="decode", choices=["decode", "seq"],
                     help="path of the T = 1 calls in --mode decode")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="batch B of the decode streams (0: the workload's); B x H streams")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -309,6 +311,8 @@ def decode_bench(args, w):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     nsteps = args.warmup + args.steps
+    if args.decode_batch > 0:
+        w = w.resized(name=f"{w.name}_b{args.decode_batch}", B=args.decode_batch)
     tok = upload_inputs(w.resized(name=w.name + "_decode", T=nsteps), dev)  # [B, H, steps, d]
     steps_in = [[x[:, :, t:t + 1].contiguous() for x in tok] for t in range(nsteps)]
     mat = (w.B, w.H, w.d, w.d)

@@ -1,17 +1,20 @@
-// Decode step (T = 1): one token per stream, each stream's rows spread over workgroups.
+// Decode step (T = 1): one token per stream, the stream's state held in registers.
 //
-// A decode call reads the carried state (S and A, d x d fp32 each) and writes it back.  With
-// one workgroup per stream most of the chip idles while a few CUs wait on two d x d loads.
-// Here workgroup (s, rt) owns rows 16 rt .. 16 rt + 15 of A and S of stream s.  It stages the
-// whole (symmetrised) A of the stream in LDS, computes the stream-wide vectors redundantly
-// with the other workgroups of the stream, and updates and writes only its own rows
-// (VLA summary §2.3 steps 1-3 and the ratio readout, for one token):
-//   z = A u,  delta = 1 + u.z,  A'[i][:] = A[i][:] - z_i z^T / delta
-//   A' khat = (A k - z (z.k) / delta) / ||k||,  ahat = A' khat / ||A' khat||
-//   S'[i][:] = S[i][:] + (v_i - S[i][:] . khat) ahat^T
-//   n' = n + phi(k),  o_i = S'[i][:] . phi(q) / (n'.phi(q) + eps)
-// Every workgroup of a stream computes delta and z identically and z_i z_j = z_j z_i, so
-// the rows written by different workgroups keep A exactly symmetric.
+// A decode call reads the carried state (S and A, d x d fp32 each), advances it by one token
+// and writes it back: per stream 16 d^2 bytes of HBM traffic for ~12 d^2 flops, so the call
+// is bound by HBM bandwidth once there are enough streams, and by latency below that.  One
+// workgroup of 256 threads takes one stream and touches each state element once: thread
+// (i, p) = (tid / 16, tid % 16) owns rows i + 16 a (a < d / 16) and, in each, the column
+// pairs 2 p + 32 b, 2 p + 32 b + 1 (b < d / 32), so that the 16 threads of a row read and
+// write 128 contiguous bytes per instruction and a row's sums are 16-lane shuffles.
+// Per stream (VLA summary §2.3 steps 1-3 and the ratio readout, for one token):
+//   z = A u,  g = A k,  delta = 1 + u.z,  A'[r][c] = A[r][c] - z_r z_c / delta
+//   y = A' khat = (g - z (z.k) / delta) / ||k||,  ahat = y / ||y||
+//   S'[r][:] = S[r][:] + (v_r - S[r][:] . khat) ahat^T
+//   n' = n + phi(k),  o_r = S'[r][:] . phi(q) / (n'.phi(q) + eps)
+// A carried A0 is used as (A0 + A0^T) / 2: the transposed element comes from a copy of A0
+// in LDS.  Both halves of a pair add the same two numbers, and every lane holds bitwise the
+// same z (butterfly sums), so A' is exactly symmetric.
 
 #include "vla_common.h"
 #include "vla_internal.h"
@@ -53,15 +56,35 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
                   float *__restrict__ A_final, const float *__restrict__ S0,
                   const float *__restrict__ A0, const float *__restrict__ n0,
                   float *__restrict__ n_final, float lambda0, float eps) {
-  constexpr int NT = 256, LDA = D + 1, NM = D / 16;
+  constexpr int R = D / 16, NB = D / 32, LDA = D + 1;
+  static_assert(D % 32 == 0, "column pairs of 16 lanes cover whole 32-column blocks");
   __shared__ float As[D][LDA];
   __shared__ float sU[D], sK[D], sQ[D], sZ[D], sG[D], sY[D], sN[D];
   __shared__ float red[5];  // ||k||^2, u.z, z.k, n'.phi(q), ||y||^2
   const int64_t s = blockIdx.x;
-  const int rt = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t tok = s * D;  // this stream's token (T = 1)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = tid >> 4, pj = tid & 15;
+  const int64_t tok = s * D, base = s * D * D;  // this stream's token (T = 1) and state
+  auto col = [&](int b, int e) { return 2 * pj + 32 * b + e; };
 
-  // token vectors and n' = n + phi(k)
+  // state loads first (the longest latency), then the token vectors
+  float2 Ar[R][NB], Sr[R][NB];
+  if (A0 != nullptr) {
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        Ar[a][b] = *reinterpret_cast<const float2 *>(A0 + base + (i + 16 * a) * D + col(b, 0));
+  }
+#pragma unroll
+  for (int a = 0; a < R; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      Sr[a][b] = S0 != nullptr
+                     ? *reinterpret_cast<const float2 *>(S0 + base + (i + 16 * a) * D + col(b, 0))
+                     : make_float2(0.f, 0.f);
+  float vr[R];
+#pragma unroll
+  for (int a = 0; a < R; ++a) vr[a] = ld_in(v, tok + i + 16 * a);
   if (tid < D) {
     sU[tid] = ld_in(u, tok + tid);
     const float kk = ld_in(k, tok + tid);
@@ -69,40 +92,55 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
     sQ[tid] = phi(ld_in(q, tok + tid));
     sN[tid] = (n0 != nullptr ? n0[s * D + tid] : 0.f) + phi(kk);
   }
-  // A, or I / lambda0
-  if (A0 != nullptr) {
-    const float *a = A0 + s * D * D;
-    for (int e = tid; e < D * D; e += NT) As[e / D][e % D] = a[e];
+  if (A0 != nullptr) {  // A <- (A0 + A0^T) / 2 through a copy in LDS
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        As[i + 16 * a][col(b, 0)] = Ar[a][b].x;
+        As[i + 16 * a][col(b, 1)] = Ar[a][b].y;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        Ar[a][b].x = 0.5f * (Ar[a][b].x + As[col(b, 0)][i + 16 * a]);
+        Ar[a][b].y = 0.5f * (Ar[a][b].y + As[col(b, 1)][i + 16 * a]);
+      }
   } else {
     const float il = 1.0f / lambda0;
-    for (int e = tid; e < D * D; e += NT) As[e / D][e % D] = (e / D == e % D) ? il : 0.f;
-  }
-  // this workgroup's rows of S (row i = tid / 16, columns j = tid % 16 + 16 m)
-  const int i = tid >> 4, pj = tid & 15, row = 16 * rt + i;
-  float Srow[NM];
 #pragma unroll
-  for (int m = 0; m < NM; ++m) Srow[m] = S0 != nullptr ? S0[s * D * D + row * D + pj + 16 * m] : 0.f;
-  const float vi = ld_in(v, tok + row);
-  __syncthreads();
-  if (A0 != nullptr) {  // (A0 + A0^T) / 2, each pair once
-    for (int e = tid; e < D * D; e += NT) {
-      const int r = e / D, c = e % D;
-      if (r < c) {
-        const float a = 0.5f * (As[r][c] + As[c][r]);
-        As[r][c] = a;
-        As[c][r] = a;
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        Ar[a][b].x = (i + 16 * a == col(b, 0)) ? il : 0.f;
+        Ar[a][b].y = (i + 16 * a == col(b, 1)) ? il : 0.f;
       }
-    }
-    __syncthreads();
   }
-  // z = A u and g = A k
-  if (tid < 2 * D) {
-    const int r = tid < D ? tid : tid - D;
-    const float *x = tid < D ? sU : sK;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < D; ++j) acc = fmaf(As[r][j], x[j], acc);
-    (tid < D ? sZ : sG)[r] = acc;
+  __syncthreads();  // token vectors visible
+  // row sums: z = A u, g = A k, S k (all lanes of a row end with the same value)
+  float z[R], g[R], sk[R];
+#pragma unroll
+  for (int a = 0; a < R; ++a) {
+    float za = 0.f, ga = 0.f, sa = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int c0 = col(b, 0), c1 = col(b, 1);
+      za = fmaf(Ar[a][b].y, sU[c1], fmaf(Ar[a][b].x, sU[c0], za));
+      ga = fmaf(Ar[a][b].y, sK[c1], fmaf(Ar[a][b].x, sK[c0], ga));
+      sa = fmaf(Sr[a][b].y, sK[c1], fmaf(Sr[a][b].x, sK[c0], sa));
+    }
+    z[a] = dec_sum16(za);
+    g[a] = dec_sum16(ga);
+    sk[a] = dec_sum16(sa);
+  }
+  if (pj == 0) {
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
+      sZ[i + 16 * a] = z[a];
+      sG[i + 16 * a] = g[a];
+    }
   }
   __syncthreads();
   if (wave == 0) {
@@ -130,31 +168,37 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
   }
   __syncthreads();
   const float ry = red[4] > 0.f ? rsqrtf(red[4]) : 0.f;  // ahat = y * ry, 0 for a zero gain
+  const float rden = 1.0f / (red[3] + eps);
   // rows: A' and S', the readout
-  float sk = 0.f;
 #pragma unroll
-  for (int m = 0; m < NM; ++m) sk = fmaf(Srow[m], sK[pj + 16 * m], sk);
-  const float r_i = vi - dec_sum16(sk) * rk;
-  float num = 0.f;
-  const float zi = sZ[row];
+  for (int a = 0; a < R; ++a) {
+    const int r = i + 16 * a;
+    const float ra = vr[a] - sk[a] * rk;
+    float num = 0.f;
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const int j = pj + 16 * m;
-    const float sn = fmaf(r_i, sY[j] * ry, Srow[m]);
-    num = fmaf(sn, sQ[j], num);
-    if (S_final != nullptr) S_final[s * D * D + row * D + j] = sn;
-    if (A_final != nullptr) A_final[s * D * D + row * D + j] = As[row][j] - zi * sZ[j] / delta;
+    for (int b = 0; b < NB; ++b) {
+      const int c0 = col(b, 0), c1 = col(b, 1);
+      float2 sn, an;
+      sn.x = fmaf(ra, sY[c0] * ry, Sr[a][b].x);
+      sn.y = fmaf(ra, sY[c1] * ry, Sr[a][b].y);
+      num = fmaf(sn.y, sQ[c1], fmaf(sn.x, sQ[c0], num));
+      an.x = Ar[a][b].x - z[a] * sZ[c0] / delta;
+      an.y = Ar[a][b].y - z[a] * sZ[c1] / delta;
+      if (S_final != nullptr) *reinterpret_cast<float2 *>(S_final + base + r * D + c0) = sn;
+      if (A_final != nullptr) *reinterpret_cast<float2 *>(A_final + base + r * D + c0) = an;
+    }
+    num = dec_sum16(num);
+    if (pj == 0) st_out(out, tok + r, num * rden);
   }
-  num = dec_sum16(num);
-  if (pj == 0) st_out(out, tok + row, num / (red[3] + eps));
-  if (rt == 0 && n_final != nullptr && tid < D) n_final[s * D + tid] = sN[tid];
+  if (n_final != nullptr && tid < D) n_final[s * D + tid] = sN[tid];
 }
 
 template <int D, typename TIn>
 static hipError_t launch_decode_t(const Problem &p, const void *q, const void *k, const void *v,
                                   const void *u, void *out, const StateIO &st, hipStream_t stream) {
+  if (p.streams > 0x7fffffff) return hipErrorInvalidValue;
   VLA_LAUNCH("vla_decode_kernel", (vla_decode_kernel<D, TIn>),
-             dim3(static_cast<unsigned>(p.streams), D / 16), dim3(256), 0, stream,
+             dim3(static_cast<unsigned>(p.streams)), dim3(256), 0, stream,
              static_cast<const TIn *>(q), static_cast<const TIn *>(k), static_cast<const TIn *>(v),
              static_cast<const TIn *>(u), static_cast<TIn *>(out), st.S_final, st.A_final, st.S0,
              st.A0, st.n0, st.n_final, p.lambda0, p.eps);
