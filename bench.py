@@ -59,6 +59,9 @@ KERNEL_WORK = {
     "k_swy_final": (lambda d: 6 * d * d + 10 * d, "mfma"),
     "k_swy_map": (lambda d: 8 * d * d, "mfma"),
     "k_gram": (lambda d: 2 * d * d, "mfma"),
+    # linear attention: S update and readout (2 d^2 each) plus the normaliser and ratio
+    "k_la_out": (lambda d: 4 * d * d + 6 * d, "mfma"),
+    "k_la_seg": (lambda d: 2 * d * d, "mfma"),
 }
 
 
@@ -110,8 +113,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per stream in the oracle sample (0 disables the CPU leg)")
     ap.add_argument("--cpu-cores", type=int, default=16)
-    ap.add_argument("--mode", default="forward", choices=["forward", "decode"],
-                    help="forward: whole sequences (default); decode: T = 1 calls, state carried")
+    ap.add_argument("--mode", default="forward", choices=["forward", "decode", "compare"],
+                    help="forward: whole sequences (default); decode: T = 1 calls, state carried; "
+                         "compare: VLA, VLA with u = 0 and linear attention on the same inputs")
     ap.add_argument("--decode-path", default="decode", choices=["decode", "seq"],
                     help="path of the T = 1 calls in --mode decode")
     ap.add_argument("--decode-batch", type=int, default=0,
@@ -186,6 +190,8 @@ def main():
     w = get_workload(args.workload)
     if args.mode == "decode":
         return decode_bench(args, w)
+    if args.mode == "compare":
+        return compare_bench(args, w)
     chunk = w.chunk if args.chunk < 0 else args.chunk
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -378,6 +384,101 @@ def decode_bench(args, w):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": kname, "kernel_ms": round(kernel_ms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _time_calls(fn, steps, warmup):
+    """Milliseconds per call (max of wall clock and stream events) and the per-kernel
+    table of the timed calls."""
+    import torch
+    from rls_associative_memory_amd import vla
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    vla.profile_reset()
+    vla.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    vla.profile_enable(False)
+    kernels = vla.profile_read()
+    return max(wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps), kernels
+
+
+def compare_bench(args, w):
+    """VLA, VLA with u = 0 (the delta rule with unit gains) and the linear-attention
+    baseline on the same resident inputs: the wall-clock price of the Sherman-Morrison
+    update that the pages put at about five times linear attention's operations."""
+    import torch
+    from rls_associative_memory_amd import vla
+    from rls_associative_memory_amd.inputs import upload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, u = upload_inputs(w, dev)
+    u0 = torch.zeros_like(u)
+    out = torch.empty_like(q)
+    shape = tuple(q.shape)
+    chunk = w.chunk if args.chunk < 0 else args.chunk
+    ws_v = vla.workspace_size(shape, q.dtype, path=args.path, chunk=chunk)
+    ws_l = vla.la_workspace_size(shape, q.dtype)
+    ws = torch.empty(max(ws_v, ws_l, 16), dtype=torch.uint8, device=dev)
+    S = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
+    A = torch.empty_like(S)
+    n = torch.empty((w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    tokens = w.B * w.H * w.T
+    res = {}
+    for name, fn in (
+            ("vla", lambda: vla.forward(q, k, v, u, w.lambda0, eps=w.eps, path=args.path, chunk=chunk,
+                                        out=out, S_final=S, A_final=A, workspace=ws)),
+            ("vla_u0", lambda: vla.forward(q, k, v, u0, w.lambda0, eps=w.eps, path=args.path,
+                                           chunk=chunk, out=out, S_final=S, A_final=A, workspace=ws)),
+            ("la", lambda: vla.linear_attention(q, k, v, eps=w.eps, out=out, S_final=S, n_final=n,
+                                                workspace=ws))):
+        ms, kernels = _time_calls(fn, args.steps, args.warmup)
+        res[name] = (ms, kernels)
+        print(f"[bench] {name}: {ms:.3f} ms/call", file=sys.stderr, flush=True)
+        for kn, (tot, cnt) in sorted(kernels.items(), key=lambda kv: -kv[1][0]):
+            print(f"[bench]   kernel {kn:16s} {tot / max(cnt, 1):9.3f} ms/launch x {cnt}",
+                  file=sys.stderr, flush=True)
+    la_ms, la_k = res["la"]
+    k_tot, k_n = la_k.get("k_la_out", (0.0, 1))
+    kernel_ms = k_tot / max(k_n, 1)
+    achieved = KERNEL_WORK["k_la_out"][0](w.d) * tokens / (kernel_ms * 1e-3) / 1e12 if kernel_ms else 0.0
+    line = {
+        "metric": "linear attention (same harness) tokens·heads/sec at 1 MI355X; VLA / LA time ratio",
+        "value": tokens / (la_ms * 1e-3),
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": la_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "input_dtype": w.dtype},
+        "compare": {
+            "vla_ms": round(res["vla"][0], 4),
+            "vla_u0_ms": round(res["vla_u0"][0], 4),
+            "la_ms": round(la_ms, 4),
+            "vla_over_la_time": round(res["vla"][0] / la_ms, 3),
+            "vla_over_la_flops": round(flops_per_token_head(w.d) / (4 * w.d * w.d + 6 * w.d), 3),
+        },
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                     "traffic": None, "kernel": "k_la_out", "kernel_ms": round(kernel_ms, 4)},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

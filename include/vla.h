@@ -124,6 +124,33 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
                                void *out, float *S_final, float *A_final, float *n_final,
                                const vla_desc_t *desc, struct ihipStream_t *stream);
 
+/*
+ * vla_linear_attention -- the baseline the VLA update is measured against: standard linear
+ * attention with the same ELU+1 feature map and ratio readout (VLA summary §2.1, the
+ * unconditional accumulation VLA replaces; §2.3, the readout; §2.4 prices the VLA update at
+ * about five times its operations), per (batch, head) stream from S_0 = 0, n_0 = 0:
+ *
+ *   S_t = S_{t-1} + v_t phi(k_t)^T,  n_t = n_{t-1} + phi(k_t),
+ *   o_t = S_t phi(q_t) / (n_t^T phi(q_t) + eps)
+ *
+ * q, k, v     device pointers, [B, H, T, d] in desc->dtype, read only, 16-byte aligned.
+ * out         device pointer, [B, H, T, d] in desc->dtype, fully overwritten; must not
+ *             alias any input.
+ * S_final     device pointer to [B, H, d, d] fp32 (S[i][j], i = value, j = key) receiving
+ *             S_T, or NULL.
+ * n_final     device pointer to [B, H, d] fp32 receiving n_T, or NULL.
+ * desc        as for vla_forward, with path VLA_PATH_AUTO and chunk 0 (or 64, the only
+ *             chunk length), else VLA_ERROR_NOT_SUPPORTED.  Chunked, time-segment parallel;
+ *             workspace as for vla_forward, sized by vla_la_workspace_size().
+ * Ownership, asynchrony and error behaviour are those of vla_forward.
+ */
+vla_status_t vla_linear_attention(const void *q, const void *k, const void *v, void *out,
+                                  float *S_final, float *n_final, const vla_desc_t *desc,
+                                  struct ihipStream_t *stream);
+
+/* Bytes of device workspace vla_linear_attention needs for this descriptor. */
+vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes);
+
 /* Bytes of device workspace vla_forward needs for this descriptor (0 for the
  * sequential path).  Same argument checks as vla_forward; no device work. */
 vla_status_t vla_workspace_size(const vla_desc_t *desc, size_t *bytes);

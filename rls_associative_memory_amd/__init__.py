@@ -6,7 +6,7 @@ tensors and the current HIP stream into it.  Importing this package loads nothin
 library is opened on first use and a missing library is an error, never a fallback.
 """
 
-__all__ = ["forward", "forward_state", "workspace_size", "library_path", "VlaError"]
+__all__ = ["forward", "forward_state", "linear_attention", "workspace_size", "library_path", "VlaError"]
 
 
 def __getattr__(name):

@@ -238,6 +238,45 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
   return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
 }
 
+vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes) {
+  if (bytes == nullptr) return VLA_ERROR_INVALID_VALUE;
+  vla_status_t st = check_desc(desc);
+  if (st != VLA_SUCCESS) return st;
+  if (desc->path != VLA_PATH_AUTO || (desc->chunk != 0 && desc->chunk != 64))
+    return VLA_ERROR_NOT_SUPPORTED;
+  *bytes = vla::la_workspace_bytes(make_problem(desc, 1.0f));
+  return VLA_SUCCESS;
+}
+
+vla_status_t vla_linear_attention(const void *q, const void *k, const void *v, void *out,
+                                  float *S_final, float *n_final, const vla_desc_t *desc,
+                                  struct ihipStream_t *stream) {
+  vla_status_t st = check_desc(desc);
+  if (st != VLA_SUCCESS) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return VLA_ERROR_INVALID_VALUE;
+  if (desc->path != VLA_PATH_AUTO || (desc->chunk != 0 && desc->chunk != 64))
+    return VLA_ERROR_NOT_SUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(S_final) ||
+      !aligned16(n_final))
+    return VLA_ERROR_NOT_SUPPORTED;
+  const vla::Problem p = make_problem(desc, 1.0f);
+  const size_t need = vla::la_workspace_bytes(p);
+  void *ws = nullptr;
+  if (desc->workspace != nullptr) {
+    if (desc->workspace_bytes < need) return VLA_ERROR_INVALID_VALUE;
+    if (!aligned16(desc->workspace)) return VLA_ERROR_NOT_SUPPORTED;
+    ws = desc->workspace;
+  }
+  if (!device_ok()) return VLA_ERROR_NO_DEVICE;
+  if (ws == nullptr) {
+    st = cached_workspace(need, &ws);
+    if (st != VLA_SUCCESS) return st;
+  }
+  const hipError_t err = vla::launch_la(p, q, k, v, out, S_final, n_final, ws,
+                                        reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
+}
+
 vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
                          float lambda0, void *out, float *S_final, float *A_final,
                          const vla_desc_t *desc, struct ihipStream_t *stream) {

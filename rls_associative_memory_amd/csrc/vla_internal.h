@@ -42,6 +42,12 @@ hipError_t launch_chunk(const Problem &p, int chunk, const void *q, const void *
                         const void *v, const void *u, void *out, const StateIO &st, void *ws,
                         hipStream_t stream);
 
+// Linear-attention baseline (chunked, time-segment parallel): out, S_T (S[i][j]) and n_T
+// of every stream; `ws` must hold la_workspace_bytes(p).  p.lambda0 is not used.
+size_t la_workspace_bytes(const Problem &p);
+hipError_t launch_la(const Problem &p, const void *q, const void *k, const void *v, void *out,
+                     float *S_final, float *n_final, void *ws, hipStream_t stream);
+
 // Event-pair timing of one kernel launch when vla_profile_enable(1) is in effect.
 class ProfScope {
  public:

@@ -15,7 +15,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["forward", "forward_state", "workspace_size", "resolve_path", "library_path", "load_library",
+__all__ = ["forward", "forward_state", "linear_attention", "la_workspace_size", "workspace_size", "resolve_path", "library_path", "load_library",
            "profile_enable", "profile_reset", "profile_read",
            "VlaError", "exported_symbols", "STATUS", "PATHS", "DTYPES", "VlaDesc"]
 
@@ -76,6 +76,10 @@ def load_library():
         lib.vla_forward_state.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(VlaDesc), vp]
         lib.vla_forward_state.restype = ctypes.c_int
+        lib.vla_linear_attention.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(VlaDesc), vp]
+        lib.vla_linear_attention.restype = ctypes.c_int
+        lib.vla_la_workspace_size.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_size_t)]
+        lib.vla_la_workspace_size.restype = ctypes.c_int
         lib.vla_workspace_size.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.vla_workspace_size.restype = ctypes.c_int
         lib.vla_resolve_path.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_int32)]
@@ -260,6 +264,54 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
             n_T.data_ptr(), ctypes.byref(desc), s.cuda_stream)
     _check(status, "vla_forward_state")
     return out, S_T, A_T, n_T
+
+
+def la_workspace_size(shape, dtype) -> int:
+    """Device workspace bytes of vla_linear_attention for [B, H, T, d] inputs."""
+    lib = load_library()
+    desc = make_desc(shape, dtype)
+    n = ctypes.c_size_t(0)
+    _check(lib.vla_la_workspace_size(ctypes.byref(desc), ctypes.byref(n)), "vla_la_workspace_size")
+    return n.value
+
+
+def linear_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eps: float = 1e-6,
+                     out: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None,
+                     n_final: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None):
+    """Linear-attention baseline (vla_linear_attention in vla.h) over [B, H, T, d] (or
+    [N, T, d]) device tensors.  Returns (out, S_T [.., d, d] fp32, n_T [.., d] fp32)."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+    desc = make_desc(tuple(q.shape), q.dtype, eps=eps, workspace=workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q in shape and dtype and be contiguous")
+    d = q.shape[-1]
+    mat_shape = tuple(q.shape[:-2]) + (d, d)
+    vec_shape = tuple(q.shape[:-2]) + (d,)
+    for name, t, shp in (("S_final", S_final, mat_shape), ("n_final", n_final, vec_shape)):
+        if t is not None and (tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 {shp} tensor")
+    if S_final is None:
+        S_final = torch.empty(mat_shape, dtype=torch.float32, device=q.device)
+    if n_final is None:
+        n_final = torch.empty(vec_shape, dtype=torch.float32, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = lib.vla_linear_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                          S_final.data_ptr(), n_final.data_ptr(), ctypes.byref(desc),
+                                          s.cuda_stream)
+    _check(status, "vla_linear_attention")
+    return out, S_final, n_final
 
 
 def profile_enable(on: bool = True) -> None:

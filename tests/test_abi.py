@@ -128,6 +128,25 @@ def test_forward_state_rejects_in_place_state(lib):
                                  fake(8 * mat), None, None, fake(mat + 256), ctypes.byref(d), None) == 1
 
 
+def test_linear_attention_argument_errors(lib):
+    """Argument errors of vla_linear_attention come back before any device work."""
+    x = ctypes.c_void_p(1 << 20)
+    d = desc(B=1, H=2, T=100, d=64)
+    assert lib.vla_linear_attention(None, x, x, x, None, None, ctypes.byref(d), None) == 1
+    assert lib.vla_linear_attention(x, x, x, x, None, None, ctypes.byref(desc(d=48)), None) == 2
+    assert lib.vla_linear_attention(x, x, x, x, None, None, ctypes.byref(desc(path=1)), None) == 2
+    assert lib.vla_linear_attention(x, x, x, x, None, None, ctypes.byref(desc(chunk=32)), None) == 2
+    assert lib.vla_linear_attention(ctypes.c_void_p((1 << 20) + 8), x, x, x, None, None,
+                                    ctypes.byref(d), None) == 2
+    small = desc(B=1, H=2, T=100, d=64, workspace=1 << 20, workspace_bytes=16)
+    assert lib.vla_linear_attention(x, x, x, x, None, None, ctypes.byref(small), None) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.vla_la_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    # 2 streams x 2 segments (one chunk each) x (d^2 + d) fp32
+    assert n.value == 2 * 2 * (64 * 64 + 64) * 4
+    assert lib.vla_la_workspace_size(ctypes.byref(desc(path=2)), ctypes.byref(n)) == 2
+
+
 def test_decode_path_resolution(lib):
     p = ctypes.c_int32(-1)
     assert lib.vla_resolve_path(ctypes.byref(desc(T=1)), ctypes.byref(p)) == 0
