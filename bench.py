@@ -113,9 +113,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per stream in the oracle sample (0 disables the CPU leg)")
     ap.add_argument("--cpu-cores", type=int, default=16)
-    ap.add_argument("--mode", default="forward", choices=["forward", "decode", "compare"],
+    ap.add_argument("--mode", default="forward", choices=["forward", "decode", "compare", "ablation"],
                     help="forward: whole sequences (default); decode: T = 1 calls, state carried; "
-                         "compare: VLA, VLA with u = 0 and linear attention on the same inputs")
+                         "compare: VLA, VLA with u = 0 and linear attention on the same inputs; "
+                         "ablation: growth of the state-transition product, unit vs raw gain")
     ap.add_argument("--decode-path", default="decode", choices=["decode", "seq"],
                     help="path of the T = 1 calls in --mode decode")
     ap.add_argument("--decode-batch", type=int, default=0,
@@ -192,6 +193,8 @@ def main():
         return decode_bench(args, w)
     if args.mode == "compare":
         return compare_bench(args, w)
+    if args.mode == "ablation":
+        return ablation_bench(args)
     chunk = w.chunk if args.chunk < 0 else args.chunk
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -480,6 +483,68 @@ def compare_bench(args, w):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
                      "traffic": None, "kernel": "k_la_out", "kernel_ms": round(kernel_ms, 4)},
         "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+LAMBDAS = (0.001, 0.01, 0.05, 0.25, 1.0, 4.0)
+
+
+def ablation_bench(args):
+    """Norm of the state-transition product prod_t (I - khat_t g_t^T) after 25, 100 and 1000
+    tokens, with the unit gain g = ahat (the method) and the raw gain g = A_t khat (the
+    ablation of VLA summary §3.1, Prop. 2), over head sizes and lambda0.
+
+    The product is the state itself: the recurrence with v = 0 from S_0 = I (carried state)
+    on the sequential kernel, continued from call to call.  Inputs: 64 streams of i.i.d.
+    N(0, 1) q, k, u (the recipe of the other workloads), fp32.  Spectral norms in fp64 on
+    the host.  One JSON line: the median and maximum over the streams per configuration."""
+    import torch
+    from rls_associative_memory_amd import vla
+    from rls_associative_memory_amd.inputs import Workload, upload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    checkpoints = (25, 100, 1000)
+    streams = 64
+    rows = []
+    t_all = time.perf_counter()
+    for d in (32, 64, 96, 128):
+        w = Workload(f"ablation_d{d}", 1, streams, checkpoints[-1], d, "f32", 1.0, 7, "iid")
+        q, k, v, u = upload_inputs(w, dev)
+        v.zero_()
+        eye = torch.eye(d, dtype=torch.float32, device=dev).expand(1, streams, d, d).contiguous()
+        for lam in LAMBDAS:
+            for gain in ("unit", "raw"):
+                S, A, n = eye, None, None
+                t0 = 0
+                rec = {"d": d, "lambda0": lam, "gain": gain}
+                for t1 in checkpoints:
+                    part = [x[:, :, t0:t1].contiguous() for x in (q, k, v, u)]
+                    _, S, A, n = vla.forward_state(*part, lam, S0=S, A0=A, n0=n, gain=gain, path="seq")
+                    torch.cuda.synchronize()
+                    mats = S.view(streams, d, d).double().cpu().numpy()
+                    norms = np.array([np.linalg.norm(m, 2) if np.all(np.isfinite(m)) else np.inf
+                                      for m in mats])
+                    finite = norms[np.isfinite(norms)]
+                    rec[f"t{t1}"] = {"median": float(np.median(norms)), "max": float(np.max(norms)),
+                                     "finite_streams": int(finite.size)}
+                    t0 = t1
+                rows.append(rec)
+                print(f"[bench] ablation d={d} lambda0={lam} {gain}: "
+                      + " ".join(f"t={c}: {rec[f't{c}']['median']:.3e}" for c in checkpoints),
+                      file=sys.stderr, flush=True)
+    line = {
+        "metric": "||prod_t (I - khat_t g_t^T)||_2 after 25/100/1000 tokens, unit vs raw gain (median over 64 streams)",
+        "value": None,
+        "unit": "spectral norm",
+        "n_gpus": 1,
+        "data": "synthetic",
+        "dtype": "f32",
+        "config": {"workload": "ablation_iid_64streams_t1000", "streams": streams, "d": [32, 64, 96, 128],
+                   "lambda0": list(LAMBDAS), "checkpoints": list(checkpoints), "path": "seq"},
+        "seconds": round(time.perf_counter() - t_all, 1),
+        "table": rows,
     }
     print(json.dumps(line), flush=True)
 

@@ -39,10 +39,12 @@ struct ihipStream_t;
 typedef enum {
   VLA_SUCCESS = 0,
   VLA_ERROR_INVALID_VALUE = 1, /* NULL required pointer, size < 1, lambda0 <= 0 or not
-                                  finite, eps < 0 or not finite, unknown dtype or path,
+                                  finite, eps < 0 or not finite, unknown dtype, path or
+                                  gain,
                                   workspace smaller than vla_workspace_size()          */
   VLA_ERROR_NOT_SUPPORTED = 2, /* d not in {32, 64, 96, 128}; a pointer not 16-byte
-                                  aligned; a forced path or chunk the shape cannot use */
+                                  aligned; a forced path, chunk or gain the shape
+                                  cannot use                                            */
   VLA_ERROR_OUT_OF_MEMORY = 3, /* internal workspace allocation failed                */
   VLA_ERROR_LAUNCH = 4,        /* a HIP launch or runtime call failed                 */
   VLA_ERROR_NO_DEVICE = 5      /* no usable gfx950 device is current                  */
@@ -54,9 +56,16 @@ typedef enum {
   VLA_PATH_AUTO = 0,  /* library chooses from (B*H, T, d)                              */
   VLA_PATH_SEQ = 1,   /* one workgroup per stream, token by token, state on chip       */
   VLA_PATH_CHUNK = 2, /* chunked (Woodbury / WY) form; parallel over time segments     */
-  VLA_PATH_DECODE = 3 /* T = 1 only: one token per stream, a stream's rows spread over
-                         d / 16 workgroups (chosen by AUTO whenever T = 1)              */
+  VLA_PATH_DECODE = 3 /* T = 1 only: one workgroup per stream with its state in
+                         registers (chosen by AUTO whenever T = 1)                      */
 } vla_path_t;
+
+/* Gain of the S update.  UNIT is the method: ahat = A_t khat / ||A_t khat|| (VLA summary
+ * §2.3 step 2).  RAW uses A_t khat without the normalisation: the ablation that §3.1
+ * (Prop. 2) contrasts with the unit gain, whose state-transition products can grow without
+ * bound.  RAW runs on the sequential and decode paths only (AUTO picks them; a forced
+ * chunked path is VLA_ERROR_NOT_SUPPORTED). */
+typedef enum { VLA_GAIN_UNIT = 0, VLA_GAIN_RAW = 1 } vla_gain_t;
 
 typedef struct {
   int64_t B, H, T, d;       /* q, k, v, u, out are [B, H, T, d], row-major, d fastest   */
@@ -66,6 +75,7 @@ typedef struct {
   int32_t chunk;            /* chunk length of the chunked path; 0 = library default    */
   void *workspace;          /* device scratch owned by the caller, or NULL              */
   size_t workspace_bytes;   /* its size in bytes; ignored when workspace is NULL        */
+  int32_t gain;             /* vla_gain_t; 0 (UNIT) is the method                       */
 } vla_desc_t;
 
 /*
@@ -139,8 +149,8 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
  * S_final     device pointer to [B, H, d, d] fp32 (S[i][j], i = value, j = key) receiving
  *             S_T, or NULL.
  * n_final     device pointer to [B, H, d] fp32 receiving n_T, or NULL.
- * desc        as for vla_forward, with path VLA_PATH_AUTO and chunk 0 (or 64, the only
- *             chunk length), else VLA_ERROR_NOT_SUPPORTED.  Chunked, time-segment parallel;
+ * desc        as for vla_forward, with path VLA_PATH_AUTO, chunk 0 (or 64, the only chunk
+ *             length) and gain VLA_GAIN_UNIT, else VLA_ERROR_NOT_SUPPORTED.  Chunked, time-segment parallel;
  *             workspace as for vla_forward, sized by vla_la_workspace_size().
  * Ownership, asynchrony and error behaviour are those of vla_forward.
  */

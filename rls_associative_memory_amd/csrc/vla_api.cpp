@@ -34,6 +34,7 @@ vla_status_t check_desc(const vla_desc_t *desc) {
   if (desc->path < VLA_PATH_AUTO || desc->path > VLA_PATH_DECODE) return VLA_ERROR_INVALID_VALUE;
   if (!(desc->eps >= 0.0f) || !std::isfinite(desc->eps)) return VLA_ERROR_INVALID_VALUE;
   if (desc->chunk < 0) return VLA_ERROR_INVALID_VALUE;
+  if (desc->gain != VLA_GAIN_UNIT && desc->gain != VLA_GAIN_RAW) return VLA_ERROR_INVALID_VALUE;
   // B*H*T*d must be addressable; B*H must fit a grid dimension.
   const int64_t lim = int64_t(1) << 40;
   if (desc->B > lim / desc->H) return VLA_ERROR_INVALID_VALUE;
@@ -52,6 +53,7 @@ vla::Problem make_problem(const vla_desc_t *desc, float lambda0) {
   p.dtype = desc->dtype == VLA_DTYPE_F32 ? vla::Dtype::F32 : vla::Dtype::BF16;
   p.lambda0 = lambda0;
   p.eps = desc->eps;
+  p.raw_gain = desc->gain == VLA_GAIN_RAW;
   return p;
 }
 
@@ -62,6 +64,8 @@ vla_status_t resolve(const vla_desc_t *desc, const vla::Problem &p, int32_t *pat
   int32_t want = desc->path;
   if (want == VLA_PATH_DECODE && p.T != 1) return VLA_ERROR_NOT_SUPPORTED;
   if (want == VLA_PATH_AUTO && p.T == 1) want = VLA_PATH_DECODE;
+  if (want == VLA_PATH_AUTO && p.raw_gain) want = VLA_PATH_SEQ;  // the only multi-token path with it
+  if (want == VLA_PATH_CHUNK && p.raw_gain) return VLA_ERROR_NOT_SUPPORTED;
   if (want == VLA_PATH_AUTO) {
     // Enough streams to fill the machine one workgroup each, or sequences too short to
     // amortise the segment passes: run token by token.  Otherwise split time.
@@ -242,7 +246,8 @@ vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes) {
   if (bytes == nullptr) return VLA_ERROR_INVALID_VALUE;
   vla_status_t st = check_desc(desc);
   if (st != VLA_SUCCESS) return st;
-  if (desc->path != VLA_PATH_AUTO || (desc->chunk != 0 && desc->chunk != 64))
+  if (desc->path != VLA_PATH_AUTO || (desc->chunk != 0 && desc->chunk != 64) ||
+      desc->gain != VLA_GAIN_UNIT)
     return VLA_ERROR_NOT_SUPPORTED;
   *bytes = vla::la_workspace_bytes(make_problem(desc, 1.0f));
   return VLA_SUCCESS;
@@ -254,7 +259,8 @@ vla_status_t vla_linear_attention(const void *q, const void *k, const void *v, v
   vla_status_t st = check_desc(desc);
   if (st != VLA_SUCCESS) return st;
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return VLA_ERROR_INVALID_VALUE;
-  if (desc->path != VLA_PATH_AUTO || (desc->chunk != 0 && desc->chunk != 64))
+  if (desc->path != VLA_PATH_AUTO || (desc->chunk != 0 && desc->chunk != 64) ||
+      desc->gain != VLA_GAIN_UNIT)
     return VLA_ERROR_NOT_SUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(S_final) ||
       !aligned16(n_final))

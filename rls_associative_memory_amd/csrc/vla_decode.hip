@@ -55,7 +55,7 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
                   const TIn *__restrict__ u, TIn *__restrict__ out, float *__restrict__ S_final,
                   float *__restrict__ A_final, const float *__restrict__ S0,
                   const float *__restrict__ A0, const float *__restrict__ n0,
-                  float *__restrict__ n_final, float lambda0, float eps) {
+                  float *__restrict__ n_final, float lambda0, float eps, int raw_gain) {
   constexpr int R = D / 16, NB = D / 32, LDA = D + 1;
   static_assert(D % 32 == 0, "column pairs of 16 lanes cover whole 32-column blocks");
   __shared__ float As[D][LDA];
@@ -167,7 +167,8 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
     if (lane == 0) red[4] = yy;
   }
   __syncthreads();
-  const float ry = red[4] > 0.f ? rsqrtf(red[4]) : 0.f;  // ahat = y * ry, 0 for a zero gain
+  // ahat = y * ry: the unit gain (0 for a zero y), or the raw gain y for the ablation
+  const float ry = raw_gain ? 1.0f : (red[4] > 0.f ? rsqrtf(red[4]) : 0.f);
   const float rden = 1.0f / (red[3] + eps);
   // rows: A' and S', the readout
 #pragma unroll
@@ -201,7 +202,7 @@ static hipError_t launch_decode_t(const Problem &p, const void *q, const void *k
              dim3(static_cast<unsigned>(p.streams)), dim3(256), 0, stream,
              static_cast<const TIn *>(q), static_cast<const TIn *>(k), static_cast<const TIn *>(v),
              static_cast<const TIn *>(u), static_cast<TIn *>(out), st.S_final, st.A_final, st.S0,
-             st.A0, st.n0, st.n_final, p.lambda0, p.eps);
+             st.A0, st.n0, st.n_final, p.lambda0, p.eps, p.raw_gain ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ struct Problem {
   Dtype dtype;
   float lambda0;
   float eps;
+  bool raw_gain = false;  // gain A_t khat without the normalisation (ablation)
 };
 
 // Carried state of every stream, fp32 device tensors: the state the recurrence starts from

@@ -49,7 +49,7 @@ vla_seq_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *
                const TIn *__restrict__ u, TIn *__restrict__ out, float *__restrict__ S_final,
                float *__restrict__ A_final, const float *__restrict__ S0,
                const float *__restrict__ A0, const float *__restrict__ n0,
-               float *__restrict__ n_final, int64_t T, float lambda0, float eps) {
+               float *__restrict__ n_final, int64_t T, float lambda0, float eps, int raw_gain) {
   using C = SeqCfg<D>;
   using IO = io<TIn>;
   constexpr int VW = IO::kVec;
@@ -239,7 +239,8 @@ vla_seq_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *
 #pragma unroll
             for (int w = 0; w < C::NWA; ++w) { sy += sRed[1][w][0]; sq += sRed[1][w][1]; }
           }
-          const float inv = sy > 0.f ? rsqrtf(sy) : 0.f;
+          // unit gain (the method) or, for the ablation, the raw gain A_t khat
+          const float inv = raw_gain ? 1.0f : (sy > 0.f ? rsqrtf(sy) : 0.f);
           const float rd = rsqrtf(delta);
           float w[C::RPL];
 #pragma unroll
@@ -385,7 +386,7 @@ static hipError_t launch_seq_t(const Problem &p, const void *q, const void *k, c
                      dim3(C::NT), 0, stream, static_cast<const TIn *>(q),
                      static_cast<const TIn *>(k), static_cast<const TIn *>(v),
                      static_cast<const TIn *>(u), static_cast<TIn *>(out), st.S_final, st.A_final,
-                     st.S0, st.A0, st.n0, st.n_final, p.T, p.lambda0, p.eps);
+                     st.S0, st.A0, st.n0, st.n_final, p.T, p.lambda0, p.eps, p.raw_gain ? 1 : 0);
   return hipGetLastError();
 }
 

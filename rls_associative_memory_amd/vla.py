@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["forward", "forward_state", "linear_attention", "la_workspace_size", "workspace_size", "resolve_path", "library_path", "load_library",
            "profile_enable", "profile_reset", "profile_read",
-           "VlaError", "exported_symbols", "STATUS", "PATHS", "DTYPES", "VlaDesc"]
+           "VlaError", "exported_symbols", "STATUS", "PATHS", "DTYPES", "GAINS", "VlaDesc"]
 
 STATUS = {
     0: "VLA_SUCCESS",
@@ -29,6 +29,7 @@ STATUS = {
 }
 PATHS = {"auto": 0, "seq": 1, "chunk": 2, "decode": 3}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+GAINS = {"unit": 0, "raw": 1}  # raw: A_t khat without the normalisation (ablation only)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "vla.h")
@@ -46,7 +47,7 @@ class VlaDesc(ctypes.Structure):
         ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64), ("d", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("path", ctypes.c_int32), ("eps", ctypes.c_float),
         ("chunk", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-        ("workspace_bytes", ctypes.c_size_t),
+        ("workspace_bytes", ctypes.c_size_t), ("gain", ctypes.c_int32),
     ]
 
 
@@ -110,7 +111,7 @@ def exported_symbols():
     return sorted(set(re.findall(r"\b(vla_[a-z_0-9]+)\s*\(", text)))
 
 
-def make_desc(shape, dtype, eps=1e-6, path="auto", chunk=0, workspace=None) -> VlaDesc:
+def make_desc(shape, dtype, eps=1e-6, path="auto", chunk=0, workspace=None, gain="unit") -> VlaDesc:
     if len(shape) == 4:
         B, H, T, d = shape
     elif len(shape) == 3:
@@ -121,8 +122,10 @@ def make_desc(shape, dtype, eps=1e-6, path="auto", chunk=0, workspace=None) -> V
         raise TypeError("dtype must be torch.float32 or torch.bfloat16")
     if path not in PATHS:
         raise ValueError(f"path must be one of {sorted(PATHS)}")
+    if gain not in GAINS:
+        raise ValueError(f"gain must be one of {sorted(GAINS)}")
     desc = VlaDesc(B=B, H=H, T=T, d=d, dtype=DTYPES[dtype], path=PATHS[path], eps=float(eps),
-                   chunk=int(chunk), workspace=None, workspace_bytes=0)
+                   chunk=int(chunk), workspace=None, workspace_bytes=0, gain=GAINS[gain])
     if workspace is not None:
         if not (workspace.is_cuda and workspace.is_contiguous()):
             raise ValueError("workspace must be a contiguous device tensor")
@@ -144,9 +147,9 @@ def workspace_size(shape, dtype, path="auto", chunk=0) -> int:
     return n.value
 
 
-def resolve_path(shape, dtype, path="auto", chunk=0) -> str:
+def resolve_path(shape, dtype, path="auto", chunk=0, gain="unit") -> str:
     lib = load_library()
-    desc = make_desc(shape, dtype, path=path, chunk=chunk)
+    desc = make_desc(shape, dtype, path=path, chunk=chunk, gain=gain)
     p = ctypes.c_int32(0)
     _check(lib.vla_resolve_path(ctypes.byref(desc), ctypes.byref(p)), "vla_resolve_path")
     return {v: k for k, v in PATHS.items()}[p.value]
@@ -214,13 +217,14 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   stream: Optional[torch.cuda.Stream] = None,
                   S_final: Optional[torch.Tensor] = None, A_final: Optional[torch.Tensor] = None,
-                  n_final: Optional[torch.Tensor] = None):
+                  n_final: Optional[torch.Tensor] = None, gain: str = "unit"):
     """VLA forward continuing from a carried state (vla_forward_state in vla.h).
 
     S0 and A0 are fp32 [.., d, d] and n0 fp32 [.., d] device tensors, or None for the fixed
     start (S = 0, A = I / lambda0, n = 0); lambda0 is only used when A0 is None.  Returns
     (out, S_T, A_T, n_T), which a next call takes as its (S0, A0, n0); S_final, A_final and
     n_final optionally give the buffers to write them to (they must not be S0, A0, n0).
+    ``gain="raw"`` runs the un-normalised-gain ablation (sequential and decode paths only).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
@@ -230,7 +234,8 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
             raise ValueError(f"{name} must be contiguous")
         if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
             raise ValueError("q, k, v, u must share shape, dtype and device")
-    desc = make_desc(tuple(q.shape), q.dtype, eps=eps, path=path, chunk=chunk, workspace=workspace)
+    desc = make_desc(tuple(q.shape), q.dtype, eps=eps, path=path, chunk=chunk, workspace=workspace,
+                     gain=gain)
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():

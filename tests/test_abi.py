@@ -19,7 +19,7 @@ def lib():
 
 def desc(**kw):
     base = dict(B=2, H=3, T=17, d=64, dtype=1, path=0, eps=1e-6, chunk=0, workspace=None,
-                workspace_bytes=0)
+                workspace_bytes=0, gain=0)
     base.update(kw)
     return vla.VlaDesc(**base)
 
@@ -145,6 +145,24 @@ def test_linear_attention_argument_errors(lib):
     # 2 streams x 2 segments (one chunk each) x (d^2 + d) fp32
     assert n.value == 2 * 2 * (64 * 64 + 64) * 4
     assert lib.vla_la_workspace_size(ctypes.byref(desc(path=2)), ctypes.byref(n)) == 2
+
+
+def test_raw_gain_descriptor(lib):
+    p = ctypes.c_int32(-1)
+    assert lib.vla_resolve_path(ctypes.byref(desc(gain=2)), ctypes.byref(p)) == 1
+    assert lib.vla_resolve_path(ctypes.byref(desc(gain=-1)), ctypes.byref(p)) == 1
+    long = desc(B=1, H=2, T=4096, d=96, gain=1)
+    assert lib.vla_resolve_path(ctypes.byref(long), ctypes.byref(p)) == 0
+    assert p.value == vla.PATHS["seq"]                    # the chunked path has no raw gain
+    assert lib.vla_resolve_path(ctypes.byref(desc(B=1, H=2, T=4096, d=96)), ctypes.byref(p)) == 0
+    assert p.value == vla.PATHS["chunk"]
+    assert lib.vla_resolve_path(ctypes.byref(desc(T=4096, path=2, gain=1)), ctypes.byref(p)) == 2
+    assert lib.vla_resolve_path(ctypes.byref(desc(T=1, gain=1)), ctypes.byref(p)) == 0
+    assert p.value == vla.PATHS["decode"]
+    n = ctypes.c_size_t(0)
+    assert lib.vla_la_workspace_size(ctypes.byref(desc(gain=1)), ctypes.byref(n)) == 2
+    with pytest.raises(ValueError):
+        vla.make_desc((1, 1, 4, 32), torch.float32, gain="half")
 
 
 def test_decode_path_resolution(lib):
