@@ -3,10 +3,11 @@
 // A decode call reads the carried state (S and A, d x d fp32 each), advances it by one token
 // and writes it back: per stream 16 d^2 bytes of HBM traffic for ~12 d^2 flops, so the call
 // is bound by HBM bandwidth once there are enough streams, and by latency below that.  One
-// workgroup of 256 threads takes one stream and touches each state element once: thread
-// (i, p) = (tid / 16, tid % 16) owns rows i + 16 a (a < d / 16) and, in each, the column
-// pairs 2 p + 32 b, 2 p + 32 b + 1 (b < d / 32), so that the 16 threads of a row read and
-// write 128 contiguous bytes per instruction and a row's sums are 16-lane shuffles.
+// workgroup of 512 threads (two waves per SIMD) takes one stream and touches each state
+// element once: thread (i, p) = (tid / 16, tid % 16) owns rows i + 32 a (a < d / 32) and, in
+// each, the column pairs 2 p + 32 b, 2 p + 32 b + 1 (b < d / 32), so that the 16 threads of a
+// row read and write 128 contiguous bytes per instruction and a row's sums are 16-lane
+// shuffles.
 // Per stream (VLA summary §2.3 steps 1-3 and the ratio readout, for one token):
 //   z = A u,  g = A k,  delta = 1 + u.z,  A'[r][c] = A[r][c] - z_r z_c / delta
 //   y = A' khat = (g - z (z.k) / delta) / ||k||,  ahat = y / ||y||
@@ -50,13 +51,13 @@ __device__ __forceinline__ float dec_sum16(float x) {  // over the 16 lanes of a
 }
 
 template <int D, typename TIn>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
                   const TIn *__restrict__ u, TIn *__restrict__ out, float *__restrict__ S_final,
                   float *__restrict__ A_final, const float *__restrict__ S0,
                   const float *__restrict__ A0, const float *__restrict__ n0,
                   float *__restrict__ n_final, float lambda0, float eps, int raw_gain) {
-  constexpr int R = D / 16, NB = D / 32, LDA = D + 1;
+  constexpr int NT = 512, RG = NT / 16, R = D / RG, NB = D / 32, LDA = D + 1;
   static_assert(D % 32 == 0, "column pairs of 16 lanes cover whole 32-column blocks");
   __shared__ float As[D][LDA];
   __shared__ float sU[D], sK[D], sQ[D], sZ[D], sG[D], sY[D], sN[D];
@@ -73,18 +74,18 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
     for (int a = 0; a < R; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        Ar[a][b] = *reinterpret_cast<const float2 *>(A0 + base + (i + 16 * a) * D + col(b, 0));
+        Ar[a][b] = *reinterpret_cast<const float2 *>(A0 + base + (i + RG * a) * D + col(b, 0));
   }
 #pragma unroll
   for (int a = 0; a < R; ++a)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
       Sr[a][b] = S0 != nullptr
-                     ? *reinterpret_cast<const float2 *>(S0 + base + (i + 16 * a) * D + col(b, 0))
+                     ? *reinterpret_cast<const float2 *>(S0 + base + (i + RG * a) * D + col(b, 0))
                      : make_float2(0.f, 0.f);
   float vr[R];
 #pragma unroll
-  for (int a = 0; a < R; ++a) vr[a] = ld_in(v, tok + i + 16 * a);
+  for (int a = 0; a < R; ++a) vr[a] = ld_in(v, tok + i + RG * a);
   if (tid < D) {
     sU[tid] = ld_in(u, tok + tid);
     const float kk = ld_in(k, tok + tid);
@@ -97,16 +98,16 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
     for (int a = 0; a < R; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        As[i + 16 * a][col(b, 0)] = Ar[a][b].x;
-        As[i + 16 * a][col(b, 1)] = Ar[a][b].y;
+        As[i + RG * a][col(b, 0)] = Ar[a][b].x;
+        As[i + RG * a][col(b, 1)] = Ar[a][b].y;
       }
     __syncthreads();
 #pragma unroll
     for (int a = 0; a < R; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        Ar[a][b].x = 0.5f * (Ar[a][b].x + As[col(b, 0)][i + 16 * a]);
-        Ar[a][b].y = 0.5f * (Ar[a][b].y + As[col(b, 1)][i + 16 * a]);
+        Ar[a][b].x = 0.5f * (Ar[a][b].x + As[col(b, 0)][i + RG * a]);
+        Ar[a][b].y = 0.5f * (Ar[a][b].y + As[col(b, 1)][i + RG * a]);
       }
   } else {
     const float il = 1.0f / lambda0;
@@ -114,8 +115,8 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
     for (int a = 0; a < R; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        Ar[a][b].x = (i + 16 * a == col(b, 0)) ? il : 0.f;
-        Ar[a][b].y = (i + 16 * a == col(b, 1)) ? il : 0.f;
+        Ar[a][b].x = (i + RG * a == col(b, 0)) ? il : 0.f;
+        Ar[a][b].y = (i + RG * a == col(b, 1)) ? il : 0.f;
       }
   }
   __syncthreads();  // token vectors visible
@@ -138,8 +139,8 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
   if (pj == 0) {
 #pragma unroll
     for (int a = 0; a < R; ++a) {
-      sZ[i + 16 * a] = z[a];
-      sG[i + 16 * a] = g[a];
+      sZ[i + RG * a] = z[a];
+      sG[i + RG * a] = g[a];
     }
   }
   __syncthreads();
@@ -173,7 +174,7 @@ vla_decode_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TI
   // rows: A' and S', the readout
 #pragma unroll
   for (int a = 0; a < R; ++a) {
-    const int r = i + 16 * a;
+    const int r = i + RG * a;
     const float ra = vr[a] - sk[a] * rk;
     float num = 0.f;
 #pragma unroll
@@ -199,7 +200,7 @@ static hipError_t launch_decode_t(const Problem &p, const void *q, const void *k
                                   const void *u, void *out, const StateIO &st, hipStream_t stream) {
   if (p.streams > 0x7fffffff) return hipErrorInvalidValue;
   VLA_LAUNCH("vla_decode_kernel", (vla_decode_kernel<D, TIn>),
-             dim3(static_cast<unsigned>(p.streams)), dim3(256), 0, stream,
+             dim3(static_cast<unsigned>(p.streams)), dim3(512), 0, stream,
              static_cast<const TIn *>(q), static_cast<const TIn *>(k), static_cast<const TIn *>(v),
              static_cast<const TIn *>(u), static_cast<TIn *>(out), st.S_final, st.A_final, st.S0,
              st.A0, st.n0, st.n_final, p.lambda0, p.eps, p.raw_gain ? 1 : 0);
