@@ -78,3 +78,29 @@ def test_linear_attention_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_linear_attention_full_long_workload_sampled():
+    """The 131072-token workload (32 streams, d = 96, bf16) at full size in the launch
+    configuration bench.py times: stream 0 checked in full against the oracle (out, S_T, n_T),
+    the first 2048 tokens of streams 1 and 31 (causal prefix)."""
+    from rls_associative_memory_amd.inputs import make_stream, upload_inputs
+    w = get_workload("long_t131072_d96")
+    q, k, v, _ = upload_inputs(w, "cuda")
+    _say(f"[case] linear attention full long workload {w.B}x{w.H}x{w.T}x{w.d}")
+    out, S, n = vla.linear_attention(q, k, v, eps=w.eps)
+    torch.cuda.synchronize()
+    o = out.view(-1, w.T, w.d)
+    tol = TOL[w.dtype]
+    for s, ntok in ((0, w.T), (1, 2048), (31, 2048)):
+        qs, ks, vs, _ = (torch.from_numpy(x[:ntok]).to(torch.bfloat16).double().numpy()
+                         for x in make_stream(w, s))
+        ro, rS, rn = la_forward(qs, ks, vs, eps=w.eps)
+        errs = {"out": rel_l2(_np(o[s, :ntok]), ro)}
+        if ntok == w.T:
+            errs["S"] = rel_l2(_np(S.view(-1, w.d, w.d)[s]), rS)
+            errs["n"] = rel_l2(_np(n.view(-1, w.d)[s]), rn)
+        _say(f"[parity] la long stream {s} ({ntok} tokens): "
+             + " ".join(f"{key}={e:.3e}" for key, e in errs.items()) + f" (tol {tol:g})")
+        for key, e in errs.items():
+            assert e < tol, f"stream {s} {key} rel L2 {e:.3e} >= {tol:g}"

@@ -193,3 +193,30 @@ def test_default_state_equals_vla_forward():
         o2, S2, A2, _ = vla.forward_state(*dev, w.lambda0, eps=w.eps, path=path)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(A1, A2), path
+
+
+def test_decode_kernel_many_streams_sampled():
+    """2048 streams (the decode bench's --decode-batch 64 shape, d = 96, bf16) from a carried
+    state: sampled streams checked against the oracle's single step."""
+    d, H, B = 96, 32, 64
+    w = get_workload("long_t131072_d96").resized(name="decode_many", B=B, H=H, T=2)
+    q, k, v, u = make_inputs(w)
+    q, k, v, u = (torch.from_numpy(x).to(torch.bfloat16).float().numpy() for x in (q, k, v, u))
+    streams = B * H
+    rng = np.random.default_rng(11)
+    # a valid carried state per stream: the oracle's state after the first token
+    pre = oracle_forward(q[:, :1], k[:, :1], v[:, :1], u[:, :1], w.lambda0, eps=w.eps, return_n=True)
+    S0, A0, n0 = (x.astype(np.float32) for x in pre[1:])
+    dev = [_dev(x[:, 1:], w, (B, H, 1, d)) for x in (q, k, v, u)]
+    _say(f"[case] decode kernel {streams} streams d={d}")
+    out, S, A, n = vla.forward_state(*dev, 0.0, S0=torch.from_numpy(S0).view(B, H, d, d).cuda(),
+                                     A0=torch.from_numpy(A0).view(B, H, d, d).cuda(),
+                                     n0=torch.from_numpy(n0).view(B, H, d).cuda(), eps=w.eps)
+    torch.cuda.synchronize()
+    pick = np.sort(rng.choice(streams, 16, replace=False))
+    st = (S0[pick], A0[pick], n0[pick])
+    ref = oracle_forward(q[pick, 1:], k[pick, 1:], v[pick, 1:], u[pick, 1:], w.lambda0, eps=w.eps,
+                         state=st, return_n=True)
+    got = (_np(out).reshape(streams, 1, d)[pick], _np(S).reshape(streams, d, d)[pick],
+           _np(A).reshape(streams, d, d)[pick], _np(n).reshape(streams, d)[pick])
+    _compare(f"decode {streams} streams (16 sampled)", TOL["bf16"], got, ref)
