@@ -7,3 +7,4 @@ may import this package.  The product path (``rls_associative_memory_amd``) neve
 
 from .vla_oracle import init_state, phi, vla_forward, vla_step  # noqa: F401
 from .la_oracle import la_forward  # noqa: F401
+from .vla_grad import vla_forward_torch, vla_grad  # noqa: F401
