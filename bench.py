@@ -113,10 +113,12 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per stream in the oracle sample (0 disables the CPU leg)")
     ap.add_argument("--cpu-cores", type=int, default=16)
-    ap.add_argument("--mode", default="forward", choices=["forward", "decode", "compare", "ablation"],
+    ap.add_argument("--mode", default="forward",
+                    choices=["forward", "decode", "compare", "ablation", "backward"],
                     help="forward: whole sequences (default); decode: T = 1 calls, state carried; "
                          "compare: VLA, VLA with u = 0 and linear attention on the same inputs; "
-                         "ablation: growth of the state-transition product, unit vs raw gain")
+                         "ablation: growth of the state-transition product, unit vs raw gain; "
+                         "backward: gradients of every input (default workload mqar_t512_d32)")
     ap.add_argument("--decode-path", default="decode", choices=["decode", "seq"],
                     help="path of the T = 1 calls in --mode decode")
     ap.add_argument("--decode-batch", type=int, default=0,
@@ -188,7 +190,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "backward" and args.workload == "long_t131072_d96":
+        args.workload = "mqar_t512_d32"  # the sequential backward suits many short streams
     w = get_workload(args.workload)
+    if args.mode == "backward":
+        return backward_bench(args, w)
     if args.mode == "decode":
         return decode_bench(args, w)
     if args.mode == "compare":
@@ -482,6 +488,55 @@ def compare_bench(args, w):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
                      "traffic": None, "kernel": "k_la_out", "kernel_ms": round(kernel_ms, 4)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def backward_bench(args, w):
+    """vla_backward over a whole workload (random cotangents for out, S_T, A_T, n_T): one
+    step is one call.  Executed work per token*head: the forward replay (12 d^2) and the
+    reverse sweep (28 d^2: 14 matrix-vector products and rank-1 updates of d x d)."""
+    import torch
+    from rls_associative_memory_amd import vla
+    from rls_associative_memory_amd.inputs import upload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v, u = upload_inputs(w, dev)
+    g = torch.Generator(device=dev).manual_seed(3)
+    d_out = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+    mat = (w.B, w.H, w.d, w.d)
+    dS = torch.randn(mat, generator=g, device=dev)
+    dA = torch.randn(mat, generator=g, device=dev)
+    dn = torch.randn((w.B, w.H, w.d), generator=g, device=dev)
+    ws = torch.empty(vla.backward_workspace_size(tuple(q.shape), q.dtype), dtype=torch.uint8, device=dev)
+    ms, kernels = _time_calls(lambda: vla.backward(q, k, v, u, w.lambda0, d_out, dS, dA, dn, eps=w.eps,
+                                                   workspace=ws), args.steps, args.warmup)
+    tokens = w.B * w.H * w.T
+    k_tot, k_n = kernels.get("vla_backward_kernel", (0.0, 1))
+    kernel_ms = k_tot / max(k_n, 1)
+    flops = (40 * w.d * w.d) * tokens
+    achieved = flops / (kernel_ms * 1e-3) / 1e12 if kernel_ms else 0.0
+    print(f"[bench] backward {w.name}: {ms:.3f} ms/call (kernel {kernel_ms:.3f} ms)", file=sys.stderr, flush=True)
+    line = {
+        "metric": "VLA backward (dq, dk, dv, du, dlambda0) tokens·heads/sec at 1 MI355X",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "input_dtype": w.dtype,
+                   "path": "seq"},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                     "kernel": "vla_backward_kernel", "kernel_ms": round(kernel_ms, 4)},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

@@ -161,6 +161,38 @@ vla_status_t vla_linear_attention(const void *q, const void *k, const void *v, v
 /* Bytes of device workspace vla_linear_attention needs for this descriptor. */
 vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes);
 
+/*
+ * vla_backward -- gradients of the recurrence of vla_forward (fixed start S_0 = 0,
+ * A_0 = I / lambda0, n_0 = 0) for the scalar loss
+ *   L = <d_out, out> + <dS_T, S_T> + <dA_T, A_T> + <dn_T, n_T>,
+ * i.e. the reverse pass of training through the layer (VLA summary §3.1 argues the unit gain
+ * keeps these gradients stable; §4 trains the models).
+ *
+ * q, k, v, u, lambda0  the forward's inputs, as for vla_forward (device, [B, H, T, d],
+ *             desc->dtype, 16-byte aligned).
+ * d_out       device pointer, [B, H, T, d] in desc->dtype: the cotangent of out.
+ * dS_T, dA_T  device pointers to [B, H, d, d] fp32 cotangents of S_T and A_T, or NULL (0).
+ * dn_T        device pointer to [B, H, d] fp32 cotangent of n_T, or NULL (0).
+ * dq, dk, dv, du  device pointers, [B, H, T, d] fp32, fully overwritten.
+ * dlambda0    device pointer to [B * H] fp32 receiving each stream's share of dL/dlambda0
+ *             (their sum is the derivative; every stream starts from I / lambda0), or NULL.
+ * desc        path VLA_PATH_AUTO or VLA_PATH_SEQ, gain VLA_GAIN_UNIT, else
+ *             VLA_ERROR_NOT_SUPPORTED; the workspace holds vla_backward_workspace_size()
+ *             bytes (per stream: T x (6 d + 8) floats of per-token vectors and the state at
+ *             every 32nd token), else the per-device cache is used as for vla_forward.
+ * Runs one workgroup per stream, token by token (a replay of the forward, then the reverse
+ * sweep).  At ||k_t|| = 0 or ||A_t khat_t|| = 0 the normalisation has no derivative; the
+ * gradient through it is taken as 0.  Outputs must not overlap inputs.  Ownership,
+ * asynchrony and error behaviour are those of vla_forward.
+ */
+vla_status_t vla_backward(const void *q, const void *k, const void *v, const void *u,
+                          float lambda0, const void *d_out, const float *dS_T, const float *dA_T,
+                          const float *dn_T, float *dq, float *dk, float *dv, float *du,
+                          float *dlambda0, const vla_desc_t *desc, struct ihipStream_t *stream);
+
+/* Bytes of device workspace vla_backward needs for this descriptor. */
+vla_status_t vla_backward_workspace_size(const vla_desc_t *desc, size_t *bytes);
+
 /* Bytes of device workspace vla_forward needs for this descriptor (0 for the
  * sequential path).  Same argument checks as vla_forward; no device work. */
 vla_status_t vla_workspace_size(const vla_desc_t *desc, size_t *bytes);

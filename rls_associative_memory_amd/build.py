@@ -24,7 +24,7 @@ LIBDIR = os.path.join(PKG, "lib")
 BUILDDIR = os.path.join(PKG, "_build")
 LIBNAME = "librls_vla.so"
 
-SOURCES = ["vla_api.cpp", "vla_profile.cpp", "vla_seq.hip", "vla_chunk.hip", "vla_decode.hip", "la_chunk.hip"]
+SOURCES = ["vla_api.cpp", "vla_profile.cpp", "vla_seq.hip", "vla_chunk.hip", "vla_decode.hip", "la_chunk.hip", "vla_backward.hip"]
 ARCH = "gfx950"
 
 

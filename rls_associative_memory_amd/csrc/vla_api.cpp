@@ -283,6 +283,49 @@ vla_status_t vla_linear_attention(const void *q, const void *k, const void *v, v
   return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
 }
 
+vla_status_t vla_backward_workspace_size(const vla_desc_t *desc, size_t *bytes) {
+  if (bytes == nullptr) return VLA_ERROR_INVALID_VALUE;
+  vla_status_t st = check_desc(desc);
+  if (st != VLA_SUCCESS) return st;
+  if ((desc->path != VLA_PATH_AUTO && desc->path != VLA_PATH_SEQ) || desc->gain != VLA_GAIN_UNIT)
+    return VLA_ERROR_NOT_SUPPORTED;
+  *bytes = vla::backward_workspace_bytes(make_problem(desc, 1.0f));
+  return VLA_SUCCESS;
+}
+
+vla_status_t vla_backward(const void *q, const void *k, const void *v, const void *u,
+                          float lambda0, const void *d_out, const float *dS_T, const float *dA_T,
+                          const float *dn_T, float *dq, float *dk, float *dv, float *du,
+                          float *dlambda0, const vla_desc_t *desc, struct ihipStream_t *stream) {
+  vla_status_t st = check_desc(desc);
+  if (st != VLA_SUCCESS) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || u == nullptr || d_out == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr || du == nullptr)
+    return VLA_ERROR_INVALID_VALUE;
+  if (!(lambda0 > 0.0f) || !std::isfinite(lambda0)) return VLA_ERROR_INVALID_VALUE;
+  if ((desc->path != VLA_PATH_AUTO && desc->path != VLA_PATH_SEQ) || desc->gain != VLA_GAIN_UNIT)
+    return VLA_ERROR_NOT_SUPPORTED;
+  const void *ptrs[] = {q, k, v, u, d_out, dS_T, dA_T, dn_T, dq, dk, dv, du, dlambda0};
+  for (const void *x : ptrs)
+    if (!aligned16(x)) return VLA_ERROR_NOT_SUPPORTED;
+  const vla::Problem p = make_problem(desc, lambda0);
+  const size_t need = vla::backward_workspace_bytes(p);
+  void *ws = nullptr;
+  if (desc->workspace != nullptr) {
+    if (desc->workspace_bytes < need) return VLA_ERROR_INVALID_VALUE;
+    if (!aligned16(desc->workspace)) return VLA_ERROR_NOT_SUPPORTED;
+    ws = desc->workspace;
+  }
+  if (!device_ok()) return VLA_ERROR_NO_DEVICE;
+  if (ws == nullptr) {
+    st = cached_workspace(need, &ws);
+    if (st != VLA_SUCCESS) return st;
+  }
+  vla::BackwardIO io{q, k, v, u, d_out, dS_T, dA_T, dn_T, dq, dk, dv, du, dlambda0};
+  const hipError_t err = vla::launch_backward(p, io, ws, reinterpret_cast<hipStream_t>(stream));
+  return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
+}
+
 vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
                          float lambda0, void *out, float *S_final, float *A_final,
                          const vla_desc_t *desc, struct ihipStream_t *stream) {

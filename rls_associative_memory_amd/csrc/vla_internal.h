@@ -49,6 +49,16 @@ size_t la_workspace_bytes(const Problem &p);
 hipError_t launch_la(const Problem &p, const void *q, const void *k, const void *v, void *out,
                      float *S_final, float *n_final, void *ws, hipStream_t stream);
 
+// Backward of the recurrence from the fixed start (sequential, one workgroup per stream).
+struct BackwardIO {
+  const void *q, *k, *v, *u, *dout;            // [streams][T][d] in the input dtype
+  const float *dS_T, *dA_T, *dn_T;             // cotangents of the final state, or NULL
+  float *dq, *dk, *dv, *du;                    // [streams][T][d] fp32
+  float *dlambda0;                             // [streams] fp32, or NULL
+};
+size_t backward_workspace_bytes(const Problem &p);
+hipError_t launch_backward(const Problem &p, const BackwardIO &io, void *ws, hipStream_t stream);
+
 // Event-pair timing of one kernel launch when vla_profile_enable(1) is in effect.
 class ProfScope {
  public:

@@ -15,7 +15,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["forward", "forward_state", "linear_attention", "la_workspace_size", "workspace_size", "resolve_path", "library_path", "load_library",
+__all__ = ["forward", "forward_state", "backward", "backward_workspace_size", "linear_attention", "la_workspace_size", "workspace_size", "resolve_path", "library_path", "load_library",
            "profile_enable", "profile_reset", "profile_read",
            "VlaError", "exported_symbols", "STATUS", "PATHS", "DTYPES", "GAINS", "VlaDesc"]
 
@@ -79,6 +79,11 @@ def load_library():
         lib.vla_forward_state.restype = ctypes.c_int
         lib.vla_linear_attention.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(VlaDesc), vp]
         lib.vla_linear_attention.restype = ctypes.c_int
+        lib.vla_backward.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.POINTER(VlaDesc), vp]
+        lib.vla_backward.restype = ctypes.c_int
+        lib.vla_backward_workspace_size.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_size_t)]
+        lib.vla_backward_workspace_size.restype = ctypes.c_int
         lib.vla_la_workspace_size.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_size_t)]
         lib.vla_la_workspace_size.restype = ctypes.c_int
         lib.vla_workspace_size.argtypes = [ctypes.POINTER(VlaDesc), ctypes.POINTER(ctypes.c_size_t)]
@@ -317,6 +322,53 @@ def linear_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eps: flo
                                           s.cuda_stream)
     _check(status, "vla_linear_attention")
     return out, S_final, n_final
+
+
+def backward_workspace_size(shape, dtype) -> int:
+    """Device workspace bytes of vla_backward for [B, H, T, d] inputs."""
+    lib = load_library()
+    desc = make_desc(shape, dtype)
+    n = ctypes.c_size_t(0)
+    _check(lib.vla_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
+           "vla_backward_workspace_size")
+    return n.value
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor, lambda0: float,
+             d_out: torch.Tensor, dS_T: Optional[torch.Tensor] = None,
+             dA_T: Optional[torch.Tensor] = None, dn_T: Optional[torch.Tensor] = None,
+             eps: float = 1e-6, workspace: Optional[torch.Tensor] = None,
+             stream: Optional[torch.cuda.Stream] = None):
+    """Gradients of <d_out, out> + <dS_T, S_T> + <dA_T, A_T> + <dn_T, n_T> through the
+    forward from the fixed start (vla_backward in vla.h).  Returns (dq, dk, dv, du) as fp32
+    tensors shaped like q and dlambda0, the per-stream shares [.., ] of dL/dlambda0."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u), ("d_out", d_out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, u, d_out must share shape, dtype and device")
+    d = q.shape[-1]
+    mat_shape = tuple(q.shape[:-2]) + (d, d)
+    vec_shape = tuple(q.shape[:-2]) + (d,)
+    for name, t, shp in (("dS_T", dS_T, mat_shape), ("dA_T", dA_T, mat_shape), ("dn_T", dn_T, vec_shape)):
+        if t is not None and (tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous()
+                              or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous fp32 {shp} tensor on q's device")
+    desc = make_desc(tuple(q.shape), q.dtype, eps=eps, workspace=workspace)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(4)]
+    dlam = torch.empty(tuple(q.shape[:-2]), dtype=torch.float32, device=q.device)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = lib.vla_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), u.data_ptr(), float(lambda0),
+                                  d_out.data_ptr(), ptr(dS_T), ptr(dA_T), ptr(dn_T),
+                                  *(g.data_ptr() for g in grads), dlam.data_ptr(), ctypes.byref(desc),
+                                  s.cuda_stream)
+    _check(status, "vla_backward")
+    return (*grads, dlam)
 
 
 def profile_enable(on: bool = True) -> None:

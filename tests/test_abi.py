@@ -165,6 +165,29 @@ def test_raw_gain_descriptor(lib):
         vla.make_desc((1, 1, 4, 32), torch.float32, gain="half")
 
 
+def test_backward_argument_errors(lib):
+    """Argument errors of vla_backward come back before any device work."""
+    x = ctypes.c_void_p(1 << 20)
+    d = desc(B=1, H=2, T=100, d=64)
+    f = ctypes.c_float(1.0)
+    args = [x, x, x, x, f, x, None, None, None, x, x, x, x, None]
+    call = lambda a, dd: lib.vla_backward(*a, ctypes.byref(dd), None)
+    bad = list(args); bad[5] = None
+    assert call(bad, d) == 1                                   # no d_out
+    bad = list(args); bad[4] = ctypes.c_float(0.0)
+    assert call(bad, d) == 1                                   # lambda0 <= 0
+    assert call(args, desc(B=1, H=2, T=100, d=64, path=2)) == 2
+    assert call(args, desc(B=1, H=2, T=100, d=64, gain=1)) == 2
+    bad = list(args); bad[9] = ctypes.c_void_p((1 << 20) + 4)
+    assert call(bad, d) == 2                                   # misaligned dq
+    small = desc(B=1, H=2, T=100, d=64, workspace=1 << 20, workspace_bytes=64)
+    assert call(args, small) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.vla_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    # per stream: T (6 d + 8) floats of records and ceil(T / 32) checkpoints of 2 d^2 floats
+    assert n.value == 2 * (100 * (6 * 64 + 8) + 4 * 2 * 64 * 64) * 4
+
+
 def test_decode_path_resolution(lib):
     p = ctypes.c_int32(-1)
     assert lib.vla_resolve_path(ctypes.byref(desc(T=1)), ctypes.byref(p)) == 0

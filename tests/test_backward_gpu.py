@@ -1,0 +1,69 @@
+"""Parity of vla_backward against the fp64 autograd oracle (GPU only).
+
+The oracle (oracle/vla_grad.py) is pinned to finite differences of the numpy forward on the
+CPU.  Here every gradient (dq, dk, dv, du and dlambda0) of the loss <d_out, out> +
+<dS_T, S_T> + <dA_T, A_T> + <dn_T, n_T> with random cotangents is compared by relative L2:
+< 1e-4 for fp32 inputs, < 1e-2 for bf16 inputs (the oracle sees the bf16-rounded inputs and
+cotangent).  Lengths cross the 32-token state checkpoints and end mid-interval.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from rls_associative_memory_amd import vla
+from rls_associative_memory_amd.inputs import get_workload, make_inputs, torch_dtype
+
+from .parity import TOL, rel_l2
+from oracle import vla_grad
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _run(d, dt, T, H=2, lam=0.8, with_state=True, seed=5):
+    w = get_workload("tiny_t256_d32").resized(name=f"bw_{d}_{dt}_{T}", B=1, H=H, T=T, d=d,
+                                              dtype=dt, lambda0=lam)
+    q, k, v, u = make_inputs(w)
+    r = np.random.default_rng(seed)
+    dout = r.standard_normal(q.shape).astype(np.float32)
+    dS = r.standard_normal((H, d, d)).astype(np.float32) if with_state else None
+    dA = r.standard_normal((H, d, d)).astype(np.float32) if with_state else None
+    dn = r.standard_normal((H, d)).astype(np.float32) if with_state else None
+    dev = [torch.from_numpy(np.ascontiguousarray(x)).view(1, H, T, d).to(torch_dtype(w)).cuda()
+           for x in (q, k, v, u, dout)]
+    seen = [x.float().cpu().numpy().reshape(H, T, d).astype(np.float64) for x in dev]
+    _say(f"[case] backward d={d} {dt} T={T} state cotangents={with_state}")
+    tens = lambda x, shp: torch.from_numpy(x).view(shp).cuda() if x is not None else None
+    got = vla.backward(*dev[:4], lam, dev[4], dS_T=tens(dS, (1, H, d, d)), dA_T=tens(dA, (1, H, d, d)),
+                       dn_T=tens(dn, (1, H, d)), eps=w.eps)
+    torch.cuda.synchronize()
+    ref = vla_grad(*seen[:4], lam, seen[4], dS, dA, dn, eps=w.eps)
+    tol = TOL[dt]
+    names = ("dq", "dk", "dv", "du")
+    errs = {n: rel_l2(g.cpu().numpy().reshape(H, T, d), rf) for n, g, rf in zip(names, got[:4], ref[:4])}
+    errs["dlambda0"] = rel_l2(got[4].cpu().numpy().reshape(H), ref[4])
+    _say(f"[parity] backward d={d} {dt} T={T}: " + " ".join(f"{n}={e:.3e}" for n, e in errs.items())
+         + f" (tol {tol:g})")
+    for n, e in errs.items():
+        assert e < tol, f"{n} rel L2 {e:.3e} >= {tol:g}"
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_matches_oracle(d, dt):
+    _run(d, dt, T=70)
+
+
+@pytest.mark.parametrize("T", [1, 32, 33])
+def test_backward_edge_lengths(T):
+    _run(64, "f32", T=T)
+
+
+def test_backward_without_state_cotangents_and_long():
+    _run(64, "f32", T=300, with_state=False, lam=0.5)
