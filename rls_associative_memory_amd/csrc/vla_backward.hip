@@ -44,22 +44,16 @@ struct BwCfg {
   static constexpr int REC = 6 * D + BW_NS;  // khat, z, ahat, r, phi(q), o, scalars
 };
 
+// Sum over each 16-lane row (DPP, no LDS round trip); every lane of the row gets the sum.
 __device__ __forceinline__ float bw_sum16(float x) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dpp_xor1(x);
+  x += dpp_xor2(x);
+  x += dpp_half_mirror(x);
+  return x + dpp_mirror(x);
 }
-__device__ __forceinline__ float bw_wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-template <typename TIn>
-__device__ __forceinline__ float bw_ld(const TIn *p, int64_t i);
-template <>
-__device__ __forceinline__ float bw_ld<float>(const float *p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float bw_ld<bf16_t>(const bf16_t *p, int64_t i) { return bf16_to_f32(p[i].bits); }
+__device__ __forceinline__ float bw_wave_sum(float x) { return wave_sum(x); }
+__device__ __forceinline__ float bw_cv(float x) { return x; }
+__device__ __forceinline__ float bw_cv(bf16_t x) { return bf16_to_f32(x.bits); }
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
 
 template <int D>
@@ -124,15 +118,24 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
   if (tid < D) sh.n[tid] = 0.f;
 
   // ---------------- forward replay: records and checkpoints ----------------
+  // Token t + 1's inputs are loaded (raw, into registers) while token t is processed.
+  TIn nk{}, nu{}, nv{}, nq{};
+  if (tid < D) {
+    const int64_t tok0 = s * T * D;
+    nk = k[tok0 + tid]; nu = u[tok0 + tid]; nv = v[tok0 + tid]; nq = q[tok0 + tid];
+  }
   for (int64_t t = 0; t < T; ++t) {
     const int64_t tok = (s * T + t) * D;
     if (tid < D) {
-      const float kk = bw_ld(k, tok + tid);
+      const float kk = bw_cv(nk);
       sh.kr[tid] = kk;
-      sh.u[tid] = bw_ld(u, tok + tid);
-      sh.v[tid] = bw_ld(v, tok + tid);
-      sh.fq[tid] = phi(bw_ld(q, tok + tid));
+      sh.u[tid] = bw_cv(nu);
+      sh.v[tid] = bw_cv(nv);
+      sh.fq[tid] = phi(bw_cv(nq));
       sh.fk[tid] = phi(kk);
+      if (t + 1 < T) {
+        nk = k[tok + D + tid]; nu = u[tok + D + tid]; nv = v[tok + D + tid]; nq = q[tok + D + tid];
+      }
     }
     __syncthreads();
     float z[R], sk[R];
@@ -276,9 +279,22 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
       for (int ww = 0; ww < C::NW; ++ww) dlam += static_cast<double>(sh.red[ww]);
     __syncthreads();
   }
+  // Token t - 1's record and inputs are loaded (into registers) while token t is processed.
+  float pr[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, psc = 0.f;
+  TIn pk{}, pu{}, pdo{}, pq{};
+  auto load_rev = [&](int64_t t) {
+    const float *rec = rec0 + t * C::REC;
+    const int64_t tok = (s * T + t) * D;
+    if (tid < D) {
+#pragma unroll
+      for (int f = 0; f < 6; ++f) pr[f] = rec[f * D + tid];
+      pk = k[tok + tid]; pu = u[tok + tid]; pdo = dout[tok + tid]; pq = q[tok + tid];
+    }
+    if (tid < BW_NS) psc = rec[6 * D + tid];
+  };
+  load_rev(T - 1);
   for (int64_t t = T - 1; t >= 0; --t) {
     const int64_t tok = (s * T + t) * D;
-    const float *rec = rec0 + t * C::REC;
     if (t % BW_CK == BW_CK - 1 && t != T - 1) {  // exact state after token t
       const float *ck = ck0 + (t / BW_CK) * 2 * D * D;
 #pragma unroll
@@ -291,18 +307,21 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
           A[a][b][0] = av.x; A[a][b][1] = av.y;
         }
     }
+    float qt = 0.f;  // raw q of token t (for dq)
     if (tid < D) {
-      sh.kh[tid] = rec[tid];
-      sh.z[tid] = rec[D + tid];
-      sh.ah[tid] = rec[2 * D + tid];
-      sh.r[tid] = rec[3 * D + tid];
-      sh.fq[tid] = rec[4 * D + tid];
-      sh.o[tid] = rec[5 * D + tid];
-      sh.kr[tid] = bw_ld(k, tok + tid);
-      sh.u[tid] = bw_ld(u, tok + tid);
-      sh.dout[tid] = bw_ld(dout, tok + tid);
+      sh.kh[tid] = pr[0];
+      sh.z[tid] = pr[1];
+      sh.ah[tid] = pr[2];
+      sh.r[tid] = pr[3];
+      sh.fq[tid] = pr[4];
+      sh.o[tid] = pr[5];
+      sh.kr[tid] = bw_cv(pk);
+      sh.u[tid] = bw_cv(pu);
+      sh.dout[tid] = bw_cv(pdo);
+      qt = bw_cv(pq);
     }
-    if (tid < BW_NS) sh.sc[tid] = rec[6 * D + tid];
+    if (tid < BW_NS) sh.sc[tid] = psc;
+    if (t > 0) load_rev(t - 1);
     __syncthreads();
     if (w == 0) {
       float x = 0.f;
@@ -345,7 +364,7 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
     if (tid < D) {
       const float fqc = sh.fq[tid];
       const float dphiq = col_total(0, tid) + dden * sh.n[tid];
-      dq[tok + tid] = dphiq * dphi(bw_ld(q, tok + tid));
+      dq[tok + tid] = dphiq * dphi(qt);
       sh.dah[tid] = col_total(1, tid);
       const float dnt = sh.dn[tid] + dden * fqc;  // gradient of n after token t
       sh.dn[tid] = dnt;
