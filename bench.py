@@ -73,14 +73,21 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = os.path.join(ROOT, "rls_associative_memory_amd", "csrc")
 
 
+# The sources the forward path's kernels and their launches are built from; a change
+# anywhere else in csrc/ (the backward, decode or linear-attention kernels) leaves the
+# stored counter readings of the forward kernels valid.
+FORWARD_SOURCES = ("vla_api.cpp", "vla_chunk.hip", "vla_seq.hip", "vla_aside_wy.h",
+                   "vla_swy_bf16.h", "vla_mfma.h", "vla_common.h", "vla_internal.h")
+
+
 def kernel_source_hash() -> str:
-    """Digest of the HIP sources; a stored counter reading is used only while it matches."""
+    """Digest of the forward path's HIP sources; a stored counter reading is used only while
+    it matches."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_SOURCES)):
-        if name.endswith((".h", ".hip", ".cpp")):
-            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in FORWARD_SOURCES:
+        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -516,6 +523,7 @@ def backward_bench(args, w):
     tokens = w.B * w.H * w.T
     k_tot, k_n = kernels.get("vla_backward_kernel", (0.0, 1))
     kernel_ms = k_tot / max(k_n, 1)
+    # replay 12 d^2 + reverse 28 d^2 (rank-1 updates and matrix-vector products) per token*head
     flops = (40 * w.d * w.d) * tokens
     achieved = flops / (kernel_ms * 1e-3) / 1e12 if kernel_ms else 0.0
     print(f"[bench] backward {w.name}: {ms:.3f} ms/call (kernel {kernel_ms:.3f} ms)", file=sys.stderr, flush=True)
