@@ -15,6 +15,11 @@ is returned for q, k, v, u and for lambda0 (per stream: each stream's own A_0 = 
 so the total derivative is the sum over streams).  The tests pin it to central finite
 differences of the numpy oracle, an independent implementation of the forward.
 Zero norms (||k|| = 0 or ||A_t khat|| = 0) have no derivative; they are not used here.
+
+``dtype`` is float64 for the oracle.  The same steps evaluated in float32 (``dtype=
+torch.float32``) are not a reference: they measure how far plain fp32 arithmetic of this
+recurrence strays from the fp64 gradients on a given input (some gradients, e.g. du where
+u_t = k_t, are ill-conditioned), which sets the tolerance the fp32 kernels are held to.
 """
 
 from __future__ import annotations
@@ -32,10 +37,10 @@ def _phi(x):
 def vla_forward_torch(q, k, v, u, lam, eps: float = 1e-6):
     """q, k, v, u: [N, T, d] float64 tensors; lam: [N] float64.  Returns out, S_T, A_T, n_T."""
     N, T, d = q.shape
-    eye = torch.eye(d, dtype=torch.float64)
+    eye = torch.eye(d, dtype=q.dtype)
     A = eye.expand(N, d, d) / lam[:, None, None]
-    S = torch.zeros(N, d, d, dtype=torch.float64)
-    n = torch.zeros(N, d, dtype=torch.float64)
+    S = torch.zeros(N, d, d, dtype=q.dtype)
+    n = torch.zeros(N, d, dtype=q.dtype)
     outs = []
     for t in range(T):
         kt, ut, vt, qt = k[:, t], u[:, t], v[:, t], q[:, t]
@@ -54,17 +59,18 @@ def vla_forward_torch(q, k, v, u, lam, eps: float = 1e-6):
     return torch.stack(outs, dim=1), S, A, n
 
 
-def vla_grad(q, k, v, u, lambda0, d_out, dS_T=None, dA_T=None, dn_T=None, eps: float = 1e-6):
+def vla_grad(q, k, v, u, lambda0, d_out, dS_T=None, dA_T=None, dn_T=None, eps: float = 1e-6,
+             dtype=torch.float64):
     """Gradients (dq, dk, dv, du [N, T, d], dlambda0 [N]) of the loss above, as float64 numpy
     arrays; inputs are [N, T, d] arrays (N independent streams)."""
-    tq, tk, tv, tu = (torch.tensor(np.asarray(x, dtype=np.float64), requires_grad=True)
+    tq, tk, tv, tu = (torch.tensor(np.asarray(x, dtype=np.float64), dtype=dtype, requires_grad=True)
                       for x in (q, k, v, u))
     N = tq.shape[0]
-    lam = torch.full((N,), float(lambda0), dtype=torch.float64, requires_grad=True)
+    lam = torch.full((N,), float(lambda0), dtype=dtype, requires_grad=True)
     out, S, A, n = vla_forward_torch(tq, tk, tv, tu, lam, eps=eps)
-    loss = (out * torch.tensor(np.asarray(d_out, dtype=np.float64))).sum()
+    loss = (out * torch.tensor(np.asarray(d_out, dtype=np.float64), dtype=dtype)).sum()
     for state, cot in ((S, dS_T), (A, dA_T), (n, dn_T)):
         if cot is not None:
-            loss = loss + (state * torch.tensor(np.asarray(cot, dtype=np.float64))).sum()
+            loss = loss + (state * torch.tensor(np.asarray(cot, dtype=np.float64), dtype=dtype)).sum()
     loss.backward()
-    return tuple(x.grad.numpy() for x in (tq, tk, tv, tu, lam))
+    return tuple(x.grad.double().numpy() for x in (tq, tk, tv, tu, lam))

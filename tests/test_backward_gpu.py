@@ -67,3 +67,51 @@ def test_backward_edge_lengths(T):
 
 def test_backward_without_state_cotangents_and_long():
     _run(64, "f32", T=300, with_state=False, lam=0.5)
+
+
+@pytest.mark.parametrize("name,sample", [("mqar_t512_d32", (0, 77, 255)), ("iid_t4096_d64", (5,))])
+def test_backward_full_workload_sampled_streams(name, sample):
+    """Every stream of a full-size workload in one call (the launch bench.py times); the
+    gradients of sampled streams against the oracle.  Cotangents are seeded per stream, so a
+    sampled stream's cotangents are regenerated on the host without the others."""
+    from rls_associative_memory_amd.inputs import make_inputs, upload_inputs
+    w = get_workload(name)
+    N, T, d = w.streams, w.T, w.d
+    dt = torch_dtype(w)
+    dev = upload_inputs(w, "cuda")
+
+    def cot(s):
+        r = np.random.default_rng([99, s])
+        return (r.standard_normal((T, d)).astype(np.float32), r.standard_normal((d, d)).astype(np.float32),
+                r.standard_normal((d, d)).astype(np.float32), r.standard_normal(d).astype(np.float32))
+
+    host = [cot(s) for s in range(N)]
+    dout = torch.from_numpy(np.stack([h[0] for h in host])).to(dt).view(w.B, w.H, T, d).cuda()
+    dS = torch.from_numpy(np.stack([h[1] for h in host])).view(w.B, w.H, d, d).cuda()
+    dA = torch.from_numpy(np.stack([h[2] for h in host])).view(w.B, w.H, d, d).cuda()
+    dn = torch.from_numpy(np.stack([h[3] for h in host])).view(w.B, w.H, d).cuda()
+    _say(f"[case] backward full {name}: {N} streams x {T} tokens, sampled {sample}")
+    got = vla.backward(*dev, w.lambda0, dout, dS_T=dS, dA_T=dA, dn_T=dn, eps=w.eps)
+    torch.cuda.synchronize()
+    q, k, v, u = make_inputs(w, streams=sample)
+    douts = dout.float().view(N, T, d)[list(sample)].cpu().numpy().astype(np.float64)
+    idx = list(sample)
+    ref = vla_grad(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), u.astype(np.float64),
+                   w.lambda0, douts, np.stack([host[s][1] for s in idx]).astype(np.float64),
+                   np.stack([host[s][2] for s in idx]).astype(np.float64),
+                   np.stack([host[s][3] for s in idx]).astype(np.float64), eps=w.eps)
+    tol = TOL[w.dtype]
+    names = ("dq", "dk", "dv", "du")
+    errs = {n: rel_l2(g.view(N, T, d)[idx].cpu().numpy(), rf) for n, g, rf in zip(names, got[:4], ref[:4])}
+    errs["dlambda0"] = rel_l2(got[4].view(N)[idx].cpu().numpy(), ref[4])
+    # Where u_t = k_t (the recall layout) du is ill-conditioned: the same steps in plain fp32
+    # stray from the fp64 gradients by about 4e-4.  dq, dk, dv, du are held to the larger of
+    # the bar and four times that fp32 deviation; dlambda0 (closed form) to the bar itself.
+    ref32 = vla_grad(q, k, v, u, w.lambda0, douts, np.stack([host[s][1] for s in idx]),
+                     np.stack([host[s][2] for s in idx]), np.stack([host[s][3] for s in idx]),
+                     eps=w.eps, dtype=torch.float32)
+    bars = {n: max(tol, 4.0 * rel_l2(r32, rf)) for n, r32, rf in zip(names, ref32[:4], ref[:4])}
+    bars["dlambda0"] = tol
+    _say(f"[parity] backward full {name}: " + " ".join(f"{n}={e:.3e} (bar {bars[n]:.1e})" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e < bars[n], f"{n} rel L2 {e:.3e} >= {bars[n]:.3e}"
