@@ -128,6 +128,9 @@ def parse():
                          "backward: gradients of every input (default workload mqar_t512_d32)")
     ap.add_argument("--decode-path", default="decode", choices=["decode", "seq"],
                     help="path of the T = 1 calls in --mode decode")
+    ap.add_argument("--decode-graph", type=int, default=0,
+                    help="decode mode: capture this many (even) T = 1 calls in one HIP graph and "
+                         "time graph replays instead of eager calls (0: eager)")
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="batch B of the decode streams (0: the workload's); B x H streams")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -357,36 +360,65 @@ def decode_bench(args, w):
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    vla.profile_reset()
-    vla.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for t in range(args.warmup, nsteps):
-        step(t)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    vla.profile_enable(False)
-    kernels = vla.profile_read()
-    ev_ms = ev0.elapsed_time(ev1) / args.steps
-    ms = max(wall * 1e3 / args.steps, ev_ms)
+    ng = args.decode_graph
+    if ng > 0:
+        # ng calls (ping-pong state, so the state ends where it started) in one HIP graph; each
+        # replay advances every stream by ng tokens (the same ng input tokens each replay)
+        if ng % 2 or ng > nsteps:
+            raise SystemExit("--decode-graph must be even and at most --warmup + --steps")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for t in range(ng):
+                step(t)
+        reps = max(1, -(-args.steps // ng))
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ncalls = reps * ng
+        ev_ms = ev0.elapsed_time(ev1) / ncalls
+        ms = max(wall * 1e3 / ncalls, ev_ms)
+        kernel_ms = ev_ms  # per call inside the graph, launch gaps included
+        kernels = {}
+    else:
+        vla.profile_reset()
+        vla.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for t in range(args.warmup, nsteps):
+            step(t)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        vla.profile_enable(False)
+        kernels = vla.profile_read()
+        ncalls = args.steps
+        ev_ms = ev0.elapsed_time(ev1) / args.steps
+        ms = max(wall * 1e3 / args.steps, ev_ms)
     streams = w.B * w.H
     kname = "vla_decode_kernel" if args.decode_path == "decode" else "vla_seq_kernel"
-    k_total, k_n = kernels.get(kname, (0.0, 1))
-    kernel_ms = k_total / max(k_n, 1)
+    if ng <= 0:
+        k_total, k_n = kernels.get(kname, (0.0, 1))
+        kernel_ms = k_total / max(k_n, 1)
     # per stream and call: S, A read and written (fp32 d x d each), n read and written,
     # q, k, v, u read and o written in the input dtype
     state_bytes = streams * (4 * w.d * w.d * 4 + 2 * w.d * 4 + 5 * w.d * w.elem_bytes)
     gbs = state_bytes / (kernel_ms * 1e-3) / 1e9 if kernel_ms > 0 else 0.0
-    print(f"[bench] decode: {args.steps} calls of T = 1 over {streams} streams: {ms * 1e3:.1f} us/call "
+    print(f"[bench] decode{' (HIP graph of %d calls)' % ng if ng > 0 else ''}: "
+          f"{ncalls} calls of T = 1 over {streams} streams: {ms * 1e3:.1f} us/call "
           f"(events {ev_ms * 1e3:.1f} us, kernel {kernel_ms * 1e3:.1f} us)", file=sys.stderr, flush=True)
     line = {
         "metric": "VLA decode (T = 1 calls, state carried) tokens·heads/sec at 1 MI355X",
         "value": streams / (ms * 1e-3),
         "unit": "tokens*heads/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": ncalls,
         "warmup": args.warmup,
         "ms_per_step": ms,
         "higher_is_better": True,
@@ -396,7 +428,7 @@ def decode_bench(args, w):
         "data": "synthetic",
         "config": {"workload": w.name + "_decode", "B": w.B, "H": w.H, "T": 1, "d": w.d,
                    "input_dtype": w.dtype, "state_dtype": "f32", "lambda0": w.lambda0,
-                   "path": args.decode_path},
+                   "path": args.decode_path, "hip_graph_calls": ng if ng > 0 else None},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "kernel": kname, "kernel_ms": round(kernel_ms, 5)},

@@ -220,3 +220,59 @@ def test_decode_kernel_many_streams_sampled():
     got = (_np(out).reshape(streams, 1, d)[pick], _np(S).reshape(streams, d, d)[pick],
            _np(A).reshape(streams, d, d)[pick], _np(n).reshape(streams, d)[pick])
     _compare(f"decode {streams} streams (16 sampled)", TOL["bf16"], got, ref)
+
+
+def test_decode_graph_replays_match_eager():
+    """A block of T = 1 decode calls captured in one HIP graph (the library enqueues only
+    kernels on the caller's stream, no allocation or memset), replayed three times with eager
+    work and synchronisations in between; every replay must equal the eager calls bitwise."""
+    d, nst = 96, 6
+    w = get_workload("tiny_t256_d32").resized(name="decode_graph", B=2, H=4, T=nst, d=d, dtype="bf16",
+                                              lambda0=0.5)
+    q, k, v, u = make_inputs(w)
+    full = [_dev(x, w, (2, 4, nst, d)) for x in (q, k, v, u)]
+    steps = [[x[:, :, t:t + 1].contiguous() for x in full] for t in range(nst)]
+    mat = (2, 4, d, d)
+    # a carried start state from a 50-token forward (so A0 and S0 are not trivial)
+    pre = get_workload("tiny_t256_d32").resized(name="decode_graph_pre", B=2, H=4, T=50, d=d, dtype="bf16",
+                                                lambda0=0.5)
+    pq = [_dev(x, pre, (2, 4, 50, d)) for x in make_inputs(pre)]
+    _, S_init, A_init, n_init = vla.forward_state(*pq, pre.lambda0, eps=pre.eps, path="seq")
+    st = [(torch.empty(mat, device="cuda"), torch.empty(mat, device="cuda"),
+           torch.empty((2, 4, d), device="cuda")) for _ in range(2)]
+    outs = [torch.empty_like(steps[0][0]) for _ in range(nst)]
+
+    def reset():
+        for dst, src in zip(st[0], (S_init, A_init, n_init)):
+            dst.copy_(src)
+
+    def run():
+        for t in range(nst):
+            S0, A0, n0 = st[t & 1]
+            S1, A1, n1 = st[(t & 1) ^ 1]
+            vla.forward_state(*steps[t], w.lambda0, S0=S0, A0=A0, n0=n0, eps=w.eps, path="decode",
+                              out=outs[t], S_final=S1, A_final=A1, n_final=n1)
+
+    _say("[case] decode graph: 6 T = 1 calls, 8 streams, d = 96, bf16; eager reference")
+    reset()
+    run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs] + [x.clone() for x in st[0]]
+    g = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = outs + list(st[0])
+        same = all(torch.equal(a, b) for a, b in zip(got, ref))
+        _say(f"[parity] decode graph replay {rep}: bitwise equal to eager: {same}")
+        assert same, f"replay {rep} differs from the eager calls"
+        _ = (torch.ones(1024, device="cuda") * 2.0).sum().item()  # eager work between replays
