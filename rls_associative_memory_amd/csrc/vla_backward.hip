@@ -45,12 +45,7 @@ struct BwCfg {
 };
 
 // Sum over each 16-lane row (DPP, no LDS round trip); every lane of the row gets the sum.
-__device__ __forceinline__ float bw_sum16(float x) {
-  x += dpp_xor1(x);
-  x += dpp_xor2(x);
-  x += dpp_half_mirror(x);
-  return x + dpp_mirror(x);
-}
+__device__ __forceinline__ float bw_sum16(float x) { return row_sum16(x); }
 __device__ __forceinline__ float bw_wave_sum(float x) { return wave_sum(x); }
 __device__ __forceinline__ float bw_cv(float x) { return x; }
 __device__ __forceinline__ float bw_cv(bf16_t x) { return bf16_to_f32(x.bits); }

@@ -71,15 +71,23 @@ __device__ __forceinline__ float dpp_mirror(float x) {  // lane i <-> 15 - i wit
 
 __device__ __forceinline__ float pair_sum(float x) { return x + dpp_xor1(x); }
 
-// Sum over all 64 lanes of the wave.
-__device__ __forceinline__ float wave_sum(float x) {
+// Sum over each 16-lane row; every lane of the row ends with bitwise the same sum.
+__device__ __forceinline__ float row_sum16(float x) {
   x = x + dpp_xor1(x);
   x = x + dpp_xor2(x);
   x = x + dpp_half_mirror(x);
-  x = x + dpp_mirror(x);
-  x = x + __shfl_xor(x, 16);
-  x = x + __shfl_xor(x, 32);
-  return x;
+  return x + dpp_mirror(x);
+}
+
+// Sum over all 64 lanes of the wave (the whole wave must be active), broadcast to every lane.
+// After the row sums, rows 1 and 3 add the last lane of rows 0 and 2 (DPP row_bcast:15), row 3
+// then adds lane 31 (row_bcast:31), and lane 63's total is read out: all on the VALU, no LDS
+// permute, in a fixed order ((r2 + r3) + (r0 + r1)).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum16(x);
+  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+  x = x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 }  // namespace vla

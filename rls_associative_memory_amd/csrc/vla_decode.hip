@@ -7,7 +7,7 @@
 // element once: thread (i, p) = (tid / 16, tid % 16) owns rows i + 32 a (a < d / 32) and, in
 // each, the column pairs 2 p + 32 b, 2 p + 32 b + 1 (b < d / 32), so that the 16 threads of a
 // row read and write 128 contiguous bytes per instruction and a row's sums are 16-lane
-// shuffles.
+// DPP sums.
 // Per stream (VLA summary §2.3 steps 1-3 and the ratio readout, for one token):
 //   z = A u,  g = A k,  delta = 1 + u.z,  A'[r][c] = A[r][c] - z_r z_c / delta
 //   y = A' khat = (g - z (z.k) / delta) / ||k||,  ahat = y / ||y||
@@ -15,7 +15,7 @@
 //   n' = n + phi(k),  o_r = S'[r][:] . phi(q) / (n'.phi(q) + eps)
 // A carried A0 is used as (A0 + A0^T) / 2: the transposed element comes from a copy of A0
 // in LDS.  Both halves of a pair add the same two numbers, and every lane holds bitwise the
-// same z (butterfly sums), so A' is exactly symmetric.
+// same z (symmetric DPP sums), so A' is exactly symmetric.
 
 #include "vla_common.h"
 #include "vla_internal.h"
@@ -39,16 +39,9 @@ __device__ __forceinline__ void st_out<bf16_t>(bf16_t *p, int64_t i, float x) {
   p[i].bits = f32_to_bf16(x);
 }
 
-__device__ __forceinline__ float dec_wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ float dec_sum16(float x) {  // over the 16 lanes of an aligned group
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
+__device__ __forceinline__ float dec_wave_sum(float x) { return wave_sum(x); }
+// over the 16 lanes of an aligned group (DPP; every lane of the group gets the same bits)
+__device__ __forceinline__ float dec_sum16(float x) { return row_sum16(x); }
 
 template <int D, typename TIn>
 __global__ void __launch_bounds__(512)
