@@ -280,20 +280,32 @@ k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0
                         : (e / D) == (e % D) ? static_cast<double>(lambda0) : 0.0;
     float *base = M + s * P * D * D + e;
     double acc = 0.0;
-    for (int64_t p = 0; p < P; ++p) {
-      const float g = (p + 1 < P) ? base[p * D * D] : 0.f;
-      base[p * D * D] = static_cast<float>(acc + init);
-      acc += g;
+    // 16 segments' Grams are loaded before any of them is replaced by its prefix, so the
+    // scan waits for one memory latency per 16 segments rather than one per segment.
+    for (int64_t p0 = 0; p0 < P; p0 += 16) {
+      float g[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) g[i] = (p0 + i + 1 < P) ? base[(p0 + i) * D * D] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (p0 + i < P) base[(p0 + i) * D * D] = static_cast<float>(acc + init);
+        acc += g[i];
+      }
     }
   }
   if (blockIdx.y == 0 && threadIdx.x < D) {
     const double init = n0 != nullptr ? static_cast<double>(n0[s * D + threadIdx.x]) : 0.0;
     float *base = nk + s * P * D + threadIdx.x;
     double acc = 0.0;
-    for (int64_t p = 0; p < P; ++p) {
-      const float g = (p + 1 < P) ? base[p * D] : 0.f;
-      base[p * D] = static_cast<float>(acc + init);
-      acc += g;
+    for (int64_t p0 = 0; p0 < P; p0 += 16) {
+      float g[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) g[i] = (p0 + i + 1 < P) ? base[(p0 + i) * D] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (p0 + i < P) base[(p0 + i) * D] = static_cast<float>(acc + init);
+        acc += g[i];
+      }
     }
   }
 }
@@ -1046,7 +1058,7 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
 // row of S_p, so each workgroup scans one 16-row tile of one stream: grid (streams, D/16).
 // Wave w owns output columns 16w..16w+15 (S^T in MFMA accumulators: X[r] = S[row li]
 // [16w + 4gq + r]) and reads its 96 x 16 column slice of Pi_p straight from memory in the
-// A-operand layout, one segment ahead.  The row tile of S_p is exchanged between the waves
+// A-operand layout, four (two at d = 128) segments ahead.  The row tile of S_p is exchanged between the waves
 // through a double-buffered LDS copy (one barrier per segment).
 // ------------------------------------------------------------------------------------
 template <int D>
@@ -1065,28 +1077,37 @@ k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P,
                                    : make_float4(0.f, 0.f, 0.f, 0.f);
   *reinterpret_cast<float4 *>(&s0[(s * P) * D * D + row * D + col]) = st0;
   *reinterpret_cast<float4 *>(&Xs[0][4 * w + gq][li][0]) = st0;
-  // a[kt][e] = Pi[16 kt + 4 gq + e][16 w + li];  b = B[row][col .. col + 3]
-  float a[NFT][4];
-  float4 b;
-  auto load = [&](int64_t pseg) {
+  // a[slot][kt][e] = Pi[16 kt + 4 gq + e][16 w + li];  b[slot] = B[row][col .. col + 3].
+  // Segment p's map lives in slot p % NSL and is loaded NSL segments ahead, so a step waits for
+  // memory only when a load takes longer than NSL steps.
+  constexpr int NSL = (D <= 96) ? 4 : 2;  // register budget at d = 128
+  float a[NSL][NFT][4];
+  float4 b[NSL];
+  auto load = [&](int64_t pseg, int slot) {
     const float *Pi = pib + (s * P + pseg) * 2 * D * D;
 #pragma unroll
     for (int kt = 0; kt < NFT; ++kt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[kt][e] = Pi[(16 * kt + 4 * gq + e) * D + 16 * w + li];
-    b = *reinterpret_cast<const float4 *>(&Pi[D * D + row * D + col]);
+      for (int e = 0; e < 4; ++e) a[slot][kt][e] = Pi[(16 * kt + 4 * gq + e) * D + 16 * w + li];
+    b[slot] = *reinterpret_cast<const float4 *>(&Pi[D * D + row * D + col]);
   };
-  if (P > 1) load(0);
-  for (int64_t p = 0; p + 1 < P; ++p) {
+#pragma unroll
+  for (int i = 0; i < NSL; ++i)
+    if (i + 1 < P) load(i, i);
+  for (int64_t p0 = 0; p0 + 1 < P; p0 += NSL)
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    const int64_t p = p0 + i;
+    if (p + 1 >= P) break;
     const int cur = static_cast<int>(p & 1);
     float ac[NFT][4];
 #pragma unroll
     for (int kt = 0; kt < NFT; ++kt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ac[kt][e] = a[kt][e];
-    f4_t y[4] = {f4_t{b.x, b.y, b.z, b.w}, f4_zero(), f4_zero(), f4_zero()};
+      for (int e = 0; e < 4; ++e) ac[kt][e] = a[i][kt][e];
+    f4_t y[4] = {f4_t{b[i].x, b[i].y, b[i].z, b[i].w}, f4_zero(), f4_zero(), f4_zero()};
     __syncthreads();
-    if (p + 2 < P) load(p + 1);
+    if (p + NSL + 1 < P) load(p + NSL, i);
     // Y^T[f][row] = B^T[f][row] + sum_f' Pi[f'][f] S^T[f'][row], four independent chains
 #pragma unroll
     for (int kt = 0; kt < NFT; ++kt) {
