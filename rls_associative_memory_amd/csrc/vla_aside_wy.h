@@ -49,7 +49,7 @@ struct AwyLds {
   float lw[4][16][20] __attribute__((aligned(16)));  // blocked LDL^T scratch
   float nbuf[2][D] __attribute__((aligned(16)));  // sum of phi(k) before the chunk
   float dtmp[2][16];
-  float norm[C::NW][C::C];
+  float norm[C::NW][C::C][4] __attribute__((aligned(16)));  // partial ||Y_c||^2 per wave and lane group
 };
 
 template <int D>
@@ -478,9 +478,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       float part = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) part = fmaf(Yt[ct][r], Yt[ct][r], part);
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (gq == 0) sh.norm[w][16 * ct + li] = part;
+      sh.norm[w][16 * ct + li][gq] = part;  // the four lane groups are summed by the readers
     }
     __syncthreads();
 #pragma unroll
@@ -488,7 +486,10 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       const int c = 16 * ct + li;
       float tot = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) tot += sh.norm[w2][c];
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const f4_t pn = *reinterpret_cast<const f4_t *>(&sh.norm[w2][c][0]);
+        tot += (pn[0] + pn[1]) + (pn[2] + pn[3]);
+      }
       const float inv = tot > 0.f ? rsqrtf(tot) : 0.f;
       if (c < m)
         *reinterpret_cast<float4 *>(&al[c0 * D + static_cast<uint32_t>(c * D + 16 * w + 4 * gq)]) =
