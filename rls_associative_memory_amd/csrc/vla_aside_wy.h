@@ -91,13 +91,17 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   // Staging: thread tid loads token tid / (D/8), features (tid % (D/8)) * 8 of u, k, q.
   // Rows past the segment are read as row 0 and zeroed when staged (no select on a load
   // result, which would make the load wait at once); offsets are 32-bit from uniform bases.
+  // Every chunk prefetches and stages a next chunk (past the segment's end: its first row,
+  // staged as zeros and never read), so no load is left pending across the loop's back edge
+  // and the loop head does not wait for the previous chunk's stores.
   uint4 pv[3];
   auto prefetch = [&](int64_t cs, int tid) {
     const int sc = tid / (D / 8), sf0 = (tid % (D / 8)) * 8;
     const uint32_t off = (cs + sc < te) ? static_cast<uint32_t>(sc * D + sf0) : 0u;
-    pv[0] = *reinterpret_cast<const uint4 *>(us + cs * D + off);
-    pv[1] = *reinterpret_cast<const uint4 *>(ks + cs * D + off);
-    pv[2] = *reinterpret_cast<const uint4 *>(qs + cs * D + off);
+    const int64_t cb = (cs < te) ? cs : tb;  // a row of this segment
+    pv[0] = *reinterpret_cast<const uint4 *>(us + cb * D + off);
+    pv[1] = *reinterpret_cast<const uint4 *>(ks + cb * D + off);
+    pv[2] = *reinterpret_cast<const uint4 *>(qs + cb * D + off);
   };
   // Rows of the chunk at cs, staged into LDS; rows past the segment become zeros.
   auto stage = [&](int64_t cs, int tid) {
@@ -138,7 +142,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // previous chunk) are visible.  The next chunk's rows are loaded now and staged once
     // this chunk has read its own (after X~).
     __syncthreads();
-    if (c0 + CH < te) prefetch(c0 + CH, tid);
+    prefetch(c0 + CH, tid);
 
     // ---- [Z0^T | P^T] = A [U^T | K^T] (rows 16w.., 32 tokens) ---------------------------
     f4_t Z0t[2], Pt[2];
@@ -451,7 +455,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
     __syncthreads();
     // the next chunk's rows (sU, sK, sQ are not read again in this chunk)
-    if (c0 + CH < te) stage(c0 + CH, tid);
+    stage(c0 + CH, tid);
     // ---- W = D^{-1/2} Z into the first buffer (Z0 is no longer read) ----------------------
     {
       f4_t Ws[2];
