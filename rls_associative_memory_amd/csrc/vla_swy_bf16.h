@@ -215,6 +215,17 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       sh.rk[tid] = tid < m ? prk : 0.f;
       if constexpr (FINAL) sh.rden[tid] = tid < m ? 1.0f / pden : 0.f;
     }
+    // Every prefetched register counts as used here, in every thread (lanes that stage nothing
+    // included), so no load is still pending when the next prefetch reuses the registers: the
+    // compiler then need not wait for the stores issued since.
+    asm volatile("" ::"v"(prk), "v"(pden));
+#pragma unroll
+    for (int i = 0; i < PK; ++i) {
+      asm volatile("" ::"v"(pk[i].x), "v"(pv[i].x));
+      if constexpr (FINAL) asm volatile("" ::"v"(pq[i].x));
+    }
+#pragma unroll
+    for (int i = 0; i < PA; ++i) asm volatile("" ::"v"(pa[i][0].x), "v"(pa[i][1].x));
     __syncthreads();
     // ---- shared tile products: Ka_tt (each with the inverse of I + Ka_tt), Ka_ba and, in
     //      the final pass, Qa_tt and Qa_ba --------------------------------------------------
