@@ -30,6 +30,7 @@
 // chunk products of the WY form and the segment-map composition.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "vla_common.h"
 #include "vla_internal.h"
@@ -579,20 +580,19 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
 #pragma unroll
   for (int i = 0; i < C::RING; ++i) fetch(tb + i, ring[i]);
 
-  for (int64_t t = tb; t < te; ++t) {
-    const int j = static_cast<int>(t - tb);
-    const int slot = j & 1;
+  // Token step; RS is the token's ring slot (t - tb) % RING, a compile-time constant so that
+  // the compiler knows which loads each step waits for (a slot chosen at run time made every
+  // step wait for all outstanding memory operations, the previous steps' stores included).
+  static_assert(C::RING == 4, "the token loop below is unrolled by four");
+  auto step = [&](const int64_t t, auto rslot) {
+    constexpr int RS = decltype(rslot)::value;
+    const int slot = RS & 1;
     float *U = sU[unit_in_blk][slot];
     float *K = sK[unit_in_blk][slot];
     float *Q = sQ[unit_in_blk][slot];
     // (a) token t from the ring into LDS (fp32; phi applied to q).
     {
-      vec_t cur[PV];
-#pragma unroll
-      for (int r = 0; r < C::RING; ++r)
-        if ((j % C::RING) == r)
-#pragma unroll
-          for (int i = 0; i < PV; ++i) cur[i] = ring[r][i];
+      const vec_t *cur = ring[RS];
 #pragma unroll
       for (int i = 0; i < PV; ++i) {
         const int vi = lu + i * C::LA;
@@ -610,13 +610,7 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
         }
       }
       // (b) refill this ring slot with token t + RING.
-      vec_t nxt[PV];
-      fetch(t + C::RING, nxt);
-#pragma unroll
-      for (int r = 0; r < C::RING; ++r)
-        if ((j % C::RING) == r)
-#pragma unroll
-          for (int i = 0; i < PV; ++i) ring[r][i] = nxt[i];
+      fetch(t + C::RING, ring[RS]);
     }
     unit_sync<C::NWA>();
     // (c) readout normaliser n_t = n_{t-1} + phi(k_t); partial of n_t . phi(q_t).
@@ -722,7 +716,17 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
       }
     }
     if constexpr (C::NWA > 1) __syncthreads();  // W and the LDS slots are rewritten next
+  };
+  int64_t t = tb;
+  for (; t + C::RING <= te; t += C::RING) {
+    step(t, std::integral_constant<int, 0>{});
+    step(t + 1, std::integral_constant<int, 1>{});
+    step(t + 2, std::integral_constant<int, 2>{});
+    step(t + 3, std::integral_constant<int, 3>{});
   }
+  if (t < te) step(t, std::integral_constant<int, 0>{});
+  if (t + 1 < te) step(t + 1, std::integral_constant<int, 1>{});
+  if (t + 2 < te) step(t + 2, std::integral_constant<int, 2>{});
   if (A_final != nullptr && p == P - 1) {
     float *dst = A_final + s * D * D;
 #pragma unroll
