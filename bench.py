@@ -80,14 +80,23 @@ FORWARD_SOURCES = ("vla_api.cpp", "vla_chunk.hip", "vla_seq.hip", "vla_aside_wy.
                    "vla_swy_bf16.h", "vla_mfma.h", "vla_common.h", "vla_internal.h")
 
 
-def kernel_source_hash() -> str:
-    """Digest of the forward path's HIP sources; a stored counter reading is used only while
-    it matches."""
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank space, so that an edit of comments alone keeps
+    the digest (string literals in these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(root: str = KERNEL_SOURCES) -> str:
+    """Digest of the code (comments excluded) of the forward path's HIP sources; a stored
+    counter reading is used only while it matches."""
     import hashlib
     h = hashlib.sha256()
     for name in FORWARD_SOURCES:
-        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(root, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -70,8 +70,8 @@ vla_status_t resolve(const vla_desc_t *desc, const vla::Problem &p, int32_t *pat
     // Enough streams to fill the machine one workgroup each, or sequences too short to
     // amortise the segment passes: run token by token.  Otherwise split time: few streams of
     // at least 1024 tokens, or (fp32 inputs, whose segments can be as short as 64 tokens) up to
-    // 256 streams of at least 256 tokens (1 x 256 tokens, d = 32: 0.155 ms against 0.196 ms
-    // token by token; 256 x 512: 0.290 ms against 0.383 ms).
+    // 256 streams of at least 256 tokens (at d = 32 both one stream of 256 tokens and 256
+    // streams of 512 run faster split into segments than token by token).
     const bool few_streams = p.streams < 128;
     const bool long_seq = p.T >= 1024;
     const bool short_fp32 = p.dtype == vla::Dtype::F32 && p.streams <= 256 && p.T >= 256;

@@ -63,7 +63,8 @@ static ChunkPlan make_plan(const Problem &p, int C) {
   // bf16 inputs, whose A side runs two six-wave workgroups per CU (more, shorter segments only
   // add rounds and segment passes); at least 64 for fp32 inputs, whose A side is one wave per
   // segment with every segment resident at once, so shorter segments shorten the chain
-  // (256 streams x 512 tokens, d = 32: 0.459 ms at 256 tokens, 0.290 ms at 64).
+  // (on 256 streams of 512 tokens at d = 32, 64-token segments take about 40 % less time than
+  // 256-token ones).
   const int64_t target = (p.streams * p.T + 2047) / 2048;
   int64_t L = (p.dtype == Dtype::F32) ? 64 : 256;
   while (L < target && L < 8192) L *= 2;
