@@ -210,3 +210,21 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 4, 32)
     with pytest.raises(ValueError):
         vla.forward(x, x, x, x, 1.0)
+
+
+@pytest.mark.parametrize("shape,dtype,want", [
+    ((1, 1, 256, 32), 0, "chunk"),        # one fp32 stream of 256 tokens: 64-token segments
+    ((64, 4, 512, 32), 0, "chunk"),       # 256 fp32 streams of 512 tokens (the recall workload)
+    ((8, 8, 4096, 64), 1, "chunk"),       # few streams, long sequences
+    ((2, 16, 43008, 128), 1, "chunk"),
+    ((1, 32, 131072, 96), 1, "chunk"),
+    ((64, 8, 512, 32), 0, "seq"),         # 512 fp32 streams fill the machine token by token
+    ((64, 4, 512, 32), 1, "seq"),         # bf16 segments are at least 256 tokens
+    ((64, 4, 128, 32), 0, "seq"),         # too short to split
+    ((8, 4, 1, 96), 1, "decode"),
+])
+def test_auto_path_choice(lib, shape, dtype, want):
+    B, H, T, d = shape
+    p = ctypes.c_int32(-1)
+    assert lib.vla_resolve_path(ctypes.byref(desc(B=B, H=H, T=T, d=d, dtype=dtype)), ctypes.byref(p)) == 0
+    assert p.value == vla.PATHS[want], (shape, dtype, p.value)
