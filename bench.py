@@ -8,12 +8,17 @@ resident in HBM.  The timed region is K steps between device synchronisations; t
 printed on stdout is a single JSON object:
 
   value        tokens*heads per second = B*H*T / seconds per step
-  roofline     the dominant kernel's algorithmic FLOP rate (12 d^2 + 20 d flops per
-               token*head, the plain count of the recurrence) over the published MI355X
-               peak of the unit it runs on, timed with HIP events on the launch stream
+  roofline     the whole call's algorithmic FLOP rate (12 d^2 + 20 d flops per token*head,
+               the plain count of the recurrence) over the published MI355X FP32 peak, the
+               whole call's HBM traffic from the committed rocprofv3 counters beside its
+               algorithmic bytes, and the dominant kernel's own rate (its flops per
+               token*head over its mean launch time, HIP events on the launch stream)
+  precision    how the path's arithmetic is carried out (fp32 state; on bf16 inputs the
+               matrix-core operands are two-term bf16 splits)
   cpu_baseline the fp64 oracle timed on the host's cores on a bounded sample of the same
-               workload (the first ``--cpu-tokens`` tokens of ``cores`` streams), whose
-               outputs also give a causal parity check of the GPU run's first tokens
+               workload (the first ``--cpu-tokens`` tokens of ``cores`` streams, one process
+               per CPU of the affinity mask), whose outputs also give a causal parity check
+               of the GPU run's first tokens
 
 Workloads are seeded synthetic inputs (rls_associative_memory_amd.inputs).
 
@@ -128,7 +133,9 @@ def parse():
     ap.add_argument("--chunk", type=int, default=-1, help="chunk length (-1: the workload's)")
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens per stream in the oracle sample (0 disables the CPU leg)")
-    ap.add_argument("--cpu-cores", type=int, default=16)
+    ap.add_argument("--cpu-cores", type=int, default=0,
+                    help="oracle processes (0: every CPU this process may run on, capped by the "
+                         "host's per-GPU CPU share in OMP_NUM_THREADS when that is set)")
     ap.add_argument("--mode", default="forward",
                     choices=["forward", "decode", "compare", "ablation", "backward"],
                     help="forward: whole sequences (default); decode: T = 1 calls, state carried; "
@@ -161,10 +168,27 @@ def _oracle_job(args):
     return stream, time.perf_counter() - t0, out
 
 
+def host_cpus():
+    """(processes to use, CPUs this process may run on, os.cpu_count()).  The pool takes every
+    CPU of the affinity mask, capped by the per-GPU CPU share that OMP_NUM_THREADS names on a
+    shared GPU host."""
+    nproc = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = nproc
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    use = min(affinity, share) if share > 0 else affinity
+    return max(1, use), affinity, nproc
+
+
 def cpu_baseline(w, tokens: int, cores: int):
     """The oracle on the first ``tokens`` tokens of ``cores`` streams, one process per
     stream (single-threaded BLAS in each).  Returns the report and the outputs."""
     import multiprocessing as mp
+    use, affinity, nproc = host_cpus()
+    if cores <= 0:
+        cores = use
     tokens = min(tokens, w.T)
     streams = list(range(min(cores, w.streams)))
     env_before = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
@@ -188,10 +212,13 @@ def cpu_baseline(w, tokens: int, cores: int):
         "value": value,
         "unit": "tokens*heads/s",
         "cores": len(streams),
+        "nproc": nproc,
+        "affinity_cpus": affinity,
         "kind": "oracle",
         "sample": (f"{w.name}: first {tokens} tokens of streams 0..{len(streams) - 1}, one "
-                   f"single-threaded fp64 numpy process per stream; {work:.1f} s of CPU work, "
-                   f"{wall:.1f} s wall including process start-up"),
+                   f"single-threaded fp64 numpy process per stream on {len(streams)} of the "
+                   f"host's {nproc} CPUs ({affinity} in this process's affinity mask); "
+                   f"{work:.1f} s of CPU work, {wall:.1f} s wall including process start-up"),
     }
     return rep, {r[0]: r[2] for r in res}, tokens
 
@@ -305,20 +332,49 @@ def main():
     work_fn, unit = KERNEL_WORK.get(dom_name, (lambda d: 0, "alu"))
     achieved = work_fn(w.d) * tokens / (kernel_ms * 1e-3) / 1e12
     path_tflops = flops_per_token_head(w.d) * tokens / (ms * 1e-3) / 1e12
+    alg_bytes = bytes_per_token_head(w.d, w.elem_bytes) * tokens
+    if w.want_state:
+        alg_bytes += 2 * w.B * w.H * w.d * w.d * 4  # S_T and A_T written
+    call_traffic = None
+    if path == "chunk":
+        per = [stored_traffic(w.name, name) for name in kernels]
+        if per and all(x is not None for x in per):
+            call_traffic = sum(per)
+    path_bound = "mfma" if path == "chunk" else "alu"
     roofline = {
-        "bound": unit,
-        "achieved": round(achieved, 3),
+        # The whole vla_forward call: F(d) = 12 d^2 + 20 d algorithmic flops per token*head
+        # over the step time, against the MI355X FP32 peak (the arithmetic is fp32; on the
+        # chunked path it runs on the matrix cores as two-term bf16 products).
+        "bound": path_bound,
+        "achieved": round(path_tflops, 3),
         "peak": PEAK_FP32_TFLOPS,
         "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
-        "traffic": stored_traffic(w.name, dom_name),
-        "kernel": dom_name,
-        "kernel_ms": round(kernel_ms, 4),
-        "path_achieved": round(path_tflops, 3),
-        "path_frac": round(path_tflops / PEAK_FP32_TFLOPS, 4),
-        "path_hbm_frac": round(bytes_per_token_head(w.d, w.elem_bytes) * tokens / (ms * 1e-3)
-                               / 1e9 / PEAK_HBM_GBS, 4),
+        "frac": round(path_tflops / PEAK_FP32_TFLOPS, 4),
+        "traffic": call_traffic,
+        "scope": "whole vla_forward call (every kernel of the path), F(d) = 12 d^2 + 20 d flops per token*head",
+        "target_frac": 0.5,
+        "algorithmic_bytes": alg_bytes,
+        "traffic_over_algorithmic": round(call_traffic / alg_bytes, 3) if call_traffic else None,
+        "hbm_frac": round(alg_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "dominant_kernel": {
+            "name": dom_name,
+            "bound": unit,
+            "ms": round(kernel_ms, 4),
+            "timing": "HIP events on the launch stream around each launch, mean over the timed steps",
+            "flops_per_token_head": work_fn(w.d),
+            "achieved": round(achieved, 3),
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+            "traffic": stored_traffic(w.name, dom_name),
+        },
     }
+    precision = ("fp32 inputs: fp32 arithmetic throughout" if w.dtype == "f32" else
+                 "bf16 inputs (exact in bf16); fp32 state and accumulation; every fp32 operand of a "
+                 "matrix-core product split into two bf16 terms (hi + lo, about 16 significant "
+                 "bits), the lo x lo term dropped; out rounded once to bf16")
+    if path == "seq":
+        precision = "fp32 state and arithmetic on the vector ALUs; out rounded once to the input dtype"
 
     cpu = None
     if args.cpu_tokens > 0:
@@ -343,6 +399,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "precision": precision,
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d,

@@ -40,8 +40,9 @@ typedef enum {
   VLA_SUCCESS = 0,
   VLA_ERROR_INVALID_VALUE = 1, /* NULL required pointer, size < 1, lambda0 <= 0 or not
                                   finite, eps < 0 or not finite, unknown dtype, path or
-                                  gain,
-                                  workspace smaller than vla_workspace_size()          */
+                                  gain, workspace smaller than vla_workspace_size(), an
+                                  output overlapping an input, another output or the
+                                  workspace                                             */
   VLA_ERROR_NOT_SUPPORTED = 2, /* d not in {32, 64, 96, 128}; a pointer not 16-byte
                                   aligned; a forced path, chunk or gain the shape
                                   cannot use                                            */
@@ -92,13 +93,18 @@ typedef struct {
  * stream      HIP stream (NULL = null stream); the call is asynchronous.
  *
  * Ownership: the caller owns every buffer; the library keeps no pointer after the call
- * returns.  Workspace: the chunked path needs vla_workspace_size() bytes of device
- * scratch.  If desc->workspace is NULL the library uses a per-device cache it grows on
- * demand (that call may allocate, so time steady-state calls or pass a workspace).
- * Calls that share a workspace (or the cache) on one device must be ordered on one
- * stream.  Errors: a status code is returned and nothing is enqueued on an argument
- * error; the call never aborts or throws.  Kernel faults surface at the caller's next
- * synchronisation.  NaN and Inf in the inputs propagate and are not checked.
+ * returns.  Outputs (out, S_final, A_final) must overlap neither one another nor any input,
+ * and a caller's workspace must overlap none of them: an overlap returns
+ * VLA_ERROR_INVALID_VALUE before any device work.  Workspace: the chunked path needs
+ * vla_workspace_size() bytes of device scratch.  If desc->workspace is NULL the library uses
+ * a cache of its own, one buffer per (device, stream), grown on demand: that call may
+ * allocate, and a growing call first waits for the earlier work of its stream (so time
+ * steady-state calls, or pass a workspace).  On a stream under graph capture a cache that
+ * would have to grow gives VLA_ERROR_NOT_SUPPORTED: capture with a workspace.  Calls that
+ * share a caller's workspace must be ordered on one stream.  Errors: a status code is
+ * returned and nothing is enqueued on an argument error; the call never aborts or throws.
+ * Kernel faults surface at the caller's next synchronisation.  NaN and Inf in the inputs
+ * propagate and are not checked.
  */
 vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
                          float lambda0, void *out, float *S_final, float *A_final,
@@ -121,8 +127,8 @@ vla_status_t vla_forward(const void *q, const void *k, const void *v, const void
  * S_final, A_final   as in vla_forward.
  * n_final     device pointer to [B, H, d] fp32 receiving n_T, or NULL.
  *             S_final, A_final and n_final must not overlap S0, A0 or n0 (no in-place
- *             update: feed a decode loop from two sets of state buffers in turn); an
- *             overlap returns VLA_ERROR_INVALID_VALUE.
+ *             update: feed a decode loop from two sets of state buffers in turn), nor one
+ *             another, out or q, k, v, u; an overlap returns VLA_ERROR_INVALID_VALUE.
  * The other arguments, ownership, workspace and error behaviour are those of vla_forward
  * (state pointers must be 16-byte aligned, else VLA_ERROR_NOT_SUPPORTED).  Splitting a
  * sequence into two calls, the second starting from the first's (S_final, A_final,
@@ -144,8 +150,9 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
  *   o_t = S_t phi(q_t) / (n_t^T phi(q_t) + eps)
  *
  * q, k, v     device pointers, [B, H, T, d] in desc->dtype, read only, 16-byte aligned.
- * out         device pointer, [B, H, T, d] in desc->dtype, fully overwritten; must not
- *             alias any input.
+ * out         device pointer, [B, H, T, d] in desc->dtype, fully overwritten; out, S_final,
+ *             n_final and a caller's workspace overlap neither one another nor q, k, v, else
+ *             VLA_ERROR_INVALID_VALUE.
  * S_final     device pointer to [B, H, d, d] fp32 (S[i][j], i = value, j = key) receiving
  *             S_T, or NULL.
  * n_final     device pointer to [B, H, d] fp32 receiving n_T, or NULL.
@@ -182,8 +189,9 @@ vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes);
  *             every 32nd token), else the per-device cache is used as for vla_forward.
  * Runs one workgroup per stream, token by token (a replay of the forward, then the reverse
  * sweep).  At ||k_t|| = 0 or ||A_t khat_t|| = 0 the normalisation has no derivative; the
- * gradient through it is taken as 0.  Outputs must not overlap inputs.  Ownership,
- * asynchrony and error behaviour are those of vla_forward.
+ * gradient through it is taken as 0.  The gradients (and a caller's workspace) must overlap
+ * neither one another nor any input, else VLA_ERROR_INVALID_VALUE.  Ownership, asynchrony and
+ * error behaviour are those of vla_forward.
  */
 vla_status_t vla_backward(const void *q, const void *k, const void *v, const void *u,
                           float lambda0, const void *d_out, const float *dS_T, const float *dA_T,

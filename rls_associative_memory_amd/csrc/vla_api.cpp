@@ -117,36 +117,65 @@ bool device_ok() {
   return info->ok;
 }
 
-// Library-owned workspace cache, one buffer per device, grown on demand.
+// Library-owned workspace cache: one buffer per (device, stream), grown on demand.  Calls on
+// one stream run in order, so they may share that stream's buffer; a call on another stream
+// gets a buffer of its own.  Growing waits for the stream's earlier work (the only work that
+// can still use the old buffer) before freeing it, which a stream under graph capture cannot
+// do: such a call returns VLA_ERROR_NOT_SUPPORTED (pass a workspace instead).
 struct WsCache {
+  int dev = -1;
+  hipStream_t stream = nullptr;
   void *ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_ws_mu;
 std::vector<WsCache> g_ws;
 
-vla_status_t cached_workspace(size_t need, void **out) {
+vla_status_t cached_workspace(size_t need, hipStream_t stream, void **out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return VLA_ERROR_NO_DEVICE;
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  if (static_cast<int>(g_ws.size()) <= dev) g_ws.resize(dev + 1);
-  WsCache &c = g_ws[dev];
-  if (c.bytes < need) {
-    if (c.ptr != nullptr) {
-      // The old buffer may still be in use by work on other streams of this device.
-      if (hipDeviceSynchronize() != hipSuccess) return VLA_ERROR_LAUNCH;
-      (void)hipFree(c.ptr);
-      c.ptr = nullptr;
-      c.bytes = 0;
+  WsCache *c = nullptr;
+  for (WsCache &e : g_ws)
+    if (e.dev == dev && e.stream == stream) c = &e;
+  if (c == nullptr) {
+    g_ws.push_back(WsCache{dev, stream, nullptr, 0});
+    c = &g_ws.back();
+  }
+  if (c->bytes < need) {
+    if (c->ptr != nullptr) {
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return VLA_ERROR_LAUNCH;
+      if (cap != hipStreamCaptureStatusNone) return VLA_ERROR_NOT_SUPPORTED;
+      if (hipStreamSynchronize(stream) != hipSuccess) return VLA_ERROR_LAUNCH;
+      (void)hipFree(c->ptr);
+      c->ptr = nullptr;
+      c->bytes = 0;
     }
-    if (hipMalloc(&c.ptr, need) != hipSuccess) {
-      c.ptr = nullptr;
+    if (hipMalloc(&c->ptr, need) != hipSuccess) {
+      c->ptr = nullptr;
       return VLA_ERROR_OUT_OF_MEMORY;
     }
-    c.bytes = need;
+    c->bytes = need;
   }
-  *out = c.ptr;
+  *out = c->ptr;
   return VLA_SUCCESS;
+}
+
+// Whether any output range overlaps another output or any input (inputs may alias one
+// another: they are only read).  NULL pointers take part in nothing.
+struct Range {
+  const void *p;
+  size_t n;
+};
+bool outputs_alias(const Range *outs, int no, const Range *ins, int ni) {
+  for (int a = 0; a < no; ++a) {
+    for (int b = a + 1; b < no; ++b)
+      if (overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n)) return true;
+    for (int b = 0; b < ni; ++b)
+      if (overlaps(outs[a].p, outs[a].n, ins[b].p, ins[b].n)) return true;
+  }
+  return false;
 }
 
 }  // namespace
@@ -188,10 +217,15 @@ vla_status_t vla_workspace_size(const vla_desc_t *desc, size_t *bytes) {
   return VLA_SUCCESS;
 }
 
-vla_status_t vla_forward_state(const void *q, const void *k, const void *v, const void *u,
-                               float lambda0, const float *S0, const float *A0, const float *n0,
-                               void *out, float *S_final, float *A_final, float *n_final,
-                               const vla_desc_t *desc, struct ihipStream_t *stream) {
+}  // extern "C"
+
+namespace {
+
+// vla_forward_state.
+vla_status_t forward_state_impl(const void *q, const void *k, const void *v, const void *u,
+                                float lambda0, const float *S0, const float *A0, const float *n0,
+                                void *out, float *S_final, float *A_final, float *n_final,
+                                const vla_desc_t *desc, struct ihipStream_t *stream) {
   vla_status_t st = check_desc(desc);
   if (st != VLA_SUCCESS) return st;
   if (q == nullptr || k == nullptr || v == nullptr || u == nullptr || out == nullptr)
@@ -201,14 +235,14 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
       !aligned16(S_final) || !aligned16(A_final) || !aligned16(n_final) || !aligned16(S0) ||
       !aligned16(A0) || !aligned16(n0))
     return VLA_ERROR_NOT_SUPPORTED;
-  {  // no output state may overlap an input state: the kernels do not update in place
-    const size_t mat = static_cast<size_t>(desc->B * desc->H) * desc->d * desc->d * sizeof(float);
-    const size_t vec = static_cast<size_t>(desc->B * desc->H) * desc->d * sizeof(float);
-    const void *outs[3] = {S_final, A_final, n_final}, *ins[3] = {S0, A0, n0};
-    const size_t osz[3] = {mat, mat, vec}, isz[3] = {mat, mat, vec};
-    for (int a = 0; a < 3; ++a)
-      for (int b = 0; b < 3; ++b)
-        if (overlaps(outs[a], osz[a], ins[b], isz[b])) return VLA_ERROR_INVALID_VALUE;
+  {  // outputs overlap neither one another nor any input (no update in place)
+    const size_t bh = static_cast<size_t>(desc->B * desc->H);
+    const size_t tok = bh * desc->T * desc->d * (desc->dtype == VLA_DTYPE_F32 ? 4 : 2);
+    const size_t mat = bh * desc->d * desc->d * sizeof(float);
+    const size_t vec = bh * desc->d * sizeof(float);
+    const Range outs[4] = {{out, tok}, {S_final, mat}, {A_final, mat}, {n_final, vec}};
+    const Range ins[7] = {{q, tok}, {k, tok}, {v, tok}, {u, tok}, {S0, mat}, {A0, mat}, {n0, vec}};
+    if (outputs_alias(outs, 4, ins, 7)) return VLA_ERROR_INVALID_VALUE;
   }
   const vla::Problem p = make_problem(desc, A0 != nullptr ? 1.0f : lambda0);
   int32_t path = 0;
@@ -222,11 +256,19 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
       if (desc->workspace_bytes < need) return VLA_ERROR_INVALID_VALUE;
       if (!aligned16(desc->workspace)) return VLA_ERROR_NOT_SUPPORTED;
       ws = desc->workspace;
+      const size_t bh = static_cast<size_t>(desc->B * desc->H);
+      const size_t tok = bh * desc->T * desc->d * (desc->dtype == VLA_DTYPE_F32 ? 4 : 2);
+      const size_t mat = bh * desc->d * desc->d * sizeof(float);
+      const size_t vec = bh * desc->d * sizeof(float);
+      const Range wr[1] = {{ws, need}};
+      const Range all[11] = {{q, tok}, {k, tok}, {v, tok}, {u, tok}, {S0, mat}, {A0, mat}, {n0, vec},
+                             {out, tok}, {S_final, mat}, {A_final, mat}, {n_final, vec}};
+      if (outputs_alias(wr, 1, all, 11)) return VLA_ERROR_INVALID_VALUE;
     }
   }
   if (!device_ok()) return VLA_ERROR_NO_DEVICE;
   if (path == VLA_PATH_CHUNK && ws == nullptr) {
-    st = cached_workspace(vla::chunk_workspace_bytes(p, chunk), &ws);
+    st = cached_workspace(vla::chunk_workspace_bytes(p, chunk), reinterpret_cast<hipStream_t>(stream), &ws);
     if (st != VLA_SUCCESS) return st;
   }
   vla::StateIO sio;
@@ -245,6 +287,18 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
   else
     err = vla::launch_chunk(p, chunk, q, k, v, u, out, sio, ws, s);
   return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+vla_status_t vla_forward_state(const void *q, const void *k, const void *v, const void *u,
+                               float lambda0, const float *S0, const float *A0, const float *n0,
+                               void *out, float *S_final, float *A_final, float *n_final,
+                               const vla_desc_t *desc, struct ihipStream_t *stream) {
+  return forward_state_impl(q, k, v, u, lambda0, S0, A0, n0, out, S_final, A_final, n_final, desc,
+                            stream);
 }
 
 vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes) {
@@ -278,9 +332,18 @@ vla_status_t vla_linear_attention(const void *q, const void *k, const void *v, v
     if (!aligned16(desc->workspace)) return VLA_ERROR_NOT_SUPPORTED;
     ws = desc->workspace;
   }
+  {  // outputs (and a caller's workspace) overlap neither one another nor any input
+    const size_t bh = static_cast<size_t>(desc->B * desc->H);
+    const size_t tok = bh * desc->T * desc->d * (desc->dtype == VLA_DTYPE_F32 ? 4 : 2);
+    const size_t mat = bh * desc->d * desc->d * sizeof(float);
+    const size_t vec = bh * desc->d * sizeof(float);
+    const Range outs[4] = {{out, tok}, {S_final, mat}, {n_final, vec}, {ws, need}};
+    const Range ins[3] = {{q, tok}, {k, tok}, {v, tok}};
+    if (outputs_alias(outs, 4, ins, 3)) return VLA_ERROR_INVALID_VALUE;
+  }
   if (!device_ok()) return VLA_ERROR_NO_DEVICE;
   if (ws == nullptr) {
-    st = cached_workspace(need, &ws);
+    st = cached_workspace(need, reinterpret_cast<hipStream_t>(stream), &ws);
     if (st != VLA_SUCCESS) return st;
   }
   const hipError_t err = vla::launch_la(p, q, k, v, out, S_final, n_final, ws,
@@ -321,9 +384,21 @@ vla_status_t vla_backward(const void *q, const void *k, const void *v, const voi
     if (!aligned16(desc->workspace)) return VLA_ERROR_NOT_SUPPORTED;
     ws = desc->workspace;
   }
+  {  // gradients (and a caller's workspace) overlap neither one another nor any input
+    const size_t bh = static_cast<size_t>(desc->B * desc->H);
+    const size_t tok = bh * desc->T * desc->d * (desc->dtype == VLA_DTYPE_F32 ? 4 : 2);
+    const size_t g32 = bh * desc->T * desc->d * sizeof(float);
+    const size_t mat = bh * desc->d * desc->d * sizeof(float);
+    const size_t vec = bh * desc->d * sizeof(float);
+    const Range outs[6] = {{dq, g32}, {dk, g32}, {dv, g32}, {du, g32}, {dlambda0, bh * sizeof(float)},
+                           {ws, need}};
+    const Range ins[8] = {{q, tok}, {k, tok}, {v, tok}, {u, tok}, {d_out, tok}, {dS_T, mat}, {dA_T, mat},
+                          {dn_T, vec}};
+    if (outputs_alias(outs, 6, ins, 8)) return VLA_ERROR_INVALID_VALUE;
+  }
   if (!device_ok()) return VLA_ERROR_NO_DEVICE;
   if (ws == nullptr) {
-    st = cached_workspace(need, &ws);
+    st = cached_workspace(need, reinterpret_cast<hipStream_t>(stream), &ws);
     if (st != VLA_SUCCESS) return st;
   }
   vla::BackwardIO io{q, k, v, u, d_out, dS_T, dA_T, dn_T, dq, dk, dv, du, dlambda0};

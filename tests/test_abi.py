@@ -228,3 +228,53 @@ def test_auto_path_choice(lib, shape, dtype, want):
     p = ctypes.c_int32(-1)
     assert lib.vla_resolve_path(ctypes.byref(desc(B=B, H=H, T=T, d=d, dtype=dtype)), ctypes.byref(p)) == 0
     assert p.value == vla.PATHS[want], (shape, dtype, p.value)
+
+
+def _fake(off):
+    return ctypes.c_void_p((1 << 24) + off)
+
+
+def test_outputs_must_not_alias_inputs(lib):
+    """out (or a state output, or a caller's workspace) overlapping an input or another output
+    is an argument error, reported before any device work (fake pointers, never touched)."""
+    if torch.cuda.is_available():
+        pytest.skip("fake device pointers are only passed where no GPU can be reached")
+    d = desc(B=1, H=2, T=64, d=32, dtype=0, path=1)
+    tok = 2 * 64 * 32 * 4
+    mat = 2 * 32 * 32 * 4
+    q, k, v, u = (_fake(i * tok) for i in range(4))
+    f = ctypes.c_float(1.0)
+    fwd = lambda out, S=None, A=None, dd=d: lib.vla_forward(q, k, v, u, f, out, S, A, ctypes.byref(dd), None)
+    assert fwd(_fake(2 * tok)) == 1                              # out is v
+    assert fwd(_fake(3 * tok + tok // 2)) == 1                   # out starts inside u
+    assert fwd(_fake(3 * tok - 256)) == 1                        # out ends inside u
+    base = 8 * tok
+    assert fwd(_fake(base), S=_fake(base + tok - 16)) == 1       # S_final inside out
+    assert fwd(_fake(base), S=_fake(base + tok), A=_fake(base + tok)) == 1   # S_final is A_final
+    assert fwd(_fake(base), S=_fake(0)) == 1                     # S_final is q
+    # disjoint buffers pass the check and stop only at the device check
+    assert fwd(_fake(base), S=_fake(base + tok), A=_fake(base + tok + mat)) == 5
+    # a caller's workspace overlapping an output
+    ch = desc(B=1, H=2, T=2048, d=32, dtype=0, path=2)
+    n = ctypes.c_size_t(0)
+    assert lib.vla_workspace_size(ctypes.byref(ch), ctypes.byref(n)) == 0
+    tk = 2 * 2048 * 32 * 4
+    q2, k2, v2, u2 = (_fake(i * tk) for i in range(4))
+    o2 = _fake(4 * tk)
+    ws_bad = desc(B=1, H=2, T=2048, d=32, dtype=0, path=2, workspace=(1 << 24) + 4 * tk + 4096,
+                  workspace_bytes=n.value)
+    assert lib.vla_forward(q2, k2, v2, u2, f, o2, None, None, ctypes.byref(ws_bad), None) == 1
+    ws_ok = desc(B=1, H=2, T=2048, d=32, dtype=0, path=2, workspace=(1 << 24) + 5 * tk,
+                 workspace_bytes=n.value)
+    assert lib.vla_forward(q2, k2, v2, u2, f, o2, None, None, ctypes.byref(ws_ok), None) == 5
+    # linear attention: out is k
+    la = desc(B=1, H=2, T=64, d=32, dtype=0)
+    assert lib.vla_linear_attention(q, k, v, _fake(tok), None, None, ctypes.byref(la), None) == 1
+    # backward: a gradient overlapping d_out, and two gradients sharing memory
+    dout = _fake(4 * tok)
+    g = [_fake(8 * tok + i * tok) for i in range(4)]
+    bw = lambda grads: lib.vla_backward(q, k, v, u, f, dout, None, None, None, *grads, None,
+                                        ctypes.byref(la), None)
+    assert bw([dout, g[1], g[2], g[3]]) == 1
+    assert bw([g[0], g[0], g[2], g[3]]) == 1
+    assert bw(g) == 5
