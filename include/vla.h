@@ -141,6 +141,29 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
                                const vla_desc_t *desc, struct ihipStream_t *stream);
 
 /*
+ * vla_forward_state_noalloc -- vla_forward_state for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It runs the same kernels as vla_forward_state on the same arguments, and the
+ * chunked path's scratch (vla_workspace_size() bytes) lives in one static device array per
+ * GPU of VLA_NOALLOC_SCRATCH_BYTES bytes, held by the library until the process ends; the
+ * call allocates nothing and creates no timing events (vla_profile_enable is ignored).
+ *
+ * desc->workspace must be NULL (VLA_ERROR_INVALID_VALUE otherwise).  A descriptor whose
+ * chunked path needs more than VLA_NOALLOC_SCRATCH_BYTES of scratch returns
+ * VLA_ERROR_NOT_SUPPORTED before any device work (the sequential and decode paths need
+ * none).  Every allocation-free call on one GPU shares that GPU's array: such calls must be
+ * ordered (one stream, or streams joined by events); calls that overlap on one GPU race and
+ * give wrong results.  Nothing in the array needs to start at any value (every byte a call
+ * reads it has written first).  Everything else is as for vla_forward_state.
+ */
+#define VLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+vla_status_t vla_forward_state_noalloc(const void *q, const void *k, const void *v, const void *u,
+                                       float lambda0, const float *S0, const float *A0,
+                                       const float *n0, void *out, float *S_final, float *A_final,
+                                       float *n_final, const vla_desc_t *desc,
+                                       struct ihipStream_t *stream);
+
+/*
  * vla_linear_attention -- the baseline the VLA update is measured against: standard linear
  * attention with the same ELU+1 feature map and ratio readout (VLA summary §2.1, the
  * unconditional accumulation VLA replaces; §2.3, the readout; §2.4 prices the VLA update at

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <optional>
 #include <vector>
 
 #include "vla.h"
@@ -221,11 +222,47 @@ vla_status_t vla_workspace_size(const vla_desc_t *desc, size_t *bytes) {
 
 namespace {
 
-// vla_forward_state.
+// Scratch of vla_forward_state_noalloc: one static array per device, never allocated by a
+// call.  In host code `scratch` names a host-side stand-in, not device memory, so its device
+// address is looked up once per device (with that device current) and only that address is
+// passed to kernels.  Every allocation-free call on a device shares the array.
+constexpr size_t kNoAllocScratchBytes = VLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+struct ScratchInfo {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void *ptr = nullptr;
+};
+std::mutex g_scratch_mu;
+std::vector<ScratchInfo *> g_scratch;
+
+vla_status_t scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return VLA_ERROR_NO_DEVICE;
+  ScratchInfo *info;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (static_cast<int>(g_scratch.size()) <= dev) g_scratch.resize(dev + 1, nullptr);
+    if (g_scratch[dev] == nullptr) g_scratch[dev] = new ScratchInfo();
+    info = g_scratch[dev];
+  }
+  std::call_once(info->once, [&] {
+    void *ptr = nullptr;
+    info->err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    info->ptr = info->err == hipSuccess ? ptr : nullptr;
+  });
+  if (info->err != hipSuccess || info->ptr == nullptr) return VLA_ERROR_LAUNCH;
+  *out = info->ptr;
+  return VLA_SUCCESS;
+}
+
+// vla_forward_state and vla_forward_state_noalloc.  With `noalloc` the chunked path's scratch
+// is the device's static array (never an allocation) and no timing events are created.
 vla_status_t forward_state_impl(const void *q, const void *k, const void *v, const void *u,
                                 float lambda0, const float *S0, const float *A0, const float *n0,
                                 void *out, float *S_final, float *A_final, float *n_final,
-                                const vla_desc_t *desc, struct ihipStream_t *stream) {
+                                const vla_desc_t *desc, struct ihipStream_t *stream, bool noalloc) {
   vla_status_t st = check_desc(desc);
   if (st != VLA_SUCCESS) return st;
   if (q == nullptr || k == nullptr || v == nullptr || u == nullptr || out == nullptr)
@@ -250,8 +287,10 @@ vla_status_t forward_state_impl(const void *q, const void *k, const void *v, con
   st = resolve(desc, p, &path, &chunk);
   if (st != VLA_SUCCESS) return st;
   void *ws = nullptr;
+  if (noalloc && desc->workspace != nullptr) return VLA_ERROR_INVALID_VALUE;
   if (path == VLA_PATH_CHUNK) {
     const size_t need = vla::chunk_workspace_bytes(p, chunk);
+    if (noalloc && need > kNoAllocScratchBytes) return VLA_ERROR_NOT_SUPPORTED;
     if (desc->workspace != nullptr) {
       if (desc->workspace_bytes < need) return VLA_ERROR_INVALID_VALUE;
       if (!aligned16(desc->workspace)) return VLA_ERROR_NOT_SUPPORTED;
@@ -268,7 +307,9 @@ vla_status_t forward_state_impl(const void *q, const void *k, const void *v, con
   }
   if (!device_ok()) return VLA_ERROR_NO_DEVICE;
   if (path == VLA_PATH_CHUNK && ws == nullptr) {
-    st = cached_workspace(vla::chunk_workspace_bytes(p, chunk), reinterpret_cast<hipStream_t>(stream), &ws);
+    st = noalloc ? scratch_address(&ws)
+                 : cached_workspace(vla::chunk_workspace_bytes(p, chunk),
+                                    reinterpret_cast<hipStream_t>(stream), &ws);
     if (st != VLA_SUCCESS) return st;
   }
   vla::StateIO sio;
@@ -279,6 +320,8 @@ vla_status_t forward_state_impl(const void *q, const void *k, const void *v, con
   sio.A_final = A_final;
   sio.n_final = n_final;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::optional<vla::ProfQuiet> quiet;  // no timing events on the allocation-free path
+  if (noalloc) quiet.emplace();
   hipError_t err;
   if (path == VLA_PATH_SEQ)
     err = vla::launch_seq(p, q, k, v, u, out, sio, s);
@@ -298,7 +341,16 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
                                void *out, float *S_final, float *A_final, float *n_final,
                                const vla_desc_t *desc, struct ihipStream_t *stream) {
   return forward_state_impl(q, k, v, u, lambda0, S0, A0, n0, out, S_final, A_final, n_final, desc,
-                            stream);
+                            stream, false);
+}
+
+vla_status_t vla_forward_state_noalloc(const void *q, const void *k, const void *v, const void *u,
+                                       float lambda0, const float *S0, const float *A0,
+                                       const float *n0, void *out, float *S_final, float *A_final,
+                                       float *n_final, const vla_desc_t *desc,
+                                       struct ihipStream_t *stream) {
+  return forward_state_impl(q, k, v, u, lambda0, S0, A0, n0, out, S_final, A_final, n_final, desc,
+                            stream, true);
 }
 
 vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes) {

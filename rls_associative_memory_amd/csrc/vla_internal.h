@@ -59,6 +59,19 @@ struct BackwardIO {
 size_t backward_workspace_bytes(const Problem &p);
 hipError_t launch_backward(const Problem &p, const BackwardIO &io, void *ws, hipStream_t stream);
 
+// While an object of this type lives, launches on the calling thread record no timing events
+// (the allocation-free entry point creates no events, whatever vla_profile_enable says).
+class ProfQuiet {
+ public:
+  ProfQuiet();
+  ~ProfQuiet();
+  ProfQuiet(const ProfQuiet &) = delete;
+  ProfQuiet &operator=(const ProfQuiet &) = delete;
+
+ private:
+  bool prev_;
+};
+
 // Event-pair timing of one kernel launch when vla_profile_enable(1) is in effect.
 class ProfScope {
  public:

@@ -25,6 +25,7 @@ struct Total {
 };
 
 std::atomic<bool> g_on{false};
+thread_local bool t_quiet = false;
 std::mutex g_mu;
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_free;
@@ -64,8 +65,11 @@ void resolve_locked() {
 
 }  // namespace
 
+ProfQuiet::ProfQuiet() : prev_(t_quiet) { t_quiet = true; }
+ProfQuiet::~ProfQuiet() { t_quiet = prev_; }
+
 ProfScope::ProfScope(const char *name, hipStream_t s) : name_(name), stream_(s) {
-  if (!g_on.load(std::memory_order_relaxed)) return;
+  if (t_quiet || !g_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);
   ev0_ = take_event();
   ev1_ = take_event();

@@ -15,7 +15,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["forward", "forward_state", "backward", "backward_workspace_size", "linear_attention", "la_workspace_size", "workspace_size", "resolve_path", "library_path", "load_library",
+__all__ = ["forward", "forward_state", "NOALLOC_SCRATCH_BYTES", "backward", "backward_workspace_size", "linear_attention", "la_workspace_size", "workspace_size", "resolve_path", "library_path", "load_library",
            "profile_enable", "profile_reset", "profile_read",
            "VlaError", "exported_symbols", "STATUS", "PATHS", "DTYPES", "GAINS", "VlaDesc"]
 
@@ -30,6 +30,8 @@ STATUS = {
 PATHS = {"auto": 0, "seq": 1, "chunk": 2, "decode": 3}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 GAINS = {"unit": 0, "raw": 1}  # raw: A_t khat without the normalisation (ablation only)
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # VLA_NOALLOC_SCRATCH_BYTES in include/vla.h
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG), "include", "vla.h")
@@ -77,6 +79,8 @@ def load_library():
         lib.vla_forward_state.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(VlaDesc), vp]
         lib.vla_forward_state.restype = ctypes.c_int
+        lib.vla_forward_state_noalloc.argtypes = lib.vla_forward_state.argtypes
+        lib.vla_forward_state_noalloc.restype = ctypes.c_int
         lib.vla_linear_attention.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(VlaDesc), vp]
         lib.vla_linear_attention.restype = ctypes.c_int
         lib.vla_backward.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -222,7 +226,8 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   stream: Optional[torch.cuda.Stream] = None,
                   S_final: Optional[torch.Tensor] = None, A_final: Optional[torch.Tensor] = None,
-                  n_final: Optional[torch.Tensor] = None, gain: str = "unit"):
+                  n_final: Optional[torch.Tensor] = None, gain: str = "unit",
+                  noalloc: bool = False):
     """VLA forward continuing from a carried state (vla_forward_state in vla.h).
 
     S0 and A0 are fp32 [.., d, d] and n0 fp32 [.., d] device tensors, or None for the fixed
@@ -230,6 +235,8 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
     (out, S_T, A_T, n_T), which a next call takes as its (S0, A0, n0); S_final, A_final and
     n_final optionally give the buffers to write them to (they must not be S0, A0, n0).
     ``gain="raw"`` runs the un-normalised-gain ablation (sequential and decode paths only).
+    ``noalloc=True`` calls vla_forward_state_noalloc instead: the library allocates no device
+    memory (the chunked path's scratch is its static per-GPU array; ``workspace`` must be None).
     """
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
@@ -267,12 +274,13 @@ def forward_state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Te
                 raise ValueError(f"{a_name} overlaps {b_name}: the state is not updated in place")
     ptr = lambda t: t.data_ptr() if t is not None else None
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    fn = lib.vla_forward_state_noalloc if noalloc else lib.vla_forward_state
     with torch.cuda.device(q.device):
-        status = lib.vla_forward_state(
+        status = fn(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), u.data_ptr(), float(lambda0),
             ptr(S0), ptr(A0), ptr(n0), out.data_ptr(), S_T.data_ptr(), A_T.data_ptr(),
             n_T.data_ptr(), ctypes.byref(desc), s.cuda_stream)
-    _check(status, "vla_forward_state")
+    _check(status, "vla_forward_state_noalloc" if noalloc else "vla_forward_state")
     return out, S_T, A_T, n_T
 
 

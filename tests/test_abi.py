@@ -278,3 +278,20 @@ def test_outputs_must_not_alias_inputs(lib):
     assert bw([dout, g[1], g[2], g[3]]) == 1
     assert bw([g[0], g[0], g[2], g[3]]) == 1
     assert bw(g) == 5
+
+
+def test_noalloc_argument_errors(lib):
+    """vla_forward_state_noalloc refuses a caller's workspace and a scratch need beyond its
+    static array before any device work (fake pointers, never touched)."""
+    x = ctypes.c_void_p(1 << 24)
+    f = ctypes.c_float(1.0)
+    call = lambda dd: lib.vla_forward_state_noalloc(x, x, x, x, f, None, None, None,
+                                                     ctypes.c_void_p((1 << 30)), None, None, None,
+                                                     ctypes.byref(dd), None)
+    assert call(desc(B=1, H=2, T=2048, d=32, dtype=0, path=2, workspace=1 << 28,
+                     workspace_bytes=1 << 26)) == 1
+    big = desc(B=8, H=8, T=4096, d=64, dtype=1, path=2)
+    n = ctypes.c_size_t(0)
+    assert lib.vla_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value > vla.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 2
