@@ -12,10 +12,13 @@
 // Layout.  Wave w holds column tile w of A (16 columns, all rows) in MFMA accumulators.
 // Because A is symmetric, those registers are also row tile w of A, i.e. exactly the
 // A operand of A [U^T | K^T] for rows 16w..16w+15, so A never goes through LDS; each
-// fp32 operand is split into NTERM bf16 terms right before use (two terms: hi + lo, about 16
-// significant bits).  Products with the raw bf16 inputs take one MFMA per term; products of
-// two derived fp32 operands take the term pairs (i, j) with i + j < NTERM (the dropped
-// ones are near 2^-16 relative), all accumulated in fp32 by v_mfma_f32_16x16x32_bf16.
+// fp32 operand is split into NTERM bf16 terms right before use: two terms (hi + lo, about 16
+// significant bits), or three (about 24 bits) where the steps cancel strongly: with u_t of
+// norm ~ sqrt(d) and a small lambda0, A_t k_t is a difference of terms up to
+// 1 + ||u||^2 / lambda0 times larger than itself while fewer than d directions have been
+// seen.  Products with the raw bf16 inputs take one MFMA per term; products of two derived
+// fp32 operands take the term pairs (i, j) with i + j < NTERM (the dropped ones are near
+// 2^-8 NTERM relative), all accumulated in fp32 by v_mfma_f32_16x16x32_bf16.
 #pragma once
 
 #include "vla_common.h"
@@ -23,7 +26,7 @@
 
 namespace vla {
 
-template <int D>
+template <int D, int TERMS = 2>
 struct AwyCfg {
   static constexpr int NW = D / 16;
   static constexpr int NT = NW * kWave;  // = 4 D
@@ -31,13 +34,13 @@ struct AwyCfg {
   static constexpr int NKS = D / 32;     // 32-wide feature slices (D = 32 -> 1)
   static constexpr int LDU = D + 8;      // padded bf16 row stride of token rows
   static constexpr int LDL = 40;         // padded bf16 row stride of the 32 x 32 matrices
-  static constexpr int NTERM = 2;        // bf16 terms per fp32 operand
+  static constexpr int NTERM = TERMS;    // bf16 terms per fp32 operand (2 or 3)
   static_assert(D % 32 == 0, "feature dimension must be a multiple of 32");
 };
 
-template <int D>
+template <int D, int TERMS>
 struct AwyLds {
-  using C = AwyCfg<D>;
+  using C = AwyCfg<D, TERMS>;
   uint16_t sU[C::C][C::LDU];
   uint16_t sK[C::C][C::LDU];
   uint16_t sQ[C::C][C::LDU];
@@ -52,18 +55,18 @@ struct AwyLds {
   float norm[C::NW][C::C][4] __attribute__((aligned(16)));  // partial ||Y_c||^2 per wave and lane group
 };
 
-template <int D>
-__global__ void __launch_bounds__(AwyCfg<D>::NT)
+template <int D, int TERMS>
+__global__ void __launch_bounds__((AwyCfg<D, TERMS>::NT))
 k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
            const bf16_t *__restrict__ u, const float *__restrict__ A0,
            const float *__restrict__ nk0, float *__restrict__ alpha, float *__restrict__ rkden,
            float *__restrict__ A_final, float *__restrict__ n_final, int64_t T, int64_t L,
            int64_t P, float eps) {
-  using C = AwyCfg<D>;
+  using C = AwyCfg<D, TERMS>;
   constexpr int NW = C::NW, NT = C::NT, CH = C::C, NTM = C::NTERM;
   constexpr int ZR_T = CH * C::LDU;       // term stride of Zr
   constexpr int LX_T = CH * C::LDL;       // term stride of LX
-  __shared__ __attribute__((aligned(16))) AwyLds<D> sh;
+  __shared__ __attribute__((aligned(16))) AwyLds<D, TERMS> sh;
 
   const int64_t s = blockIdx.x, p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, gq = lane >> 4;

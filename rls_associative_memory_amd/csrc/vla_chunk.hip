@@ -1177,8 +1177,16 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
   }
   if constexpr (sizeof(TIn) == 2) {
     // bf16 inputs: chunked A side on the bf16 matrix cores.
-    VLA_LAUNCH("k_aside_wy", (k_aside_wy<D>), dim3(S, P), dim3(AwyCfg<D>::NT), 0, st, qq, kk,
-               uu, Mw, nkw, alw, rdw, A_final, n_final, pl.T, pl.L, pl.P, pr.eps);
+    // Three-term operands when the Sherman-Morrison steps cancel strongly: from A_0 = I / lambda0
+    // with lambda0 < d / 256 (unit-variance inputs then give cancellation factors above ~256,
+    // which two-term operands, 16 significant bits, cannot absorb).
+    if (sio.A0 == nullptr && pr.lambda0 < static_cast<float>(D) / 256.0f) {
+      VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 3>), dim3(S, P), dim3(AwyCfg<D, 3>::NT), 0, st, qq,
+                 kk, uu, Mw, nkw, alw, rdw, A_final, n_final, pl.T, pl.L, pl.P, pr.eps);
+    } else {
+      VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2>), dim3(S, P), dim3(AwyCfg<D, 2>::NT), 0, st, qq,
+                 kk, uu, Mw, nkw, alw, rdw, A_final, n_final, pl.T, pl.L, pl.P, pr.eps);
+    }
   } else {
     using AC = AsideCfg<D>;
     const int64_t units = pl.S * pl.P;
