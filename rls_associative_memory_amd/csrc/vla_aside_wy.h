@@ -43,20 +43,30 @@ struct AwyLds {
   using C = AwyCfg<D, TERMS>;
   uint16_t sU[C::C][C::LDU];
   uint16_t sK[C::C][C::LDU];
-  uint16_t sQ[C::C][C::LDU];
   uint16_t Zr[C::NTERM][C::C][C::LDU];          // row-major Z0 terms, later W terms
   uint16_t Zb[C::NTERM][C::C][C::LDU];          // row-major Z terms
   float G[C::C][C::C + 4];               // I + U A U^T (lower part used); then L^{-1}, row-major
-  uint16_t LX[C::NTERM][C::C][C::LDL];          // X~ terms (B operand)
+  union {                                       // live in different phases of a chunk
+    uint16_t LX[C::NTERM][C::C][C::LDL];        // X~ terms (B operand), after the factorisation
+    float lw[4][16][20];                        // blocked LDL^T scratch, during it
+  } __attribute__((aligned(16)));
   float rsd[C::C], rd[C::C];
-  float lw[4][16][20] __attribute__((aligned(16)));  // blocked LDL^T scratch
   float nbuf[2][D] __attribute__((aligned(16)));  // sum of phi(k) before the chunk
-  float dtmp[2][16];
-  float norm[C::NW][C::C][4] __attribute__((aligned(16)));  // partial ||Y_c||^2 per wave and lane group
+  float dpart[C::NKS][C::C], apart[C::NKS][C::C], kpart[C::NKS][C::C];  // per-slice shares
+  float norm[C::NW][C::C];                       // partial ||Y_c||^2 per wave
 };
+
+// Two workgroups share a CU only when each stays within 128 VGPRs and about 53 KB of LDS:
+// a workgroup's waves are placed from the first SIMD on, so with six waves (d = 96) two of the
+// SIMDs hold four waves of two workgroups, and larger LDS requests leave room for one
+// workgroup only (both measured on gfx950).  d = 64 and d = 96 with two-term operands are
+// compiled for four waves per SIMD; with one workgroup per CU the scheduler keeps its choice.
+template <int D, int TERMS>
+constexpr int awy_waves_per_simd() { return (TERMS == 2 && (D == 64 || D == 96)) ? 4 : 1; }
 
 template <int D, int TERMS>
 __global__ void __launch_bounds__((AwyCfg<D, TERMS>::NT))
+__attribute__((amdgpu_waves_per_eu(awy_waves_per_simd<D, TERMS>())))
 k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
            const bf16_t *__restrict__ u, const float *__restrict__ A0,
            const float *__restrict__ nk0, float *__restrict__ alpha, float *__restrict__ rkden,
@@ -66,7 +76,13 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   constexpr int NW = C::NW, NT = C::NT, CH = C::C, NTM = C::NTERM;
   constexpr int ZR_T = CH * C::LDU;       // term stride of Zr
   constexpr int LX_T = CH * C::LDL;       // term stride of LX
-  __shared__ __attribute__((aligned(16))) AwyLds<D, TERMS> sh;
+  // The chunk buffers, or (after the last chunk) A_T being symmetrised.
+  union Shared {
+    AwyLds<D, TERMS> sh;
+    float sym[D][D + 1];
+  };
+  __shared__ __attribute__((aligned(16))) Shared shu;
+  AwyLds<D, TERMS> &sh = shu.sh;
 
   const int64_t s = blockIdx.x, p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, gq = lane >> 4;
@@ -91,20 +107,20 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   // number c reads nbuf[c & 1] and its update is written to nbuf[(c & 1) ^ 1].
   for (int f = tid; f < D; f += NT) sh.nbuf[0][f] = nk0[(s * P + p) * D + f];
 
-  // Staging: thread tid loads token tid / (D/8), features (tid % (D/8)) * 8 of u, k, q.
+  // Staging: thread tid loads token tid / (D/8), features (tid % (D/8)) * 8 of u and k (q is
+  // read only by the denominator waves, straight from memory into registers).
   // Rows past the segment are read as row 0 and zeroed when staged (no select on a load
   // result, which would make the load wait at once); offsets are 32-bit from uniform bases.
   // Every chunk prefetches and stages a next chunk (past the segment's end: its first row,
   // staged as zeros and never read), so no load is left pending across the loop's back edge
   // and the loop head does not wait for the previous chunk's stores.
-  uint4 pv[3];
+  uint4 pv[2];
   auto prefetch = [&](int64_t cs, int tid) {
     const int sc = tid / (D / 8), sf0 = (tid % (D / 8)) * 8;
     const uint32_t off = (cs + sc < te) ? static_cast<uint32_t>(sc * D + sf0) : 0u;
     const int64_t cb = (cs < te) ? cs : tb;  // a row of this segment
     pv[0] = *reinterpret_cast<const uint4 *>(us + cb * D + off);
     pv[1] = *reinterpret_cast<const uint4 *>(ks + cb * D + off);
-    pv[2] = *reinterpret_cast<const uint4 *>(qs + cb * D + off);
   };
   // Rows of the chunk at cs, staged into LDS; rows past the segment become zeros.
   auto stage = [&](int64_t cs, int tid) {
@@ -112,7 +128,6 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     const bool ok = cs + sc < te;
     *reinterpret_cast<uint4 *>(&sh.sU[sc][sf0]) = keep_if(ok, pv[0]);
     *reinterpret_cast<uint4 *>(&sh.sK[sc][sf0]) = keep_if(ok, pv[1]);
-    *reinterpret_cast<uint4 *>(&sh.sQ[sc][sf0]) = keep_if(ok, pv[2]);
   };
   prefetch(tb, tid);
   stage(tb, tid);
@@ -146,6 +161,18 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     // this chunk has read its own (after X~).
     __syncthreads();
     prefetch(c0 + CH, tid);
+    // The denominator waves' q rows (tokens 16 it + li, their slice's features 4 gq.. and
+    // 16 + 4 gq..): used mid-chunk, so one load latency is covered by the products before.
+    uint2 qd[2][2];
+    if (w >= 1 && w <= C::NKS) {
+      const int fa = 32 * (w - 1) + 4 * gq;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int64_t row = (c0 + 16 * it + li < te) ? c0 + 16 * it + li : tb;  // a row of the segment
+        qd[it][0] = *reinterpret_cast<const uint2 *>(qs + row * D + fa);
+        qd[it][1] = *reinterpret_cast<const uint2 *>(qs + row * D + fa + 16);
+      }
+    }
 
     // ---- [Z0^T | P^T] = A [U^T | K^T] (rows 16w.., 32 tokens) ---------------------------
     f4_t Z0t[2], Pt[2];
@@ -206,7 +233,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       }
     }
     __syncthreads();
-    // ---- wave 0: G = L D L^T and L^{-1};  waves >= 1: readout denominators ----------------
+    // ---- wave 0: G = L D L^T and L^{-1};  waves 1..D/32: readout denominators --------------
     if (w == 0) {
       // Blocked LDL^T of G in two 16-column panels.  In a panel, lanes hold rows (of G, or of
       // the Schur complement) restricted to the panel's 16 columns, lanes 32..47 hold the
@@ -317,85 +344,91 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int r = 0; r < 16; ++r) sh.G[16 + r][mcol] = y[r];  // L^{-1}_21 | L^{-1}_22
       }
-    } else {
-      // Readout denominators and key norms of the chunk, on the matrix cores of the waves
-      // that are otherwise idle here.  With M = phi(Q) phi(K)^T and n0 the sum of phi(k)
-      // before the chunk,  den_c = phi(q_c) . n0 + sum_{i <= c} M[c][i].  Jobs: token tile 0,
-      // token tile 1 (denominators and ||k||), then the 64-feature blocks of n's update.
-      constexpr int NH = NW - 1, NJ = 2 + (D + 63) / 64;
+    } else if (w <= C::NKS) {
+      // Readout denominators, key norms and the normaliser update of the chunk, one 32-feature
+      // slice per wave (slice w - 1), on the matrix cores of waves that are otherwise idle
+      // here.  With M = phi(Q) phi(K)^T and n0 the sum of phi(k) before the chunk,
+      //   den_c = phi(q_c) . n0 + sum_{i <= c} M[c][i] + eps,
+      // each slice giving its share of both sums and of ||k_c||^2; the shares are added after
+      // the barrier.  The slice's features of n advance by the column sums of phi(K).
+      const int sl = w - 1;
       const int pc = static_cast<int>((c0 - tb) / CH) & 1;
       const float *n0 = sh.nbuf[pc];
-      for (int job = w - 1; job < NJ; job += NH) {
-        if (job < 2) {
-          const int it = job;
-          f4_t macc[2] = {f4_zero(), f4_zero()};
-          float asum = 0.f, ksq = 0.f;
+      const int fa = 32 * sl + 4 * gq, fb = fa + 16;
+      const f4_t na = *reinterpret_cast<const f4_t *>(&n0[fa]);
+      const f4_t nb = *reinterpret_cast<const f4_t *>(&n0[fb]);
+      Split2 aq[2], ak[2];
+      float asum[2], ksq[2], ncol[8];
 #pragma unroll
-          for (int ksl = 0; ksl < C::NKS; ++ksl) {
-            const int fa = 32 * ksl + 4 * gq, fb = fa + 16;
-            const bf16x8_t qr = ld_bf4x2(&sh.sQ[16 * it + li][fa], &sh.sQ[16 * it + li][fb]);
-            const f4_t na = *reinterpret_cast<const f4_t *>(&n0[fa]);
-            const f4_t nb = *reinterpret_cast<const f4_t *>(&n0[fb]);
-            float qv[8];
+      for (int e = 0; e < 8; ++e) ncol[e] = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              qv[e] = phi(static_cast<float>(qr[e]));
-              asum = fmaf(qv[e], e < 4 ? na[e] : nb[e - 4], asum);
-            }
-            const Split2 aq = split2(qv);
+      for (int it = 0; it < 2; ++it) {
+        const bf16x8_t qr = __builtin_bit_cast(bf16x8_t, make_uint4(qd[it][0].x, qd[it][0].y, qd[it][1].x, qd[it][1].y));
+        const bf16x8_t kr = ld_bf4x2(&sh.sK[16 * it + li][fa], &sh.sK[16 * it + li][fb]);
+        const bool valid = 16 * it + li < m;
+        float qv[8], kv[8];
+        asum[it] = 0.f;
+        ksq[it] = 0.f;
 #pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-              if (jt > it) continue;
-              const bf16x8_t kr = ld_bf4x2(&sh.sK[16 * jt + li][fa], &sh.sK[16 * jt + li][fb]);
-              float kv[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float kf = static_cast<float>(kr[e]);
-                if (jt == it) ksq = fmaf(kf, kf, ksq);
-                kv[e] = phi(kf);
-              }
-              macc[jt] = mm2_ss(aq, split2(kv), macc[jt]);
-            }
-          }
-          // macc[jt][r] = M[16 it + 4 gq + r][16 jt + li]: masked sums over li (a lane row).
-          float rs[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * gq + r;
-            const float dg = it ? macc[1][r] : macc[0][r];  // diagonal tile
-            float v = (li <= i) ? dg : 0.f;
-            if (it == 1) v += macc[0][r];
-            v += dpp_xor1(v);
-            v += dpp_xor2(v);
-            v += dpp_half_mirror(v);
-            rs[r] = v + dpp_mirror(v);
-          }
-          // phi(q_c) . n0 and ||k_c||^2 of token 16 it + li: sums over the lane's gq copies.
-          asum += __shfl_xor(asum, 16);
-          asum += __shfl_xor(asum, 32);
-          ksq += __shfl_xor(ksq, 16);
-          ksq += __shfl_xor(ksq, 32);
-          if (li == 0)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sh.dtmp[it][4 * gq + r] = rs[r];
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int c = 16 * it + li;
-          if (gq == 0 && c < m)
-            *reinterpret_cast<float2 *>(&rd[(c0 + c) * 2]) =
-                make_float2(ksq > 0.f ? rsqrtf(ksq) : 0.f, asum + sh.dtmp[it][li] + eps);
-        } else {
-          const int f = 64 * (job - 2) + lane;
-          if (f < D) {
-            float sum = 0.f;
-            for (int c = 0; c < m; ++c) sum += phi(bf_val(sh.sK[c][f]));
-            sh.nbuf[pc ^ 1][f] = n0[f] + sum;
-          }
+        for (int e = 0; e < 8; ++e) {
+          qv[e] = phi(static_cast<float>(qr[e]));
+          asum[it] = fmaf(qv[e], e < 4 ? na[e] : nb[e - 4], asum[it]);
+          const float kf = static_cast<float>(kr[e]);
+          ksq[it] = fmaf(kf, kf, ksq[it]);
+          kv[e] = phi(kf);
+          ncol[e] += valid ? kv[e] : 0.f;
         }
+        aq[it] = split2(qv);
+        ak[it] = split2(kv);
+      }
+      // M tiles over this slice: m00 = (0,0), m10 = (1,0), m11 = (1,1);
+      // element r of a tile is M[16 it + 4 gq + r][16 jt + li]
+      const f4_t m00 = mm2_ss(aq[0], ak[0], f4_zero());
+      const f4_t m10 = mm2_ss(aq[1], ak[0], f4_zero());
+      const f4_t m11 = mm2_ss(aq[1], ak[1], f4_zero());
+      float rs0[4], rs1[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * gq + r;
+        rs0[r] = row_sum16(li <= i ? m00[r] : 0.f);
+        rs1[r] = row_sum16(m10[r] + (li <= i ? m11[r] : 0.f));
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {  // token 16 it + li: sums over the four lane groups
+        asum[it] += __shfl_xor(asum[it], 16);
+        asum[it] += __shfl_xor(asum[it], 32);
+        ksq[it] += __shfl_xor(ksq[it], 16);
+        ksq[it] += __shfl_xor(ksq[it], 32);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ncol[e] = row_sum16(ncol[e]);
+      if (li == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sh.dpart[sl][4 * gq + r] = rs0[r];
+          sh.dpart[sl][16 + 4 * gq + r] = rs1[r];
+        }
+        *reinterpret_cast<f4_t *>(&sh.nbuf[pc ^ 1][fa]) = na + f4_t{ncol[0], ncol[1], ncol[2], ncol[3]};
+        *reinterpret_cast<f4_t *>(&sh.nbuf[pc ^ 1][fb]) = nb + f4_t{ncol[4], ncol[5], ncol[6], ncol[7]};
+      }
+      if (gq == 0) {
+        sh.apart[sl][li] = asum[0];
+        sh.apart[sl][16 + li] = asum[1];
+        sh.kpart[sl][li] = ksq[0];
+        sh.kpart[sl][16 + li] = ksq[1];
       }
     }
     __syncthreads();
+    // the chunk's (1/||k||, den) from the slices' shares
+    if (w == NW - 1 && lane < CH) {
+      float den = eps, kk = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < C::NKS; ++sl) {
+        den += sh.dpart[sl][lane] + sh.apart[sl][lane];
+        kk += sh.kpart[sl][lane];
+      }
+      if (lane < m) *reinterpret_cast<float2 *>(&rd[(c0 + lane) * 2]) = make_float2(kk > 0.f ? rsqrtf(kk) : 0.f, den);
+    }
     // ---- Z^T = Z0^T L^{-T} ---------------------------------------------------------------
     f4_t Zt[2];
     {
@@ -457,7 +490,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       }
     }
     __syncthreads();
-    // the next chunk's rows (sU, sK, sQ are not read again in this chunk)
+    // the next chunk's rows (sU, sK are not read again in this chunk)
     stage(c0 + CH, tid);
     // ---- W = D^{-1/2} Z into the first buffer (Z0 is no longer read) ----------------------
     {
@@ -485,7 +518,9 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       float part = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) part = fmaf(Yt[ct][r], Yt[ct][r], part);
-      sh.norm[w][16 * ct + li][gq] = part;  // the four lane groups are summed by the readers
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (gq == 0) sh.norm[w][16 * ct + li] = part;
     }
     __syncthreads();
 #pragma unroll
@@ -493,10 +528,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       const int c = 16 * ct + li;
       float tot = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
-        const f4_t pn = *reinterpret_cast<const f4_t *>(&sh.norm[w2][c][0]);
-        tot += (pn[0] + pn[1]) + (pn[2] + pn[3]);
-      }
+      for (int w2 = 0; w2 < NW; ++w2) tot += sh.norm[w2][c];
       const float inv = tot > 0.f ? rsqrtf(tot) : 0.f;
       if (c < m)
         *reinterpret_cast<float4 *>(&al[c0 * D + static_cast<uint32_t>(c * D + 16 * w + 4 * gq)]) =
@@ -529,7 +561,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   if (A_final != nullptr && p == P - 1) {
     // Symmetrise through LDS: A_T <- (A + A^T) / 2.
     __syncthreads();
-    float(*sym)[D + 1] = reinterpret_cast<float(*)[D + 1]>(&sh);
+    float(*sym)[D + 1] = shu.sym;
 #pragma unroll
     for (int it = 0; it < NW; ++it)
 #pragma unroll
