@@ -1203,7 +1203,11 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
                s0w, pl.P, sio.S0);
-    VLA_LAUNCH("k_swy_final", (k_swyb<D, CH, true>), dim3(S, P), dim3(SwbCfg<D, CH, true>::NT), 0,
+    // The final pass runs in chunks of at most 32 tokens whatever the map pass uses: its
+    // workgroup then fits twice per CU (54 KB of LDS and 127 VGPRs at d = 96), and the
+    // segment maps it starts from do not depend on either pass's chunking.
+    constexpr int CF = CH < 32 ? CH : 32;
+    VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT), 0,
                st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
   } else {
     if (P > 1) {
