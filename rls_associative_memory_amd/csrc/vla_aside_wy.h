@@ -69,8 +69,8 @@ __global__ void __launch_bounds__((AwyCfg<D, TERMS>::NT))
 __attribute__((amdgpu_waves_per_eu(awy_waves_per_simd<D, TERMS>())))
 k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
            const bf16_t *__restrict__ u, const float *__restrict__ A0,
-           const float *__restrict__ nk0, float *__restrict__ alpha, float *__restrict__ rkden,
-           float *__restrict__ A_final, float *__restrict__ n_final, int64_t T, int64_t L,
+           float *__restrict__ nk, float *__restrict__ alpha, float *__restrict__ rkden,
+           float *__restrict__ A_final, int64_t T, int64_t L,
            int64_t P, float eps) {
   using C = AwyCfg<D, TERMS>;
   constexpr int NW = C::NW, NT = C::NT, CH = C::C, NTM = C::NTERM;
@@ -103,9 +103,12 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
       for (int r = 0; r < 4; ++r) At[it][r] = a0[(16 * it + 4 * gq + r) * D + 16 * w + li];
   }
-  // Readout normaliser n (sum of phi(k) before the chunk), double buffered in LDS: chunk
-  // number c reads nbuf[c & 1] and its update is written to nbuf[(c & 1) ^ 1].
-  for (int f = tid; f < D; f += NT) sh.nbuf[0][f] = nk0[(s * P + p) * D + f];
+  // Readout normaliser from the segment start (sum of phi(k) over the segment's tokens before
+  // the chunk), double buffered in LDS: chunk number c reads nbuf[c & 1] and its update is
+  // written to nbuf[(c & 1) ^ 1].  The denominators written here omit phi(q) . n_p, n_p the
+  // normaliser at the segment start: the final pass adds it once the segment sums written at
+  // the end (nk) have been scanned.
+  for (int f = tid; f < D; f += NT) sh.nbuf[0][f] = 0.f;
 
   // Staging: thread tid loads token tid / (D/8), features (tid % (D/8)) * 8 of u and k (q is
   // read only by the denominator waves, straight from memory into registers).
@@ -551,12 +554,12 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     }
   }
 
-  if (n_final != nullptr && p == P - 1) {
-    // n after the segment's last chunk (chunk c writes nbuf[(c & 1) ^ 1]), before any reuse
-    // of the LDS below.
+  {
+    // the segment's sum of phi(k) (chunk c writes nbuf[(c & 1) ^ 1]), before any reuse of the
+    // LDS below
     __syncthreads();
     const int nch = static_cast<int>((te - tb + CH - 1) / CH);
-    for (int f = tid; f < D; f += NT) n_final[s * D + f] = sh.nbuf[nch & 1][f];
+    for (int f = tid; f < D; f += NT) nk[(s * P + p) * D + f] = sh.nbuf[nch & 1][f];
   }
   if (A_final != nullptr && p == P - 1) {
     // Symmetrise through LDS: A_T <- (A + A^T) / 2.

@@ -118,7 +118,8 @@ __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, int64_t i, float x
 }
 
 // ------------------------------------------------------------------------------------
-// k_gram: Gram_p = sum_{t in segment p} u_t u_t^T, nk_p = sum phi(k_t)   (segments 0..P-2)
+// k_gram: Gram_p = sum_{t in segment p} u_t u_t^T (segments 0..P-2) and, for fp32 inputs,
+// nk_p = sum phi(k_t) (for bf16 inputs the A side forms these sums from the keys it stages)
 // bf16 inputs: v_mfma_f32_16x16x32_bf16 on the raw inputs (every product exact in fp32);
 // fp32 inputs: v_mfma_f32_16x16x4_f32.  Tokens are staged 64 at a time, transposed and
 // packed so each lane's MFMA operand is one 16-byte LDS read; the next block's 16-byte
@@ -146,6 +147,7 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
   constexpr int TPW = (NTILE + 3) / 4;
   constexpr int TB = 64;
   constexpr bool BF = sizeof(TIn) == 2;
+  constexpr bool NEEDK = !BF;          // phi(k) sums here only for fp32 inputs
   using IO = io<TIn>;
   using vec_t = typename IO::vec_t;
   constexpr int VW = IO::kVec;
@@ -188,7 +190,7 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
       const int c = ui % TB, f0 = (ui / TB) * VW;
       const bool ok = c < nt;
       pu[i] = ok ? *reinterpret_cast<const vec_t *>(us + (t0 + c) * D + f0) : vec_t{};
-      pk[i] = ok ? *reinterpret_cast<const vec_t *>(ks + (t0 + c) * D + f0) : vec_t{};
+      if constexpr (NEEDK) pk[i] = ok ? *reinterpret_cast<const vec_t *>(ks + (t0 + c) * D + f0) : vec_t{};
     }
   };
   prefetch(tb);
@@ -212,11 +214,13 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
 #pragma unroll
         for (int e = 0; e < VW; ++e) sUf[c / 4][f0 + e][c % 4] = x[e];
       }
-      float kx[VW];
-      IO::unpack(pk[i], kx);
-      if (c < nt)
+      if constexpr (NEEDK) {
+        float kx[VW];
+        IO::unpack(pk[i], kx);
+        if (c < nt)
 #pragma unroll
-        for (int e = 0; e < VW; ++e) nka[i][e] += phi(kx[e]);
+          for (int e = 0; e < VW; ++e) nka[i][e] += phi(kx[e]);
+      }
     }
     __syncthreads();
     if (t0 + TB < te) prefetch(t0 + TB);
@@ -260,6 +264,7 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
     }
   }
   // phi(k) sums: lanes of a wave share the feature block and differ in the token.
+  if constexpr (NEEDK)
 #pragma unroll
   for (int i = 0; i < PU; ++i) {
     const int f0 = ((tid + 256 * i) / TB) * VW;
@@ -278,7 +283,7 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
 template <int D>
 __global__ void __launch_bounds__(256)
 k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0,
-         const float *__restrict__ Minit, const float *__restrict__ n0) {
+         const float *__restrict__ Minit, const float *__restrict__ n0, int with_n) {
   const int64_t s = blockIdx.x;
   const int e = blockIdx.y * 256 + threadIdx.x;
   if (e < D * D) {
@@ -299,7 +304,7 @@ k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0
       }
     }
   }
-  if (blockIdx.y == 0 && threadIdx.x < D) {
+  if (with_n && blockIdx.y == 0 && threadIdx.x < D) {
     const double init = n0 != nullptr ? static_cast<double>(n0[s * D + threadIdx.x]) : 0.0;
     float *base = nk + s * P * D + threadIdx.x;
     double acc = 0.0;
@@ -1073,10 +1078,30 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
 template <int D>
 __global__ void __launch_bounds__(D / 16 * kWave)
 k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P,
-          const float *__restrict__ S0) {
+          const float *__restrict__ S0, float *__restrict__ nk, const float *__restrict__ n0,
+          float *__restrict__ n_final) {
   constexpr int NFT = D / 16;
   __shared__ __attribute__((aligned(16))) float Xs[2][D / 4][16][4];  // S^T[f'][row], f' % 4 minor
   const int64_t s = blockIdx.x;
+  // bf16 inputs: the readout normaliser at every segment start, n_p = n_0 + sum_{p' < p} nk_p'
+  // (nk_p' = the sum of phi(k) over segment p', formed by the A side), in place, in fp64
+  // sums, and n_T when wanted.
+  if (nk != nullptr && blockIdx.y == 0 && threadIdx.x < D) {
+    const int f = threadIdx.x;
+    double acc = n0 != nullptr ? static_cast<double>(n0[s * D + f]) : 0.0;
+    float *base = nk + s * P * D + f;
+    for (int64_t p0 = 0; p0 < P; p0 += 16) {
+      float g[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) g[i] = (p0 + i < P) ? base[(p0 + i) * D] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (p0 + i < P) base[(p0 + i) * D] = static_cast<float>(acc);
+        acc += g[i];
+      }
+    }
+    if (n_final != nullptr) n_final[s * D + f] = static_cast<float>(acc);
+  }
   const int rt = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, gq = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1168,8 +1193,9 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                static_cast<int64_t>(D) * D);
     VLA_LAUNCH("k_inv", (k_inv<D>), dim3(S, 1), dim3(256), 0, st, miw, int64_t(1));
   }
+  constexpr bool BF = sizeof(TIn) == 2;  // bf16: the A side forms the segment sums of phi(k)
   VLA_LAUNCH("k_prefix", (k_prefix<D>), gmat, dim3(256), 0, st, Mw, nkw, pl.P, pr.lambda0,
-             sio.A0 != nullptr ? static_cast<const float *>(miw) : nullptr, sio.n0);
+             sio.A0 != nullptr ? static_cast<const float *>(miw) : nullptr, sio.n0, BF ? 0 : 1);
   VLA_LAUNCH("k_inv", (k_inv<D>), dim3(S, P), dim3(256), 0, st, Mw, pl.P);
   if (sio.A0 != nullptr) {  // the first segment starts from A_0 itself
     VLA_LAUNCH("k_sym_copy", (k_sym_copy<D>), gmat, dim3(256), 0, st, sio.A0, Mw,
@@ -1182,10 +1208,10 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // which two-term operands, 16 significant bits, cannot absorb).
     if (sio.A0 == nullptr && pr.lambda0 < static_cast<float>(D) / 256.0f) {
       VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 3>), dim3(S, P), dim3(AwyCfg<D, 3>::NT), 0, st, qq,
-                 kk, uu, Mw, nkw, alw, rdw, A_final, n_final, pl.T, pl.L, pl.P, pr.eps);
+                 kk, uu, Mw, nkw, alw, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
     } else {
       VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2>), dim3(S, P), dim3(AwyCfg<D, 2>::NT), 0, st, qq,
-                 kk, uu, Mw, nkw, alw, rdw, A_final, n_final, pl.T, pl.L, pl.P, pr.eps);
+                 kk, uu, Mw, nkw, alw, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
     }
   } else {
     using AC = AsideCfg<D>;
@@ -1199,16 +1225,16 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, P - 1),
                  dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
-                 S_final, pl.T, pl.L, pl.P);
+                 S_final, static_cast<const float *>(nullptr), pl.T, pl.L, pl.P);
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
-               s0w, pl.P, sio.S0);
+               s0w, pl.P, sio.S0, nkw, sio.n0, n_final);
     // The final pass runs in chunks of at most 32 tokens whatever the map pass uses: its
     // workgroup then fits twice per CU (54 KB of LDS and 127 VGPRs at d = 96), and the
     // segment maps it starts from do not depend on either pass's chunking.
     constexpr int CF = CH < 32 ? CH : 32;
     VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT), 0,
-               st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, pl.T, pl.L, pl.P);
+               st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, nkw, pl.T, pl.L, pl.P);
   } else {
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),
@@ -1216,7 +1242,8 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                  S_final, pl.T, pl.L, pl.P);
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
-               s0w, pl.P, sio.S0);
+               s0w, pl.P, sio.S0, static_cast<float *>(nullptr), static_cast<const float *>(nullptr),
+               static_cast<float *>(nullptr));
     VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P),
                dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final,
                pl.T, pl.L, pl.P);

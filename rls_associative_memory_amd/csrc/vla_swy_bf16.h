@@ -57,7 +57,8 @@ struct SwbLds {
   uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_tt (final pass)
   uint16_t KaO[2][C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // -Ka_ba of each step
   uint16_t QaO[2][FINAL && C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // Qa_ba (final pass)
-  float Kd[C::NCT][16][20];                   // -Ka_b transposed, fp32, for the block inverses
+  float Kd[C::NCT][16][16];                   // -Ka_b transposed, fp32, for the block inverses
+  alignas(16) uint16_t nst[FINAL ? 2 : 1][FINAL ? D : 8];   // normaliser at the segment start, two terms
   float rk[CH];                               // 1 / ||k||
   float rden[CH];                             // 1 / readout denominator
 };
@@ -67,7 +68,8 @@ __global__ void __launch_bounds__((SwbCfg<D, CH, FINAL>::NT))
 k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
        const float *__restrict__ alpha, const float *__restrict__ rkden,
        const float *__restrict__ s0, float *__restrict__ pib, bf16_t *__restrict__ out,
-       float *__restrict__ S_final, int64_t T, int64_t L, int64_t P) {
+       float *__restrict__ S_final, const float *__restrict__ nstart, int64_t T, int64_t L,
+       int64_t P) {
   using C = SwbCfg<D, CH, FINAL>;
   constexpr int NT = C::NT, NCT = C::NCT, NFT = C::NFT, NKS = C::NKS;
   constexpr int TQ = SwbLds<D, CH, FINAL>::QR * C::LDF;
@@ -153,6 +155,14 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     if constexpr (FINAL) pden = rc[toff + 1];
   };
   prefetch(tb, tid);
+  if constexpr (FINAL) {  // phi(q) . n_p completes the A side's denominators (see below)
+    for (int f = tid; f < D; f += NT) {
+      uint16_t h, l;
+      split2_1(nstart[(s * P + p) * D + f], h, l);
+      sh.nst[0][f] = h;
+      sh.nst[1][f] = l;
+    }
+  }
 
   for (int64_t c0 = tb; c0 < te; c0 += CH) {
     const int m = static_cast<int>(std::min<int64_t>(CH, te - c0));
@@ -213,7 +223,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     }
     if (tid < CH) {
       sh.rk[tid] = tid < m ? prk : 0.f;
-      if constexpr (FINAL) sh.rden[tid] = tid < m ? 1.0f / pden : 0.f;
+      if constexpr (FINAL) sh.rden[tid] = tid < m ? pden : 1.f;  // completed below
     }
     // Every prefetched register counts as used here, in every thread (lanes that stage nothing
     // included), so no load is still pending when the next prefetch reuses the registers: the
@@ -337,6 +347,34 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
             uint4 *dst = reinterpret_cast<uint4 *>(&sh.InvS[term][ct][j][0]);
             dst[0] = make_uint4(w[0][term], w[1][term], w[2][term], w[3][term]);
             dst[1] = make_uint4(w[4][term], w[5][term], w[6][term], w[7][term]);
+          }
+        }
+      }
+    }
+    if constexpr (FINAL) {
+      // The A side's denominators count the normaliser from the segment start only; with n_p
+      // the normaliser at the segment start,  den_c = phi(q_c) . n_p + (A side's value): one
+      // product over features per token tile (n_p in column 0 of the B operand, both in two
+      // bf16 terms), token tile ct on wave NWT - 1 - ct, whose tile job above is a light one
+      // when there are waves to spare.
+      for (int ct = C::NWT - 1 - wave; ct < NCT; ct += C::NWT) {
+        f4_t part[NKS];
+#pragma unroll
+        for (int ksl = 0; ksl < NKS; ++ksl) {
+          const int fa = 32 * ksl + 4 * gq;
+          const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
+          Split2 b = ld2_4x2(&sh.nst[0][fa], &sh.nst[0][fa + 16], D);
+          if (li != 0) b = Split2{bf16x8_t{}, bf16x8_t{}};
+          part[ksl] = mm2_ss(a, b, f4_zero());
+        }
+        f4_t acc = part[0];
+#pragma unroll
+        for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
+        if (li == 0) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 16 * ct + 4 * gq + r;
+            sh.rden[c] = 1.0f / (sh.rden[c] + acc[r]);
           }
         }
       }
