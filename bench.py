@@ -128,7 +128,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="long_t131072_d96")
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default long_t131072_d96; mqar_t512_d32 for --mode backward)")
     ap.add_argument("--path", default="auto", choices=["auto", "seq", "chunk"])
     ap.add_argument("--chunk", type=int, default=-1, help="chunk length (-1: the workload's)")
     ap.add_argument("--cpu-tokens", type=int, default=32768,
@@ -142,6 +143,9 @@ def parse():
                          "compare: VLA, VLA with u = 0 and linear attention on the same inputs; "
                          "ablation: growth of the state-transition product, unit vs raw gain; "
                          "backward: gradients of every input (default workload mqar_t512_d32)")
+    ap.add_argument("--bw-seq-steps", type=int, default=1,
+                    help="--mode backward on time segments: calls of the one-segment-per-stream path "
+                         "timed beside it (0: none)")
     ap.add_argument("--decode-path", default="decode", choices=["decode", "seq"],
                     help="path of the T = 1 calls in --mode decode")
     ap.add_argument("--graph", action="store_true",
@@ -238,8 +242,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    if args.mode == "backward" and args.workload == "long_t131072_d96":
-        args.workload = "mqar_t512_d32"  # the sequential backward suits many short streams
+    if args.workload is None:
+        args.workload = "mqar_t512_d32" if args.mode == "backward" else "long_t131072_d96"
     w = get_workload(args.workload)
     if args.mode == "backward":
         return backward_bench(args, w)
@@ -622,8 +626,12 @@ def compare_bench(args, w):
 
 def backward_bench(args, w):
     """vla_backward over a whole workload (random cotangents for out, S_T, A_T, n_T): one
-    step is one call.  Executed work per token*head: the forward replay (12 d^2) and the
-    reverse sweep (28 d^2: 14 matrix-vector products and rank-1 updates of d x d)."""
+    step is one call, on --path (auto: time segments for few long streams, else one segment
+    per stream).  When the call runs on time segments, the one-segment-per-stream call is
+    timed beside it (--bw-seq-steps calls, after one warm-up).  Work per token*head is counted
+    as the kernels execute it, two flops per multiply-add: the forward replay 12 d^2, the
+    reverse sweep 27 d^2 and, on time segments, the du correction 2 d^2 (the segment maps'
+    10 d^2 and the chunked forward passes are left out of the count)."""
     import torch
     from rls_associative_memory_amd import vla
     from rls_associative_memory_amd.inputs import upload_inputs
@@ -637,16 +645,37 @@ def backward_bench(args, w):
     dS = torch.randn(mat, generator=g, device=dev)
     dA = torch.randn(mat, generator=g, device=dev)
     dn = torch.randn((w.B, w.H, w.d), generator=g, device=dev)
-    ws = torch.empty(vla.backward_workspace_size(tuple(q.shape), q.dtype), dtype=torch.uint8, device=dev)
-    ms, kernels = _time_calls(lambda: vla.backward(q, k, v, u, w.lambda0, d_out, dS, dA, dn, eps=w.eps,
-                                                   workspace=ws), args.steps, args.warmup)
+    shape = tuple(q.shape)
     tokens = w.B * w.H * w.T
-    k_tot, k_n = kernels.get("vla_backward_kernel", (0.0, 1))
-    kernel_ms = k_tot / max(k_n, 1)
-    # replay 12 d^2 + reverse 28 d^2 (rank-1 updates and matrix-vector products) per token*head
-    flops = (40 * w.d * w.d) * tokens
-    achieved = flops / (kernel_ms * 1e-3) / 1e12 if kernel_ms else 0.0
-    print(f"[bench] backward {w.name}: {ms:.3f} ms/call (kernel {kernel_ms:.3f} ms)", file=sys.stderr, flush=True)
+
+    def run(path, steps, warmup):
+        ws = torch.empty(vla.backward_workspace_size(shape, q.dtype, path=path), dtype=torch.uint8, device=dev)
+        ms, kernels = _time_calls(lambda: vla.backward(q, k, v, u, w.lambda0, d_out, dS, dA, dn, eps=w.eps,
+                                                       workspace=ws, path=path), steps, warmup)
+        del ws
+        torch.cuda.empty_cache()
+        return ms, kernels
+
+    ms, kernels = run(args.path, args.steps, args.warmup)
+    segmented = "k_bw_dsmap" in kernels or "k_bw_fix" in kernels
+    print(f"[bench] backward {w.name} ({'time segments' if segmented else 'one segment per stream'}): "
+          f"{ms:.3f} ms/call", file=sys.stderr, flush=True)
+    for kn, (tot, cnt) in sorted(kernels.items(), key=lambda kv: -kv[1][0]):
+        print(f"[bench]   kernel {kn:16s} {tot / max(cnt, 1):9.3f} ms/launch x {cnt}", file=sys.stderr, flush=True)
+    d2 = w.d * w.d
+    flops = (12 + 27) * d2 * tokens
+    if segmented:
+        flops += 2 * d2 * tokens  # the segment maps' 10 d^2 (not on the first segment) are not counted
+    achieved = flops / (ms * 1e-3) / 1e12
+    seq = None
+    if segmented and args.bw_seq_steps > 0:
+        seq_ms, seq_k = run("seq", args.bw_seq_steps, 1)
+        print(f"[bench] backward {w.name} (one segment per stream): {seq_ms:.3f} ms/call", file=sys.stderr,
+              flush=True)
+        seq = {"ms_per_call": round(seq_ms, 3), "calls": args.bw_seq_steps,
+               "tokens_heads_per_s": tokens / (seq_ms * 1e-3),
+               "kernels_ms": {kn: round(tot / max(cnt, 1), 3) for kn, (tot, cnt) in seq_k.items()},
+               "speedup_of_segments": round(seq_ms / ms, 2)}
     line = {
         "metric": "VLA backward (dq, dk, dv, du, dlambda0) tokens·heads/sec at 1 MI355X",
         "value": tokens / (ms * 1e-3),
@@ -661,10 +690,12 @@ def backward_bench(args, w):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "input_dtype": w.dtype,
-                   "path": "seq"},
+                   "path": "segments" if segmented else "seq"},
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4), "traffic": None,
-                     "kernel": "vla_backward_kernel", "kernel_ms": round(kernel_ms, 4)},
+                     "scope": "whole vla_backward call, executed flops (see the docstring)"},
+        "kernels_ms": {kn: round(tot / max(cnt, 1), 3) for kn, (tot, cnt) in kernels.items()},
+        "sequential": seq,
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

@@ -403,13 +403,42 @@ vla_status_t vla_linear_attention(const void *q, const void *k, const void *v, v
   return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
 }
 
+// The backward's segmentation: chunk 0 = one segment per stream (VLA_PATH_SEQ), else the
+// chunked path's segments (VLA_PATH_CHUNK).  AUTO splits time when few streams would leave most
+// of the machine idle and the split gives at least four segments per stream.
+vla_status_t resolve_backward(const vla_desc_t *desc, const vla::Problem &p, int *chunk) {
+  if (desc->gain != VLA_GAIN_UNIT) return VLA_ERROR_NOT_SUPPORTED;
+  int c = desc->chunk;
+  switch (desc->path) {
+    case VLA_PATH_SEQ:
+      *chunk = 0;
+      return VLA_SUCCESS;
+    case VLA_PATH_CHUNK:
+      if (c == 0) c = vla::chunk_default(p);
+      if (!vla::chunk_supported(p, c)) return VLA_ERROR_NOT_SUPPORTED;
+      *chunk = c;
+      return VLA_SUCCESS;
+    case VLA_PATH_AUTO: {
+      if (c == 0) c = vla::chunk_default(p);
+      int64_t L = 0, P = 0;
+      if (p.streams < 128 && vla::chunk_supported(p, c)) vla::chunk_segments(p, c, &L, &P);
+      *chunk = P >= 4 ? c : 0;
+      return VLA_SUCCESS;
+    }
+    default:
+      return VLA_ERROR_NOT_SUPPORTED;
+  }
+}
+
 vla_status_t vla_backward_workspace_size(const vla_desc_t *desc, size_t *bytes) {
   if (bytes == nullptr) return VLA_ERROR_INVALID_VALUE;
   vla_status_t st = check_desc(desc);
   if (st != VLA_SUCCESS) return st;
-  if ((desc->path != VLA_PATH_AUTO && desc->path != VLA_PATH_SEQ) || desc->gain != VLA_GAIN_UNIT)
-    return VLA_ERROR_NOT_SUPPORTED;
-  *bytes = vla::backward_workspace_bytes(make_problem(desc, 1.0f));
+  const vla::Problem p = make_problem(desc, 1.0f);
+  int chunk = 0;
+  st = resolve_backward(desc, p, &chunk);
+  if (st != VLA_SUCCESS) return st;
+  *bytes = vla::backward_workspace_bytes(p, chunk);
   return VLA_SUCCESS;
 }
 
@@ -423,13 +452,14 @@ vla_status_t vla_backward(const void *q, const void *k, const void *v, const voi
       dq == nullptr || dk == nullptr || dv == nullptr || du == nullptr)
     return VLA_ERROR_INVALID_VALUE;
   if (!(lambda0 > 0.0f) || !std::isfinite(lambda0)) return VLA_ERROR_INVALID_VALUE;
-  if ((desc->path != VLA_PATH_AUTO && desc->path != VLA_PATH_SEQ) || desc->gain != VLA_GAIN_UNIT)
-    return VLA_ERROR_NOT_SUPPORTED;
+  const vla::Problem p = make_problem(desc, lambda0);
+  int chunk = 0;
+  st = resolve_backward(desc, p, &chunk);
+  if (st != VLA_SUCCESS) return st;
   const void *ptrs[] = {q, k, v, u, d_out, dS_T, dA_T, dn_T, dq, dk, dv, du, dlambda0};
   for (const void *x : ptrs)
     if (!aligned16(x)) return VLA_ERROR_NOT_SUPPORTED;
-  const vla::Problem p = make_problem(desc, lambda0);
-  const size_t need = vla::backward_workspace_bytes(p);
+  const size_t need = vla::backward_workspace_bytes(p, chunk);
   void *ws = nullptr;
   if (desc->workspace != nullptr) {
     if (desc->workspace_bytes < need) return VLA_ERROR_INVALID_VALUE;
@@ -454,7 +484,7 @@ vla_status_t vla_backward(const void *q, const void *k, const void *v, const voi
     if (st != VLA_SUCCESS) return st;
   }
   vla::BackwardIO io{q, k, v, u, d_out, dS_T, dA_T, dn_T, dq, dk, dv, du, dlambda0};
-  const hipError_t err = vla::launch_backward(p, io, ws, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t err = vla::launch_backward(p, chunk, io, ws, reinterpret_cast<hipStream_t>(stream));
   return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
 }
 

@@ -4,29 +4,47 @@
 //   khat = k / ||k||, z = A u, delta = 1 + u.z, A' = A - z z^T / delta,
 //   y = A' khat, ahat = y / ||y||, r = v - S khat, S' = S + r ahat^T,
 //   n' = n + phi(k), o = S' phi(q) / (n'.phi(q) + eps)
-// Reverse of one token, with the upstream gradients dS, dA (of the state after the token),
-// dn and do:
+// Reverse of one token, with the cotangents dS, dn of the state after the token and do:
 //   dnum = do / den, dden = -(do.o) / den, dS += dnum phi(q)^T, dphi(q) = S'^T dnum + dden n',
 //   dn += dden phi(q), dphi(k) = dn,
 //   dr = dS ahat, dahat = dS^T r, dv = dr, dS -= dr khat^T, dkhat = -S^T dr (S before),
-//   dy = (dahat - ahat (ahat.dahat)) / ||y||, dA += dy khat^T, dkhat += A' dy,
-//   dz = -(dA + dA^T) z / delta + ddelta u, ddelta = z^T dA z / delta^2, du = ddelta z,
-//   dA += dz u^T, du += A^T dz (A before; A is symmetric), dk += (dkhat - khat (khat.dkhat)) / ||k||
-// dlambda0 uses the closed form A_t = (lambda0 I + sum_{s<=t} u_s u_s^T)^{-1} (Sherman-Morrison
-// tracks it exactly, VLA summary §2.2), so dA_t / dlambda0 = -A_t^2 and lambda0 reaches the
-// loss through y_t = A_t khat_t and the cotangent of A_T only:
-//   dlambda0 = -sum_t (A_t dy_t) . y_t - <dA_T, A_T^2>
-// Each term is weighted by A_t^2, which shrinks along the sequence; the equal quantity
-// -tr(dA_0) / lambda0^2 of the reverse sweep is a small difference of large fp32 terms.
+//   dy = (dahat - ahat (ahat.dahat)) / ||y||, w = A' dy, dkhat += w,
+//   dk = (dkhat - khat (khat.dkhat)) / ||k|| + dn phi'(k).
+// The inverse penalty needs no cotangent of its own.  Sherman-Morrison keeps
+// A_t = (lambda0 I + sum_{s<=t} u_s u_s^T)^{-1} exactly (VLA summary §2.2), and A_t reaches the
+// loss only through y_t = A_t khat_t and the final state.  With dA_t/dX = -A_t (dX) A_t for
+// X = lambda0 I + sum u u^T, the cotangent of u_s and of lambda0 collapse to
+//   du_s = -2 R_s u_s,    dlambda0 = -tr R_0,
+//   R_s = sum_{t>=s} (w_t y_t^T + y_t w_t^T) / 2 + A_T sym(dA_T) A_T,   w_t = A_t dy_t,
+// a suffix sum of rank-2 terms (the step-by-step adjoint of the Sherman-Morrison update gives
+// the same values; only the symmetric part of a cotangent of A reaches u or lambda0).
 //
-// One workgroup of 512 threads per stream.  Thread (i, p) = (tid / 16, tid % 16) holds rows
-// i + 32 a and column pairs 2 p + 32 b of S, A, dS and dA in registers (the layout of the
-// decode kernel), so row sums are 16-lane shuffles and column sums go through one LDS pass
-// over the eight waves in a fixed order (deterministic).  A forward replay writes each
-// token's vectors (khat, z, ahat, r, phi(q), o and four scalars) and the state after every
-// 32nd token to the workspace; the reverse sweep undoes the rank-1 updates token by token
-// (S -= r ahat^T, A += z z^T / delta) and reloads the exact state at every checkpoint, so
-// rounding cannot drift over more than 32 steps.
+// Time segments.  dS obeys dS_{t-1} = (dS_t + dnum_t phi(q_t)^T)(I - ahat_t khat_t^T), affine in
+// dS_t with coefficients the forward fixes, so a segment maps the cotangent at its end E to the
+// one at its start as  E Lmap + Bmap  (Lmap = the segment's forward map, transposed), and the
+// maps compose; dn is a suffix sum and so is R.  Passes, every one parallel over (stream,
+// segment) except the two scans:
+//   (chunked forward passes: S, A, n at every segment start)
+//   k_bw_replay   the forward token by token from the segment start: per-token vectors and the
+//                 state at every 32nd token (and the segment's last)
+//   k_bw_dsmap    per segment from the end: (Lmap, Bmap) and the segment's sum of dden phi(q)
+//   scan          dS and dn at every segment end (reverse order, so the forward scan applies)
+//   k_bw_grad     per segment from the end, the true dS and dn: dq, dk, dv, du with R local to
+//                 the segment, the segment's R sum and its trace
+//   scan          R at every segment end (suffix sums, the final-state term first)
+//   k_bw_fix      du_t -= 2 R_end u_t over each segment's tokens
+//   k_bw_lambda   dlambda0 = -(tr of every segment's R sum + tr of the final-state term)
+// With one segment per stream the pipeline is replay, grad (R starting from the final-state
+// term) and lambda.
+//
+// Layout of the per-token kernels: one workgroup of 512 threads per segment.  Thread (i, p) =
+// (tid / 16, tid % 16) holds rows i + 32 a and column pairs 2 p + 32 b of each d x d matrix in
+// registers, so row sums are 16-lane shuffles and column sums go through one LDS pass over the
+// eight waves in a fixed order (deterministic).  The reverse sweep undoes the rank-1 updates
+// token by token (S -= r ahat^T, A += z z^T / delta) and reloads the exact state at every
+// checkpoint, so rounding cannot drift over more than 32 steps.
+
+#include <algorithm>
 
 #include "vla_common.h"
 #include "vla_internal.h"
@@ -35,91 +53,95 @@ namespace vla {
 namespace {
 
 constexpr int BW_NT = 512;
+constexpr int BW_NW = BW_NT / kWave;
 constexpr int BW_CK = 32;  // tokens between state checkpoints
 constexpr int BW_NS = 8;   // scalar slots per token record
 
 template <int D>
 struct BwCfg {
-  static constexpr int RG = 32, R = D / RG, NB = D / 32, NW = BW_NT / kWave;
+  static constexpr int R = D / 32, NB = D / 32;
   static constexpr int REC = 6 * D + BW_NS;  // khat, z, ahat, r, phi(q), o, scalars
 };
 
-// Sum over each 16-lane row (DPP, no LDS round trip); every lane of the row gets the sum.
-__device__ __forceinline__ float bw_sum16(float x) { return row_sum16(x); }
-__device__ __forceinline__ float bw_wave_sum(float x) { return wave_sum(x); }
 __device__ __forceinline__ float bw_cv(float x) { return x; }
 __device__ __forceinline__ float bw_cv(bf16_t x) { return bf16_to_f32(x.bits); }
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
 
+// Sum over the block's d-vector x . y of LDS arrays, computed redundantly by every wave (no
+// barrier, the same value in every lane of every wave).
 template <int D>
-struct BwShared {
-  float kr[D], u[D], v[D], fq[D], fk[D], n[D];  // raw k, u, v; phi(q), phi(k); normaliser
-  float z[D], g[D], sk[D], y[D];                // forward vectors
-  float kh[D], ah[D], r[D], o[D], dout[D], dnum[D], dah[D], dy[D], dkh[D], dz[D];
-  float dr[D], ady[D], daz[D], datz[D], adz[D], dn[D];
-  float part[2][BwCfg<D>::NW][D];
-  float red[8];
-  float sc[BW_NS];
+__device__ __forceinline__ float bw_dot(const float *x, const float *y, int lane) {
+  float a = 0.f;
+#pragma unroll
+  for (int c = lane; c < D; c += kWave) a = fmaf(x[c], y[c], a);
+  return wave_sum(a);
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_bw_replay: the forward over segment p from its start state (S0seg, A0seg, n0seg at
+// [stream][P]; NULL = the fixed start S = 0, A = I / lambda0, n = 0).  Writes each token's
+// record (khat, z, ahat, r, phi(q), o, delta, ||y||, 1/||k||, den) and the state (S, A) after
+// every 32nd token and after the segment's last token, and n after the segment.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+struct BwRepShared {
+  float kr[D], u[D], v[D], fq[D], fk[D], n[D];
+  float z[D], g[D], sk[D], y[D];
+  float yy[BW_NW];
 };
 
 template <int D, typename TIn>
 __global__ void __launch_bounds__(BW_NT)
-vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
-                    const TIn *__restrict__ u, const TIn *__restrict__ dout,
-                    const float *__restrict__ dS_T, const float *__restrict__ dA_T,
-                    const float *__restrict__ dn_T, float *__restrict__ dq, float *__restrict__ dk,
-                    float *__restrict__ dv, float *__restrict__ du, float *__restrict__ dlambda0,
-                    float *__restrict__ ws, int64_t T, float lambda0, float eps) {
+k_bw_replay(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
+            const TIn *__restrict__ u, const float *__restrict__ S0seg,
+            const float *__restrict__ A0seg, const float *__restrict__ n0seg,
+            float *__restrict__ recs, float *__restrict__ cks, float *__restrict__ n_end,
+            int64_t T, int64_t L, int64_t P, float lambda0, float eps) {
   using C = BwCfg<D>;
   constexpr int R = C::R, NB = C::NB;
-  __shared__ BwShared<D> sh;
-  const int64_t s = blockIdx.x;
+  __shared__ BwRepShared<D> sh;
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = tid >> 4, pj = tid & 15;
   const int64_t NC = (T + BW_CK - 1) / BW_CK;
-  float *rec0 = ws + s * (T * C::REC + NC * 2 * D * D);  // this stream's records
-  float *ck0 = rec0 + T * C::REC;                        // then its checkpoints
-  auto row = [&](int a) { return i + C::RG * a; };
+  float *rec0 = recs + s * T * C::REC;
+  float *ck0 = cks + s * NC * 2 * D * D;
+  auto row = [&](int a) { return i + 32 * a; };
   auto col = [&](int b, int e) { return 2 * pj + 32 * b + e; };
-  // column sums over this thread's rows -> sh.part[slot][wave][c] (lanes 0..15 of a wave)
-  auto col_part = [&](int slot, const float (&p)[NB][2]) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        float x = p[b][e];
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        if (lane < 16) sh.part[slot][w][col(b, e)] = x;
-      }
-  };
-  auto col_total = [&](int slot, int c) {
-    float x = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < C::NW; ++ww) x += sh.part[slot][ww][c];
-    return x;
-  };
 
   float S[R][NB][2], A[R][NB][2];
-  const float il = 1.0f / lambda0;
+  if (S0seg != nullptr) {
+    const float *s0 = S0seg + (s * P + p) * D * D, *a0 = A0seg + (s * P + p) * D * D;
 #pragma unroll
-  for (int a = 0; a < R; ++a)
+    for (int a = 0; a < R; ++a)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        S[a][b][e] = 0.f;
-        A[a][b][e] = row(a) == col(b, e) ? il : 0.f;
+      for (int b = 0; b < NB; ++b) {
+        const float2 sv = *reinterpret_cast<const float2 *>(s0 + row(a) * D + col(b, 0));
+        const float2 av = *reinterpret_cast<const float2 *>(a0 + row(a) * D + col(b, 0));
+        S[a][b][0] = sv.x; S[a][b][1] = sv.y;
+        A[a][b][0] = av.x; A[a][b][1] = av.y;
       }
-  if (tid < D) sh.n[tid] = 0.f;
+  } else {
+    const float il = 1.0f / lambda0;
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          S[a][b][e] = 0.f;
+          A[a][b][e] = row(a) == col(b, e) ? il : 0.f;
+        }
+  }
+  if (tid < D) sh.n[tid] = n0seg != nullptr ? n0seg[(s * P + p) * D + tid] : 0.f;
 
-  // ---------------- forward replay: records and checkpoints ----------------
   // Token t + 1's inputs are loaded (raw, into registers) while token t is processed.
   TIn nk{}, nu{}, nv{}, nq{};
   if (tid < D) {
-    const int64_t tok0 = s * T * D;
+    const int64_t tok0 = (s * T + tb) * D;
     nk = k[tok0 + tid]; nu = u[tok0 + tid]; nv = v[tok0 + tid]; nq = q[tok0 + tid];
   }
-  for (int64_t t = 0; t < T; ++t) {
+  for (int64_t t = tb; t < te; ++t) {
     const int64_t tok = (s * T + t) * D;
     if (tid < D) {
       const float kk = bw_cv(nk);
@@ -128,7 +150,7 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
       sh.v[tid] = bw_cv(nv);
       sh.fq[tid] = phi(bw_cv(nq));
       sh.fk[tid] = phi(kk);
-      if (t + 1 < T) {
+      if (t + 1 < te) {
         nk = k[tok + D + tid]; nu = u[tok + D + tid]; nv = v[tok + D + tid]; nq = q[tok + D + tid];
       }
     }
@@ -146,9 +168,9 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
           gp = fmaf(A[a][b][e], sh.kr[c], gp);
           sp = fmaf(S[a][b][e], sh.kr[c], sp);
         }
-      z[a] = bw_sum16(zp);
-      const float g = bw_sum16(gp);
-      sk[a] = bw_sum16(sp);
+      z[a] = row_sum16(zp);
+      const float g = row_sum16(gp);
+      sk[a] = row_sum16(sp);
       if (pj == 0) {
         sh.z[row(a)] = z[a];
         sh.g[row(a)] = g;
@@ -156,35 +178,35 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
       }
     }
     __syncthreads();
-    if (w == 0) {
-      float kk = 0.f, uz = 0.f, zk = 0.f, nq = 0.f;
-      for (int c = lane; c < D; c += kWave) {
-        kk = fmaf(sh.kr[c], sh.kr[c], kk);
-        uz = fmaf(sh.u[c], sh.z[c], uz);
-        zk = fmaf(sh.z[c], sh.kr[c], zk);
-        nq = fmaf(sh.n[c] + sh.fk[c], sh.fq[c], nq);
-      }
-      kk = bw_wave_sum(kk); uz = bw_wave_sum(uz); zk = bw_wave_sum(zk); nq = bw_wave_sum(nq);
-      if (lane == 0) { sh.red[0] = kk; sh.red[1] = uz; sh.red[2] = zk; sh.red[3] = nq; }
+    // every wave forms the token's scalars itself (no further barrier)
+    const float kk = bw_dot<D>(sh.kr, sh.kr, lane);
+    const float uz = bw_dot<D>(sh.u, sh.z, lane);
+    const float zk = bw_dot<D>(sh.z, sh.kr, lane);
+    float nq = 0.f;
+    for (int c = lane; c < D; c += kWave) nq = fmaf(sh.n[c] + sh.fk[c], sh.fq[c], nq);
+    nq = wave_sum(nq);
+    const float delta = 1.0f + uz;
+    const float rk = kk > 0.f ? rsqrtf(kk) : 0.f;
+    const float czk = zk / delta;
+    const float den = nq + eps;
+    // y = A' khat for this thread's rows, ||y||^2 from row-owner partial sums
+    float yr[R];
+    float yyp = 0.f;
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
+      yr[a] = (sh.g[row(a)] - z[a] * czk) * rk;
+      if (pj == 0) yyp = fmaf(yr[a], yr[a], yyp);
     }
+    yyp = wave_sum(yyp);
+    if (lane == 0) sh.yy[w] = yyp;
+    if (pj == 0)
+#pragma unroll
+      for (int a = 0; a < R; ++a) sh.y[row(a)] = yr[a];
     __syncthreads();
-    const float delta = 1.0f + sh.red[1];
-    const float rk = sh.red[0] > 0.f ? rsqrtf(sh.red[0]) : 0.f;
-    const float czk = sh.red[2] / delta;
-    const float den = sh.red[3] + eps;
-    if (tid < D) {
-      sh.y[tid] = (sh.g[tid] - sh.z[tid] * czk) * rk;
-      sh.n[tid] += sh.fk[tid];
-    }
-    __syncthreads();
-    if (w == 0) {
-      float yy = 0.f;
-      for (int c = lane; c < D; c += kWave) yy = fmaf(sh.y[c], sh.y[c], yy);
-      yy = bw_wave_sum(yy);
-      if (lane == 0) sh.red[4] = yy;
-    }
-    __syncthreads();
-    const float ry = sh.red[4] > 0.f ? rsqrtf(sh.red[4]) : 0.f;
+    float yy = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < BW_NW; ++ww) yy += sh.yy[ww];
+    const float ry = yy > 0.f ? rsqrtf(yy) : 0.f;
     float *rec = rec0 + t * C::REC;
 #pragma unroll
     for (int a = 0; a < R; ++a) {
@@ -199,7 +221,7 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
           S[a][b][e] = fmaf(ra, sh.y[c] * ry, S[a][b][e]);
           np = fmaf(S[a][b][e], sh.fq[c], np);
         }
-      const float num = bw_sum16(np);
+      const float num = row_sum16(np);
       if (pj == 0) {
         rec[3 * D + row(a)] = ra;          // r
         rec[5 * D + row(a)] = num / den;   // o
@@ -210,14 +232,15 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
       rec[D + tid] = sh.z[tid];            // z
       rec[2 * D + tid] = sh.y[tid] * ry;   // ahat
       rec[4 * D + tid] = sh.fq[tid];       // phi(q)
+      sh.n[tid] += sh.fk[tid];             // only this thread reads n[tid] until the barrier
     }
     if (tid == 0) {
       rec[6 * D + 0] = delta;
-      rec[6 * D + 1] = sh.red[4] > 0.f ? sqrtf(sh.red[4]) : 0.f;  // ||y||
+      rec[6 * D + 1] = yy > 0.f ? sqrtf(yy) : 0.f;  // ||y||
       rec[6 * D + 2] = rk;
       rec[6 * D + 3] = den;
     }
-    if (t % BW_CK == BW_CK - 1 || t == T - 1) {
+    if (t % BW_CK == BW_CK - 1 || t == te - 1) {
       float *ck = ck0 + (t / BW_CK) * 2 * D * D;
 #pragma unroll
       for (int a = 0; a < R; ++a)
@@ -228,52 +251,205 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
               make_float2(A[a][b][0], A[a][b][1]);
         }
     }
-    __syncthreads();  // records and checkpoints are re-read by this workgroup's threads
+    __syncthreads();
   }
-  __threadfence_block();
+  if (tid < D) n_end[(s * P + p) * D + tid] = sh.n[tid];
+}
 
-  // ---------------- reverse sweep ----------------
-  float dS[R][NB][2], dA[R][NB][2];
+// ---------------------------------------------------------------------------------------------
+// k_bw_dsmap: segment p = blockIdx.y + 1 (the first segment's map is never needed) from its end
+// with the cotangent E at the end left symbolic: E_start = E Lmap + Bmap, Lmap = prod of
+// (I - ahat khat^T)^T from the last token down, Bmap the same recursion from 0 with the readout
+// terms.  Written to slot P - 1 - p of lb ([stream][P][2][d][d]: Lmap, Bmap) and nd
+// ([stream][P][d]: the segment's sum of dden phi(q)), so that the forward scans, run over the
+// slots, give the cotangents at every segment end.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+struct BwMapShared {
+  float kh[2][D], ah[2][D], fq[2][D], dnum[2][D], x[2][D];
+};
+
+template <int D, typename TIn>
+__global__ void __launch_bounds__(BW_NT)
+k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs, float *__restrict__ lb,
+           float *__restrict__ nd, int64_t T, int64_t L, int64_t P) {
+  using C = BwCfg<D>;
+  constexpr int R = C::R, NB = C::NB;
+  __shared__ BwMapShared<D> sh;
+  const int64_t s = blockIdx.x, p = blockIdx.y + 1;
+  const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
+  const int tid = threadIdx.x, lane = tid & 63, i = tid >> 4, pj = tid & 15;
+  const float *rec0 = recs + s * T * C::REC;
+  auto row = [&](int a) { return i + 32 * a; };
+  auto col = [&](int b, int e) { return 2 * pj + 32 * b + e; };
+
+  float Lm[R][NB][2], Bm[R][NB][2];
 #pragma unroll
   for (int a = 0; a < R; ++a)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int64_t off = s * D * D + row(a) * D + col(b, e);
-        dS[a][b][e] = dS_T != nullptr ? dS_T[off] : 0.f;
-        dA[a][b][e] = dA_T != nullptr ? dA_T[off] : 0.f;
+        Lm[a][b][e] = row(a) == col(b, e) ? 1.f : 0.f;
+        Bm[a][b][e] = 0.f;
       }
-  if (tid < D) sh.dn[tid] = dn_T != nullptr ? dn_T[s * D + tid] : 0.f;
-  double dlam = 0.0;  // -dL/dlambda0 accumulated by thread 0
-  if (dlambda0 != nullptr && dA_T != nullptr) {
-    // <dA_T, A_T^2> with A_T staged in LDS (A is symmetric: (A^2)[r][c] = sum_m A[r][m] A[c][m])
-    __shared__ float As[D][D + 1];
-#pragma unroll
-    for (int a = 0; a < R; ++a)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) As[row(a)][col(b, e)] = A[a][b][e];
+  float ndp = 0.f;  // thread f < d: sum of dden phi(q)_f
+
+  // token t - 1's record is loaded while token t is processed
+  float pk = 0.f, pa = 0.f, pf = 0.f, po = 0.f, pden = 1.f;
+  TIn pdo{};
+  auto load = [&](int64_t t) {
+    const float *rec = rec0 + t * C::REC;
+    if (tid < D) {
+      pk = rec[tid];
+      pa = rec[2 * D + tid];
+      pf = rec[4 * D + tid];
+      po = rec[5 * D + tid];
+      pdo = dout[(s * T + t) * D + tid];
+    }
+    pden = rec[6 * D + 3];
+  };
+  load(te - 1);
+  for (int64_t t = te - 1; t >= tb; --t) {
+    const int buf = static_cast<int>(t & 1);
+    // Double-buffered staging: a thread writes this token's buffer only after the previous
+    // token's barrier, past which nobody reads the buffer two tokens back.
+    if (tid < D) {
+      const float dd = bw_cv(pdo);
+      sh.kh[buf][tid] = pk;
+      sh.ah[buf][tid] = pa;
+      sh.fq[buf][tid] = pf;
+      sh.dnum[buf][tid] = dd / pden;
+      sh.x[buf][tid] = dd * po;
+    }
+    const float den = pden;
+    if (t > tb) load(t - 1);
     __syncthreads();
-    float x = 0.f;
+    float xo = 0.f;
+    for (int c = lane; c < D; c += kWave) xo += sh.x[buf][c];
+    xo = wave_sum(xo);
+    if (tid < D) ndp = fmaf(-xo / den, sh.fq[buf][tid], ndp);
 #pragma unroll
-    for (int a = 0; a < R; ++a)
+    for (int a = 0; a < R; ++a) {
+      const float dn_r = sh.dnum[buf][row(a)];
+      float bp = 0.f, lp = 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          float p2 = 0.f;
-          for (int m = 0; m < D; ++m) p2 = fmaf(As[row(a)][m], As[col(b, e)][m], p2);
-          x = fmaf(dA[a][b][e], p2, x);
+          const int c = col(b, e);
+          Bm[a][b][e] = fmaf(dn_r, sh.fq[buf][c], Bm[a][b][e]);
+          bp = fmaf(Bm[a][b][e], sh.ah[buf][c], bp);
+          lp = fmaf(Lm[a][b][e], sh.ah[buf][c], lp);
         }
-    x = bw_wave_sum(x);
-    if (lane == 0) sh.red[w] = x;
-    __syncthreads();
-    if (tid == 0)
-      for (int ww = 0; ww < C::NW; ++ww) dlam += static_cast<double>(sh.red[ww]);
-    __syncthreads();
+      bp = row_sum16(bp);
+      lp = row_sum16(lp);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int c = col(b, e);
+          Bm[a][b][e] = fmaf(-bp, sh.kh[buf][c], Bm[a][b][e]);
+          Lm[a][b][e] = fmaf(-lp, sh.kh[buf][c], Lm[a][b][e]);
+        }
+    }
   }
+  const int64_t slot = s * P + (P - 1 - p);
+  float *dst = lb + slot * 2 * D * D;
+#pragma unroll
+  for (int a = 0; a < R; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      *reinterpret_cast<float2 *>(dst + row(a) * D + col(b, 0)) = make_float2(Lm[a][b][0], Lm[a][b][1]);
+      *reinterpret_cast<float2 *>(dst + D * D + row(a) * D + col(b, 0)) = make_float2(Bm[a][b][0], Bm[a][b][1]);
+    }
+  if (tid < D) nd[slot * D + tid] = ndp;
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_bw_grad: the reverse sweep over segment p from the true cotangents at its end (Ebuf, ndbuf
+// at slot [stream][P - 1 - p]; NULL = 0), with R starting from Rinit[stream] (NULL = 0).
+// Writes dq, dk, dv, du = -2 R u with this R, the segment's R sum to Wbuf slot P - 1 - p when
+// Wbuf is not NULL, and the trace of the segment's own R sum (sum of w . y) to trw.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+struct BwGradShared {
+  float kh[D], z[D], ah[D], r[D], fq[D], o[D], kr[D], u[D], dout[D];
+  float n[D], dn[D], dr[D], dah[D], w[D], dkh[D];
+  float part[2][BW_NW][D];
+  float sc[BW_NS];
+};
+
+template <int D, typename TIn>
+__global__ void __launch_bounds__(BW_NT)
+k_bw_grad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ u,
+          const TIn *__restrict__ dout, const float *__restrict__ recs,
+          const float *__restrict__ cks, const float *__restrict__ n_end,
+          const float *__restrict__ Ebuf, const float *__restrict__ ndbuf,
+          const float *__restrict__ Rinit, float *__restrict__ dq, float *__restrict__ dk,
+          float *__restrict__ dv, float *__restrict__ du, float *__restrict__ Wbuf,
+          double *__restrict__ trw, int64_t T, int64_t L, int64_t P) {
+  using C = BwCfg<D>;
+  constexpr int R = C::R, NB = C::NB;
+  __shared__ BwGradShared<D> sh;
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = tid >> 4, pj = tid & 15;
+  const int64_t NC = (T + BW_CK - 1) / BW_CK;
+  const float *rec0 = recs + s * T * C::REC;
+  const float *ck0 = cks + s * NC * 2 * D * D;
+  const int64_t slot = s * P + (P - 1 - p);
+  auto row = [&](int a) { return i + 32 * a; };
+  auto col = [&](int b, int e) { return 2 * pj + 32 * b + e; };
+  // column sums over this thread's rows -> sh.part[slot][wave][c] (lanes 0..15 of a wave)
+  auto col_part = [&](int sl, const float (&x)[NB][2]) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float y = x[b][e];
+        y += __shfl_xor(y, 16);
+        y += __shfl_xor(y, 32);
+        if (lane < 16) sh.part[sl][w][col(b, e)] = y;
+      }
+  };
+  auto col_total = [&](int sl, int c) {
+    float y = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < BW_NW; ++ww) y += sh.part[sl][ww][c];
+    return y;
+  };
+  auto load_state = [&](int64_t t, float (&S)[R][NB][2], float (&A)[R][NB][2]) {
+    const float *ck = ck0 + (t / BW_CK) * 2 * D * D;
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float2 sv = *reinterpret_cast<const float2 *>(ck + row(a) * D + col(b, 0));
+        const float2 av = *reinterpret_cast<const float2 *>(ck + D * D + row(a) * D + col(b, 0));
+        S[a][b][0] = sv.x; S[a][b][1] = sv.y;
+        A[a][b][0] = av.x; A[a][b][1] = av.y;
+      }
+  };
+
+  float S[R][NB][2], A[R][NB][2], dS[R][NB][2], Rm[R][NB][2];
+  load_state(te - 1, S, A);
+#pragma unroll
+  for (int a = 0; a < R; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int64_t off = row(a) * D + col(b, e);
+        dS[a][b][e] = Ebuf != nullptr ? Ebuf[slot * D * D + off] : 0.f;
+        Rm[a][b][e] = Rinit != nullptr ? Rinit[s * D * D + off] : 0.f;
+      }
+  if (tid < D) {
+    sh.dn[tid] = ndbuf != nullptr ? ndbuf[slot * D + tid] : 0.f;
+    sh.n[tid] = n_end[(s * P + p) * D + tid];
+  }
+  double trace = 0.0;  // thread 0: sum of w . y over the segment
+
   // Token t - 1's record and inputs are loaded (into registers) while token t is processed.
   float pr[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, psc = 0.f;
   TIn pk{}, pu{}, pdo{}, pq{};
@@ -287,21 +463,10 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
     }
     if (tid < BW_NS) psc = rec[6 * D + tid];
   };
-  load_rev(T - 1);
-  for (int64_t t = T - 1; t >= 0; --t) {
+  load_rev(te - 1);
+  for (int64_t t = te - 1; t >= tb; --t) {
     const int64_t tok = (s * T + t) * D;
-    if (t % BW_CK == BW_CK - 1 && t != T - 1) {  // exact state after token t
-      const float *ck = ck0 + (t / BW_CK) * 2 * D * D;
-#pragma unroll
-      for (int a = 0; a < R; ++a)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const float2 sv = *reinterpret_cast<const float2 *>(ck + row(a) * D + col(b, 0));
-          const float2 av = *reinterpret_cast<const float2 *>(ck + D * D + row(a) * D + col(b, 0));
-          S[a][b][0] = sv.x; S[a][b][1] = sv.y;
-          A[a][b][0] = av.x; A[a][b][1] = av.y;
-        }
-    }
+    if (t % BW_CK == BW_CK - 1 && t != te - 1) load_state(t, S, A);  // exact state after token t
     float qt = 0.f;  // raw q of token t (for dq)
     if (tid < D) {
       sh.kh[tid] = pr[0];
@@ -316,27 +481,20 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
       qt = bw_cv(pq);
     }
     if (tid < BW_NS) sh.sc[tid] = psc;
-    if (t > 0) load_rev(t - 1);
-    __syncthreads();
-    if (w == 0) {
-      float x = 0.f;
-      for (int c = lane; c < D; c += kWave) x = fmaf(sh.dout[c], sh.o[c], x);
-      x = bw_wave_sum(x);
-      if (lane == 0) sh.red[0] = x;
-    }
+    if (t > tb) load_rev(t - 1);
     __syncthreads();
     const float delta = sh.sc[0], ynorm = sh.sc[1], rk = sh.sc[2], den = sh.sc[3];
-    const float dden = -sh.red[0] / den;
-    if (tid < D) sh.dnum[tid] = sh.dout[tid] / den;
-    __syncthreads();
+    const float iden = 1.0f / den;
+    const float dden = -bw_dot<D>(sh.dout, sh.o, lane) * iden;
     // dS += dnum phi(q)^T; column sums S^T dnum and dS^T r; row sums dS ahat
+    float drr[R];
     {
       float p1[NB][2], p2[NB][2];
 #pragma unroll
       for (int b = 0; b < NB; ++b) p1[b][0] = p1[b][1] = p2[b][0] = p2[b][1] = 0.f;
 #pragma unroll
       for (int a = 0; a < R; ++a) {
-        const float dn_r = sh.dnum[row(a)], r_r = sh.r[row(a)];
+        const float dn_r = sh.dout[row(a)] * iden, r_r = sh.r[row(a)];
         float rp = 0.f;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -348,166 +506,299 @@ vla_backward_kernel(const TIn *__restrict__ q, const TIn *__restrict__ k, const 
             p2[b][e] = fmaf(dS[a][b][e], r_r, p2[b][e]);
             rp = fmaf(dS[a][b][e], sh.ah[c], rp);
           }
-        const float dr = bw_sum16(rp);
-        if (pj == 0) sh.dr[row(a)] = dr;
+        drr[a] = row_sum16(rp);
+        if (pj == 0) sh.dr[row(a)] = drr[a];
       }
       col_part(0, p1);
       col_part(1, p2);
     }
     __syncthreads();
-    float dk_acc = 0.f, du_acc = 0.f;
+    float dk_acc = 0.f;
     if (tid < D) {
-      const float fqc = sh.fq[tid];
       const float dphiq = col_total(0, tid) + dden * sh.n[tid];
       dq[tok + tid] = dphiq * dphi(qt);
       sh.dah[tid] = col_total(1, tid);
-      const float dnt = sh.dn[tid] + dden * fqc;  // gradient of n after token t
+      const float dnt = sh.dn[tid] + dden * sh.fq[tid];  // cotangent of n after token t
       sh.dn[tid] = dnt;
       dk_acc = dnt * dphi(sh.kr[tid]);
       dv[tok + tid] = sh.dr[tid];
     }
     __syncthreads();
-    if (w == 0) {
-      float x = 0.f;
-      for (int c = lane; c < D; c += kWave) x = fmaf(sh.ah[c], sh.dah[c], x);
-      x = bw_wave_sum(x);
-      if (lane == 0) sh.red[1] = x;
-    }
-    __syncthreads();
-    if (tid < D) sh.dy[tid] = ynorm > 0.f ? (sh.dah[tid] - sh.ah[tid] * sh.red[1]) / ynorm : 0.f;
-    // S before the token, and dS -= dr khat^T
-#pragma unroll
-    for (int a = 0; a < R; ++a) {
-      const float r_r = sh.r[row(a)], dr_r = sh.dr[row(a)];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int c = col(b, e);
-          S[a][b][e] = fmaf(-r_r, sh.ah[c], S[a][b][e]);
-          dS[a][b][e] = fmaf(-dr_r, sh.kh[c], dS[a][b][e]);
-        }
-    }
-    __syncthreads();
-    // dA += dy khat^T; row sums A dy and dA z; column sums S^T dr (S before) and dA^T z
+    const float ad = bw_dot<D>(sh.ah, sh.dah, lane);
+    const float iy = ynorm > 0.f ? 1.0f / ynorm : 0.f;
+    // S before the token and dS -= dr khat^T; row sums A' dy; column sums S^T dr (S before)
     {
-      float p1[NB][2], p2[NB][2];
+      float p1[NB][2];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) p1[b][0] = p1[b][1] = p2[b][0] = p2[b][1] = 0.f;
+      for (int b = 0; b < NB; ++b) p1[b][0] = p1[b][1] = 0.f;
 #pragma unroll
       for (int a = 0; a < R; ++a) {
-        const float dy_r = sh.dy[row(a)], dr_r = sh.dr[row(a)], z_r = sh.z[row(a)];
-        float ap = 0.f, zp = 0.f;
+        const float r_r = sh.r[row(a)], dr_r = drr[a];
+        float ap = 0.f;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int c = col(b, e);
-            dA[a][b][e] = fmaf(dy_r, sh.kh[c], dA[a][b][e]);
-            ap = fmaf(A[a][b][e], sh.dy[c], ap);
-            zp = fmaf(dA[a][b][e], sh.z[c], zp);
+            const float dyc = (sh.dah[c] - sh.ah[c] * ad) * iy;
+            S[a][b][e] = fmaf(-r_r, sh.ah[c], S[a][b][e]);
+            dS[a][b][e] = fmaf(-dr_r, sh.kh[c], dS[a][b][e]);
+            ap = fmaf(A[a][b][e], dyc, ap);
             p1[b][e] = fmaf(S[a][b][e], dr_r, p1[b][e]);
-            p2[b][e] = fmaf(dA[a][b][e], z_r, p2[b][e]);
           }
-        const float ady = bw_sum16(ap), daz = bw_sum16(zp);
-        if (pj == 0) {
-          sh.ady[row(a)] = ady;
-          sh.daz[row(a)] = daz;
-        }
+        const float wr = row_sum16(ap);
+        if (pj == 0) sh.w[row(a)] = wr;
       }
       col_part(0, p1);
-      col_part(1, p2);
     }
     __syncthreads();
-    if (tid < D) {
-      sh.dkh[tid] = sh.ady[tid] - col_total(0, tid);
-      sh.datz[tid] = col_total(1, tid);
-    }
+    if (tid < D) sh.dkh[tid] = sh.w[tid] - col_total(0, tid);
     __syncthreads();
-    if (w == 0) {
-      float zz = 0.f, kd = 0.f, ly = 0.f;
-      for (int c = lane; c < D; c += kWave) {
-        zz = fmaf(sh.z[c], sh.daz[c], zz);
-        kd = fmaf(sh.kh[c], sh.dkh[c], kd);
-        ly = fmaf(sh.ady[c], sh.ah[c], ly);  // (A_t dy) . ahat; y = ahat ||y||
+    const float kd = bw_dot<D>(sh.kh, sh.dkh, lane);
+    const float wa = bw_dot<D>(sh.w, sh.ah, lane);
+    if (tid == 0) trace += static_cast<double>(wa) * ynorm;
+    // R += (w y^T + y w^T) / 2 (y = ahat ||y||), du = -2 R u, A before the token
+    {
+      const float hy = 0.5f * ynorm;
+#pragma unroll
+      for (int a = 0; a < R; ++a) {
+        const float w_r = sh.w[row(a)], ah_r = sh.ah[row(a)], z_r = sh.z[row(a)];
+        float rp = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int c = col(b, e);
+            Rm[a][b][e] = fmaf(hy, fmaf(w_r, sh.ah[c], ah_r * sh.w[c]), Rm[a][b][e]);
+            rp = fmaf(Rm[a][b][e], sh.u[c], rp);
+            A[a][b][e] += z_r * sh.z[c] / delta;
+          }
+        const float ru = row_sum16(rp);
+        if (pj == 0) du[tok + row(a)] = -2.0f * ru;
       }
-      zz = bw_wave_sum(zz);
-      kd = bw_wave_sum(kd);
-      ly = bw_wave_sum(ly);
-      if (lane == 0) {
-        sh.red[2] = zz;
-        sh.red[3] = kd;
-        dlam += static_cast<double>(ly) * ynorm;
-      }
     }
-    __syncthreads();
-    const float ddelta = sh.red[2] / (delta * delta);
     if (tid < D) {
-      sh.dz[tid] = -(sh.daz[tid] + sh.datz[tid]) / delta + ddelta * sh.u[tid];
-      du_acc = ddelta * sh.z[tid];
-      dk_acc += (sh.dkh[tid] - sh.kh[tid] * sh.red[3]) * rk;
-    }
-    __syncthreads();
-    // A before the token; dA += dz u^T; row sums A dz (A before, symmetric)
-#pragma unroll
-    for (int a = 0; a < R; ++a) {
-      const float z_r = sh.z[row(a)], dz_r = sh.dz[row(a)];
-      float ap = 0.f;
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int c = col(b, e);
-          A[a][b][e] += z_r * sh.z[c] / delta;
-          dA[a][b][e] = fmaf(dz_r, sh.u[c], dA[a][b][e]);
-          ap = fmaf(A[a][b][e], sh.dz[c], ap);
-        }
-      const float adz = bw_sum16(ap);
-      if (pj == 0) sh.adz[row(a)] = adz;
-    }
-    __syncthreads();
-    if (tid < D) {
-      du[tok + tid] = du_acc + sh.adz[tid];
-      dk[tok + tid] = dk_acc;
+      dk[tok + tid] = dk_acc + (sh.dkh[tid] - sh.kh[tid] * kd) * rk;
       sh.n[tid] -= phi(sh.kr[tid]);  // n before the token
     }
     __syncthreads();
   }
-  if (dlambda0 != nullptr && tid == 0) dlambda0[s] = static_cast<float>(-dlam);
+  if (Wbuf != nullptr) {
+    float *dst = Wbuf + slot * D * D;
+    const float *r0 = Rinit != nullptr ? Rinit + s * D * D : nullptr;
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float2 x = make_float2(Rm[a][b][0], Rm[a][b][1]);
+        if (r0 != nullptr) {
+          x.x -= r0[row(a) * D + col(b, 0)];
+          x.y -= r0[row(a) * D + col(b, 1)];
+        }
+        *reinterpret_cast<float2 *>(dst + row(a) * D + col(b, 0)) = x;
+      }
+  }
+  if (tid == 0) trw[s * P + p] = trace;
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_bw_terminal: X = A_T sym(dA_T) A_T per stream (A_T = the state after the last token, from
+// the replay's checkpoint), through the scratch matrix Y = sym(dA_T) A_T.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+k_bw_terminal(const float *__restrict__ cks, const float *__restrict__ dA_T,
+              float *__restrict__ Y, float *__restrict__ X, int64_t T) {
+  const int64_t s = blockIdx.x;
+  const int64_t NC = (T + BW_CK - 1) / BW_CK;
+  const float *AT = cks + s * NC * 2 * D * D + ((T - 1) / BW_CK) * 2 * D * D + D * D;
+  const float *G = dA_T + s * D * D;
+  float *Ys = Y + s * D * D, *Xs = X + s * D * D;
+  for (int e = threadIdx.x; e < D * D; e += 256) {
+    const int r = e / D, c = e % D;
+    float acc = 0.f;
+    for (int m = 0; m < D; ++m) acc = fmaf(0.5f * (G[r * D + m] + G[m * D + r]), AT[m * D + c], acc);
+    Ys[e] = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < D * D; e += 256) {
+    const int r = e / D, c = e % D;
+    float acc = 0.f;
+    for (int m = 0; m < D; ++m) acc = fmaf(AT[r * D + m], Ys[m * D + c], acc);
+    Xs[e] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_bw_fix: du_t -= 2 R_end u_t over 64 tokens of segment p (R_end at Rend slot P - 1 - p), one
+// 32-row slab of R at a time.
+// ---------------------------------------------------------------------------------------------
+template <int D, typename TIn>
+__global__ void __launch_bounds__(256)
+k_bw_fix(const TIn *__restrict__ u, const float *__restrict__ Rend, float *__restrict__ du,
+         int64_t T, int64_t L, int64_t P) {
+  __shared__ float sU[64][D + 1];
+  __shared__ float sR[32][D + 1];
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int64_t t0 = p * L + static_cast<int64_t>(blockIdx.z) * 64;
+  const int64_t te = std::min<int64_t>(std::min<int64_t>(T, p * L + L), t0 + 64);
+  if (t0 >= te) return;
+  const int nt = static_cast<int>(te - t0);
+  const int tid = threadIdx.x, rr = tid & 31, tg = tid >> 5;
+  const float *Rs = Rend + (s * P + (P - 1 - p)) * D * D;
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int j = e / D, c = e % D;
+    sU[j][c] = j < nt ? bw_cv(u[(s * T + t0 + j) * D + c]) : 0.f;
+  }
+  for (int slab = 0; slab < D / 32; ++slab) {
+    __syncthreads();
+    for (int e = tid; e < 32 * D; e += 256) sR[e / D][e % D] = Rs[(32 * slab + e / D) * D + e % D];
+    __syncthreads();
+    for (int j = tg; j < nt; j += 8) {
+      float acc = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) acc = fmaf(sR[rr][c], sU[j][c], acc);
+      du[(s * T + t0 + j) * D + 32 * slab + rr] -= 2.0f * acc;
+    }
+  }
+}
+
+// dlambda0 = -(trace of the final-state term + every segment's sum of w . y)
+template <int D>
+__global__ void __launch_bounds__(64)
+k_bw_lambda(const float *__restrict__ X, const double *__restrict__ trw, float *__restrict__ dlambda0,
+            int64_t P) {
+  const int64_t s = blockIdx.x;
+  double acc = 0.0;
+  for (int64_t j = threadIdx.x; j < P; j += 64) acc += trw[s * P + j];
+  if (X != nullptr)
+    for (int c = threadIdx.x; c < D; c += 64) acc += static_cast<double>(X[s * D * D + c * D + c]);
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (threadIdx.x == 0) dlambda0[s] = static_cast<float>(-acc);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------------------------
+struct BwPlan {
+  int64_t L = 0, P = 1;
+  size_t off_chunk = 0, off_md = 0, off_rec = 0, off_ck = 0, off_nend = 0, off_x = 0, off_y = 0,
+         off_trw = 0;
+  size_t total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+BwPlan make_bw_plan(const Problem &p, int chunk) {
+  BwPlan b;
+  b.L = p.T;
+  b.P = 1;
+  size_t off = 0;
+  if (chunk > 0) {
+    chunk_segments(p, chunk, &b.L, &b.P);
+    if (b.P > 1) {
+      b.off_chunk = 0;
+      off = align256(chunk_workspace_bytes(p, chunk));
+      b.off_md = off;
+      off = align256(off + static_cast<size_t>(p.streams * b.P) * p.d * p.d * sizeof(double));
+    } else {
+      b.L = p.T;
+    }
+  }
+  const size_t S = static_cast<size_t>(p.streams), T = static_cast<size_t>(p.T);
+  const size_t D = static_cast<size_t>(p.d), P = static_cast<size_t>(b.P);
+  const size_t NC = (T + BW_CK - 1) / BW_CK;
+  b.off_rec = off;  off = align256(off + S * T * (6 * D + BW_NS) * 4);
+  b.off_ck = off;   off = align256(off + S * NC * 2 * D * D * 4);
+  b.off_nend = off; off = align256(off + S * P * D * 4);
+  b.off_x = off;    off = align256(off + S * D * D * 4);
+  b.off_y = off;    off = align256(off + S * D * D * 4);
+  b.off_trw = off;  off = align256(off + S * P * 8);
+  b.total = off;
+  return b;
 }
 
 template <int D, typename TIn>
-hipError_t launch_bw_t(const Problem &p, const BackwardIO &io, void *ws, hipStream_t st) {
-  VLA_LAUNCH("vla_backward_kernel", (vla_backward_kernel<D, TIn>), dim3(static_cast<unsigned>(p.streams)),
-             dim3(BW_NT), 0, st, static_cast<const TIn *>(io.q), static_cast<const TIn *>(io.k),
-             static_cast<const TIn *>(io.v), static_cast<const TIn *>(io.u),
-             static_cast<const TIn *>(io.dout), io.dS_T, io.dA_T, io.dn_T, io.dq, io.dk, io.dv, io.du,
-             io.dlambda0, static_cast<float *>(ws), p.T, p.lambda0, p.eps);
+hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void *ws, hipStream_t st) {
+  const BwPlan bp = make_bw_plan(pr, chunk);
+  char *base = static_cast<char *>(ws);
+  float *rec = reinterpret_cast<float *>(base + bp.off_rec);
+  float *ck = reinterpret_cast<float *>(base + bp.off_ck);
+  float *nend = reinterpret_cast<float *>(base + bp.off_nend);
+  float *X = io.dA_T != nullptr ? reinterpret_cast<float *>(base + bp.off_x) : nullptr;
+  float *Y = reinterpret_cast<float *>(base + bp.off_y);
+  double *trw = reinterpret_cast<double *>(base + bp.off_trw);
+  const TIn *q = static_cast<const TIn *>(io.q), *k = static_cast<const TIn *>(io.k);
+  const TIn *v = static_cast<const TIn *>(io.v), *u = static_cast<const TIn *>(io.u);
+  const TIn *dout = static_cast<const TIn *>(io.dout);
+  const unsigned S = static_cast<unsigned>(pr.streams), P = static_cast<unsigned>(bp.P);
+  hipError_t err;
+
+  ChunkStates cs;
+  if (bp.P > 1) {
+    // segment-start A from an fp64 inversion: dlambda0 sums terms weighted by A_t^2, so an
+    // fp32 inverse's error (about cond * 2^-24) would show in it
+    err = launch_chunk_states(pr, chunk, io.q, io.k, io.v, io.u, base + bp.off_chunk,
+                              reinterpret_cast<double *>(base + bp.off_md), st, &cs);
+    if (err != hipSuccess) return err;
+  }
+  VLA_LAUNCH("k_bw_replay", (k_bw_replay<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, v, u,
+             static_cast<const float *>(cs.S_seg), static_cast<const float *>(cs.A_seg),
+             static_cast<const float *>(cs.n_seg), rec, ck, nend, pr.T, bp.L, bp.P, pr.lambda0, pr.eps);
+  if (X != nullptr)
+    VLA_LAUNCH("k_bw_terminal", (k_bw_terminal<D>), dim3(S), dim3(256), 0, st,
+               static_cast<const float *>(ck), io.dA_T, Y, X, pr.T);
+  if (bp.P > 1) {
+    // After the replay the segment-start buffers are free: the maps go where the forward
+    // pass's maps were, the end cotangents of S where its start states were, the segment sums
+    // of dden phi(q) where the normalisers were and the segment R sums where A was.
+    float *lb = cs.pib, *E = cs.S_seg, *nd = cs.n_seg, *W = cs.A_seg;
+    VLA_LAUNCH("k_bw_dsmap", (k_bw_dsmap<D, TIn>), dim3(S, P - 1), dim3(BW_NT), 0, st, dout,
+               static_cast<const float *>(rec), lb, nd, pr.T, bp.L, bp.P);
+    err = launch_affine_prefix(pr, lb, E, bp.P, io.dS_T, nd, io.dn_T, st);
+    if (err != hipSuccess) return err;
+    VLA_LAUNCH("k_bw_grad", (k_bw_grad<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, u, dout,
+               static_cast<const float *>(rec), static_cast<const float *>(ck),
+               static_cast<const float *>(nend), static_cast<const float *>(E),
+               static_cast<const float *>(nd), static_cast<const float *>(nullptr), io.dq, io.dk,
+               io.dv, io.du, W, trw, pr.T, bp.L, bp.P);
+    err = launch_matrix_prefix(pr, W, bp.P, X, st);
+    if (err != hipSuccess) return err;
+    const unsigned nz = static_cast<unsigned>((bp.L + 63) / 64);
+    VLA_LAUNCH("k_bw_fix", (k_bw_fix<D, TIn>), dim3(S, P, nz), dim3(256), 0, st, u,
+               static_cast<const float *>(W), io.du, pr.T, bp.L, bp.P);
+  } else {
+    VLA_LAUNCH("k_bw_grad", (k_bw_grad<D, TIn>), dim3(S, 1), dim3(BW_NT), 0, st, q, k, u, dout,
+               static_cast<const float *>(rec), static_cast<const float *>(ck),
+               static_cast<const float *>(nend), io.dS_T, io.dn_T, static_cast<const float *>(X),
+               io.dq, io.dk, io.dv, io.du, static_cast<float *>(nullptr), trw, pr.T, bp.L, bp.P);
+  }
+  if (io.dlambda0 != nullptr)
+    VLA_LAUNCH("k_bw_lambda", (k_bw_lambda<D>), dim3(S), dim3(64), 0, st,
+               static_cast<const float *>(X), static_cast<const double *>(trw), io.dlambda0, bp.P);
   return hipGetLastError();
 }
 
 template <typename TIn>
-hipError_t launch_bw_dt(const Problem &p, const BackwardIO &io, void *ws, hipStream_t st) {
+hipError_t launch_bw_dt(const Problem &p, int chunk, const BackwardIO &io, void *ws, hipStream_t st) {
   switch (p.d) {
-    case 32: return launch_bw_t<32, TIn>(p, io, ws, st);
-    case 64: return launch_bw_t<64, TIn>(p, io, ws, st);
-    case 96: return launch_bw_t<96, TIn>(p, io, ws, st);
-    case 128: return launch_bw_t<128, TIn>(p, io, ws, st);
+    case 32: return launch_bw_t<32, TIn>(p, chunk, io, ws, st);
+    case 64: return launch_bw_t<64, TIn>(p, chunk, io, ws, st);
+    case 96: return launch_bw_t<96, TIn>(p, chunk, io, ws, st);
+    case 128: return launch_bw_t<128, TIn>(p, chunk, io, ws, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-size_t backward_workspace_bytes(const Problem &p) {
-  const int64_t NC = (p.T + BW_CK - 1) / BW_CK;
-  const int64_t per = p.T * (6 * int64_t(p.d) + BW_NS) + NC * 2 * int64_t(p.d) * p.d;
-  return static_cast<size_t>(p.streams * per) * sizeof(float);
-}
+size_t backward_workspace_bytes(const Problem &p, int chunk) { return make_bw_plan(p, chunk).total; }
 
-hipError_t launch_backward(const Problem &p, const BackwardIO &io, void *ws, hipStream_t stream) {
-  if (p.dtype == Dtype::F32) return launch_bw_dt<float>(p, io, ws, stream);
-  return launch_bw_dt<bf16_t>(p, io, ws, stream);
+hipError_t launch_backward(const Problem &p, int chunk, const BackwardIO &io, void *ws,
+                           hipStream_t stream) {
+  if (chunk > 0 && !chunk_supported(p, chunk)) return hipErrorInvalidValue;
+  if (p.dtype == Dtype::F32) return launch_bw_dt<float>(p, chunk, io, ws, stream);
+  return launch_bw_dt<bf16_t>(p, chunk, io, ws, stream);
 }
 
 }  // namespace vla

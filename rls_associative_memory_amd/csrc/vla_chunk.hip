@@ -283,7 +283,8 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
 template <int D>
 __global__ void __launch_bounds__(256)
 k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0,
-         const float *__restrict__ Minit, const float *__restrict__ n0, int with_n) {
+         const float *__restrict__ Minit, const float *__restrict__ n0, int with_n,
+         double *__restrict__ Md) {
   const int64_t s = blockIdx.x;
   const int e = blockIdx.y * 256 + threadIdx.x;
   if (e < D * D) {
@@ -292,14 +293,20 @@ k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0
     float *base = M + s * P * D * D + e;
     double acc = 0.0;
     // 16 segments' Grams are loaded before any of them is replaced by its prefix, so the
-    // scan waits for one memory latency per 16 segments rather than one per segment.
+    // scan waits for one memory latency per 16 segments rather than one per segment.  With
+    // Md the prefixes go there in fp64 instead (M keeps the Grams).
     for (int64_t p0 = 0; p0 < P; p0 += 16) {
       float g[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) g[i] = (p0 + i + 1 < P) ? base[(p0 + i) * D * D] : 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (p0 + i < P) base[(p0 + i) * D * D] = static_cast<float>(acc + init);
+        if (p0 + i < P) {
+          if (Md != nullptr)
+            Md[(s * P + p0 + i) * D * D + e] = acc + init;
+          else
+            base[(p0 + i) * D * D] = static_cast<float>(acc + init);
+        }
         acc += g[i];
       }
     }
@@ -319,6 +326,59 @@ k_prefix(float *__restrict__ M, float *__restrict__ nk, int64_t P, float lambda0
       }
     }
   }
+}
+
+// ------------------------------------------------------------------------------------
+// k_inv64: M_p <- (Md_p)^{-1} in fp64 (Gauss-Jordan without pivoting, Md_p SPD), rounded once
+// to fp32.  For callers that need the segment-start inverse penalty to fp32 accuracy whatever
+// the conditioning of lambda0 I + Gram (the fp32 inversion loses about cond * 2^-24).
+// Thread (ri, cj) = (tid / 16, tid % 16) holds rows ri + 16 a and columns cj + 16 b; pivot row
+// and column are broadcast through LDS, double buffered (one barrier per pivot).
+// ------------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) k_inv64(const double *__restrict__ Md, float *__restrict__ M,
+                                               int64_t P) {
+  constexpr int NR = D / 16;
+  __shared__ double rowk[2][D], colk[2][D];
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int tid = threadIdx.x, ri = tid >> 4, cj = tid & 15;
+  const double *src = Md + (s * P + p) * D * D;
+  double a[NR][NR];
+#pragma unroll
+  for (int x = 0; x < NR; ++x)
+#pragma unroll
+    for (int y = 0; y < NR; ++y) a[x][y] = src[(ri + 16 * x) * D + cj + 16 * y];
+  for (int k = 0; k < D; ++k) {
+    const int b = k & 1, kx = k >> 4, kr = k & 15;
+    if (ri == kr)
+#pragma unroll
+      for (int y = 0; y < NR; ++y) rowk[b][cj + 16 * y] = a[kx][y];
+    if (cj == kr)
+#pragma unroll
+      for (int x = 0; x < NR; ++x) colk[b][ri + 16 * x] = a[x][kx];
+    __syncthreads();
+    const double ip = 1.0 / rowk[b][k];
+#pragma unroll
+    for (int x = 0; x < NR; ++x) {
+      const int i = ri + 16 * x;
+      const double cik = colk[b][i] * ip;
+#pragma unroll
+      for (int y = 0; y < NR; ++y) {
+        const int j = cj + 16 * y;
+        if (i == k)
+          a[x][y] = (j == k) ? ip : a[x][y] * ip;
+        else if (j == k)
+          a[x][y] = -cik;
+        else
+          a[x][y] = fma(-cik, rowk[b][j], a[x][y]);
+      }
+    }
+  }
+  float *dst = M + (s * P + p) * D * D;
+#pragma unroll
+  for (int x = 0; x < NR; ++x)
+#pragma unroll
+    for (int y = 0; y < NR; ++y) dst[(ri + 16 * x) * D + cj + 16 * y] = static_cast<float>(a[x][y]);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1167,7 +1227,8 @@ k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P,
 template <int D, int CH, typename TIn>
 static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const void *q,
                                  const void *k, const void *v, const void *u, void *out,
-                                 const StateIO &sio, char *ws, hipStream_t st) {
+                                 const StateIO &sio, char *ws, hipStream_t st, bool states_only,
+                                 double *Md) {
   const TIn *qq = static_cast<const TIn *>(q);
   const TIn *kk = static_cast<const TIn *>(k);
   const TIn *vv = static_cast<const TIn *>(v);
@@ -1195,8 +1256,12 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
   }
   constexpr bool BF = sizeof(TIn) == 2;  // bf16: the A side forms the segment sums of phi(k)
   VLA_LAUNCH("k_prefix", (k_prefix<D>), gmat, dim3(256), 0, st, Mw, nkw, pl.P, pr.lambda0,
-             sio.A0 != nullptr ? static_cast<const float *>(miw) : nullptr, sio.n0, BF ? 0 : 1);
-  VLA_LAUNCH("k_inv", (k_inv<D>), dim3(S, P), dim3(256), 0, st, Mw, pl.P);
+             sio.A0 != nullptr ? static_cast<const float *>(miw) : nullptr, sio.n0, BF ? 0 : 1, Md);
+  if (Md != nullptr)
+    VLA_LAUNCH("k_inv64", (k_inv64<D>), dim3(S, P), dim3(256), 0, st, static_cast<const double *>(Md),
+               Mw, pl.P);
+  else
+    VLA_LAUNCH("k_inv", (k_inv<D>), dim3(S, P), dim3(256), 0, st, Mw, pl.P);
   if (sio.A0 != nullptr) {  // the first segment starts from A_0 itself
     VLA_LAUNCH("k_sym_copy", (k_sym_copy<D>), gmat, dim3(256), 0, st, sio.A0, Mw,
                static_cast<int64_t>(pl.P) * D * D);
@@ -1229,6 +1294,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
                s0w, pl.P, sio.S0, nkw, sio.n0, n_final);
+    if (states_only) return hipGetLastError();
     // The final pass runs in chunks of at most 32 tokens whatever the map pass uses: its
     // workgroup then fits twice per CU (54 KB of LDS and 127 VGPRs at d = 96), and the
     // segment maps it starts from do not depend on either pass's chunking.
@@ -1244,6 +1310,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
                s0w, pl.P, sio.S0, static_cast<float *>(nullptr), static_cast<const float *>(nullptr),
                static_cast<float *>(nullptr));
+    if (states_only) return hipGetLastError();
     VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P),
                dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final,
                pl.T, pl.L, pl.P);
@@ -1254,9 +1321,11 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
 template <typename TIn>
 static hipError_t launch_chunk_dt(const Problem &pr, const ChunkPlan &pl, const void *q,
                                   const void *k, const void *v, const void *u, void *out,
-                                  const StateIO &sio, char *ws, hipStream_t st) {
+                                  const StateIO &sio, char *ws, hipStream_t st, bool states_only,
+                                  double *Md) {
 #define VLA_CASE(DD, CC)                                                                      \
-  if (pr.d == DD && pl.C == CC) return launch_chunk_t<DD, CC, TIn>(pr, pl, q, k, v, u, out, sio, ws, st);
+  if (pr.d == DD && pl.C == CC)                                                               \
+    return launch_chunk_t<DD, CC, TIn>(pr, pl, q, k, v, u, out, sio, ws, st, states_only, Md);
   VLA_CASE(32, 16) VLA_CASE(32, 32) VLA_CASE(32, 64)
   VLA_CASE(64, 16) VLA_CASE(64, 32) VLA_CASE(64, 64)
   VLA_CASE(96, 16) VLA_CASE(96, 32) VLA_CASE(96, 64)
@@ -1271,8 +1340,59 @@ hipError_t launch_chunk(const Problem &p, int chunk, const void *q, const void *
   if (!chunk_supported(p, chunk)) return hipErrorInvalidValue;
   const ChunkPlan pl = make_plan(p, chunk);
   char *w = static_cast<char *>(ws);
-  if (p.dtype == Dtype::F32) return launch_chunk_dt<float>(p, pl, q, k, v, u, out, st, w, stream);
-  return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, out, st, w, stream);
+  if (p.dtype == Dtype::F32) return launch_chunk_dt<float>(p, pl, q, k, v, u, out, st, w, stream, false, nullptr);
+  return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, out, st, w, stream, false, nullptr);
+}
+
+void chunk_segments(const Problem &p, int chunk, int64_t *L, int64_t *P) {
+  const ChunkPlan pl = make_plan(p, chunk);
+  *L = pl.L;
+  *P = pl.P;
+}
+
+hipError_t launch_chunk_states(const Problem &p, int chunk, const void *q, const void *k,
+                               const void *v, const void *u, void *ws, double *Md,
+                               hipStream_t stream, ChunkStates *cs) {
+  if (!chunk_supported(p, chunk)) return hipErrorInvalidValue;
+  const ChunkPlan pl = make_plan(p, chunk);
+  char *w = static_cast<char *>(ws);
+  cs->S_seg = reinterpret_cast<float *>(w + pl.off_s0);
+  cs->A_seg = reinterpret_cast<float *>(w + pl.off_m);
+  cs->n_seg = reinterpret_cast<float *>(w + pl.off_nk);
+  cs->pib = reinterpret_cast<float *>(w + pl.off_pib);
+  cs->L = pl.L;
+  cs->P = pl.P;
+  const StateIO none{};
+  if (p.dtype == Dtype::F32) return launch_chunk_dt<float>(p, pl, q, k, v, u, nullptr, none, w, stream, true, Md);
+  return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, nullptr, none, w, stream, true, Md);
+}
+
+hipError_t launch_matrix_prefix(const Problem &p, float *M, int64_t P, const float *Minit,
+                                hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(p.streams), static_cast<unsigned>((p.d * p.d + 255) / 256));
+#define VLA_CASE(DD)                                                                          \
+  if (p.d == DD) {                                                                            \
+    VLA_LAUNCH("k_prefix", (k_prefix<DD>), grid, dim3(256), 0, st, M, static_cast<float *>(nullptr), \
+               P, 0.0f, Minit, static_cast<const float *>(nullptr), 0, static_cast<double *>(nullptr)); \
+    return hipGetLastError();                                                                 \
+  }
+  VLA_CASE(32) VLA_CASE(64) VLA_CASE(96) VLA_CASE(128)
+#undef VLA_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_affine_prefix(const Problem &p, const float *pib, float *s0, int64_t P,
+                                const float *S0, float *nk, const float *n0, hipStream_t st) {
+  const unsigned S = static_cast<unsigned>(p.streams);
+#define VLA_CASE(DD)                                                                          \
+  if (p.d == DD) {                                                                            \
+    VLA_LAUNCH("k_sprefix", (k_sprefix<DD>), dim3(S, DD / 16), dim3(DD / 16 * kWave), 0, st,  \
+               pib, s0, P, S0, nk, n0, static_cast<float *>(nullptr));                        \
+    return hipGetLastError();                                                                 \
+  }
+  VLA_CASE(32) VLA_CASE(64) VLA_CASE(96) VLA_CASE(128)
+#undef VLA_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace vla

@@ -43,21 +43,46 @@ hipError_t launch_chunk(const Problem &p, int chunk, const void *q, const void *
                         const void *v, const void *u, void *out, const StateIO &st, void *ws,
                         hipStream_t stream);
 
+// The chunked path's passes up to the segment-start states (no outputs): S, A and n at the
+// start of every segment [streams][P][...] and the pass's segment-map buffer
+// [streams][P][2][d][d] (free for reuse once this returns), all inside `ws`.  With Md (fp64
+// [streams][P][d][d], device) the segment-start A come from an fp64 inversion.
+struct ChunkStates {
+  float *S_seg = nullptr, *A_seg = nullptr, *n_seg = nullptr, *pib = nullptr;
+  int64_t L = 0, P = 0;
+};
+void chunk_segments(const Problem &p, int chunk, int64_t *L, int64_t *P);
+hipError_t launch_chunk_states(const Problem &p, int chunk, const void *q, const void *k,
+                               const void *v, const void *u, void *ws, double *Md,
+                               hipStream_t stream, ChunkStates *cs);
+// In place over each stream's P matrices [streams][P][d][d]: M_j <- M0 + sum_{j' < j} M_j' (fp64
+// sums; M0 = Minit[stream], or 0 when Minit is NULL).
+hipError_t launch_matrix_prefix(const Problem &p, float *M, int64_t P, const float *Minit,
+                                hipStream_t stream);
+// X_0 = S0[stream] (0 when NULL), X_{j+1} = X_j Pi_j + B_j with pib [streams][P][2][d][d] =
+// (Pi_j, B_j), into s0 [streams][P][d][d]; when nk is not NULL also, in place over
+// [streams][P][d], nk_j <- n0[stream] + sum_{j' < j} nk_j' (fp64 sums, n0 NULL = 0).
+hipError_t launch_affine_prefix(const Problem &p, const float *pib, float *s0, int64_t P,
+                                const float *S0, float *nk, const float *n0, hipStream_t stream);
+
 // Linear-attention baseline (chunked, time-segment parallel): out, S_T (S[i][j]) and n_T
 // of every stream; `ws` must hold la_workspace_bytes(p).  p.lambda0 is not used.
 size_t la_workspace_bytes(const Problem &p);
 hipError_t launch_la(const Problem &p, const void *q, const void *k, const void *v, void *out,
                      float *S_final, float *n_final, void *ws, hipStream_t stream);
 
-// Backward of the recurrence from the fixed start (sequential, one workgroup per stream).
+// Backward of the recurrence from the fixed start (one workgroup per segment of a stream).
 struct BackwardIO {
   const void *q, *k, *v, *u, *dout;            // [streams][T][d] in the input dtype
   const float *dS_T, *dA_T, *dn_T;             // cotangents of the final state, or NULL
   float *dq, *dk, *dv, *du;                    // [streams][T][d] fp32
   float *dlambda0;                             // [streams] fp32, or NULL
 };
-size_t backward_workspace_bytes(const Problem &p);
-hipError_t launch_backward(const Problem &p, const BackwardIO &io, void *ws, hipStream_t stream);
+// chunk = 0: one segment per stream (token by token); else the chunked path's segments with
+// that chunk length (chunk_supported must hold).
+size_t backward_workspace_bytes(const Problem &p, int chunk);
+hipError_t launch_backward(const Problem &p, int chunk, const BackwardIO &io, void *ws,
+                           hipStream_t stream);
 
 // While an object of this type lives, launches on the calling thread record no timing events
 // (the allocation-free entry point creates no events, whatever vla_profile_enable says).

@@ -332,10 +332,10 @@ def linear_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eps: flo
     return out, S_final, n_final
 
 
-def backward_workspace_size(shape, dtype) -> int:
+def backward_workspace_size(shape, dtype, path="auto", chunk=0) -> int:
     """Device workspace bytes of vla_backward for [B, H, T, d] inputs."""
     lib = load_library()
-    desc = make_desc(shape, dtype)
+    desc = make_desc(shape, dtype, path=path, chunk=chunk)
     n = ctypes.c_size_t(0)
     _check(lib.vla_backward_workspace_size(ctypes.byref(desc), ctypes.byref(n)),
            "vla_backward_workspace_size")
@@ -346,10 +346,12 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
              d_out: torch.Tensor, dS_T: Optional[torch.Tensor] = None,
              dA_T: Optional[torch.Tensor] = None, dn_T: Optional[torch.Tensor] = None,
              eps: float = 1e-6, workspace: Optional[torch.Tensor] = None,
-             stream: Optional[torch.cuda.Stream] = None):
+             stream: Optional[torch.cuda.Stream] = None, path: str = "auto", chunk: int = 0):
     """Gradients of <d_out, out> + <dS_T, S_T> + <dA_T, A_T> + <dn_T, n_T> through the
-    forward from the fixed start (vla_backward in vla.h).  Returns (dq, dk, dv, du) as fp32
-    tensors shaped like q and dlambda0, the per-stream shares [.., ] of dL/dlambda0."""
+    forward from the fixed start (vla_backward in vla.h).  path "seq" runs one segment per
+    stream, "chunk" the chunked path's time segments in parallel, "auto" picks.  Returns
+    (dq, dk, dv, du) as fp32 tensors shaped like q and dlambda0, the per-stream shares [.., ] of
+    dL/dlambda0."""
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("u", u), ("d_out", d_out)):
         if not t.is_cuda:
@@ -365,7 +367,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, u: torch.Tensor,
         if t is not None and (tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_contiguous()
                               or t.device != q.device):
             raise ValueError(f"{name} must be a contiguous fp32 {shp} tensor on q's device")
-    desc = make_desc(tuple(q.shape), q.dtype, eps=eps, workspace=workspace)
+    desc = make_desc(tuple(q.shape), q.dtype, eps=eps, workspace=workspace, path=path, chunk=chunk)
     grads = [torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(4)]
     dlam = torch.empty(tuple(q.shape[:-2]), dtype=torch.float32, device=q.device)
     ptr = lambda t: t.data_ptr() if t is not None else None

@@ -176,7 +176,8 @@ def test_backward_argument_errors(lib):
     assert call(bad, d) == 1                                   # no d_out
     bad = list(args); bad[4] = ctypes.c_float(0.0)
     assert call(bad, d) == 1                                   # lambda0 <= 0
-    assert call(args, desc(B=1, H=2, T=100, d=64, path=2)) == 2
+    assert call(args, desc(B=1, H=2, T=100, d=64, path=3)) == 2    # decode
+    assert call(args, desc(B=1, H=2, T=100, d=64, path=2, chunk=48)) == 2
     assert call(args, desc(B=1, H=2, T=100, d=64, gain=1)) == 2
     bad = list(args); bad[9] = ctypes.c_void_p((1 << 20) + 4)
     assert call(bad, d) == 2                                   # misaligned dq
@@ -184,8 +185,20 @@ def test_backward_argument_errors(lib):
     assert call(args, small) == 1
     n = ctypes.c_size_t(0)
     assert lib.vla_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
-    # per stream: T (6 d + 8) floats of records and ceil(T / 32) checkpoints of 2 d^2 floats
-    assert n.value == 2 * (100 * (6 * 64 + 8) + 4 * 2 * 64 * 64) * 4
+    # one segment per stream: T (6 d + 8) floats of records, ceil(T / 32) checkpoints of
+    # 2 d^2 floats, n after the segment, two d x d matrices and one double, per stream, each
+    # buffer 256-byte aligned
+    al = lambda x: (x + 255) // 256 * 256
+    seq = (al(2 * 100 * (6 * 64 + 8) * 4) + al(2 * 4 * 2 * 64 * 64 * 4) + al(2 * 64 * 4)
+           + 2 * al(2 * 64 * 64 * 4) + al(2 * 8))
+    assert n.value == seq
+    assert lib.vla_backward_workspace_size(ctypes.byref(desc(B=1, H=2, T=100, d=64, path=1)),
+                                           ctypes.byref(n)) == 0 and n.value == seq
+    # few long streams: AUTO splits time (the chunked path's segments, its workspace on top)
+    ws = lambda **kw: (lib.vla_backward_workspace_size(ctypes.byref(desc(**kw)), ctypes.byref(n)), n.value)[1]
+    long_auto = ws(B=1, H=2, T=4096, d=96)
+    assert long_auto == ws(B=1, H=2, T=4096, d=96, path=2) > ws(B=1, H=2, T=4096, d=96, path=1)
+    assert ws(B=1, H=256, T=4096, d=96) == ws(B=1, H=256, T=4096, d=96, path=1)
 
 
 def test_decode_path_resolution(lib):

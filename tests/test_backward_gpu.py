@@ -26,7 +26,7 @@ def _say(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def _run(d, dt, T, H=2, lam=0.8, with_state=True, seed=5):
+def _run(d, dt, T, H=2, lam=0.8, with_state=True, seed=5, path="auto"):
     w = get_workload("tiny_t256_d32").resized(name=f"bw_{d}_{dt}_{T}", B=1, H=H, T=T, d=d,
                                               dtype=dt, lambda0=lam)
     q, k, v, u = make_inputs(w)
@@ -38,10 +38,10 @@ def _run(d, dt, T, H=2, lam=0.8, with_state=True, seed=5):
     dev = [torch.from_numpy(np.ascontiguousarray(x)).view(1, H, T, d).to(torch_dtype(w)).cuda()
            for x in (q, k, v, u, dout)]
     seen = [x.float().cpu().numpy().reshape(H, T, d).astype(np.float64) for x in dev]
-    _say(f"[case] backward d={d} {dt} T={T} state cotangents={with_state}")
+    _say(f"[case] backward d={d} {dt} T={T} state cotangents={with_state} path={path}")
     tens = lambda x, shp: torch.from_numpy(x).view(shp).cuda() if x is not None else None
     got = vla.backward(*dev[:4], lam, dev[4], dS_T=tens(dS, (1, H, d, d)), dA_T=tens(dA, (1, H, d, d)),
-                       dn_T=tens(dn, (1, H, d)), eps=w.eps)
+                       dn_T=tens(dn, (1, H, d)), eps=w.eps, path=path)
     torch.cuda.synchronize()
     ref = vla_grad(*seen[:4], lam, seen[4], dS, dA, dn, eps=w.eps)
     tol = TOL[dt]
@@ -63,6 +63,60 @@ def test_backward_matches_oracle(d, dt):
 @pytest.mark.parametrize("T", [1, 32, 33])
 def test_backward_edge_lengths(T):
     _run(64, "f32", T=T)
+
+
+# Time-segment parallel backward on shapes that split into several segments (64-token segments
+# for fp32 inputs, 256-token ones for bf16), including a last segment of a single token.
+@pytest.mark.parametrize("d,dt,T", [(64, "f32", 300), (32, "f32", 129), (96, "f32", 257),
+                                    (64, "bf16", 1100), (128, "bf16", 600), (96, "bf16", 513)])
+def test_backward_segments_match_oracle(d, dt, T):
+    _run(d, dt, T, path="chunk")
+
+
+def test_backward_segments_without_state_cotangents():
+    _run(64, "f32", T=200, with_state=False, lam=0.5, path="chunk")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_backward_few_long_streams(dt):
+    """Two streams of 4096 tokens at d = 96 (64 segments of 64 tokens for fp32 inputs, 16 of
+    256 for bf16), on the path the library picks for them (time segments), against the fp64
+    oracle; the gradients of the token-by-token path beside them.  Bars as for the full
+    workloads: the larger of the forward's bar and four times the deviation of the same
+    steps in plain fp32 (dlambda0, a closed form, at the bar itself)."""
+    H, T, d, lam = 2, 4096, 96, 0.8
+    w = get_workload("tiny_t256_d32").resized(name=f"bw_long_{dt}", B=1, H=H, T=T, d=d, dtype=dt,
+                                              lambda0=lam)
+    q, k, v, u = make_inputs(w)
+    r = np.random.default_rng(17)
+    dout = r.standard_normal(q.shape).astype(np.float32)
+    dS = r.standard_normal((H, d, d)).astype(np.float32)
+    dA = r.standard_normal((H, d, d)).astype(np.float32)
+    dn = r.standard_normal((H, d)).astype(np.float32)
+    dev = [torch.from_numpy(np.ascontiguousarray(x)).view(1, H, T, d).to(torch_dtype(w)).cuda()
+           for x in (q, k, v, u, dout)]
+    seen = [x.float().cpu().numpy().reshape(H, T, d) for x in dev]
+    cots = dict(dS_T=torch.from_numpy(dS).view(1, H, d, d).cuda(), dA_T=torch.from_numpy(dA).view(1, H, d, d).cuda(),
+                dn_T=torch.from_numpy(dn).view(1, H, d).cuda())
+    assert vla.backward_workspace_size((1, H, T, d), torch_dtype(w)) == \
+        vla.backward_workspace_size((1, H, T, d), torch_dtype(w), path="chunk")
+    _say(f"[case] backward few long streams {dt}: {H} x {T} tokens, d = {d}")
+    got = vla.backward(*dev[:4], lam, dev[4], eps=w.eps, **cots)
+    seq = vla.backward(*dev[:4], lam, dev[4], eps=w.eps, path="seq", **cots)
+    torch.cuda.synchronize()
+    ref = vla_grad(*(x.astype(np.float64) for x in seen[:4]), lam, seen[4].astype(np.float64),
+                   dS.astype(np.float64), dA.astype(np.float64), dn.astype(np.float64), eps=w.eps)
+    ref32 = vla_grad(*seen[:4], lam, seen[4], dS, dA, dn, eps=w.eps, dtype=torch.float32)
+    tol = TOL[dt]
+    names = ("dq", "dk", "dv", "du")
+    bars = {n: max(tol, 4.0 * rel_l2(r32, rf)) for n, r32, rf in zip(names, ref32[:4], ref[:4])}
+    bars["dlambda0"] = tol
+    for label, res in (("segments", got), ("token by token", seq)):
+        errs = {n: rel_l2(g.cpu().numpy().reshape(H, T, d), rf) for n, g, rf in zip(names, res[:4], ref[:4])}
+        errs["dlambda0"] = rel_l2(res[4].cpu().numpy().reshape(H), ref[4])
+        _say(f"[parity] backward {label} {dt}: " + " ".join(f"{n}={e:.3e} (bar {bars[n]:.1e})" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e < bars[n], f"{label}: {n} rel L2 {e:.3e} >= {bars[n]:.3e}"
 
 
 def test_backward_without_state_cotangents_and_long():
