@@ -57,14 +57,20 @@ struct SwbLds {
   uint16_t QaD[2][FINAL ? C::NCT : 1][16][C::LDI];  // Qa_tt (final pass)
   uint16_t KaO[2][C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // -Ka_ba of each step
   uint16_t QaO[2][FINAL && C::NOD > 0 ? C::NOD : 1][16][C::LDI];  // Qa_ba (final pass)
-  float Kd[C::NCT][16][16];                   // -Ka_b transposed, fp32, for the block inverses
-  alignas(16) uint16_t nst[FINAL ? 2 : 1][FINAL ? D : 8];   // normaliser at the segment start, two terms
+  alignas(16) float np[FINAL ? D : 4];        // normaliser at the segment start
   float rk[CH];                               // 1 / ||k||
-  float rden[CH];                             // 1 / readout denominator
+  float rden[CH];                             // readout denominator (its reciprocal once complete)
+  float dpart[FINAL ? CH : 1][FINAL ? D / 32 : 1];  // phi(q) . n_p over 32 features of a token
 };
+
+// The final pass at d <= 96 is held to 128 VGPRs (four waves per SIMD), so that two of its
+// workgroups share a CU.
+template <int D, bool FINAL>
+constexpr int swb_waves_per_simd() { return (FINAL && D <= 96) ? 4 : 1; }
 
 template <int D, int CH, bool FINAL>
 __global__ void __launch_bounds__((SwbCfg<D, CH, FINAL>::NT))
+__attribute__((amdgpu_waves_per_eu(swb_waves_per_simd<D, FINAL>())))
 k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
        const float *__restrict__ alpha, const float *__restrict__ rkden,
        const float *__restrict__ s0, float *__restrict__ pib, bf16_t *__restrict__ out,
@@ -155,14 +161,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     if constexpr (FINAL) pden = rc[toff + 1];
   };
   prefetch(tb, tid);
-  if constexpr (FINAL) {  // phi(q) . n_p completes the A side's denominators (see below)
-    for (int f = tid; f < D; f += NT) {
-      uint16_t h, l;
-      split2_1(nstart[(s * P + p) * D + f], h, l);
-      sh.nst[0][f] = h;
-      sh.nst[1][f] = l;
-    }
-  }
+  if constexpr (FINAL)  // phi(q) . n_p completes the A side's denominators (see below)
+    for (int f = tid; f < D; f += NT) sh.np[f] = nstart[(s * P + p) * D + f];
 
   for (int64_t c0 = tb; c0 < te; c0 += CH) {
     const int m = static_cast<int>(std::min<int64_t>(CH, te - c0));
@@ -184,11 +184,25 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         if constexpr (FINAL) {
           float qf[8];
           io<bf16_t>::unpack(pq[i], qf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[e] = c < m ? phi(qf[e]) : 0.f;
+          // The A side's denominators count the normaliser from the segment start only;
+          // den = phi(q) . n_p + (A side's value), n_p the normaliser at the segment start:
+          // this thread's 8 features of the dot product, in fp32 (summed in the tile phase).
+          const float4 n0 = *reinterpret_cast<const float4 *>(&sh.np[f0]);
+          const float4 n1 = *reinterpret_cast<const float4 *>(&sh.np[f0 + 4]);
+          float part = ((qf[0] * n0.x + qf[1] * n0.y) + (qf[2] * n0.z + qf[3] * n0.w)) +
+                       ((qf[4] * n1.x + qf[5] * n1.y) + (qf[6] * n1.z + qf[7] * n1.w));
+          // lanes ui ^ 1, ui ^ 2 stage the neighbouring 8-feature pieces of the same token
+          // (d / 8 is a multiple of 4, and so is every unit count here): one sum per 32 features
+          part += __shfl_xor(part, 1);
+          part += __shfl_xor(part, 2);
+          if ((ui & 3) == 0) sh.dpart[c][f0 / 32] = part;
           uint32_t hw[4], lw[4];
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             uint32_t t2[2];
-            split_pk<2>(c < m ? phi(qf[e]) : 0.f, c < m ? phi(qf[e + 1]) : 0.f, t2);
+            split_pk<2>(qf[e], qf[e + 1], t2);
             hw[e / 2] = t2[0];
             lw[e / 2] = t2[1];
           }
@@ -223,7 +237,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     }
     if (tid < CH) {
       sh.rk[tid] = tid < m ? prk : 0.f;
-      if constexpr (FINAL) sh.rden[tid] = tid < m ? pden : 1.f;  // completed below
+      if constexpr (FINAL) sh.rden[tid] = tid < m ? pden : 1.f;  // completed in the tile phase
     }
     // Every prefetched register counts as used here, in every thread (lanes that stage nothing
     // included), so no load is still pending when the next prefetch reuses the registers: the
@@ -301,82 +315,69 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
             *reinterpret_cast<uint2 *>(dst + ts) = t.l;
           }
         } else {
-          f4_t nk;
+          if (diag) {
+            // (I + Ka_b)^{-1} by forward substitution, column j = lane (lanes 0..15 keep theirs).
+            // -Ka[r][q] is value r % 4 of nv in lane 16 (r / 4) + q, read into a scalar register.
+            // The four values are formed one by one and kept opaque (a vector read this way is
+            // miscompiled), and the reads of pivot q + 1 are tied to x_q so that at most two
+            // pivots' values occupy scalar registers at a time.
+            float nv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) nk[r] = -acc[r] * sh.rk[16 * ct + i + r];
-          if (diag) {  // Kd[q][i] = -Ka[i][q]
-            f4_t kd;
+            for (int e = 0; e < 4; ++e) {
+              nv[e] = -acc[e] * sh.rk[16 * ct + i + e];
+              asm volatile("" : "+v"(nv[e]));
+            }
+            auto rd = [&](int r, int q) {
+              return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nv[r & 3]), 16 * (r >> 2) + q));
+            };
+            float x[16];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) kd[r] = li >= i + r ? 0.f : nk[r];
-            *reinterpret_cast<f4_t *>(&sh.Kd[ct][li][i]) = kd;
+            for (int r = 0; r < 16; ++r) x[r] = (r == lane) ? 1.f : 0.f;
+            float kc[16], kn[16];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) kc[r] = rd(r, 0);
+#pragma unroll
+            for (int q = 0; q < 15; ++q) {
+              asm volatile("" : "+v"(nv[0]), "+v"(nv[1]), "+v"(nv[2]), "+v"(nv[3]) : "v"(x[q]));
+              if (q + 1 < 15)
+#pragma unroll
+                for (int r = q + 2; r < 16; ++r) kn[r] = rd(r, q + 1);
+#pragma unroll
+              for (int r = q + 1; r < 16; ++r) x[r] = fmaf(kc[r], x[q], x[r]);
+#pragma unroll
+              for (int r = q + 2; r < 16; ++r) kc[r] = kn[r];
+            }
+            if (lane < 16) {
+              // column j of the inverse, transposed: row j of InvS, 16 values per term
+              uint32_t w[8][2];
+#pragma unroll
+              for (int r = 0; r < 16; r += 2) split_pk<2>(x[r], x[r + 1], w[r / 2]);
+#pragma unroll
+              for (int term = 0; term < 2; ++term) {
+                uint4 *dst = reinterpret_cast<uint4 *>(&sh.InvS[term][ct][lane][0]);
+                dst[0] = make_uint4(w[0][term], w[1][term], w[2][term], w[3][term]);
+                dst[1] = make_uint4(w[4][term], w[5][term], w[6][term], w[7][term]);
+              }
+            }
           } else {
+            f4_t nk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nk[r] = -acc[r] * sh.rk[16 * ct + i + r];
             const Split2h t = split2_4h(nk);
             *reinterpret_cast<uint2 *>(&sh.KaO[0][jk - NCT][li][i]) = t.h;
             *reinterpret_cast<uint2 *>(&sh.KaO[1][jk - NCT][li][i]) = t.l;
           }
         }
       }
-      if (!isq && diag) {
-        // (I + Ka_b)^{-1} by forward substitution in lanes 0..15 (column j = lane),
-        // right-looking: once x_q is final it is applied to all later rows at once, so the
-        // dependent chain is one multiply-add per pivot.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < 16) {
-          const int j = lane;
-          float x[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
-#pragma unroll
-          for (int q = 0; q < 15; ++q) {
-#pragma unroll
-            for (int i4 = (q + 1) / 4; i4 < 4; ++i4) {
-              const f4_t kc = *reinterpret_cast<const f4_t *>(&sh.Kd[ct][q][4 * i4]);  // -Ka column q
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (4 * i4 + e > q) x[4 * i4 + e] = fmaf(kc[e], x[q], x[4 * i4 + e]);
-            }
-          }
-          // column j of the inverse, transposed: row j of InvS, 16 values per term
-          uint32_t w[8][2];
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) split_pk<2>(x[i], x[i + 1], w[i / 2]);
-#pragma unroll
-          for (int term = 0; term < 2; ++term) {
-            uint4 *dst = reinterpret_cast<uint4 *>(&sh.InvS[term][ct][j][0]);
-            dst[0] = make_uint4(w[0][term], w[1][term], w[2][term], w[3][term]);
-            dst[1] = make_uint4(w[4][term], w[5][term], w[6][term], w[7][term]);
-          }
-        }
-      }
     }
     if constexpr (FINAL) {
-      // The A side's denominators count the normaliser from the segment start only; with n_p
-      // the normaliser at the segment start,  den_c = phi(q_c) . n_p + (A side's value): one
-      // product over features per token tile (n_p in column 0 of the B operand, both in two
-      // bf16 terms), token tile ct on wave NWT - 1 - ct, whose tile job above is a light one
-      // when there are waves to spare.
-      for (int ct = C::NWT - 1 - wave; ct < NCT; ct += C::NWT) {
-        f4_t part[NKS];
+      // Complete the denominators (the staging threads' partial dot products phi(q) . n_p,
+      // summed in a fixed order) and keep their reciprocals, on the last wave (a light tile job).
+      if (wave == C::NWT - 1 && lane < CH) {
+        float dn = 0.f;
 #pragma unroll
-        for (int ksl = 0; ksl < NKS; ++ksl) {
-          const int fa = 32 * ksl + 4 * gq;
-          const Split2 a = ld2_4x2(&sh.sFq[0][16 * ct + li][fa], &sh.sFq[0][16 * ct + li][fa + 16], TQ);
-          Split2 b = ld2_4x2(&sh.nst[0][fa], &sh.nst[0][fa + 16], D);
-          if (li != 0) b = Split2{bf16x8_t{}, bf16x8_t{}};
-          part[ksl] = mm2_ss(a, b, f4_zero());
-        }
-        f4_t acc = part[0];
-#pragma unroll
-        for (int ksl = 1; ksl < NKS; ++ksl) acc += part[ksl];
-        if (li == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int c = 16 * ct + 4 * gq + r;
-            sh.rden[c] = 1.0f / (sh.rden[c] + acc[r]);
-          }
-        }
+        for (int g = 0; g < D / 32; ++g) dn += sh.dpart[lane][g];
+        sh.rden[lane] = 1.0f / (sh.rden[lane] + dn);
       }
     }
     __syncthreads();
