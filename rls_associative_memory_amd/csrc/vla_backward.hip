@@ -630,35 +630,68 @@ k_bw_terminal(const float *__restrict__ cks, const float *__restrict__ dA_T,
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_bw_fix: du_t -= 2 R_end u_t over 64 tokens of segment p (R_end at Rend slot P - 1 - p), one
-// 32-row slab of R at a time.
+// k_bw_fix: du_t -= 2 R_end u_t over up to 256 tokens of segment p (R_end at Rend slot P - 1 - p,
+// symmetric), 64 tokens at a time.  R_end and the token block sit in LDS; thread (tg, rg) forms
+// tokens 4 tg .. 4 tg + 3 against rows rg + 16 m, 16-byte operands from LDS (16 multiply-adds
+// per pair of reads).
 // ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float4 bw_ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+__device__ __forceinline__ float4 bw_ld4(const bf16_t *p) {
+  const uint2 w = *reinterpret_cast<const uint2 *>(p);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
 template <int D, typename TIn>
 __global__ void __launch_bounds__(256)
 k_bw_fix(const TIn *__restrict__ u, const float *__restrict__ Rend, float *__restrict__ du,
          int64_t T, int64_t L, int64_t P) {
-  __shared__ float sU[64][D + 1];
-  __shared__ float sR[32][D + 1];
+  constexpr int RPT = D / 16, LDR = D + 4;
+  __shared__ __attribute__((aligned(16))) float sR[D][LDR];
+  __shared__ __attribute__((aligned(16))) float sU[64][LDR];
   const int64_t s = blockIdx.x, p = blockIdx.y;
-  const int64_t t0 = p * L + static_cast<int64_t>(blockIdx.z) * 64;
-  const int64_t te = std::min<int64_t>(std::min<int64_t>(T, p * L + L), t0 + 64);
-  if (t0 >= te) return;
-  const int nt = static_cast<int>(te - t0);
-  const int tid = threadIdx.x, rr = tid & 31, tg = tid >> 5;
+  const int64_t seg_end = std::min<int64_t>(T, p * L + L);
+  const int64_t t_beg = p * L + static_cast<int64_t>(blockIdx.z) * 256;
+  if (t_beg >= seg_end) return;  // the whole workgroup
+  const int tid = threadIdx.x, tg = tid >> 4, rg = tid & 15;
   const float *Rs = Rend + (s * P + (P - 1 - p)) * D * D;
-  for (int e = tid; e < 64 * D; e += 256) {
-    const int j = e / D, c = e % D;
-    sU[j][c] = j < nt ? bw_cv(u[(s * T + t0 + j) * D + c]) : 0.f;
-  }
-  for (int slab = 0; slab < D / 32; ++slab) {
+  for (int e = 4 * tid; e < D * D; e += 1024)
+    *reinterpret_cast<float4 *>(&sR[e / D][e % D]) = bw_ld4(Rs + e);
+  for (int blk = 0; blk < 4; ++blk) {
+    const int64_t t0 = t_beg + 64 * blk;
+    if (t0 >= seg_end) break;  // uniform
+    const int nt = static_cast<int>(std::min<int64_t>(64, seg_end - t0));
+    __syncthreads();  // R staged; the previous block's readers are done
+    for (int e = 4 * tid; e < 64 * D; e += 1024) {
+      const int j = e / D, c = e % D;
+      *reinterpret_cast<float4 *>(&sU[j][c]) =
+          j < nt ? bw_ld4(u + (s * T + t0 + j) * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     __syncthreads();
-    for (int e = tid; e < 32 * D; e += 256) sR[e / D][e % D] = Rs[(32 * slab + e / D) * D + e % D];
-    __syncthreads();
-    for (int j = tg; j < nt; j += 8) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < D; ++c) acc = fmaf(sR[rr][c], sU[j][c], acc);
-      du[(s * T + t0 + j) * D + 32 * slab + rr] -= 2.0f * acc;
+    float acc[4][RPT];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) acc[a][m] = 0.f;
+#pragma unroll 2
+    for (int c = 0; c < D; c += 4) {
+      float4 uv[4], rv[RPT];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) uv[a] = *reinterpret_cast<const float4 *>(&sU[4 * tg + a][c]);
+#pragma unroll
+      for (int m = 0; m < RPT; ++m) rv[m] = *reinterpret_cast<const float4 *>(&sR[rg + 16 * m][c]);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+          acc[a][m] = fmaf(uv[a].x, rv[m].x, fmaf(uv[a].y, rv[m].y, fmaf(uv[a].z, rv[m].z, fmaf(uv[a].w, rv[m].w, acc[a][m]))));
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int j = 4 * tg + a;
+      if (j < nt)
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) du[(s * T + t0 + j) * D + rg + 16 * m] -= 2.0f * acc[a][m];
     }
   }
 }
@@ -764,7 +797,7 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
                io.dv, io.du, W, trw, pr.T, bp.L, bp.P);
     err = launch_matrix_prefix(pr, W, bp.P, X, st);
     if (err != hipSuccess) return err;
-    const unsigned nz = static_cast<unsigned>((bp.L + 63) / 64);
+    const unsigned nz = static_cast<unsigned>((bp.L + 255) / 256);
     VLA_LAUNCH("k_bw_fix", (k_bw_fix<D, TIn>), dim3(S, P, nz), dim3(256), 0, st, u,
                static_cast<const float *>(W), io.du, pr.T, bp.L, bp.P);
   } else {

@@ -350,12 +350,15 @@ __global__ void __launch_bounds__(256) k_inv64(const double *__restrict__ Md, fl
     for (int y = 0; y < NR; ++y) a[x][y] = src[(ri + 16 * x) * D + cj + 16 * y];
   for (int k = 0; k < D; ++k) {
     const int b = k & 1, kx = k >> 4, kr = k & 15;
-    if (ri == kr)
+    // (register indices stay compile-time constants: the block of the pivot is selected by
+    // predicate, not by indexing, which would put the matrix in scratch memory)
 #pragma unroll
-      for (int y = 0; y < NR; ++y) rowk[b][cj + 16 * y] = a[kx][y];
-    if (cj == kr)
+    for (int x = 0; x < NR; ++x)
 #pragma unroll
-      for (int x = 0; x < NR; ++x) colk[b][ri + 16 * x] = a[x][kx];
+      for (int y = 0; y < NR; ++y) {
+        if (x == kx && ri == kr) rowk[b][cj + 16 * y] = a[x][y];
+        if (y == kx && cj == kr) colk[b][ri + 16 * x] = a[x][y];
+      }
     __syncthreads();
     const double ip = 1.0 / rowk[b][k];
 #pragma unroll
