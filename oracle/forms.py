@@ -1,9 +1,10 @@
 """Second formulations of the VLA recurrence, in fp64, for pinning the algebra the GPU uses.
 
 TEST INFRASTRUCTURE ONLY (same rule as ``oracle/vla_oracle.py``): imported by ``tests/``
-only.  The recurrence itself is in ``vla_oracle.py``; the two functions here re-derive
-the same result in the blocked forms the kernels are built on, and the tests check them
-against the sequential oracle before any kernel is trusted.  The pages name a parallel
+only.  The recurrence itself is in ``vla_oracle.py``; the functions here re-derive the same
+results in the blocked forms the kernels are built on (the forward in chunks and in time
+segments, and the gradients in time segments), and the tests check them against the
+sequential oracle and the autograd oracle before any kernel is trusted.  The pages name a parallel
 scan formulation but give no detail (VLA summary §2.4); the blocked forms below are
 derived from the recurrence of §2.3 with the Woodbury identity and the UT/WY transform.
 
@@ -30,7 +31,7 @@ import numpy as np
 
 from .vla_oracle import phi
 
-__all__ = ["ldl_unit_lower", "chunk_step", "chunked_forward", "segment_forward"]
+__all__ = ["ldl_unit_lower", "chunk_step", "chunked_forward", "segment_forward", "segment_backward"]
 
 
 def _unit_rows(x):
@@ -132,3 +133,107 @@ def segment_forward(q, k, v, u, lambda0, eps=1e-6, seg=64):
             out[a + j] = Sx @ Fq[j] / (n @ Fq[j] + eps)
         S = S @ Pi + B
     return out, S, maps[-1][3]
+
+
+def segment_backward(q, k, v, u, lambda0, d_out, dS_T=None, dA_T=None, dn_T=None, eps=1e-6, seg=64):
+    """Gradients (dq, dk, dv, du [T, d], dlambda0) of
+    L = <d_out, out> + <dS_T, S_T> + <dA_T, A_T> + <dn_T, n_T>  for one stream [T, d], in
+    time segments of ``seg`` tokens: the form the segment-parallel backward kernels follow.
+
+    * The cotangent of A_t is never formed.  A_t = (lambda0 I + sum_{s<=t} u_s u_s^T)^{-1}
+      (Sherman-Morrison keeps it exactly, VLA summary §2.2) reaches the loss only through
+      y_t = A_t khat_t and through A_T, and d(X^{-1}) = -X^{-1} dX X^{-1}; so with
+      w_t = A_t dy_t and R_s = sum_{t>=s} (w_t y_t^T + y_t w_t^T) / 2 + A_T sym(dA_T) A_T,
+          du_s = -2 R_s u_s,      dlambda0 = -tr R_0.
+    * The cotangent of S obeys dS_{t-1} = (dS_t + dnum_t phi(q_t)^T)(I - ahat_t khat_t^T):
+      affine in dS_t with coefficients fixed by the forward, so each segment maps the
+      cotangent E at its end to  E Lm + Bm  at its start; the maps compose from the last
+      segment back.  dn is a suffix sum of dden_t phi(q_t); R a suffix sum over segments.
+    * Each segment is then swept from its end with the true dS and dn, R local to the
+      segment, and du is completed with -2 R_end u over the segment's tokens.
+    """
+    q, k, v, u, d_out = (np.asarray(x, dtype=np.float64) for x in (q, k, v, u, d_out))
+    T, d = q.shape
+    dS_T = np.zeros((d, d)) if dS_T is None else np.asarray(dS_T, dtype=np.float64)
+    dA_T = np.zeros((d, d)) if dA_T is None else np.asarray(dA_T, dtype=np.float64)
+    dn_T = np.zeros(d) if dn_T is None else np.asarray(dn_T, dtype=np.float64)
+    dphi = lambda x: np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+    bounds = [(a, min(T, a + seg)) for a in range(0, T, seg)]
+    P = len(bounds)
+    # forward per segment from its start state (the start states by a plain forward), keeping
+    # each token's quantities and the state after it
+    S, A, n = np.zeros((d, d)), np.eye(d) / lambda0, np.zeros(d)
+    recs = []
+    for a, b in bounds:
+        rs = []
+        for t in range(a, b):
+            rk = 1.0 / np.linalg.norm(k[t])
+            kh = k[t] * rk
+            z = A @ u[t]
+            A = A - np.outer(z, z) / (1.0 + u[t] @ z)
+            y = A @ kh
+            yn = np.linalg.norm(y)
+            ah = y / yn
+            r = v[t] - S @ kh
+            S_prev = S
+            S = S + np.outer(r, ah)
+            n = n + phi(k[t])
+            fq = phi(q[t])
+            den = n @ fq + eps
+            rs.append(dict(kh=kh, ah=ah, y=y, yn=yn, rk=rk, r=r, fq=fq, den=den, o=S @ fq / den,
+                           S=S, S_prev=S_prev, A=A, n=n))
+        recs.append(rs)
+    A_T = A
+    # segment maps of the S cotangent and segment sums of dden phi(q) (not needed for the
+    # first segment)
+    Lm, Bm, nd = [None] * P, [None] * P, [None] * P
+    for p in range(1, P):
+        a, _ = bounds[p]
+        L, B, ndp = np.eye(d), np.zeros((d, d)), np.zeros(d)
+        for j in reversed(range(len(recs[p]))):
+            rc, t = recs[p][j], a + j
+            ndp = ndp - (d_out[t] @ rc["o"]) / rc["den"] * rc["fq"]
+            B = B + np.outer(d_out[t] / rc["den"], rc["fq"])
+            B = B - np.outer(B @ rc["ah"], rc["kh"])
+            L = L - np.outer(L @ rc["ah"], rc["kh"])
+        Lm[p], Bm[p], nd[p] = L, B, ndp
+    # the cotangents at every segment end, from the last segment back
+    E, dn_end = [None] * P, [None] * P
+    E[P - 1], dn_end[P - 1] = dS_T, dn_T
+    for p in range(P - 1, 0, -1):
+        E[p - 1] = E[p] @ Lm[p] + Bm[p]
+        dn_end[p - 1] = dn_end[p] + nd[p]
+    # per segment, from its end: gradients with R local to the segment
+    dq, dk, dv, du = (np.zeros((T, d)) for _ in range(4))
+    W, trace = [None] * P, 0.0
+    for p in range(P):
+        a, _ = bounds[p]
+        dS, dn, R = E[p].copy(), dn_end[p].copy(), np.zeros((d, d))
+        for j in reversed(range(len(recs[p]))):
+            rc, t = recs[p][j], a + j
+            dden = -(d_out[t] @ rc["o"]) / rc["den"]
+            dnum = d_out[t] / rc["den"]
+            dS = dS + np.outer(dnum, rc["fq"])
+            dq[t] = (rc["S"].T @ dnum + dden * rc["n"]) * dphi(q[t])
+            dn = dn + dden * rc["fq"]
+            dr = dS @ rc["ah"]
+            dah = dS.T @ rc["r"]
+            dv[t] = dr
+            dy = (dah - rc["ah"] * (rc["ah"] @ dah)) / rc["yn"]
+            dS = dS - np.outer(dr, rc["kh"])
+            w = rc["A"] @ dy
+            dkh = w - rc["S_prev"].T @ dr
+            R = R + 0.5 * (np.outer(w, rc["y"]) + np.outer(rc["y"], w))
+            trace += w @ rc["y"]
+            du[t] = -2.0 * R @ u[t]
+            dk[t] = (dkh - rc["kh"] * (rc["kh"] @ dkh)) * rc["rk"] + dn * dphi(k[t])
+        W[p] = R
+    # R at every segment end (suffix sums after the final-state term) completes du
+    X = A_T @ (0.5 * (dA_T + dA_T.T)) @ A_T
+    R_end = X.copy()
+    for p in range(P - 1, -1, -1):
+        a, b = bounds[p]
+        du[a:b] -= 2.0 * u[a:b] @ R_end
+        R_end = R_end + W[p]
+    dlambda0 = -(trace + np.trace(X))
+    return dq, dk, dv, du, dlambda0

@@ -9,7 +9,7 @@ difference (L(x + h) - L(x - h)) / 2h has error O(h^2) ~ 1e-10 relative at h = 1
 import numpy as np
 import pytest
 
-from oracle import vla_forward, vla_forward_torch, vla_grad
+from oracle import forms, vla_forward, vla_forward_torch, vla_grad
 
 
 def _loss(q, k, v, u, lam, cot, eps):
@@ -91,3 +91,23 @@ def test_planted_mistake_in_the_forward_fails_the_pin():
         fd = (_loss(q, plus, v, u, 0.9, cot, 1e-6) - _loss(q, minus, v, u, 0.9, cot, 1e-6)) / (2 * h)
         worst = max(worst, abs(tk.grad.numpy()[idx] - fd) / max(1.0, abs(fd)))
     assert worst > 1e-3
+
+
+@pytest.mark.parametrize("T,seg,d,lam,state", [(23, 8, 4, 0.7, True), (17, 17, 3, 1.3, True),
+                                                (25, 6, 5, 0.2, False), (9, 4, 2, 2.0, True)])
+def test_segment_backward_form_equals_autograd(T, seg, d, lam, state):
+    """The time-segment form of the gradients (the cotangent of A replaced by the suffix sum R,
+    the S cotangent through per-segment affine maps, last segments ragged or a single segment)
+    equals the autograd oracle, which is itself pinned to finite differences above."""
+    r = np.random.default_rng([T, seg, d])
+    q, k, v, u, dout = (r.standard_normal((T, d)) for _ in range(5))
+    dS = r.standard_normal((d, d)) if state else None
+    dA = r.standard_normal((d, d)) if state else None
+    dn = r.standard_normal(d) if state else None
+    got = forms.segment_backward(q, k, v, u, lam, dout, dS, dA, dn, eps=1e-6, seg=seg)
+    ref = vla_grad(q[None], k[None], v[None], u[None], lam, dout[None],
+                   None if dS is None else dS[None], None if dA is None else dA[None],
+                   None if dn is None else dn[None], eps=1e-6)
+    for name, g, rf in zip(("dq", "dk", "dv", "du"), got[:4], ref[:4]):
+        assert np.allclose(g, rf[0], rtol=1e-9, atol=1e-9 * np.abs(rf[0]).max()), name
+    assert abs(got[4] - ref[4][0]) <= 1e-9 * max(1.0, abs(ref[4][0]))
