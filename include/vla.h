@@ -206,12 +206,20 @@ vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes);
  * dq, dk, dv, du  device pointers, [B, H, T, d] fp32, fully overwritten.
  * dlambda0    device pointer to [B * H] fp32 receiving each stream's share of dL/dlambda0
  *             (their sum is the derivative; every stream starts from I / lambda0), or NULL.
- * desc        path VLA_PATH_AUTO or VLA_PATH_SEQ, gain VLA_GAIN_UNIT, else
- *             VLA_ERROR_NOT_SUPPORTED; the workspace holds vla_backward_workspace_size()
- *             bytes (per stream: T x (6 d + 8) floats of per-token vectors and the state at
- *             every 32nd token), else the per-device cache is used as for vla_forward.
- * Runs one workgroup per stream, token by token (a replay of the forward, then the reverse
- * sweep).  At ||k_t|| = 0 or ||A_t khat_t|| = 0 the normalisation has no derivative; the
+ * desc        gain VLA_GAIN_UNIT, else VLA_ERROR_NOT_SUPPORTED.  path VLA_PATH_SEQ: one segment
+ *             per stream (a replay of the forward token by token, then the reverse sweep).
+ *             VLA_PATH_CHUNK: time split into the chunked forward's segments (desc->chunk, 0 =
+ *             default; unsupported chunk or d: VLA_ERROR_NOT_SUPPORTED), all segments run in
+ *             parallel: the chunked forward's passes give the state at every segment start,
+ *             the cotangent of S crosses segments through per-segment affine maps (the reverse
+ *             of the forward's segment maps) and the cotangents of n and of the penalty through
+ *             suffix sums.  VLA_PATH_AUTO: CHUNK for fewer than 128 streams when that gives at
+ *             least four segments per stream, else SEQ.  VLA_PATH_DECODE: NOT_SUPPORTED.
+ *             The workspace holds vla_backward_workspace_size() bytes (per stream T x (6 d + 8)
+ *             floats of per-token vectors and the state at every 32nd token; with time segments
+ *             the chunked forward's workspace and an fp64 d x d matrix per segment on top), else
+ *             the per-device cache is used as for vla_forward.
+ * At ||k_t|| = 0 or ||A_t khat_t|| = 0 the normalisation has no derivative; the
  * gradient through it is taken as 0.  The gradients (and a caller's workspace) must overlap
  * neither one another nor any input, else VLA_ERROR_INVALID_VALUE.  Ownership, asynchrony and
  * error behaviour are those of vla_forward.
