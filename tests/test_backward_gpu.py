@@ -169,3 +169,50 @@ def test_backward_full_workload_sampled_streams(name, sample):
     _say(f"[parity] backward full {name}: " + " ".join(f"{n}={e:.3e} (bar {bars[n]:.1e})" for n, e in errs.items()))
     for n, e in errs.items():
         assert e < bars[n], f"{n} rel L2 {e:.3e} >= {bars[n]:.3e}"
+
+
+# Time segments on the method's edge cases: u = 0 (the delta rule, A stays I / lambda0) and
+# u = k with a small lambda0 (ill-conditioned segment starts), and d = 128 with fp32 inputs.
+# Bars as for the long streams: the larger of the forward's bar and four times the deviation
+# of the same steps in plain fp32 for dq, dk, dv, du; dlambda0 (a closed form) at the bar.
+BW_EDGE = [("u0", "f32", 64, 300, 0.7), ("u0", "bf16", 96, 600, 0.7),
+           ("uk", "f32", 32, 300, 0.05), ("uk", "bf16", 96, 1100, 0.05),
+           ("iid", "f32", 128, 200, 0.9)]
+
+
+@pytest.mark.parametrize("kind,dt,d,T,lam", BW_EDGE)
+def test_backward_segments_edge_cases(kind, dt, d, T, lam):
+    H = 2
+    w = get_workload("tiny_t256_d32").resized(name=f"bwe_{kind}_{dt}_{d}_{T}", B=1, H=H, T=T, d=d,
+                                              dtype=dt, lambda0=lam)
+    q, k, v, u = make_inputs(w)
+    if kind == "u0":
+        u = np.zeros_like(u)
+    elif kind == "uk":
+        u = k.copy()
+    r = np.random.default_rng([23, d, T])
+    dout = r.standard_normal(q.shape).astype(np.float32)
+    dS = r.standard_normal((H, d, d)).astype(np.float32)
+    dA = r.standard_normal((H, d, d)).astype(np.float32)
+    dn = r.standard_normal((H, d)).astype(np.float32)
+    dev = [torch.from_numpy(np.ascontiguousarray(x)).view(1, H, T, d).to(torch_dtype(w)).cuda()
+           for x in (q, k, v, u, dout)]
+    seen = [x.float().cpu().numpy().reshape(H, T, d) for x in dev]
+    _say(f"[case] backward time segments {kind} {dt} d={d} T={T} lambda0={lam}")
+    got = vla.backward(*dev[:4], lam, dev[4], dS_T=torch.from_numpy(dS).view(1, H, d, d).cuda(),
+                       dA_T=torch.from_numpy(dA).view(1, H, d, d).cuda(),
+                       dn_T=torch.from_numpy(dn).view(1, H, d).cuda(), eps=w.eps, path="chunk")
+    torch.cuda.synchronize()
+    ref = vla_grad(*(x.astype(np.float64) for x in seen[:4]), lam, seen[4].astype(np.float64),
+                   dS.astype(np.float64), dA.astype(np.float64), dn.astype(np.float64), eps=w.eps)
+    ref32 = vla_grad(*seen[:4], lam, seen[4], dS, dA, dn, eps=w.eps, dtype=torch.float32)
+    tol = TOL[dt]
+    names = ("dq", "dk", "dv", "du")
+    bars = {n: max(tol, 4.0 * rel_l2(r32, rf)) for n, r32, rf in zip(names, ref32[:4], ref[:4])}
+    bars["dlambda0"] = tol
+    errs = {n: rel_l2(g.cpu().numpy().reshape(H, T, d), rf) for n, g, rf in zip(names, got[:4], ref[:4])}
+    errs["dlambda0"] = rel_l2(got[4].cpu().numpy().reshape(H), ref[4])
+    _say(f"[parity] backward time segments {kind} {dt} d={d}: " +
+         " ".join(f"{n}={e:.3e} (bar {bars[n]:.1e})" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e < bars[n], f"{n} rel L2 {e:.3e} >= {bars[n]:.3e}"
