@@ -258,7 +258,8 @@ vla_status_t scratch_address(void **out) {
 }
 
 // vla_forward_state and vla_forward_state_noalloc.  With `noalloc` the chunked path's scratch
-// is the device's static array (never an allocation) and no timing events are created.
+// is the device's static array (never an allocation), and neither timing events nor the
+// events of a two-stream split of large calls are created.
 vla_status_t forward_state_impl(const void *q, const void *k, const void *v, const void *u,
                                 float lambda0, const float *S0, const float *A0, const float *n0,
                                 void *out, float *S_final, float *A_final, float *n_final,
@@ -328,7 +329,7 @@ vla_status_t forward_state_impl(const void *q, const void *k, const void *v, con
   else if (path == VLA_PATH_DECODE)
     err = vla::launch_decode(p, q, k, v, u, out, sio, s);
   else
-    err = vla::launch_chunk(p, chunk, q, k, v, u, out, sio, ws, s);
+    err = vla::launch_chunk(p, chunk, q, k, v, u, out, sio, ws, s, !noalloc);
   return err == hipSuccess ? VLA_SUCCESS : VLA_ERROR_LAUNCH;
 }
 

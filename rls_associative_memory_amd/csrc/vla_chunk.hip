@@ -15,7 +15,8 @@
 //   Num = Fq X_start^T + tril0(Fq ahat^T) E,
 // whose rows e_j = v_j - S_{j-1} khat_j are exactly the sequential residuals.
 //
-// Passes (launched in order on one stream; every pass is parallel over (stream, segment)):
+// Passes (launched in order on one stream; every pass is parallel over (stream, segment);
+// large calls run their streams as two groups, each in this order on its own HIP stream):
 //   k_gram     Gram_p = U_p^T U_p (MFMA) and sum phi(k) per segment
 //   k_prefix   exclusive prefix over segments in fp64: M_p = lambda0 I + sum_{p'<p} Gram
 //   k_inv      A at each segment start = M_p^{-1} (in-place Gauss-Jordan, SPD, fp32)
@@ -30,7 +31,9 @@
 // chunk products of the WY form and the segment-map composition.
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "vla_common.h"
 #include "vla_internal.h"
@@ -1337,14 +1340,108 @@ static hipError_t launch_chunk_dt(const Problem &pr, const ChunkPlan &pl, const 
   return hipErrorInvalidValue;
 }
 
+// Streams [h, h + n) of a call: the same segments (L and P of the whole call's plan, so every
+// stream's arithmetic is the same as in one launch over all streams), every workspace array
+// and every input, output and state pointer moved to stream h (all are stream-major).
+static hipError_t launch_chunk_group(const Problem &p, const ChunkPlan &pl, int64_t h, int64_t n,
+                                     const void *q, const void *k, const void *v, const void *u,
+                                     void *out, const StateIO &st, char *w, hipStream_t stream) {
+  const size_t D = static_cast<size_t>(pl.D), P = static_cast<size_t>(pl.P);
+  const size_t T = static_cast<size_t>(pl.T), hs = static_cast<size_t>(h);
+  ChunkPlan g = pl;
+  g.S = n;
+  g.off_m += hs * P * D * D * 4;
+  g.off_nk += hs * P * D * 4;
+  g.off_alpha += hs * T * D * 4;
+  g.off_rkden += hs * T * 2 * 4;
+  g.off_pib += hs * P * 2 * D * D * 4;
+  g.off_s0 += hs * P * D * D * 4;
+  g.off_minv += hs * D * D * 4;
+  Problem gp = p;
+  gp.streams = n;
+  const size_t tok = hs * T * D * (p.dtype == Dtype::F32 ? 4 : 2);
+  auto in = [&](const void *x) { return static_cast<const void *>(static_cast<const char *>(x) + tok); };
+  auto mat = [&](auto *x, size_t per) { return x != nullptr ? x + hs * per : x; };
+  StateIO gs;
+  gs.S0 = mat(st.S0, D * D);
+  gs.A0 = mat(st.A0, D * D);
+  gs.n0 = mat(st.n0, D);
+  gs.S_final = mat(st.S_final, D * D);
+  gs.A_final = mat(st.A_final, D * D);
+  gs.n_final = mat(st.n_final, D);
+  void *o = static_cast<char *>(out) + tok;
+  if (p.dtype == Dtype::F32)
+    return launch_chunk_dt<float>(gp, g, in(q), in(k), in(v), in(u), o, gs, w, stream, false, nullptr);
+  return launch_chunk_dt<bf16_t>(gp, g, in(q), in(k), in(v), in(u), o, gs, w, stream, false, nullptr);
+}
+
+// The library's second HIP stream on the current device: created once, default priority,
+// not synchronised with the legacy null stream (ordering comes from events only).  nullptr if
+// it cannot be created.
+static hipStream_t side_stream() {
+  static std::mutex mu;
+  static std::vector<hipStream_t> per_device;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (static_cast<int>(per_device.size()) <= dev) per_device.resize(dev + 1, nullptr);
+  if (per_device[dev] == nullptr) {
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess) per_device[dev] = s;
+  }
+  return per_device[dev];
+}
+
+// Whether a call's streams run as two groups on two HIP streams.  Each pass then ends in two
+// partly filled last waves of workgroups instead of one, and each group's short scan passes
+// (k_prefix, k_inv, k_sprefix: a few hundred workgroups) run beside the other group's long
+// ones.  On 32 streams x 131072 tokens at d = 96 this takes about 3 % off the call, on
+// 32 x 43008 at d = 128 about 8 %; below about 2^20 tokens per call the extra launches and
+// events cost more than the overlap gains (4 x 8 x 4096 at d = 64: 2 % slower).  Not used
+// while the stream is being captured into a graph.
+static bool split_in_two(const Problem &p, hipStream_t stream) {
+  if (p.streams < 2 || p.streams * p.T < (int64_t(1) << 20)) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();  // not a failure of this call
+    return false;
+  }
+  return cs == hipStreamCaptureStatusNone;
+}
+
 hipError_t launch_chunk(const Problem &p, int chunk, const void *q, const void *k,
                         const void *v, const void *u, void *out, const StateIO &st, void *ws,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool may_split) {
   if (!chunk_supported(p, chunk)) return hipErrorInvalidValue;
   const ChunkPlan pl = make_plan(p, chunk);
   char *w = static_cast<char *>(ws);
-  if (p.dtype == Dtype::F32) return launch_chunk_dt<float>(p, pl, q, k, v, u, out, st, w, stream, false, nullptr);
-  return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, out, st, w, stream, false, nullptr);
+  hipStream_t side = may_split && split_in_two(p, stream) ? side_stream() : nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (side != nullptr &&
+      (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
+       hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess ||
+       hipEventRecord(fork, stream) != hipSuccess ||
+       hipStreamWaitEvent(side, fork, 0) != hipSuccess)) {
+    // no second stream after all: one launch over all streams on the caller's stream (a
+    // recorded fork event that the side stream waits for orders nothing of this call)
+    if (fork != nullptr) (void)hipEventDestroy(fork);
+    if (join != nullptr) (void)hipEventDestroy(join);
+    (void)hipGetLastError();
+    side = nullptr;
+  }
+  if (side == nullptr) return launch_chunk_group(p, pl, 0, p.streams, q, k, v, u, out, st, w, stream);
+  const int64_t h = p.streams / 2;
+  hipError_t e0 = launch_chunk_group(p, pl, 0, h, q, k, v, u, out, st, w, stream);
+  hipError_t e1 = launch_chunk_group(p, pl, h, p.streams - h, q, k, v, u, out, st, w, side);
+  // the caller's stream waits for the side stream's group whatever happened above, so that
+  // nothing of this call is still running on it once the caller's stream has passed
+  hipError_t e2 = hipEventRecord(join, side);
+  if (e2 == hipSuccess) e2 = hipStreamWaitEvent(stream, join, 0);
+  (void)hipEventDestroy(fork);
+  (void)hipEventDestroy(join);
+  if (e0 != hipSuccess) return e0;
+  if (e1 != hipSuccess) return e1;
+  return e2;
 }
 
 void chunk_segments(const Problem &p, int chunk, int64_t *L, int64_t *P) {

@@ -39,9 +39,12 @@ hipError_t launch_decode(const Problem &p, const void *q, const void *k, const v
 size_t chunk_workspace_bytes(const Problem &p, int chunk);
 bool chunk_supported(const Problem &p, int chunk);
 int chunk_default(const Problem &p);
+// With `may_split`, calls of at least 2^20 tokens on two or more streams (not under graph
+// capture) run half of the streams on a library-owned second HIP stream of the device, forked
+// from and joined back into `stream` with events; the result is the same either way.
 hipError_t launch_chunk(const Problem &p, int chunk, const void *q, const void *k,
                         const void *v, const void *u, void *out, const StateIO &st, void *ws,
-                        hipStream_t stream);
+                        hipStream_t stream, bool may_split);
 
 // The chunked path's passes up to the segment-start states (no outputs): S, A and n at the
 // start of every segment [streams][P][...] and the pass's segment-map buffer

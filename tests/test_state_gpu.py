@@ -85,6 +85,31 @@ def test_state_continuation_matches_oracle(d, dt, path):
     _compare(f"state d={d} {dt} {path}", TOL[dt], got, ref)
 
 
+# A chunked-path call of at least 2^20 tokens on two or more streams runs its streams as two
+# groups, the second on a second HIP stream of the library, each with its own slices of the
+# inputs, outputs, carried states and workspace.  An odd stream count gives groups of unequal
+# size (here 2 and 3); every stream is checked on its own against the oracle.  The wide
+# workloads (32 streams at d = 96 and d = 128) cover the two groups at full size.
+@pytest.mark.timeout(600)
+def test_state_continuation_two_stream_groups():
+    d, H, T0, T1 = 32, 5, 100, 210000
+    assert H * T1 >= 1 << 20
+    _say(f"[case] carried state, two stream groups: {H} streams x {T1} tokens, d={d}, bf16")
+    w, (q, k, v, u), (S0, A0, n0), ref = _case(d, "bf16", T0, T1, H=H)
+    shp = (1, H, T1, d)
+    dq, dk, dv, du = (_dev(x[:, T0:], w, shp) for x in (q, k, v, u))
+    out, S, A, n = vla.forward_state(dq, dk, dv, du, 0.0, S0=torch.from_numpy(S0).view(1, H, d, d).cuda(),
+                                     A0=torch.from_numpy(A0).view(1, H, d, d).cuda(),
+                                     n0=torch.from_numpy(n0).view(1, H, d).cuda(), eps=w.eps,
+                                     path="chunk", chunk=64)
+    torch.cuda.synchronize()
+    got = (_np(out).reshape(H, T1, d), _np(S).reshape(H, d, d), _np(A).reshape(H, d, d),
+           _np(n).reshape(H, d))
+    for s in range(H):
+        _compare(f"two groups d={d} stream {s}", TOL["bf16"], tuple(g[s] for g in got),
+                 tuple(r[s] for r in ref))
+
+
 @pytest.mark.parametrize("path", ["seq", "chunk"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_two_calls_equal_one_call(path, dt):
