@@ -7,7 +7,8 @@
 //   Z  = L^{-1} (U A)        row j is z_j = A_{j-1} u_j,  D_jj = delta_j
 //   Y  = K A - tril0(K Z^T) D^{-1} Z          row j is A_j k_j (gate before normalising)
 //   A <- A - Z^T D^{-1} Z
-// and ahat_j = Y_j / ||Y_j|| (§2.3 step 2; the key's norm cancels).
+// and ahat_j = Y_j / ||Y_j|| (§2.3 step 2; the key's norm cancels), written as its two bf16
+// terms (hi, then the residual lo) in a row of 2d per token, which the S passes use as they are.
 //
 // Layout.  Wave w holds column tile w of A (16 columns, all rows) in MFMA accumulators.
 // Because A is symmetric, those registers are also row tile w of A, i.e. exactly the
@@ -69,7 +70,7 @@ __global__ void __launch_bounds__((AwyCfg<D, TERMS>::NT))
 __attribute__((amdgpu_waves_per_eu(awy_waves_per_simd<D, TERMS>())))
 k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
            const bf16_t *__restrict__ u, const float *__restrict__ A0,
-           float *__restrict__ nk, float *__restrict__ alpha, float *__restrict__ rkden,
+           float *__restrict__ nk, uint16_t *__restrict__ ahat, float *__restrict__ rkden,
            float *__restrict__ A_final, int64_t T, int64_t L,
            int64_t P, float eps) {
   using C = AwyCfg<D, TERMS>;
@@ -91,7 +92,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   const uint16_t *us = reinterpret_cast<const uint16_t *>(u) + s * T * D;
   const uint16_t *ks = reinterpret_cast<const uint16_t *>(k) + s * T * D;
   const uint16_t *qs = reinterpret_cast<const uint16_t *>(q) + s * T * D;
-  float *al = alpha + s * T * D;
+  uint16_t *al = ahat + s * T * 2 * D;
   float *rd = rkden + s * T * 2;
 
   // Column tile w of A: At[it][r] = A[16 it + 4 gq + r][16 w + li].
@@ -533,9 +534,23 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) tot += sh.norm[w2][c];
       const float inv = tot > 0.f ? rsqrtf(tot) : 0.f;
-      if (c < m)
-        *reinterpret_cast<float4 *>(&al[c0 * D + static_cast<uint32_t>(c * D + 16 * w + 4 * gq)]) =
-            make_float4(Yt[ct][0] * inv, Yt[ct][1] * inv, Yt[ct][2] * inv, Yt[ct][3] * inv);
+      if (c < m) {
+        // ahat as its two bf16 terms, hi then lo, each token's row [term][d]: the S passes
+        // take the terms as they are
+        // (the fp32 value is rounded first, not contracted into the residuals of the split)
+        float a4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          a4[r] = Yt[ct][r] * inv;
+          asm volatile("" : "+v"(a4[r]));
+        }
+        uint32_t w01[2], w23[2];
+        split_pk<2>(a4[0], a4[1], w01);
+        split_pk<2>(a4[2], a4[3], w23);
+        uint16_t *row = &al[c0 * 2 * D + static_cast<uint32_t>(c * 2 * D + 16 * w + 4 * gq)];
+        *reinterpret_cast<uint2 *>(row) = make_uint2(w01[0], w23[0]);
+        *reinterpret_cast<uint2 *>(row + D) = make_uint2(w01[1], w23[1]);
+      }
     }
     // ---- A <- A - W^T W on this wave's column tile ------------------------------------------
     {

@@ -1243,6 +1243,8 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
   float *Mw = reinterpret_cast<float *>(ws + pl.off_m);
   float *nkw = reinterpret_cast<float *>(ws + pl.off_nk);
   float *alw = reinterpret_cast<float *>(ws + pl.off_alpha);
+  // bf16 inputs: ahat as its two bf16 terms, each token's row [hi d | lo d] (same bytes)
+  uint16_t *alh = reinterpret_cast<uint16_t *>(ws + pl.off_alpha);
   float *rdw = reinterpret_cast<float *>(ws + pl.off_rkden);
   float *pbw = reinterpret_cast<float *>(ws + pl.off_pib);
   float *s0w = reinterpret_cast<float *>(ws + pl.off_s0);
@@ -1279,10 +1281,10 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // which two-term operands, 16 significant bits, cannot absorb).
     if (sio.A0 == nullptr && pr.lambda0 < static_cast<float>(D) / 256.0f) {
       VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 3>), dim3(S, P), dim3(AwyCfg<D, 3>::NT), 0, st, qq,
-                 kk, uu, Mw, nkw, alw, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
+                 kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
     } else {
       VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2>), dim3(S, P), dim3(AwyCfg<D, 2>::NT), 0, st, qq,
-                 kk, uu, Mw, nkw, alw, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
+                 kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
     }
   } else {
     using AC = AsideCfg<D>;
@@ -1295,7 +1297,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // bf16 inputs: S side on the bf16 matrix cores.
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, P - 1),
-                 dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
+                 dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alh, rdw, s0w, pbw, oo,
                  S_final, static_cast<const float *>(nullptr), pl.T, pl.L, pl.P);
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
@@ -1306,7 +1308,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // segment maps it starts from do not depend on either pass's chunking.
     constexpr int CF = CH < 32 ? CH : 32;
     VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT), 0,
-               st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final, nkw, pl.T, pl.L, pl.P);
+               st, qq, kk, vv, alh, rdw, s0w, pbw, oo, S_final, nkw, pl.T, pl.L, pl.P);
   } else {
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),

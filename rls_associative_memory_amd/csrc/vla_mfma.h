@@ -113,6 +113,13 @@ __device__ __forceinline__ bf16x8_t ld_tr4x2(const uint16_t *m, int ld, int r0, 
   return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
 }
 
+// The first block of ld_tr4x2 (lane i gets M[r0 + e][c0 + i]) and zeros for the second.
+__device__ __forceinline__ bf16x8_t ld_tr4z(const uint16_t *m, int ld, int r0, int c0, int li) {
+  const int dr = li >> 2, dc = 4 * (li & 3);
+  const uint2 a = ld_tr4(m + (r0 + dr) * ld + c0 + dc);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, 0u, 0u));
+}
+
 // N terms of a row-major matrix (term stride in elements), each read as ld_tr4x2
 template <int N>
 __device__ __forceinline__ void ld_tr_n(bf16x8_t (&dst)[N], const uint16_t *m, int term_stride, int ld,

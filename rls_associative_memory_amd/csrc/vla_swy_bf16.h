@@ -15,7 +15,8 @@
 // v_mfma_f32_16x16x32_bf16.  Raw k and v are exact bf16; khat = rk * k is applied after the
 // product.  ahat, phi(q), the state, Ka, Qa and E are fp32 values split into two bf16 terms
 // (hi + lo, about 16 significant bits) multiplied term pair by term pair with fp32
-// accumulation, which keeps each product's relative error near 2^-16.
+// accumulation, which keeps each product's relative error near 2^-16.  ahat arrives already
+// split (the A side writes each token's row as [hi d | lo d]) and is staged by token as it is.
 #pragma once
 
 #include "vla_common.h"
@@ -38,7 +39,6 @@ struct SwbCfg {
   static constexpr int NKS = D / 32;          // 32-feature slices
   static constexpr int NKT = NCT * (NCT + 1) / 2;
   static constexpr int LDF = D + 8;           // bf16 row stride of token rows
-  static constexpr int LDC = CH + 8;          // bf16 row stride of token-indexed columns
   static constexpr int LDI = 24;              // bf16 row stride of the 16 x 16 inverses
   static_assert(D % 32 == 0, "feature dimension must be a multiple of 32");
 };
@@ -49,7 +49,7 @@ struct SwbLds {
   static constexpr int QR = FINAL ? CH : 1;
   uint16_t sK[CH][C::LDF];                    // raw k, by token
   uint16_t sV[CH][C::LDF];                    // raw v, by token
-  uint16_t sAt[2][D][C::LDC];                 // ahat terms, by feature (read transposed for Ka, Qa)
+  uint16_t sAt[2][CH][C::LDF];                // ahat terms, by token (read transposed for the state update)
   uint16_t sFq[2][QR][C::LDF];                // phi(q) terms, by token (final pass)
   // 16 x 16 tiles as two bf16 terms, stored transposed ([col][row]): a lane writes its column
   // with wide stores, and the A operands are read back with the transposing load.
@@ -72,14 +72,14 @@ template <int D, int CH, bool FINAL>
 __global__ void __launch_bounds__((SwbCfg<D, CH, FINAL>::NT))
 __attribute__((amdgpu_waves_per_eu(swb_waves_per_simd<D, FINAL>())))
 k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
-       const float *__restrict__ alpha, const float *__restrict__ rkden,
+       const uint16_t *__restrict__ ahat, const float *__restrict__ rkden,
        const float *__restrict__ s0, float *__restrict__ pib, bf16_t *__restrict__ out,
        float *__restrict__ S_final, const float *__restrict__ nstart, int64_t T, int64_t L,
        int64_t P) {
   using C = SwbCfg<D, CH, FINAL>;
   constexpr int NT = C::NT, NCT = C::NCT, NFT = C::NFT, NKS = C::NKS;
   constexpr int TQ = SwbLds<D, CH, FINAL>::QR * C::LDF;
-  constexpr int TA = D * C::LDC;
+  constexpr int TA = CH * C::LDF;
   constexpr int TQD = (FINAL ? NCT : 1) * 16 * C::LDI;
   constexpr int NOD = C::NOD, NPR = C::NPR;
   constexpr int TKO = (NOD > 0 ? NOD : 1) * 16 * C::LDI;
@@ -94,7 +94,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   const uint16_t *ks = reinterpret_cast<const uint16_t *>(k) + s * T * D;
   const uint16_t *vs = reinterpret_cast<const uint16_t *>(v) + s * T * D;
   const uint16_t *qs = reinterpret_cast<const uint16_t *>(q) + s * T * D;
-  const float *als = alpha + s * T * D;
+  const uint16_t *als = ahat + s * T * 2 * D;
   const float *rds = rkden + s * T * 2;
 
   const bool pi_rows = !FINAL && wave < C::NWV;
@@ -125,18 +125,20 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   // selected on (which would make the load wait at once).
   constexpr int RV = D / 8;                   // uint4 per token row
   constexpr int UK = CH * RV;
-  constexpr int UA = CH / 2 * D / 4;          // (token pair, 4 features) units of ahat
+  constexpr int RA = 2 * D / 8;               // uint4 per token row of ahat terms
+  constexpr int UA = CH * RA;
   constexpr int PK = (UK + NT - 1) / NT;
   constexpr int PA = (UA + NT - 1) / NT;
   uint4 pk[PK], pq[FINAL ? PK : 1], pv[PK];
-  float4 pa[PA][2];
+  uint4 pa[PA];
   float prk = 0.f, pden = 1.f;
   // Per-lane offsets are 32-bit (one stream's rows span far less than 4 GiB) from a
   // workgroup-uniform base, so each load needs one offset register.
   auto prefetch = [&](int64_t cs, int tid) {
     const int mm = static_cast<int>(std::min<int64_t>(CH, te - cs));
     const uint16_t *kc = ks + cs * D, *qc = qs + cs * D, *vc = vs + cs * D;
-    const float *ac = als + cs * D, *rc = rds + cs * 2;
+    const uint16_t *ac = als + cs * 2 * D;
+    const float *rc = rds + cs * 2;
 #pragma unroll
     for (int i = 0; i < PK; ++i) {
       const int ui = tid + i * NT;
@@ -149,12 +151,9 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
     for (int i = 0; i < PA; ++i) {
       const int ui = tid + i * NT;
-      const int c = 2 * (ui % (CH / 2)), f0 = (ui / (CH / 2)) * 4;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t off = (ui < UA && c + h < mm) ? static_cast<uint32_t>((c + h) * D + f0) : 0u;
-        pa[i][h] = *reinterpret_cast<const float4 *>(ac + off);
-      }
+      const int c = ui / RA, j0 = (ui % RA) * 8;
+      const uint32_t off = (ui < UA && c < mm) ? static_cast<uint32_t>(c * 2 * D + j0) : 0u;
+      pa[i] = *reinterpret_cast<const uint4 *>(ac + off);
     }
     const uint32_t toff = (tid < mm) ? static_cast<uint32_t>(tid * 2) : 0u;
     prk = rc[toff];
@@ -215,24 +214,9 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     for (int i = 0; i < PA; ++i) {
       const int ui = tid + i * NT;
       if (ui < UA) {
-        const int c = 2 * (ui % (CH / 2)), f0 = (ui / (CH / 2)) * 4;
-        // w[t][pr][term]: features (f0 + 2 pr, f0 + 2 pr + 1) of token c + t
-        uint32_t w[2][2][2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bool ok = c + t < m;
-          split_pk<2>(ok ? pa[i][t].x : 0.f, ok ? pa[i][t].y : 0.f, w[t][0]);
-          split_pk<2>(ok ? pa[i][t].z : 0.f, ok ? pa[i][t].w : 0.f, w[t][1]);
-        }
-        // by feature: the two tokens of the pair in one 32-bit word
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-          for (int term = 0; term < 2; ++term) {
-            const uint32_t a = w[0][pr][term], b = w[1][pr][term];
-            *reinterpret_cast<uint32_t *>(&sh.sAt[term][f0 + 2 * pr][c]) = (a & 0xffffu) | (b << 16);
-            *reinterpret_cast<uint32_t *>(&sh.sAt[term][f0 + 2 * pr + 1][c]) = (a >> 16) | (b & 0xffff0000u);
-          }
+        const int c = ui / RA, j0 = (ui % RA) * 8;
+        const int term = j0 / D, f0 = j0 % D;
+        *reinterpret_cast<uint4 *>(&sh.sAt[term][c][f0]) = keep_if(c < m, pa[i]);
       }
     }
     if (tid < CH) {
@@ -249,7 +233,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       if constexpr (FINAL) asm volatile("" ::"v"(pq[i].x));
     }
 #pragma unroll
-    for (int i = 0; i < PA; ++i) asm volatile("" ::"v"(pa[i][0].x), "v"(pa[i][1].x));
+    for (int i = 0; i < PA; ++i) asm volatile("" ::"v"(pa[i].x));
     __syncthreads();
     // ---- shared tile products: Ka_tt (each with the inverse of I + Ka_tt), Ka_ba and, in
     //      the final pass, Qa_tt and Qa_ba --------------------------------------------------
@@ -269,9 +253,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
         for (int ksl = 0; ksl < NKS; ++ksl) {
           const int fa = 32 * ksl + 4 * gq;
-          // Ahat[16 ct2 + li][fa + e], [fa + 16 + e] from the by-feature copy, transposed
-          b[ksl].h = ld_tr4x2(&sh.sAt[0][0][0], C::LDC, fa, fa + 16, 16 * ct2, li);
-          b[ksl].l = ld_tr4x2(&sh.sAt[1][0][0], C::LDC, fa, fa + 16, 16 * ct2, li);
+          // Ahat[16 ct2 + li][fa + e], [fa + 16 + e]
+          b[ksl] = ld2_4x2(&sh.sAt[0][16 * ct2 + li][fa], &sh.sAt[0][16 * ct2 + li][fa + 16], TA);
         }
         f4_t part[NKS];
         if (isq) {
@@ -316,37 +299,48 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           }
         } else {
           if (diag) {
-            // (I + Ka_b)^{-1} by forward substitution, column j = lane (lanes 0..15 keep theirs).
-            // -Ka[r][q] is value r % 4 of nv in lane 16 (r / 4) + q, read into a scalar register.
-            // The four values are formed one by one and kept opaque (a vector read this way is
-            // miscompiled), and the reads of pivot q + 1 are tied to x_q so that at most two
-            // pivots' values occupy scalar registers at a time.
-            float nv[4];
+            // (I + Ka_b)^{-1} by forward substitution, column j = li in every lane group (lanes
+            // 0..15 keep theirs).  M = -Ka_b with rows scaled by 1/||k|| is first stored by
+            // column in fp32 over this tile's InvS slots (the inverse overwrites them at the
+            // end): columns 0..11 in the term-0 slot, 12..15 in the term-1 slot, 16 floats
+            // each.  Pivot q then reads column q with broadcast loads (every lane the same
+            // address), one column ahead of its use.
+            float *mc0 = reinterpret_cast<float *>(&sh.InvS[0][ct][0][0]);
+            float *mc1 = reinterpret_cast<float *>(&sh.InvS[1][ct][0][0]);
+            {
+              f4_t nv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              nv[e] = -acc[e] * sh.rk[16 * ct + i + e];
-              asm volatile("" : "+v"(nv[e]));
+              for (int e = 0; e < 4; ++e) nv[e] = -acc[e] * sh.rk[16 * ct + i + e];
+              float *dstc = (li < 12 ? mc0 + 16 * li : mc1 + 16 * (li - 12)) + i;
+              *reinterpret_cast<f4_t *>(dstc) = nv;
             }
-            auto rd = [&](int r, int q) {
-              return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, nv[r & 3]), 16 * (r >> 2) + q));
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            auto col = [&](int q, f4_t (&c)[4]) {
+              const float *src = q < 12 ? mc0 + 16 * q : mc1 + 16 * (q - 12);
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+                if (4 * g + 3 > q) c[g] = *reinterpret_cast<const f4_t *>(src + 4 * g);
             };
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == lane) ? 1.f : 0.f;
-            float kc[16], kn[16];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) kc[r] = rd(r, 0);
+            for (int r = 0; r < 16; ++r) x[r] = (r == li) ? 1.f : 0.f;
+            f4_t cc[2][4];
+            col(0, cc[0]);
 #pragma unroll
             for (int q = 0; q < 15; ++q) {
-              asm volatile("" : "+v"(nv[0]), "+v"(nv[1]), "+v"(nv[2]), "+v"(nv[3]) : "v"(x[q]));
-              if (q + 1 < 15)
+              if (q + 1 < 15) col(q + 1, cc[(q + 1) & 1]);
+              __builtin_amdgcn_sched_barrier(0);  // one column of loads in flight at a time
 #pragma unroll
-                for (int r = q + 2; r < 16; ++r) kn[r] = rd(r, q + 1);
-#pragma unroll
-              for (int r = q + 1; r < 16; ++r) x[r] = fmaf(kc[r], x[q], x[r]);
-#pragma unroll
-              for (int r = q + 2; r < 16; ++r) kc[r] = kn[r];
+              for (int r = q + 1; r < 16; ++r) x[r] = fmaf(cc[q & 1][r >> 2][r & 3], x[q], x[r]);
+              // x[q + 1] is final: formed here in every lane, not sunk into the store branch
+              asm volatile("" : "+v"(x[q + 1]));
+              __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (lane < 16) {
               // column j of the inverse, transposed: row j of InvS, 16 values per term
               uint32_t w[8][2];
@@ -441,9 +435,15 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       Split2 aT[NFT];
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) {
-        const int fr = 16 * ft + li, ca = 16 * ta + 4 * gq;
-        aT[ft] = two ? ld2_4x2(&sh.sAt[0][fr][ca], &sh.sAt[0][fr][ca + 16], TA)
-                     : ld2_4z(&sh.sAt[0][fr][ca], TA);
+        // Ahat[ca + e][16 ft + li] and Ahat[ca + 16 + e][16 ft + li]: the token rows, transposed
+        const int ca = 16 * ta + 4 * gq;
+        if (two) {
+          aT[ft].h = ld_tr4x2(&sh.sAt[0][0][0], C::LDF, ca, ca + 16, 16 * ft, li);
+          aT[ft].l = ld_tr4x2(&sh.sAt[1][0][0], C::LDF, ca, ca + 16, 16 * ft, li);
+        } else {
+          aT[ft].h = ld_tr4z(&sh.sAt[0][0][0], C::LDF, ca, 16 * ft, li);
+          aT[ft].l = ld_tr4z(&sh.sAt[1][0][0], C::LDF, ca, 16 * ft, li);
+        }
       }
       // E_a = (I + Ka_aa)^{-1} R_a;  E_b = (I + Ka_bb)^{-1} (R_b - Ka_ba E_a)
       f4_t E[2];
