@@ -105,6 +105,11 @@ typedef struct {
  * returned and nothing is enqueued on an argument error; the call never aborts or throws.
  * Kernel faults surface at the caller's next synchronisation.  NaN and Inf in the inputs
  * propagate and are not checked.
+ * Streams: a chunked-path call of at least 2^20 tokens (B*H*T) on two or more streams, not
+ * under graph capture, runs half of its (batch, head) streams on a second HIP stream of the
+ * device that the library creates on first use and keeps (default priority, non-blocking),
+ * forked from `stream` and joined back into it with events: the call stays ordered on
+ * `stream` like any other, and its results are those of one launch over all streams.
  */
 vla_status_t vla_forward(const void *q, const void *k, const void *v, const void *u,
                          float lambda0, void *out, float *S_final, float *A_final,
@@ -146,7 +151,8 @@ vla_status_t vla_forward_state(const void *q, const void *k, const void *v, cons
  * hipMalloc.  It runs the same kernels as vla_forward_state on the same arguments, and the
  * chunked path's scratch (vla_workspace_size() bytes) lives in one static device array per
  * GPU of VLA_NOALLOC_SCRATCH_BYTES bytes, held by the library until the process ends; the
- * call allocates nothing and creates no timing events (vla_profile_enable is ignored).
+ * call allocates nothing, creates no timing events (vla_profile_enable is ignored) and never
+ * runs streams on the library's second HIP stream.
  *
  * desc->workspace must be NULL (VLA_ERROR_INVALID_VALUE otherwise).  A descriptor whose
  * chunked path needs more than VLA_NOALLOC_SCRATCH_BYTES of scratch returns
