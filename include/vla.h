@@ -219,7 +219,7 @@ vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes);
  *             parallel: the chunked forward's passes give the state at every segment start,
  *             the cotangent of S crosses segments through per-segment affine maps (the reverse
  *             of the forward's segment maps) and the cotangents of n and of the penalty through
- *             suffix sums.  VLA_PATH_AUTO: CHUNK for fewer than 128 streams when that gives at
+ *             suffix sums.  VLA_PATH_AUTO: CHUNK for at most 256 streams when that gives at
  *             least four segments per stream, else SEQ.  VLA_PATH_DECODE: NOT_SUPPORTED.
  *             The workspace holds vla_backward_workspace_size() bytes (per stream T x (6 d + 8)
  *             floats of per-token vectors and the state at every 32nd token; with time segments

@@ -198,7 +198,10 @@ def test_backward_argument_errors(lib):
     ws = lambda **kw: (lib.vla_backward_workspace_size(ctypes.byref(desc(**kw)), ctypes.byref(n)), n.value)[1]
     long_auto = ws(B=1, H=2, T=4096, d=96)
     assert long_auto == ws(B=1, H=2, T=4096, d=96, path=2) > ws(B=1, H=2, T=4096, d=96, path=1)
-    assert ws(B=1, H=256, T=4096, d=96) == ws(B=1, H=256, T=4096, d=96, path=1)
+    assert ws(B=1, H=256, T=4096, d=96) == ws(B=1, H=256, T=4096, d=96, path=2)
+    assert ws(B=1, H=257, T=4096, d=96) == ws(B=1, H=257, T=4096, d=96, path=1)
+    # 256 fp32 streams of 512 tokens (the recall workload): 64-token segments, eight per stream
+    assert ws(B=64, H=4, T=512, d=32, dtype=0) == ws(B=64, H=4, T=512, d=32, dtype=0, path=2)
 
 
 def test_decode_path_resolution(lib):

@@ -123,10 +123,13 @@ def test_backward_without_state_cotangents_and_long():
     _run(64, "f32", T=300, with_state=False, lam=0.5)
 
 
-@pytest.mark.parametrize("name,sample", [("mqar_t512_d32", (0, 77, 255)), ("iid_t4096_d64", (5,))])
-def test_backward_full_workload_sampled_streams(name, sample):
-    """Every stream of a full-size workload in one call (the launch bench.py times); the
-    gradients of sampled streams against the oracle.  Cotangents are seeded per stream, so a
+@pytest.mark.parametrize("name,sample,path", [("mqar_t512_d32", (0, 77, 255), "auto"),
+                                              ("mqar_t512_d32", (0, 77, 255), "seq"),
+                                              ("iid_t4096_d64", (5,), "auto")])
+def test_backward_full_workload_sampled_streams(name, sample, path):
+    """Every stream of a full-size workload in one call (the launch bench.py times: AUTO, time
+    segments on both workloads); the gradients of sampled streams against the oracle, and the
+    recall workload with one segment per stream as well.  Cotangents are seeded per stream, so a
     sampled stream's cotangents are regenerated on the host without the others."""
     from rls_associative_memory_amd.inputs import make_inputs, upload_inputs
     w = get_workload(name)
@@ -144,8 +147,8 @@ def test_backward_full_workload_sampled_streams(name, sample):
     dS = torch.from_numpy(np.stack([h[1] for h in host])).view(w.B, w.H, d, d).cuda()
     dA = torch.from_numpy(np.stack([h[2] for h in host])).view(w.B, w.H, d, d).cuda()
     dn = torch.from_numpy(np.stack([h[3] for h in host])).view(w.B, w.H, d).cuda()
-    _say(f"[case] backward full {name}: {N} streams x {T} tokens, sampled {sample}")
-    got = vla.backward(*dev, w.lambda0, dout, dS_T=dS, dA_T=dA, dn_T=dn, eps=w.eps)
+    _say(f"[case] backward full {name}: {N} streams x {T} tokens, sampled {sample}, path {path}")
+    got = vla.backward(*dev, w.lambda0, dout, dS_T=dS, dA_T=dA, dn_T=dn, eps=w.eps, path=path)
     torch.cuda.synchronize()
     q, k, v, u = make_inputs(w, streams=sample)
     douts = dout.float().view(N, T, d)[list(sample)].cpu().numpy().astype(np.float64)
@@ -166,7 +169,7 @@ def test_backward_full_workload_sampled_streams(name, sample):
                      eps=w.eps, dtype=torch.float32)
     bars = {n: max(tol, 4.0 * rel_l2(r32, rf)) for n, r32, rf in zip(names, ref32[:4], ref[:4])}
     bars["dlambda0"] = tol
-    _say(f"[parity] backward full {name}: " + " ".join(f"{n}={e:.3e} (bar {bars[n]:.1e})" for n, e in errs.items()))
+    _say(f"[parity] backward full {name} {path}: " + " ".join(f"{n}={e:.3e} (bar {bars[n]:.1e})" for n, e in errs.items()))
     for n, e in errs.items():
         assert e < bars[n], f"{n} rel L2 {e:.3e} >= {bars[n]:.3e}"
 
