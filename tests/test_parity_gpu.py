@@ -337,3 +337,39 @@ def test_forward_graph_replays_match_eager(path, dt):
         _say(f"[parity] forward graph {path} {dt} replay {rep}: bitwise equal to eager: {same}")
         assert same, f"replay {rep} differs from the eager call"
         _ = (torch.ones(4096, device="cuda") * 3.0).sum().item()  # eager work between replays
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_two_stream_groups_equal_one_launch(d):
+    """A chunked call of at least 2^20 tokens runs its streams as two groups on two HIP streams
+    (here 2 and 3 of 5 streams); the same call captured in a HIP graph runs as one launch over
+    all streams (the library does not split under capture).  The segment length is the whole
+    call's in both, so the outputs must be bitwise equal."""
+    T = 1 << 18
+    w = get_workload("long_t131072_d96").resized(name=f"groups_d{d}", B=1, H=5, T=T, d=d)
+    q, k, v, u = upload_inputs(w, "cuda")
+    n = vla.workspace_size(tuple(q.shape), q.dtype, path="chunk", chunk=64)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    S = torch.empty((1, 5, d, d), dtype=torch.float32, device="cuda")
+    A = torch.empty_like(S)
+
+    def call():
+        vla.forward(q, k, v, u, w.lambda0, path="chunk", chunk=64, out=out, S_final=S, A_final=A, workspace=ws)
+
+    _say(f"[case] two stream groups vs one launch: 5 x {T} tokens, d = {d}")
+    call()
+    torch.cuda.synchronize()
+    eager = (out.clone(), S.clone(), A.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for t in (out, S, A):
+        t.zero_()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    same = [torch.equal(a, b) for a, b in zip((out, S, A), eager)]
+    _say(f"[parity] two stream groups d={d}: out, S_T, A_T bitwise equal to one launch: {same}")
+    assert all(same)
