@@ -399,10 +399,8 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       }
 #pragma unroll
       for (int it = 0; it < 2; ++it) {  // token 16 it + li: sums over the four lane groups
-        asum[it] += __shfl_xor(asum[it], 16);
-        asum[it] += __shfl_xor(asum[it], 32);
-        ksq[it] += __shfl_xor(ksq[it], 16);
-        ksq[it] += __shfl_xor(ksq[it], 32);
+        asum[it] = sum_rows4(asum[it]);
+        ksq[it] = sum_rows4(ksq[it]);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) ncol[e] = row_sum16(ncol[e]);
@@ -522,8 +520,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       float part = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) part = fmaf(Yt[ct][r], Yt[ct][r], part);
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
+      part = sum_rows4(part);
       if (gq == 0) sh.norm[w][16 * ct + li] = part;
     }
     __syncthreads();

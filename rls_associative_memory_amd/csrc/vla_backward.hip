@@ -41,7 +41,7 @@
 // (tid / 16, tid % 16) holds rows i + 32 a and column pairs 2 p + 32 b of each d x d matrix in
 // registers, so row sums are 16-lane shuffles and column sums go through one LDS pass over the
 // eight waves in a fixed order (deterministic).  The reverse sweep undoes the rank-1 updates
-// token by token (S -= r ahat^T, A += z z^T / delta) and reloads the exact state at every
+// token by token (S -= r ahat^T, A += s s^T with s = z / sqrt(delta)) and reloads the exact state at every
 // checkpoint, so rounding cannot drift over more than 32 steps.
 
 #include <algorithm>
@@ -208,16 +208,25 @@ k_bw_replay(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__r
     for (int ww = 0; ww < BW_NW; ++ww) yy += sh.yy[ww];
     const float ry = yy > 0.f ? rsqrtf(yy) : 0.f;
     float *rec = rec0 + t * C::REC;
+    // A' = A - s s^T with s = z / sqrt(delta): one division per token, and entry (i, j) takes
+    // the same product s_i s_j as entry (j, i), so A stays exactly symmetric
+    const float rsd = 1.0f / sqrtf(delta);
+    float sc[NB][2];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) sc[b][e] = sh.z[col(b, e)] * rsd;
 #pragma unroll
     for (int a = 0; a < R; ++a) {
       const float ra = sh.v[row(a)] - sk[a] * rk;
+      const float sa = z[a] * rsd;
       float np = 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int c = col(b, e);
-          A[a][b][e] -= z[a] * sh.z[c] / delta;
+          A[a][b][e] = fmaf(-sa, sc[b][e], A[a][b][e]);
           S[a][b][e] = fmaf(ra, sh.y[c] * ry, S[a][b][e]);
           np = fmaf(S[a][b][e], sh.fq[c], np);
         }
@@ -407,9 +416,7 @@ k_bw_grad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__res
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        float y = x[b][e];
-        y += __shfl_xor(y, 16);
-        y += __shfl_xor(y, 32);
+        const float y = sum_rows4(x[b][e]);
         if (lane < 16) sh.part[sl][w][col(b, e)] = y;
       }
   };
@@ -558,11 +565,18 @@ k_bw_grad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__res
     const float wa = bw_dot<D>(sh.w, sh.ah, lane);
     if (tid == 0) trace += static_cast<double>(wa) * ynorm;
     // R += (w y^T + y w^T) / 2 (y = ahat ||y||), du = -2 R u, A before the token
+    // (A + s s^T, s = z / sqrt(delta), the replay's downdate undone)
     {
       const float hy = 0.5f * ynorm;
+      const float rsd = 1.0f / sqrtf(delta);
+      float sc[NB][2];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) sc[b][e] = sh.z[col(b, e)] * rsd;
 #pragma unroll
       for (int a = 0; a < R; ++a) {
-        const float w_r = sh.w[row(a)], ah_r = sh.ah[row(a)], z_r = sh.z[row(a)];
+        const float w_r = sh.w[row(a)], ah_r = sh.ah[row(a)], s_r = sh.z[row(a)] * rsd;
         float rp = 0.f;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -571,7 +585,7 @@ k_bw_grad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__res
             const int c = col(b, e);
             Rm[a][b][e] = fmaf(hy, fmaf(w_r, sh.ah[c], ah_r * sh.w[c]), Rm[a][b][e]);
             rp = fmaf(Rm[a][b][e], sh.u[c], rp);
-            A[a][b][e] += z_r * sh.z[c] / delta;
+            A[a][b][e] = fmaf(s_r, sc[b][e], A[a][b][e]);
           }
         const float ru = row_sum16(rp);
         if (pj == 0) du[tok + row(a)] = -2.0f * ru;

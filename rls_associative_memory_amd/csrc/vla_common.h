@@ -79,6 +79,17 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x + dpp_mirror(x);
 }
 
+// y summed over the four 16-lane rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48), in every
+// lane: two gfx950 row swaps on the VALU (v_permlane16_swap_b32, v_permlane32_swap_b32; with
+// both operands y, the two results of a swap add up to y plus its partner row's y), where
+// __shfl_xor would go through the LDS crossbar (ds_bpermute) and wait for it.
+__device__ __forceinline__ float sum_rows4(float y) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Sum over all 64 lanes of the wave (the whole wave must be active), broadcast to every lane.
 // After the row sums, rows 1 and 3 add the last lane of rows 0 and 2 (DPP row_bcast:15), row 3
 // then adds lane 31 (row_bcast:31), and lane 63's total is read out: all on the VALU, no LDS

@@ -194,8 +194,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
                        ((qf[4] * n1.x + qf[5] * n1.y) + (qf[6] * n1.z + qf[7] * n1.w));
           // lanes ui ^ 1, ui ^ 2 stage the neighbouring 8-feature pieces of the same token
           // (d / 8 is a multiple of 4, and so is every unit count here): one sum per 32 features
-          part += __shfl_xor(part, 1);
-          part += __shfl_xor(part, 2);
+          part = part + dpp_xor1(part);
+          part = part + dpp_xor2(part);
           if ((ui & 3) == 0) sh.dpart[c][f0 / 32] = part;
           uint32_t hw[4], lw[4];
 #pragma unroll
