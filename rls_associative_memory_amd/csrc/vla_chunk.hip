@@ -123,23 +123,12 @@ __device__ __forceinline__ void store_elem<bf16_t>(bf16_t *p, int64_t i, float x
 // ------------------------------------------------------------------------------------
 // k_gram: Gram_p = sum_{t in segment p} u_t u_t^T (segments 0..P-2) and, for fp32 inputs,
 // nk_p = sum phi(k_t) (for bf16 inputs the A side forms these sums from the keys it stages)
-// bf16 inputs: v_mfma_f32_16x16x32_bf16 on the raw inputs (every product exact in fp32);
-// fp32 inputs: v_mfma_f32_16x16x4_f32.  Tokens are staged 64 at a time, transposed and
-// packed so each lane's MFMA operand is one 16-byte LDS read; the next block's 16-byte
-// global loads are issued before the current block is multiplied.
+// bf16 inputs: v_mfma_f32_16x16x32_bf16 on the raw inputs (every product exact in fp32),
+// tokens staged 64 at a time as they are (token rows, 16-byte copies) and read by feature
+// with the transposing load ds_read_b64_tr_b16; fp32 inputs: v_mfma_f32_16x16x4_f32, tokens
+// transposed and packed at staging so each lane's operand is one 16-byte LDS read.  The next
+// block's 16-byte global loads are issued before the current block is multiplied.
 // ------------------------------------------------------------------------------------
-template <typename TIn>
-struct GramLds;
-template <>
-struct GramLds<bf16_t> {  // [f][token] bf16, rows padded to 72 tokens
-  static constexpr int LT = 72;
-  using elem = uint16_t;
-};
-template <>
-struct GramLds<float> {   // [token/4][f][token%4] fp32
-  static constexpr int LT = 0;
-  using elem = float;
-};
 
 template <int D, typename TIn>
 __global__ void __launch_bounds__(256)
@@ -157,7 +146,8 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
   constexpr int UB = TB * D / VW;      // vectors per array per block
   constexpr int PU = UB / 256;         // per thread (exact for every supported D)
   static_assert(UB % 256 == 0, "block staging must tile the threads");
-  __shared__ __attribute__((aligned(16))) uint16_t sUb[BF ? D : 1][BF ? GramLds<bf16_t>::LT : 1];
+  constexpr int LDR = D + 8;           // bf16 token rows (52-word rows at d = 96)
+  __shared__ __attribute__((aligned(16))) uint16_t sUb[BF ? TB : 1][BF ? LDR : 1];
   __shared__ __attribute__((aligned(16))) float sUf[BF ? 1 : TB / 4][BF ? 1 : D + 1][4];
 
   const int64_t s = blockIdx.x;
@@ -205,12 +195,7 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
       const int ui = tid + 256 * i;
       const int c = ui % TB, f0 = (ui / TB) * VW;
       if constexpr (BF) {
-        const uint32_t w[4] = {pu[i].x, pu[i].y, pu[i].z, pu[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sUb[f0 + 2 * e][c] = static_cast<uint16_t>(w[e] & 0xffffu);
-          sUb[f0 + 2 * e + 1][c] = static_cast<uint16_t>(w[e] >> 16);
-        }
+        *reinterpret_cast<uint4 *>(&sUb[c][f0]) = pu[i];
       } else {
         float x[VW];
         IO::unpack(pu[i], x);
@@ -232,12 +217,13 @@ k_gram(const TIn *__restrict__ u, const TIn *__restrict__ k, float *__restrict__
       if (wave + 4 * m < NTILE) {
         const int fi = 16 * ti_i[m] + li, fj = 16 * ti_j[m] + li;
         if constexpr (BF) {
+          // lane (li, gq): U[32 kk + 8 gq + e][16 ti + li], e = 0..7, for both operands
 #pragma unroll
           for (int kk = 0; kk < TB / 32; ++kk) {
-            const uint4 a = *reinterpret_cast<const uint4 *>(&sUb[fi][32 * kk + 8 * gq]);
-            const uint4 b = *reinterpret_cast<const uint4 *>(&sUb[fj][32 * kk + 8 * gq]);
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                             __builtin_bit_cast(bf16x8_t, b), acc[m], 0, 0, 0);
+            const int r0 = 32 * kk + 8 * gq;
+            const bf16x8_t a = ld_tr4x2(&sUb[0][0], LDR, r0, r0 + 4, 16 * ti_i[m], li);
+            const bf16x8_t b = ld_tr4x2(&sUb[0][0], LDR, r0, r0 + 4, 16 * ti_j[m], li);
+            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[m], 0, 0, 0);
           }
         } else {
 #pragma unroll
