@@ -156,26 +156,37 @@ k_bw_replay(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__r
     }
     __syncthreads();
     float z[R], sk[R];
+    {
+      float rs[3 * R];  // row sums of A u, A k, S k for every row of this thread
 #pragma unroll
-    for (int a = 0; a < R; ++a) {
-      float zp = 0.f, gp = 0.f, sp = 0.f;
+      for (int a = 0; a < R; ++a) {
+        float zp = 0.f, gp = 0.f, sp = 0.f;
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int c = col(b, e);
-          zp = fmaf(A[a][b][e], sh.u[c], zp);
-          gp = fmaf(A[a][b][e], sh.kr[c], gp);
-          sp = fmaf(S[a][b][e], sh.kr[c], sp);
-        }
-      z[a] = row_sum16(zp);
-      const float g = row_sum16(gp);
-      sk[a] = row_sum16(sp);
-      if (pj == 0) {
-        sh.z[row(a)] = z[a];
-        sh.g[row(a)] = g;
-        sh.sk[row(a)] = sk[a];
+          for (int e = 0; e < 2; ++e) {
+            const int c = col(b, e);
+            zp = fmaf(A[a][b][e], sh.u[c], zp);
+            gp = fmaf(A[a][b][e], sh.kr[c], gp);
+            sp = fmaf(S[a][b][e], sh.kr[c], sp);
+          }
+        rs[3 * a] = zp;
+        rs[3 * a + 1] = gp;
+        rs[3 * a + 2] = sp;
       }
+      row_sum16_n(rs);
+#pragma unroll
+      for (int a = 0; a < R; ++a) {
+        z[a] = rs[3 * a];
+        sk[a] = rs[3 * a + 2];
+      }
+      if (pj == 0)
+#pragma unroll
+        for (int a = 0; a < R; ++a) {
+          sh.z[row(a)] = rs[3 * a];
+          sh.g[row(a)] = rs[3 * a + 1];
+          sh.sk[row(a)] = rs[3 * a + 2];
+        }
     }
     __syncthreads();
     // every wave forms the token's scalars itself (no further barrier)
@@ -216,24 +227,29 @@ k_bw_replay(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__r
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int e = 0; e < 2; ++e) sc[b][e] = sh.z[col(b, e)] * rsd;
+    float ra[R], np[R];
 #pragma unroll
     for (int a = 0; a < R; ++a) {
-      const float ra = sh.v[row(a)] - sk[a] * rk;
+      ra[a] = sh.v[row(a)] - sk[a] * rk;
       const float sa = z[a] * rsd;
-      float np = 0.f;
+      np[a] = 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int c = col(b, e);
           A[a][b][e] = fmaf(-sa, sc[b][e], A[a][b][e]);
-          S[a][b][e] = fmaf(ra, sh.y[c] * ry, S[a][b][e]);
-          np = fmaf(S[a][b][e], sh.fq[c], np);
+          S[a][b][e] = fmaf(ra[a], sh.y[c] * ry, S[a][b][e]);
+          np[a] = fmaf(S[a][b][e], sh.fq[c], np[a]);
         }
-      const float num = row_sum16(np);
-      if (pj == 0) {
-        rec[3 * D + row(a)] = ra;          // r
-        rec[5 * D + row(a)] = num / den;   // o
+    }
+    row_sum16_n(np);
+    if (pj == 0) {
+      const float rden = 1.0f / den;
+#pragma unroll
+      for (int a = 0; a < R; ++a) {
+        rec[3 * D + row(a)] = ra[a];          // r
+        rec[5 * D + row(a)] = np[a] * rden;   // o
       }
     }
     if (tid < D) {
@@ -338,6 +354,7 @@ k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs, float *
     for (int c = lane; c < D; c += kWave) xo += sh.x[buf][c];
     xo = wave_sum(xo);
     if (tid < D) ndp = fmaf(-xo / den, sh.fq[buf][tid], ndp);
+    float bl[2 * R];  // row sums of B ahat and L ahat for every row of this thread
 #pragma unroll
     for (int a = 0; a < R; ++a) {
       const float dn_r = sh.dnum[buf][row(a)];
@@ -351,15 +368,19 @@ k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs, float *
           bp = fmaf(Bm[a][b][e], sh.ah[buf][c], bp);
           lp = fmaf(Lm[a][b][e], sh.ah[buf][c], lp);
         }
-      bp = row_sum16(bp);
-      lp = row_sum16(lp);
+      bl[2 * a] = bp;
+      bl[2 * a + 1] = lp;
+    }
+    row_sum16_n(bl);
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int c = col(b, e);
-          Bm[a][b][e] = fmaf(-bp, sh.kh[buf][c], Bm[a][b][e]);
-          Lm[a][b][e] = fmaf(-lp, sh.kh[buf][c], Lm[a][b][e]);
+          Bm[a][b][e] = fmaf(-bl[2 * a], sh.kh[buf][c], Bm[a][b][e]);
+          Lm[a][b][e] = fmaf(-bl[2 * a + 1], sh.kh[buf][c], Lm[a][b][e]);
         }
     }
   }
@@ -513,9 +534,12 @@ k_bw_grad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__res
             p2[b][e] = fmaf(dS[a][b][e], r_r, p2[b][e]);
             rp = fmaf(dS[a][b][e], sh.ah[c], rp);
           }
-        drr[a] = row_sum16(rp);
-        if (pj == 0) sh.dr[row(a)] = drr[a];
+        drr[a] = rp;
       }
+      row_sum16_n(drr);
+      if (pj == 0)
+#pragma unroll
+        for (int a = 0; a < R; ++a) sh.dr[row(a)] = drr[a];
       col_part(0, p1);
       col_part(1, p2);
     }
@@ -538,24 +562,33 @@ k_bw_grad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__res
       float p1[NB][2];
 #pragma unroll
       for (int b = 0; b < NB; ++b) p1[b][0] = p1[b][1] = 0.f;
+      float dyc[NB][2], ap[R];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int c = col(b, e);
+          dyc[b][e] = (sh.dah[c] - sh.ah[c] * ad) * iy;
+        }
 #pragma unroll
       for (int a = 0; a < R; ++a) {
         const float r_r = sh.r[row(a)], dr_r = drr[a];
-        float ap = 0.f;
+        ap[a] = 0.f;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int c = col(b, e);
-            const float dyc = (sh.dah[c] - sh.ah[c] * ad) * iy;
             S[a][b][e] = fmaf(-r_r, sh.ah[c], S[a][b][e]);
             dS[a][b][e] = fmaf(-dr_r, sh.kh[c], dS[a][b][e]);
-            ap = fmaf(A[a][b][e], dyc, ap);
+            ap[a] = fmaf(A[a][b][e], dyc[b][e], ap[a]);
             p1[b][e] = fmaf(S[a][b][e], dr_r, p1[b][e]);
           }
-        const float wr = row_sum16(ap);
-        if (pj == 0) sh.w[row(a)] = wr;
       }
+      row_sum16_n(ap);
+      if (pj == 0)
+#pragma unroll
+        for (int a = 0; a < R; ++a) sh.w[row(a)] = ap[a];
       col_part(0, p1);
     }
     __syncthreads();
@@ -574,22 +607,25 @@ k_bw_grad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__res
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 2; ++e) sc[b][e] = sh.z[col(b, e)] * rsd;
+      float rp[R];
 #pragma unroll
       for (int a = 0; a < R; ++a) {
         const float w_r = sh.w[row(a)], ah_r = sh.ah[row(a)], s_r = sh.z[row(a)] * rsd;
-        float rp = 0.f;
+        rp[a] = 0.f;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const int c = col(b, e);
             Rm[a][b][e] = fmaf(hy, fmaf(w_r, sh.ah[c], ah_r * sh.w[c]), Rm[a][b][e]);
-            rp = fmaf(Rm[a][b][e], sh.u[c], rp);
+            rp[a] = fmaf(Rm[a][b][e], sh.u[c], rp[a]);
             A[a][b][e] = fmaf(s_r, sc[b][e], A[a][b][e]);
           }
-        const float ru = row_sum16(rp);
-        if (pj == 0) du[tok + row(a)] = -2.0f * ru;
       }
+      row_sum16_n(rp);
+      if (pj == 0)
+#pragma unroll
+        for (int a = 0; a < R; ++a) du[tok + row(a)] = -2.0f * rp[a];
     }
     if (tid < D) {
       dk[tok + tid] = dk_acc + (sh.dkh[tid] - sh.kh[tid] * kd) * rk;

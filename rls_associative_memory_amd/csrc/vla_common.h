@@ -79,6 +79,21 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x + dpp_mirror(x);
 }
 
+// row_sum16 of N independent values, stage by stage across the values, so that each DPP
+// move has other work between it and the addition that produced its operand (no wait states
+// between the stages of one chain); every value's sum is bitwise row_sum16's.
+template <int N>
+__device__ __forceinline__ void row_sum16_n(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = x[i] + dpp_xor1(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = x[i] + dpp_xor2(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = x[i] + dpp_half_mirror(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = x[i] + dpp_mirror(x[i]);
+}
+
 // y summed over the four 16-lane rows of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48), in every
 // lane: two gfx950 row swaps on the VALU (v_permlane16_swap_b32, v_permlane32_swap_b32; with
 // both operands y, the two results of a swap add up to y plus its partner row's y), where
