@@ -65,14 +65,16 @@ struct AwyLds {
 template <int D, int TERMS>
 constexpr int awy_waves_per_simd() { return (TERMS == 2 && (D == 64 || D == 96)) ? 4 : 1; }
 
-template <int D, int TERMS>
+// With REC the kernel also writes its part of the backward's token records (z, ahat in fp32,
+// delta, ||A khat||) and the A half of the state checkpoints (brec, bck: BwRec layout).
+template <int D, int TERMS, bool REC = false>
 __global__ void __launch_bounds__((AwyCfg<D, TERMS>::NT))
 __attribute__((amdgpu_waves_per_eu(awy_waves_per_simd<D, TERMS>())))
 k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
            const bf16_t *__restrict__ u, const float *__restrict__ A0,
            float *__restrict__ nk, uint16_t *__restrict__ ahat, float *__restrict__ rkden,
            float *__restrict__ A_final, int64_t T, int64_t L,
-           int64_t P, float eps) {
+           int64_t P, float eps, float *__restrict__ brec, float *__restrict__ bck) {
   using C = AwyCfg<D, TERMS>;
   constexpr int NW = C::NW, NT = C::NT, CH = C::C, NTM = C::NTERM;
   constexpr int ZR_T = CH * C::LDU;       // term stride of Zr
@@ -94,6 +96,9 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   const uint16_t *qs = reinterpret_cast<const uint16_t *>(q) + s * T * D;
   uint16_t *al = ahat + s * T * 2 * D;
   float *rd = rkden + s * T * 2;
+  constexpr int RF = BwRec<D>::F;
+  float *brs = REC ? brec + s * T * RF : nullptr;
+  float *bcs = REC ? bck + s * ((T + kBwCk - 1) / kBwCk) * 2 * D * D + D * D : nullptr;  // A halves
 
   // Column tile w of A: At[it][r] = A[16 it + 4 gq + r][16 w + li].
   f4_t At[NW];
@@ -299,6 +304,8 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       if (lane < 16) {
         sh.rd[lane] = __builtin_amdgcn_rcpf(myd0);
         sh.rsd[lane] = rsqrtf(myd0);
+        if constexpr (REC)
+          if (lane < m) brs[(c0 + lane) * RF + 6 * D] = myd0;  // delta: the LDL^T pivot
       } else if (lane < 32) {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
@@ -344,6 +351,8 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       if (lane < 16) {
         sh.rd[16 + lane] = __builtin_amdgcn_rcpf(myd1);
         sh.rsd[16 + lane] = rsqrtf(myd1);
+        if constexpr (REC)
+          if (16 + lane < m) brs[(c0 + 16 + lane) * RF + 6 * D] = myd1;
       } else if (lane >= 32) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sh.G[16 + r][mcol] = y[r];  // L^{-1}_21 | L^{-1}_22
@@ -429,7 +438,9 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         den += sh.dpart[sl][lane] + sh.apart[sl][lane];
         kk += sh.kpart[sl][lane];
       }
-      if (lane < m) *reinterpret_cast<float2 *>(&rd[(c0 + lane) * 2]) = make_float2(kk > 0.f ? rsqrtf(kk) : 0.f, den);
+      const float rkv = kk > 0.f ? rsqrtf(kk) : 0.f;
+      if (lane < m) *reinterpret_cast<float2 *>(&rd[(c0 + lane) * 2]) = make_float2(rkv, den);
+      if constexpr (REC) sh.kpart[0][lane] = rkv;  // read back for ||A khat|| (kpart is free until the next chunk)
     }
     // ---- Z^T = Z0^T L^{-T} ---------------------------------------------------------------
     f4_t Zt[2];
@@ -450,6 +461,15 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                              l[ct][1][0], l[ct][1][1], l[ct][1][2], l[ct][1][3]};
         split_n8<NTM>(lv, b);
         Zt[ct] = mmn_ss<NTM>(a, b, f4_zero());
+      }
+    }
+    if constexpr (REC) {  // z_t = A_{t-1} u_t: this wave's 16 features of each token
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int c = 16 * ct + li;
+        if (c < m)
+          *reinterpret_cast<float4 *>(&brs[(c0 + c) * RF + D + 16 * w + 4 * gq]) =
+              make_float4(Zt[ct][0], Zt[ct][1], Zt[ct][2], Zt[ct][3]);
       }
     }
     // ---- publish Z into the second buffer (for K Z^T and X~ Z) ----------------------------
@@ -547,6 +567,11 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         uint16_t *row = &al[c0 * 2 * D + static_cast<uint32_t>(c * 2 * D + 16 * w + 4 * gq)];
         *reinterpret_cast<uint2 *>(row) = make_uint2(w01[0], w23[0]);
         *reinterpret_cast<uint2 *>(row + D) = make_uint2(w01[1], w23[1]);
+        if constexpr (REC) {  // ahat in fp32, and ||A_t khat|| = ||Y_t|| / ||k_t||
+          float *rr = &brs[(c0 + c) * RF];
+          *reinterpret_cast<float4 *>(&rr[2 * D + 16 * w + 4 * gq]) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+          if (w == 0 && gq == 0) rr[6 * D + 1] = sqrtf(tot) * sh.kpart[0][c];
+        }
       }
     }
     // ---- A <- A - W^T W on this wave's column tile ------------------------------------------
@@ -563,6 +588,13 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int r = 0; r < 4; ++r) At[it][r] -= t4[r];
       }
+    }
+    if constexpr (REC) {  // A after the chunk's last token: the checkpoint's A half
+      float *dst = bcs + ((c0 + m - 1) / kBwCk) * 2 * D * D;
+#pragma unroll
+      for (int it = 0; it < NW; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(16 * it + 4 * gq + r) * D + 16 * w + li] = At[it][r];
     }
   }
 

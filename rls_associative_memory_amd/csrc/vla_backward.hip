@@ -54,13 +54,13 @@ namespace {
 
 constexpr int BW_NT = 512;
 constexpr int BW_NW = BW_NT / kWave;
-constexpr int BW_CK = 32;  // tokens between state checkpoints
-constexpr int BW_NS = 8;   // scalar slots per token record
+constexpr int BW_CK = kBwCk;       // tokens between state checkpoints
+constexpr int BW_NS = kBwScalars;  // scalar slots per token record
 
 template <int D>
 struct BwCfg {
   static constexpr int R = D / 32, NB = D / 32;
-  static constexpr int REC = 6 * D + BW_NS;  // khat, z, ahat, r, phi(q), o, scalars
+  static constexpr int REC = BwRec<D>::F;  // khat, z, ahat, r, phi(q), o, scalars
 };
 
 __device__ __forceinline__ float bw_cv(float x) { return x; }
@@ -818,23 +818,38 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
   hipError_t err;
 
   ChunkStates cs;
+  bool replay = true;
   if (bp.P > 1) {
     // segment-start A from an fp64 inversion: dlambda0 sums terms weighted by A_t^2, so an
     // fp32 inverse's error (about cond * 2^-24) would show in it
-    err = launch_chunk_states(pr, chunk, io.q, io.k, io.v, io.u, base + bp.off_chunk,
-                              reinterpret_cast<double *>(base + bp.off_md), st, &cs);
+    double *Md = reinterpret_cast<double *>(base + bp.off_md);
+    if constexpr (sizeof(TIn) == 2) {
+      // bf16 inputs: the chunked forward's passes (A side, final pass) write the token records
+      // and the state checkpoints themselves, from their chunk products, so no token-by-token
+      // replay runs
+      BwRecords r;
+      r.rec = rec;
+      r.ck = ck;
+      r.n_end = nend;
+      err = launch_chunk_records(pr, chunk, io.q, io.k, io.v, io.u, base + bp.off_chunk, Md, st, r, &cs);
+      replay = false;
+    } else {
+      err = launch_chunk_states(pr, chunk, io.q, io.k, io.v, io.u, base + bp.off_chunk, Md, st, &cs);
+    }
     if (err != hipSuccess) return err;
   }
-  VLA_LAUNCH("k_bw_replay", (k_bw_replay<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, v, u,
-             static_cast<const float *>(cs.S_seg), static_cast<const float *>(cs.A_seg),
-             static_cast<const float *>(cs.n_seg), rec, ck, nend, pr.T, bp.L, bp.P, pr.lambda0, pr.eps);
+  if (replay)
+    VLA_LAUNCH("k_bw_replay", (k_bw_replay<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, v, u,
+               static_cast<const float *>(cs.S_seg), static_cast<const float *>(cs.A_seg),
+               static_cast<const float *>(cs.n_seg), rec, ck, nend, pr.T, bp.L, bp.P, pr.lambda0, pr.eps);
   if (X != nullptr)
     VLA_LAUNCH("k_bw_terminal", (k_bw_terminal<D>), dim3(S), dim3(256), 0, st,
                static_cast<const float *>(ck), io.dA_T, Y, X, pr.T);
   if (bp.P > 1) {
-    // After the replay the segment-start buffers are free: the maps go where the forward
-    // pass's maps were, the end cotangents of S where its start states were, the segment sums
-    // of dden phi(q) where the normalisers were and the segment R sums where A was.
+    // After the replay (or the forward's final pass) the segment-start buffers are free: the
+    // maps go where the forward pass's maps were, the end cotangents of S where its start states
+    // were, the segment sums of dden phi(q) where the normalisers were and the segment R sums
+    // where A was.
     float *lb = cs.pib, *E = cs.S_seg, *nd = cs.n_seg, *W = cs.A_seg;
     VLA_LAUNCH("k_bw_dsmap", (k_bw_dsmap<D, TIn>), dim3(S, P - 1), dim3(BW_NT), 0, st, dout,
                static_cast<const float *>(rec), lb, nd, pr.T, bp.L, bp.P);

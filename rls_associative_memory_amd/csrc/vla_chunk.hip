@@ -1131,7 +1131,7 @@ template <int D>
 __global__ void __launch_bounds__(D / 16 * kWave)
 k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P,
           const float *__restrict__ S0, float *__restrict__ nk, const float *__restrict__ n0,
-          float *__restrict__ n_final) {
+          float *__restrict__ n_final, float *__restrict__ n_end) {
   constexpr int NFT = D / 16;
   __shared__ __attribute__((aligned(16))) float Xs[2][D / 4][16][4];  // S^T[f'][row], f' % 4 minor
   const int64_t s = blockIdx.x;
@@ -1150,6 +1150,8 @@ k_sprefix(const float *__restrict__ pib, float *__restrict__ s0, int64_t P,
       for (int i = 0; i < 16; ++i) {
         if (p0 + i < P) base[(p0 + i) * D] = static_cast<float>(acc);
         acc += g[i];
+        // n after segment p0 + i (the backward's records)
+        if (n_end != nullptr && p0 + i < P) n_end[(s * P + p0 + i) * D + f] = static_cast<float>(acc);
       }
     }
     if (n_final != nullptr) n_final[s * D + f] = static_cast<float>(acc);
@@ -1220,7 +1222,8 @@ template <int D, int CH, typename TIn>
 static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const void *q,
                                  const void *k, const void *v, const void *u, void *out,
                                  const StateIO &sio, char *ws, hipStream_t st, bool states_only,
-                                 double *Md) {
+                                 double *Md, const BwRecords *rec = nullptr) {
+  if (rec != nullptr && (sizeof(TIn) != 2 || states_only)) return hipErrorInvalidValue;
   const TIn *qq = static_cast<const TIn *>(q);
   const TIn *kk = static_cast<const TIn *>(k);
   const TIn *vv = static_cast<const TIn *>(v);
@@ -1265,12 +1268,22 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // Three-term operands when the Sherman-Morrison steps cancel strongly: from A_0 = I / lambda0
     // with lambda0 < d / 256 (unit-variance inputs then give cancellation factors above ~256,
     // which two-term operands, 16 significant bits, cannot absorb).
-    if (sio.A0 == nullptr && pr.lambda0 < static_cast<float>(D) / 256.0f) {
+    const bool three = sio.A0 == nullptr && pr.lambda0 < static_cast<float>(D) / 256.0f;
+    if (rec != nullptr) {  // with the backward's records (z, ahat, delta, ||A khat||, A checkpoints)
+      if (three)
+        VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 3, true>), dim3(S, P), dim3(AwyCfg<D, 3>::NT), 0, st,
+                   qq, kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps, rec->rec, rec->ck);
+      else
+        VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2, true>), dim3(S, P), dim3(AwyCfg<D, 2>::NT), 0, st,
+                   qq, kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps, rec->rec, rec->ck);
+    } else if (three) {
       VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 3>), dim3(S, P), dim3(AwyCfg<D, 3>::NT), 0, st, qq,
-                 kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
+                 kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps,
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     } else {
       VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2>), dim3(S, P), dim3(AwyCfg<D, 2>::NT), 0, st, qq,
-                 kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps);
+                 kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps,
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     }
   } else {
     using AC = AsideCfg<D>;
@@ -1284,17 +1297,24 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, P - 1),
                  dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alh, rdw, s0w, pbw, oo,
-                 S_final, static_cast<const float *>(nullptr), pl.T, pl.L, pl.P);
+                 S_final, static_cast<const float *>(nullptr), pl.T, pl.L, pl.P,
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
-               s0w, pl.P, sio.S0, nkw, sio.n0, n_final);
+               s0w, pl.P, sio.S0, nkw, sio.n0, n_final, rec != nullptr ? rec->n_end : nullptr);
     if (states_only) return hipGetLastError();
     // The final pass runs in chunks of at most 32 tokens whatever the map pass uses: its
     // workgroup then fits twice per CU (54 KB of LDS and 127 VGPRs at d = 96), and the
     // segment maps it starts from do not depend on either pass's chunking.
     constexpr int CF = CH < 32 ? CH : 32;
-    VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT), 0,
-               st, qq, kk, vv, alh, rdw, s0w, pbw, oo, S_final, nkw, pl.T, pl.L, pl.P);
+    if (rec != nullptr)  // the backward's records (khat, r, phi(q), o, 1/||k||, den, S checkpoints)
+      VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT),
+                 0, st, qq, kk, vv, alh, rdw, s0w, pbw, static_cast<TIn *>(nullptr), S_final, nkw, pl.T,
+                 pl.L, pl.P, rec->rec, rec->ck);
+    else
+      VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT), 0,
+                 st, qq, kk, vv, alh, rdw, s0w, pbw, oo, S_final, nkw, pl.T, pl.L, pl.P,
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr));
   } else {
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),
@@ -1303,7 +1323,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
                s0w, pl.P, sio.S0, static_cast<float *>(nullptr), static_cast<const float *>(nullptr),
-               static_cast<float *>(nullptr));
+               static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     if (states_only) return hipGetLastError();
     VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P),
                dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final,
@@ -1316,10 +1336,10 @@ template <typename TIn>
 static hipError_t launch_chunk_dt(const Problem &pr, const ChunkPlan &pl, const void *q,
                                   const void *k, const void *v, const void *u, void *out,
                                   const StateIO &sio, char *ws, hipStream_t st, bool states_only,
-                                  double *Md) {
+                                  double *Md, const BwRecords *rec = nullptr) {
 #define VLA_CASE(DD, CC)                                                                      \
   if (pr.d == DD && pl.C == CC)                                                               \
-    return launch_chunk_t<DD, CC, TIn>(pr, pl, q, k, v, u, out, sio, ws, st, states_only, Md);
+    return launch_chunk_t<DD, CC, TIn>(pr, pl, q, k, v, u, out, sio, ws, st, states_only, Md, rec);
   VLA_CASE(32, 16) VLA_CASE(32, 32) VLA_CASE(32, 64)
   VLA_CASE(64, 16) VLA_CASE(64, 32) VLA_CASE(64, 64)
   VLA_CASE(96, 16) VLA_CASE(96, 32) VLA_CASE(96, 64)
@@ -1455,6 +1475,22 @@ hipError_t launch_chunk_states(const Problem &p, int chunk, const void *q, const
   return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, nullptr, none, w, stream, true, Md);
 }
 
+hipError_t launch_chunk_records(const Problem &p, int chunk, const void *q, const void *k,
+                                const void *v, const void *u, void *ws, double *Md,
+                                hipStream_t stream, const BwRecords &rec, ChunkStates *cs) {
+  if (!chunk_supported(p, chunk) || p.dtype != Dtype::BF16) return hipErrorInvalidValue;
+  const ChunkPlan pl = make_plan(p, chunk);
+  char *w = static_cast<char *>(ws);
+  cs->S_seg = reinterpret_cast<float *>(w + pl.off_s0);
+  cs->A_seg = reinterpret_cast<float *>(w + pl.off_m);
+  cs->n_seg = reinterpret_cast<float *>(w + pl.off_nk);
+  cs->pib = reinterpret_cast<float *>(w + pl.off_pib);
+  cs->L = pl.L;
+  cs->P = pl.P;
+  const StateIO none{};
+  return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, nullptr, none, w, stream, false, Md, &rec);
+}
+
 hipError_t launch_matrix_prefix(const Problem &p, float *M, int64_t P, const float *Minit,
                                 hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.streams), static_cast<unsigned>((p.d * p.d + 255) / 256));
@@ -1475,7 +1511,7 @@ hipError_t launch_affine_prefix(const Problem &p, const float *pib, float *s0, i
 #define VLA_CASE(DD)                                                                          \
   if (p.d == DD) {                                                                            \
     VLA_LAUNCH("k_sprefix", (k_sprefix<DD>), dim3(S, DD / 16), dim3(DD / 16 * kWave), 0, st,  \
-               pib, s0, P, S0, nk, n0, static_cast<float *>(nullptr));                        \
+               pib, s0, P, S0, nk, n0, static_cast<float *>(nullptr), static_cast<float *>(nullptr)); \
     return hipGetLastError();                                                                 \
   }
   VLA_CASE(32) VLA_CASE(64) VLA_CASE(96) VLA_CASE(128)

@@ -68,14 +68,18 @@ struct SwbLds {
 template <int D, bool FINAL>
 constexpr int swb_waves_per_simd() { return (FINAL && D <= 96) ? 4 : 1; }
 
-template <int D, int CH, bool FINAL>
+// With REC (final pass only) the kernel writes its part of the backward's token records (khat,
+// r, phi(q), o in fp32, 1/||k||, den) and the S half of the state checkpoints (brec, bck:
+// BwRec layout) in place of the outputs.
+template <int D, int CH, bool FINAL, bool REC = false>
 __global__ void __launch_bounds__((SwbCfg<D, CH, FINAL>::NT))
 __attribute__((amdgpu_waves_per_eu(swb_waves_per_simd<D, FINAL>())))
 k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
        const uint16_t *__restrict__ ahat, const float *__restrict__ rkden,
        const float *__restrict__ s0, float *__restrict__ pib, bf16_t *__restrict__ out,
        float *__restrict__ S_final, const float *__restrict__ nstart, int64_t T, int64_t L,
-       int64_t P) {
+       int64_t P, float *__restrict__ brec, float *__restrict__ bck) {
+  static_assert(FINAL || !REC, "records come from the final pass");
   using C = SwbCfg<D, CH, FINAL>;
   constexpr int NT = C::NT, NCT = C::NCT, NFT = C::NFT, NKS = C::NKS;
   constexpr int TQ = SwbLds<D, CH, FINAL>::QR * C::LDF;
@@ -96,6 +100,9 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   const uint16_t *qs = reinterpret_cast<const uint16_t *>(q) + s * T * D;
   const uint16_t *als = ahat + s * T * 2 * D;
   const float *rds = rkden + s * T * 2;
+  constexpr int RF = BwRec<D>::F;
+  float *brs = REC ? brec + s * T * RF : nullptr;
+  float *bcs = REC ? bck + s * ((T + kBwCk - 1) / kBwCk) * 2 * D * D : nullptr;  // S halves
 
   const bool pi_rows = !FINAL && wave < C::NWV;
   const int rowbase = 16 * (wave % C::NWV);
@@ -185,6 +192,12 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           io<bf16_t>::unpack(pq[i], qf);
 #pragma unroll
           for (int e = 0; e < 8; ++e) qf[e] = c < m ? phi(qf[e]) : 0.f;
+          if constexpr (REC)
+            if (c < m) {
+              float *rq = &brs[(c0 + c) * RF + 4 * D + f0];
+              *reinterpret_cast<float4 *>(rq) = make_float4(qf[0], qf[1], qf[2], qf[3]);
+              *reinterpret_cast<float4 *>(rq + 4) = make_float4(qf[4], qf[5], qf[6], qf[7]);
+            }
           // The A side's denominators count the normaliser from the segment start only;
           // den = phi(q) . n_p + (A side's value), n_p the normaliser at the segment start:
           // this thread's 8 features of the dot product, in fp32 (summed in the tile phase).
@@ -371,14 +384,33 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         float dn = 0.f;
 #pragma unroll
         for (int g = 0; g < D / 32; ++g) dn += sh.dpart[lane][g];
-        sh.rden[lane] = 1.0f / (sh.rden[lane] + dn);
+        const float den = sh.rden[lane] + dn;
+        sh.rden[lane] = 1.0f / den;
+        if constexpr (REC)
+          if (lane < m) {
+            brs[(c0 + lane) * RF + 6 * D + 2] = sh.rk[lane];
+            brs[(c0 + lane) * RF + 6 * D + 3] = den;
+          }
+      }
+      if constexpr (REC) {  // khat = k / ||k|| of the chunk, from the staged rows
+        for (int idx = tid; idx < CH * (D / 8); idx += NT) {
+          const int c = idx / (D / 8), f0 = (idx % (D / 8)) * 8;
+          if (c < m) {
+            float kf[8];
+            io<bf16_t>::unpack(*reinterpret_cast<const uint4 *>(&sh.sK[c][f0]), kf);
+            const float rk = sh.rk[c];
+            float *rkh = &brs[(c0 + c) * RF + f0];
+            *reinterpret_cast<float4 *>(rkh) = make_float4(kf[0] * rk, kf[1] * rk, kf[2] * rk, kf[3] * rk);
+            *reinterpret_cast<float4 *>(rkh + 4) = make_float4(kf[4] * rk, kf[5] * rk, kf[6] * rk, kf[7] * rk);
+          }
+        }
       }
     }
     __syncthreads();
     // ---- this wave's rows: two tiles per step ---------------------------------------------
     // The next chunk's loads fly during the steps.
     if (c0 + CH < te) prefetch(c0 + CH, tid);
-    uint16_t *os = reinterpret_cast<uint16_t *>(out) + (s * T + c0) * D;
+    uint16_t *os = REC ? nullptr : reinterpret_cast<uint16_t *>(out) + (s * T + c0) * D;
 #pragma unroll
     for (int pr = 0; pr < NPR; ++pr) {
       const int ta = 2 * pr, tbb = 2 * pr + 1;
@@ -455,6 +487,18 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         E[1] = mm2h_ss(ld2_tr4h(&sh.InvS[0][tbb][0][0], C::LDI, TI, gq, li), split2_4h(rb), f4_zero());
         esb = split2_4h(E[1]);
       }
+      if constexpr (REC) {  // r_t = v_t - S_{t-1} khat_t: the rows of E
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ct = 2 * pr + h;
+          if (ct >= NCT) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 16 * ct + 4 * gq + r;
+            if (c < m) brs[(c0 + c) * RF + 3 * D + rowbase + li] = E[h][r];
+          }
+        }
+      }
       if constexpr (FINAL) {
         // Num_t = Phi(q)_t X^T + sum_{t' <= t} Qa_tt' E_t', then o = Num / den.
 #pragma unroll
@@ -463,12 +507,20 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           if (ct >= NCT) continue;
           f4_t num = mm2h_ss(ld2_tr4h(&sh.QaD[0][ct][0][0], C::LDI, TQD, gq, li), h ? esb : esa, numq[h]);
           if (h) num = mm2h_ss(ld2_tr4h(&sh.QaO[0][pr][0][0], C::LDI, TQO, gq, li), esa, num);
+          if constexpr (REC) {  // o in fp32 (no output is written)
 #pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            const int c = 16 * ct + 4 * gq + r;
-            const uint32_t o2 = pk_bf16(num[r] * sh.rden[c], num[r + 1] * sh.rden[c + 1]);
-            if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = static_cast<uint16_t>(o2);
-            if (c + 1 < m) os[static_cast<uint32_t>((c + 1) * D + rowbase + li)] = static_cast<uint16_t>(o2 >> 16);
+            for (int r = 0; r < 4; ++r) {
+              const int c = 16 * ct + 4 * gq + r;
+              if (c < m) brs[(c0 + c) * RF + 5 * D + rowbase + li] = num[r] * sh.rden[c];
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+              const int c = 16 * ct + 4 * gq + r;
+              const uint32_t o2 = pk_bf16(num[r] * sh.rden[c], num[r + 1] * sh.rden[c + 1]);
+              if (c < m) os[static_cast<uint32_t>(c * D + rowbase + li)] = static_cast<uint16_t>(o2);
+              if (c + 1 < m) os[static_cast<uint32_t>((c + 1) * D + rowbase + li)] = static_cast<uint16_t>(o2 >> 16);
+            }
           }
         }
       }
@@ -478,6 +530,13 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       ep.l = __builtin_bit_cast(bf16x8_t, make_uint4(esa.l.x, esa.l.y, two ? esb.l.x : 0u, two ? esb.l.y : 0u));
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) X[ft] = mm2_ss(aT[ft], ep, X[ft]);
+    }
+    if constexpr (REC) {  // S after the chunk's last token: the checkpoint's S half
+      float *dst = bcs + ((c0 + m - 1) / kBwCk) * 2 * D * D;
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+        *reinterpret_cast<float4 *>(&dst[(rowbase + li) * D + 16 * ft + 4 * gq]) =
+            make_float4(X[ft][0], X[ft][1], X[ft][2], X[ft][3]);
     }
   }
 
