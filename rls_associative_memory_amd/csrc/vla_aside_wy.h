@@ -589,7 +589,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         for (int r = 0; r < 4; ++r) At[it][r] -= t4[r];
       }
     }
-    if constexpr (REC) {  // A after the chunk's last token: the checkpoint's A half
+    if (REC && ((c0 + m) % kBwCk == 0 || c0 + m == te)) {  // A after a checkpoint token
       float *dst = bcs + ((c0 + m - 1) / kBwCk) * 2 * D * D;
 #pragma unroll
       for (int it = 0; it < NW; ++it)

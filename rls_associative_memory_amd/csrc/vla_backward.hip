@@ -26,7 +26,7 @@
 // segment) except the two scans:
 //   (chunked forward passes: S, A, n at every segment start)
 //   k_bw_replay   the forward token by token from the segment start: per-token vectors and the
-//                 state at every 32nd token (and the segment's last)
+//                 state at every 64th token (and the segment's last)
 //   k_bw_dsmap    per segment from the end: (Lmap, Bmap) and the segment's sum of dden phi(q)
 //   scan          dS and dn at every segment end (reverse order, so the forward scan applies)
 //   k_bw_grad     per segment from the end, the true dS and dn: dq, dk, dv, du with R local to
@@ -81,7 +81,7 @@ __device__ __forceinline__ float bw_dot(const float *x, const float *y, int lane
 // k_bw_replay: the forward over segment p from its start state (S0seg, A0seg, n0seg at
 // [stream][P]; NULL = the fixed start S = 0, A = I / lambda0, n = 0).  Writes each token's
 // record (khat, z, ahat, r, phi(q), o, delta, ||y||, 1/||k||, den) and the state (S, A) after
-// every 32nd token and after the segment's last token, and n after the segment.
+// every 64th token and after the segment's last token, and n after the segment.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 struct BwRepShared {
@@ -823,19 +823,14 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
     // segment-start A from an fp64 inversion: dlambda0 sums terms weighted by A_t^2, so an
     // fp32 inverse's error (about cond * 2^-24) would show in it
     double *Md = reinterpret_cast<double *>(base + bp.off_md);
-    if constexpr (sizeof(TIn) == 2) {
-      // bf16 inputs: the chunked forward's passes (A side, final pass) write the token records
-      // and the state checkpoints themselves, from their chunk products, so no token-by-token
-      // replay runs
-      BwRecords r;
-      r.rec = rec;
-      r.ck = ck;
-      r.n_end = nend;
-      err = launch_chunk_records(pr, chunk, io.q, io.k, io.v, io.u, base + bp.off_chunk, Md, st, r, &cs);
-      replay = false;
-    } else {
-      err = launch_chunk_states(pr, chunk, io.q, io.k, io.v, io.u, base + bp.off_chunk, Md, st, &cs);
-    }
+    // the chunked forward's passes (A side, final pass) write the token records and the state
+    // checkpoints themselves, so no token-by-token replay runs
+    BwRecords r;
+    r.rec = rec;
+    r.ck = ck;
+    r.n_end = nend;
+    err = launch_chunk_records(pr, chunk, io.q, io.k, io.v, io.u, base + bp.off_chunk, Md, st, r, &cs);
+    replay = false;
     if (err != hipSuccess) return err;
   }
   if (replay)

@@ -573,12 +573,15 @@ __device__ __forceinline__ void unit_sync() {
   }
 }
 
-template <int D, typename TIn>
+// With REC the kernel also writes the backward's token records it holds (khat, z, ahat,
+// phi(q), delta, ||A khat||, 1/||k||, den) and the A half of the state checkpoints.
+template <int D, typename TIn, bool REC = false>
 __global__ void __launch_bounds__(AsideCfg<D>::NT)
 k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ u,
         const float *__restrict__ A0, const float *__restrict__ nk0, float *__restrict__ alpha,
         float *__restrict__ rkden, float *__restrict__ A_final, float *__restrict__ n_final,
-        int64_t S, int64_t T, int64_t L, int64_t P, float eps) {
+        int64_t S, int64_t T, int64_t L, int64_t P, float eps, float *__restrict__ brec,
+        float *__restrict__ bck, float *__restrict__ bnend) {
   using C = AsideCfg<D>;
   using IO = io<TIn>;
   using vec_t = typename IO::vec_t;
@@ -605,6 +608,9 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
   float *al = alpha + s * T * D;
   float *rd = rkden + s * T * 2;
   float *W = sW[unit_in_blk];
+  constexpr int RF = BwRec<D>::F;
+  float *brs = REC ? brec + s * T * RF : nullptr;
+  float *bcs = REC ? bck + s * ((T + kBwCk - 1) / kBwCk) * 2 * D * D + D * D : nullptr;  // A halves
 
   float Mr[C::RPL][C::CW];
   const float *a0 = A0 + (s * P + p) * D * D;
@@ -761,6 +767,24 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
       }
     }
     if (lu == 0) *reinterpret_cast<float2 *>(&rd[t * 2]) = make_float2(rk, dp + eps);
+    if constexpr (REC) {
+      float *rr = brs + t * RF;
+      if (h == 0)
+#pragma unroll
+        for (int r = 0; r < C::RPL; ++r) {
+          const int row = g + r * C::HALF;
+          rr[row] = K[row] * rk;           // khat
+          rr[D + row] = z[r];              // z
+          rr[2 * D + row] = y[r] * inv;    // ahat
+          rr[4 * D + row] = Q[row];        // phi(q)
+        }
+      if (lu == 0) {
+        rr[6 * D] = delta;
+        rr[6 * D + 1] = sy > 0.f ? sqrtf(sy) : 0.f;
+        rr[6 * D + 2] = rk;
+        rr[6 * D + 3] = dp + eps;
+      }
+    }
     unit_sync<C::NWA>();
 #pragma unroll
     for (int m = 0; m < C::CW / 4; ++m) {
@@ -772,6 +796,15 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
         Mr[r][4 * m + 2] = fmaf(-w[r], w4.z, Mr[r][4 * m + 2]);
         Mr[r][4 * m + 3] = fmaf(-w[r], w4.w, Mr[r][4 * m + 3]);
       }
+    }
+    if (REC && ((t + 1) % kBwCk == 0 || t == te - 1)) {  // A after a checkpoint token
+      float *dst = bcs + (t / kBwCk) * 2 * D * D;
+#pragma unroll
+      for (int r = 0; r < C::RPL; ++r)
+#pragma unroll
+        for (int m = 0; m < C::CW / 4; ++m)
+          *reinterpret_cast<float4 *>(&dst[(g + r * C::HALF) * D + c0 + 4 * m]) =
+              make_float4(Mr[r][4 * m], Mr[r][4 * m + 1], Mr[r][4 * m + 2], Mr[r][4 * m + 3]);
     }
     if constexpr (C::NWA > 1) __syncthreads();  // W and the LDS slots are rewritten next
   };
@@ -803,6 +836,13 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
       if (feat < D) n_final[s * D + feat] = nrun[f];
     }
   }
+  if constexpr (REC) {  // n after the segment (the backward's records)
+#pragma unroll
+    for (int f = 0; f < C::NF; ++f) {
+      const int feat = lu + f * C::LA;
+      if (feat < D) bnend[(s * P + p) * D + feat] = nrun[f];
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -829,12 +869,16 @@ __device__ __forceinline__ float4 lds4(const float *p) {
   return *reinterpret_cast<const float4 *>(p);
 }
 
-template <int D, int CH, bool FINAL, typename TIn>
+// With REC (final pass only) the kernel writes r and o of the backward's token records and the
+// S half of the state checkpoints in place of the outputs.
+template <int D, int CH, bool FINAL, typename TIn, bool REC = false>
 __global__ void __launch_bounds__((SwyCfg<D, CH, FINAL>::NT))
 k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
       const float *__restrict__ alpha, const float *__restrict__ rkden,
       const float *__restrict__ s0, float *__restrict__ pib, TIn *__restrict__ out,
-      float *__restrict__ S_final, int64_t T, int64_t L, int64_t P) {
+      float *__restrict__ S_final, int64_t T, int64_t L, int64_t P, float *__restrict__ brec,
+      float *__restrict__ bck) {
+  static_assert(FINAL || !REC, "records come from the final pass");
   using C = SwyCfg<D, CH, FINAL>;
   using IO = io<TIn>;
   using vec_t = typename IO::vec_t;
@@ -860,6 +904,9 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
   const TIn *qs = q + s * T * D;
   const float *als = alpha + s * T * D;
   const float *rds = rkden + s * T * 2;
+  constexpr int RF = BwRec<D>::F;
+  float *brs = REC ? brec + s * T * RF : nullptr;
+  float *bcs = REC ? bck + s * ((T + kBwCk - 1) / kBwCk) * 2 * D * D : nullptr;  // S halves
 
   const bool pi_rows = !FINAL && blockIdx.z == 0;
   const int rowbase = 16 * wave;
@@ -1063,9 +1110,18 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
       e = mfma_f32_16x16x4(i4.w, acc[3], e);
       E[ct] = e;
     }
+    if constexpr (REC) {  // r_t = v_t - S_{t-1} khat_t: the rows of E
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * ct + 4 * gq + r;
+          if (c < m) brs[(c0 + c) * RF + 3 * D + rowbase + li] = E[ct][r];
+        }
+    }
     if constexpr (FINAL) {
       // Num = Fq X_start^T + lower(Fq ahat^T) E, then o = Num / den.
-      TIn *os = out + s * T * D;
+      TIn *os = REC ? nullptr : out + s * T * D;
 #pragma unroll
       for (int ct = 0; ct < C::NCT; ++ct) {
         f4_t acc = f4_zero();
@@ -1088,7 +1144,11 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * gq + r;
-          if (c < m) store_elem(os, (c0 + c) * D + rowbase + li, acc[r] * sRden[c]);
+          if constexpr (REC) {
+            if (c < m) brs[(c0 + c) * RF + 5 * D + rowbase + li] = acc[r] * sRden[c];  // o, fp32
+          } else {
+            if (c < m) store_elem(os, (c0 + c) * D + rowbase + li, acc[r] * sRden[c]);
+          }
         }
       }
     }
@@ -1103,6 +1163,13 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
         X[ft] = mfma_f32_16x16x4(a4.z, E[ct][2], X[ft]);
         X[ft] = mfma_f32_16x16x4(a4.w, E[ct][3], X[ft]);
       }
+    if (REC && ((c0 + m) % kBwCk == 0 || c0 + m == te)) {  // S after a checkpoint token
+      float *dst = bcs + ((c0 + m - 1) / kBwCk) * 2 * D * D;
+#pragma unroll
+      for (int ft = 0; ft < C::NFT; ++ft)
+        *reinterpret_cast<float4 *>(&dst[(rowbase + li) * D + 16 * ft + 4 * gq]) =
+            make_float4(X[ft][0], X[ft][1], X[ft][2], X[ft][3]);
+    }
   }
 
   float *dst = nullptr;
@@ -1223,7 +1290,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                                  const void *k, const void *v, const void *u, void *out,
                                  const StateIO &sio, char *ws, hipStream_t st, bool states_only,
                                  double *Md, const BwRecords *rec = nullptr) {
-  if (rec != nullptr && (sizeof(TIn) != 2 || states_only)) return hipErrorInvalidValue;
+  if (rec != nullptr && states_only) return hipErrorInvalidValue;
   const TIn *qq = static_cast<const TIn *>(q);
   const TIn *kk = static_cast<const TIn *>(k);
   const TIn *vv = static_cast<const TIn *>(v);
@@ -1289,8 +1356,14 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     using AC = AsideCfg<D>;
     const int64_t units = pl.S * pl.P;
     const unsigned blocks = static_cast<unsigned>((units + AC::UPB - 1) / AC::UPB);
-    VLA_LAUNCH("k_aside", (k_aside<D, TIn>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
-               nkw, alw, rdw, A_final, n_final, pl.S, pl.T, pl.L, pl.P, pr.eps);
+    if (rec != nullptr)  // with the backward's records (khat, z, ahat, phi(q), scalars, A checkpoints)
+      VLA_LAUNCH("k_aside", (k_aside<D, TIn, true>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
+                 nkw, alw, rdw, A_final, n_final, pl.S, pl.T, pl.L, pl.P, pr.eps, rec->rec, rec->ck,
+                 rec->n_end);
+    else
+      VLA_LAUNCH("k_aside", (k_aside<D, TIn>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
+                 nkw, alw, rdw, A_final, n_final, pl.S, pl.T, pl.L, pl.P, pr.eps,
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr), static_cast<float *>(nullptr));
   }
   if constexpr (sizeof(TIn) == 2) {
     // bf16 inputs: S side on the bf16 matrix cores.
@@ -1319,15 +1392,20 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),
                  dim3(SwyCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
-                 S_final, pl.T, pl.L, pl.P);
+                 S_final, pl.T, pl.L, pl.P, static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
                s0w, pl.P, sio.S0, static_cast<float *>(nullptr), static_cast<const float *>(nullptr),
                static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     if (states_only) return hipGetLastError();
-    VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P),
-               dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final,
-               pl.T, pl.L, pl.P);
+    if (rec != nullptr)  // the backward's records (r, o) and S checkpoints
+      VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn, true>), dim3(S, P),
+                 dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw,
+                 static_cast<TIn *>(nullptr), S_final, pl.T, pl.L, pl.P, rec->rec, rec->ck);
+    else
+      VLA_LAUNCH("k_swy_final", (k_swy<D, CH, true, TIn>), dim3(S, P),
+                 dim3(SwyCfg<D, CH, true>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo, S_final,
+                 pl.T, pl.L, pl.P, static_cast<float *>(nullptr), static_cast<float *>(nullptr));
   }
   return hipGetLastError();
 }
@@ -1478,7 +1556,7 @@ hipError_t launch_chunk_states(const Problem &p, int chunk, const void *q, const
 hipError_t launch_chunk_records(const Problem &p, int chunk, const void *q, const void *k,
                                 const void *v, const void *u, void *ws, double *Md,
                                 hipStream_t stream, const BwRecords &rec, ChunkStates *cs) {
-  if (!chunk_supported(p, chunk) || p.dtype != Dtype::BF16) return hipErrorInvalidValue;
+  if (!chunk_supported(p, chunk)) return hipErrorInvalidValue;
   const ChunkPlan pl = make_plan(p, chunk);
   char *w = static_cast<char *>(ws);
   cs->S_seg = reinterpret_cast<float *>(w + pl.off_s0);
@@ -1488,6 +1566,7 @@ hipError_t launch_chunk_records(const Problem &p, int chunk, const void *q, cons
   cs->L = pl.L;
   cs->P = pl.P;
   const StateIO none{};
+  if (p.dtype == Dtype::F32) return launch_chunk_dt<float>(p, pl, q, k, v, u, nullptr, none, w, stream, false, Md, &rec);
   return launch_chunk_dt<bf16_t>(p, pl, q, k, v, u, nullptr, none, w, stream, false, Md, &rec);
 }
 

@@ -53,9 +53,9 @@ template <> struct io<bf16_t> {
 // The backward's per-token record, fp32: khat, z = A_{t-1} u, ahat, r = v - S_{t-1} khat, phi(q),
 // o (d values each), then delta = 1 + u . z, ||A_t khat||, 1/||k||, den and spare slots; and the
 // state (S, A) after every kBwCk-th token and after each segment's last token.  Written by the
-// backward's replay, or by the chunked forward (bf16 inputs) for the backward.
+// backward's replay, or by the chunked forward's passes for the backward.
 constexpr int kBwScalars = 8;
-constexpr int kBwCk = 32;
+constexpr int kBwCk = 64;
 template <int D>
 struct BwRec {
   static constexpr int F = 6 * D + kBwScalars;  // floats per token record

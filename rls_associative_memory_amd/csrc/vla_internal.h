@@ -58,9 +58,9 @@ void chunk_segments(const Problem &p, int chunk, int64_t *L, int64_t *P);
 hipError_t launch_chunk_states(const Problem &p, int chunk, const void *q, const void *k,
                                const void *v, const void *u, void *ws, double *Md,
                                hipStream_t stream, ChunkStates *cs);
-// The backward's token records and state checkpoints (bf16 inputs), written by the chunked
-// forward's passes in place of a token-by-token replay: rec [streams][T][6d + 8] fp32, ck
-// [streams][ceil(T / 32)][2][d][d] (S, A after every 32nd token and each segment's last),
+// The backward's token records and state checkpoints, written by the chunked forward's passes
+// in place of a token-by-token replay: rec [streams][T][6d + 8] fp32, ck
+// [streams][ceil(T / 64)][2][d][d] (S, A after every 64th token and each segment's last),
 // n_end [streams][P][d] (n after each segment).  Also gives the segment-start states (cs).
 struct BwRecords {
   float *rec = nullptr, *ck = nullptr, *n_end = nullptr;

@@ -531,7 +531,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) X[ft] = mm2_ss(aT[ft], ep, X[ft]);
     }
-    if constexpr (REC) {  // S after the chunk's last token: the checkpoint's S half
+    if (REC && ((c0 + m) % kBwCk == 0 || c0 + m == te)) {  // S after a checkpoint token
       float *dst = bcs + ((c0 + m - 1) / kBwCk) * 2 * D * D;
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
