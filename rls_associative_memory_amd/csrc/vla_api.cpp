@@ -405,11 +405,14 @@ vla_status_t vla_linear_attention(const void *q, const void *k, const void *v, v
 }
 
 // The backward's segmentation: chunk 0 = one segment per stream (VLA_PATH_SEQ), else the
-// chunked path's segments (VLA_PATH_CHUNK).  AUTO splits time for at most 256 streams when the
-// split gives at least four segments per stream: measured on MI355X, time segments take 0.70
-// against 1.88 ms at 128 fp32 streams of 512 tokens (d = 32), 1.20 against 2.00 ms at 256, are
-// level at 512 (2.21 against 2.38 ms; 30.2 against 29.2 ms for 512 bf16 streams of 4096
-// tokens at d = 64) and slower from 1024 streams on (4.07 against 3.66 ms).
+// chunked path's segments (VLA_PATH_CHUNK).  AUTO splits time whenever the split gives at least
+// two segments per stream, at d = 128 only up to 128 streams.  Measured on MI355X (ms per call,
+// time segments against one segment per stream): fp32, d = 32, 512 tokens: 0.91 / 1.86 at 256
+// streams, 2.89 / 3.81 at 1024; bf16, 4096 tokens: 33.5 / 41.9 at 1024 streams (d = 64), 72.0 /
+// 80.4 (d = 96); at d = 128 (2048 tokens) 8.1 / 13.3 at 128 streams but 15.8 / 13.4 at 256 (the
+// segment passes add work, which pays only while one segment per stream leaves CUs idle).  The
+// split gives one segment per stream, and so the same work as SEQ, once streams x T reaches
+// about 2048 segments of the shortest length.
 vla_status_t resolve_backward(const vla_desc_t *desc, const vla::Problem &p, int *chunk) {
   if (desc->gain != VLA_GAIN_UNIT) return VLA_ERROR_NOT_SUPPORTED;
   int c = desc->chunk;
@@ -425,8 +428,9 @@ vla_status_t resolve_backward(const vla_desc_t *desc, const vla::Problem &p, int
     case VLA_PATH_AUTO: {
       if (c == 0) c = vla::chunk_default(p);
       int64_t L = 0, P = 0;
-      if (p.streams <= 256 && vla::chunk_supported(p, c)) vla::chunk_segments(p, c, &L, &P);
-      *chunk = P >= 4 ? c : 0;
+      if ((p.d <= 96 || p.streams <= 128) && vla::chunk_supported(p, c))
+        vla::chunk_segments(p, c, &L, &P);
+      *chunk = P >= 2 ? c : 0;
       return VLA_SUCCESS;
     }
     default:

@@ -198,8 +198,12 @@ def test_backward_argument_errors(lib):
     ws = lambda **kw: (lib.vla_backward_workspace_size(ctypes.byref(desc(**kw)), ctypes.byref(n)), n.value)[1]
     long_auto = ws(B=1, H=2, T=4096, d=96)
     assert long_auto == ws(B=1, H=2, T=4096, d=96, path=2) > ws(B=1, H=2, T=4096, d=96, path=1)
-    assert ws(B=1, H=256, T=4096, d=96) == ws(B=1, H=256, T=4096, d=96, path=2)
-    assert ws(B=1, H=257, T=4096, d=96) == ws(B=1, H=257, T=4096, d=96, path=1)
+    assert ws(B=1, H=1024, T=4096, d=96) == ws(B=1, H=1024, T=4096, d=96, path=2)
+    # at d = 128 only up to 128 streams; a split into one segment per stream is SEQ
+    assert ws(B=1, H=128, T=2048, d=128) == ws(B=1, H=128, T=2048, d=128, path=2)
+    assert ws(B=1, H=129, T=2048, d=128) == ws(B=1, H=129, T=2048, d=128, path=1)
+    assert ws(B=1, H=2048, T=512, d=32, dtype=0) == ws(B=1, H=2048, T=512, d=32, dtype=0, path=1)
+    assert ws(B=1, H=1024, T=512, d=32, dtype=0) == ws(B=1, H=1024, T=512, d=32, dtype=0, path=2)
     # 256 fp32 streams of 512 tokens (the recall workload): 64-token segments, eight per stream
     assert ws(B=64, H=4, T=512, d=32, dtype=0) == ws(B=64, H=4, T=512, d=32, dtype=0, path=2)
 
