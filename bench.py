@@ -641,9 +641,12 @@ def backward_bench(args, w):
     step is one call, on --path (auto: time segments for few long streams, else one segment
     per stream).  When the call runs on time segments, the one-segment-per-stream call is
     timed beside it (--bw-seq-steps calls, after one warm-up).  Work per token*head is counted
-    as the kernels execute it, two flops per multiply-add: the forward replay 12 d^2, the
-    reverse sweep 27 d^2 and, on time segments, the du correction 2 d^2 (the segment maps'
-    10 d^2 and the chunked forward passes are left out of the count)."""
+    as the kernels execute it, two flops per multiply-add: the forward (token by token, or the
+    chunked forward passes) 12 d^2; the S cotangent sweep 6 d^2; the chunked gradient pass
+    14 d^2 of products with a d x d operand plus 704 d of products within its 32-token chunks
+    (the 32 x 32 matrices: 5 of 2 * 32 d each, and 8 triangular products of about 3/4 of
+    2 * 32 d each); on time segments the du correction 2 d^2 (the segment maps' 10 d^2 are left
+    out of the count)."""
     import torch
     from rls_associative_memory_amd import vla
     from rls_associative_memory_amd.inputs import upload_inputs
@@ -675,7 +678,7 @@ def backward_bench(args, w):
     for kn, (tot, cnt) in sorted(kernels.items(), key=lambda kv: -kv[1][0]):
         print(f"[bench]   kernel {kn:16s} {tot / max(cnt, 1):9.3f} ms/launch x {cnt}", file=sys.stderr, flush=True)
     d2 = w.d * w.d
-    flops = (12 + 27) * d2 * tokens
+    flops = ((12 + 6 + 14) * d2 + 704 * w.d) * tokens
     if segmented:
         flops += 2 * d2 * tokens  # the segment maps' 10 d^2 (not on the first segment) are not counted
     achieved = flops / (ms * 1e-3) / 1e12

@@ -24,30 +24,30 @@
 // one at its start as  E Lmap + Bmap  (Lmap = the segment's forward map, transposed), and the
 // maps compose; dn is a suffix sum and so is R.  Passes, every one parallel over (stream,
 // segment) except the two scans:
-//   (chunked forward passes: S, A, n at every segment start)
-//   k_bw_replay   the forward token by token from the segment start: per-token vectors and the
-//                 state at every 64th token (and the segment's last)
+//   (chunked forward passes, or k_bw_replay with one segment per stream: the per-token
+//    vectors and the state at every 64th token and at every segment's last)
 //   k_bw_dsmap    per segment from the end: (Lmap, Bmap) and the segment's sum of dden phi(q)
 //   scan          dS and dn at every segment end (reverse order, so the forward scan applies)
-//   k_bw_grad     per segment from the end, the true dS and dn: dq, dk, dv, du with R local to
-//                 the segment, the segment's R sum and its trace
+//   k_bw_esweep   per segment from the end, the true dS: dr_t = dv_t token by token, and the
+//                 S cotangent at every 32nd token
+//   k_bw_cgrad    per segment, 32-token chunks from the end, on the fp32 matrix cores: dq, dk,
+//                 du with R local to the segment, the segment's R sum and its trace
 //   scan          R at every segment end (suffix sums, the final-state term first)
 //   k_bw_fix      du_t -= 2 R_end u_t over each segment's tokens
 //   k_bw_lambda   dlambda0 = -(tr of every segment's R sum + tr of the final-state term)
-// With one segment per stream the pipeline is replay, grad (R starting from the final-state
-// term) and lambda.
+// With one segment per stream the pipeline is replay, sweep, chunked pass (R starting from the
+// final-state term) and lambda.
 //
 // Layout of the per-token kernels: one workgroup of 512 threads per segment.  Thread (i, p) =
 // (tid / 16, tid % 16) holds rows i + 32 a and column pairs 2 p + 32 b of each d x d matrix in
 // registers, so row sums are 16-lane shuffles and column sums go through one LDS pass over the
-// eight waves in a fixed order (deterministic).  The reverse sweep undoes the rank-1 updates
-// token by token (S -= r ahat^T, A += s s^T with s = z / sqrt(delta)) and reloads the exact state at every
-// checkpoint, so rounding cannot drift over more than 32 steps.
+// eight waves in a fixed order (deterministic).
 
 #include <algorithm>
 
 #include "vla_common.h"
 #include "vla_internal.h"
+#include "vla_mfma.h"
 
 namespace vla {
 namespace {
@@ -56,6 +56,7 @@ constexpr int BW_NT = 512;
 constexpr int BW_NW = BW_NT / kWave;
 constexpr int BW_CK = kBwCk;       // tokens between state checkpoints
 constexpr int BW_NS = kBwScalars;  // scalar slots per token record
+constexpr int BW_CC = 32;          // tokens per chunk of the chunked gradient pass
 
 template <int D>
 struct BwCfg {
@@ -397,255 +398,579 @@ k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs, float *
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_bw_grad: the reverse sweep over segment p from the true cotangents at its end (Ebuf, ndbuf
-// at slot [stream][P - 1 - p]; NULL = 0), with R starting from Rinit[stream] (NULL = 0).
-// Writes dq, dk, dv, du = -2 R u with this R, the segment's R sum to Wbuf slot P - 1 - p when
-// Wbuf is not NULL, and the trace of the segment's own R sum (sum of w . y) to trw.
+// k_bw_esweep: the cotangent of S through segment p from its end (Ebuf at slot P - 1 - p; NULL =
+// 0), token by token in reverse.  With X the cotangent arriving at token t from later tokens,
+//   Shat = X + dnum_t phi(q_t)^T,   dr_t = Shat ahat_t (= dv_t),   X <- Shat - dr_t khat_t^T.
+// The rows of X evolve independently, so row sums stay inside a 16-lane row (no exchange
+// between waves).  Writes dv and, at the last token of every BW_CC-token chunk, X before that
+// token's terms ([stream][ceil(T / BW_CC)][d][d]): the chunked pass forms every other
+// gradient term of the chunk from it.
 // ---------------------------------------------------------------------------------------------
 template <int D>
-struct BwGradShared {
-  float kh[D], z[D], ah[D], r[D], fq[D], o[D], kr[D], u[D], dout[D];
-  float n[D], dn[D], dr[D], dah[D], w[D], dkh[D];
-  float part[2][BW_NW][D];
-  float sc[BW_NS];
+struct BwSweepShared {
+  float kh[2][D], ah[2][D], fq[2][D], dnum[2][D];
 };
 
 template <int D, typename TIn>
 __global__ void __launch_bounds__(BW_NT)
-k_bw_grad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ u,
-          const TIn *__restrict__ dout, const float *__restrict__ recs,
-          const float *__restrict__ cks, const float *__restrict__ n_end,
-          const float *__restrict__ Ebuf, const float *__restrict__ ndbuf,
-          const float *__restrict__ Rinit, float *__restrict__ dq, float *__restrict__ dk,
-          float *__restrict__ dv, float *__restrict__ du, float *__restrict__ Wbuf,
-          double *__restrict__ trw, int64_t T, int64_t L, int64_t P) {
+k_bw_esweep(const TIn *__restrict__ dout, const float *__restrict__ recs,
+            const float *__restrict__ Ebuf, float *__restrict__ dv, float *__restrict__ Xc,
+            int64_t T, int64_t L, int64_t P) {
   using C = BwCfg<D>;
   constexpr int R = C::R, NB = C::NB;
-  __shared__ BwGradShared<D> sh;
+  __shared__ BwSweepShared<D> sh;
   const int64_t s = blockIdx.x, p = blockIdx.y;
   const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, i = tid >> 4, pj = tid & 15;
-  const int64_t NC = (T + BW_CK - 1) / BW_CK;
+  const int tid = threadIdx.x, i = tid >> 4, pj = tid & 15;
+  const int64_t NX = (T + BW_CC - 1) / BW_CC;
   const float *rec0 = recs + s * T * C::REC;
-  const float *ck0 = cks + s * NC * 2 * D * D;
   const int64_t slot = s * P + (P - 1 - p);
   auto row = [&](int a) { return i + 32 * a; };
   auto col = [&](int b, int e) { return 2 * pj + 32 * b + e; };
-  // column sums over this thread's rows -> sh.part[slot][wave][c] (lanes 0..15 of a wave)
-  auto col_part = [&](int sl, const float (&x)[NB][2]) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float y = sum_rows4(x[b][e]);
-        if (lane < 16) sh.part[sl][w][col(b, e)] = y;
-      }
-  };
-  auto col_total = [&](int sl, int c) {
-    float y = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < BW_NW; ++ww) y += sh.part[sl][ww][c];
-    return y;
-  };
-  auto load_state = [&](int64_t t, float (&S)[R][NB][2], float (&A)[R][NB][2]) {
-    const float *ck = ck0 + (t / BW_CK) * 2 * D * D;
-#pragma unroll
-    for (int a = 0; a < R; ++a)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float2 sv = *reinterpret_cast<const float2 *>(ck + row(a) * D + col(b, 0));
-        const float2 av = *reinterpret_cast<const float2 *>(ck + D * D + row(a) * D + col(b, 0));
-        S[a][b][0] = sv.x; S[a][b][1] = sv.y;
-        A[a][b][0] = av.x; A[a][b][1] = av.y;
-      }
-  };
 
-  float S[R][NB][2], A[R][NB][2], dS[R][NB][2], Rm[R][NB][2];
-  load_state(te - 1, S, A);
+  float X[R][NB][2];
 #pragma unroll
   for (int a = 0; a < R; ++a)
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t off = row(a) * D + col(b, e);
-        dS[a][b][e] = Ebuf != nullptr ? Ebuf[slot * D * D + off] : 0.f;
-        Rm[a][b][e] = Rinit != nullptr ? Rinit[s * D * D + off] : 0.f;
-      }
-  if (tid < D) {
-    sh.dn[tid] = ndbuf != nullptr ? ndbuf[slot * D + tid] : 0.f;
-    sh.n[tid] = n_end[(s * P + p) * D + tid];
-  }
-  double trace = 0.0;  // thread 0: sum of w . y over the segment
+    for (int b = 0; b < NB; ++b) {
+      float2 x = make_float2(0.f, 0.f);
+      if (Ebuf != nullptr) x = *reinterpret_cast<const float2 *>(Ebuf + slot * D * D + row(a) * D + col(b, 0));
+      X[a][b][0] = x.x;
+      X[a][b][1] = x.y;
+    }
 
-  // Token t - 1's record and inputs are loaded (into registers) while token t is processed.
-  float pr[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, psc = 0.f;
-  TIn pk{}, pu{}, pdo{}, pq{};
-  auto load_rev = [&](int64_t t) {
+  // token t - 1's record is loaded while token t is processed
+  float pk = 0.f, pa = 0.f, pf = 0.f, pden = 1.f;
+  TIn pdo{};
+  auto load = [&](int64_t t) {
     const float *rec = rec0 + t * C::REC;
-    const int64_t tok = (s * T + t) * D;
     if (tid < D) {
-#pragma unroll
-      for (int f = 0; f < 6; ++f) pr[f] = rec[f * D + tid];
-      pk = k[tok + tid]; pu = u[tok + tid]; pdo = dout[tok + tid]; pq = q[tok + tid];
+      pk = rec[tid];
+      pa = rec[2 * D + tid];
+      pf = rec[4 * D + tid];
+      pdo = dout[(s * T + t) * D + tid];
     }
-    if (tid < BW_NS) psc = rec[6 * D + tid];
+    pden = rec[6 * D + 3];
   };
-  load_rev(te - 1);
+  load(te - 1);
   for (int64_t t = te - 1; t >= tb; --t) {
-    const int64_t tok = (s * T + t) * D;
-    if (t % BW_CK == BW_CK - 1 && t != te - 1) load_state(t, S, A);  // exact state after token t
-    float qt = 0.f;  // raw q of token t (for dq)
-    if (tid < D) {
-      sh.kh[tid] = pr[0];
-      sh.z[tid] = pr[1];
-      sh.ah[tid] = pr[2];
-      sh.r[tid] = pr[3];
-      sh.fq[tid] = pr[4];
-      sh.o[tid] = pr[5];
-      sh.kr[tid] = bw_cv(pk);
-      sh.u[tid] = bw_cv(pu);
-      sh.dout[tid] = bw_cv(pdo);
-      qt = bw_cv(pq);
-    }
-    if (tid < BW_NS) sh.sc[tid] = psc;
-    if (t > tb) load_rev(t - 1);
-    __syncthreads();
-    const float delta = sh.sc[0], ynorm = sh.sc[1], rk = sh.sc[2], den = sh.sc[3];
-    const float iden = 1.0f / den;
-    const float dden = -bw_dot<D>(sh.dout, sh.o, lane) * iden;
-    // dS += dnum phi(q)^T; column sums S^T dnum and dS^T r; row sums dS ahat
-    float drr[R];
-    {
-      float p1[NB][2], p2[NB][2];
+    if (t % BW_CC == BW_CC - 1 || t == te - 1) {
+      float *dst = Xc + (s * NX + t / BW_CC) * D * D;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) p1[b][0] = p1[b][1] = p2[b][0] = p2[b][1] = 0.f;
-#pragma unroll
-      for (int a = 0; a < R; ++a) {
-        const float dn_r = sh.dout[row(a)] * iden, r_r = sh.r[row(a)];
-        float rp = 0.f;
+      for (int a = 0; a < R; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int c = col(b, e);
-            dS[a][b][e] = fmaf(dn_r, sh.fq[c], dS[a][b][e]);
-            p1[b][e] = fmaf(S[a][b][e], dn_r, p1[b][e]);
-            p2[b][e] = fmaf(dS[a][b][e], r_r, p2[b][e]);
-            rp = fmaf(dS[a][b][e], sh.ah[c], rp);
-          }
-        drr[a] = rp;
-      }
-      row_sum16_n(drr);
-      if (pj == 0)
-#pragma unroll
-        for (int a = 0; a < R; ++a) sh.dr[row(a)] = drr[a];
-      col_part(0, p1);
-      col_part(1, p2);
+          *reinterpret_cast<float2 *>(dst + row(a) * D + col(b, 0)) = make_float2(X[a][b][0], X[a][b][1]);
     }
-    __syncthreads();
-    float dk_acc = 0.f;
+    const int buf = static_cast<int>(t & 1);
+    // double-buffered staging: this token's buffer was last read two tokens back, before the
+    // previous token's barrier
     if (tid < D) {
-      const float dphiq = col_total(0, tid) + dden * sh.n[tid];
-      dq[tok + tid] = dphiq * dphi(qt);
-      sh.dah[tid] = col_total(1, tid);
-      const float dnt = sh.dn[tid] + dden * sh.fq[tid];  // cotangent of n after token t
-      sh.dn[tid] = dnt;
-      dk_acc = dnt * dphi(sh.kr[tid]);
-      dv[tok + tid] = sh.dr[tid];
+      sh.kh[buf][tid] = pk;
+      sh.ah[buf][tid] = pa;
+      sh.fq[buf][tid] = pf;
+      sh.dnum[buf][tid] = bw_cv(pdo) / pden;
     }
+    if (t > tb) load(t - 1);
     __syncthreads();
-    const float ad = bw_dot<D>(sh.ah, sh.dah, lane);
-    const float iy = ynorm > 0.f ? 1.0f / ynorm : 0.f;
-    // S before the token and dS -= dr khat^T; row sums A' dy; column sums S^T dr (S before)
-    {
-      float p1[NB][2];
+    float dr[R];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) p1[b][0] = p1[b][1] = 0.f;
-      float dyc[NB][2], ap[R];
+    for (int a = 0; a < R; ++a) {
+      const float dn_r = sh.dnum[buf][row(a)];
+      float x = 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int c = col(b, e);
-          dyc[b][e] = (sh.dah[c] - sh.ah[c] * ad) * iy;
+          X[a][b][e] = fmaf(dn_r, sh.fq[buf][c], X[a][b][e]);
+          x = fmaf(X[a][b][e], sh.ah[buf][c], x);
         }
-#pragma unroll
-      for (int a = 0; a < R; ++a) {
-        const float r_r = sh.r[row(a)], dr_r = drr[a];
-        ap[a] = 0.f;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int c = col(b, e);
-            S[a][b][e] = fmaf(-r_r, sh.ah[c], S[a][b][e]);
-            dS[a][b][e] = fmaf(-dr_r, sh.kh[c], dS[a][b][e]);
-            ap[a] = fmaf(A[a][b][e], dyc[b][e], ap[a]);
-            p1[b][e] = fmaf(S[a][b][e], dr_r, p1[b][e]);
-          }
-      }
-      row_sum16_n(ap);
-      if (pj == 0)
-#pragma unroll
-        for (int a = 0; a < R; ++a) sh.w[row(a)] = ap[a];
-      col_part(0, p1);
+      dr[a] = x;
     }
-    __syncthreads();
-    if (tid < D) sh.dkh[tid] = sh.w[tid] - col_total(0, tid);
-    __syncthreads();
-    const float kd = bw_dot<D>(sh.kh, sh.dkh, lane);
-    const float wa = bw_dot<D>(sh.w, sh.ah, lane);
-    if (tid == 0) trace += static_cast<double>(wa) * ynorm;
-    // R += (w y^T + y w^T) / 2 (y = ahat ||y||), du = -2 R u, A before the token
-    // (A + s s^T, s = z / sqrt(delta), the replay's downdate undone)
-    {
-      const float hy = 0.5f * ynorm;
-      const float rsd = 1.0f / sqrtf(delta);
-      float sc[NB][2];
+    row_sum16_n(dr);
+#pragma unroll
+    for (int a = 0; a < R; ++a) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) sc[b][e] = sh.z[col(b, e)] * rsd;
-      float rp[R];
-#pragma unroll
-      for (int a = 0; a < R; ++a) {
-        const float w_r = sh.w[row(a)], ah_r = sh.ah[row(a)], s_r = sh.z[row(a)] * rsd;
-        rp[a] = 0.f;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int c = col(b, e);
-            Rm[a][b][e] = fmaf(hy, fmaf(w_r, sh.ah[c], ah_r * sh.w[c]), Rm[a][b][e]);
-            rp[a] = fmaf(Rm[a][b][e], sh.u[c], rp[a]);
-            A[a][b][e] = fmaf(s_r, sc[b][e], A[a][b][e]);
-          }
-      }
-      row_sum16_n(rp);
-      if (pj == 0)
-#pragma unroll
-        for (int a = 0; a < R; ++a) du[tok + row(a)] = -2.0f * rp[a];
+        for (int e = 0; e < 2; ++e) X[a][b][e] = fmaf(-dr[a], sh.kh[buf][col(b, e)], X[a][b][e]);
+      if (pj == 0) dv[(s * T + t) * D + row(a)] = dr[a];
     }
-    if (tid < D) {
-      dk[tok + tid] = dk_acc + (sh.dkh[tid] - sh.kh[tid] * kd) * rk;
-      sh.n[tid] -= phi(sh.kr[tid]);  // n before the token
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_bw_cgrad: every gradient term but dv over segment p, in chunks of BW_CC tokens from the end,
+// on the fp32 matrix cores.  Within a chunk [c0, c1) (rows: the chunk's tokens), with X the
+// S cotangent at its last token (k_bw_esweep), dR the rows dr_t (= dv), Dn the rows
+// dnum_t = do_t / den_t, Rr the residuals r_t, S0 and A0 the state before c0:
+//   dAhat = Rr X + triu0(Rr Dn^T) Phi(q) - triu1(Rr dR^T) Khat          (dahat_t = Shat_t^T r_t)
+//   dY    = (dAhat - ahat (ahat . dAhat)) / ||y||                        (row by row)
+//   W     = dY A0 - tril0(dY Z^T) D^{-1} Z                               (w_t = A_t dy_t)
+//   dKhat = W - dR S0 - tril(-1)(dR Rr^T) Ahat                           (- S_{t-1}^T dr_t + w_t)
+//   dPhiq = Dn S0 + tril0(Dn Rr^T) Ahat + dden n_t                       (S_t^T dnum_t + dden n_t)
+//   dU    = -2 U R1 - triu0(U Y^T) W - triu0(U W^T) Y                    (-2 R_s u_s, R local)
+//   R0    = R1 + (W^T Y + Y^T W) / 2,    Y = diag(||y||) Ahat
+// where S_t = S0 + sum_{i <= t} r_i ahat_i^T and A_t = A0 - sum_{i <= t} z_i z_i^T / delta_i
+// (the forward's own updates), and dn_t, n_t are suffix sums over the chunk.  The state before
+// c0 is the checkpoint before c0 when c0 is a multiple of BW_CK, else the checkpoint after
+// c1 - 1 with the chunk's own updates undone (two more products).  Wave w owns features
+// 16 w .. 16 w + 15 of every token-by-feature result, and the matching column tiles of S0, A0,
+// X and R in registers (in the accumulator layout, which is the B-operand layout of the
+// permuted contraction index).  Same outputs and buffers as the token-by-token sweep: dq, dk,
+// du = -2 R u with R local to the segment (from Rinit, NULL = 0), the segment's R sum to Wbuf
+// slot P - 1 - p when Wbuf is not NULL, and the sum of w . y to trw.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+struct CgCfg {
+  static constexpr int NW = D / 16;      // waves
+  static constexpr int NT = NW * kWave;
+  static constexpr int KB = D / 16;      // 16-feature blocks of a contraction over features
+  static constexpr int LDT = D + 4;      // fp32 stride of token rows
+  static constexpr int LDC = BW_CC + 4;  // fp32 stride of the chunk-by-chunk matrices
+  static constexpr int G4 = D / 4;       // float4 groups per token row
+};
+
+template <int D>
+struct CgShared {
+  using C = CgCfg<D>;
+  float Rr[BW_CC][C::LDT];  // residuals r; W once dAhat is formed
+  float Dn[BW_CC][C::LDT];  // dnum
+  float dR[BW_CC][C::LDT];  // dr
+  float Fq[BW_CC][C::LDT];  // phi(q); dY once dAhat is formed
+  float Kh[BW_CC][C::LDT];  // khat
+  float Ah[BW_CC][C::LDT];  // ahat
+  float Zr[BW_CC][C::LDT];  // z
+  float Ur[BW_CC][C::LDT];  // u
+  float M1[BW_CC][C::LDC];  // Rr Dn^T (upper, with the diagonal); U Y^T later
+  float M2[BW_CC][C::LDC];  // Rr dR^T (strictly upper); U W^T later
+  float M3[BW_CC][C::LDC];  // dY Z^T D^{-1} (lower, with the diagonal)
+  float rd[BW_CC], yn[BW_CC], rk[BW_CC], den[BW_CC], dd[BW_CC];
+  float dpo[BW_CC][C::G4];  // do . o over 4 features
+  float part[3][C::NW][BW_CC];
+  float dn[D], n[D];        // cotangent of n and n at the chunk's last token
+};
+
+template <int D, typename TIn>
+__global__ void __launch_bounds__(CgCfg<D>::NT)
+k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ u,
+           const TIn *__restrict__ dout, const float *__restrict__ recs,
+           const float *__restrict__ cks, const float *__restrict__ n_end,
+           const float *__restrict__ Xc, const float *__restrict__ dv,
+           const float *__restrict__ ndbuf, const float *__restrict__ Rinit,
+           float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ du,
+           float *__restrict__ Wbuf, double *__restrict__ trw, int64_t T, int64_t L, int64_t P,
+           float lambda0) {
+  using C = CgCfg<D>;
+  constexpr int NW = C::NW, KB = C::KB, NT = C::NT, G4 = C::G4, REC = BwRec<D>::F;
+  __shared__ __attribute__((aligned(16))) CgShared<D> sh;
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, gq = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int f = 16 * w + li;  // this lane's feature in every token-by-feature result
+  const int64_t NC = (T + BW_CK - 1) / BW_CK, NX = (T + BW_CC - 1) / BW_CC;
+  const float *rec0 = recs + s * T * REC;
+  const float *ck0 = cks + s * NC * 2 * D * D;
+  const int64_t slot = s * P + (P - 1 - p);
+  auto ld4 = [](const float *x) { return *reinterpret_cast<const f4_t *>(x); };
+  // acc + sgn * A B over the feature index for one 16 x 16 tile: A's row is arow (this lane's
+  // token row in LDS, read 16 bytes at a time), B a register column tile in the accumulator
+  // layout.  The next block's operand is read before this block's products, and nothing moves
+  // across the blocks, so at most two blocks of operands are live.
+  auto mm_rt = [&](f4_t acc, const float *arow, const f4_t (&bt)[KB], float sgn) {
+    f4_t a = ld4(arow + 4 * gq);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f4_t an = a;
+      if (kb + 1 < KB) an = ld4(arow + 16 * (kb + 1) + 4 * gq);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = mfma_f32_16x16x4(sgn * a[r], bt[kb][r], acc);
+      a = an;
+    }
+    return acc;
+  };
+  // A B^T over the feature index for one tile: both operands token rows in LDS
+  auto mm_rr = [&](const float *arow, const float *brow, float bs) {
+    f4_t acc = f4_zero();
+    f4_t a = ld4(arow + 4 * gq), b = ld4(brow + 4 * gq);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f4_t an = a, bn = b;
+      if (kb + 1 < KB) {
+        an = ld4(arow + 16 * (kb + 1) + 4 * gq);
+        bn = ld4(brow + 16 * (kb + 1) + 4 * gq);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = mfma_f32_16x16x4(a[r], b[r] * bs, acc);
+      a = an;
+      b = bn;
+    }
+    return acc;
+  };
+
+  // R[16 kb + 4 gq + r][f] in Rt[kb][r]
+  f4_t Rt[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      Rt[kb][r] = Rinit != nullptr ? Rinit[s * D * D + (16 * kb + 4 * gq + r) * D + f] : 0.f;
+  if (tid < D) {
+    sh.dn[tid] = ndbuf != nullptr ? ndbuf[slot * D + tid] : 0.f;
+    sh.n[tid] = n_end[(s * P + p) * D + tid];
+  }
+  double trace = 0.0;  // thread 0
+
+  for (int64_t c1 = te; c1 > tb;) {
+    const int64_t c0 = std::max<int64_t>(tb, ((c1 - 1) / BW_CC) * BW_CC);
+    const int m = static_cast<int>(c1 - c0);
+    // Opaque per-chunk copies of the lane indices: the LDS and memory addresses derived from
+    // them are formed again in each chunk instead of being hoisted out of the loop and held.
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, li = lane & 15, gq = lane >> 4, f = 16 * w + li;
+    // The state (S, A) the products start from: before c0 when c0 is a checkpoint boundary
+    // (the fixed start at c0 = 0), else after c1 - 1, with the chunk's own rank-1 terms taken
+    // back through the other triangle of the chunk matrices.
+    const bool bef = (c0 % BW_CK) == 0;
+    const bool init = bef && c0 == 0;
+    const float *ck = ck0 + (bef ? (init ? 0 : (c0 - 1) / BW_CK) : (c1 - 1) / BW_CK) * 2 * D * D;
+    // the chunk's rows: uniform bases, 32-bit offsets within the chunk
+    const int64_t tok0 = (s * T + c0) * D;
+    const float *rcb = rec0 + c0 * REC;
+    const TIn *qb = q + tok0, *kb0 = k + tok0, *ub = u + tok0, *dob = dout + tok0;
+    const float *dvb = dv + tok0;
+    float *dqb = dq + tok0, *dkb = dk + tok0, *dub = du + tok0;
+    // column tile of a d x d matrix in the accumulator layout: x[16 kb + 4 gq + r][f], or
+    // dg times the identity where x is NULL
+    auto ld_tile = [&](const float *x, float dg, f4_t (&t)[KB]) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rw = 16 * kb + 4 * gq + r;
+          t[kb][r] = x != nullptr ? x[rw * D + f] : (rw == f ? dg : 0.f);
+        }
+    };
+    __syncthreads();  // the previous chunk's readers are done
+    // ---- stage the chunk's rows (rows past the chunk are zeros) ----
+    for (int e = tid; e < BW_CC * G4; e += NT) {
+      const int t = e / G4, c = 4 * (e % G4);
+      f4_t rr = f4_zero(), dn = f4_zero(), dr = f4_zero(), fq = f4_zero(), kh = f4_zero(),
+           ah = f4_zero(), zz = f4_zero(), uu = f4_zero();
+      float po = 0.f;
+      if (t < m) {
+        const float *rec = rcb + static_cast<uint32_t>(t * REC);
+        const uint32_t o = static_cast<uint32_t>(t * D + c);
+        const float rden = 1.0f / rec[6 * D + 3];
+        const f4_t oo = ld4(rec + 5 * D + c);
+        kh = ld4(rec + c);
+        zz = ld4(rec + D + c);
+        ah = ld4(rec + 2 * D + c);
+        rr = ld4(rec + 3 * D + c);
+        fq = ld4(rec + 4 * D + c);
+        dr = ld4(dvb + o);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float d = bw_cv(dob[o + j]);
+          dn[j] = d * rden;
+          po = fmaf(d, oo[j], po);
+          uu[j] = bw_cv(ub[o + j]);
+        }
+      }
+      *reinterpret_cast<f4_t *>(&sh.Rr[t][c]) = rr;
+      *reinterpret_cast<f4_t *>(&sh.Dn[t][c]) = dn;
+      *reinterpret_cast<f4_t *>(&sh.dR[t][c]) = dr;
+      *reinterpret_cast<f4_t *>(&sh.Fq[t][c]) = fq;
+      *reinterpret_cast<f4_t *>(&sh.Kh[t][c]) = kh;
+      *reinterpret_cast<f4_t *>(&sh.Ah[t][c]) = ah;
+      *reinterpret_cast<f4_t *>(&sh.Zr[t][c]) = zz;
+      *reinterpret_cast<f4_t *>(&sh.Ur[t][c]) = uu;
+      sh.dpo[t][c / 4] = po;
+    }
+    if (tid < BW_CC) {
+      const int t = tid;
+      const float *rec = rcb + static_cast<uint32_t>((t < m ? t : 0) * REC);
+      sh.rd[t] = t < m ? 1.0f / rec[6 * D + 0] : 0.f;
+      sh.yn[t] = t < m ? rec[6 * D + 1] : 0.f;
+      sh.rk[t] = t < m ? rec[6 * D + 2] : 0.f;
+      sh.den[t] = t < m ? rec[6 * D + 3] : 1.f;
+    }
+    f4_t Xt[KB];
+    ld_tile(Xc + (s * NX + (c1 - 1) / BW_CC) * D * D, 0.f, Xt);
+    __syncthreads();
+    // dden_t = -(do_t . o_t) / den_t, the partial sums added in a fixed order
+    if (tid < BW_CC) {
+      float x = 0.f;
+#pragma unroll
+      for (int g = 0; g < G4; ++g) x += sh.dpo[tid][g];
+      sh.dd[tid] = -x / sh.den[tid];
+    }
+    // ---- M1 = Rr Dn^T, M2 = Rr dR^T (all four tiles) ----
+    for (int job = w; job < 8; job += NW) {
+      const int mat = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
+      const float(*B)[C::LDT] = mat == 0 ? sh.Dn : sh.dR;
+      const f4_t acc = mm_rr(&sh.Rr[16 * ti + li][0], &B[16 * tj + li][0], 1.f);
+      float(*M)[C::LDC] = mat == 0 ? sh.M1 : sh.M2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) M[16 * ti + 4 * gq + r][16 * tj + li] = acc[r];
     }
     __syncthreads();
+    // ---- dAhat = Rr X + triu0(M1) Phi(q) - triu1(M2) Khat; dN_t = sum_{j >= t} dden_j phi(q_j) ----
+    f4_t dA[2], DN[2];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      f4_t acc = mm_rt(f4_zero(), &sh.Rr[16 * ti + li][0], Xt, 1.f), dacc = f4_zero();
+      const int tr = 16 * ti + li;  // the A operand's row (token)
+#pragma unroll
+      for (int kb = ti; kb < 2; ++kb) {
+        const f4_t a1 = ld4(&sh.M1[tr][16 * kb + 4 * gq]);
+        const f4_t a2 = ld4(&sh.M2[tr][16 * kb + 4 * gq]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * kb + 4 * gq + r;
+          const float fqj = sh.Fq[j][f];
+          acc = mfma_f32_16x16x4(j >= tr ? a1[r] : 0.f, fqj, acc);
+          acc = mfma_f32_16x16x4(j > tr ? -a2[r] : 0.f, sh.Kh[j][f], acc);
+          dacc = mfma_f32_16x16x4(j >= tr ? sh.dd[j] : 0.f, fqj, dacc);
+        }
+      }
+      dA[ti] = acc;
+      DN[ti] = dacc;
+    }
+    {
+      float x[8];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[4 * ti + r] = dA[ti][r] * sh.Ah[16 * ti + 4 * gq + r][f];
+      row_sum16_n(x);
+      if (li == 0)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sh.part[0][w][16 * ti + 4 * gq + r] = x[4 * ti + r];
+    }
+    __syncthreads();
+    // dY over the phi(q) rows (each wave's own columns; the other waves' reads of phi(q) and
+    // of the partial sums are behind the barrier)
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * gq + r;
+        float ad = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) ad += sh.part[0][ww][t];
+        const float y = sh.yn[t];
+        sh.Fq[t][f] = y > 0.f ? (dA[ti][r] - sh.Ah[t][f] * ad) / y : 0.f;
+      }
+    __syncthreads();
+    // ---- M3 = dY Z^T D^{-1} (all four tiles) ----
+    for (int job = w; job < 4; job += NW) {
+      const int ti = job >> 1, tj = job & 1;
+      const f4_t acc = mm_rr(&sh.Fq[16 * ti + li][0], &sh.Zr[16 * tj + li][0], 1.f);
+      const float rdj = sh.rd[16 * tj + li];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sh.M3[16 * ti + 4 * gq + r][16 * tj + li] = acc[r] * rdj;
+    }
+    f4_t Mt[KB];  // A's column tile
+    ld_tile(init ? nullptr : ck + D * D, 1.0f / lambda0, Mt);
+    __syncthreads();
+    // ---- W = dY A - (sum over i <= t | - sum over i > t) M3[t][i] z_i, over the residual rows ----
+    f4_t Wv[2];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      f4_t acc = mm_rt(f4_zero(), &sh.Fq[16 * ti + li][0], Mt, 1.f);
+      const int tr = 16 * ti + li;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (bef ? kb > ti : kb < ti) continue;  // whole tile masked (uniform)
+        const f4_t av = ld4(&sh.M3[tr][16 * kb + 4 * gq]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * kb + 4 * gq + r;
+          const float a = bef ? (j <= tr ? -av[r] : 0.f) : (j > tr ? av[r] : 0.f);
+          acc = mfma_f32_16x16x4(a, sh.Zr[j][f], acc);
+        }
+      }
+      Wv[ti] = acc;
+    }
+    ld_tile(init ? nullptr : ck, 0.f, Mt);  // S's column tile
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sh.Rr[16 * ti + 4 * gq + r][f] = Wv[ti][r];
+    // ---- dKhat = W - dR S -/+ (M2^T part) Ahat;  dPhiq = Dn S +/- (M1^T part) Ahat ----
+    f4_t dK[2], dQ[2];
+    // raw k of every token of the chunk at this lane's feature (for n_t and phi'(k))
+    float kr[BW_CC];
+#pragma unroll
+    for (int j = 0; j < BW_CC; ++j) kr[j] = bw_cv(kb0[static_cast<uint32_t>((j < m ? j : 0) * D + f)]);
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      f4_t ak = mm_rt(Wv[ti], &sh.dR[16 * ti + li][0], Mt, -1.f);
+      f4_t aq = mm_rt(f4_zero(), &sh.Dn[16 * ti + li][0], Mt, 1.f);
+      const int tr = 16 * ti + li;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (bef ? kb > ti : kb < ti) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * kb + 4 * gq + r;
+          const float ahj = sh.Ah[j][f];
+          const float m2 = sh.M2[j][tr], m1 = sh.M1[j][tr];
+          // before: S_{t-1} = S0 + sum_{j < t}, S_t = S0 + sum_{j <= t};
+          // after:  S_{t-1} = Se - sum_{j >= t}, S_t = Se - sum_{j > t}
+          ak = mfma_f32_16x16x4(bef ? (j < tr ? -m2 : 0.f) : (j >= tr ? m2 : 0.f), ahj, ak);
+          aq = mfma_f32_16x16x4(bef ? (j <= tr ? m1 : 0.f) : (j > tr ? -m1 : 0.f), ahj, aq);
+        }
+      }
+      dK[ti] = ak;
+      dQ[ti] = aq;
+    }
+    {
+      float x[16];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * ti + 4 * gq + r;
+          x[4 * ti + r] = dK[ti][r] * sh.Kh[t][f];
+          x[8 + 4 * ti + r] = Wv[ti][r] * sh.Ah[t][f];
+        }
+      row_sum16_n(x);
+      if (li == 0)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sh.part[1][w][16 * ti + 4 * gq + r] = x[4 * ti + r];
+            sh.part[2][w][16 * ti + 4 * gq + r] = x[8 + 4 * ti + r];
+          }
+    }
+    __syncthreads();
+    // ---- dq, dk ----
+    const float dnf = sh.dn[f];
+    // n_t token by token backwards from the chunk's last token, n_{t-1} = n_t - phi(k_t): the
+    // exact inverse of the forward's additions where the forward added token by token (a
+    // chunk sum subtracted at once would not be, and n_t for early tokens is a small
+    // difference of large sums)
+    float nv[2][4], kv[2][4], n_prev = sh.n[f];
+#pragma unroll
+    for (int j = BW_CC - 1; j >= 0; --j) {
+      if (((j >> 2) & 3) == gq) {  // token j is this lane's output position (j >> 4, j & 3)
+        nv[j >> 4][j & 3] = n_prev;
+        kv[j >> 4][j & 3] = kr[j];
+      }
+      if (j < m) n_prev -= phi(kr[j]);
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * gq + r;
+        if (t < m) {
+          float kd = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww) kd += sh.part[1][ww][t];
+          const uint32_t o = static_cast<uint32_t>(t * D + f);
+          const float dnt = dnf + DN[ti][r];
+          dqb[o] = (dQ[ti][r] + sh.dd[t] * nv[ti][r]) * dphi(bw_cv(qb[o]));
+          dkb[o] = (dK[ti][r] - sh.Kh[t][f] * kd) * sh.rk[t] + dnt * dphi(kv[ti][r]);
+        }
+      }
+    if (tid == 0) {
+      double tr = 0.0;
+      for (int t = 0; t < m; ++t) {
+        float wy = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) wy += sh.part[2][ww][t];
+        tr += static_cast<double>(wy) * sh.yn[t];
+      }
+      trace += tr;
+    }
+    // dn carried to the previous chunk: lanes gq = 0 hold token 0's sum
+    const float dn_prev = dnf + DN[0][0];
+    // ---- M1 <- U Y^T, M2 <- U W^T (all four tiles) ----
+    for (int job = w; job < 8; job += NW) {
+      const int mat = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
+      const float ys = mat == 0 ? sh.yn[16 * tj + li] : 1.f;
+      const float(*B)[C::LDT] = mat == 0 ? sh.Ah : sh.Rr;
+      const f4_t acc = mm_rr(&sh.Ur[16 * ti + li][0], &B[16 * tj + li][0], ys);
+      float(*M)[C::LDC] = mat == 0 ? sh.M1 : sh.M2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) M[16 * ti + 4 * gq + r][16 * tj + li] = acc[r];
+    }
+    __syncthreads();
+    if (gq == 0) {
+      sh.dn[f] = dn_prev;
+      sh.n[f] = n_prev;
+    }
+    // ---- du = -2 U R - triu0(U Y^T) W - triu0(U W^T) Y ----
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const f4_t a1 = mm_rt(f4_zero(), &sh.Ur[16 * ti + li][0], Rt, 1.f);
+      f4_t a2 = f4_zero();
+      const int tr = 16 * ti + li;
+#pragma unroll
+      for (int kb = ti; kb < 2; ++kb) {
+        const f4_t m4 = ld4(&sh.M1[tr][16 * kb + 4 * gq]);
+        const f4_t m5 = ld4(&sh.M2[tr][16 * kb + 4 * gq]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * kb + 4 * gq + r;
+          a2 = mfma_f32_16x16x4(j >= tr ? m4[r] : 0.f, sh.Rr[j][f], a2);
+          a2 = mfma_f32_16x16x4(j >= tr ? m5[r] : 0.f, sh.Ah[j][f] * sh.yn[j], a2);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * gq + r;
+        if (t < m) dub[static_cast<uint32_t>(t * D + f)] = -2.0f * a1[r] - a2[r];
+      }
+    }
+    // ---- R += (W^T Y + Y^T W) / 2 ----
+    {
+      float yh[8], yf[8], wf[8];
+#pragma unroll
+      for (int q8 = 0; q8 < 8; ++q8) {
+        const int t = 16 * (q8 >> 2) + 4 * gq + (q8 & 3);
+        yh[q8] = 0.5f * sh.yn[t];
+        yf[q8] = sh.Ah[t][f] * yh[q8];
+        wf[q8] = sh.Rr[t][f];
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        float wa[8], aa[8];
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) {
+          const int t = 16 * (q8 >> 2) + 4 * gq + (q8 & 3);
+          wa[q8] = sh.Rr[t][16 * kb + li];
+          aa[q8] = sh.Ah[t][16 * kb + li];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q8 = 0; q8 < 8; ++q8) {
+          Rt[kb] = mfma_f32_16x16x4(wa[q8], yf[q8], Rt[kb]);
+          Rt[kb] = mfma_f32_16x16x4(aa[q8] * yh[q8], wf[q8], Rt[kb]);
+        }
+      }
+    }
+    c1 = c0;
   }
   if (Wbuf != nullptr) {
     float *dst = Wbuf + slot * D * D;
-    const float *r0 = Rinit != nullptr ? Rinit + s * D * D : nullptr;
 #pragma unroll
-    for (int a = 0; a < R; ++a)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        float2 x = make_float2(Rm[a][b][0], Rm[a][b][1]);
-        if (r0 != nullptr) {
-          x.x -= r0[row(a) * D + col(b, 0)];
-          x.y -= r0[row(a) * D + col(b, 1)];
-        }
-        *reinterpret_cast<float2 *>(dst + row(a) * D + col(b, 0)) = x;
+      for (int r = 0; r < 4; ++r) {
+        const int rw = 16 * kb + 4 * gq + r;
+        dst[rw * D + f] = Rt[kb][r] - (Rinit != nullptr ? Rinit[s * D * D + rw * D + f] : 0.f);
       }
   }
   if (tid == 0) trw[s * P + p] = trace;
@@ -765,8 +1090,8 @@ k_bw_lambda(const float *__restrict__ X, const double *__restrict__ trw, float *
 // ---------------------------------------------------------------------------------------------
 struct BwPlan {
   int64_t L = 0, P = 1;
-  size_t off_chunk = 0, off_md = 0, off_rec = 0, off_ck = 0, off_nend = 0, off_x = 0, off_y = 0,
-         off_trw = 0;
+  size_t off_chunk = 0, off_md = 0, off_rec = 0, off_ck = 0, off_xc = 0, off_nend = 0, off_x = 0,
+         off_y = 0, off_trw = 0;
   size_t total = 0;
 };
 
@@ -793,6 +1118,7 @@ BwPlan make_bw_plan(const Problem &p, int chunk) {
   const size_t NC = (T + BW_CK - 1) / BW_CK;
   b.off_rec = off;  off = align256(off + S * T * (6 * D + BW_NS) * 4);
   b.off_ck = off;   off = align256(off + S * NC * 2 * D * D * 4);
+  b.off_xc = off;   off = align256(off + S * ((T + BW_CC - 1) / BW_CC) * D * D * 4);
   b.off_nend = off; off = align256(off + S * P * D * 4);
   b.off_x = off;    off = align256(off + S * D * D * 4);
   b.off_y = off;    off = align256(off + S * D * D * 4);
@@ -811,6 +1137,7 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
   float *X = io.dA_T != nullptr ? reinterpret_cast<float *>(base + bp.off_x) : nullptr;
   float *Y = reinterpret_cast<float *>(base + bp.off_y);
   double *trw = reinterpret_cast<double *>(base + bp.off_trw);
+  float *xc = reinterpret_cast<float *>(base + bp.off_xc);
   const TIn *q = static_cast<const TIn *>(io.q), *k = static_cast<const TIn *>(io.k);
   const TIn *v = static_cast<const TIn *>(io.v), *u = static_cast<const TIn *>(io.u);
   const TIn *dout = static_cast<const TIn *>(io.dout);
@@ -850,21 +1177,28 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
                static_cast<const float *>(rec), lb, nd, pr.T, bp.L, bp.P);
     err = launch_affine_prefix(pr, lb, E, bp.P, io.dS_T, nd, io.dn_T, st);
     if (err != hipSuccess) return err;
-    VLA_LAUNCH("k_bw_grad", (k_bw_grad<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, u, dout,
-               static_cast<const float *>(rec), static_cast<const float *>(ck),
-               static_cast<const float *>(nend), static_cast<const float *>(E),
-               static_cast<const float *>(nd), static_cast<const float *>(nullptr), io.dq, io.dk,
-               io.dv, io.du, W, trw, pr.T, bp.L, bp.P);
+    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, dout,
+               static_cast<const float *>(rec), static_cast<const float *>(E), io.dv, xc, pr.T,
+               bp.L, bp.P);
+    VLA_LAUNCH("k_bw_cgrad", (k_bw_cgrad<D, TIn>), dim3(S, P), dim3(CgCfg<D>::NT), 0, st, q, k, u,
+               dout, static_cast<const float *>(rec), static_cast<const float *>(ck),
+               static_cast<const float *>(nend), static_cast<const float *>(xc),
+               static_cast<const float *>(io.dv), static_cast<const float *>(nd),
+               static_cast<const float *>(nullptr), io.dq, io.dk, io.du, W, trw, pr.T, bp.L, bp.P,
+               pr.lambda0);
     err = launch_matrix_prefix(pr, W, bp.P, X, st);
     if (err != hipSuccess) return err;
     const unsigned nz = static_cast<unsigned>((bp.L + 255) / 256);
     VLA_LAUNCH("k_bw_fix", (k_bw_fix<D, TIn>), dim3(S, P, nz), dim3(256), 0, st, u,
                static_cast<const float *>(W), io.du, pr.T, bp.L, bp.P);
   } else {
-    VLA_LAUNCH("k_bw_grad", (k_bw_grad<D, TIn>), dim3(S, 1), dim3(BW_NT), 0, st, q, k, u, dout,
-               static_cast<const float *>(rec), static_cast<const float *>(ck),
-               static_cast<const float *>(nend), io.dS_T, io.dn_T, static_cast<const float *>(X),
-               io.dq, io.dk, io.dv, io.du, static_cast<float *>(nullptr), trw, pr.T, bp.L, bp.P);
+    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, 1), dim3(BW_NT), 0, st, dout,
+               static_cast<const float *>(rec), io.dS_T, io.dv, xc, pr.T, bp.L, bp.P);
+    VLA_LAUNCH("k_bw_cgrad", (k_bw_cgrad<D, TIn>), dim3(S, 1), dim3(CgCfg<D>::NT), 0, st, q, k, u,
+               dout, static_cast<const float *>(rec), static_cast<const float *>(ck),
+               static_cast<const float *>(nend), static_cast<const float *>(xc),
+               static_cast<const float *>(io.dv), io.dn_T, static_cast<const float *>(X), io.dq,
+               io.dk, io.du, static_cast<float *>(nullptr), trw, pr.T, bp.L, bp.P, pr.lambda0);
   }
   if (io.dlambda0 != nullptr)
     VLA_LAUNCH("k_bw_lambda", (k_bw_lambda<D>), dim3(S), dim3(64), 0, st,
