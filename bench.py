@@ -645,7 +645,7 @@ def backward_bench(args, w):
     chunked forward passes) 12 d^2; the S cotangent sweep 6 d^2; the chunked gradient pass
     14 d^2 of products with a d x d operand plus 704 d of products within its 32-token chunks
     (the 32 x 32 matrices: 5 of 2 * 32 d each, and 8 triangular products of about 3/4 of
-    2 * 32 d each); on time segments the du correction 2 d^2 (the segment maps' 10 d^2 are left
+    2 * 32 d each); on time segments the du correction 2 d^2 (the segment maps' 6 d^2 are left
     out of the count)."""
     import torch
     from rls_associative_memory_amd import vla
@@ -680,7 +680,7 @@ def backward_bench(args, w):
     d2 = w.d * w.d
     flops = ((12 + 6 + 14) * d2 + 704 * w.d) * tokens
     if segmented:
-        flops += 2 * d2 * tokens  # the segment maps' 10 d^2 (not on the first segment) are not counted
+        flops += 2 * d2 * tokens  # the segment maps' 6 d^2 (not on the first segment) are not counted
     achieved = flops / (ms * 1e-3) / 1e12
     seq = None
     if segmented and args.bw_seq_steps > 0:

@@ -284,11 +284,13 @@ k_bw_replay(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__r
 
 // ---------------------------------------------------------------------------------------------
 // k_bw_dsmap: segment p = blockIdx.y + 1 (the first segment's map is never needed) from its end
-// with the cotangent E at the end left symbolic: E_start = E Lmap + Bmap, Lmap = prod of
-// (I - ahat khat^T)^T from the last token down, Bmap the same recursion from 0 with the readout
-// terms.  Written to slot P - 1 - p of lb ([stream][P][2][d][d]: Lmap, Bmap) and nd
-// ([stream][P][d]: the segment's sum of dden phi(q)), so that the forward scans, run over the
-// slots, give the cotangents at every segment end.
+// with the cotangent E at the end left symbolic: E_start = E Lmap + Bmap.  Lmap, the product of
+// (I - ahat_t khat_t^T) from the last token down, is the transpose of the forward's segment map
+// Pi_p (the product of (I - khat_t ahat_t^T) in token order), which the chunked forward's map
+// pass left in fpm ([stream][P][2][d][d], Pi_p first); Bmap is that recursion from 0 with the
+// readout terms, token by token (rows independent).  Written to slot P - 1 - p of lb
+// ([stream][P][2][d][d]: Lmap, Bmap) and nd ([stream][P][d]: the segment's sum of dden phi(q)),
+// so that the forward scans, run over the slots, give the cotangents at every segment end.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 struct BwMapShared {
@@ -297,8 +299,9 @@ struct BwMapShared {
 
 template <int D, typename TIn>
 __global__ void __launch_bounds__(BW_NT)
-k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs, float *__restrict__ lb,
-           float *__restrict__ nd, int64_t T, int64_t L, int64_t P) {
+k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs,
+           const float *__restrict__ fpm, float *__restrict__ lb, float *__restrict__ nd, int64_t T,
+           int64_t L, int64_t P) {
   using C = BwCfg<D>;
   constexpr int R = C::R, NB = C::NB;
   __shared__ BwMapShared<D> sh;
@@ -309,16 +312,24 @@ k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs, float *
   auto row = [&](int a) { return i + 32 * a; };
   auto col = [&](int b, int e) { return 2 * pj + 32 * b + e; };
 
-  float Lm[R][NB][2], Bm[R][NB][2];
+  const int64_t slot = s * P + (P - 1 - p);
+  {  // Lmap = Pi_p^T
+    const float *pi = fpm + (s * P + p) * 2 * D * D;
+    float *dst = lb + slot * 2 * D * D;
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        *reinterpret_cast<float2 *>(dst + row(a) * D + col(b, 0)) =
+            make_float2(pi[col(b, 0) * D + row(a)], pi[col(b, 1) * D + row(a)]);
+  }
+  float Bm[R][NB][2];
 #pragma unroll
   for (int a = 0; a < R; ++a)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        Lm[a][b][e] = row(a) == col(b, e) ? 1.f : 0.f;
-        Bm[a][b][e] = 0.f;
-      }
+      for (int e = 0; e < 2; ++e) Bm[a][b][e] = 0.f;
   float ndp = 0.f;  // thread f < d: sum of dden phi(q)_f
 
   // token t - 1's record is loaded while token t is processed
@@ -351,15 +362,17 @@ k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs, float *
     const float den = pden;
     if (t > tb) load(t - 1);
     __syncthreads();
-    float xo = 0.f;
-    for (int c = lane; c < D; c += kWave) xo += sh.x[buf][c];
-    xo = wave_sum(xo);
-    if (tid < D) ndp = fmaf(-xo / den, sh.fq[buf][tid], ndp);
-    float bl[2 * R];  // row sums of B ahat and L ahat for every row of this thread
+    if (tid < (D + kWave - 1) / kWave * kWave) {  // the waves that hold n's features (uniform)
+      float xo = 0.f;
+      for (int c = lane; c < D; c += kWave) xo += sh.x[buf][c];
+      xo = wave_sum(xo);
+      if (tid < D) ndp = fmaf(-xo / den, sh.fq[buf][tid], ndp);
+    }
+    float bl[R];  // row sums of B ahat for every row of this thread
 #pragma unroll
     for (int a = 0; a < R; ++a) {
       const float dn_r = sh.dnum[buf][row(a)];
-      float bp = 0.f, lp = 0.f;
+      float bp = 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -367,33 +380,23 @@ k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs, float *
           const int c = col(b, e);
           Bm[a][b][e] = fmaf(dn_r, sh.fq[buf][c], Bm[a][b][e]);
           bp = fmaf(Bm[a][b][e], sh.ah[buf][c], bp);
-          lp = fmaf(Lm[a][b][e], sh.ah[buf][c], lp);
         }
-      bl[2 * a] = bp;
-      bl[2 * a + 1] = lp;
+      bl[a] = bp;
     }
     row_sum16_n(bl);
 #pragma unroll
-    for (int a = 0; a < R; ++a) {
+    for (int a = 0; a < R; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int c = col(b, e);
-          Bm[a][b][e] = fmaf(-bl[2 * a], sh.kh[buf][c], Bm[a][b][e]);
-          Lm[a][b][e] = fmaf(-bl[2 * a + 1], sh.kh[buf][c], Lm[a][b][e]);
-        }
-    }
+        for (int e = 0; e < 2; ++e) Bm[a][b][e] = fmaf(-bl[a], sh.kh[buf][col(b, e)], Bm[a][b][e]);
   }
-  const int64_t slot = s * P + (P - 1 - p);
   float *dst = lb + slot * 2 * D * D;
 #pragma unroll
   for (int a = 0; a < R; ++a)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      *reinterpret_cast<float2 *>(dst + row(a) * D + col(b, 0)) = make_float2(Lm[a][b][0], Lm[a][b][1]);
+    for (int b = 0; b < NB; ++b)
       *reinterpret_cast<float2 *>(dst + D * D + row(a) * D + col(b, 0)) = make_float2(Bm[a][b][0], Bm[a][b][1]);
-    }
   if (tid < D) nd[slot * D + tid] = ndp;
 }
 
@@ -1168,13 +1171,15 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
     VLA_LAUNCH("k_bw_terminal", (k_bw_terminal<D>), dim3(S), dim3(256), 0, st,
                static_cast<const float *>(ck), io.dA_T, Y, X, pr.T);
   if (bp.P > 1) {
-    // After the replay (or the forward's final pass) the segment-start buffers are free: the
-    // maps go where the forward pass's maps were, the end cotangents of S where its start states
-    // were, the segment sums of dden phi(q) where the normalisers were and the segment R sums
-    // where A was.
-    float *lb = cs.pib, *E = cs.S_seg, *nd = cs.n_seg, *W = cs.A_seg;
+    // After the forward's final pass the segment-start buffers are free: the maps go into the
+    // fp64 penalty buffer (the same bytes as two fp32 d x d matrices per segment), the end
+    // cotangents of S where the start states were, the segment sums of dden phi(q) where the
+    // normalisers were and the segment R sums where A was; the forward's own maps (Pi_p) are
+    // read for the L part of the backward's.
+    float *lb = reinterpret_cast<float *>(base + bp.off_md), *E = cs.S_seg, *nd = cs.n_seg, *W = cs.A_seg;
     VLA_LAUNCH("k_bw_dsmap", (k_bw_dsmap<D, TIn>), dim3(S, P - 1), dim3(BW_NT), 0, st, dout,
-               static_cast<const float *>(rec), lb, nd, pr.T, bp.L, bp.P);
+               static_cast<const float *>(rec), static_cast<const float *>(cs.pib), lb, nd, pr.T,
+               bp.L, bp.P);
     err = launch_affine_prefix(pr, lb, E, bp.P, io.dS_T, nd, io.dn_T, st);
     if (err != hipSuccess) return err;
     VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, dout,

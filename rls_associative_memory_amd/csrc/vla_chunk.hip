@@ -1368,7 +1368,9 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
   if constexpr (sizeof(TIn) == 2) {
     // bf16 inputs: S side on the bf16 matrix cores.
     if (P > 1) {
-      VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, P - 1),
+      // with the backward's records the last segment's map too (the backward reads every
+      // segment's Pi but the first's)
+      VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, rec != nullptr ? P : P - 1),
                  dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alh, rdw, s0w, pbw, oo,
                  S_final, static_cast<const float *>(nullptr), pl.T, pl.L, pl.P,
                  static_cast<float *>(nullptr), static_cast<float *>(nullptr));
@@ -1390,7 +1392,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                  static_cast<float *>(nullptr), static_cast<float *>(nullptr));
   } else {
     if (P > 1) {
-      VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, P - 1, 2),
+      VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, rec != nullptr ? P : P - 1, 2),
                  dim3(SwyCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alw, rdw, s0w, pbw, oo,
                  S_final, pl.T, pl.L, pl.P, static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     }
