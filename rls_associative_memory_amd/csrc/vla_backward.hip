@@ -525,6 +525,17 @@ k_bw_esweep(const TIn *__restrict__ dout, const float *__restrict__ recs,
 // du = -2 R u with R local to the segment (from Rinit, NULL = 0), the segment's R sum to Wbuf
 // slot P - 1 - p when Wbuf is not NULL, and the sum of w . y to trw.
 // ---------------------------------------------------------------------------------------------
+// base[i] with a 32-bit byte offset from a uniform base (the offset goes into the load's
+// register operand, with no 64-bit address arithmetic per element)
+template <typename T>
+__device__ __forceinline__ T &at32(T *base, uint32_t i) {
+  return *reinterpret_cast<T *>(reinterpret_cast<char *>(base) + i * static_cast<uint32_t>(sizeof(T)));
+}
+template <typename T>
+__device__ __forceinline__ const T &at32(const T *base, uint32_t i) {
+  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + i * static_cast<uint32_t>(sizeof(T)));
+}
+
 template <int D>
 struct CgCfg {
   static constexpr int NW = D / 16;      // waves
@@ -578,6 +589,11 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
   const float *ck0 = cks + s * NC * 2 * D * D;
   const int64_t slot = s * P + (P - 1 - p);
   auto ld4 = [](const float *x) { return *reinterpret_cast<const f4_t *>(x); };
+  // The chunk-by-chunk tile jobs go round the four SIMDs (a workgroup's waves sit on SIMD
+  // w % 4), and among the waves of one SIMD in turn, so that every SIMD gets the same share.
+  constexpr int NS = NW < 4 ? NW : 4;
+  const int jsimd = w % NS, jn = (NW - jsimd + NS - 1) / NS;
+  const int job0 = jsimd + NS * (w / NS), jstep = NS * jn;
   // acc + sgn * A B over the feature index for one 16 x 16 tile: A's row is arow (this lane's
   // token row in LDS, read 16 bytes at a time), B a register column tile in the accumulator
   // layout.  The next block's operand is read before this block's products, and nothing moves
@@ -621,7 +637,7 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      Rt[kb][r] = Rinit != nullptr ? Rinit[s * D * D + (16 * kb + 4 * gq + r) * D + f] : 0.f;
+      Rt[kb][r] = Rinit != nullptr ? Rinit[s * D * D + static_cast<uint32_t>((16 * kb + 4 * gq + r) * D + f)] : 0.f;
   if (tid < D) {
     sh.dn[tid] = ndbuf != nullptr ? ndbuf[slot * D + tid] : 0.f;
     sh.n[tid] = n_end[(s * P + p) * D + tid];
@@ -650,14 +666,22 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
     float *dqb = dq + tok0, *dkb = dk + tok0, *dub = du + tok0;
     // column tile of a d x d matrix in the accumulator layout: x[16 kb + 4 gq + r][f], or
     // dg times the identity where x is NULL
+    // (32-bit byte offsets from the uniform base: no 64-bit address arithmetic per element)
     auto ld_tile = [&](const float *x, float dg, f4_t (&t)[KB]) {
+      if (x != nullptr) {
+        const char *xb = reinterpret_cast<const char *>(x);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rw = 16 * kb + 4 * gq + r;
-          t[kb][r] = x != nullptr ? x[rw * D + f] : (rw == f ? dg : 0.f);
-        }
+          for (int r = 0; r < 4; ++r)
+            t[kb][r] = *reinterpret_cast<const float *>(
+                xb + static_cast<uint32_t>(((16 * kb + 4 * gq + r) * D + f) * 4));
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[kb][r] = 16 * kb + 4 * gq + r == f ? dg : 0.f;
+      }
     };
     __syncthreads();  // the previous chunk's readers are done
     // ---- stage the chunk's rows (rows past the chunk are zeros) ----
@@ -667,22 +691,22 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
            ah = f4_zero(), zz = f4_zero(), uu = f4_zero();
       float po = 0.f;
       if (t < m) {
-        const float *rec = rcb + static_cast<uint32_t>(t * REC);
-        const uint32_t o = static_cast<uint32_t>(t * D + c);
-        const float rden = 1.0f / rec[6 * D + 3];
-        const f4_t oo = ld4(rec + 5 * D + c);
-        kh = ld4(rec + c);
-        zz = ld4(rec + D + c);
-        ah = ld4(rec + 2 * D + c);
-        rr = ld4(rec + 3 * D + c);
-        fq = ld4(rec + 4 * D + c);
-        dr = ld4(dvb + o);
+        const uint32_t rb = static_cast<uint32_t>(t * REC), o = static_cast<uint32_t>(t * D + c);
+        const f4_t *rc4 = reinterpret_cast<const f4_t *>(rcb);
+        const float rden = 1.0f / at32(rcb, rb + 6 * D + 3);
+        const f4_t oo = at32(rc4, (rb + 5 * D + c) / 4);
+        kh = at32(rc4, (rb + c) / 4);
+        zz = at32(rc4, (rb + D + c) / 4);
+        ah = at32(rc4, (rb + 2 * D + c) / 4);
+        rr = at32(rc4, (rb + 3 * D + c) / 4);
+        fq = at32(rc4, (rb + 4 * D + c) / 4);
+        dr = at32(reinterpret_cast<const f4_t *>(dvb), o / 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float d = bw_cv(dob[o + j]);
+          const float d = bw_cv(at32(dob, o + j));
           dn[j] = d * rden;
           po = fmaf(d, oo[j], po);
-          uu[j] = bw_cv(ub[o + j]);
+          uu[j] = bw_cv(at32(ub, o + j));
         }
       }
       *reinterpret_cast<f4_t *>(&sh.Rr[t][c]) = rr;
@@ -697,11 +721,11 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
     }
     if (tid < BW_CC) {
       const int t = tid;
-      const float *rec = rcb + static_cast<uint32_t>((t < m ? t : 0) * REC);
-      sh.rd[t] = t < m ? 1.0f / rec[6 * D + 0] : 0.f;
-      sh.yn[t] = t < m ? rec[6 * D + 1] : 0.f;
-      sh.rk[t] = t < m ? rec[6 * D + 2] : 0.f;
-      sh.den[t] = t < m ? rec[6 * D + 3] : 1.f;
+      const uint32_t rb = static_cast<uint32_t>((t < m ? t : 0) * REC) + 6 * D;
+      sh.rd[t] = t < m ? 1.0f / at32(rcb, rb) : 0.f;
+      sh.yn[t] = t < m ? at32(rcb, rb + 1) : 0.f;
+      sh.rk[t] = t < m ? at32(rcb, rb + 2) : 0.f;
+      sh.den[t] = t < m ? at32(rcb, rb + 3) : 1.f;
     }
     f4_t Xt[KB];
     ld_tile(Xc + (s * NX + (c1 - 1) / BW_CC) * D * D, 0.f, Xt);
@@ -714,7 +738,7 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
       sh.dd[tid] = -x / sh.den[tid];
     }
     // ---- M1 = Rr Dn^T, M2 = Rr dR^T (all four tiles) ----
-    for (int job = w; job < 8; job += NW) {
+    for (int job = job0; job < 8; job += jstep) {
       const int mat = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
       const float(*B)[C::LDT] = mat == 0 ? sh.Dn : sh.dR;
       const f4_t acc = mm_rr(&sh.Rr[16 * ti + li][0], &B[16 * tj + li][0], 1.f);
@@ -774,7 +798,7 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
       }
     __syncthreads();
     // ---- M3 = dY Z^T D^{-1} (all four tiles) ----
-    for (int job = w; job < 4; job += NW) {
+    for (int job = job0; job < 4; job += jstep) {
       const int ti = job >> 1, tj = job & 1;
       const f4_t acc = mm_rr(&sh.Fq[16 * ti + li][0], &sh.Zr[16 * tj + li][0], 1.f);
       const float rdj = sh.rd[16 * tj + li];
@@ -813,7 +837,7 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
     // raw k of every token of the chunk at this lane's feature (for n_t and phi'(k))
     float kr[BW_CC];
 #pragma unroll
-    for (int j = 0; j < BW_CC; ++j) kr[j] = bw_cv(kb0[static_cast<uint32_t>((j < m ? j : 0) * D + f)]);
+    for (int j = 0; j < BW_CC; ++j) kr[j] = bw_cv(at32(kb0, static_cast<uint32_t>((j < m ? j : 0) * D + f)));
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
       f4_t ak = mm_rt(Wv[ti], &sh.dR[16 * ti + li][0], Mt, -1.f);
@@ -883,8 +907,8 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
           for (int ww = 0; ww < NW; ++ww) kd += sh.part[1][ww][t];
           const uint32_t o = static_cast<uint32_t>(t * D + f);
           const float dnt = dnf + DN[ti][r];
-          dqb[o] = (dQ[ti][r] + sh.dd[t] * nv[ti][r]) * dphi(bw_cv(qb[o]));
-          dkb[o] = (dK[ti][r] - sh.Kh[t][f] * kd) * sh.rk[t] + dnt * dphi(kv[ti][r]);
+          at32(dqb, o) = (dQ[ti][r] + sh.dd[t] * nv[ti][r]) * dphi(bw_cv(at32(qb, o)));
+          at32(dkb, o) = (dK[ti][r] - sh.Kh[t][f] * kd) * sh.rk[t] + dnt * dphi(kv[ti][r]);
         }
       }
     if (tid == 0) {
@@ -900,7 +924,7 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
     // dn carried to the previous chunk: lanes gq = 0 hold token 0's sum
     const float dn_prev = dnf + DN[0][0];
     // ---- M1 <- U Y^T, M2 <- U W^T (all four tiles) ----
-    for (int job = w; job < 8; job += NW) {
+    for (int job = job0; job < 8; job += jstep) {
       const int mat = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
       const float ys = mat == 0 ? sh.yn[16 * tj + li] : 1.f;
       const float(*B)[C::LDT] = mat == 0 ? sh.Ah : sh.Rr;
@@ -934,7 +958,7 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * ti + 4 * gq + r;
-        if (t < m) dub[static_cast<uint32_t>(t * D + f)] = -2.0f * a1[r] - a2[r];
+        if (t < m) at32(dub, static_cast<uint32_t>(t * D + f)) = -2.0f * a1[r] - a2[r];
       }
     }
     // ---- R += (W^T Y + Y^T W) / 2 ----
