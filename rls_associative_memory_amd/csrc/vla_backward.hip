@@ -1004,6 +1004,498 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
 }
 
 // ---------------------------------------------------------------------------------------------
+// k_bw_cgradb: k_bw_cgrad for bf16 inputs (d <= 96) with every product on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16), the fp32 operands as two bf16 terms (about 16 significant bits,
+// the accuracy the chunked forward's records carry for bf16 inputs; u is exact in one term).
+// The token rows are staged as their two terms; the chunk-by-chunk matrices are stored as two
+// terms too, already masked to the triangle each product takes (M1u = triu0(Rr Dn^T) and
+// M2u = triu1(Rr dR^T) for dAhat and, with the state before the chunk, for dPhi(q) and dKhat;
+// M1l, M2l the other triangles for the state after it).  W is staged as W' = diag(||y||) W, so
+// that the products with Y = diag(||y||) Ahat take Ahat itself:
+//   dU = -2 U R - triu0(U Ahat^T) W' - triu0(U W'^T) Ahat,   R += (W'^T Ahat + Ahat^T W') / 2.
+// Operands over tokens are read with the transposing load (ds_read_b64_tr_b16).  Same inputs,
+// outputs and buffers as k_bw_cgrad.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+struct CbCfg {
+  static constexpr int NW = D / 16;
+  static constexpr int NT = NW * kWave;
+  static constexpr int KB = D / 16;
+  static constexpr int LDB = D + 8;       // bf16 stride of token rows
+  static constexpr int LDM = BW_CC + 8;   // bf16 stride of the chunk-by-chunk matrices
+  static constexpr int G4 = D / 4;
+  static constexpr int TS = BW_CC * LDB;  // term stride of a token matrix
+  static constexpr int MS = BW_CC * LDM;  // term stride of a chunk-by-chunk matrix
+};
+
+template <int D>
+struct CbShared {
+  using C = CbCfg<D>;
+  uint16_t Rr[2][BW_CC][C::LDB];  // residuals r; W' once dAhat is formed
+  uint16_t Dn[2][BW_CC][C::LDB];  // dnum
+  uint16_t dR[2][BW_CC][C::LDB];  // dr
+  uint16_t Fq[2][BW_CC][C::LDB];  // phi(q); dY once dAhat is formed
+  uint16_t Kh[2][BW_CC][C::LDB];  // khat
+  uint16_t Ah[2][BW_CC][C::LDB];  // ahat
+  uint16_t Zr[2][BW_CC][C::LDB];  // z
+  uint16_t Ur[BW_CC][C::LDB];     // u (exact)
+  uint16_t M1u[2][BW_CC][C::LDM], M1l[2][BW_CC][C::LDM];  // U Ahat^T, U W'^T later (in M1u, M2u)
+  uint16_t M2u[2][BW_CC][C::LDM], M2l[2][BW_CC][C::LDM];
+  uint16_t M3[2][BW_CC][C::LDM];
+  float rd[BW_CC], yn[BW_CC], rk[BW_CC], den[BW_CC], dd[BW_CC];
+  float dpo[BW_CC][C::G4];
+  float part[3][C::NW][BW_CC];
+  float dn[D], n[D];
+};
+
+// two terms of a token-major (or chunk-by-chunk) matrix read over its rows r0.. and r1.. at
+// column c0 + li, as an operand over the row index
+__device__ __forceinline__ Split2 ld2_tr(const uint16_t *m, int ts, int ld, int r0, int r1, int c0, int li) {
+  return Split2{ld_tr4x2(m, ld, r0, r1, c0, li), ld_tr4x2(m + ts, ld, r0, r1, c0, li)};
+}
+
+template <int D>
+__global__ void __launch_bounds__(CbCfg<D>::NT)
+k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ u,
+            const bf16_t *__restrict__ dout, const float *__restrict__ recs,
+            const float *__restrict__ cks, const float *__restrict__ n_end,
+            const float *__restrict__ Xc, const float *__restrict__ dv,
+            const float *__restrict__ ndbuf, const float *__restrict__ Rinit,
+            float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ du,
+            float *__restrict__ Wbuf, double *__restrict__ trw, int64_t T, int64_t L, int64_t P,
+            float lambda0) {
+  using C = CbCfg<D>;
+  constexpr int NW = C::NW, KB = C::KB, NT = C::NT, G4 = C::G4, REC = BwRec<D>::F;
+  constexpr int TS = C::TS, MS = C::MS, LDB = C::LDB, LDM = C::LDM, KS = KB / 2;
+  static_assert(KB % 2 == 0, "feature blocks go in pairs");
+  __shared__ __attribute__((aligned(16))) CbShared<D> sh;
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int64_t NC = (T + BW_CK - 1) / BW_CK, NX = (T + BW_CC - 1) / BW_CC;
+  const float *rec0 = recs + s * T * REC;
+  const float *ck0 = cks + s * NC * 2 * D * D;
+  const int64_t slot = s * P + (P - 1 - p);
+  constexpr int NS = NW < 4 ? NW : 4;  // tile jobs round the SIMDs, as in k_bw_cgrad
+  const int jsimd = w % NS, jn = (NW - jsimd + NS - 1) / NS;
+  const int job0 = jsimd + NS * (w / NS), jstep = NS * jn;
+  auto val2 = [](const uint16_t *x, int ts) { return bf_val(x[0]) + bf_val(x[ts]); };
+  auto put2 = [](uint16_t *x, int ts, float v) {
+    uint16_t t2[2];
+    split_n<2>(v, t2);
+    x[0] = t2[0];
+    x[ts] = t2[1];
+  };
+  // a column tile in the accumulator layout as two-term operands over its rows, blocks of 32
+  auto split_tile = [](const f4_t (&t)[KB], Split2 (&o)[KS]) {
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const float x[8] = {t[2 * s2][0], t[2 * s2][1], t[2 * s2][2], t[2 * s2][3],
+                          t[2 * s2 + 1][0], t[2 * s2 + 1][1], t[2 * s2 + 1][2], t[2 * s2 + 1][3]};
+      o[s2] = split2(x);
+    }
+  };
+
+  f4_t Rt[KB];
+  {
+    const int gq = (threadIdx.x & 63) >> 4, f = 16 * w + (threadIdx.x & 15);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Rt[kb][r] = Rinit != nullptr ? Rinit[s * D * D + static_cast<uint32_t>((16 * kb + 4 * gq + r) * D + f)] : 0.f;
+  }
+  if (threadIdx.x < D) {
+    sh.dn[threadIdx.x] = ndbuf != nullptr ? ndbuf[slot * D + threadIdx.x] : 0.f;
+    sh.n[threadIdx.x] = n_end[(s * P + p) * D + threadIdx.x];
+  }
+  double trace = 0.0;
+
+  for (int64_t c1 = te; c1 > tb;) {
+    const int64_t c0 = std::max<int64_t>(tb, ((c1 - 1) / BW_CC) * BW_CC);
+    const int m = static_cast<int>(c1 - c0);
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, li = lane & 15, gq = lane >> 4, f = 16 * w + li;
+    const bool bef = (c0 % BW_CK) == 0;
+    const bool init = bef && c0 == 0;
+    const float *ck = ck0 + (bef ? (init ? 0 : (c0 - 1) / BW_CK) : (c1 - 1) / BW_CK) * 2 * D * D;
+    const int64_t tok0 = (s * T + c0) * D;
+    const float *rcb = rec0 + c0 * REC;
+    const bf16_t *qb = q + tok0, *kb0 = k + tok0, *ub = u + tok0, *dob = dout + tok0;
+    const float *dvb = dv + tok0;
+    float *dqb = dq + tok0, *dkb = dk + tok0, *dub = du + tok0;
+    auto ld_tile = [&](const float *x, float dg, f4_t (&t)[KB]) {
+      if (x != nullptr) {
+        const char *xb = reinterpret_cast<const char *>(x);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            t[kb][r] = *reinterpret_cast<const float *>(
+                xb + static_cast<uint32_t>(((16 * kb + 4 * gq + r) * D + f) * 4));
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) t[kb][r] = 16 * kb + 4 * gq + r == f ? dg : 0.f;
+      }
+    };
+    __syncthreads();  // the previous chunk's readers are done
+    // ---- stage the chunk's rows as two terms (rows past the chunk are zeros) ----
+    for (int e = tid; e < BW_CC * G4; e += NT) {
+      const int t = e / G4, c = 4 * (e % G4);
+      f4_t rr = f4_zero(), dn = f4_zero(), dr = f4_zero(), fq = f4_zero(), kh = f4_zero(),
+           ah = f4_zero(), zz = f4_zero();
+      uint2 uu = make_uint2(0u, 0u);
+      float po = 0.f;
+      if (t < m) {
+        const uint32_t rb = static_cast<uint32_t>(t * REC), o = static_cast<uint32_t>(t * D + c);
+        const f4_t *rc4 = reinterpret_cast<const f4_t *>(rcb);
+        const float rden = 1.0f / at32(rcb, rb + 6 * D + 3);
+        const f4_t oo = at32(rc4, (rb + 5 * D + c) / 4);
+        kh = at32(rc4, (rb + c) / 4);
+        zz = at32(rc4, (rb + D + c) / 4);
+        ah = at32(rc4, (rb + 2 * D + c) / 4);
+        rr = at32(rc4, (rb + 3 * D + c) / 4);
+        fq = at32(rc4, (rb + 4 * D + c) / 4);
+        dr = at32(reinterpret_cast<const f4_t *>(dvb), o / 4);
+        const uint2 dw = at32(reinterpret_cast<const uint2 *>(dob), o / 4);
+        uu = at32(reinterpret_cast<const uint2 *>(ub), o / 4);
+        const float dd4[4] = {pk_lo_val(dw.x), pk_hi_val(dw.x), pk_lo_val(dw.y), pk_hi_val(dw.y)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dn[j] = dd4[j] * rden;
+          po = fmaf(dd4[j], oo[j], po);
+        }
+      }
+      auto stage2 = [&](uint16_t (*X)[BW_CC][LDB], const f4_t &v) {
+        uint32_t a[2], b[2];
+        split_pk<2>(v[0], v[1], a);
+        split_pk<2>(v[2], v[3], b);
+        *reinterpret_cast<uint2 *>(&X[0][t][c]) = make_uint2(a[0], b[0]);
+        *reinterpret_cast<uint2 *>(&X[1][t][c]) = make_uint2(a[1], b[1]);
+      };
+      stage2(sh.Rr, rr);
+      stage2(sh.Dn, dn);
+      stage2(sh.dR, dr);
+      stage2(sh.Fq, fq);
+      stage2(sh.Kh, kh);
+      stage2(sh.Ah, ah);
+      stage2(sh.Zr, zz);
+      *reinterpret_cast<uint2 *>(&sh.Ur[t][c]) = uu;
+      sh.dpo[t][c / 4] = po;
+    }
+    if (tid < BW_CC) {
+      const int t = tid;
+      const uint32_t rb = static_cast<uint32_t>((t < m ? t : 0) * REC) + 6 * D;
+      sh.rd[t] = t < m ? 1.0f / at32(rcb, rb) : 0.f;
+      sh.yn[t] = t < m ? at32(rcb, rb + 1) : 0.f;
+      sh.rk[t] = t < m ? at32(rcb, rb + 2) : 0.f;
+      sh.den[t] = t < m ? at32(rcb, rb + 3) : 1.f;
+    }
+    Split2 Bs[KS];  // the B-operand tile of the current products
+    {
+      f4_t Xt[KB];
+      ld_tile(Xc + (s * NX + (c1 - 1) / BW_CC) * D * D, 0.f, Xt);
+      split_tile(Xt, Bs);
+    }
+    __syncthreads();
+    if (tid < BW_CC) {
+      float x = 0.f;
+#pragma unroll
+      for (int g = 0; g < G4; ++g) x += sh.dpo[tid][g];
+      sh.dd[tid] = -x / sh.den[tid];
+    }
+    // ---- M1 = Rr Dn^T, M2 = Rr dR^T, stored masked: u = the upper part (with the diagonal
+    // for M1, without for M2), l = the rest ----
+    for (int job = job0; job < 8; job += jstep) {
+      const int mat = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
+      const uint16_t *bsrc = mat == 0 ? &sh.Dn[0][16 * tj + li][0] : &sh.dR[0][16 * tj + li][0];
+      const uint16_t *asrc = &sh.Rr[0][16 * ti + li][0];
+      f4_t acc = f4_zero();
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        acc = mm2_ss(ld2_4x2(asrc + 32 * s2 + 4 * gq, asrc + 32 * s2 + 16 + 4 * gq, TS),
+                     ld2_4x2(bsrc + 32 * s2 + 4 * gq, bsrc + 32 * s2 + 16 + 4 * gq, TS), acc);
+      uint16_t(*Mu)[BW_CC][LDM] = mat == 0 ? sh.M1u : sh.M2u;
+      uint16_t(*Ml)[BW_CC][LDM] = mat == 0 ? sh.M1l : sh.M2l;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + 4 * gq + r, j = 16 * tj + li;
+        const bool up = mat == 0 ? j >= i : j > i;
+        put2(&Mu[0][i][j], MS, up ? acc[r] : 0.f);
+        put2(&Ml[0][i][j], MS, up ? 0.f : acc[r]);
+      }
+    }
+    __syncthreads();
+    // ---- dAhat = Rr X + M1u Phi(q) - M2u Khat;  dN_t = sum_{j >= t} dden_j phi(q_j) ----
+    f4_t dA[2], DN[2];
+    {
+      const Split2 bq = ld2_tr(&sh.Fq[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
+      const Split2 bk = ld2_tr(&sh.Kh[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const int tr = 16 * ti + li;
+        const uint16_t *ar = &sh.Rr[0][tr][0];
+        f4_t acc = f4_zero(), neg = f4_zero(), dacc = f4_zero();
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2)
+          acc = mm2_ss(ld2_4x2(ar + 32 * s2 + 4 * gq, ar + 32 * s2 + 16 + 4 * gq, TS), Bs[s2], acc);
+        acc = mm2_ss(ld2_4x2(&sh.M1u[0][tr][4 * gq], &sh.M1u[0][tr][16 + 4 * gq], MS), bq, acc);
+        neg = mm2_ss(ld2_4x2(&sh.M2u[0][tr][4 * gq], &sh.M2u[0][tr][16 + 4 * gq], MS), bk, neg);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = e < 4 ? 4 * gq + e : 16 + 4 * gq + (e - 4);
+          x[e] = j >= tr ? sh.dd[j] : 0.f;
+        }
+        dacc = mm2_ss(split2(x), bq, dacc);
+        dA[ti] = acc - neg;
+        DN[ti] = dacc;
+      }
+    }
+    {
+      float x[8];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[4 * ti + r] = dA[ti][r] * val2(&sh.Ah[0][16 * ti + 4 * gq + r][f], TS);
+      row_sum16_n(x);
+      if (li == 0)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sh.part[0][w][16 * ti + 4 * gq + r] = x[4 * ti + r];
+    }
+    {
+      f4_t At[KB];
+      ld_tile(init ? nullptr : ck + D * D, 1.0f / lambda0, At);
+      split_tile(At, Bs);
+    }
+    __syncthreads();
+    // dY over the phi(q) rows (each wave its own columns; the reads of phi(q) and of the partial
+    // sums are behind the barrier)
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * gq + r;
+        float ad = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) ad += sh.part[0][ww][t];
+        const float y = sh.yn[t];
+        put2(&sh.Fq[0][t][f], TS, y > 0.f ? (dA[ti][r] - val2(&sh.Ah[0][t][f], TS) * ad) / y : 0.f);
+      }
+    __syncthreads();
+    // ---- M3 = dY Z^T D^{-1}, masked: lower with the diagonal (state before the chunk), or
+    // strictly upper (state after it) ----
+    for (int job = job0; job < 4; job += jstep) {
+      const int ti = job >> 1, tj = job & 1;
+      const uint16_t *asrc = &sh.Fq[0][16 * ti + li][0], *bsrc = &sh.Zr[0][16 * tj + li][0];
+      f4_t acc = f4_zero();
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        acc = mm2_ss(ld2_4x2(asrc + 32 * s2 + 4 * gq, asrc + 32 * s2 + 16 + 4 * gq, TS),
+                     ld2_4x2(bsrc + 32 * s2 + 4 * gq, bsrc + 32 * s2 + 16 + 4 * gq, TS), acc);
+      const int j = 16 * tj + li;
+      const float rdj = sh.rd[j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + 4 * gq + r;
+        put2(&sh.M3[0][i][j], MS, (bef ? j <= i : j > i) ? acc[r] * rdj : 0.f);
+      }
+    }
+    __syncthreads();
+    // ---- W = dY A -/+ M3 Z;  W' = diag(||y||) W over the residual rows ----
+    f4_t Wv[2];
+    {
+      const Split2 bz = ld2_tr(&sh.Zr[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const int tr = 16 * ti + li;
+        const uint16_t *ar = &sh.Fq[0][tr][0];
+        f4_t acc = f4_zero(), m3 = f4_zero();
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2)
+          acc = mm2_ss(ld2_4x2(ar + 32 * s2 + 4 * gq, ar + 32 * s2 + 16 + 4 * gq, TS), Bs[s2], acc);
+        m3 = mm2_ss(ld2_4x2(&sh.M3[0][tr][4 * gq], &sh.M3[0][tr][16 + 4 * gq], MS), bz, m3);
+        Wv[ti] = bef ? acc - m3 : acc + m3;
+      }
+    }
+    {
+      f4_t St[KB];
+      ld_tile(init ? nullptr : ck, 0.f, St);
+      split_tile(St, Bs);
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * gq + r;
+        put2(&sh.Rr[0][t][f], TS, sh.yn[t] * Wv[ti][r]);
+      }
+    // ---- dKhat = W - dR S -/+ (M2 part)^T Ahat;  dPhi(q) = Dn S +/- (M1 part)^T Ahat ----
+    f4_t dK[2], dQ[2];
+    float kr[BW_CC];
+#pragma unroll
+    for (int j = 0; j < BW_CC; ++j) kr[j] = bw_cv(at32(kb0, static_cast<uint32_t>((j < m ? j : 0) * D + f)));
+    {
+      const Split2 ba = ld2_tr(&sh.Ah[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
+      const uint16_t *m1 = bef ? &sh.M1u[0][0][0] : &sh.M1l[0][0][0];
+      const uint16_t *m2 = bef ? &sh.M2u[0][0][0] : &sh.M2l[0][0][0];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const uint16_t *a1 = &sh.dR[0][16 * ti + li][0], *a2 = &sh.Dn[0][16 * ti + li][0];
+        f4_t ak = f4_zero(), aq = f4_zero();
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          ak = mm2_ss(ld2_4x2(a1 + 32 * s2 + 4 * gq, a1 + 32 * s2 + 16 + 4 * gq, TS), Bs[s2], ak);
+          aq = mm2_ss(ld2_4x2(a2 + 32 * s2 + 4 * gq, a2 + 32 * s2 + 16 + 4 * gq, TS), Bs[s2], aq);
+        }
+        // (M^T)[t][i] = M[i][t]: the chunk matrix read over its rows at column t
+        const f4_t t2 = mm2_ss(ld2_tr(m2, MS, LDM, 4 * gq, 16 + 4 * gq, 16 * ti, li), ba, f4_zero());
+        const f4_t t1 = mm2_ss(ld2_tr(m1, MS, LDM, 4 * gq, 16 + 4 * gq, 16 * ti, li), ba, f4_zero());
+        // before: S_{t-1} = S0 + sum_{i < t}, S_t = S0 + sum_{i <= t};
+        // after:  S_{t-1} = Se - sum_{i >= t}, S_t = Se - sum_{i > t}
+        dK[ti] = bef ? Wv[ti] - ak - t2 : Wv[ti] - ak + t2;
+        dQ[ti] = bef ? aq + t1 : aq - t1;
+      }
+    }
+    {
+      float x[16];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * ti + 4 * gq + r;
+          x[4 * ti + r] = dK[ti][r] * val2(&sh.Kh[0][t][f], TS);
+          x[8 + 4 * ti + r] = Wv[ti][r] * val2(&sh.Ah[0][t][f], TS);
+        }
+      row_sum16_n(x);
+      if (li == 0)
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sh.part[1][w][16 * ti + 4 * gq + r] = x[4 * ti + r];
+            sh.part[2][w][16 * ti + 4 * gq + r] = x[8 + 4 * ti + r];
+          }
+    }
+    {
+      f4_t Rc[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) Rc[kb] = Rt[kb];
+      split_tile(Rc, Bs);  // R before this chunk's terms, for du
+    }
+    __syncthreads();
+    // ---- dq, dk ----
+    const float dnf = sh.dn[f];
+    float nv[2][4], kv[2][4], n_prev = sh.n[f];
+#pragma unroll
+    for (int j = BW_CC - 1; j >= 0; --j) {
+      if (((j >> 2) & 3) == gq) {
+        nv[j >> 4][j & 3] = n_prev;
+        kv[j >> 4][j & 3] = kr[j];
+      }
+      if (j < m) n_prev -= phi(kr[j]);
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * gq + r;
+        if (t < m) {
+          float kd = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww) kd += sh.part[1][ww][t];
+          const uint32_t o = static_cast<uint32_t>(t * D + f);
+          const float dnt = dnf + DN[ti][r];
+          at32(dqb, o) = (dQ[ti][r] + sh.dd[t] * nv[ti][r]) * dphi(bw_cv(at32(qb, o)));
+          at32(dkb, o) = (dK[ti][r] - val2(&sh.Kh[0][t][f], TS) * kd) * sh.rk[t] + dnt * dphi(kv[ti][r]);
+        }
+      }
+    if (tid == 0) {
+      double tr = 0.0;
+      for (int t = 0; t < m; ++t) {
+        float wy = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) wy += sh.part[2][ww][t];
+        tr += static_cast<double>(wy) * sh.yn[t];
+      }
+      trace += tr;
+    }
+    const float dn_prev = dnf + DN[0][0];
+    // ---- M1u <- U Ahat^T, M2u <- U W'^T (upper with the diagonal) ----
+    for (int job = job0; job < 8; job += jstep) {
+      const int mat = job >> 2, ti = (job >> 1) & 1, tj = job & 1;
+      const uint16_t *asrc = &sh.Ur[16 * ti + li][0];
+      const uint16_t *bsrc = mat == 0 ? &sh.Ah[0][16 * tj + li][0] : &sh.Rr[0][16 * tj + li][0];
+      f4_t acc = f4_zero();
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        acc = mm2_xs(ld_bf4x2(asrc + 32 * s2 + 4 * gq, asrc + 32 * s2 + 16 + 4 * gq),
+                     ld2_4x2(bsrc + 32 * s2 + 4 * gq, bsrc + 32 * s2 + 16 + 4 * gq, TS), acc);
+      uint16_t(*M)[BW_CC][LDM] = mat == 0 ? sh.M1u : sh.M2u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + 4 * gq + r, j = 16 * tj + li;
+        put2(&M[0][i][j], MS, j >= i ? acc[r] : 0.f);
+      }
+    }
+    __syncthreads();
+    if (gq == 0) {
+      sh.dn[f] = dn_prev;
+      sh.n[f] = n_prev;
+    }
+    // ---- du = -2 U R - M1u W' - M2u Ahat ----
+    {
+      const Split2 bw = ld2_tr(&sh.Rr[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
+      const Split2 ba = ld2_tr(&sh.Ah[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const int tr = 16 * ti + li;
+        const uint16_t *ar = &sh.Ur[tr][0];
+        f4_t a1 = f4_zero(), a2 = f4_zero();
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2)
+          a1 = mm2_xs(ld_bf4x2(ar + 32 * s2 + 4 * gq, ar + 32 * s2 + 16 + 4 * gq), Bs[s2], a1);
+        a2 = mm2_ss(ld2_4x2(&sh.M1u[0][tr][4 * gq], &sh.M1u[0][tr][16 + 4 * gq], MS), bw, a2);
+        a2 = mm2_ss(ld2_4x2(&sh.M2u[0][tr][4 * gq], &sh.M2u[0][tr][16 + 4 * gq], MS), ba, a2);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * ti + 4 * gq + r;
+          if (t < m) at32(dub, static_cast<uint32_t>(t * D + f)) = -2.0f * a1[r] - a2[r];
+        }
+      }
+      // ---- R += (W'^T Ahat + Ahat^T W') / 2 ----
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const Split2 aw = ld2_tr(&sh.Rr[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * kb, li);
+        const Split2 aa = ld2_tr(&sh.Ah[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * kb, li);
+        f4_t x = mm2_ss(aw, ba, f4_zero());
+        x = mm2_ss(aa, bw, x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Rt[kb][r] = fmaf(0.5f, x[r], Rt[kb][r]);
+      }
+    }
+    c1 = c0;
+  }
+  const int gq = (threadIdx.x & 63) >> 4, f = 16 * w + (threadIdx.x & 15);
+  if (Wbuf != nullptr) {
+    float *dst = Wbuf + slot * D * D;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rw = 16 * kb + 4 * gq + r;
+        dst[rw * D + f] = Rt[kb][r] - (Rinit != nullptr ? Rinit[s * D * D + rw * D + f] : 0.f);
+      }
+  }
+  if (threadIdx.x == 0) trw[s * P + p] = trace;
+}
+
+// ---------------------------------------------------------------------------------------------
 // k_bw_terminal: X = A_T sym(dA_T) A_T per stream (A_T = the state after the last token, from
 // the replay's checkpoint), through the scratch matrix Y = sym(dA_T) A_T.
 // ---------------------------------------------------------------------------------------------
@@ -1154,6 +1646,24 @@ BwPlan make_bw_plan(const Problem &p, int chunk) {
   return b;
 }
 
+// The chunked gradient pass: on the bf16 matrix cores (two-term operands) for bf16 inputs at
+// d <= 96, on the fp32 matrix cores otherwise (fp32 inputs, and d = 128, whose two-term LDS
+// staging would not fit).
+template <int D, typename TIn>
+void launch_cgrad(const TIn *q, const TIn *k, const TIn *u, const TIn *dout, const float *rec,
+                  const float *ck, const float *nend, const float *xc, const float *dv,
+                  const float *ndbuf, const float *Rinit, float *dq, float *dk, float *du,
+                  float *Wbuf, double *trw, const Problem &pr, const BwPlan &bp, hipStream_t st) {
+  const unsigned S = static_cast<unsigned>(pr.streams), P = static_cast<unsigned>(bp.P);
+  if constexpr (sizeof(TIn) == 2 && D <= 96)
+    VLA_LAUNCH("k_bw_cgrad", (k_bw_cgradb<D>), dim3(S, P), dim3(CbCfg<D>::NT), 0, st, q, k, u, dout,
+               rec, ck, nend, xc, dv, ndbuf, Rinit, dq, dk, du, Wbuf, trw, pr.T, bp.L, bp.P, pr.lambda0);
+  else
+    VLA_LAUNCH("k_bw_cgrad", (k_bw_cgrad<D, TIn>), dim3(S, P), dim3(CgCfg<D>::NT), 0, st, q, k, u,
+               dout, rec, ck, nend, xc, dv, ndbuf, Rinit, dq, dk, du, Wbuf, trw, pr.T, bp.L, bp.P,
+               pr.lambda0);
+}
+
 template <int D, typename TIn>
 hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void *ws, hipStream_t st) {
   const BwPlan bp = make_bw_plan(pr, chunk);
@@ -1209,12 +1719,8 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
     VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, dout,
                static_cast<const float *>(rec), static_cast<const float *>(E), io.dv, xc, pr.T,
                bp.L, bp.P);
-    VLA_LAUNCH("k_bw_cgrad", (k_bw_cgrad<D, TIn>), dim3(S, P), dim3(CgCfg<D>::NT), 0, st, q, k, u,
-               dout, static_cast<const float *>(rec), static_cast<const float *>(ck),
-               static_cast<const float *>(nend), static_cast<const float *>(xc),
-               static_cast<const float *>(io.dv), static_cast<const float *>(nd),
-               static_cast<const float *>(nullptr), io.dq, io.dk, io.du, W, trw, pr.T, bp.L, bp.P,
-               pr.lambda0);
+    launch_cgrad<D, TIn>(q, k, u, dout, rec, ck, nend, xc, io.dv, nd, nullptr, io.dq, io.dk, io.du,
+                         W, trw, pr, bp, st);
     err = launch_matrix_prefix(pr, W, bp.P, X, st);
     if (err != hipSuccess) return err;
     const unsigned nz = static_cast<unsigned>((bp.L + 255) / 256);
@@ -1223,11 +1729,8 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
   } else {
     VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, 1), dim3(BW_NT), 0, st, dout,
                static_cast<const float *>(rec), io.dS_T, io.dv, xc, pr.T, bp.L, bp.P);
-    VLA_LAUNCH("k_bw_cgrad", (k_bw_cgrad<D, TIn>), dim3(S, 1), dim3(CgCfg<D>::NT), 0, st, q, k, u,
-               dout, static_cast<const float *>(rec), static_cast<const float *>(ck),
-               static_cast<const float *>(nend), static_cast<const float *>(xc),
-               static_cast<const float *>(io.dv), io.dn_T, static_cast<const float *>(X), io.dq,
-               io.dk, io.du, static_cast<float *>(nullptr), trw, pr.T, bp.L, bp.P, pr.lambda0);
+    launch_cgrad<D, TIn>(q, k, u, dout, rec, ck, nend, xc, io.dv, io.dn_T, X, io.dq, io.dk, io.du,
+                         nullptr, trw, pr, bp, st);
   }
   if (io.dlambda0 != nullptr)
     VLA_LAUNCH("k_bw_lambda", (k_bw_lambda<D>), dim3(S), dim3(64), 0, st,
