@@ -1046,6 +1046,7 @@ struct CbShared {
   float dpo[BW_CC][C::G4];
   float part[3][C::NW][BW_CC];
   float dn[D], n[D];
+  float Pk[BW_CC][D + 4];         // phi(k), formed once at staging
 };
 
 // two terms of a token-major (or chunk-by-chunk) matrix read over its rows r0.. and r1.. at
@@ -1079,6 +1080,8 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
   constexpr int NS = NW < 4 ? NW : 4;  // tile jobs round the SIMDs, as in k_bw_cgrad
   const int jsimd = w % NS, jn = (NW - jsimd + NS - 1) / NS;
   const int job0 = jsimd + NS * (w / NS), jstep = NS * jn;
+  // per-token scalar work goes to a wave that has its SIMD to itself (wave 3 of six)
+  constexpr int LW = NW >= 4 ? 3 : NW - 1;
   auto val2 = [](const uint16_t *x, int ts) { return bf_val(x[0]) + bf_val(x[ts]); };
   auto put2 = [](uint16_t *x, int ts, float v) {
     uint16_t t2[2];
@@ -1109,7 +1112,7 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
     sh.dn[threadIdx.x] = ndbuf != nullptr ? ndbuf[slot * D + threadIdx.x] : 0.f;
     sh.n[threadIdx.x] = n_end[(s * P + p) * D + threadIdx.x];
   }
-  double trace = 0.0;
+  double trace = 0.0;  // wave LW, lane t < BW_CC: the sum of w . y over the tokens at chunk slot t
 
   for (int64_t c1 = te; c1 > tb;) {
     const int64_t c0 = std::max<int64_t>(tb, ((c1 - 1) / BW_CC) * BW_CC);
@@ -1122,7 +1125,7 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
     const float *ck = ck0 + (bef ? (init ? 0 : (c0 - 1) / BW_CK) : (c1 - 1) / BW_CK) * 2 * D * D;
     const int64_t tok0 = (s * T + c0) * D;
     const float *rcb = rec0 + c0 * REC;
-    const bf16_t *qb = q + tok0, *kb0 = k + tok0, *ub = u + tok0, *dob = dout + tok0;
+    const bf16_t *kb0 = k + tok0, *ub = u + tok0, *dob = dout + tok0;
     const float *dvb = dv + tok0;
     float *dqb = dq + tok0, *dkb = dk + tok0, *dub = du + tok0;
     auto ld_tile = [&](const float *x, float dg, f4_t (&t)[KB]) {
@@ -1148,6 +1151,7 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
       f4_t rr = f4_zero(), dn = f4_zero(), dr = f4_zero(), fq = f4_zero(), kh = f4_zero(),
            ah = f4_zero(), zz = f4_zero();
       uint2 uu = make_uint2(0u, 0u);
+      f4_t pk = f4_zero();
       float po = 0.f;
       if (t < m) {
         const uint32_t rb = static_cast<uint32_t>(t * REC), o = static_cast<uint32_t>(t * D + c);
@@ -1162,6 +1166,8 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
         dr = at32(reinterpret_cast<const f4_t *>(dvb), o / 4);
         const uint2 dw = at32(reinterpret_cast<const uint2 *>(dob), o / 4);
         uu = at32(reinterpret_cast<const uint2 *>(ub), o / 4);
+        const uint2 kw = at32(reinterpret_cast<const uint2 *>(kb0), o / 4);
+        pk = f4_t{phi(pk_lo_val(kw.x)), phi(pk_hi_val(kw.x)), phi(pk_lo_val(kw.y)), phi(pk_hi_val(kw.y))};
         const float dd4[4] = {pk_lo_val(dw.x), pk_hi_val(dw.x), pk_lo_val(dw.y), pk_hi_val(dw.y)};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1184,10 +1190,11 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
       stage2(sh.Ah, ah);
       stage2(sh.Zr, zz);
       *reinterpret_cast<uint2 *>(&sh.Ur[t][c]) = uu;
+      *reinterpret_cast<f4_t *>(&sh.Pk[t][c]) = pk;
       sh.dpo[t][c / 4] = po;
     }
-    if (tid < BW_CC) {
-      const int t = tid;
+    if (w == LW && lane < BW_CC) {
+      const int t = lane;
       const uint32_t rb = static_cast<uint32_t>((t < m ? t : 0) * REC) + 6 * D;
       sh.rd[t] = t < m ? 1.0f / at32(rcb, rb) : 0.f;
       sh.yn[t] = t < m ? at32(rcb, rb + 1) : 0.f;
@@ -1201,11 +1208,11 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
       split_tile(Xt, Bs);
     }
     __syncthreads();
-    if (tid < BW_CC) {
+    if (w == LW && lane < BW_CC) {
       float x = 0.f;
 #pragma unroll
-      for (int g = 0; g < G4; ++g) x += sh.dpo[tid][g];
-      sh.dd[tid] = -x / sh.den[tid];
+      for (int g = 0; g < G4; ++g) x += sh.dpo[lane][g];
+      sh.dd[lane] = -x / sh.den[lane];
     }
     // ---- M1 = Rr Dn^T, M2 = Rr dR^T, stored masked: u = the upper part (with the diagonal
     // for M1, without for M2), l = the rest ----
@@ -1275,7 +1282,9 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
     }
     __syncthreads();
     // dY over the phi(q) rows (each wave its own columns; the reads of phi(q) and of the partial
-    // sums are behind the barrier)
+    // sums are behind the barrier).  phi'(q) = min(phi(q), 1) at this lane's output positions
+    // is kept first.
+    float dpq[2][4];
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
@@ -1285,6 +1294,7 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) ad += sh.part[0][ww][t];
         const float y = sh.yn[t];
+        dpq[ti][r] = fminf(val2(&sh.Fq[0][t][f], TS), 1.0f);
         put2(&sh.Fq[0][t][f], TS, y > 0.f ? (dA[ti][r] - val2(&sh.Ah[0][t][f], TS) * ad) / y : 0.f);
       }
     __syncthreads();
@@ -1337,9 +1347,6 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
       }
     // ---- dKhat = W - dR S -/+ (M2 part)^T Ahat;  dPhi(q) = Dn S +/- (M1 part)^T Ahat ----
     f4_t dK[2], dQ[2];
-    float kr[BW_CC];
-#pragma unroll
-    for (int j = 0; j < BW_CC; ++j) kr[j] = bw_cv(at32(kb0, static_cast<uint32_t>((j < m ? j : 0) * D + f)));
     {
       const Split2 ba = ld2_tr(&sh.Ah[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
       const uint16_t *m1 = bef ? &sh.M1u[0][0][0] : &sh.M1l[0][0][0];
@@ -1394,11 +1401,12 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
     float nv[2][4], kv[2][4], n_prev = sh.n[f];
 #pragma unroll
     for (int j = BW_CC - 1; j >= 0; --j) {
+      const float pkj = sh.Pk[j][f];  // 0 past the chunk
       if (((j >> 2) & 3) == gq) {
         nv[j >> 4][j & 3] = n_prev;
-        kv[j >> 4][j & 3] = kr[j];
+        kv[j >> 4][j & 3] = fminf(pkj, 1.0f);  // phi'(k) = min(phi(k), 1)
       }
-      if (j < m) n_prev -= phi(kr[j]);
+      n_prev -= pkj;
     }
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
@@ -1411,19 +1419,15 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
           for (int ww = 0; ww < NW; ++ww) kd += sh.part[1][ww][t];
           const uint32_t o = static_cast<uint32_t>(t * D + f);
           const float dnt = dnf + DN[ti][r];
-          at32(dqb, o) = (dQ[ti][r] + sh.dd[t] * nv[ti][r]) * dphi(bw_cv(at32(qb, o)));
-          at32(dkb, o) = (dK[ti][r] - val2(&sh.Kh[0][t][f], TS) * kd) * sh.rk[t] + dnt * dphi(kv[ti][r]);
+          at32(dqb, o) = (dQ[ti][r] + sh.dd[t] * nv[ti][r]) * dpq[ti][r];
+          at32(dkb, o) = (dK[ti][r] - val2(&sh.Kh[0][t][f], TS) * kd) * sh.rk[t] + dnt * kv[ti][r];
         }
       }
-    if (tid == 0) {
-      double tr = 0.0;
-      for (int t = 0; t < m; ++t) {
-        float wy = 0.f;
+    if (w == LW && lane < m) {
+      float wy = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) wy += sh.part[2][ww][t];
-        tr += static_cast<double>(wy) * sh.yn[t];
-      }
-      trace += tr;
+      for (int ww = 0; ww < NW; ++ww) wy += sh.part[2][ww][lane];
+      trace += static_cast<double>(wy) * sh.yn[lane];
     }
     const float dn_prev = dnf + DN[0][0];
     // ---- M1u <- U Ahat^T, M2u <- U W'^T (upper with the diagonal) ----
@@ -1492,7 +1496,11 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
         dst[rw * D + f] = Rt[kb][r] - (Rinit != nullptr ? Rinit[s * D * D + rw * D + f] : 0.f);
       }
   }
-  if (threadIdx.x == 0) trw[s * P + p] = trace;
+  if (w == LW) {  // the 32 slot sums, pairwise in a fixed order
+#pragma unroll
+    for (int off = 1; off < BW_CC; off <<= 1) trace += __shfl_xor(trace, off);
+    if ((threadIdx.x & 63) == 0) trw[s * P + p] = trace;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
