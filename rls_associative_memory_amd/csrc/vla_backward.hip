@@ -1532,68 +1532,71 @@ k_bw_terminal(const float *__restrict__ cks, const float *__restrict__ dA_T,
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_bw_fix: du_t -= 2 R_end u_t over up to 256 tokens of segment p (R_end at Rend slot P - 1 - p,
-// symmetric), 64 tokens at a time.  R_end and the token block sit in LDS; thread (tg, rg) forms
-// tokens 4 tg .. 4 tg + 3 against rows rg + 16 m, 16-byte operands from LDS (16 multiply-adds
-// per pair of reads).
+// k_bw_fix: du_t -= 2 R_end u_t over up to 256 tokens of segment p (R_end at Rend slot P - 1 - p)
+// on the matrix cores: wave w forms features 16 w .. 16 w + 15 of (R_end u_t) for 16 tokens at a
+// time, with R_end's rows 16 w .. as the B operand in registers (B[k][f] = R_end[f][k]) and the
+// token rows of u read straight from memory as the A operand.  bf16 inputs: u exact in one bf16
+// term, R_end in two (v_mfma_f32_16x16x32_bf16); fp32 inputs: fp32 products.
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ float4 bw_ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
-__device__ __forceinline__ float4 bw_ld4(const bf16_t *p) {
-  const uint2 w = *reinterpret_cast<const uint2 *>(p);
-  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
-}
-
 template <int D, typename TIn>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(D / 16 * kWave)
 k_bw_fix(const TIn *__restrict__ u, const float *__restrict__ Rend, float *__restrict__ du,
          int64_t T, int64_t L, int64_t P) {
-  constexpr int RPT = D / 16, LDR = D + 4;
-  __shared__ __attribute__((aligned(16))) float sR[D][LDR];
-  __shared__ __attribute__((aligned(16))) float sU[64][LDR];
+  constexpr int KB = D / 16;
   const int64_t s = blockIdx.x, p = blockIdx.y;
   const int64_t seg_end = std::min<int64_t>(T, p * L + L);
   const int64_t t_beg = p * L + static_cast<int64_t>(blockIdx.z) * 256;
   if (t_beg >= seg_end) return;  // the whole workgroup
-  const int tid = threadIdx.x, tg = tid >> 4, rg = tid & 15;
+  const int nt = static_cast<int>(std::min<int64_t>(256, seg_end - t_beg));
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63, li = lane & 15, gq = lane >> 4, f = 16 * w + li;
   const float *Rs = Rend + (s * P + (P - 1 - p)) * D * D;
-  for (int e = 4 * tid; e < D * D; e += 1024)
-    *reinterpret_cast<float4 *>(&sR[e / D][e % D]) = bw_ld4(Rs + e);
-  for (int blk = 0; blk < 4; ++blk) {
-    const int64_t t0 = t_beg + 64 * blk;
-    if (t0 >= seg_end) break;  // uniform
-    const int nt = static_cast<int>(std::min<int64_t>(64, seg_end - t0));
-    __syncthreads();  // R staged; the previous block's readers are done
-    for (int e = 4 * tid; e < 64 * D; e += 1024) {
-      const int j = e / D, c = e % D;
-      *reinterpret_cast<float4 *>(&sU[j][c]) =
-          j < nt ? bw_ld4(u + (s * T + t0 + j) * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  // Rt[kb][r] = R_end[f][16 kb + 4 gq + r]
+  f4_t Rt[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) Rt[kb] = at32(reinterpret_cast<const f4_t *>(Rs), static_cast<uint32_t>((f * D + 16 * kb + 4 * gq) / 4));
+  const TIn *ub = u + (s * T + t_beg) * D;
+  float *db = du + (s * T + t_beg) * D;
+  if constexpr (sizeof(TIn) == 2) {
+    Split2 Bs[KB / 2];
+#pragma unroll
+    for (int s2 = 0; s2 < KB / 2; ++s2) {
+      const float x[8] = {Rt[2 * s2][0], Rt[2 * s2][1], Rt[2 * s2][2], Rt[2 * s2][3],
+                          Rt[2 * s2 + 1][0], Rt[2 * s2 + 1][1], Rt[2 * s2 + 1][2], Rt[2 * s2 + 1][3]};
+      Bs[s2] = split2(x);
     }
-    __syncthreads();
-    float acc[4][RPT];
+    const uint2 *u2 = reinterpret_cast<const uint2 *>(ub);
+    for (int t0 = 0; t0 < nt; t0 += 16) {
+      const int tr = t0 + li < nt ? t0 + li : 0;  // rows past the block: any row, never stored
+      f4_t acc = f4_zero();
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int s2 = 0; s2 < KB / 2; ++s2) {
+        const uint2 a0 = at32(u2, static_cast<uint32_t>((tr * D + 32 * s2 + 4 * gq) / 4));
+        const uint2 a1 = at32(u2, static_cast<uint32_t>((tr * D + 32 * s2 + 16 + 4 * gq) / 4));
+        acc = mm2_xs(__builtin_bit_cast(bf16x8_t, make_uint4(a0.x, a0.y, a1.x, a1.y)), Bs[s2], acc);
+      }
 #pragma unroll
-      for (int m = 0; m < RPT; ++m) acc[a][m] = 0.f;
-#pragma unroll 2
-    for (int c = 0; c < D; c += 4) {
-      float4 uv[4], rv[RPT];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) uv[a] = *reinterpret_cast<const float4 *>(&sU[4 * tg + a][c]);
-#pragma unroll
-      for (int m = 0; m < RPT; ++m) rv[m] = *reinterpret_cast<const float4 *>(&sR[rg + 16 * m][c]);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int m = 0; m < RPT; ++m)
-          acc[a][m] = fmaf(uv[a].x, rv[m].x, fmaf(uv[a].y, rv[m].y, fmaf(uv[a].z, rv[m].z, fmaf(uv[a].w, rv[m].w, acc[a][m]))));
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * gq + r;
+        if (t < nt) at32(db, static_cast<uint32_t>(t * D + f)) -= 2.0f * acc[r];
+      }
     }
+  } else {
+    const f4_t *u4 = reinterpret_cast<const f4_t *>(ub);
+    for (int t0 = 0; t0 < nt; t0 += 16) {
+      const int tr = t0 + li < nt ? t0 + li : 0;
+      f4_t acc = f4_zero();
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int j = 4 * tg + a;
-      if (j < nt)
+      for (int kb = 0; kb < KB; ++kb) {
+        const f4_t a = at32(u4, static_cast<uint32_t>((tr * D + 16 * kb + 4 * gq) / 4));
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) du[(s * T + t0 + j) * D + rg + 16 * m] -= 2.0f * acc[a][m];
+        for (int r = 0; r < 4; ++r) acc = mfma_f32_16x16x4(a[r], Rt[kb][r], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * gq + r;
+        if (t < nt) at32(db, static_cast<uint32_t>(t * D + f)) -= 2.0f * acc[r];
+      }
     }
   }
 }
@@ -1732,7 +1735,7 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
     err = launch_matrix_prefix(pr, W, bp.P, X, st);
     if (err != hipSuccess) return err;
     const unsigned nz = static_cast<unsigned>((bp.L + 255) / 256);
-    VLA_LAUNCH("k_bw_fix", (k_bw_fix<D, TIn>), dim3(S, P, nz), dim3(256), 0, st, u,
+    VLA_LAUNCH("k_bw_fix", (k_bw_fix<D, TIn>), dim3(S, P, nz), dim3(D / 16 * kWave), 0, st, u,
                static_cast<const float *>(W), io.du, pr.T, bp.L, bp.P);
   } else {
     VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, 1), dim3(BW_NT), 0, st, dout,
