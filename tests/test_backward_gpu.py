@@ -68,7 +68,8 @@ def test_backward_edge_lengths(T):
 # Time-segment parallel backward on shapes that split into several segments (64-token segments
 # for fp32 inputs, 256-token ones for bf16), including a last segment of a single token.
 @pytest.mark.parametrize("d,dt,T", [(64, "f32", 300), (32, "f32", 129), (96, "f32", 257),
-                                    (64, "bf16", 1100), (128, "bf16", 600), (96, "bf16", 513)])
+                                    (64, "bf16", 1100), (128, "bf16", 600), (96, "bf16", 513),
+                                    (32, "bf16", 777)])
 def test_backward_segments_match_oracle(d, dt, T):
     _run(d, dt, T, path="chunk")
 
