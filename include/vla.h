@@ -222,7 +222,7 @@ vla_status_t vla_la_workspace_size(const vla_desc_t *desc, size_t *bytes);
  *             suffix sums.  VLA_PATH_AUTO: CHUNK when that gives at least two segments per
  *             stream (at d = 128 only for at most 128 streams), else SEQ.
  *             VLA_PATH_DECODE: NOT_SUPPORTED.
- *             The workspace holds vla_backward_workspace_size() bytes (per stream T x (6 d + 8)
+ *             The workspace holds vla_backward_workspace_size() bytes (per stream T x (4 d + 8)
  *             floats of per-token vectors, the state at every 64th token and the cotangent of S
  *             at every 32nd token; with time segments
  *             the chunked forward's workspace and an fp64 d x d matrix per segment on top), else

@@ -305,7 +305,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         sh.rd[lane] = __builtin_amdgcn_rcpf(myd0);
         sh.rsd[lane] = rsqrtf(myd0);
         if constexpr (REC)
-          if (lane < m) brs[(c0 + lane) * RF + 6 * D] = myd0;  // delta: the LDL^T pivot
+          if (lane < m) brs[(c0 + lane) * RF + BwRec<D>::SC] = myd0;  // delta: the LDL^T pivot
       } else if (lane < 32) {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4)
@@ -352,7 +352,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         sh.rd[16 + lane] = __builtin_amdgcn_rcpf(myd1);
         sh.rsd[16 + lane] = rsqrtf(myd1);
         if constexpr (REC)
-          if (16 + lane < m) brs[(c0 + 16 + lane) * RF + 6 * D] = myd1;
+          if (16 + lane < m) brs[(c0 + 16 + lane) * RF + BwRec<D>::SC] = myd1;
       } else if (lane >= 32) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sh.G[16 + r][mcol] = y[r];  // L^{-1}_21 | L^{-1}_22
@@ -468,7 +468,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       for (int ct = 0; ct < 2; ++ct) {
         const int c = 16 * ct + li;
         if (c < m)
-          *reinterpret_cast<float4 *>(&brs[(c0 + c) * RF + D + 16 * w + 4 * gq]) =
+          *reinterpret_cast<float4 *>(&brs[(c0 + c) * RF + BwRec<D>::Z + 16 * w + 4 * gq]) =
               make_float4(Zt[ct][0], Zt[ct][1], Zt[ct][2], Zt[ct][3]);
       }
     }
@@ -569,8 +569,8 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         *reinterpret_cast<uint2 *>(row + D) = make_uint2(w01[1], w23[1]);
         if constexpr (REC) {  // ahat in fp32, and ||A_t khat|| = ||Y_t|| / ||k_t||
           float *rr = &brs[(c0 + c) * RF];
-          *reinterpret_cast<float4 *>(&rr[2 * D + 16 * w + 4 * gq]) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-          if (w == 0 && gq == 0) rr[6 * D + 1] = sqrtf(tot) * sh.kpart[0][c];
+          *reinterpret_cast<float4 *>(&rr[BwRec<D>::AH + 16 * w + 4 * gq]) = make_float4(a4[0], a4[1], a4[2], a4[3]);
+          if (w == 0 && gq == 0) rr[BwRec<D>::SC + 1] = sqrtf(tot) * sh.kpart[0][c];
         }
       }
     }

@@ -61,7 +61,7 @@ constexpr int BW_CC = 32;          // tokens per chunk of the chunked gradient p
 template <int D>
 struct BwCfg {
   static constexpr int R = D / 32, NB = D / 32;
-  static constexpr int REC = BwRec<D>::F;  // khat, z, ahat, r, phi(q), o, scalars
+  static constexpr int REC = BwRec<D>::F;  // z, ahat, r, o, scalars
 };
 
 __device__ __forceinline__ float bw_cv(float x) { return x; }
@@ -81,7 +81,7 @@ __device__ __forceinline__ float bw_dot(const float *x, const float *y, int lane
 // ---------------------------------------------------------------------------------------------
 // k_bw_replay: the forward over segment p from its start state (S0seg, A0seg, n0seg at
 // [stream][P]; NULL = the fixed start S = 0, A = I / lambda0, n = 0).  Writes each token's
-// record (khat, z, ahat, r, phi(q), o, delta, ||y||, 1/||k||, den) and the state (S, A) after
+// record (z, ahat, r, o, delta, ||y||, 1/||k||, den) and the state (S, A) after
 // every 64th token and after the segment's last token, and n after the segment.
 // ---------------------------------------------------------------------------------------------
 template <int D>
@@ -249,22 +249,20 @@ k_bw_replay(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__r
       const float rden = 1.0f / den;
 #pragma unroll
       for (int a = 0; a < R; ++a) {
-        rec[3 * D + row(a)] = ra[a];          // r
-        rec[5 * D + row(a)] = np[a] * rden;   // o
+        rec[BwRec<D>::R + row(a)] = ra[a];
+        rec[BwRec<D>::O + row(a)] = np[a] * rden;
       }
     }
     if (tid < D) {
-      rec[tid] = sh.kr[tid] * rk;          // khat
-      rec[D + tid] = sh.z[tid];            // z
-      rec[2 * D + tid] = sh.y[tid] * ry;   // ahat
-      rec[4 * D + tid] = sh.fq[tid];       // phi(q)
+      rec[BwRec<D>::Z + tid] = sh.z[tid];
+      rec[BwRec<D>::AH + tid] = sh.y[tid] * ry;
       sh.n[tid] += sh.fk[tid];             // only this thread reads n[tid] until the barrier
     }
     if (tid == 0) {
-      rec[6 * D + 0] = delta;
-      rec[6 * D + 1] = yy > 0.f ? sqrtf(yy) : 0.f;  // ||y||
-      rec[6 * D + 2] = rk;
-      rec[6 * D + 3] = den;
+      rec[BwRec<D>::SC + 0] = delta;
+      rec[BwRec<D>::SC + 1] = yy > 0.f ? sqrtf(yy) : 0.f;  // ||y||
+      rec[BwRec<D>::SC + 2] = rk;
+      rec[BwRec<D>::SC + 3] = den;
     }
     if (t % BW_CK == BW_CK - 1 || t == te - 1) {
       float *ck = ck0 + (t / BW_CK) * 2 * D * D;
@@ -299,9 +297,9 @@ struct BwMapShared {
 
 template <int D, typename TIn>
 __global__ void __launch_bounds__(BW_NT)
-k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs,
-           const float *__restrict__ fpm, float *__restrict__ lb, float *__restrict__ nd, int64_t T,
-           int64_t L, int64_t P) {
+k_bw_dsmap(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ dout,
+           const float *__restrict__ recs, const float *__restrict__ fpm, float *__restrict__ lb,
+           float *__restrict__ nd, int64_t T, int64_t L, int64_t P) {
   using C = BwCfg<D>;
   constexpr int R = C::R, NB = C::NB;
   __shared__ BwMapShared<D> sh;
@@ -333,18 +331,20 @@ k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs,
   float ndp = 0.f;  // thread f < d: sum of dden phi(q)_f
 
   // token t - 1's record is loaded while token t is processed
-  float pk = 0.f, pa = 0.f, pf = 0.f, po = 0.f, pden = 1.f;
-  TIn pdo{};
+  float pa = 0.f, po = 0.f, prk = 0.f, pden = 1.f;
+  TIn pdo{}, pkr{}, pq{};
   auto load = [&](int64_t t) {
     const float *rec = rec0 + t * C::REC;
+    const int64_t tok = (s * T + t) * D;
     if (tid < D) {
-      pk = rec[tid];
-      pa = rec[2 * D + tid];
-      pf = rec[4 * D + tid];
-      po = rec[5 * D + tid];
-      pdo = dout[(s * T + t) * D + tid];
+      pa = rec[BwRec<D>::AH + tid];
+      po = rec[BwRec<D>::O + tid];
+      pdo = dout[tok + tid];
+      pkr = k[tok + tid];
+      pq = q[tok + tid];
     }
-    pden = rec[6 * D + 3];
+    prk = rec[BwRec<D>::SC + 2];
+    pden = rec[BwRec<D>::SC + 3];
   };
   load(te - 1);
   for (int64_t t = te - 1; t >= tb; --t) {
@@ -353,9 +353,9 @@ k_bw_dsmap(const TIn *__restrict__ dout, const float *__restrict__ recs,
     // token's barrier, past which nobody reads the buffer two tokens back.
     if (tid < D) {
       const float dd = bw_cv(pdo);
-      sh.kh[buf][tid] = pk;
+      sh.kh[buf][tid] = bw_cv(pkr) * prk;  // khat and phi(q) as the forward formed them
       sh.ah[buf][tid] = pa;
-      sh.fq[buf][tid] = pf;
+      sh.fq[buf][tid] = phi(bw_cv(pq));
       sh.dnum[buf][tid] = dd / pden;
       sh.x[buf][tid] = dd * po;
     }
@@ -416,9 +416,9 @@ struct BwSweepShared {
 
 template <int D, typename TIn>
 __global__ void __launch_bounds__(BW_NT)
-k_bw_esweep(const TIn *__restrict__ dout, const float *__restrict__ recs,
-            const float *__restrict__ Ebuf, float *__restrict__ dv, float *__restrict__ Xc,
-            int64_t T, int64_t L, int64_t P) {
+k_bw_esweep(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ dout,
+            const float *__restrict__ recs, const float *__restrict__ Ebuf, float *__restrict__ dv,
+            float *__restrict__ Xc, int64_t T, int64_t L, int64_t P) {
   using C = BwCfg<D>;
   constexpr int R = C::R, NB = C::NB;
   __shared__ BwSweepShared<D> sh;
@@ -443,17 +443,19 @@ k_bw_esweep(const TIn *__restrict__ dout, const float *__restrict__ recs,
     }
 
   // token t - 1's record is loaded while token t is processed
-  float pk = 0.f, pa = 0.f, pf = 0.f, pden = 1.f;
-  TIn pdo{};
+  float pa = 0.f, prk = 0.f, pden = 1.f;
+  TIn pdo{}, pkr{}, pq{};
   auto load = [&](int64_t t) {
     const float *rec = rec0 + t * C::REC;
+    const int64_t tok = (s * T + t) * D;
     if (tid < D) {
-      pk = rec[tid];
-      pa = rec[2 * D + tid];
-      pf = rec[4 * D + tid];
-      pdo = dout[(s * T + t) * D + tid];
+      pa = rec[BwRec<D>::AH + tid];
+      pdo = dout[tok + tid];
+      pkr = k[tok + tid];
+      pq = q[tok + tid];
     }
-    pden = rec[6 * D + 3];
+    prk = rec[BwRec<D>::SC + 2];
+    pden = rec[BwRec<D>::SC + 3];
   };
   load(te - 1);
   for (int64_t t = te - 1; t >= tb; --t) {
@@ -469,9 +471,9 @@ k_bw_esweep(const TIn *__restrict__ dout, const float *__restrict__ recs,
     // double-buffered staging: this token's buffer was last read two tokens back, before the
     // previous token's barrier
     if (tid < D) {
-      sh.kh[buf][tid] = pk;
+      sh.kh[buf][tid] = bw_cv(pkr) * prk;  // khat and phi(q) as the forward formed them
       sh.ah[buf][tid] = pa;
-      sh.fq[buf][tid] = pf;
+      sh.fq[buf][tid] = phi(bw_cv(pq));
       sh.dnum[buf][tid] = bw_cv(pdo) / pden;
     }
     if (t > tb) load(t - 1);
@@ -693,13 +695,12 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
       if (t < m) {
         const uint32_t rb = static_cast<uint32_t>(t * REC), o = static_cast<uint32_t>(t * D + c);
         const f4_t *rc4 = reinterpret_cast<const f4_t *>(rcb);
-        const float rden = 1.0f / at32(rcb, rb + 6 * D + 3);
-        const f4_t oo = at32(rc4, (rb + 5 * D + c) / 4);
-        kh = at32(rc4, (rb + c) / 4);
-        zz = at32(rc4, (rb + D + c) / 4);
-        ah = at32(rc4, (rb + 2 * D + c) / 4);
-        rr = at32(rc4, (rb + 3 * D + c) / 4);
-        fq = at32(rc4, (rb + 4 * D + c) / 4);
+        const float rkt = at32(rcb, rb + BwRec<D>::SC + 2);
+        const float rden = 1.0f / at32(rcb, rb + BwRec<D>::SC + 3);
+        const f4_t oo = at32(rc4, (rb + BwRec<D>::O + c) / 4);
+        zz = at32(rc4, (rb + BwRec<D>::Z + c) / 4);
+        ah = at32(rc4, (rb + BwRec<D>::AH + c) / 4);
+        rr = at32(rc4, (rb + BwRec<D>::R + c) / 4);
         dr = at32(reinterpret_cast<const f4_t *>(dvb), o / 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -707,6 +708,8 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
           dn[j] = d * rden;
           po = fmaf(d, oo[j], po);
           uu[j] = bw_cv(at32(ub, o + j));
+          kh[j] = bw_cv(at32(kb0, o + j)) * rkt;  // khat and phi(q) as the forward formed them
+          fq[j] = phi(bw_cv(at32(qb, o + j)));
         }
       }
       *reinterpret_cast<f4_t *>(&sh.Rr[t][c]) = rr;
@@ -721,7 +724,7 @@ k_bw_cgrad(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__re
     }
     if (tid < BW_CC) {
       const int t = tid;
-      const uint32_t rb = static_cast<uint32_t>((t < m ? t : 0) * REC) + 6 * D;
+      const uint32_t rb = static_cast<uint32_t>((t < m ? t : 0) * REC) + BwRec<D>::SC;
       sh.rd[t] = t < m ? 1.0f / at32(rcb, rb) : 0.f;
       sh.yn[t] = t < m ? at32(rcb, rb + 1) : 0.f;
       sh.rk[t] = t < m ? at32(rcb, rb + 2) : 0.f;
@@ -1125,7 +1128,7 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
     const float *ck = ck0 + (bef ? (init ? 0 : (c0 - 1) / BW_CK) : (c1 - 1) / BW_CK) * 2 * D * D;
     const int64_t tok0 = (s * T + c0) * D;
     const float *rcb = rec0 + c0 * REC;
-    const bf16_t *kb0 = k + tok0, *ub = u + tok0, *dob = dout + tok0;
+    const bf16_t *qb = q + tok0, *kb0 = k + tok0, *ub = u + tok0, *dob = dout + tok0;
     const float *dvb = dv + tok0;
     float *dqb = dq + tok0, *dkb = dk + tok0, *dub = du + tok0;
     auto ld_tile = [&](const float *x, float dg, f4_t (&t)[KB]) {
@@ -1156,18 +1159,25 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
       if (t < m) {
         const uint32_t rb = static_cast<uint32_t>(t * REC), o = static_cast<uint32_t>(t * D + c);
         const f4_t *rc4 = reinterpret_cast<const f4_t *>(rcb);
-        const float rden = 1.0f / at32(rcb, rb + 6 * D + 3);
-        const f4_t oo = at32(rc4, (rb + 5 * D + c) / 4);
-        kh = at32(rc4, (rb + c) / 4);
-        zz = at32(rc4, (rb + D + c) / 4);
-        ah = at32(rc4, (rb + 2 * D + c) / 4);
-        rr = at32(rc4, (rb + 3 * D + c) / 4);
-        fq = at32(rc4, (rb + 4 * D + c) / 4);
+        const float rkt = at32(rcb, rb + BwRec<D>::SC + 2);
+        const float rden = 1.0f / at32(rcb, rb + BwRec<D>::SC + 3);
+        const f4_t oo = at32(rc4, (rb + BwRec<D>::O + c) / 4);
+        zz = at32(rc4, (rb + BwRec<D>::Z + c) / 4);
+        ah = at32(rc4, (rb + BwRec<D>::AH + c) / 4);
+        rr = at32(rc4, (rb + BwRec<D>::R + c) / 4);
         dr = at32(reinterpret_cast<const f4_t *>(dvb), o / 4);
         const uint2 dw = at32(reinterpret_cast<const uint2 *>(dob), o / 4);
         uu = at32(reinterpret_cast<const uint2 *>(ub), o / 4);
         const uint2 kw = at32(reinterpret_cast<const uint2 *>(kb0), o / 4);
-        pk = f4_t{phi(pk_lo_val(kw.x)), phi(pk_hi_val(kw.x)), phi(pk_lo_val(kw.y)), phi(pk_hi_val(kw.y))};
+        const uint2 qw = at32(reinterpret_cast<const uint2 *>(qb), o / 4);
+        const f4_t k4{pk_lo_val(kw.x), pk_hi_val(kw.x), pk_lo_val(kw.y), pk_hi_val(kw.y)};
+        const f4_t q4{pk_lo_val(qw.x), pk_hi_val(qw.x), pk_lo_val(qw.y), pk_hi_val(qw.y)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // khat and phi(q) as the forward formed them
+          kh[j] = k4[j] * rkt;
+          fq[j] = phi(q4[j]);
+          pk[j] = phi(k4[j]);
+        }
         const float dd4[4] = {pk_lo_val(dw.x), pk_hi_val(dw.x), pk_lo_val(dw.y), pk_hi_val(dw.y)};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1195,7 +1205,7 @@ k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf
     }
     if (w == LW && lane < BW_CC) {
       const int t = lane;
-      const uint32_t rb = static_cast<uint32_t>((t < m ? t : 0) * REC) + 6 * D;
+      const uint32_t rb = static_cast<uint32_t>((t < m ? t : 0) * REC) + BwRec<D>::SC;
       sh.rd[t] = t < m ? 1.0f / at32(rcb, rb) : 0.f;
       sh.yn[t] = t < m ? at32(rcb, rb + 1) : 0.f;
       sh.rk[t] = t < m ? at32(rcb, rb + 2) : 0.f;
@@ -1646,7 +1656,7 @@ BwPlan make_bw_plan(const Problem &p, int chunk) {
   const size_t S = static_cast<size_t>(p.streams), T = static_cast<size_t>(p.T);
   const size_t D = static_cast<size_t>(p.d), P = static_cast<size_t>(b.P);
   const size_t NC = (T + BW_CK - 1) / BW_CK;
-  b.off_rec = off;  off = align256(off + S * T * (6 * D + BW_NS) * 4);
+  b.off_rec = off;  off = align256(off + S * T * (4 * D + BW_NS) * 4);
   b.off_ck = off;   off = align256(off + S * NC * 2 * D * D * 4);
   b.off_xc = off;   off = align256(off + S * ((T + BW_CC - 1) / BW_CC) * D * D * 4);
   b.off_nend = off; off = align256(off + S * P * D * 4);
@@ -1722,12 +1732,12 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
     // normalisers were and the segment R sums where A was; the forward's own maps (Pi_p) are
     // read for the L part of the backward's.
     float *lb = reinterpret_cast<float *>(base + bp.off_md), *E = cs.S_seg, *nd = cs.n_seg, *W = cs.A_seg;
-    VLA_LAUNCH("k_bw_dsmap", (k_bw_dsmap<D, TIn>), dim3(S, P - 1), dim3(BW_NT), 0, st, dout,
+    VLA_LAUNCH("k_bw_dsmap", (k_bw_dsmap<D, TIn>), dim3(S, P - 1), dim3(BW_NT), 0, st, q, k, dout,
                static_cast<const float *>(rec), static_cast<const float *>(cs.pib), lb, nd, pr.T,
                bp.L, bp.P);
     err = launch_affine_prefix(pr, lb, E, bp.P, io.dS_T, nd, io.dn_T, st);
     if (err != hipSuccess) return err;
-    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, dout,
+    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, dout,
                static_cast<const float *>(rec), static_cast<const float *>(E), io.dv, xc, pr.T,
                bp.L, bp.P);
     launch_cgrad<D, TIn>(q, k, u, dout, rec, ck, nend, xc, io.dv, nd, nullptr, io.dq, io.dk, io.du,
@@ -1738,7 +1748,7 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
     VLA_LAUNCH("k_bw_fix", (k_bw_fix<D, TIn>), dim3(S, P, nz), dim3(D / 16 * kWave), 0, st, u,
                static_cast<const float *>(W), io.du, pr.T, bp.L, bp.P);
   } else {
-    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, 1), dim3(BW_NT), 0, st, dout,
+    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, 1), dim3(BW_NT), 0, st, q, k, dout,
                static_cast<const float *>(rec), io.dS_T, io.dv, xc, pr.T, bp.L, bp.P);
     launch_cgrad<D, TIn>(q, k, u, dout, rec, ck, nend, xc, io.dv, io.dn_T, X, io.dq, io.dk, io.du,
                          nullptr, trw, pr, bp, st);

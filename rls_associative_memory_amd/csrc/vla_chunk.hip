@@ -573,8 +573,8 @@ __device__ __forceinline__ void unit_sync() {
   }
 }
 
-// With REC the kernel also writes the backward's token records it holds (khat, z, ahat,
-// phi(q), delta, ||A khat||, 1/||k||, den) and the A half of the state checkpoints.
+// With REC the kernel also writes the backward's token records it holds (z, ahat, delta,
+// ||A khat||, 1/||k||, den) and the A half of the state checkpoints.
 template <int D, typename TIn, bool REC = false>
 __global__ void __launch_bounds__(AsideCfg<D>::NT)
 k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ u,
@@ -773,16 +773,14 @@ k_aside(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restr
 #pragma unroll
         for (int r = 0; r < C::RPL; ++r) {
           const int row = g + r * C::HALF;
-          rr[row] = K[row] * rk;           // khat
-          rr[D + row] = z[r];              // z
-          rr[2 * D + row] = y[r] * inv;    // ahat
-          rr[4 * D + row] = Q[row];        // phi(q)
+          rr[BwRec<D>::Z + row] = z[r];
+          rr[BwRec<D>::AH + row] = y[r] * inv;
         }
       if (lu == 0) {
-        rr[6 * D] = delta;
-        rr[6 * D + 1] = sy > 0.f ? sqrtf(sy) : 0.f;
-        rr[6 * D + 2] = rk;
-        rr[6 * D + 3] = dp + eps;
+        rr[BwRec<D>::SC] = delta;
+        rr[BwRec<D>::SC + 1] = sy > 0.f ? sqrtf(sy) : 0.f;
+        rr[BwRec<D>::SC + 2] = rk;
+        rr[BwRec<D>::SC + 3] = dp + eps;
       }
     }
     unit_sync<C::NWA>();
@@ -1116,7 +1114,7 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * gq + r;
-          if (c < m) brs[(c0 + c) * RF + 3 * D + rowbase + li] = E[ct][r];
+          if (c < m) brs[(c0 + c) * RF + BwRec<D>::R + rowbase + li] = E[ct][r];
         }
     }
     if constexpr (FINAL) {
@@ -1145,7 +1143,7 @@ k_swy(const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restric
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * ct + 4 * gq + r;
           if constexpr (REC) {
-            if (c < m) brs[(c0 + c) * RF + 5 * D + rowbase + li] = acc[r] * sRden[c];  // o, fp32
+            if (c < m) brs[(c0 + c) * RF + BwRec<D>::O + rowbase + li] = acc[r] * sRden[c];  // o, fp32
           } else {
             if (c < m) store_elem(os, (c0 + c) * D + rowbase + li, acc[r] * sRden[c]);
           }
@@ -1356,7 +1354,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     using AC = AsideCfg<D>;
     const int64_t units = pl.S * pl.P;
     const unsigned blocks = static_cast<unsigned>((units + AC::UPB - 1) / AC::UPB);
-    if (rec != nullptr)  // with the backward's records (khat, z, ahat, phi(q), scalars, A checkpoints)
+    if (rec != nullptr)  // with the backward's records (z, ahat, scalars, A checkpoints)
       VLA_LAUNCH("k_aside", (k_aside<D, TIn, true>), dim3(blocks), dim3(AC::NT), 0, st, qq, kk, uu, Mw,
                  nkw, alw, rdw, A_final, n_final, pl.S, pl.T, pl.L, pl.P, pr.eps, rec->rec, rec->ck,
                  rec->n_end);
@@ -1382,7 +1380,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // workgroup then fits twice per CU (54 KB of LDS and 127 VGPRs at d = 96), and the
     // segment maps it starts from do not depend on either pass's chunking.
     constexpr int CF = CH < 32 ? CH : 32;
-    if (rec != nullptr)  // the backward's records (khat, r, phi(q), o, 1/||k||, den, S checkpoints)
+    if (rec != nullptr)  // the backward's records (r, o, 1/||k||, den, S checkpoints)
       VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT),
                  0, st, qq, kk, vv, alh, rdw, s0w, pbw, static_cast<TIn *>(nullptr), S_final, nkw, pl.T,
                  pl.L, pl.P, rec->rec, rec->ck);

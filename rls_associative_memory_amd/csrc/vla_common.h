@@ -50,15 +50,17 @@ template <> struct io<bf16_t> {
   }
 };
 
-// The backward's per-token record, fp32: khat, z = A_{t-1} u, ahat, r = v - S_{t-1} khat, phi(q),
-// o (d values each), then delta = 1 + u . z, ||A_t khat||, 1/||k||, den and spare slots; and the
-// state (S, A) after every kBwCk-th token and after each segment's last token.  Written by the
-// backward's replay, or by the chunked forward's passes for the backward.
+// The backward's per-token record, fp32: z = A_{t-1} u, ahat, r = v - S_{t-1} khat, o (d values
+// each), then delta = 1 + u . z, ||A_t khat||, 1/||k||, den and spare slots (khat = k / ||k|| and
+// phi(q) are formed again from the inputs where they are needed); and the state (S, A) after
+// every kBwCk-th token and after each segment's last token.  Written by the backward's replay,
+// or by the chunked forward's passes for the backward.
 constexpr int kBwScalars = 8;
 constexpr int kBwCk = 64;
 template <int D>
 struct BwRec {
-  static constexpr int F = 6 * D + kBwScalars;  // floats per token record
+  static constexpr int Z = 0, AH = D, R = 2 * D, O = 3 * D, SC = 4 * D;  // field offsets
+  static constexpr int F = 4 * D + kBwScalars;  // floats per token record
 };
 
 // ELU(x) + 1 with alpha = 1.

@@ -68,9 +68,9 @@ struct SwbLds {
 template <int D, bool FINAL>
 constexpr int swb_waves_per_simd() { return (FINAL && D <= 96) ? 4 : 1; }
 
-// With REC (final pass only) the kernel writes its part of the backward's token records (khat,
-// r, phi(q), o in fp32, 1/||k||, den) and the S half of the state checkpoints (brec, bck:
-// BwRec layout) in place of the outputs.
+// With REC (final pass only) the kernel writes its part of the backward's token records (r and
+// o in fp32, 1/||k||, den) and the S half of the state checkpoints (brec, bck: BwRec layout) in
+// place of the outputs.
 template <int D, int CH, bool FINAL, bool REC = false>
 __global__ void __launch_bounds__((SwbCfg<D, CH, FINAL>::NT))
 __attribute__((amdgpu_waves_per_eu(swb_waves_per_simd<D, FINAL>())))
@@ -192,12 +192,6 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
           io<bf16_t>::unpack(pq[i], qf);
 #pragma unroll
           for (int e = 0; e < 8; ++e) qf[e] = c < m ? phi(qf[e]) : 0.f;
-          if constexpr (REC)
-            if (c < m) {
-              float *rq = &brs[(c0 + c) * RF + 4 * D + f0];
-              *reinterpret_cast<float4 *>(rq) = make_float4(qf[0], qf[1], qf[2], qf[3]);
-              *reinterpret_cast<float4 *>(rq + 4) = make_float4(qf[4], qf[5], qf[6], qf[7]);
-            }
           // The A side's denominators count the normaliser from the segment start only;
           // den = phi(q) . n_p + (A side's value), n_p the normaliser at the segment start:
           // this thread's 8 features of the dot product, in fp32 (summed in the tile phase).
@@ -388,22 +382,9 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
         sh.rden[lane] = 1.0f / den;
         if constexpr (REC)
           if (lane < m) {
-            brs[(c0 + lane) * RF + 6 * D + 2] = sh.rk[lane];
-            brs[(c0 + lane) * RF + 6 * D + 3] = den;
+            brs[(c0 + lane) * RF + BwRec<D>::SC + 2] = sh.rk[lane];
+            brs[(c0 + lane) * RF + BwRec<D>::SC + 3] = den;
           }
-      }
-      if constexpr (REC) {  // khat = k / ||k|| of the chunk, from the staged rows
-        for (int idx = tid; idx < CH * (D / 8); idx += NT) {
-          const int c = idx / (D / 8), f0 = (idx % (D / 8)) * 8;
-          if (c < m) {
-            float kf[8];
-            io<bf16_t>::unpack(*reinterpret_cast<const uint4 *>(&sh.sK[c][f0]), kf);
-            const float rk = sh.rk[c];
-            float *rkh = &brs[(c0 + c) * RF + f0];
-            *reinterpret_cast<float4 *>(rkh) = make_float4(kf[0] * rk, kf[1] * rk, kf[2] * rk, kf[3] * rk);
-            *reinterpret_cast<float4 *>(rkh + 4) = make_float4(kf[4] * rk, kf[5] * rk, kf[6] * rk, kf[7] * rk);
-          }
-        }
       }
     }
     __syncthreads();
@@ -495,7 +476,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int c = 16 * ct + 4 * gq + r;
-            if (c < m) brs[(c0 + c) * RF + 3 * D + rowbase + li] = E[h][r];
+            if (c < m) brs[(c0 + c) * RF + BwRec<D>::R + rowbase + li] = E[h][r];
           }
         }
       }
@@ -511,7 +492,7 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int c = 16 * ct + 4 * gq + r;
-              if (c < m) brs[(c0 + c) * RF + 5 * D + rowbase + li] = num[r] * sh.rden[c];
+              if (c < m) brs[(c0 + c) * RF + BwRec<D>::O + rowbase + li] = num[r] * sh.rden[c];
             }
           } else {
 #pragma unroll

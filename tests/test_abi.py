@@ -185,11 +185,11 @@ def test_backward_argument_errors(lib):
     assert call(args, small) == 1
     n = ctypes.c_size_t(0)
     assert lib.vla_backward_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
-    # one segment per stream: T (6 d + 8) floats of records, ceil(T / 64) checkpoints of
+    # one segment per stream: T (4 d + 8) floats of records, ceil(T / 64) checkpoints of
     # 2 d^2 floats, ceil(T / 32) S cotangents of d^2 floats, n after the segment, two d x d
     # matrices and one double, per stream, each buffer 256-byte aligned
     al = lambda x: (x + 255) // 256 * 256
-    seq = (al(2 * 100 * (6 * 64 + 8) * 4) + al(2 * 2 * 2 * 64 * 64 * 4) + al(2 * 4 * 64 * 64 * 4)
+    seq = (al(2 * 100 * (4 * 64 + 8) * 4) + al(2 * 2 * 2 * 64 * 64 * 4) + al(2 * 4 * 64 * 64 * 4)
            + al(2 * 64 * 4) + 2 * al(2 * 64 * 64 * 4) + al(2 * 8))
     assert n.value == seq
     assert lib.vla_backward_workspace_size(ctypes.byref(desc(B=1, H=2, T=100, d=64, path=1)),
