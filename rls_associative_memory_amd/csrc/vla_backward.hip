@@ -1058,6 +1058,250 @@ __device__ __forceinline__ Split2 ld2_tr(const uint16_t *m, int ts, int ld, int 
   return Split2{ld_tr4x2(m, ld, r0, r1, c0, li), ld_tr4x2(m + ts, ld, r0, r1, c0, li)};
 }
 
+// ---------------------------------------------------------------------------------------------
+// k_bw_xsweepb: the S-cotangent sweep of k_bw_esweep for bf16 inputs (d <= 96) in chunks of
+// BW_CC tokens on the bf16 matrix cores (two-term operands).  Within a chunk, with X the
+// cotangent at its last token (before that token's terms) and the rows dr_t, the token chain
+//   Shat_t = X + sum_{j >= t} dnum_j phi_j^T - sum_{j > t} dr_j khat_j^T,  dr_t = Shat_t ahat_t
+// is the unit upper-triangular system
+//   (I + triu1(Ahat Khat^T)) dR = Ahat X^T + triu0(Ahat Phi^T) Dn,
+// solved through the inverses of its two 16 x 16 diagonal blocks (each column by back
+// substitution in one lane), and the cotangent before the chunk is, in transposed form,
+//   X^T <- X^T + Phi^T Dn - Khat^T dR.
+// Wave w keeps the column tile w of X^T (rows 16 w .. of X) in registers, in the accumulator
+// layout that is also the B operand of Ahat X^T.  Writes dv and X at every chunk's last token
+// (before its terms), as k_bw_esweep does.
+// ---------------------------------------------------------------------------------------------
+template <int D>
+struct XsCfg {
+  static constexpr int NW = D / 16, NT = NW * kWave, KB = D / 16, KS = KB / 2;
+  static constexpr int LDB = D + 8;   // bf16 stride of token rows
+  static constexpr int TS = BW_CC * LDB;
+  static constexpr int LDM = BW_CC + 8;
+  static constexpr int MS = BW_CC * LDM;
+  static constexpr int LDH = 24;      // bf16 stride of the 16 x 16 blocks
+  static constexpr int HS = 16 * LDH;
+  static constexpr int G4 = D / 4;
+};
+
+template <int D>
+struct XsShared {
+  using C = XsCfg<D>;
+  uint16_t Ah[2][BW_CC][C::LDB], Kh[2][BW_CC][C::LDB], Fq[2][BW_CC][C::LDB], Dn[2][BW_CC][C::LDB];
+  uint16_t Ma[2][BW_CC][C::LDM];        // triu0(Ahat Phi^T)
+  uint16_t Mk[2][16][C::LDH];           // the (0, 1) block of Ahat Khat^T
+  uint16_t Iv[2][2][16][C::LDH];        // (I + N_bb)^{-1} of the two diagonal blocks
+  float Nd[2][16][17];                  // N_bb = strictly upper part of the diagonal blocks
+};
+
+template <int D>
+__global__ void __launch_bounds__(XsCfg<D>::NT)
+k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+             const bf16_t *__restrict__ dout, const float *__restrict__ recs,
+             const float *__restrict__ Ebuf, float *__restrict__ dv, float *__restrict__ Xc,
+             int64_t T, int64_t L, int64_t P) {
+  using C = XsCfg<D>;
+  constexpr int NW = C::NW, NT = C::NT, KB = C::KB, KS = C::KS, G4 = C::G4, REC = BwRec<D>::F;
+  constexpr int TS = C::TS, MS = C::MS, HS = C::HS, LDB = C::LDB;
+  static_assert(KB % 2 == 0, "feature blocks go in pairs");
+  __shared__ __attribute__((aligned(16))) XsShared<D> sh;
+  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int64_t NX = (T + BW_CC - 1) / BW_CC;
+  const float *rec0 = recs + s * T * REC;
+  const int64_t slot = s * P + (P - 1 - p);
+  constexpr int NS = NW < 4 ? NW : 4;
+  const int jsimd = w % NS, jn = (NW - jsimd + NS - 1) / NS;
+  const int job0 = jsimd + NS * (w / NS), jstep = NS * jn;
+  constexpr int LW = NW >= 4 ? 3 : NW - 1;  // the inverses: a wave with its SIMD to itself
+  auto put2 = [](uint16_t *x, int ts, float v) {
+    uint16_t t2[2];
+    split_n<2>(v, t2);
+    x[0] = t2[0];
+    x[ts] = t2[1];
+  };
+
+  // X^T[16 kb + 4 gq + r][16 w + li] = X[16 w + li][16 kb + 4 gq + r] in Xt[kb][r]
+  f4_t Xt[KB];
+  {
+    const int lane = threadIdx.x & 63, li = lane & 15, gq = lane >> 4;
+    const float *e0 = Ebuf != nullptr ? Ebuf + slot * D * D : nullptr;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      Xt[kb] = e0 != nullptr ? at32(reinterpret_cast<const f4_t *>(e0), static_cast<uint32_t>(((16 * w + li) * D + 16 * kb + 4 * gq) / 4))
+                             : f4_zero();
+  }
+
+  // The chunk's inputs are loaded one chunk ahead into registers (two elements of 4 features
+  // per thread: 32 tokens x d / 4 groups over d / 16 waves) and staged when the chunk starts.
+  static_assert(BW_CC * G4 == 2 * NT, "two staging elements per thread");
+  struct Pf {
+    f4_t ah;
+    uint2 kw, qw, dw;
+    float rk, den;
+  };
+  Pf pf[2];
+  auto fetch = [&](int64_t cs, int mm, int tid) {
+    const int64_t tok = (s * T + cs) * D;
+    const float *rc = rec0 + cs * REC;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = tid + it * NT, t = e / G4, c = 4 * (e % G4);
+      const int tt = t < mm ? t : 0;  // rows past the chunk: a row of it, zeroed when staged
+      const uint32_t rb = static_cast<uint32_t>(tt * REC), o = static_cast<uint32_t>(tt * D + c);
+      pf[it].ah = at32(reinterpret_cast<const f4_t *>(rc), (rb + BwRec<D>::AH + c) / 4);
+      pf[it].kw = at32(reinterpret_cast<const uint2 *>(k + tok), o / 4);
+      pf[it].qw = at32(reinterpret_cast<const uint2 *>(q + tok), o / 4);
+      pf[it].dw = at32(reinterpret_cast<const uint2 *>(dout + tok), o / 4);
+      pf[it].rk = at32(rc, rb + BwRec<D>::SC + 2);
+      pf[it].den = at32(rc, rb + BwRec<D>::SC + 3);
+    }
+  };
+  {
+    const int64_t c0f = std::max<int64_t>(tb, ((te - 1) / BW_CC) * BW_CC);
+    fetch(c0f, static_cast<int>(te - c0f), threadIdx.x);
+  }
+
+  for (int64_t c1 = te; c1 > tb;) {
+    const int64_t c0 = std::max<int64_t>(tb, ((c1 - 1) / BW_CC) * BW_CC);
+    const int m = static_cast<int>(c1 - c0);
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, lane = tid & 63, li = lane & 15, gq = lane >> 4;
+    // X at the chunk's last token, before its terms
+    {
+      f4_t *xc = reinterpret_cast<f4_t *>(Xc + (s * NX + (c1 - 1) / BW_CC) * D * D);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) at32(xc, static_cast<uint32_t>(((16 * w + li) * D + 16 * kb + 4 * gq) / 4)) = Xt[kb];
+    }
+    const int64_t tok0 = (s * T + c0) * D;
+    __syncthreads();  // the previous chunk's readers are done
+    // ---- stage ahat, khat, phi(q), dnum as two terms (rows past the chunk are zeros) ----
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = tid + it * NT, t = e / G4, c = 4 * (e % G4);
+      f4_t ah = f4_zero(), kh = f4_zero(), fq = f4_zero(), dn = f4_zero();
+      if (t < m) {
+        const Pf &v = pf[it];
+        ah = v.ah;
+        const f4_t k4{pk_lo_val(v.kw.x), pk_hi_val(v.kw.x), pk_lo_val(v.kw.y), pk_hi_val(v.kw.y)};
+        const f4_t q4{pk_lo_val(v.qw.x), pk_hi_val(v.qw.x), pk_lo_val(v.qw.y), pk_hi_val(v.qw.y)};
+        const f4_t d4{pk_lo_val(v.dw.x), pk_hi_val(v.dw.x), pk_lo_val(v.dw.y), pk_hi_val(v.dw.y)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // khat, phi(q) and dnum as the forward and the sweep form them
+          kh[j] = k4[j] * v.rk;
+          fq[j] = phi(q4[j]);
+          dn[j] = d4[j] / v.den;
+        }
+      }
+      auto stage2 = [&](uint16_t (*X)[BW_CC][LDB], const f4_t &x) {
+        uint32_t a[2], b[2];
+        split_pk<2>(x[0], x[1], a);
+        split_pk<2>(x[2], x[3], b);
+        *reinterpret_cast<uint2 *>(&X[0][t][c]) = make_uint2(a[0], b[0]);
+        *reinterpret_cast<uint2 *>(&X[1][t][c]) = make_uint2(a[1], b[1]);
+      };
+      stage2(sh.Ah, ah);
+      stage2(sh.Kh, kh);
+      stage2(sh.Fq, fq);
+      stage2(sh.Dn, dn);
+    }
+    if (c0 > tb) {  // the next chunk's inputs, in flight during this chunk's products
+      const int64_t c0n = std::max<int64_t>(tb, ((c0 - 1) / BW_CC) * BW_CC);
+      fetch(c0n, static_cast<int>(c0 - c0n), tid);
+    }
+    __syncthreads();
+    // ---- Ma = triu0(Ahat Phi^T); the diagonal blocks of Ahat Khat^T (strictly upper, fp32)
+    // and its (0, 1) block (two terms) ----
+    for (int job = job0; job < 6; job += jstep) {
+      const int ti = job == 2 || job == 4 ? 1 : 0, tj = job == 0 || job == 3 ? 0 : 1;
+      const uint16_t *asrc = &sh.Ah[0][16 * ti + li][0];
+      const uint16_t *bsrc = job < 3 ? &sh.Fq[0][16 * tj + li][0] : &sh.Kh[0][16 * tj + li][0];
+      f4_t acc = f4_zero();
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        acc = mm2_ss(ld2_4x2(asrc + 32 * s2 + 4 * gq, asrc + 32 * s2 + 16 + 4 * gq, TS),
+                     ld2_4x2(bsrc + 32 * s2 + 4 * gq, bsrc + 32 * s2 + 16 + 4 * gq, TS), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int il = 4 * gq + r, jl = li;  // within the 16 x 16 tile
+        if (job < 3) {
+          put2(&sh.Ma[0][16 * ti + il][16 * tj + jl], MS, 16 * tj + jl >= 16 * ti + il ? acc[r] : 0.f);
+          if (job == 2) put2(&sh.Ma[0][16 + il][jl], MS, 0.f);  // the (1, 0) block: below the diagonal
+        } else if (job == 5) {
+          put2(&sh.Mk[0][il][jl], HS, acc[r]);
+        } else {
+          sh.Nd[ti][il][jl] = jl > il ? acc[r] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+    // ---- (I + N_bb)^{-1} for both diagonal blocks: lane (b, j) finds column j of block b by back
+    // substitution (v_i = [i == j] - sum_{k > i} N[i][k] v_k, zero below the diagonal) ----
+    if (w == LW && lane < 32) {
+      const int bb = lane >> 4, j = lane & 15;
+      float v[16];
+#pragma unroll
+      for (int i = 15; i >= 0; --i) {
+        float x = i == j ? 1.f : 0.f;
+#pragma unroll
+        for (int kk = i + 1; kk < 16; ++kk) x = fmaf(-sh.Nd[bb][i][kk], v[kk], x);
+        v[i] = x;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) put2(&sh.Iv[bb][0][i][j], HS, v[i]);
+    }
+    // ---- rhs = Ahat X^T + Ma Dn (this wave's 16 columns) ----
+    const Split2 bdn = ld2_tr(&sh.Dn[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
+    f4_t rhs[2];
+    {
+      Split2 Bs[KS];
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) {
+        const float x[8] = {Xt[2 * s2][0], Xt[2 * s2][1], Xt[2 * s2][2], Xt[2 * s2][3],
+                            Xt[2 * s2 + 1][0], Xt[2 * s2 + 1][1], Xt[2 * s2 + 1][2], Xt[2 * s2 + 1][3]};
+        Bs[s2] = split2(x);
+      }
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) {
+        const int tr = 16 * ti + li;
+        const uint16_t *ar = &sh.Ah[0][tr][0];
+        f4_t acc = f4_zero();
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2)
+          acc = mm2_ss(ld2_4x2(ar + 32 * s2 + 4 * gq, ar + 32 * s2 + 16 + 4 * gq, TS), Bs[s2], acc);
+        rhs[ti] = mm2_ss(ld2_4x2(&sh.Ma[0][tr][4 * gq], &sh.Ma[0][tr][16 + 4 * gq], MS), bdn, acc);
+      }
+    }
+    __syncthreads();  // the inverses
+    // ---- dR_b = Iv_b rhs_b, dR_a = Iv_a (rhs_a - Mk dR_b) (K = 16 products) ----
+    const f4_t dRb = mm2h_ss(ld2_4h(&sh.Iv[1][0][li][4 * gq], HS), split2_4h(rhs[1]), f4_zero());
+    const f4_t cor = mm2h_ss(ld2_4h(&sh.Mk[0][li][4 * gq], HS), split2_4h(dRb), f4_zero());
+    const f4_t dRa = mm2h_ss(ld2_4h(&sh.Iv[0][0][li][4 * gq], HS), split2_4h(rhs[0] - cor), f4_zero());
+    {
+      float *dvb = dv + tok0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ta = 4 * gq + r, tbb = 16 + 4 * gq + r;
+        if (ta < m) at32(dvb, static_cast<uint32_t>(ta * D + 16 * w + li)) = dRa[r];
+        if (tbb < m) at32(dvb, static_cast<uint32_t>(tbb * D + 16 * w + li)) = dRb[r];
+      }
+    }
+    // ---- X^T += Phi^T Dn - Khat^T dR ----
+    {
+      const float nx[8] = {-dRa[0], -dRa[1], -dRa[2], -dRa[3], -dRb[0], -dRb[1], -dRb[2], -dRb[3]};
+      const Split2 bdr = split2(nx);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        Xt[kb] = mm2_ss(ld2_tr(&sh.Fq[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * kb, li), bdn, Xt[kb]);
+        Xt[kb] = mm2_ss(ld2_tr(&sh.Kh[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * kb, li), bdr, Xt[kb]);
+      }
+    }
+    c1 = c0;
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(CbCfg<D>::NT)
 k_bw_cgradb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ u,
@@ -1685,6 +1929,20 @@ void launch_cgrad(const TIn *q, const TIn *k, const TIn *u, const TIn *dout, con
                pr.lambda0);
 }
 
+// The S-cotangent sweep: in 32-token chunks on the bf16 matrix cores for bf16 inputs at d <= 96,
+// token by token otherwise.
+template <int D, typename TIn>
+void launch_sweep(const TIn *q, const TIn *k, const TIn *dout, const float *rec, const float *E,
+                  float *dv, float *xc, const Problem &pr, const BwPlan &bp, unsigned P, hipStream_t st) {
+  const unsigned S = static_cast<unsigned>(pr.streams);
+  if constexpr (sizeof(TIn) == 2 && D <= 96)
+    VLA_LAUNCH("k_bw_esweep", (k_bw_xsweepb<D>), dim3(S, P), dim3(XsCfg<D>::NT), 0, st, q, k, dout, rec,
+               E, dv, xc, pr.T, bp.L, bp.P);
+  else
+    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, dout, rec,
+               E, dv, xc, pr.T, bp.L, bp.P);
+}
+
 template <int D, typename TIn>
 hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void *ws, hipStream_t st) {
   const BwPlan bp = make_bw_plan(pr, chunk);
@@ -1737,9 +1995,7 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
                bp.L, bp.P);
     err = launch_affine_prefix(pr, lb, E, bp.P, io.dS_T, nd, io.dn_T, st);
     if (err != hipSuccess) return err;
-    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, dout,
-               static_cast<const float *>(rec), static_cast<const float *>(E), io.dv, xc, pr.T,
-               bp.L, bp.P);
+    launch_sweep<D, TIn>(q, k, dout, rec, E, io.dv, xc, pr, bp, P, st);
     launch_cgrad<D, TIn>(q, k, u, dout, rec, ck, nend, xc, io.dv, nd, nullptr, io.dq, io.dk, io.du,
                          W, trw, pr, bp, st);
     err = launch_matrix_prefix(pr, W, bp.P, X, st);
@@ -1748,8 +2004,7 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
     VLA_LAUNCH("k_bw_fix", (k_bw_fix<D, TIn>), dim3(S, P, nz), dim3(D / 16 * kWave), 0, st, u,
                static_cast<const float *>(W), io.du, pr.T, bp.L, bp.P);
   } else {
-    VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, 1), dim3(BW_NT), 0, st, q, k, dout,
-               static_cast<const float *>(rec), io.dS_T, io.dv, xc, pr.T, bp.L, bp.P);
+    launch_sweep<D, TIn>(q, k, dout, rec, io.dS_T, io.dv, xc, pr, bp, 1u, st);
     launch_cgrad<D, TIn>(q, k, u, dout, rec, ck, nend, xc, io.dv, io.dn_T, X, io.dq, io.dk, io.du,
                          nullptr, trw, pr, bp, st);
   }
