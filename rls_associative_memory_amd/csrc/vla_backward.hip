@@ -1092,20 +1092,23 @@ struct XsShared {
   uint16_t Mk[2][16][C::LDH];           // the (0, 1) block of Ahat Khat^T
   uint16_t Iv[2][2][16][C::LDH];        // (I + N_bb)^{-1} of the two diagonal blocks
   float Nd[2][16][17];                  // N_bb = strictly upper part of the diagonal blocks
+  float dpo[BW_CC][C::G4];              // the map: do . o over 4 features
+  float dd[BW_CC];                      // the map: dden
 };
 
-template <int D>
+template <int D, bool MAP>
 __global__ void __launch_bounds__(XsCfg<D>::NT)
 k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
              const bf16_t *__restrict__ dout, const float *__restrict__ recs,
              const float *__restrict__ Ebuf, float *__restrict__ dv, float *__restrict__ Xc,
+             const float *__restrict__ fpm, float *__restrict__ lb, float *__restrict__ nd,
              int64_t T, int64_t L, int64_t P) {
   using C = XsCfg<D>;
   constexpr int NW = C::NW, NT = C::NT, KB = C::KB, KS = C::KS, G4 = C::G4, REC = BwRec<D>::F;
   constexpr int TS = C::TS, MS = C::MS, HS = C::HS, LDB = C::LDB;
   static_assert(KB % 2 == 0, "feature blocks go in pairs");
   __shared__ __attribute__((aligned(16))) XsShared<D> sh;
-  const int64_t s = blockIdx.x, p = blockIdx.y;
+  const int64_t s = blockIdx.x, p = MAP ? blockIdx.y + 1 : blockIdx.y;
   const int64_t tb = p * L, te = std::min<int64_t>(T, tb + L);
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int64_t NX = (T + BW_CC - 1) / BW_CC;
@@ -1126,7 +1129,7 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   f4_t Xt[KB];
   {
     const int lane = threadIdx.x & 63, li = lane & 15, gq = lane >> 4;
-    const float *e0 = Ebuf != nullptr ? Ebuf + slot * D * D : nullptr;
+    const float *e0 = !MAP && Ebuf != nullptr ? Ebuf + slot * D * D : nullptr;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
       Xt[kb] = e0 != nullptr ? at32(reinterpret_cast<const f4_t *>(e0), static_cast<uint32_t>(((16 * w + li) * D + 16 * kb + 4 * gq) / 4))
@@ -1137,10 +1140,11 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
   // per thread: 32 tokens x d / 4 groups over d / 16 waves) and staged when the chunk starts.
   static_assert(BW_CC * G4 == 2 * NT, "two staging elements per thread");
   struct Pf {
-    f4_t ah;
+    f4_t ah, oo;  // oo: o, for the map's dden
     uint2 kw, qw, dw;
     float rk, den;
   };
+  float ndp = 0.f;  // MAP, lane (li, gq = 0) of wave w: feature 16 w + li of sum_t dden_t phi(q_t)
   Pf pf[2];
   auto fetch = [&](int64_t cs, int mm, int tid) {
     const int64_t tok = (s * T + cs) * D;
@@ -1151,6 +1155,7 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       const int tt = t < mm ? t : 0;  // rows past the chunk: a row of it, zeroed when staged
       const uint32_t rb = static_cast<uint32_t>(tt * REC), o = static_cast<uint32_t>(tt * D + c);
       pf[it].ah = at32(reinterpret_cast<const f4_t *>(rc), (rb + BwRec<D>::AH + c) / 4);
+      if constexpr (MAP) pf[it].oo = at32(reinterpret_cast<const f4_t *>(rc), (rb + BwRec<D>::O + c) / 4);
       pf[it].kw = at32(reinterpret_cast<const uint2 *>(k + tok), o / 4);
       pf[it].qw = at32(reinterpret_cast<const uint2 *>(q + tok), o / 4);
       pf[it].dw = at32(reinterpret_cast<const uint2 *>(dout + tok), o / 4);
@@ -1170,7 +1175,7 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     asm volatile("" : "+v"(tid_o));
     const int tid = tid_o, lane = tid & 63, li = lane & 15, gq = lane >> 4;
     // X at the chunk's last token, before its terms
-    {
+    if constexpr (!MAP) {
       f4_t *xc = reinterpret_cast<f4_t *>(Xc + (s * NX + (c1 - 1) / BW_CC) * D * D);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) at32(xc, static_cast<uint32_t>(((16 * w + li) * D + 16 * kb + 4 * gq) / 4)) = Xt[kb];
@@ -1182,6 +1187,7 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     for (int it = 0; it < 2; ++it) {
       const int e = tid + it * NT, t = e / G4, c = 4 * (e % G4);
       f4_t ah = f4_zero(), kh = f4_zero(), fq = f4_zero(), dn = f4_zero();
+      float po = 0.f;
       if (t < m) {
         const Pf &v = pf[it];
         ah = v.ah;
@@ -1193,7 +1199,12 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
           kh[j] = k4[j] * v.rk;
           fq[j] = phi(q4[j]);
           dn[j] = d4[j] / v.den;
+          if constexpr (MAP) po = fmaf(d4[j], v.oo[j], po);
         }
+      }
+      if constexpr (MAP) {
+        sh.dpo[t][c / 4] = po;
+        if (c == 0) sh.dd[t] = t < m ? pf[it].den : 1.f;  // den, turned into dden below
       }
       auto stage2 = [&](uint16_t (*X)[BW_CC][LDB], const f4_t &x) {
         uint32_t a[2], b[2];
@@ -1212,6 +1223,12 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       fetch(c0n, static_cast<int>(c0 - c0n), tid);
     }
     __syncthreads();
+    if (MAP && w == LW && lane < BW_CC) {  // dden_t = -(do_t . o_t) / den_t, in a fixed order
+      float x = 0.f;
+#pragma unroll
+      for (int g = 0; g < G4; ++g) x += sh.dpo[lane][g];
+      sh.dd[lane] = -x / sh.dd[lane];
+    }
     // ---- Ma = triu0(Ahat Phi^T); the diagonal blocks of Ahat Khat^T (strictly upper, fp32)
     // and its (0, 1) block (two terms) ----
     for (int job = job0; job < 6; job += jstep) {
@@ -1274,12 +1291,23 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
         rhs[ti] = mm2_ss(ld2_4x2(&sh.Ma[0][tr][4 * gq], &sh.Ma[0][tr][16 + 4 * gq], MS), bdn, acc);
       }
     }
+    if constexpr (MAP) {  // sum_t dden_t phi(q_t) at feature 16 w + li
+      const Split2 fq = ld2_tr(&sh.Fq[0][0][0], TS, LDB, 4 * gq, 16 + 4 * gq, 16 * w, li);
+      float x = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f0 = bf_val(__builtin_bit_cast(uint16_t, fq.h[e])) + bf_val(__builtin_bit_cast(uint16_t, fq.l[e]));
+        const float f1 = bf_val(__builtin_bit_cast(uint16_t, fq.h[4 + e])) + bf_val(__builtin_bit_cast(uint16_t, fq.l[4 + e]));
+        x = fmaf(sh.dd[4 * gq + e], f0, fmaf(sh.dd[16 + 4 * gq + e], f1, x));
+      }
+      ndp += sum_rows4(x);
+    }
     __syncthreads();  // the inverses
     // ---- dR_b = Iv_b rhs_b, dR_a = Iv_a (rhs_a - Mk dR_b) (K = 16 products) ----
     const f4_t dRb = mm2h_ss(ld2_4h(&sh.Iv[1][0][li][4 * gq], HS), split2_4h(rhs[1]), f4_zero());
     const f4_t cor = mm2h_ss(ld2_4h(&sh.Mk[0][li][4 * gq], HS), split2_4h(dRb), f4_zero());
     const f4_t dRa = mm2h_ss(ld2_4h(&sh.Iv[0][0][li][4 * gq], HS), split2_4h(rhs[0] - cor), f4_zero());
-    {
+    if constexpr (!MAP) {
       float *dvb = dv + tok0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1299,6 +1327,16 @@ k_bw_xsweepb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
       }
     }
     c1 = c0;
+  }
+  if constexpr (MAP) {  // Lmap = Pi_p^T, Bmap = X, and the segment's sum of dden phi(q), at slot P - 1 - p
+    const int lane = threadIdx.x & 63, li = lane & 15, gq = lane >> 4;
+    float *dst = lb + slot * 2 * D * D;
+    const float *pi = fpm + (s * P + p) * 2 * D * D;
+    for (int idx = threadIdx.x; idx < D * D; idx += NT) dst[idx] = pi[(idx % D) * D + idx / D];
+    f4_t *bm = reinterpret_cast<f4_t *>(dst + D * D);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) at32(bm, static_cast<uint32_t>(((16 * w + li) * D + 16 * kb + 4 * gq) / 4)) = Xt[kb];
+    if (gq == 0) nd[slot * D + 16 * w + li] = ndp;
   }
 }
 
@@ -1936,8 +1974,9 @@ void launch_sweep(const TIn *q, const TIn *k, const TIn *dout, const float *rec,
                   float *dv, float *xc, const Problem &pr, const BwPlan &bp, unsigned P, hipStream_t st) {
   const unsigned S = static_cast<unsigned>(pr.streams);
   if constexpr (sizeof(TIn) == 2 && D <= 96)
-    VLA_LAUNCH("k_bw_esweep", (k_bw_xsweepb<D>), dim3(S, P), dim3(XsCfg<D>::NT), 0, st, q, k, dout, rec,
-               E, dv, xc, pr.T, bp.L, bp.P);
+    VLA_LAUNCH("k_bw_esweep", (k_bw_xsweepb<D, false>), dim3(S, P), dim3(XsCfg<D>::NT), 0, st, q, k,
+               dout, rec, E, dv, xc, static_cast<const float *>(nullptr), static_cast<float *>(nullptr),
+               static_cast<float *>(nullptr), pr.T, bp.L, bp.P);
   else
     VLA_LAUNCH("k_bw_esweep", (k_bw_esweep<D, TIn>), dim3(S, P), dim3(BW_NT), 0, st, q, k, dout, rec,
                E, dv, xc, pr.T, bp.L, bp.P);
@@ -1990,9 +2029,15 @@ hipError_t launch_bw_t(const Problem &pr, int chunk, const BackwardIO &io, void 
     // normalisers were and the segment R sums where A was; the forward's own maps (Pi_p) are
     // read for the L part of the backward's.
     float *lb = reinterpret_cast<float *>(base + bp.off_md), *E = cs.S_seg, *nd = cs.n_seg, *W = cs.A_seg;
-    VLA_LAUNCH("k_bw_dsmap", (k_bw_dsmap<D, TIn>), dim3(S, P - 1), dim3(BW_NT), 0, st, q, k, dout,
-               static_cast<const float *>(rec), static_cast<const float *>(cs.pib), lb, nd, pr.T,
-               bp.L, bp.P);
+    if constexpr (sizeof(TIn) == 2 && D <= 96)  // the chunked sweep from a zero cotangent
+      VLA_LAUNCH("k_bw_dsmap", (k_bw_xsweepb<D, true>), dim3(S, P - 1), dim3(XsCfg<D>::NT), 0, st, q, k,
+                 dout, static_cast<const float *>(rec), static_cast<const float *>(nullptr),
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr),
+                 static_cast<const float *>(cs.pib), lb, nd, pr.T, bp.L, bp.P);
+    else
+      VLA_LAUNCH("k_bw_dsmap", (k_bw_dsmap<D, TIn>), dim3(S, P - 1), dim3(BW_NT), 0, st, q, k, dout,
+                 static_cast<const float *>(rec), static_cast<const float *>(cs.pib), lb, nd, pr.T,
+                 bp.L, bp.P);
     err = launch_affine_prefix(pr, lb, E, bp.P, io.dS_T, nd, io.dn_T, st);
     if (err != hipSuccess) return err;
     launch_sweep<D, TIn>(q, k, dout, rec, E, io.dv, xc, pr, bp, P, st);
