@@ -1334,16 +1334,28 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // with lambda0 < d / 256 (unit-variance inputs then give cancellation factors above ~256,
     // which two-term operands, 16 significant bits, cannot absorb).
     const bool three = sio.A0 == nullptr && pr.lambda0 < static_cast<float>(D) / 256.0f;
+    // d = 96, two-term operands, an even number of streams: the same segment of two streams per
+    // workgroup (twelve waves, three per SIMD), in the A side and in the final pass
+    constexpr int NP = D == 96 ? 2 : 1;
+    const bool pair = NP == 2 && S % 2 == 0;
     if (rec != nullptr) {  // with the backward's records (z, ahat, delta, ||A khat||, A checkpoints)
       if (three)
         VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 3, true>), dim3(S, P), dim3(AwyCfg<D, 3>::NT), 0, st,
                    qq, kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps, rec->rec, rec->ck);
+      else if (pair)
+        VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2, true, NP>), dim3(S / NP, P), dim3(NP * AwyCfg<D, 2>::NT),
+                   0, st, qq, kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps, rec->rec,
+                   rec->ck);
       else
         VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2, true>), dim3(S, P), dim3(AwyCfg<D, 2>::NT), 0, st,
                    qq, kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps, rec->rec, rec->ck);
     } else if (three) {
       VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 3>), dim3(S, P), dim3(AwyCfg<D, 3>::NT), 0, st, qq,
                  kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps,
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr));
+    } else if (pair) {
+      VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2, false, NP>), dim3(S / NP, P), dim3(NP * AwyCfg<D, 2>::NT),
+                 0, st, qq, kk, uu, Mw, nkw, alh, rdw, A_final, pl.T, pl.L, pl.P, pr.eps,
                  static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     } else {
       VLA_LAUNCH("k_aside_wy", (k_aside_wy<D, 2>), dim3(S, P), dim3(AwyCfg<D, 2>::NT), 0, st, qq,
@@ -1380,10 +1392,21 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // workgroup then fits twice per CU (54 KB of LDS and 127 VGPRs at d = 96), and the
     // segment maps it starts from do not depend on either pass's chunking.
     constexpr int CF = CH < 32 ? CH : 32;
-    if (rec != nullptr)  // the backward's records (r, o, 1/||k||, den, S checkpoints)
+    // d = 96 and an even number of streams: the same segment of two streams per workgroup
+    constexpr int NP = D == 96 ? 2 : 1;
+    const bool pair = NP == 2 && S % 2 == 0;
+    if (rec != nullptr && pair)  // the backward's records (r, o, 1/||k||, den, S checkpoints)
+      VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true, true, NP>), dim3(S / NP, P),
+                 dim3(NP * SwbCfg<D, CF, true>::NT), 0, st, qq, kk, vv, alh, rdw, s0w, pbw,
+                 static_cast<TIn *>(nullptr), S_final, nkw, pl.T, pl.L, pl.P, rec->rec, rec->ck);
+    else if (rec != nullptr)
       VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT),
                  0, st, qq, kk, vv, alh, rdw, s0w, pbw, static_cast<TIn *>(nullptr), S_final, nkw, pl.T,
                  pl.L, pl.P, rec->rec, rec->ck);
+    else if (pair)
+      VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true, false, NP>), dim3(S / NP, P),
+                 dim3(NP * SwbCfg<D, CF, true>::NT), 0, st, qq, kk, vv, alh, rdw, s0w, pbw, oo, S_final,
+                 nkw, pl.T, pl.L, pl.P, static_cast<float *>(nullptr), static_cast<float *>(nullptr));
     else
       VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT), 0,
                  st, qq, kk, vv, alh, rdw, s0w, pbw, oo, S_final, nkw, pl.T, pl.L, pl.P,

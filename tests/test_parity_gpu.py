@@ -161,6 +161,26 @@ def test_chunk_small_shapes(d, dt, T, C):
     _check(w, range(3), out, S, A, refs, f"chunk d={d} {dt} T={T} C={C}")
 
 
+@pytest.mark.parametrize("T,C", [(37, 16), (700, 32), (1300, 64)])
+def test_chunk_two_streams_per_workgroup(T, C):
+    """bf16 inputs at d = 96 with an even number of streams run the A side and the final pass
+    with the same segment of two streams in one workgroup; an odd number runs one stream per
+    workgroup.  On 4 streams: parity of every stream against the oracle, and the first 3 streams
+    bitwise equal to a 3-stream call on the same inputs (both calls have the same segments: at
+    most 4 x 1300 tokens per call, far below 2048 segments of the shortest bf16 length, 256)."""
+    w = get_workload("long_t131072_d96").resized(name=f"pair_T{T}_C{C}", B=1, H=4, T=T, lambda0=0.7)
+    _say(f"[case] two streams per workgroup: 4 (and 3) x {T} tokens, d = 96, C = {C}")
+    out4, S4, A4 = _run(w, "chunk", chunk=C)
+    out3, S3, A3 = _run(w, "chunk", streams=range(3), chunk=C)
+    q, k, v, u = make_inputs(w)
+    refs = [oracle_forward(q[s], k[s], v[s], u[s], w.lambda0, eps=w.eps) for s in range(4)]
+    _check(w, range(4), out4, S4, A4, refs, f"pair d=96 bf16 T={T} C={C}")
+    same = [torch.equal(a.reshape(-1)[: b.numel()], b.reshape(-1))
+            for a, b in ((out4, out3), (S4, S3), (A4, A3))]
+    _say(f"[parity] pair T={T} C={C}: streams 0..2 of 4 bitwise equal to 3 streams: {same}")
+    assert all(same)
+
+
 @pytest.mark.parametrize("name", ["mqar_t512_d32", "iid_t4096_d64"])
 def test_chunk_workloads_all_streams(name):
     w = get_workload(name)
