@@ -339,30 +339,53 @@ __global__ void __launch_bounds__(256) k_inv64(const double *__restrict__ Md, fl
     for (int y = 0; y < NR; ++y) a[x][y] = src[(ri + 16 * x) * D + cj + 16 * y];
   for (int k = 0; k < D; ++k) {
     const int b = k & 1, kx = k >> 4, kr = k & 15;
-    // (register indices stay compile-time constants: the block of the pivot is selected by
-    // predicate, not by indexing, which would put the matrix in scratch memory)
-#pragma unroll
-    for (int x = 0; x < NR; ++x)
+    // Register indices stay compile-time constants: the pivot's block of rows (columns) is
+    // picked by a chain of selects, not by indexing, which would put the matrix in scratch
+    // memory; the threads of the pivot row (column) then write their values in one guarded
+    // region instead of one per element.
+    if (ri == kr) {
 #pragma unroll
       for (int y = 0; y < NR; ++y) {
-        if (x == kx && ri == kr) rowk[b][cj + 16 * y] = a[x][y];
-        if (y == kx && cj == kr) colk[b][ri + 16 * x] = a[x][y];
+        double v = a[0][y];
+#pragma unroll
+        for (int x = 1; x < NR; ++x) v = (x == kx) ? a[x][y] : v;
+        rowk[b][cj + 16 * y] = v;
       }
+    }
+    if (cj == kr) {
+#pragma unroll
+      for (int x = 0; x < NR; ++x) {
+        double v = a[x][0];
+#pragma unroll
+        for (int y = 1; y < NR; ++y) v = (y == kx) ? a[x][y] : v;
+        colk[b][ri + 16 * x] = v;
+      }
+    }
     __syncthreads();
+    // In-place Gauss-Jordan step with r = the pivot row scaled by 1/pivot, its pivot entry
+    // 1/pivot, and c_i = A[i][k] (-1 for the pivot row):  A[i][j] <- keep * A[i][j] - c_i r_j,
+    // keep = 0 on the pivot row and the pivot column.  So the pivot row becomes r, the pivot
+    // column -A[i][k]/pivot, and every other entry A[i][j] - A[i][k] A[k][j]/pivot: one fma and
+    // one select per entry.
     const double ip = 1.0 / rowk[b][k];
+    double ry[NR], cx[NR];
+#pragma unroll
+    for (int y = 0; y < NR; ++y) {
+      const int j = cj + 16 * y;
+      ry[y] = (j == k) ? ip : rowk[b][j] * ip;
+    }
 #pragma unroll
     for (int x = 0; x < NR; ++x) {
       const int i = ri + 16 * x;
-      const double cik = colk[b][i] * ip;
+      cx[x] = (i == k) ? -1.0 : colk[b][i];
+    }
+#pragma unroll
+    for (int x = 0; x < NR; ++x) {
+      const bool prow = ri + 16 * x == k;
 #pragma unroll
       for (int y = 0; y < NR; ++y) {
-        const int j = cj + 16 * y;
-        if (i == k)
-          a[x][y] = (j == k) ? ip : a[x][y] * ip;
-        else if (j == k)
-          a[x][y] = -cik;
-        else
-          a[x][y] = fma(-cik, rowk[b][j], a[x][y]);
+        const bool keep = !prow && cj + 16 * y != k;
+        a[x][y] = fma(-cx[x], ry[y], keep ? a[x][y] : 0.0);
       }
     }
   }
