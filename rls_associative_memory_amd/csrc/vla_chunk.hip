@@ -50,6 +50,7 @@ struct ChunkPlan {
   int D = 0, C = 0;
   int64_t S = 0, T = 0, L = 0, P = 0;
   size_t off_m = 0, off_nk = 0, off_alpha = 0, off_rkden = 0, off_pib = 0, off_s0 = 0, off_minv = 0;
+  size_t off_tiles = 0;  // bf16 inputs with more than one segment and C >= 32, else unused
   size_t total = 0;
 };
 
@@ -85,6 +86,10 @@ static ChunkPlan make_plan(const Problem &p, int C) {
   pl.off_pib = off;   off = align256(off + S * P * 2 * D * D * 4);
   pl.off_s0 = off;    off = align256(off + S * P * D * D * 4);
   pl.off_minv = off;  off = align256(off + S * D * D * 4);  // A0^{-1} of a carried state
+  if (swb_shares_tiles(p.dtype == Dtype::F32, pl.P, C)) {  // the S passes' shared tiles
+    pl.off_tiles = off;
+    off = align256(off + S * static_cast<size_t>(swb_tile_blocks(pl.T)) * kSwbTileBlock * 2);
+  }
   pl.total = off;
   return pl;
 }
@@ -1399,14 +1404,18 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
                  static_cast<float *>(nullptr), static_cast<float *>(nullptr), static_cast<float *>(nullptr));
   }
   if constexpr (sizeof(TIn) == 2) {
-    // bf16 inputs: S side on the bf16 matrix cores.
+    // bf16 inputs: S side on the bf16 matrix cores.  The map pass covers the segments
+    // p < npre (with the backward's records all of them: the backward reads every segment's
+    // Pi but the first's) and leaves its tiles for the final pass to load.
+    const unsigned npre = rec != nullptr ? P : P - 1;
+    uint16_t *tlw = swb_shares_tiles(false, pl.P, CH) ? reinterpret_cast<uint16_t *>(ws + pl.off_tiles)
+                                                      : nullptr;
+    const int64_t npf = static_cast<int64_t>(npre);
     if (P > 1) {
-      // with the backward's records the last segment's map too (the backward reads every
-      // segment's Pi but the first's)
-      VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, rec != nullptr ? P : P - 1),
+      VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, npre),
                  dim3(SwbCfg<D, CH, false>::NT), 0, st, qq, kk, vv, alh, rdw, s0w, pbw, oo,
                  S_final, static_cast<const float *>(nullptr), pl.T, pl.L, pl.P,
-                 static_cast<float *>(nullptr), static_cast<float *>(nullptr));
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr), tlw, int64_t(0));
     }
     VLA_LAUNCH("k_sprefix", (k_sprefix<D>), dim3(S, D / 16), dim3(D / 16 * kWave), 0, st, pbw,
                s0w, pl.P, sio.S0, nkw, sio.n0, n_final, rec != nullptr ? rec->n_end : nullptr);
@@ -1421,19 +1430,20 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     if (rec != nullptr && pair)  // the backward's records (r, o, 1/||k||, den, S checkpoints)
       VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true, true, NP>), dim3(S / NP, P),
                  dim3(NP * SwbCfg<D, CF, true>::NT), 0, st, qq, kk, vv, alh, rdw, s0w, pbw,
-                 static_cast<TIn *>(nullptr), S_final, nkw, pl.T, pl.L, pl.P, rec->rec, rec->ck);
+                 static_cast<TIn *>(nullptr), S_final, nkw, pl.T, pl.L, pl.P, rec->rec, rec->ck, tlw, npf);
     else if (rec != nullptr)
       VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT),
                  0, st, qq, kk, vv, alh, rdw, s0w, pbw, static_cast<TIn *>(nullptr), S_final, nkw, pl.T,
-                 pl.L, pl.P, rec->rec, rec->ck);
+                 pl.L, pl.P, rec->rec, rec->ck, tlw, npf);
     else if (pair)
       VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true, false, NP>), dim3(S / NP, P),
                  dim3(NP * SwbCfg<D, CF, true>::NT), 0, st, qq, kk, vv, alh, rdw, s0w, pbw, oo, S_final,
-                 nkw, pl.T, pl.L, pl.P, static_cast<float *>(nullptr), static_cast<float *>(nullptr));
+                 nkw, pl.T, pl.L, pl.P, static_cast<float *>(nullptr), static_cast<float *>(nullptr), tlw,
+                 npf);
     else
       VLA_LAUNCH("k_swy_final", (k_swyb<D, CF, true>), dim3(S, P), dim3(SwbCfg<D, CF, true>::NT), 0,
                  st, qq, kk, vv, alh, rdw, s0w, pbw, oo, S_final, nkw, pl.T, pl.L, pl.P,
-                 static_cast<float *>(nullptr), static_cast<float *>(nullptr));
+                 static_cast<float *>(nullptr), static_cast<float *>(nullptr), tlw, npf);
   } else {
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swy<D, CH, false, TIn>), dim3(S, rec != nullptr ? P : P - 1, 2),
@@ -1489,6 +1499,7 @@ static hipError_t launch_chunk_group(const Problem &p, const ChunkPlan &pl, int6
   g.off_pib += hs * P * 2 * D * D * 4;
   g.off_s0 += hs * P * D * D * 4;
   g.off_minv += hs * D * D * 4;
+  g.off_tiles += hs * static_cast<size_t>(swb_tile_blocks(pl.T)) * kSwbTileBlock * 2;
   Problem gp = p;
   gp.streams = n;
   const size_t tok = hs * T * D * (p.dtype == Dtype::F32 ? 4 : 2);

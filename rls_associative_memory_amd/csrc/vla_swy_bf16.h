@@ -63,6 +63,19 @@ struct SwbLds {
   float dpart[FINAL ? CH : 1][FINAL ? D / 32 : 1];  // phi(q) . n_p over 32 features of a token
 };
 
+// Tiles shared by the two S passes.  The inverses (I + Ka_tt)^{-1} of the 16-token diagonal
+// tiles and the off-diagonal tiles -Ka_ba of each 32-token block depend only on that block's
+// tokens (k, ahat, 1/||k||), not on the chunking, so the map pass (chunks of 32 or 64) writes
+// them and the final pass (chunks of 32) loads them for every segment the map pass covered
+// instead of forming them again.  Per stream and 32-token block (blocks counted from the
+// stream's first token): [3 tiles: inverse of tile 0, of tile 1, -Ka_10][2 bf16 terms]
+// [16 columns][16 rows], each tile as the passes keep it in LDS (transposed), 3 KB a block.
+constexpr int kSwbTileBlock = 3 * 2 * 16 * 16;  // uint16 per 32-token block
+__host__ __device__ inline int64_t swb_tile_blocks(int64_t T) { return (T + 31) / 32; }
+inline bool swb_shares_tiles(bool fp32_inputs, int64_t P, int chunk) {
+  return !fp32_inputs && P > 1 && chunk >= 32;
+}
+
 // The final pass at d <= 96 is held to 128 VGPRs (four waves per SIMD), so that two of its
 // workgroups share a CU.  A workgroup's waves are placed from the first SIMD on, so two
 // six-wave workgroups (d = 96) put four waves on two SIMDs and two on the others.  NSEG = 2
@@ -83,7 +96,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
        const uint16_t *__restrict__ ahat, const float *__restrict__ rkden,
        const float *__restrict__ s0, float *__restrict__ pib, bf16_t *__restrict__ out,
        float *__restrict__ S_final, const float *__restrict__ nstart, int64_t T, int64_t L,
-       int64_t P, float *__restrict__ brec, float *__restrict__ bck) {
+       int64_t P, float *__restrict__ brec, float *__restrict__ bck, uint16_t *__restrict__ tiles,
+       int64_t npre) {
   static_assert(FINAL || !REC, "records come from the final pass");
   using C = SwbCfg<D, CH, FINAL>;
   constexpr int NT = C::NT, NCT = C::NCT, NFT = C::NFT, NKS = C::NKS;
@@ -112,6 +126,13 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   constexpr int RF = BwRec<D>::F;
   float *brs = REC ? brec + s * T * RF : nullptr;
   float *bcs = REC ? bck + s * ((T + kBwCk - 1) / kBwCk) * 2 * D * D : nullptr;  // S halves
+
+  // the shared tiles: written by the map pass (chunks of 32 or 64 tokens), read by the final
+  // pass (chunks of 32) for the segments p < npre that the map pass covered
+  static_assert(CH % 32 == 0 || CH == 16, "chunks of 16, 32 or 64 tokens");
+  constexpr bool TSH = CH >= 32 && (!FINAL || CH == 32);
+  uint16_t *tls = (TSH && tiles != nullptr) ? tiles + s * swb_tile_blocks(T) * kSwbTileBlock : nullptr;
+  const bool pre = FINAL && tls != nullptr && p < npre;
 
   const bool pi_rows = !FINAL && wave < C::NWV;
   const int rowbase = 16 * (wave % C::NWV);
@@ -147,6 +168,11 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   constexpr int PA = (UA + NT - 1) / NT;
   uint4 pk[PK], pq[FINAL ? PK : 1], pv[PK];
   uint4 pa[PA];
+  // final pass: units tid, tid + NT, ... (16 bytes each) of the chunk's shared tiles
+  constexpr int UT = kSwbTileBlock / 8, PT = (UT + NT - 1) / NT;
+  uint4 ptl[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) ptl[i] = make_uint4(0u, 0u, 0u, 0u);
   float prk = 0.f, pden = 1.f;
   // Per-lane offsets are 32-bit (one stream's rows span far less than 4 GiB) from a
   // workgroup-uniform base, so each load needs one offset register.
@@ -174,6 +200,12 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     const uint32_t toff = (tid < mm) ? static_cast<uint32_t>(tid * 2) : 0u;
     prk = rc[toff];
     if constexpr (FINAL) pden = rc[toff + 1];
+    if constexpr (FINAL && TSH)  // units of the 32-token block at cs: 8 of its uint16 each
+      if (pre)
+#pragma unroll
+        for (int i = 0; i < PT; ++i)
+          if (tid + i * NT < UT)
+            ptl[i] = *reinterpret_cast<const uint4 *>(tls + (cs / 32) * kSwbTileBlock + 8 * (tid + i * NT));
   };
   prefetch(tb, tid);
   if constexpr (FINAL)  // phi(q) . n_p completes the A side's denominators (see below)
@@ -239,6 +271,18 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       sh.rk[tid] = tid < m ? prk : 0.f;
       if constexpr (FINAL) sh.rden[tid] = tid < m ? pden : 1.f;  // completed in the tile phase
     }
+    if constexpr (FINAL && TSH) {  // the block's tiles into the slots the Ka jobs would fill
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int u = tid + i * NT;
+        if (pre && u < UT) {
+          const int tile = u >> 6, term = (u >> 5) & 1, row = (u >> 1) & 15, h8 = u & 1;
+          uint16_t *dst = tile < 2 ? &sh.InvS[term][tile][row][8 * h8] : &sh.KaO[term][0][row][8 * h8];
+          *reinterpret_cast<uint4 *>(dst) = ptl[i];
+        }
+        asm volatile("" ::"v"(ptl[i].x));
+      }
+    }
     // Every prefetched register counts as used here, in every thread (lanes that stage nothing
     // included), so no load is still pending when the next prefetch reuses the registers: the
     // compiler then need not wait for the stores issued since.
@@ -256,7 +300,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
     //      jobs: [0, NCT) Ka_tt, [NCT, NCT + NOD) Ka_ba, then Qa_tt, Qa_ba
     constexpr int NKJ = NCT + NOD;
     constexpr int NJOB = (FINAL ? 2 : 1) * NKJ;
-    for (int job = wave; job < NJOB; job += C::NWT) {
+    // with the shared tiles staged, the final pass runs the Qa jobs only
+    for (int job = (pre ? NKJ : 0) + wave; job < NJOB; job += C::NWT) {
       const bool isq = job >= NKJ;
       const int jk = isq ? job - NKJ : job;
       const bool diag = jk < NCT;
@@ -397,6 +442,21 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
       }
     }
     __syncthreads();
+    if constexpr (!FINAL && TSH) {  // the map pass hands its tiles to the final pass
+      if (tls != nullptr) {
+        constexpr int NBK = CH / 32, UNITS = kSwbTileBlock / 8;  // 32-token blocks, uint4 each
+        for (int u = tid; u < NBK * UNITS; u += NT) {
+          const int bb = u / UNITS, r = u % UNITS;
+          const int tile = r >> 6, term = (r >> 5) & 1, row = (r >> 1) & 15, h8 = r & 1;
+          if (c0 + 32 * bb < te) {
+            const uint16_t *src = tile < 2 ? &sh.InvS[term][2 * bb + tile][row][8 * h8]
+                                           : &sh.KaO[term][bb][row][8 * h8];
+            *reinterpret_cast<uint4 *>(tls + (c0 / 32 + bb) * kSwbTileBlock + 8 * r) =
+                *reinterpret_cast<const uint4 *>(src);
+          }
+        }
+      }
+    }
     // ---- this wave's rows: two tiles per step ---------------------------------------------
     // The next chunk's loads fly during the steps.
     if (c0 + CH < te) prefetch(c0 + CH, tid);
