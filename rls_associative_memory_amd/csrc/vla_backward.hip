@@ -1928,7 +1928,7 @@ BwPlan make_bw_plan(const Problem &p, int chunk) {
     chunk_segments(p, chunk, &b.L, &b.P);
     if (b.P > 1) {
       b.off_chunk = 0;
-      off = align256(chunk_workspace_bytes(p, chunk));
+      off = align256(chunk_workspace_bytes(p, chunk, true));
       b.off_md = off;
       off = align256(off + static_cast<size_t>(p.streams * b.P) * p.d * p.d * sizeof(double));
     } else {

@@ -50,13 +50,17 @@ struct ChunkPlan {
   int D = 0, C = 0;
   int64_t S = 0, T = 0, L = 0, P = 0;
   size_t off_m = 0, off_nk = 0, off_alpha = 0, off_rkden = 0, off_pib = 0, off_s0 = 0, off_minv = 0;
-  size_t off_tiles = 0;  // bf16 inputs with more than one segment and C >= 32, else unused
+  size_t off_tiles = 0;  // valid when tiles: the S passes' shared tiles
+  bool tiles = false;
   size_t total = 0;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-static ChunkPlan make_plan(const Problem &p, int C) {
+// records: the plan of the backward's chunked forward, whose S passes do not share tiles (its
+// final pass writes the token records and is bound by those stores: loading the tiles,
+// 403 MB at 32 x 131072 tokens, took it from 2.65 to 2.76 ms, forming them costs less).
+static ChunkPlan make_plan(const Problem &p, int C, bool records = false) {
   ChunkPlan pl;
   pl.D = p.d;
   pl.C = C;
@@ -86,7 +90,8 @@ static ChunkPlan make_plan(const Problem &p, int C) {
   pl.off_pib = off;   off = align256(off + S * P * 2 * D * D * 4);
   pl.off_s0 = off;    off = align256(off + S * P * D * D * 4);
   pl.off_minv = off;  off = align256(off + S * D * D * 4);  // A0^{-1} of a carried state
-  if (swb_shares_tiles(p.dtype == Dtype::F32, pl.P, C)) {  // the S passes' shared tiles
+  pl.tiles = !records && swb_shares_tiles(p.dtype == Dtype::F32, pl.P, C);
+  if (pl.tiles) {  // the S passes' shared tiles, last (a plan without them is a prefix)
     pl.off_tiles = off;
     off = align256(off + S * static_cast<size_t>(swb_tile_blocks(pl.T)) * kSwbTileBlock * 2);
   }
@@ -102,7 +107,9 @@ bool chunk_supported(const Problem &p, int chunk) {
   return p.d == 32 || p.d == 64 || p.d == 96 || p.d == 128;
 }
 
-size_t chunk_workspace_bytes(const Problem &p, int chunk) { return make_plan(p, chunk).total; }
+size_t chunk_workspace_bytes(const Problem &p, int chunk, bool records) {
+  return make_plan(p, chunk, records).total;
+}
 
 // ------------------------------------------------------------------------------------
 // Input staging helper: 16-byte vector of the input type -> fp32
@@ -1408,8 +1415,7 @@ static hipError_t launch_chunk_t(const Problem &pr, const ChunkPlan &pl, const v
     // p < npre (with the backward's records all of them: the backward reads every segment's
     // Pi but the first's) and leaves its tiles for the final pass to load.
     const unsigned npre = rec != nullptr ? P : P - 1;
-    uint16_t *tlw = swb_shares_tiles(false, pl.P, CH) ? reinterpret_cast<uint16_t *>(ws + pl.off_tiles)
-                                                      : nullptr;
+    uint16_t *tlw = pl.tiles && rec == nullptr ? reinterpret_cast<uint16_t *>(ws + pl.off_tiles) : nullptr;
     const int64_t npf = static_cast<int64_t>(npre);
     if (P > 1) {
       VLA_LAUNCH("k_swy_map", (k_swyb<D, CH, false>), dim3(S, npre),
@@ -1597,7 +1603,7 @@ hipError_t launch_chunk_states(const Problem &p, int chunk, const void *q, const
                                const void *v, const void *u, void *ws, double *Md,
                                hipStream_t stream, ChunkStates *cs) {
   if (!chunk_supported(p, chunk)) return hipErrorInvalidValue;
-  const ChunkPlan pl = make_plan(p, chunk);
+  const ChunkPlan pl = make_plan(p, chunk, true);
   char *w = static_cast<char *>(ws);
   cs->S_seg = reinterpret_cast<float *>(w + pl.off_s0);
   cs->A_seg = reinterpret_cast<float *>(w + pl.off_m);
@@ -1614,7 +1620,7 @@ hipError_t launch_chunk_records(const Problem &p, int chunk, const void *q, cons
                                 const void *v, const void *u, void *ws, double *Md,
                                 hipStream_t stream, const BwRecords &rec, ChunkStates *cs) {
   if (!chunk_supported(p, chunk)) return hipErrorInvalidValue;
-  const ChunkPlan pl = make_plan(p, chunk);
+  const ChunkPlan pl = make_plan(p, chunk, true);
   char *w = static_cast<char *>(ws);
   cs->S_seg = reinterpret_cast<float *>(w + pl.off_s0);
   cs->A_seg = reinterpret_cast<float *>(w + pl.off_m);

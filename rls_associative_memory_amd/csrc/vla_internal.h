@@ -36,7 +36,8 @@ hipError_t launch_decode(const Problem &p, const void *q, const void *k, const v
                          const void *u, void *out, const StateIO &st, hipStream_t stream);
 
 // Chunked path (time-segment parallel).  `ws` must hold chunk_workspace_bytes(p, C).
-size_t chunk_workspace_bytes(const Problem &p, int chunk);
+// records: the workspace of the backward's chunked forward (launch_chunk_records)
+size_t chunk_workspace_bytes(const Problem &p, int chunk, bool records = false);
 bool chunk_supported(const Problem &p, int chunk);
 int chunk_default(const Problem &p);
 // With `may_split`, calls of at least 2^20 tokens on two or more streams (not under graph
