@@ -130,7 +130,8 @@ k_swyb(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t 
   // the shared tiles: written by the map pass (chunks of 32 or 64 tokens), read by the final
   // pass (chunks of 32) for the segments p < npre that the map pass covered
   static_assert(CH % 32 == 0 || CH == 16, "chunks of 16, 32 or 64 tokens");
-  constexpr bool TSH = CH >= 32 && (!FINAL || CH == 32);
+  // (not with the backward's records: that final pass forms its own tiles)
+  constexpr bool TSH = CH >= 32 && (!FINAL || CH == 32) && !REC;
   uint16_t *tls = (TSH && tiles != nullptr) ? tiles + s * swb_tile_blocks(T) * kSwbTileBlock : nullptr;
   const bool pre = FINAL && tls != nullptr && p < npre;
 
