@@ -434,15 +434,29 @@ k_sym_copy(const float *__restrict__ src, float *__restrict__ dst, int64_t dst_s
 // with every block product on v_mfma_f32_16x16x4_f32 (operands packed k-minor in LDS).
 // ------------------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(256) k_inv(float *__restrict__ M, int64_t P) {
+// The symmetrisation buffer lies over the elimination buffers (it is used after the last block
+// step only), and at d = 96 the kernel is held to 128 VGPRs: four workgroups per CU, not two.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 96 ? 4 : 1)))
+k_inv(float *__restrict__ M, int64_t P) {
   constexpr int NB = D / 16;
   constexpr int NOWN = (NB * NB + 3) / 4;  // blocks per wave
-  __shared__ __attribute__((aligned(16))) float Pd[16][17];         // diagonal block, scalar GJ
-  __shared__ __attribute__((aligned(16))) float PiA[4][16][4];      // P^-1 as A operand [k/4][i][k%4]
-  __shared__ __attribute__((aligned(16))) float PiB[4][16][4];      // P^-1 as B operand [k/4][j][k%4]
-  __shared__ __attribute__((aligned(16))) float CP[NB][4][16][4];   // column panel (A operands)
-  __shared__ __attribute__((aligned(16))) float RP[NB][4][16][4];   // row panel (B operands)
-  __shared__ float sym[D][D + 1];
+  union Lds {
+    struct {
+      float Pd[16][17];         // diagonal block, scalar GJ
+      float PiA[4][16][4];      // P^-1 as A operand [k/4][i][k%4]
+      float PiB[4][16][4];      // P^-1 as B operand [k/4][j][k%4]
+      float CP[NB][4][16][4];   // column panel (A operands)
+      float RP[NB][4][16][4];   // row panel (B operands)
+    } e;
+    float sym[D][D + 1];        // the result, symmetrised at the end
+  };
+  __shared__ __attribute__((aligned(16))) Lds lds;
+  auto &Pd = lds.e.Pd;
+  auto &PiA = lds.e.PiA;
+  auto &PiB = lds.e.PiB;
+  auto &CP = lds.e.CP;
+  auto &RP = lds.e.RP;
+  auto &sym = lds.sym;
   const int64_t s = blockIdx.x, p = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15, gq = lane >> 4;
   float *base = M + (s * P + p) * D * D;
