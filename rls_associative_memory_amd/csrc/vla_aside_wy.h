@@ -255,6 +255,11 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
     __syncthreads();
     // ---- wave 0: G = L D L^T and L^{-1};  waves 1..D/32: readout denominators --------------
     if (w == 0) {
+      // The factorisation is the chunk's critical path, and its wave shares a SIMD with a
+      // denominator wave (of the other stream at d = 96): it issues first while it runs (the
+      // wave's own priority; on 32 x 131072 tokens at d = 96 the A side 1.95-2.00 -> 1.87-1.89 ms
+      // per launch).
+      __builtin_amdgcn_s_setprio(3);
       // Blocked LDL^T of G in two 16-column panels.  In a panel, lanes hold rows (of G, or of
       // the Schur complement) restricted to the panel's 16 columns, lanes 32..47 hold the
       // columns of the panel block of L^{-1} (starting from the identity), and pivots go two
@@ -368,6 +373,7 @@ k_aside_wy(const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
 #pragma unroll
         for (int r = 0; r < 16; ++r) sh.G[16 + r][mcol] = y[r];  // L^{-1}_21 | L^{-1}_22
       }
+      __builtin_amdgcn_s_setprio(0);
     } else if (w <= C::NKS) {
       // Readout denominators, key norms and the normaliser update of the chunk, one 32-feature
       // slice per wave (slice w - 1), on the matrix cores of waves that are otherwise idle
